@@ -1,0 +1,28 @@
+"""CPU fp64 reference for the gated delta-rule hot path.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or run
+anything in this package: only the test suite, the smoke check of the package
+entry point and the CPU-baseline leg of the benchmark use it. It shares no code
+with the HIP library; it takes plain numpy arrays and returns numpy arrays.
+
+Every function is written from the two pages that define the method:
+
+* "LeapQuant: an 8-bit recurrent state that stops rounding every token"
+  (ai.satyajit.si) -- the delta-rule and Gated DeltaNet updates (section "The
+  state, from the update rule up", eq. 1 and eq. 3), per-token rounding (section
+  "Rounding every token", eq. 2), the window leap (section "Fix one: leap over a
+  window", eq. 4 and eq. 10), compensator tokens (section "Fix two", eq. 5) and
+  row smoothing (section "Fix three", eq. 7), and the stored layout (section
+  "What 1.19 bytes buys").
+* "ZeCO: Zero Communication Overhead Sequence Parallelism for Linear Attention"
+  (paper summary) -- gated linear attention per token and per chunk (section
+  "Gated Linear Attention (GLA) Formulation"), and the decomposition of a shard
+  around its incoming state (section "Global State Update Formula", eq. 6).
+
+Orientation: every state is ``[d_v][d_k]`` (rows are value channels). The pages
+write ``d_k x d_v``; their formulas are used transposed.
+
+Parity status of each function is stated in its docstring; the only function
+without a pin is ``leapq.toy_error_trend`` (a trend, "parity unpinned").
+"""
+from . import gdn, gla, leapq  # noqa: F401

@@ -1,0 +1,233 @@
+"""Pins of the LeapQuant oracle against what the LeapQuant page fixes."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import gdn, leapq
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _inputs(rng, T, N, d, amu=4.0):
+    q = rng.standard_normal((T, N, d))
+    k = rng.standard_normal((T, N, d))
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((T, N, d))
+    a = 1 / (1 + np.exp(-rng.normal(amu, 1, (T, N))))
+    b = 1 / (1 + np.exp(-rng.normal(0, 1, (T, N))))
+    return q, k, v, a, b
+
+
+def _tn(x):   # [T][N][d] -> [N][T][d]
+    return np.swapaxes(x, 0, 1)
+
+
+def test_window_one_no_extras_equals_per_token_rounding_eq2():
+    """Eq. 2 rounding after every token, written separately, must equal the
+    windowed scheme with W = 1, no compensator tokens and no smoothing."""
+    rng = np.random.default_rng(1)
+    T, N, d = 24, 3, 16
+    q, k, v, a, b = _inputs(rng, T, N, d)
+    S0 = 0.05 * rng.standard_normal((N, d, d))
+    o1, Z1, s1 = leapq.per_step_int8(q, k, v, a, b, S0)
+    r = leapq.decode_run(q, k, v, a, b, S0, None, window=1, rank=0, smooth_mode=2,
+                         buf_dtype=np.float64)
+    np.testing.assert_array_equal(r["st"]["Z"], Z1)
+    np.testing.assert_array_equal(r["st"]["s"], s1)
+    np.testing.assert_allclose(r["o"], o1, rtol=0, atol=1e-12)
+
+
+def test_eq10_readout_equals_dense_eq4_state():
+    rng = np.random.default_rng(2)
+    N, d, m = 3, 16, 9
+    S0 = rng.standard_normal((N, d, d))
+    Q0 = rng.standard_normal((d, 4))
+    st = leapq.flush(S0, Q0, rank=4)
+    buf = [(rng.standard_normal((N, d)), rng.standard_normal((N, d)), rng.uniform(0.5, 1, N))
+           for _ in range(m)]
+    x = rng.standard_normal((N, d))
+    dense = leapq.rebuild(st, buf)
+    np.testing.assert_allclose(leapq.readout(st, buf, x), np.einsum("nvk,nk->nv", dense, x),
+                               atol=1e-12)
+    # the rebuild itself: decayed stored state plus decayed rank-one writes
+    g = np.prod(np.stack([bb[2] for bb in buf]), axis=0)
+    ref = g[:, None, None] * leapq.dequant(st)
+    for j, (kj, uj, _) in enumerate(buf):
+        gj = np.prod(np.stack([bb[2] for bb in buf[j + 1:]] + [np.ones(N)]), axis=0)
+        ref += gj[:, None, None] * uj[:, :, None] * kj[:, None, :]
+    np.testing.assert_allclose(dense, ref, atol=1e-12)
+
+
+def test_rank_r_state_is_caught_by_compensators():
+    """A state of rank <= r lies in the fitted subspace after one round from a
+    generic start, so the unquantised residual S - (S Q) Q^T vanishes."""
+    rng = np.random.default_rng(3)
+    N, d, r = 2, 32, 4
+    S = np.einsum("nvr,nkr->nvk", rng.standard_normal((N, d, r)), rng.standard_normal((N, d, r)))
+    Q0 = rng.standard_normal((d, r))
+    Q = leapq.fit_compensators(S, Q0, r, iters=1)
+    np.testing.assert_allclose(np.swapaxes(Q, -1, -2) @ Q, np.broadcast_to(np.eye(r), (N, r, r)),
+                               atol=1e-5)
+    # the subspace is exact: project onto an exactly orthonormal basis of it
+    Qh = np.linalg.qr(Q)[0]
+    R = S - (S @ Qh) @ np.swapaxes(Qh, -1, -2)
+    assert np.abs(R).max() < 1e-10 * np.abs(S).max()
+    # the Gram shift leaves the fitted columns short of unit norm by ~1e-6 only
+    R = S - (S @ Q) @ np.swapaxes(Q, -1, -2)
+    assert np.abs(R).max() < 2e-5 * np.abs(S).max()
+    st = leapq.flush(S, Q0, rank=r)
+    # what is left after subtracting the fp16 pieces is fp16 rounding only
+    R16 = S - np.swapaxes(st["ut"], -1, -2) @ st["kt"]
+    assert np.abs(R16).max() < 4e-3 * np.abs(S).max()
+
+
+def test_subspace_iteration_reaches_eckart_young_bound():
+    """With a spectral gap and enough rounds, the fitted pieces achieve the
+    Eckart-Young minimum ||S - S_r||_F^2 = sum_{i>r} sigma_i^2; the SVD mode
+    achieves it exactly."""
+    rng = np.random.default_rng(4)
+    d, r = 24, 4
+    U, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    V, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    sig = np.concatenate([[40, 30, 20, 10], np.linspace(1, 0.1, d - r)])
+    S = (U * sig) @ V.T
+    tail = np.sum(sig[r:] ** 2)
+    for Q in (leapq.fit_compensators(S[None], rng.standard_normal((d, r)), r, iters=40),
+              leapq.fit_compensators(S[None], None, r, svd=True)):
+        R = S - (S @ Q[0]) @ Q[0].T
+        np.testing.assert_allclose(np.sum(R ** 2), tail, rtol=1e-8)
+    # one round from a random start is worse than the bound but far below ||S||^2
+    Q1 = leapq.fit_compensators(S[None], rng.standard_normal((d, r)), r, iters=1)
+    R1 = S - (S @ Q1[0]) @ Q1[0].T
+    assert tail <= np.sum(R1 ** 2) < 0.2 * np.sum(sig ** 2)
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_reconstruction_within_half_a_step(mode):
+    rng = np.random.default_rng(5)
+    N, d = 3, 32
+    S = rng.standard_normal((N, d, d))
+    S[:, :, 3] *= 50
+    st = leapq.flush(S, rng.standard_normal((d, 4)), rank=4, smooth_mode=mode)
+    err = np.abs(leapq.dequant(st) - S)
+    step = st["s"][:, :, None] / 127.0 * st["c"][:, None, :]
+    assert np.all(err <= 0.5 * step * (1 + 1e-5) + 1e-12)
+
+
+def test_smoothing_statistic_and_quant_scale_orientation():
+    """Smoothing is one factor per key channel (page: per key row), the root of
+    the mean magnitude over the value channels; the quantisation scale is one
+    per value channel, its largest smoothed magnitude, which maps to +-127."""
+    d = 8
+    m = np.arange(1, d + 1, dtype=np.float64)               # column magnitudes
+    signs = np.where(np.add.outer(np.arange(d), np.arange(d)) % 2 == 0, 1.0, -1.0)
+    S = (signs * m[None, :])[None]                          # |S[v,k]| = m_k
+    st = leapq.flush(S, None, rank=0, smooth_mode=0)
+    np.testing.assert_allclose(st["c"][0], np.sqrt(m), rtol=1e-7)
+    st1 = leapq.flush(S, None, rank=0, smooth_mode=1)
+    np.testing.assert_allclose(st1["c"][0], m, rtol=1e-7)          # root mean square of a constant column
+    np.testing.assert_allclose(st["s"][0], np.full(d, np.sqrt(m[-1])), rtol=1e-7)
+    assert np.all(np.abs(st["Z"][0][:, -1]) == 127)
+    # a column that is not constant separates the two statistics
+    S2 = S.copy()
+    S2[0, 0, 0] = 9.0
+    c0 = leapq.flush(S2, None, rank=0, smooth_mode=0)["c"][0, 0]
+    c1 = leapq.flush(S2, None, rank=0, smooth_mode=1)["c"][0, 0]
+    np.testing.assert_allclose(c0, np.sqrt((9 + 7) / 8), rtol=1e-7)
+    np.testing.assert_allclose(c1, np.sqrt((81 + 7) / 8), rtol=1e-7)
+
+
+def test_codes_invariant_under_power_of_four_scaling():
+    rng = np.random.default_rng(6)
+    S = rng.standard_normal((2, 16, 16))
+    Q0 = rng.standard_normal((16, 4))
+    base = leapq.flush(S, Q0, rank=0, smooth_mode=0)
+    for f in (4.0, 1 / 16):
+        st = leapq.flush(f * S, Q0, rank=0, smooth_mode=0)
+        np.testing.assert_array_equal(st["Z"], base["Z"])
+        np.testing.assert_allclose(st["s"], np.sqrt(f) * base["s"], rtol=0)
+
+
+def test_zero_state_is_finite_and_zero():
+    st = leapq.flush(np.zeros((2, 16, 16)), np.ones((16, 4)), rank=4, smooth_mode=0)
+    for key in ("s", "c", "kt", "ut"):
+        assert np.all(np.isfinite(st[key]))
+    assert np.all(st["Z"] == 0)
+    assert np.all(leapq.dequant(st) == 0)
+
+
+def test_stored_bytes_match_page_layout():
+    with open(os.path.join(GOLD, "leapq_layout.json")) as f:
+        g = json.load(f)
+    n = leapq.stored_bytes(g["d_v"], g["d_k"], g["rank"])
+    assert n == g["bytes"]
+    assert n / (g["d_v"] * g["d_k"]) == g["bytes_per_element"]
+
+
+def test_decay_freezing_counts_of_the_roundings():
+    """The page's exhaustive count of values that never decay when re-rounded,
+    reproduced with the bf16 cast of the input generator (torch) and the fp16
+    cast of the compensator tokens (numpy)."""
+    with open(os.path.join(GOLD, "decay_freeze.json")) as f:
+        g = json.load(f)
+    lo, hi = np.log10(g["range"][0]), np.log10(g["range"][1])
+    x = 10.0 ** np.linspace(lo, hi, 200001)
+    xb = torch.tensor(x, dtype=torch.float32).to(torch.bfloat16)
+    for a, want in g["bf16"].items():
+        y = (xb.float() * torch.tensor(float(a))).to(torch.bfloat16)
+        assert abs((y == xb).float().mean().item() - want) <= g["tol"], a
+    xh = leapq.fp16(x)
+    for a, want in g["fp16"].items():
+        y = leapq.fp16(np.float32(xh) * np.float32(a))
+        assert abs(np.mean(y == xh) - want) <= g["tol"], a
+
+
+def test_windowed_run_tracks_exact_trajectory():
+    """With the window, compensators and smoothing, the read-outs stay close
+    to the exact fp64 recurrence on a 128-dim head with outlier channels."""
+    rng = np.random.default_rng(8)
+    T, N, d = 64, 2, 128
+    q, k, v, a, b = _inputs(rng, T, N, d)
+    S0 = 0.05 * rng.standard_normal((N, d, d))
+    S0[:, :, [5, 77]] *= 50
+    Q0 = rng.standard_normal((d, 4))
+    r = leapq.decode_run(q, k, v, a, b, S0, Q0)
+    o_ex, _ = gdn.gdn_recurrent(_tn(q), _tn(k), _tn(v), a.T, b.T, S0)
+    err = np.abs(r["o"] - _tn(o_ex)).max() / np.abs(o_ex).max()
+    assert err < 2e-2
+
+
+def test_error_ordering_trend_on_a_toy_head():
+    """Trend only (parity unpinned): on a toy head in the spirit of the page's
+    simulator, the relative state error orders as per-token INT8 > window >
+    window with compensator tokens and smoothing."""
+    rng = np.random.default_rng(9)
+    T, N, d = 512, 1, 32
+    k = rng.standard_normal((T, N, d))
+    k[..., :2] += 2.0
+    k[..., 2:6] *= 3.0
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    q = k[::-1].copy()
+    v = rng.standard_normal((T, N, d))
+    v[..., :2] += 4.0
+    a = np.full((T, N), 0.995)
+    b = rng.uniform(0.05, 0.15, (T, N))
+    S0 = np.zeros((N, d, d))
+    _, S_ex = gdn.gdn_recurrent(_tn(q), _tn(k), _tn(v), a.T, b.T, S0)
+
+    def final_dense(r):
+        return leapq.rebuild(r["st"], r["buf"])
+
+    e = {}
+    _, Zp, sp = leapq.per_step_int8(q, k, v, a, b, S0)
+    e["step"] = np.linalg.norm(sp[:, :, None] * Zp / 127.0 - S_ex) / np.linalg.norm(S_ex)
+    r = leapq.decode_run(q, k, v, a, b, S0, None, window=16, rank=0, smooth_mode=2)
+    e["window"] = np.linalg.norm(final_dense(r) - S_ex) / np.linalg.norm(S_ex)
+    r = leapq.decode_run(q, k, v, a, b, S0, rng.standard_normal((d, 4)), window=16, rank=4,
+                         smooth_mode=0)
+    e["full"] = np.linalg.norm(final_dense(r) - S_ex) / np.linalg.norm(S_ex)
+    assert e["step"] > e["window"] > e["full"], e
