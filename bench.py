@@ -1,0 +1,201 @@
+"""Benchmark of the gated delta-rule hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--rows decode,leapq,gla,gdn]
+
+Headline (`value`): Gated DeltaNet decode of one layer, 512 streams x 32 heads,
+d_k = d_v = 128, fp32 state resident in HBM, bf16 q/k/v; one step = one token for
+every stream (one gdn_decode_step launch over 16,384 heads); `value` is
+stream-tokens per second over K timed steps. The other rows of the hot path are
+measured in the same run and reported under "rows".
+
+Timing: W untimed warm-up steps, then K steps bracketed by synchronisation;
+HIP events recorded on the stream the kernels run on give the per-launch time.
+The CPU baseline times the fp64 oracle on a bounded sample of heads.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import delta_rule_recurrent_amd as m  # noqa: E402
+from delta_rule_recurrent_amd import synth  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+PEAK_BF16_TFLOPS = 2500.0      # dense bf16 MFMA, published
+D = 128
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def timed(fn, K, W):
+    """Run fn(i) W times untimed, then K times between events on the current
+    stream. Returns (ms per call, wall seconds)."""
+    for i in range(W):
+        fn(i)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(s)
+    for i in range(K):
+        fn(W + i)
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / K, time.perf_counter() - t0
+
+
+# ------------------------------------------------------------------- decode
+
+DECODE_B, DECODE_H = 512, 32
+
+
+def decode_bytes_per_head_step(io_bytes=2):
+    # fp32 state read + written, q/k/v in, o out, alpha/beta in
+    return 2 * D * D * 4 + 3 * D * io_bytes + D * io_bytes + 2 * 4
+
+
+def bench_decode(K, W, gen_steps=256):
+    B, H = DECODE_B, DECODE_H
+    N = B * H
+    log(f"[decode] generating B={B} H={H} steps={gen_steps}")
+    inp = synth.gdn_decode(B=B, H=H, steps=gen_steps, device="cuda")
+    S = inp["S0"].clone()
+    o = torch.empty((N, 1, D), dtype=torch.bfloat16, device="cuda")
+    q, k, v, a, b = (inp[n] for n in ("q", "k", "v", "alpha", "beta"))
+
+    def step(i):
+        t = i % gen_steps
+        m.gdn_decode_step(S, q[t, :, None], k[t, :, None], v[t, :, None],
+                          a[t, :, None], b[t, :, None], o)
+
+    ms, wall = timed(step, K, W)
+    bytes_launch = decode_bytes_per_head_step() * N
+    gbs = bytes_launch / (ms * 1e-3) / 1e9
+    return dict(workload=f"gdn_decode B={B} H={H} d_k=d_v=128 fp32 state, bf16 q/k/v, T=1 per launch",
+                ms_per_step=ms, tokens_per_s=B / (ms * 1e-3), head_steps=N,
+                bytes_per_launch=bytes_launch, achieved_gbs=gbs, frac_hbm=gbs / PEAK_HBM_GBS,
+                wall_s=wall), inp
+
+
+def cpu_baseline_decode(inp, target_s=10.0):
+    """The fp64 oracle recurrence on a bounded sample of heads (every 8th head of
+    the batch, slow and fast heads alike) over all generated steps, reported as
+    stream-tokens per second (head-steps per second / 32 heads). numpy's einsum
+    runs on one thread."""
+    from oracle import gdn
+    steps = inp["q"].shape[0]
+    H = DECODE_H
+    N = inp["q"].shape[1]
+
+    def run(heads, T):
+        sel = lambda x: x[:T, heads].transpose(0, 1).to("cpu", torch.float64).numpy()
+        args = [sel(inp[n]) for n in ("q", "k", "v", "alpha", "beta")]
+        S0 = inp["S0"][heads].to("cpu", torch.float64).numpy()
+        t0 = time.perf_counter()
+        gdn.gdn_recurrent(*args, S0)
+        return time.perf_counter() - t0
+
+    probe = torch.arange(0, N, 8)[:64]
+    per_head_step = run(probe, 16) / (len(probe) * 16)
+    n_heads = int(min(N // 8, max(64, target_s / max(per_head_step * steps, 1e-12))))
+    heads = torch.arange(0, N, 8)[:n_heads]
+    dt = run(heads, steps)
+    return dict(value=n_heads * steps / dt / H, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"{n_heads} heads (every 8th of 16,384) x {steps} decode steps of the "
+                       f"B=512 H=32 workload in {dt:.1f} s; stream-tokens/s = head-steps/s / 32")
+
+
+def counter_traffic(kernel):
+    """HBM bytes per launch measured by rocprofv3 counters (profiles/counters.json),
+    or None if the kernel's sources changed since they were taken."""
+    import hashlib
+    try:
+        with open(os.path.join(ROOT, "profiles", "counters.json")) as f:
+            rec = json.load(f)[kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    for path, want in rec["sources"].items():
+        with open(os.path.join(ROOT, path), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest()[:16] != want:
+                return None
+    return rec["traffic_bytes"]
+
+
+# ------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--rows", default="decode")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    m.lib()
+    rows = [r.strip() for r in args.rows.split(",") if r.strip()]
+    res, inp = bench_decode(args.steps, args.warmup)
+    log(f"[decode] {res['ms_per_step']*1e3:.1f} us/step  {res['achieved_gbs']:.0f} GB/s  "
+        f"{res['tokens_per_s']/1e6:.3f} M tok/s")
+    out_rows = {"decode": res}
+    if args.copy_probe:
+        # a plain copy of known size: 1 GiB read + 1 GiB written per launch
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[cpu] timing the oracle on a sample")
+        cpu = cpu_baseline_decode(inp)
+    del inp
+    line = {
+        "metric": "GDN decode tokens/s at B=512 (one layer, 32 heads, d=128)",
+        "value": res["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": res["workload"], "streams": DECODE_B, "heads": DECODE_H,
+                   "d_k": D, "d_v": D},
+        "roofline": {"bound": "hbm", "achieved": res["achieved_gbs"], "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": res["frac_hbm"],
+                     "traffic": counter_traffic("gdn_decode_kernel")},
+        "cpu_baseline": cpu,
+        "rows": out_rows,
+        "host": {"cpus": os.cpu_count(), "machine": platform.processor() or platform.machine(),
+                 "torch": torch.__version__, "hip": torch.version.hip},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

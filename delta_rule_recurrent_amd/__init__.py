@@ -1,0 +1,16 @@
+"""MI355X-native gated delta-rule recurrent state update.
+
+Five entry points over the gdnrt HIP library (C ABI in include/gdnrt.h):
+``gdn_decode_step``, ``gla_chunk_fwd``, ``gdn_chunk_fwd``, ``leapq_decode_step``
+and ``leapq_window_flush``. ``synth`` draws the seeded synthetic workloads.
+"""
+from .binding import (  # noqa: F401
+    GdnrtError,
+    LeapqBuffers,
+    gdn_chunk_fwd,
+    gdn_decode_step,
+    gla_chunk_fwd,
+    leapq_decode_step,
+    leapq_window_flush,
+    lib,
+)

@@ -1,0 +1,233 @@
+"""Thin Python binding of the gdnrt C ABI (include/gdnrt.h).
+
+Argument marshalling only: every step of the computation runs in the HIP kernels
+of ``libgdnrt.so``. torch supplies device memory and the current stream. If the
+library has not been built, or no GPU is visible, calls raise; there is no CPU
+fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgdnrt.so")
+
+OK, EINVAL, ESHAPE, EALIGN, EDTYPE, ESTATE, ELAUNCH = range(7)
+F32, BF16 = 0, 1
+D = 128
+CHUNK = 64
+
+_c_int, _vp, _fp = ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p
+
+
+class LeapqState(ctypes.Structure):
+    """Mirror of ``leapq_state`` (device pointers + sizes)."""
+    _fields_ = [("codes", _vp), ("vscale", _vp), ("ksmooth", _vp), ("ct_k", _vp),
+                ("ct_u", _vp), ("buf_k", _vp), ("buf_u", _vp), ("buf_a", _vp),
+                ("N", _c_int), ("dk", _c_int), ("dv", _c_int), ("rank", _c_int),
+                ("window", _c_int)]
+
+
+# exported symbol -> (argtypes, restype); mirrors include/gdnrt.h
+SIGNATURES = {
+    "gdn_decode_step": ([_vp] * 7 + [_c_int] * 5 + [_vp], _c_int),
+    "gla_chunk_fwd": ([_vp] * 7 + [_c_int] * 6 + [_vp], _c_int),
+    "gdn_chunk_fwd": ([_vp] * 8 + [_c_int] * 6 + [_vp], _c_int),
+    "leapq_decode_step": ([ctypes.POINTER(LeapqState), _c_int] + [_vp] * 6 + [_c_int, _vp], _c_int),
+    "leapq_window_flush": ([ctypes.POINTER(LeapqState), _c_int, _vp, _vp, _c_int, _c_int, _vp, _vp],
+                           _c_int),
+    "gdnrt_last_error": ([], ctypes.c_char_p),
+}
+
+_LIB = None
+
+
+class GdnrtError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+def lib():
+    """Load libgdnrt.so (built in-tree) and declare every exported signature."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m delta_rule_recurrent_amd.build` "
+                "(the HIP library is required; there is no fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (argt, rest) in SIGNATURES.items():
+            f = getattr(L, name, None)
+            if f is None:
+                continue
+            f.argtypes = argt
+            f.restype = rest
+        _LIB = L
+    return _LIB
+
+
+def _check(fn, status):
+    if status != OK:
+        raise GdnrtError(fn, status, lib().gdnrt_last_error().decode())
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t, name, dtype=None, shape=None, device=True):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _io(dtype):
+    if dtype == torch.float32:
+        return F32
+    if dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"q/k/v must be float32 or bfloat16, got {dtype}")
+
+
+# ---------------------------------------------------------------- entry points
+
+def gdn_decode_step(S, q, k, v, alpha, beta, o=None):
+    """Gated DeltaNet recurrent step(s), state updated in place.
+
+    S [N][128][128] fp32; q, k, v [N][T][128] (fp32 or bf16, one dtype);
+    alpha, beta [N][T] fp32. Returns o [N][T][128] in the dtype of q."""
+    N, T, _ = q.shape
+    io = _io(q.dtype)
+    _need(S, "S", torch.float32, (N, D, D))
+    for n_, t_ in (("q", q), ("k", k), ("v", v)):
+        _need(t_, n_, q.dtype, (N, T, D))
+    _need(alpha, "alpha", torch.float32, (N, T))
+    _need(beta, "beta", torch.float32, (N, T))
+    if o is None:
+        o = torch.empty((N, T, D), dtype=q.dtype, device=q.device)
+    _need(o, "o", q.dtype, (N, T, D))
+    _check("gdn_decode_step", lib().gdn_decode_step(
+        _ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(o),
+        N, T, D, D, io, _stream()))
+    return o
+
+
+def gla_chunk_fwd(q, k, v, log_g, S0=None, ST=None, o=None, chunk=CHUNK):
+    """Gated linear attention chunkwise forward from an incoming state.
+
+    q, k, v [N][T][128] bf16; log_g [N][T][128] fp32; S0 [N][128][128] fp32 or
+    None. Returns (o [N][T][128] bf16, ST [N][128][128] fp32)."""
+    N, T, _ = q.shape
+    for n_, t_ in (("q", q), ("k", k), ("v", v)):
+        _need(t_, n_, torch.bfloat16, (N, T, D))
+    _need(log_g, "log_g", torch.float32, (N, T, D))
+    if S0 is not None:
+        _need(S0, "S0", torch.float32, (N, D, D))
+    if ST is None:
+        ST = torch.empty((N, D, D), dtype=torch.float32, device=q.device)
+    _need(ST, "ST", torch.float32, (N, D, D))
+    if o is None:
+        o = torch.empty((N, T, D), dtype=torch.bfloat16, device=q.device)
+    _need(o, "o", torch.bfloat16, (N, T, D))
+    _check("gla_chunk_fwd", lib().gla_chunk_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(S0), _ptr(ST), _ptr(o),
+        N, T, D, D, chunk, BF16, _stream()))
+    return o, ST
+
+
+def gdn_chunk_fwd(q, k, v, alpha, beta, S0=None, ST=None, o=None, chunk=CHUNK):
+    """Gated DeltaNet chunkwise forward (prefill).
+
+    q, k, v [N][T][128] bf16; alpha, beta [N][T] fp32; S0 [N][128][128] fp32 or
+    None. Returns (o [N][T][128] bf16, ST [N][128][128] fp32)."""
+    N, T, _ = q.shape
+    for n_, t_ in (("q", q), ("k", k), ("v", v)):
+        _need(t_, n_, torch.bfloat16, (N, T, D))
+    _need(alpha, "alpha", torch.float32, (N, T))
+    _need(beta, "beta", torch.float32, (N, T))
+    if S0 is not None:
+        _need(S0, "S0", torch.float32, (N, D, D))
+    if ST is None:
+        ST = torch.empty((N, D, D), dtype=torch.float32, device=q.device)
+    _need(ST, "ST", torch.float32, (N, D, D))
+    if o is None:
+        o = torch.empty((N, T, D), dtype=torch.bfloat16, device=q.device)
+    _need(o, "o", torch.bfloat16, (N, T, D))
+    _check("gdn_chunk_fwd", lib().gdn_chunk_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(ST), _ptr(o),
+        N, T, D, D, chunk, BF16, _stream()))
+    return o, ST
+
+
+class LeapqBuffers:
+    """Caller-owned device memory of a LeapQuant state for N heads (see
+    ``leapq_state`` in include/gdnrt.h). Allocated once by torch."""
+
+    def __init__(self, N, rank=4, window=16, device="cuda"):
+        self.N, self.rank, self.window = N, rank, window
+        f = dict(dtype=torch.float32, device=device)
+        self.codes = torch.zeros((N, D, D), dtype=torch.int8, device=device)
+        self.vscale = torch.zeros((N, D), **f)
+        self.ksmooth = torch.ones((N, D), **f)
+        # fp16 bit patterns; view as torch.float16 for reading
+        self.ct_k = torch.zeros((N, max(rank, 1), D), dtype=torch.float16, device=device)
+        self.ct_u = torch.zeros((N, max(rank, 1), D), dtype=torch.float16, device=device)
+        self.buf_k = torch.zeros((N, window, D), **f)
+        self.buf_u = torch.zeros((N, window, D), **f)
+        self.buf_a = torch.zeros((N, window), **f)
+        self.pos = 0
+        self._st = LeapqState(
+            _ptr(self.codes), _ptr(self.vscale), _ptr(self.ksmooth), _ptr(self.ct_k),
+            _ptr(self.ct_u), _ptr(self.buf_k), _ptr(self.buf_u), _ptr(self.buf_a),
+            N, D, D, rank, window)
+
+    @property
+    def struct(self):
+        return self._st
+
+
+def leapq_window_flush(st: LeapqBuffers, q0, dense=None, iters=1, smooth_mode=0, pre_round=None):
+    """Rebuild (or take ``dense``), fit compensator tokens, smooth, round once.
+    Resets the window position to 0."""
+    _need(q0, "q0", torch.float32, (D, st.rank) if st.rank > 0 else None)
+    if dense is not None:
+        _need(dense, "dense", torch.float32, (st.N, D, D))
+    if pre_round is not None:
+        _need(pre_round, "pre_round", torch.float32, (st.N, D, D))
+    _check("leapq_window_flush", lib().leapq_window_flush(
+        ctypes.byref(st.struct), st.pos, _ptr(dense), _ptr(q0), iters, smooth_mode,
+        _ptr(pre_round), _stream()))
+    st.pos = 0
+
+
+def leapq_decode_step(st: LeapqBuffers, q, k, v, alpha, beta, o=None):
+    """One token per head inside the open window; appends its record."""
+    N = st.N
+    io = _io(q.dtype)
+    for n_, t_ in (("q", q), ("k", k), ("v", v)):
+        _need(t_, n_, q.dtype, (N, D))
+    _need(alpha, "alpha", torch.float32, (N,))
+    _need(beta, "beta", torch.float32, (N,))
+    if o is None:
+        o = torch.empty((N, D), dtype=q.dtype, device=q.device)
+    _need(o, "o", q.dtype, (N, D))
+    _check("leapq_decode_step", lib().leapq_decode_step(
+        ctypes.byref(st.struct), st.pos, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+        _ptr(o), io, _stream()))
+    st.pos += 1
+    return o

@@ -1,0 +1,55 @@
+"""Build the gdnrt HIP library in-tree for gfx950 (``libgdnrt.so`` next to this file).
+
+    python -m delta_rule_recurrent_amd.build
+
+hipcc cross-compiles for gfx950 without a GPU. Packed fp32 VALU instructions are
+disabled for every device compilation.
+"""
+from __future__ import annotations
+
+import glob
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+LIB = os.path.join(HERE, "libgdnrt.so")
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found (ROCm is required to build the gdnrt library)")
+
+
+def sources():
+    src = sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
+    src += sorted(glob.glob(os.path.join(HERE, "csrc", "*.cpp")))
+    return src
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source into libgdnrt.so (always recompiles)."""
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
+           "-fvisibility=hidden", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-I", os.path.join(ROOT, "include"), "-o", tmp] + sources()
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, cwd=ROOT, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
+    if err.strip() and verbose:
+        print(err, file=sys.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

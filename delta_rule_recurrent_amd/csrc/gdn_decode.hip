@@ -1,0 +1,103 @@
+// Gated DeltaNet recurrent step (decode), fp32 state streamed through HBM.
+//
+// Method: "LeapQuant: an 8-bit recurrent state that stops rounding every token",
+// section "The state, from the update rule up" (delta rule with a scalar decay,
+// eq. 3's correction form) and section "Why a decode step is a memory copy". In the
+// [d_v][d_k] layout the update S_t = a S (I - b k k^T) + b v k^T splits by rows:
+// row i needs only its own dot products with k and q,
+//
+//     u_i = b (v_i - a S_i.k),   o_i = a S_i.q + u_i (k.q),   S_i <- a S_i + u_i k,
+//
+// so one read and one write of each 512-byte row per token is the whole traffic;
+// o uses the pre-update row and k.q instead of a second pass over the new row.
+//
+// Mapping: a 256-thread block (four 64-lane waves) owns 8 rows of one head, so a
+// head is 16 blocks. Each row is held by 32 lanes, four consecutive floats per
+// lane: one 16-byte load per lane covers two whole rows, a perfectly coalesced
+// 1 KiB per wave instruction. The state is touched once per step and does not fit
+// in any cache, so it is read and written with non-temporal hints. Measured on
+// MI355X, many small blocks holding one float4 per lane beat fewer blocks that
+// keep more rows in flight per wave (and beat a plain copy kernel), which is why
+// the block is this small. Row sums use DPP inside 16-lane rows plus one swizzle
+// across the two halves of a 32-lane group.
+#include "common.hpp"
+
+namespace gdnrt {
+
+template <typename IO>
+__global__ __launch_bounds__(256) void gdn_decode_kernel(
+    float* __restrict__ S, const IO* __restrict__ q, const IO* __restrict__ k,
+    const IO* __restrict__ v, const float* __restrict__ alpha, const float* __restrict__ beta,
+    IO* __restrict__ o, int T) {
+  constexpr int kRowsPerBlock = 8;
+  constexpr int BPH = kD / kRowsPerBlock;   // blocks per head
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int head = blockIdx.x / BPH;
+  const int row = (blockIdx.x % BPH) * kRowsPerBlock + wave * 2 + (lane >> 5);
+  const int col = (lane & 31) * 4;      // first key column of this lane
+
+  f32x4* Sp = reinterpret_cast<f32x4*>(S + (size_t)head * kD * kD + (size_t)row * kD + col);
+  f32x4 s = __builtin_nontemporal_load(Sp);
+
+  for (int t = 0; t < T; ++t) {
+    const size_t tok = (size_t)head * T + t;
+    const f32x4 k4 = io_traits<IO>::ld4(k, tok * kD + col);
+    const f32x4 q4 = io_traits<IO>::ld4(q, tok * kD + col);
+    const float a = alpha[tok];
+    const float b = beta[tok];
+    const float vi = io_traits<IO>::ld(v, tok * kD + row);
+    const float kq = sum32(k4.x * q4.x + k4.y * q4.y + k4.z * q4.z + k4.w * q4.w);
+    const float pk = sum32(s.x * k4.x + s.y * k4.y + s.z * k4.z + s.w * k4.w);
+    const float pq = sum32(s.x * q4.x + s.y * q4.y + s.z * q4.z + s.w * q4.w);
+    const float u = b * (vi - a * pk);
+    const float oi = a * pq + u * kq;
+    s = a * s + u * k4;
+    if ((lane & 31) == 0) io_traits<IO>::st(o, tok * kD + row, oi);
+  }
+  __builtin_nontemporal_store(s, Sp);
+}
+
+template <typename IO>
+static void launch_decode(float* S, const void* q, const void* k, const void* v,
+                          const float* alpha, const float* beta, void* o, int N, int T,
+                          hipStream_t stream) {
+  hipLaunchKernelGGL((gdn_decode_kernel<IO>), dim3(N * (kD / 8)), dim3(256), 0, stream, S,
+                     static_cast<const IO*>(q), static_cast<const IO*>(k),
+                     static_cast<const IO*>(v), alpha, beta, static_cast<IO*>(o), T);
+}
+
+}  // namespace gdnrt
+
+using namespace gdnrt;
+
+extern "C" int gdn_decode_step(float* S, const void* q, const void* k, const void* v,
+                               const float* alpha, const float* beta, void* o, int N, int T,
+                               int dk, int dv, int io, void* stream) {
+  if (N < 0 || T < 0) return set_error(GDNRT_ESHAPE, "gdn_decode_step: N=%d T=%d must be >= 0", N, T);
+  if (dk != kD || dv != kD)
+    return set_error(GDNRT_ESHAPE, "gdn_decode_step: d_k=%d d_v=%d, only 128 is supported", dk, dv);
+  if (io != GDNRT_F32 && io != GDNRT_BF16) return set_error(GDNRT_EDTYPE, "gdn_decode_step: io=%d", io);
+  if (N == 0 || T == 0) return clear_error();
+  if (!S || !q || !k || !v || !alpha || !beta || !o)
+    return set_error(GDNRT_EINVAL, "gdn_decode_step: null pointer argument");
+  if ((size_t)N * (kD / 8) > 0x7fffffffu || (size_t)N * (size_t)T > ((size_t)1 << 36))
+    return set_error(GDNRT_ESHAPE, "gdn_decode_step: N=%d T=%d too large", N, T);
+  if (!aligned16(S) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      !aligned4(alpha) || !aligned4(beta))
+    return set_error(GDNRT_EALIGN, "gdn_decode_step: S, q, k, v, o must be 16-byte aligned, gates 4-byte");
+  const size_t es = io == GDNRT_F32 ? 4 : 2;
+  const size_t ntok = (size_t)N * T;
+  const size_t nS = (size_t)N * kD * kD * 4, nIO = ntok * kD * es, nG = ntok * 4;
+  if (overlaps(o, nIO, S, nS) || overlaps(o, nIO, q, nIO) || overlaps(o, nIO, k, nIO) ||
+      overlaps(o, nIO, v, nIO) || overlaps(o, nIO, alpha, nG) || overlaps(o, nIO, beta, nG) ||
+      overlaps(S, nS, q, nIO) || overlaps(S, nS, k, nIO) || overlaps(S, nS, v, nIO) ||
+      overlaps(S, nS, alpha, nG) || overlaps(S, nS, beta, nG))
+    return set_error(GDNRT_EINVAL, "gdn_decode_step: S or o overlaps another buffer");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (io == GDNRT_F32)
+    launch_decode<float>(S, q, k, v, alpha, beta, o, N, T, s);
+  else
+    launch_decode<uint16_t>(S, q, k, v, alpha, beta, o, N, T, s);
+  return check_launch("gdn_decode_step");
+}

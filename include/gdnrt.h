@@ -1,0 +1,187 @@
+/*
+ * gdnrt -- gated delta-rule recurrent state update on AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels. Every pointer argument is device memory
+ * owned by the caller (except the leapq_state struct itself, which is read on the
+ * host during the call). The library allocates no device memory and keeps no
+ * state between calls. Work is enqueued on `stream` (a hipStream_t; NULL means the
+ * null stream) and is complete when that stream is synchronised.
+ *
+ * Orientation: every recurrent state is stored [d_v][d_k] row-major fp32: one row
+ * per value channel, contiguous along the key channels. The pages that define the
+ * method write d_k x d_v; their formulas apply transposed.
+ *
+ * Errors: arguments are validated on the host before anything is launched; on a
+ * failed check nothing is launched and a gdnrt_status is returned. Nothing throws
+ * across the ABI and no call aborts. gdnrt_last_error() returns a message for
+ * the calling thread's last non-OK status.
+ *
+ * Shapes supported by this build: d_k = d_v = 128, chunk = 64, window <= 16,
+ * rank <= 8. Anything else returns GDNRT_ESHAPE. Empty work (N == 0 or T == 0)
+ * returns GDNRT_OK and launches nothing.
+ *
+ * Precision: accumulation is fp32. Inputs q, k, v and the output o have the dtype
+ * `io` (GDNRT_F32 or GDNRT_BF16); gates and states are fp32. q and k are used as
+ * given: the library does not normalise them and applies no 1/sqrt(d) scale.
+ */
+#ifndef GDNRT_H
+#define GDNRT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define GDNRT_API __attribute__((visibility("default")))
+#else
+#define GDNRT_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDNRT_OK = 0,
+  GDNRT_EINVAL = 1,  /* null pointer, bad enum, overlapping buffers            */
+  GDNRT_ESHAPE = 2,  /* unsupported or negative size                           */
+  GDNRT_EALIGN = 3,  /* a pointer is not 16-byte aligned                       */
+  GDNRT_EDTYPE = 4,  /* io is not GDNRT_F32 / GDNRT_BF16                       */
+  GDNRT_ESTATE = 5,  /* window position out of range                           */
+  GDNRT_ELAUNCH = 6  /* the HIP runtime reported an error at launch            */
+} gdnrt_status;
+
+typedef enum { GDNRT_F32 = 0, GDNRT_BF16 = 1 } gdnrt_dtype;
+
+/*
+ * Gated DeltaNet recurrent step ("LeapQuant: an 8-bit recurrent state that stops
+ * rounding every token", section "The state, from the update rule up": the delta
+ * rule with a scalar per-token decay; section "Why a decode step is a memory
+ * copy"). For each of N independent heads and each of T consecutive tokens:
+ *
+ *     S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *     o_t = S_t q_t.
+ *
+ *   S      [N][dv][dk] fp32, read and updated in place (initial -> final state).
+ *   q, k   [N][T][dk]  io dtype.       v, o  [N][T][dv] io dtype.
+ *   alpha, beta [N][T] fp32.
+ * o must not overlap any input. Decode is T = 1 per call; T > 1 runs the tokens
+ * back to back with the state held on chip.
+ */
+GDNRT_API int gdn_decode_step(float* S, const void* q, const void* k, const void* v,
+                    const float* alpha, const float* beta, void* o,
+                    int N, int T, int dk, int dv, int io, void* stream);
+
+/*
+ * Gated linear attention, chunkwise forward of one sequence shard that starts
+ * from an incoming state ("ZeCO: Zero Communication Overhead Sequence Parallelism
+ * for Linear Attention", section "Gated Linear Attention (GLA) Formulation" for
+ * the per-token and chunk forms, section "Global State Update Formula", eq. 6, for
+ * the incoming state). Per token, with per-key-channel log-gates g_t:
+ *
+ *     S_t[v,k] = exp(g_t[k]) S_{t-1}[v,k] + v_t[v] k_t[k],   o_t = S_t q_t.
+ *
+ *   q, k   [N][T][dk] bf16.   v, o [N][T][dv] bf16.   log_g [N][T][dk] fp32 (<= 0).
+ *   S0     [N][dv][dk] fp32 incoming state, or NULL for zero.
+ *   ST     [N][dv][dk] fp32 final state (may equal S0: read before written).
+ * T must be a multiple of chunk (64).
+ */
+GDNRT_API int gla_chunk_fwd(const void* q, const void* k, const void* v, const float* log_g,
+                  const float* S0, float* ST, void* o,
+                  int N, int T, int dk, int dv, int chunk, int io, void* stream);
+
+/*
+ * Gated DeltaNet chunkwise forward (prefill): the same recurrence as
+ * gdn_decode_step over T tokens, computed per chunk of 64 tokens through the
+ * UT / WY form of the intra-chunk delta rule (derived from eq. 3 of the LeapQuant
+ * page's section "The state, from the update rule up" by unrolling within a
+ * chunk; the pages print no chunk form for the delta rule).
+ *
+ *   q, k [N][T][dk] bf16 (q, k as given).   v, o [N][T][dv] bf16.
+ *   alpha, beta [N][T] fp32.   S0 [N][dv][dk] fp32 or NULL (zero).
+ *   ST [N][dv][dk] fp32 final state (may equal S0).
+ * T must be a multiple of chunk (64).
+ */
+GDNRT_API int gdn_chunk_fwd(const void* q, const void* k, const void* v,
+                  const float* alpha, const float* beta,
+                  const float* S0, float* ST, void* o,
+                  int N, int T, int dk, int dv, int chunk, int io, void* stream);
+
+/*
+ * LeapQuant windowed 8-bit state ("LeapQuant: an 8-bit recurrent state that stops
+ * rounding every token": section "Fix one: leap over a window" eq. 4 and eq. 10,
+ * section "Fix two: pull the outliers out as tokens" eq. 5, section "Fix three:
+ * smooth what is left" eq. 7, layout from section "What 1.19 bytes buys").
+ * A host struct of caller-owned device pointers, per head n of N:
+ *
+ *   codes   [N][dv][dk] int8   residual codes Z in [-127, 127]
+ *   vscale  [N][dv]     fp32   one scale per value channel (row): its largest
+ *                              smoothed residual magnitude
+ *   ksmooth [N][dk]     fp32   one smoothing factor per key channel (column)
+ *   ct_k    [N][rank][dk] fp16 compensator-token keys (unit norm before rounding)
+ *   ct_u    [N][rank][dv] fp16 compensator-token values
+ *   buf_k   [N][window][dk] fp32, buf_u [N][window][dv] fp32, buf_a [N][window] fp32:
+ *                              the open window's records (k_t, u_t, alpha_t)
+ *
+ * The stored state is S_hat[v,k] = vscale[v] * codes[v,k] / 127 * ksmooth[k]
+ *                                   + sum_r ct_u[r][v] ct_k[r][k].
+ * The compensator tokens enter the window ahead of the real tokens with decay 1,
+ * so they decay together with the residual.
+ */
+typedef struct {
+  int8_t* codes;
+  float* vscale;
+  float* ksmooth;
+  uint16_t* ct_k;
+  uint16_t* ct_u;
+  float* buf_k;
+  float* buf_u;
+  float* buf_a;
+  int N, dk, dv, rank, window;
+} leapq_state;
+
+/*
+ * One decode token per head inside a window. `pos` real tokens (0 <= pos < window)
+ * are already buffered. Reads the stored state and the buffer, and with
+ * x -> S_pos x evaluated by eq. 10,
+ *
+ *     u_t = beta_t (v_t - alpha_t S_pos k_t),   o_t = alpha_t S_pos q_t + u_t (k_t . q_t),
+ *
+ * then appends (k_t, u_t, alpha_t) at buffer slot pos. Writes no state.
+ *   q, k [N][dk], v, o [N][dv] io dtype; alpha, beta [N] fp32.
+ * pos outside [0, window) returns GDNRT_ESTATE.
+ */
+GDNRT_API int leapq_decode_step(const leapq_state* st, int pos,
+                      const void* q, const void* k, const void* v,
+                      const float* alpha, const float* beta, void* o,
+                      int io, void* stream);
+
+/*
+ * Window flush: rebuild the dense state S_pos (eq. 4) from the stored state and
+ * the first `pos` buffered records -- or take `dense` ([N][dv][dk] fp32) instead
+ * when it is not NULL, to encode an initial state -- then
+ *   1. fit `rank` compensator tokens: `iters` rounds of Q <- orth(S^T (S Q)) from
+ *      the start block q0 ([dk][rank] fp32, device), each orthonormalised by two
+ *      CholeskyQR passes whose Gram matrix is shifted by 1e-6 * trace + 1e-30;
+ *      ct_k = fp16(Q^T), ct_u = fp16((S Q)^T) (round to nearest even);
+ *   2. R = S - sum_r ct_u[r] ct_k[r]^T (the rounded pieces);
+ *   3. smoothing per key channel k: smooth_mode 0: sqrt(mean_v |R[v,k]|),
+ *      1: sqrt(mean_v R[v,k]^2), 2: none (1); clamped below at 1e-12;
+ *   4. vscale[v] = max_k |R[v,k] / ksmooth[k]|;
+ *   5. x = (R[v,k] / ksmooth[k]) * (127 / vscale[v]) in fp32 (0 when vscale is 0),
+ *      codes = clamp(rint(x), -127, 127), round half to even.
+ * The stored state is overwritten; the buffer is then empty (next pos = 0).
+ * pre_round, when not NULL ([N][dv][dk] fp32), receives x.
+ * pos outside [0, window] returns GDNRT_ESTATE.
+ */
+GDNRT_API int leapq_window_flush(const leapq_state* st, int pos, const float* dense,
+                       const float* q0, int iters, int smooth_mode,
+                       float* pre_round, void* stream);
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+GDNRT_API const char* gdnrt_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDNRT_H */
