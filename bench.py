@@ -117,6 +117,65 @@ def cpu_baseline_decode(inp, target_s=10.0):
                        f"B=512 H=32 workload in {dt:.1f} s; stream-tokens/s = head-steps/s / 32")
 
 
+# ------------------------------------------------------------------- LeapQuant
+
+def leapq_bytes_per_head_window(W=16, rank=4):
+    """Algorithmic bytes of one head over one window (W decode steps + flush).
+    Step at position m reads codes 16,384 + scales 1,024 + compensators 4*r*128
+    + m buffered records (k, u fp32 and a) + q, k, v (bf16) and alpha, beta; it
+    writes one record and o (bf16). The flush reads the stored state and the W
+    records and writes the stored state."""
+    stored = D * D + 2 * D * 4 + rank * 2 * D * 2          # 19,456 at r = 4
+    rec = 2 * D * 4 + 4                                   # 1,028
+    io_in, io_out = 3 * D * 2 + 2 * 4, D * 2
+    steps = sum(stored + m * rec + io_in + rec + io_out for m in range(W))
+    flush = stored + W * rec + stored
+    return steps + flush
+
+
+def bench_leapq(tokens=4096, B=DECODE_B, H=DECODE_H, W=16, rank=4):
+    N = B * H
+    log(f"[leapq] generating B={B} H={H} steps={tokens}")
+    inp = synth.leapq_decode(B=B, H=H, steps=tokens, device="cuda")
+    st = m.LeapqBuffers(N, rank=rank, window=W)
+    Q0 = inp["Q0"].cuda()
+    q, k, v, a, b = (inp[n] for n in ("q", "k", "v", "alpha", "beta"))
+    o = torch.empty((N, D), dtype=torch.bfloat16, device="cuda")
+
+    def run_window(w):
+        for j in range(W):
+            t = (w * W + j) % tokens
+            m.leapq_decode_step(st, q[t], k[t], v[t], a[t], b[t], o)
+        m.leapq_window_flush(st, Q0)
+
+    m.leapq_window_flush(st, Q0, dense=inp["S0"])      # encode the initial state
+    n_win = tokens // W
+    ms_win, wall = timed(run_window, n_win, 1)
+    ms_step = ms_win / W
+    bpw = leapq_bytes_per_head_window(W, rank) * N
+    # per-kernel split from events around each launch of one window
+    s = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(W + 2)]
+    ev[0].record(s)
+    for j in range(W):
+        m.leapq_decode_step(st, q[j], k[j], v[j], a[j], b[j], o)
+        ev[j + 1].record(s)
+    m.leapq_window_flush(st, Q0)
+    ev[W + 1].record(s)
+    torch.cuda.synchronize()
+    dec_ms = ev[0].elapsed_time(ev[W]) / W
+    flush_ms = ev[W].elapsed_time(ev[W + 1])
+    res = dict(workload=f"leapq_decode B={B} H={H} d=128, INT8 residual + fp32 scales + {rank} fp16 "
+                        f"compensators, {W}-token fp32 buffer, {tokens} tokens",
+               ms_per_step=ms_step, tokens_per_s=B / (ms_step * 1e-3),
+               bytes_per_head_step=bpw / N / W, achieved_gbs=bpw / (ms_win * 1e-3) / 1e9,
+               decode_kernel_ms=dec_ms, flush_kernel_ms=flush_ms, wall_s=wall,
+               decode_kernel_gbs=None)
+    res["frac_hbm"] = res["achieved_gbs"] / PEAK_HBM_GBS
+    del inp
+    return res
+
+
 def counter_traffic(kernel):
     """HBM bytes per launch measured by rocprofv3 counters (profiles/counters.json),
     or None if the kernel's sources changed since they were taken."""
@@ -140,7 +199,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--rows", default="decode")
+    ap.add_argument("--rows", default="decode,leapq")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -171,6 +230,15 @@ def main():
         log("[cpu] timing the oracle on a sample")
         cpu = cpu_baseline_decode(inp)
     del inp
+    torch.cuda.empty_cache()
+    if "leapq" in rows:
+        r = bench_leapq()
+        r["speedup_vs_fp32_decode"] = res["ms_per_step"] / r["ms_per_step"]
+        out_rows["leapq"] = r
+        log(f"[leapq] {r['ms_per_step']*1e3:.1f} us/step ({r['decode_kernel_ms']*1e3:.1f} us decode "
+            f"+ {r['flush_kernel_ms']*1e3:.1f} us flush per window)  {r['achieved_gbs']:.0f} GB/s  "
+            f"{r['tokens_per_s']/1e6:.3f} M tok/s  {r['speedup_vs_fp32_decode']:.2f}x fp32 decode")
+        torch.cuda.empty_cache()
     line = {
         "metric": "GDN decode tokens/s at B=512 (one layer, 32 heads, d=128)",
         "value": res["tokens_per_s"],

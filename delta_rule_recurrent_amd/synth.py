@@ -91,6 +91,24 @@ def gdn_prefill(B=1, H=32, T=16384, d=D, device="cpu", seed=1002, S0_std=0.0):
     return dict(q=q, k=k, v=v, alpha=alpha, beta=beta, S0=S0)
 
 
+CHUNK_STEPS = 256
+
+
+def _decode_tokens(steps, N, d, g, device, io):
+    """q, k (L2-normalised) and v for ``steps`` decode steps, drawn in chunks of
+    256 steps (q chunks, then k chunks, then v chunks) so that long runs need no
+    full-size fp32 temporaries."""
+    out = []
+    for norm in (True, True, False):
+        x = torch.empty((steps, N, d), dtype=io, device=device)
+        for s0 in range(0, steps, CHUNK_STEPS):
+            s1 = min(steps, s0 + CHUNK_STEPS)
+            c = _randn((s1 - s0, N, d), g, device)
+            x[s0:s1] = (_l2n(c) if norm else c).to(io)
+        out.append(x)
+    return out
+
+
 def _decode_gates(steps, B, H, g, device):
     """Heads h < H/2 are slow heads with alpha = 0.999 on every token; the
     rest draw alpha = sigmoid(N(2,1)) per (stream, token)."""
@@ -106,9 +124,7 @@ def gdn_decode(B=512, H=32, steps=256, d=D, device="cpu", seed=1003, io=torch.bf
     N(0, 0.05) resident on the device, one token per stream per step."""
     g = _gen(device, seed)
     N = B * H
-    q = _l2n(_randn((steps, N, d), g, device)).to(io)
-    k = _l2n(_randn((steps, N, d), g, device)).to(io)
-    v = _randn((steps, N, d), g, device).to(io)
+    q, k, v = _decode_tokens(steps, N, d, g, device, io)
     alpha = _decode_gates(steps, B, H, g, device)
     beta = torch.sigmoid(_randn((steps, N), g, device, 0.0, 1.0))
     S0 = _randn((N, d, d), g, device, 0.0, 0.05)
@@ -123,9 +139,7 @@ def leapq_decode(B=512, H=32, steps=4096, d=D, device="cpu", seed=1004,
     ``Q0`` ([d_k][4], N(0,1), its own seed) of the compensator fit."""
     g = _gen(device, seed)
     N = B * H
-    q = _l2n(_randn((steps, N, d), g, device)).to(torch.bfloat16)
-    k = _l2n(_randn((steps, N, d), g, device)).to(torch.bfloat16)
-    v = _randn((steps, N, d), g, device).to(torch.bfloat16)
+    q, k, v = _decode_tokens(steps, N, d, g, device, torch.bfloat16)
     alpha = _decode_gates(steps, B, H, g, device)
     beta = torch.sigmoid(_randn((steps, N), g, device, 0.0, 1.0))
     S0 = _randn((N, d, d), g, device, 0.0, 0.05)

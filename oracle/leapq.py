@@ -137,6 +137,16 @@ def flush(S, Q0=None, rank=4, iters=1, smooth_mode=0, svd=False):
         kt = np.zeros((N, 0, dk))
         ut = np.zeros((N, 0, dv))
         R = S
+    out = encode_residual(R, smooth_mode)
+    out.update(kt=kt, ut=ut)
+    return out
+
+
+def encode_residual(R, smooth_mode=0):
+    """Smooth and round a residual R ([N][d_v][d_k]) once: returns dict(Z, s, c,
+    pre) -- codes, value-channel scales, key-channel smoothing factors (fp32) and
+    the fp32 pre-rounding values."""
+    R = np.asarray(R, np.float64)
     c = fp32(smoothing(R, smooth_mode))                        # [N][dk]
     Rc = R / c[:, None, :]
     s = fp32(np.max(np.abs(Rc), axis=-1))                      # [N][dv]
@@ -144,7 +154,7 @@ def flush(S, Q0=None, rank=4, iters=1, smooth_mode=0, svd=False):
         pre = np.where(s[:, :, None] > 0, Rc * (127.0 / s[:, :, None]), 0.0)
     pre = pre.astype(np.float32)
     Z = round_codes(pre)
-    return dict(Z=Z, s=s, c=c, kt=kt, ut=ut, pre=pre)
+    return dict(Z=Z, s=s, c=c, pre=pre)
 
 
 def dequant(st):
