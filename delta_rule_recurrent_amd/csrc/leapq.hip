@@ -29,12 +29,14 @@ __device__ __forceinline__ float sb(uint32_t w, int b) { return (float)((int32_t
 //   S_m x = G0 [ vscale * (Z (ksmooth o x)) / 127 + sum_r uc_r (kc_r . x) ]
 //         + sum_j G_j u_j (k_j . x),   G0 = prod_{i<m} a_i,  G_j = prod_{j<i<m} a_i.
 // The token then gives u = b (v - a S_m k), o = a S_m q + u (k . q), and its record
-// is appended at slot m. A block owns 32 value rows of one head (4 blocks per
-// head): 8 lanes per 128-byte code row, one 16-byte load each; per-head dot
-// products with the buffered and compensator keys are formed by 16-lane groups.
-
-constexpr int kLqRows = 32;   // value rows per decode block
-constexpr int kLqBPH = kD / kLqRows;
+// is appended at slot m.
+//
+// One 256-thread block per head; thread (row = tid/2, half = tid%2) owns 64 codes
+// of one value row. Every global load that does not depend on another (codes,
+// this row's buffered corrections and compensator values, the key vectors of the
+// dot products) is issued before the first barrier, so a block waits for memory
+// once. 16-lane groups form the per-head dot products of q and k with the
+// compensator keys, the buffered keys and k itself.
 
 template <typename IO>
 __global__ __launch_bounds__(256) void leapq_decode_kernel(
@@ -44,70 +46,93 @@ __global__ __launch_bounds__(256) void leapq_decode_kernel(
     float* __restrict__ buf_a, int rank, int window, int m,
     const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, IO* __restrict__ o) {
-  __shared__ float s_k[kD], s_q[kD], s_xk[kD], s_xq[kD];
-  __shared__ float s_dk[kMaxRank + kMaxWindow + 1], s_dq[kMaxRank + kMaxWindow + 1];
-  __shared__ float s_g[kMaxWindow + 1];   // s_g[j] = G_j for j < m, s_g[m] = G0
+  __shared__ f32x4 s_x4[2][kD / 4];            // ksmooth o k, ksmooth o q
+  __shared__ float s_k[kD], s_q[kD];
+  __shared__ float s_dk[32], s_dq[32];
+  __shared__ float s_g[kMaxWindow + 1];        // s_g[j] = G_j for j < m, s_g[m] = G0
 
   const int tid = threadIdx.x;
-  const int head = blockIdx.x / kLqBPH;
-  const int rb = blockIdx.x % kLqBPH;
-  const float a = alpha[head];
-  const float b = beta[head];
+  const int head = blockIdx.x;
+  const int row = tid >> 1, hf = tid & 1;
   const size_t hk = (size_t)head * kD;
   float* bk = buf_k + (size_t)head * window * kD;
   float* bu = buf_u + (size_t)head * window * kD;
   const float* ba = buf_a + (size_t)head * window;
+  const int nv = rank + m + 1;   // dot-product vectors: compensators, buffered keys, k
 
+  // ---- independent loads
+  const uint4* zp = reinterpret_cast<const uint4*>(codes + (hk + row) * kD + hf * 64);
+  const uint4 z0 = zp[0], z1 = zp[1], z2 = zp[2], z3 = zp[3];
+  float bur[kMaxWindow / 2];
+#pragma unroll
+  for (int i = 0; i < kMaxWindow / 2; ++i) {
+    const int j = 2 * i + hf;
+    bur[i] = j < m ? bu[(size_t)j * kD + row] : 0.f;
+  }
+  float cur[kMaxRank / 2];
+#pragma unroll
+  for (int i = 0; i < kMaxRank / 2; ++i) {
+    const int r = 2 * i + hf;
+    cur[i] = r < rank ? h2f(ct_u[((size_t)head * rank + r) * kD + row]) : 0.f;
+  }
+  const float vrow = io_traits<IO>::ld(v, hk + row);
+  const float vs = vscale[hk + row];
+  const float a = alpha[head];
+  const float b = beta[head];
+  const int grp = tid >> 4, l16 = tid & 15, c0 = l16 * 8;
+  float w[2][8];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int vi = grp + 16 * p;
+    if (vi < rank) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(ct_k + ((size_t)head * rank + vi) * kD + c0);
+      const uint32_t r4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        w[p][2 * e] = h2f(uint16_t(r4[e] & 0xffffu));
+        w[p][2 * e + 1] = h2f(uint16_t(r4[e] >> 16));
+      }
+    } else if (vi < rank + m) {
+      const f32x4* pp = reinterpret_cast<const f32x4*>(bk + (size_t)(vi - rank) * kD + c0);
+      const f32x4 x0 = pp[0], x1 = pp[1];
+      w[p][0] = x0.x; w[p][1] = x0.y; w[p][2] = x0.z; w[p][3] = x0.w;
+      w[p][4] = x1.x; w[p][5] = x1.y; w[p][6] = x1.z; w[p][7] = x1.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[p][e] = 0.f;
+    }
+  }
   if (tid < kD) {
     const float kv = io_traits<IO>::ld(k, hk + tid);
     const float qv = io_traits<IO>::ld(q, hk + tid);
     const float c = ksmooth[hk + tid];
     s_k[tid] = kv;
     s_q[tid] = qv;
-    s_xk[tid] = c * kv;
-    s_xq[tid] = c * qv;
-    // append this token's key: each of the head's blocks writes its quarter
-    if ((tid >> 5) == rb) bk[(size_t)m * kD + tid] = kv;
+    reinterpret_cast<float*>(s_x4[0])[tid] = c * kv;
+    reinterpret_cast<float*>(s_x4[1])[tid] = c * qv;
+    bk[(size_t)m * kD + tid] = kv;          // append this token's key
   } else if (tid == kD) {
     float g = 1.f;
-    for (int j = m - 1; j >= 0; --j) {   // suffix products of the buffered decays
+    for (int j = m - 1; j >= 0; --j) {      // suffix products of the buffered decays
       s_g[j] = g;
       g *= ba[j];
     }
     s_g[m] = g;
-    if (rb == 0) buf_a[(size_t)head * window + m] = a;
+    buf_a[(size_t)head * window + m] = a;
   }
   __syncthreads();
 
-  // dot products of q and k with every compensator key, buffered key, and k itself
-  const int nv = rank + m + 1;
-  {
-    const int grp = tid >> 4, l16 = tid & 15;
-    const int c0 = l16 * 8;
-    for (int vi = grp; vi < nv; vi += 16) {
-      float w[8];
-      if (vi < rank) {
-        const uint4 raw = *reinterpret_cast<const uint4*>(ct_k + ((size_t)head * rank + vi) * kD + c0);
-        const uint32_t r4[4] = {raw.x, raw.y, raw.z, raw.w};
+  // ---- per-head dot products
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          w[2 * e] = h2f(uint16_t(r4[e] & 0xffffu));
-          w[2 * e + 1] = h2f(uint16_t(r4[e] >> 16));
-        }
-      } else if (vi < rank + m) {
-        const f32x4* p = reinterpret_cast<const f32x4*>(bk + (size_t)(vi - rank) * kD + c0);
-        const f32x4 x0 = p[0], x1 = p[1];
-        w[0] = x0.x; w[1] = x0.y; w[2] = x0.z; w[3] = x0.w;
-        w[4] = x1.x; w[5] = x1.y; w[6] = x1.z; w[7] = x1.w;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) w[e] = s_k[c0 + e];
-      }
+  for (int p = 0; p < 2; ++p) {
+    const int vi = grp + 16 * p;
+    if (vi < nv) {
       float pk = 0.f, pq = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        pk += w[e] * s_k[c0 + e];
-        pq += w[e] * s_q[c0 + e];
+        const float we = vi == rank + m ? s_k[c0 + e] : w[p][e];
+        pk += we * s_k[c0 + e];
+        pq += we * s_q[c0 + e];
       }
       pk = sum16(pk);
       pq = sum16(pq);
@@ -119,47 +144,45 @@ __global__ __launch_bounds__(256) void leapq_decode_kernel(
   }
   __syncthreads();
 
-  // rows: 8 lanes per row, 16 codes per lane
-  const int rl = tid >> 3, sub = tid & 7;
-  const int row = rb * kLqRows + rl;
-  const int c0 = sub * 16;
-  const uint4 zw = *reinterpret_cast<const uint4*>(codes + ((size_t)head * kD + row) * kD + c0);
-  const uint32_t z4[4] = {zw.x, zw.y, zw.z, zw.w};
+  // ---- this row
+  const uint32_t zz[16] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w,
+                           z2.x, z2.y, z2.z, z2.w, z3.x, z3.y, z3.z, z3.w};
   float yk = 0.f, yq = 0.f;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
+  for (int e = 0; e < 16; ++e) {
+    const f32x4 xk = s_x4[0][hf * 16 + e];
+    const f32x4 xq = s_x4[1][hf * 16 + e];
+    const float z_0 = sb(zz[e], 0), z_1 = sb(zz[e], 1), z_2 = sb(zz[e], 2), z_3 = sb(zz[e], 3);
+    yk += z_0 * xk.x + z_1 * xk.y + z_2 * xk.z + z_3 * xk.w;
+    yq += z_0 * xq.x + z_1 * xq.y + z_2 * xq.z + z_3 * xq.w;
+  }
+  float ck = 0.f, cq = 0.f, tk = 0.f, tq = 0.f;
 #pragma unroll
-    for (int bb = 0; bb < 4; ++bb) {
-      const float z = sb(z4[e], bb);
-      yk += z * s_xk[c0 + 4 * e + bb];
-      yq += z * s_xq[c0 + 4 * e + bb];
+  for (int i = 0; i < kMaxRank / 2; ++i) {
+    const int r = 2 * i + hf;
+    if (r < rank) {
+      ck += cur[i] * s_dk[r];
+      cq += cur[i] * s_dq[r];
     }
   }
-  // compensator and buffered contributions of this row, split over the 8 lanes
-  float ck = 0.f, cq = 0.f, tk = 0.f, tq = 0.f;
-  for (int r = sub; r < rank; r += 8) {
-    const float uc = h2f(ct_u[((size_t)head * rank + r) * kD + row]);
-    ck += uc * s_dk[r];
-    cq += uc * s_dq[r];
+#pragma unroll
+  for (int i = 0; i < kMaxWindow / 2; ++i) {
+    const int j = 2 * i + hf;
+    if (j < m) {
+      const float wj = s_g[j] * bur[i];
+      tk += wj * s_dk[rank + j];
+      tq += wj * s_dq[rank + j];
+    }
   }
-  for (int j = sub; j < m; j += 8) {
-    const float w = s_g[j] * bu[(size_t)j * kD + row];
-    tk += w * s_dk[rank + j];
-    tq += w * s_dq[rank + j];
-  }
-  yk = sum8(yk);
-  yq = sum8(yq);
-  ck = sum8(ck);
-  cq = sum8(cq);
-  tk = sum8(tk);
-  tq = sum8(tq);
   const float g0 = s_g[m];
-  const float sv = vscale[hk + row] * (1.0f / 127.0f);
-  const float Sk = g0 * (sv * yk + ck) + tk;
-  const float Sq = g0 * (sv * yq + cq) + tq;
-  const float u = b * (io_traits<IO>::ld(v, hk + row) - a * Sk);
+  const float sv = vs * (1.0f / 127.0f);
+  float Sk = g0 * (sv * yk + ck) + tk;     // this half-row's share; linear in the parts
+  float Sq = g0 * (sv * yq + cq) + tq;
+  Sk += dpp<0xB1>(Sk);                     // add the other half (adjacent lane)
+  Sq += dpp<0xB1>(Sq);
+  const float u = b * (vrow - a * Sk);
   const float oi = a * Sq + u * s_dq[rank + m];
-  if (sub == 0) {
+  if (hf == 0) {
     bu[(size_t)m * kD + row] = u;
     io_traits<IO>::st(o, hk + row, oi);
   }
@@ -167,276 +190,278 @@ __global__ __launch_bounds__(256) void leapq_decode_kernel(
 
 // ============================================================== window flush
 //
-// One 256-thread block per head; the dense state lives in LDS as [128][129] fp32.
-// Thread t works on value row (t & 127) over key columns [64h, 64h+64), h = t >> 7,
-// for row operations, and on key column (t & 127) over value rows [64h, 64h+64)
-// for column operations; the two halves are combined through LDS. Steps:
-//   rebuild (eq. 4) or load `dense`; compensator fit by subspace iteration with
-//   CholeskyQR2; subtract the fp16-rounded pieces; smoothing factors; value-channel
-//   scales; codes.
+// One block of 128*NQ threads per head. Thread t owns value row v = t % 128 and
+// key columns [c0, c0 + 128/NQ), c0 = (t / 128) * 128/NQ, of the dense state in
+// registers; a copy in LDS ([128][129] fp32, conflict-free by rows and columns)
+// serves the column operations. Steps: rebuild (eq. 4) or load `dense`;
+// compensator fit by subspace iteration with CholeskyQR2; subtract the
+// fp16-rounded pieces; smoothing factors; value-channel scales; codes.
 
-constexpr int kP = kD + 1;   // LDS pitch of the dense state (conflict-free rows and columns)
+constexpr int kP = kD + 1;
+constexpr int kFlushNQ = 8;   // 1024 threads per flush block, 16 key columns each
 
-__device__ __forceinline__ void block_sync() { __syncthreads(); }
-
-// LDS scratch of one flush block
+template <int NQ>
 struct FlushSmem {
-  float S[kD * kP];                          // dense state, then residual
-  float K[(kMaxRank + kMaxWindow) * kD];      // keys of the rank-one terms (rebuild), fp32
-  float Q[kD * kMaxRank];                    // [c][r] current orthonormal block
-  float Y[kD * kMaxRank];                    // [v][r] S Q
-  float part[2 * kD * kMaxRank];             // half-sums
-  float G[kMaxRank * kMaxRank];              // Gram / Cholesky factor
-  float col[kD];                             // per key column: 1 / smoothing factor
-  float red[2 * kD];
+  float S[kD * kP];
+  float K[(kMaxRank + kMaxWindow) * kD];   // keys of the rank-one terms (rebuild)
+  float Qa[kD * kMaxRank];                 // [c][r]
+  float Qb[kD * kMaxRank];
+  float Y[kD * kMaxRank];                  // [v][r]
+  float part[NQ * kD * kMaxRank];
+  float col[kD];
+  float red[NQ * kD];
 };
 
-// Q <- Q L^{-T} where L L^T = Q^T Q + (1e-6 tr + 1e-30) I, twice (CholeskyQR2).
-// Input and output in sm.Q ([c][r]); all threads participate.
-__device__ void cholqr2(FlushSmem& sm, int rank) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int pass = 0; pass < 2; ++pass) {
-    // Gram entries (i, j), i <= j, one wave per entry at a time: 2 rows per lane
-    const int ne = rank * rank;
-    for (int e = wave; e < ne; e += 4) {
-      const int i = e / rank, j = e % rank;
-      if (i > j) continue;
-      float p = sm.Q[(2 * lane) * kMaxRank + i] * sm.Q[(2 * lane) * kMaxRank + j] +
-                sm.Q[(2 * lane + 1) * kMaxRank + i] * sm.Q[(2 * lane + 1) * kMaxRank + j];
-      p = sum64(p);
-      if (lane == 0) sm.G[i * kMaxRank + j] = p;
-    }
-    block_sync();
-    if (tid == 0) {
-      float tr = 0.f;
-      for (int i = 0; i < rank; ++i) tr += sm.G[i * kMaxRank + i];
-      const float sh = 1e-6f * tr + 1e-30f;
-      // Cholesky in place (lower factor in sm.G[i][j], j <= i), from the upper entries
-      for (int i = 0; i < rank; ++i) {
-        for (int j = 0; j <= i; ++j) {
-          float s = sm.G[j * kMaxRank + i] + (i == j ? sh : 0.f);   // G[j][i] == G[i][j]
-          for (int p = 0; p < j; ++p) s -= sm.G[i * kMaxRank + p] * sm.G[j * kMaxRank + p];
-          if (i == j) sm.G[i * kMaxRank + i] = sqrtf(fmaxf(s, 0.f));
-          else sm.G[i * kMaxRank + j] = s / sm.G[j * kMaxRank + j];
-        }
-      }
-    }
-    block_sync();
-    if (tid < kD) {   // row c of Q: solve x L^T = Q[c, :]
-      float x[kMaxRank];
+// Y[x][r] = sum over the NQ partial sums (threads t < 128 combine)
+template <int NQ, int RANK>
+__device__ __forceinline__ void combine_parts(FlushSmem<NQ>& sm, float* dst) {
+  const int t = threadIdx.x;
+  if (t < kD) {
 #pragma unroll
-      for (int j = 0; j < kMaxRank; ++j) {
-        if (j < rank) {
-          float s = sm.Q[tid * kMaxRank + j];
+    for (int r = 0; r < RANK; ++r) {
+      float acc = 0.f;
 #pragma unroll
-          for (int p = 0; p < j; ++p) s -= x[p] * sm.G[j * kMaxRank + p];
-          x[j] = s / sm.G[j * kMaxRank + j];
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < kMaxRank; ++j)
-        if (j < rank) sm.Q[tid * kMaxRank + j] = x[j];
+      for (int p = 0; p < NQ; ++p) acc += sm.part[(p * kD + t) * kMaxRank + r];
+      dst[t * kMaxRank + r] = acc;
     }
-    block_sync();
   }
 }
 
-// Y = S Q ([v][r]) from the dense state in LDS
-__device__ void mul_SQ(FlushSmem& sm, int rank) {
-  const int tid = threadIdx.x, v = tid & (kD - 1), h = tid >> 7;
-  float acc[kMaxRank];
+// One CholeskyQR pass: dst = src L^{-T}, L L^T = src^T src + (1e-6 tr + 1e-30) I.
+// Every wave forms the Gram matrix itself (two rows per lane, wave sums), so the
+// only barrier is the one after the rows are written.
+template <int RANK>
+__device__ void cholqr_pass(const float* src, float* dst) {
+  const int lane = threadIdx.x & 63;
+  float x0[RANK], x1[RANK];
 #pragma unroll
-  for (int r = 0; r < kMaxRank; ++r) acc[r] = 0.f;
-  for (int i = 0; i < 64; ++i) {
-    const int c = h * 64 + i;
-    const float s = sm.S[v * kP + c];
-#pragma unroll
-    for (int r = 0; r < kMaxRank; ++r)
-      if (r < rank) acc[r] += s * sm.Q[c * kMaxRank + r];
+  for (int i = 0; i < RANK; ++i) {
+    x0[i] = src[(2 * lane) * kMaxRank + i];
+    x1[i] = src[(2 * lane + 1) * kMaxRank + i];
   }
+  float G[RANK][RANK];
 #pragma unroll
-  for (int r = 0; r < kMaxRank; ++r)
-    if (r < rank) sm.part[(h * kD + v) * kMaxRank + r] = acc[r];
-  block_sync();
-  if (tid < kD)
-    for (int r = 0; r < rank; ++r)
-      sm.Y[tid * kMaxRank + r] = sm.part[tid * kMaxRank + r] + sm.part[(kD + tid) * kMaxRank + r];
-  block_sync();
+  for (int i = 0; i < RANK; ++i)
+#pragma unroll
+    for (int j = i; j < RANK; ++j) G[i][j] = sum64(x0[i] * x0[j] + x1[i] * x1[j]);
+  float tr = 0.f;
+#pragma unroll
+  for (int i = 0; i < RANK; ++i) tr += G[i][i];
+  const float sh = 1e-6f * tr + 1e-30f;
+  float L[RANK][RANK];
+#pragma unroll
+  for (int i = 0; i < RANK; ++i) {
+#pragma unroll
+    for (int j = 0; j <= i; ++j) {
+      float s = G[j][i] + (i == j ? sh : 0.f);
+#pragma unroll
+      for (int p = 0; p < j; ++p) s -= L[i][p] * L[j][p];
+      L[i][j] = i == j ? sqrtf(fmaxf(s, 0.f)) : s / L[j][j];
+    }
+  }
+  const int t = threadIdx.x;
+  if (t < kD) {   // row t: solve x L^T = src[t, :]
+    float x[RANK];
+#pragma unroll
+    for (int j = 0; j < RANK; ++j) {
+      float s = src[t * kMaxRank + j];
+#pragma unroll
+      for (int p = 0; p < j; ++p) s -= x[p] * L[j][p];
+      x[j] = s / L[j][j];
+      dst[t * kMaxRank + j] = x[j];
+    }
+  }
+  __syncthreads();
 }
 
-// Q = S^T Y ([c][r])
-__device__ void mul_StY(FlushSmem& sm, int rank) {
-  const int tid = threadIdx.x, c = tid & (kD - 1), h = tid >> 7;
-  float acc[kMaxRank];
-#pragma unroll
-  for (int r = 0; r < kMaxRank; ++r) acc[r] = 0.f;
-  for (int i = 0; i < 64; ++i) {
-    const int v = h * 64 + i;
-    const float s = sm.S[v * kP + c];
-#pragma unroll
-    for (int r = 0; r < kMaxRank; ++r)
-      if (r < rank) acc[r] += s * sm.Y[v * kMaxRank + r];
-  }
-#pragma unroll
-  for (int r = 0; r < kMaxRank; ++r)
-    if (r < rank) sm.part[(h * kD + c) * kMaxRank + r] = acc[r];
-  block_sync();
-  if (tid < kD)
-    for (int r = 0; r < rank; ++r)
-      sm.Q[tid * kMaxRank + r] = sm.part[tid * kMaxRank + r] + sm.part[(kD + tid) * kMaxRank + r];
-  block_sync();
-}
-
-__global__ __launch_bounds__(256) void leapq_flush_kernel(
+template <int NQ, int RANK>
+__global__ __launch_bounds__(128 * NQ) void leapq_flush_kernel(
     int8_t* __restrict__ codes, float* __restrict__ vscale, float* __restrict__ ksmooth,
     uint16_t* __restrict__ ct_k, uint16_t* __restrict__ ct_u, const float* __restrict__ buf_k,
-    const float* __restrict__ buf_u, const float* __restrict__ buf_a, int rank, int window, int m,
+    const float* __restrict__ buf_u, const float* __restrict__ buf_a, int window, int m,
     const float* __restrict__ dense, const float* __restrict__ q0, int iters, int smooth_mode,
     float* __restrict__ pre_round) {
-  __shared__ FlushSmem sm;
+  constexpr int NT = 128 * NQ, FC = kD / NQ;
+  constexpr int rank = RANK;
+  __shared__ FlushSmem<NQ> sm;
   const int tid = threadIdx.x;
   const int head = blockIdx.x;
   const size_t hk = (size_t)head * kD;
-  const int v = tid & (kD - 1), h = tid >> 7;
+  const int v = tid & (kD - 1), qd = tid >> 7, c0 = qd * FC;
+  float S[FC];
 
   // ---------------------------------------------------------------- dense state
   if (dense) {
-    const float* Dh = dense + hk * kD;
-    for (int i = tid; i < kD * kD / 4; i += 256) {
-      const f32x4 x = reinterpret_cast<const f32x4*>(Dh)[i];
-      const int r = (4 * i) / kD, c = (4 * i) % kD;
-      sm.S[r * kP + c] = x.x;
-      sm.S[r * kP + c + 1] = x.y;
-      sm.S[r * kP + c + 2] = x.z;
-      sm.S[r * kP + c + 3] = x.w;
+    const f32x4* Dp = reinterpret_cast<const f32x4*>(dense + (hk + v) * kD + c0);
+#pragma unroll
+    for (int i = 0; i < FC / 4; ++i) {
+      const f32x4 x = Dp[i];
+      S[4 * i] = x.x; S[4 * i + 1] = x.y; S[4 * i + 2] = x.z; S[4 * i + 3] = x.w;
     }
-    block_sync();
   } else {
-    // keys of the rank-one terms: compensator keys first, then the buffered keys
     const int nt = rank + m;
-    for (int i = tid; i < nt * kD; i += 256) {
+    for (int i = tid; i < nt * kD; i += NT) {
       const int j = i / kD, c = i % kD;
       sm.K[i] = j < rank ? h2f(ct_k[((size_t)head * rank + j) * kD + c])
                          : buf_k[((size_t)head * window + (j - rank)) * kD + c];
     }
     if (tid < kD) sm.col[tid] = ksmooth[hk + tid];
-    block_sync();
-    // row v, columns [64h, 64h+64): buffered writes (newest first, suffix-product
-    // decays), then the compensator pieces and the dequantised residual, both
-    // decayed by G0
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < FC; ++i) S[i] = 0.f;
     const float* ba = buf_a + (size_t)head * window;
-    float acc[64];
-#pragma unroll
-    for (int i = 0; i < 64; ++i) acc[i] = 0.f;
     float g = 1.f;
-    for (int j = m - 1; j >= 0; --j) {
+    for (int j = m - 1; j >= 0; --j) {       // newest record first: suffix-product decays
       const float cj = g * buf_u[((size_t)head * window + j) * kD + v];
-      const float* Kj = sm.K + (rank + j) * kD + h * 64;
+      const f32x4* Kj = reinterpret_cast<const f32x4*>(sm.K + (rank + j) * kD + c0);
 #pragma unroll
-      for (int i = 0; i < 64; ++i) acc[i] += cj * Kj[i];
+      for (int i = 0; i < FC / 4; ++i) {
+        const f32x4 kk = Kj[i];
+        S[4 * i] += cj * kk.x; S[4 * i + 1] += cj * kk.y; S[4 * i + 2] += cj * kk.z; S[4 * i + 3] += cj * kk.w;
+      }
       g *= ba[j];
     }
     const float g0 = g;
     for (int r = 0; r < rank; ++r) {
       const float cr = g0 * h2f(ct_u[((size_t)head * rank + r) * kD + v]);
-      const float* Kr = sm.K + r * kD + h * 64;
+      const f32x4* Kr = reinterpret_cast<const f32x4*>(sm.K + r * kD + c0);
 #pragma unroll
-      for (int i = 0; i < 64; ++i) acc[i] += cr * Kr[i];
+      for (int i = 0; i < FC / 4; ++i) {
+        const f32x4 kk = Kr[i];
+        S[4 * i] += cr * kk.x; S[4 * i + 1] += cr * kk.y; S[4 * i + 2] += cr * kk.z; S[4 * i + 3] += cr * kk.w;
+      }
     }
     const float sv = g0 * vscale[hk + v] * (1.0f / 127.0f);
-    const int8_t* zr = codes + (hk + v) * kD + h * 64;
+    const uint4* zp = reinterpret_cast<const uint4*>(codes + (hk + v) * kD + c0);
 #pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4) {
-      const uint4 zw = *reinterpret_cast<const uint4*>(zr + 16 * c4);
+    for (int c16 = 0; c16 < FC / 16; ++c16) {
+      const uint4 zw = zp[c16];
       const uint32_t z4[4] = {zw.x, zw.y, zw.z, zw.w};
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int i = 16 * c4 + e;
-        acc[i] += sv * sb(z4[e >> 2], e & 3) * sm.col[h * 64 + i];
+        const int i = 16 * c16 + e;
+        S[i] += sv * sb(z4[e >> 2], e & 3) * sm.col[c0 + i];
       }
     }
-#pragma unroll
-    for (int i = 0; i < 64; ++i) sm.S[v * kP + h * 64 + i] = acc[i];
-    block_sync();
   }
+#pragma unroll
+  for (int i = 0; i < FC; ++i) sm.S[v * kP + c0 + i] = S[i];
 
   // ---------------------------------------------------------------- compensators
-  if (rank > 0) {
-    for (int i = tid; i < kD * rank; i += 256) sm.Q[(i / rank) * kMaxRank + (i % rank)] = q0[i];
-    block_sync();
-    for (int it = 0; it < iters; ++it) {
-      mul_SQ(sm, rank);
-      mul_StY(sm, rank);
-      cholqr2(sm, rank);
+  if constexpr (RANK > 0) {
+    for (int i = tid; i < kD * rank; i += NT) sm.Qa[(i / rank) * kMaxRank + (i % rank)] = q0[i];
+    __syncthreads();
+    for (int it = 0; it <= iters; ++it) {
+      // Y = S Q from the registers
+      float acc[RANK];
+#pragma unroll
+      for (int r = 0; r < RANK; ++r) acc[r] = 0.f;
+#pragma unroll
+      for (int i = 0; i < FC; ++i) {
+        const float* qr = sm.Qa + (c0 + i) * kMaxRank;
+#pragma unroll
+        for (int r = 0; r < RANK; ++r) acc[r] += S[i] * qr[r];
+      }
+#pragma unroll
+      for (int r = 0; r < RANK; ++r) sm.part[(qd * kD + v) * kMaxRank + r] = acc[r];
+      __syncthreads();
+      combine_parts<NQ, RANK>(sm, sm.Y);
+      __syncthreads();
+      if (it == iters) break;   // final Y = S Q: the compensator values
+      // Q = S^T Y from the LDS copy: column c = v over rows [c0, c0 + FC)
+#pragma unroll
+      for (int r = 0; r < RANK; ++r) acc[r] = 0.f;
+#pragma unroll
+      for (int i = 0; i < FC; ++i) {
+        const int vv = c0 + i;
+        const float sc = sm.S[vv * kP + v];
+        const float* yr = sm.Y + vv * kMaxRank;
+#pragma unroll
+        for (int r = 0; r < RANK; ++r) acc[r] += sc * yr[r];
+      }
+#pragma unroll
+      for (int r = 0; r < RANK; ++r) sm.part[(qd * kD + v) * kMaxRank + r] = acc[r];
+      __syncthreads();
+      combine_parts<NQ, RANK>(sm, sm.Qa);
+      __syncthreads();
+      cholqr_pass<RANK>(sm.Qa, sm.Qb);
+      cholqr_pass<RANK>(sm.Qb, sm.Qa);
     }
-    mul_SQ(sm, rank);
     // round to fp16, store, keep the rounded values for the residual
     if (tid < kD) {
       for (int r = 0; r < rank; ++r) {
-        const uint16_t hq = f2h(sm.Q[tid * kMaxRank + r]);
+        const uint16_t hq = f2h(sm.Qa[tid * kMaxRank + r]);
         const uint16_t hy = f2h(sm.Y[tid * kMaxRank + r]);
         ct_k[((size_t)head * rank + r) * kD + tid] = hq;
         ct_u[((size_t)head * rank + r) * kD + tid] = hy;
-        sm.Q[tid * kMaxRank + r] = h2f(hq);
-        sm.Y[tid * kMaxRank + r] = h2f(hy);
+        sm.Qb[tid * kMaxRank + r] = h2f(hq);
+        sm.part[tid * kMaxRank + r] = h2f(hy);
       }
     }
-    block_sync();
-    // residual R = S - sum_r uh_r kh_r^T, row-wise in place
-    for (int i = 0; i < 64; ++i) {
-      const int c = h * 64 + i;
-      float s = sm.S[v * kP + c];
-      for (int r = 0; r < rank; ++r) s -= sm.Y[v * kMaxRank + r] * sm.Q[c * kMaxRank + r];
-      sm.S[v * kP + c] = s;
+    __syncthreads();
+    // residual R = S - sum_r uh_r kh_r^T
+    float yh[RANK];
+#pragma unroll
+    for (int r = 0; r < RANK; ++r) yh[r] = sm.part[v * kMaxRank + r];
+#pragma unroll
+    for (int i = 0; i < FC; ++i) {
+      const float* qr = sm.Qb + (c0 + i) * kMaxRank;
+#pragma unroll
+      for (int r = 0; r < RANK; ++r) S[i] -= yh[r] * qr[r];
+      sm.S[v * kP + c0 + i] = S[i];
     }
-    block_sync();
   }
+  __syncthreads();
 
   // ---------------------------------------------------------------- smoothing
   {
-    const int c = v;
     float acc = 0.f;
-    for (int i = 0; i < 64; ++i) {
-      const float x = sm.S[(h * 64 + i) * kP + c];
+#pragma unroll
+    for (int i = 0; i < FC; ++i) {
+      const float x = sm.S[(c0 + i) * kP + v];   // column v, rows [c0, c0 + FC)
       acc += smooth_mode == 1 ? x * x : fabsf(x);
     }
-    sm.red[h * kD + c] = acc;
-    block_sync();
+    sm.red[qd * kD + v] = acc;
+    __syncthreads();
     if (tid < kD) {
-      float cf = 1.f;
-      if (smooth_mode != 2) cf = fmaxf(sqrtf((sm.red[tid] + sm.red[kD + tid]) * (1.0f / kD)), 1e-12f);
+      float tot = 0.f;
+#pragma unroll
+      for (int p = 0; p < NQ; ++p) tot += sm.red[p * kD + tid];
+      const float cf = smooth_mode == 2 ? 1.f : fmaxf(sqrtf(tot * (1.0f / kD)), 1e-12f);
       ksmooth[hk + tid] = cf;
       sm.col[tid] = 1.0f / cf;
     }
-    block_sync();
+    __syncthreads();
   }
 
   // ---------------------------------------------------------------- scales, codes
   {
     float mx = 0.f;
-    for (int i = 0; i < 64; ++i) {
-      const int c = h * 64 + i;
-      mx = fmaxf(mx, fabsf(sm.S[v * kP + c] * sm.col[c]));
-    }
-    sm.red[h * kD + v] = mx;
-    block_sync();
-    const float s = fmaxf(sm.red[v], sm.red[kD + v]);
-    if (h == 0) vscale[hk + v] = s;
-    const float sc = s > 0.f ? 127.0f / s : 0.f;
-    int8_t* zr = codes + (hk + v) * kD + h * 64;
-    float* pr = pre_round ? pre_round + (hk + v) * kD + h * 64 : nullptr;
 #pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4) {
+    for (int i = 0; i < FC; ++i) {
+      S[i] *= sm.col[c0 + i];
+      mx = fmaxf(mx, fabsf(S[i]));
+    }
+    sm.red[qd * kD + v] = mx;
+    __syncthreads();
+    float s = 0.f;
+#pragma unroll
+    for (int p = 0; p < NQ; ++p) s = fmaxf(s, sm.red[p * kD + v]);
+    if (qd == 0) vscale[hk + v] = s;
+    const float sc = s > 0.f ? 127.0f / s : 0.f;
+    uint4* zr = reinterpret_cast<uint4*>(codes + (hk + v) * kD + c0);
+    float* pr = pre_round ? pre_round + (hk + v) * kD + c0 : nullptr;
+#pragma unroll
+    for (int c16 = 0; c16 < FC / 16; ++c16) {
       uint32_t w[4] = {0, 0, 0, 0};
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int c = h * 64 + 16 * c4 + e;
-        const float x = (sm.S[v * kP + c] * sm.col[c]) * sc;
-        if (pr) pr[16 * c4 + e] = x;
+        const float x = S[16 * c16 + e] * sc;
+        if (pr) pr[16 * c16 + e] = x;
         const float qz = fminf(fmaxf(rintf(x), -127.f), 127.f);
         w[e >> 2] |= (uint32_t)((int32_t)qz & 0xff) << (8 * (e & 3));
       }
-      *reinterpret_cast<uint4*>(zr + 16 * c4) = make_uint4(w[0], w[1], w[2], w[3]);
+      zr[c16] = make_uint4(w[0], w[1], w[2], w[3]);
     }
   }
 }
@@ -450,7 +475,7 @@ static int check_state(const leapq_state* st, const char* fn) {
     return set_error(GDNRT_ESHAPE, "%s: rank=%d must be in [0, %d]", fn, st->rank, kMaxRank);
   if (st->window < 1 || st->window > kMaxWindow)
     return set_error(GDNRT_ESHAPE, "%s: window=%d must be in [1, %d]", fn, st->window, kMaxWindow);
-  if ((size_t)st->N * kLqBPH > 0x7fffffffu) return set_error(GDNRT_ESHAPE, "%s: N too large", fn);
+  if ((size_t)st->N > 0x7fffffffu) return set_error(GDNRT_ESHAPE, "%s: N too large", fn);
   if (st->N == 0) return GDNRT_OK;
   if (!st->codes || !st->vscale || !st->ksmooth || !st->buf_k || !st->buf_u || !st->buf_a ||
       (st->rank > 0 && (!st->ct_k || !st->ct_u)))
@@ -486,7 +511,7 @@ extern "C" int leapq_decode_step(const leapq_state* st, int pos, const void* q, 
       overlaps(o, nIO, st->codes, N * kD * kD))
     return set_error(GDNRT_EINVAL, "leapq_decode_step: o overlaps another buffer");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid((unsigned)(N * kLqBPH)), block(256);
+  const dim3 grid((unsigned)N), block(256);
   if (io == GDNRT_F32)
     hipLaunchKernelGGL(leapq_decode_kernel<float>, grid, block, 0, s, st->codes, st->vscale,
                        st->ksmooth, st->ct_k, st->ct_u, st->buf_k, st->buf_u, st->buf_a, st->rank,
@@ -520,8 +545,17 @@ extern "C" int leapq_window_flush(const leapq_state* st, int pos, const float* d
       (pre_round && overlaps(pre_round, nS, st->codes, N * kD * kD)))
     return set_error(GDNRT_EINVAL, "leapq_window_flush: dense / pre_round overlap the state");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(leapq_flush_kernel, dim3((unsigned)N), dim3(256), 0, s, st->codes,
-                     st->vscale, st->ksmooth, st->ct_k, st->ct_u, st->buf_k, st->buf_u, st->buf_a,
-                     st->rank, st->window, pos, dense, q0, iters, smooth_mode, pre_round);
+  switch (st->rank) {
+#define GDNRT_FLUSH(R)                                                                            \
+  case R:                                                                                         \
+    hipLaunchKernelGGL((leapq_flush_kernel<kFlushNQ, R>), dim3((unsigned)N), dim3(128 * kFlushNQ), \
+                       0, s, st->codes, st->vscale, st->ksmooth, st->ct_k, st->ct_u, st->buf_k,   \
+                       st->buf_u, st->buf_a, st->window, pos, dense, q0, iters, smooth_mode,      \
+                       pre_round);                                                                \
+    break;
+    GDNRT_FLUSH(0) GDNRT_FLUSH(1) GDNRT_FLUSH(2) GDNRT_FLUSH(3) GDNRT_FLUSH(4)
+    GDNRT_FLUSH(5) GDNRT_FLUSH(6) GDNRT_FLUSH(7) GDNRT_FLUSH(8)
+#undef GDNRT_FLUSH
+  }
   return check_launch("leapq_window_flush");
 }
