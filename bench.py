@@ -176,6 +176,45 @@ def bench_leapq(tokens=4096, B=DECODE_B, H=DECODE_H, W=16, rank=4):
     return res
 
 
+# ------------------------------------------------------------------- prefill
+
+def gla_chunk_work(C=64):
+    """Algorithmic FLOPs (multiply-add = 2) of one chunk of one sequence, with the
+    causal products at triangular size, and the dense-tile count MFMA executes."""
+    tri = C * (C + 1) // 2
+    alg = 2 * tri * D + 2 * C * D * D + 2 * tri * D + 2 * D * D * C   # QK^T, QS^T, AV, V^T K
+    dense = 2 * C * C * D + 2 * C * D * D + 2 * C * C * D + 2 * D * D * C
+    return alg, dense
+
+
+def bench_gla(K=20, W=3, B=4, H=16, T=4096):
+    N = B * H
+    log(f"[gla] generating B={B} H={H} T={T}")
+    inp = synth.gla_prefill(B=B, H=H, T=T, device="cuda")
+    ST = torch.empty_like(inp["S0"])
+    o = torch.empty_like(inp["q"])
+
+    def run(i):
+        m.gla_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_g"], inp["S0"], ST, o)
+
+    ms, wall = timed(run, K, W)
+    alg, dense = gla_chunk_work()
+    chunks = N * T // 64
+    flops, dflops = alg * chunks, dense * chunks
+    byts = N * T * D * (3 * 2 + 4 + 2) + 2 * N * D * D * 4    # q,k,v bf16, gates fp32, o bf16, S0, ST
+    res = dict(workload=f"gla_chunk_fwd B={B} H={H} T={T} d=128 chunk 64, bf16 q/k/v, fp32 gates, "
+                        f"fp32 incoming state",
+               ms=ms, tokens_per_s=B * T / (ms * 1e-3), gflop=flops / 1e9, gflop_dense=dflops / 1e9,
+               tflops=flops / (ms * 1e-3) / 1e12, tflops_dense=dflops / (ms * 1e-3) / 1e12,
+               bytes=byts, achieved_gbs=byts / (ms * 1e-3) / 1e9, wall_s=wall)
+    res["frac_hbm"] = res["achieved_gbs"] / PEAK_HBM_GBS
+    res["frac_mfma"] = res["tflops"] / PEAK_BF16_TFLOPS
+    res["frac_mfma_dense"] = res["tflops_dense"] / PEAK_BF16_TFLOPS
+    res["roofline_bound"] = "hbm"
+    del inp
+    return res
+
+
 def counter_traffic(kernel):
     """HBM bytes per launch measured by rocprofv3 counters (profiles/counters.json),
     or None if the kernel's sources changed since they were taken."""
@@ -199,7 +238,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--rows", default="decode,leapq")
+    ap.add_argument("--rows", default="decode,leapq,gla")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -231,6 +270,12 @@ def main():
         cpu = cpu_baseline_decode(inp)
     del inp
     torch.cuda.empty_cache()
+    if "gla" in rows:
+        r = bench_gla()
+        out_rows["gla"] = r
+        log(f"[gla] {r['ms']*1e3:.1f} us  {r['tflops']:.1f} TFLOP/s ({r['frac_mfma']*100:.1f}% MFMA)  "
+            f"{r['achieved_gbs']:.0f} GB/s ({r['frac_hbm']*100:.1f}% HBM)  {r['tokens_per_s']/1e6:.2f} M tok/s")
+        torch.cuda.empty_cache()
     if "leapq" in rows:
         r = bench_leapq()
         r["speedup_vs_fp32_decode"] = res["ms_per_step"] / r["ms_per_step"]
