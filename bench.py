@@ -215,6 +215,49 @@ def bench_gla(K=20, W=3, B=4, H=16, T=4096):
     return res
 
 
+def gdn_chunk_work(C=64):
+    """Algorithmic FLOPs of one chunk of one head in the UT / WY form: Gram k.k
+    (strict lower), triangular inverse (C^3/3 multiply-adds), scores q.k (lower),
+    W and U~ (lower-triangular T times K, V), W S^T, Q S^T, A U (lower), U^T K;
+    and the dense-tile count."""
+    tri, stri = C * (C + 1) // 2, C * (C - 1) // 2
+    alg = (2 * stri * D + 2 * C ** 3 // 3 + 2 * tri * D + 2 * 2 * tri * D
+           + 2 * C * D * D * 2 + 2 * tri * D + 2 * D * D * C)
+    dense = (2 * C * C * D * 2 + 2 * C ** 3 // 3 + 2 * 2 * C * C * D
+             + 2 * C * D * D * 2 + 2 * C * C * D + 2 * D * D * C)
+    return alg, dense
+
+
+def bench_gdn_chunk(K=10, W=2, B=1, H=32, T=16384):
+    N = B * H
+    log(f"[gdn_chunk] generating B={B} H={H} T={T}")
+    inp = synth.gdn_prefill(B=B, H=H, T=T, device="cuda")
+    ws = m.gdn_chunk_workspace(N, T)
+    ST = torch.empty((N, D, D), device="cuda")
+    o = torch.empty_like(inp["q"])
+
+    def run(i):
+        m.gdn_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], None, ST, o, ws)
+
+    ms, wall = timed(run, K, W)
+    alg, dense = gdn_chunk_work()
+    chunks = N * T // 64
+    flops, dflops = alg * chunks, dense * chunks
+    byts = N * T * (3 * D * 2 + 2 * 4 + D * 2) + N * D * D * 4   # q,k,v, alpha,beta, o, ST
+    res = dict(workload=f"gdn_chunk_fwd B={B} H={H} T={T} d=128 chunk 64, bf16 q/k/v (q, k "
+                        f"L2-normalised), fp32 gates, zero initial state",
+               ms=ms, tokens_per_s=B * T / (ms * 1e-3), gflop=flops / 1e9, gflop_dense=dflops / 1e9,
+               tflops=flops / (ms * 1e-3) / 1e12, tflops_dense=dflops / (ms * 1e-3) / 1e12,
+               bytes=byts, achieved_gbs=byts / (ms * 1e-3) / 1e9,
+               workspace_bytes=int(ws.numel()), wall_s=wall)
+    res["frac_hbm"] = res["achieved_gbs"] / PEAK_HBM_GBS
+    res["frac_mfma"] = res["tflops"] / PEAK_BF16_TFLOPS
+    res["frac_mfma_dense"] = res["tflops_dense"] / PEAK_BF16_TFLOPS
+    res["roofline_bound"] = "hbm (at the knee)"
+    del inp, ws
+    return res
+
+
 def counter_traffic(kernel):
     """HBM bytes per launch measured by rocprofv3 counters (profiles/counters.json),
     or None if the kernel's sources changed since they were taken."""
@@ -238,7 +281,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--rows", default="decode,leapq,gla")
+    ap.add_argument("--rows", default="decode,leapq,gla,gdn")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -274,6 +317,12 @@ def main():
         r = bench_gla()
         out_rows["gla"] = r
         log(f"[gla] {r['ms']*1e3:.1f} us  {r['tflops']:.1f} TFLOP/s ({r['frac_mfma']*100:.1f}% MFMA)  "
+            f"{r['achieved_gbs']:.0f} GB/s ({r['frac_hbm']*100:.1f}% HBM)  {r['tokens_per_s']/1e6:.2f} M tok/s")
+        torch.cuda.empty_cache()
+    if "gdn" in rows:
+        r = bench_gdn_chunk()
+        out_rows["gdn_chunk"] = r
+        log(f"[gdn_chunk] {r['ms']*1e3:.1f} us  {r['tflops']:.1f} TFLOP/s ({r['frac_mfma']*100:.1f}% MFMA)  "
             f"{r['achieved_gbs']:.0f} GB/s ({r['frac_hbm']*100:.1f}% HBM)  {r['tokens_per_s']/1e6:.2f} M tok/s")
         torch.cuda.empty_cache()
     if "leapq" in rows:

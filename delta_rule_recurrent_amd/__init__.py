@@ -8,6 +8,7 @@ from .binding import (  # noqa: F401
     GdnrtError,
     LeapqBuffers,
     gdn_chunk_fwd,
+    gdn_chunk_workspace,
     gdn_decode_step,
     gla_chunk_fwd,
     leapq_decode_step,

@@ -35,7 +35,8 @@ class LeapqState(ctypes.Structure):
 SIGNATURES = {
     "gdn_decode_step": ([_vp] * 7 + [_c_int] * 5 + [_vp], _c_int),
     "gla_chunk_fwd": ([_vp] * 7 + [_c_int] * 6 + [_vp], _c_int),
-    "gdn_chunk_fwd": ([_vp] * 8 + [_c_int] * 6 + [_vp], _c_int),
+    "gdn_chunk_fwd": ([_vp] * 8 + [_c_int] * 6 + [_vp, ctypes.c_size_t, _vp], _c_int),
+    "gdn_chunk_fwd_workspace_bytes": ([_c_int] * 5, ctypes.c_size_t),
     "leapq_decode_step": ([ctypes.POINTER(LeapqState), _c_int] + [_vp] * 6 + [_c_int, _vp], _c_int),
     "leapq_window_flush": ([ctypes.POINTER(LeapqState), _c_int, _vp, _vp, _c_int, _c_int, _vp, _vp],
                            _c_int),
@@ -150,11 +151,18 @@ def gla_chunk_fwd(q, k, v, log_g, S0=None, ST=None, o=None, chunk=CHUNK):
     return o, ST
 
 
-def gdn_chunk_fwd(q, k, v, alpha, beta, S0=None, ST=None, o=None, chunk=CHUNK):
+def gdn_chunk_workspace(N, T, device="cuda", chunk=CHUNK):
+    """Allocate the workspace gdn_chunk_fwd needs for N sequences of T tokens."""
+    nb = lib().gdn_chunk_fwd_workspace_bytes(N, T, D, D, chunk)
+    return torch.empty(max(nb, 16), dtype=torch.uint8, device=device)
+
+
+def gdn_chunk_fwd(q, k, v, alpha, beta, S0=None, ST=None, o=None, workspace=None, chunk=CHUNK):
     """Gated DeltaNet chunkwise forward (prefill).
 
     q, k, v [N][T][128] bf16; alpha, beta [N][T] fp32; S0 [N][128][128] fp32 or
-    None. Returns (o [N][T][128] bf16, ST [N][128][128] fp32)."""
+    None; workspace from gdn_chunk_workspace (allocated here if None).
+    Returns (o [N][T][128] bf16, ST [N][128][128] fp32)."""
     N, T, _ = q.shape
     for n_, t_ in (("q", q), ("k", k), ("v", v)):
         _need(t_, n_, torch.bfloat16, (N, T, D))
@@ -168,9 +176,12 @@ def gdn_chunk_fwd(q, k, v, alpha, beta, S0=None, ST=None, o=None, chunk=CHUNK):
     if o is None:
         o = torch.empty((N, T, D), dtype=torch.bfloat16, device=q.device)
     _need(o, "o", torch.bfloat16, (N, T, D))
+    if workspace is None:
+        workspace = gdn_chunk_workspace(N, T, q.device, chunk)
+    _need(workspace, "workspace", torch.uint8)
     _check("gdn_chunk_fwd", lib().gdn_chunk_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(ST), _ptr(o),
-        N, T, D, D, chunk, BF16, _stream()))
+        N, T, D, D, chunk, BF16, _ptr(workspace), workspace.numel(), _stream()))
     return o, ST
 
 

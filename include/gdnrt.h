@@ -94,17 +94,28 @@ GDNRT_API int gla_chunk_fwd(const void* q, const void* k, const void* v, const f
  * gdn_decode_step over T tokens, computed per chunk of 64 tokens through the
  * UT / WY form of the intra-chunk delta rule (derived from eq. 3 of the LeapQuant
  * page's section "The state, from the update rule up" by unrolling within a
- * chunk; the pages print no chunk form for the delta rule).
+ * chunk; the pages print no chunk form for the delta rule):
+ *   (I + L) U = diag(beta) V - diag(beta g) K S_0^T, L[r,j] = beta_r (g_r/g_j) k_r.k_j (j < r),
+ *   O = diag(g) Q S_0^T + A U, A[r,j] = (g_r/g_j) q_r.k_j (j <= r),
+ *   S_C = g_C S_0 + U^T diag(g_C/g) K,  g_r = prod_{i<=r} alpha_i within the chunk.
  *
  *   q, k [N][T][dk] bf16 (q, k as given).   v, o [N][T][dv] bf16.
- *   alpha, beta [N][T] fp32.   S0 [N][dv][dk] fp32 or NULL (zero).
+ *   alpha (in (0,1)), beta [N][T] fp32.   S0 [N][dv][dk] fp32 or NULL (zero).
  *   ST [N][dv][dk] fp32 final state (may equal S0).
+ *   workspace: caller-owned device memory of gdn_chunk_fwd_workspace_bytes() bytes,
+ *   16-byte aligned, overwritten (the per-chunk state-independent operands W, U~, A
+ *   in bf16, 40,960 bytes per chunk).
  * T must be a multiple of chunk (64).
  */
 GDNRT_API int gdn_chunk_fwd(const void* q, const void* k, const void* v,
-                  const float* alpha, const float* beta,
-                  const float* S0, float* ST, void* o,
-                  int N, int T, int dk, int dv, int chunk, int io, void* stream);
+                            const float* alpha, const float* beta,
+                            const float* S0, float* ST, void* o,
+                            int N, int T, int dk, int dv, int chunk, int io,
+                            void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace bytes gdn_chunk_fwd needs for this shape (0 if the shape is unsupported
+ * or empty). */
+GDNRT_API size_t gdn_chunk_fwd_workspace_bytes(int N, int T, int dk, int dv, int chunk);
 
 /*
  * LeapQuant windowed 8-bit state ("LeapQuant: an 8-bit recurrent state that stops

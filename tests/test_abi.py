@@ -1,0 +1,98 @@
+"""The C ABI on the CPU: the library loads, exports every function the header
+declares, and rejects bad arguments with the documented status before touching
+the GPU (no GPU is needed for these calls)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdnrt.h")
+LIB = os.path.join(ROOT, "delta_rule_recurrent_amd", "libgdnrt.so")
+
+OK, EINVAL, ESHAPE, EALIGN, EDTYPE, ESTATE = range(6)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from delta_rule_recurrent_amd import build
+        build.build()
+    from delta_rule_recurrent_amd import binding
+    return binding.lib()
+
+
+def declared():
+    text = open(HEADER).read()
+    return re.findall(r"GDNRT_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def test_header_declares_the_five_entry_points():
+    names = set(declared())
+    for n in ("gdn_decode_step", "gla_chunk_fwd", "gdn_chunk_fwd", "leapq_decode_step",
+              "leapq_window_flush", "gdnrt_last_error", "gdn_chunk_fwd_workspace_bytes"):
+        assert n in names, n
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    for n in declared():
+        assert n in exported, n
+        assert getattr(lib, n) is not None
+
+
+def _err(lib):
+    return lib.gdnrt_last_error().decode()
+
+
+def test_decode_validation(lib):
+    f = lib.gdn_decode_step
+    p = ctypes.c_void_p(4096)   # never dereferenced: every call below fails validation
+    assert f(p, p, p, p, p, p, p, 4, 1, 64, 128, 1, None) == ESHAPE and "128" in _err(lib)
+    assert f(p, p, p, p, p, p, p, -1, 1, 128, 128, 1, None) == ESHAPE
+    assert f(p, p, p, p, p, p, p, 4, 1, 128, 128, 7, None) == EDTYPE
+    assert f(None, p, p, p, p, p, p, 4, 1, 128, 128, 1, None) == EINVAL
+    assert f(p, ctypes.c_void_p(4098), p, p, p, p, p, 4, 1, 128, 128, 1, None) == EALIGN
+    assert f(p, p, p, p, p, p, p, 0, 1, 128, 128, 1, None) == OK          # empty: no launch
+    big = ctypes.c_void_p(1 << 40)
+    # o overlapping the state
+    assert f(big, p, p, p, p, p, big, 4, 1, 128, 128, 1, None) == EINVAL
+
+
+def test_chunk_validation(lib):
+    p = ctypes.c_void_p(4096)
+    g = lib.gla_chunk_fwd
+    assert g(p, p, p, p, None, p, p, 2, 100, 128, 128, 64, 1, None) == ESHAPE     # T % 64
+    assert g(p, p, p, p, None, p, p, 2, 128, 128, 128, 32, 1, None) == ESHAPE     # chunk
+    assert g(p, p, p, p, None, p, p, 2, 128, 128, 128, 64, 0, None) == EDTYPE     # fp32 io
+    d = lib.gdn_chunk_fwd
+    assert lib.gdn_chunk_fwd_workspace_bytes(32, 16384, 128, 128, 64) == 32 * 256 * 40960
+    assert lib.gdn_chunk_fwd_workspace_bytes(32, 100, 128, 128, 64) == 0
+    assert d(p, p, p, p, p, None, p, p, 2, 128, 128, 128, 64, 1, p, 10, None) == EINVAL  # workspace
+
+
+def _state(lib, **kw):
+    from delta_rule_recurrent_amd.binding import LeapqState
+    a = dict(codes=4096, vscale=4096, ksmooth=4096, ct_k=4096, ct_u=4096, buf_k=4096,
+             buf_u=4096, buf_a=4096, N=8, dk=128, dv=128, rank=4, window=16)
+    a.update(kw)
+    return LeapqState(**a)
+
+
+def test_leapq_validation(lib):
+    p = ctypes.c_void_p(4096)
+    st = _state(lib)
+    f = lib.leapq_decode_step
+    assert f(ctypes.byref(st), 16, p, p, p, p, p, p, 1, None) == ESTATE     # window full
+    assert f(ctypes.byref(st), -1, p, p, p, p, p, p, 1, None) == ESTATE
+    assert f(ctypes.byref(_state(lib, rank=9)), 0, p, p, p, p, p, p, 1, None) == ESHAPE
+    assert f(ctypes.byref(_state(lib, window=17)), 0, p, p, p, p, p, p, 1, None) == ESHAPE
+    assert f(ctypes.byref(_state(lib, codes=4097)), 0, p, p, p, p, p, p, 1, None) == EALIGN
+    assert f(None, 0, p, p, p, p, p, p, 1, None) == EINVAL
+    fl = lib.leapq_window_flush
+    assert fl(ctypes.byref(st), 17, None, p, 1, 0, None, None) == ESTATE
+    assert fl(ctypes.byref(st), 0, None, p, 1, 3, None, None) == EINVAL      # smooth_mode
+    assert fl(ctypes.byref(st), 0, None, None, 1, 0, None, None) == EINVAL   # q0 missing
