@@ -59,6 +59,7 @@ def timed(fn, K, W):
 # ------------------------------------------------------------------- decode
 
 DECODE_B, DECODE_H = 512, 32
+DECODE_WORKLOAD = "gdn_decode B=512 H=32 d_k=d_v=128 fp32 state, bf16 q/k/v, T=1 per launch"
 
 
 def decode_bytes_per_head_step(io_bytes=2):
@@ -83,7 +84,7 @@ def bench_decode(K, W, gen_steps=256):
     ms, wall = timed(step, K, W)
     bytes_launch = decode_bytes_per_head_step() * N
     gbs = bytes_launch / (ms * 1e-3) / 1e9
-    return dict(workload=f"gdn_decode B={B} H={H} d_k=d_v=128 fp32 state, bf16 q/k/v, T=1 per launch",
+    return dict(workload=DECODE_WORKLOAD,
                 ms_per_step=ms, tokens_per_s=B / (ms * 1e-3), head_steps=N,
                 bytes_per_launch=bytes_launch, achieved_gbs=gbs, frac_hbm=gbs / PEAK_HBM_GBS,
                 wall_s=wall), inp
@@ -295,24 +296,26 @@ def main():
         sys.exit(1)
     m.lib()
     rows = [r.strip() for r in args.rows.split(",") if r.strip()]
-    res, inp = bench_decode(args.steps, args.warmup)
-    log(f"[decode] {res['ms_per_step']*1e3:.1f} us/step  {res['achieved_gbs']:.0f} GB/s  "
-        f"{res['tokens_per_s']/1e6:.3f} M tok/s")
-    out_rows = {"decode": res}
-    if args.copy_probe:
-        # a plain copy of known size: 1 GiB read + 1 GiB written per launch
-        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("[cpu] timing the oracle on a sample")
-        cpu = cpu_baseline_decode(inp)
-    del inp
-    torch.cuda.empty_cache()
+    out_rows = {}
+    res, cpu = None, None
+    if "decode" in rows:
+        res, inp = bench_decode(args.steps, args.warmup)
+        log(f"[decode] {res['ms_per_step']*1e3:.1f} us/step  {res['achieved_gbs']:.0f} GB/s  "
+            f"{res['tokens_per_s']/1e6:.3f} M tok/s")
+        out_rows["decode"] = res
+        if args.copy_probe:
+            # a plain copy of known size: 1 GiB read + 1 GiB written per launch
+            src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            del src, dst
+        if not args.no_cpu_baseline:
+            log("[cpu] timing the oracle on a sample")
+            cpu = cpu_baseline_decode(inp)
+        del inp
+        torch.cuda.empty_cache()
     if "gla" in rows:
         r = bench_gla()
         out_rows["gla"] = r
@@ -327,30 +330,30 @@ def main():
         torch.cuda.empty_cache()
     if "leapq" in rows:
         r = bench_leapq()
-        r["speedup_vs_fp32_decode"] = res["ms_per_step"] / r["ms_per_step"]
+        r["speedup_vs_fp32_decode"] = res["ms_per_step"] / r["ms_per_step"] if res else None
         out_rows["leapq"] = r
         log(f"[leapq] {r['ms_per_step']*1e3:.1f} us/step ({r['decode_kernel_ms']*1e3:.1f} us decode "
             f"+ {r['flush_kernel_ms']*1e3:.1f} us flush per window)  {r['achieved_gbs']:.0f} GB/s  "
-            f"{r['tokens_per_s']/1e6:.3f} M tok/s  {r['speedup_vs_fp32_decode']:.2f}x fp32 decode")
+            f"{r['tokens_per_s']/1e6:.3f} M tok/s")
         torch.cuda.empty_cache()
     line = {
         "metric": "GDN decode tokens/s at B=512 (one layer, 32 heads, d=128)",
-        "value": res["tokens_per_s"],
+        "value": res["tokens_per_s"] if res else None,
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": res["ms_per_step"],
+        "ms_per_step": res["ms_per_step"] if res else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": res["workload"], "streams": DECODE_B, "heads": DECODE_H,
+        "config": {"workload": DECODE_WORKLOAD, "streams": DECODE_B, "heads": DECODE_H,
                    "d_k": D, "d_v": D},
-        "roofline": {"bound": "hbm", "achieved": res["achieved_gbs"], "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": res["frac_hbm"],
-                     "traffic": counter_traffic("gdn_decode_kernel")},
+        "roofline": ({"bound": "hbm", "achieved": res["achieved_gbs"], "peak": PEAK_HBM_GBS,
+                      "unit": "GB/s", "frac": res["frac_hbm"],
+                      "traffic": counter_traffic("gdn_decode_kernel")} if res else None),
         "cpu_baseline": cpu,
         "rows": out_rows,
         "host": {"cpus": os.cpu_count(), "machine": platform.processor() or platform.machine(),

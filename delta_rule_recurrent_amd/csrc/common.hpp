@@ -46,12 +46,16 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 
-// fp32 -> bf16, round to nearest even (quiet NaN kept quiet).
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16, round to nearest even: gfx950's packed convert (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+// two fp32 -> two bf16 in one dword (lo in bits 0..15)
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const f32x2 x = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
 }
 
 // Cross-lane moves inside a 16-lane row (DPP). Controls: row_mirror 0x140,

@@ -26,16 +26,19 @@ namespace gdnrt {
 namespace gdc {
 
 constexpr int C = kChunk;   // 64
-constexpr int PQ = kD + 8;  // bf16 pitch of 128-wide rows
+constexpr int NT = 512;     // threads per block, both kernels
+constexpr int PQ = kD + 8;  // bf16 pitch of 128-wide rows (16-byte aligned, conflict-free reads)
 constexpr int PC = C + 8;   // bf16 pitch of 64-wide rows
-constexpr int PF = C + 1;   // fp32 pitch of 64-wide rows
+constexpr int PF = C + 4;   // fp32 pitch of 64-wide rows (16-byte aligned)
 
 // workspace per chunk: W [64][128] bf16, U~ [64][128] bf16, A [64][64] bf16
 constexpr size_t kWsW = 0, kWsU = (size_t)C * kD * 2, kWsA = 2 * (size_t)C * kD * 2;
 constexpr size_t kWsChunk = kWsA + (size_t)C * C * 2;   // 40,960 bytes
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));   // register-promotable across loops
+
 __device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -52,11 +55,23 @@ __device__ __forceinline__ float wave_scan(float x) {
   return x;
 }
 
+__device__ __forceinline__ float lo_bf(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+
 struct PrepSmem {
-  uint16_t Q[C * PQ];     // [r][k]
-  uint16_t K[C * PQ];     // [j][k]
+  union {
+    struct {
+      uint16_t Q[C * PQ];     // [r][k]
+      uint16_t K[C * PQ];     // [j][k]
+    } in;
+    struct {
+      uint16_t W[C * PQ];     // staged W   [r][k]
+      uint16_t U[C * PQ];     // staged U~  [r][v]
+    } out;
+  } u;
   uint16_t Kt[kD * PC];   // [k][j]
   uint16_t Vt[kD * PC];   // [v][j]
+  uint16_t A[C * PC];     // masked decayed scores [r][j]
   float L[C * PF];        // strict lower part of (I + L)
   float T[C * PF];        // (I + L)^-1
   float M[3 * 16 * 17];   // block-row partial products
@@ -68,7 +83,10 @@ struct PrepSmem {
 }  // namespace gdc
 
 // ============================================================== kernel 1: per-chunk prep
-__global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(
+//
+// Thread t stages key channels (2cp, 2cp+1) of tokens [8e, 8e+8) (cp = t % 64,
+// e = t / 64): q, k row-major and k, v transposed with 16-byte writes.
+__global__ __launch_bounds__(512) void gdn_chunk_prep_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, uint8_t* __restrict__ ws,
     int T) {
@@ -76,93 +94,110 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(
   __shared__ PrepSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lq = lane >> 4;
+  const int cp = tid & 63, e8 = tid >> 6;
   const int nc = T / C;
   const int n = blockIdx.x / nc, ci = blockIdx.x % nc;
   const size_t tok0 = (size_t)n * T + (size_t)ci * C;
   uint8_t* wsc = ws + (size_t)blockIdx.x * kWsChunk;
 
-  // ---- stage q, k (and k^T), v^T; cumulative log-decays
+  // ---- stage q, k (row-major), k^T and v^T; cumulative log-decays
+  {
+    unsigned qw[8], kw[8], vw[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int p = tid + 256 * i, row = p >> 4, seg = p & 15;
-    const size_t off = (tok0 + row) * kD + seg * 8;
-    const uint4 qw = *reinterpret_cast<const uint4*>(q + off);
-    const uint4 kw = *reinterpret_cast<const uint4*>(k + off);
-    const uint4 vw = *reinterpret_cast<const uint4*>(v + off);
-    *reinterpret_cast<uint4*>(sm.Q + row * PQ + seg * 8) = qw;
-    *reinterpret_cast<uint4*>(sm.K + row * PQ + seg * 8) = kw;
-    const uint32_t k4[4] = {kw.x, kw.y, kw.z, kw.w}, v4[4] = {vw.x, vw.y, vw.z, vw.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sm.Kt[(seg * 8 + 2 * e) * PC + row] = uint16_t(k4[e] & 0xffffu);
-      sm.Kt[(seg * 8 + 2 * e + 1) * PC + row] = uint16_t(k4[e] >> 16);
-      sm.Vt[(seg * 8 + 2 * e) * PC + row] = uint16_t(v4[e] & 0xffffu);
-      sm.Vt[(seg * 8 + 2 * e + 1) * PC + row] = uint16_t(v4[e] >> 16);
+    for (int i = 0; i < 8; ++i) {
+      const size_t off = (tok0 + 8 * e8 + i) * kD + 2 * cp;
+      qw[i] = *reinterpret_cast<const unsigned*>(q + off);
+      kw[i] = *reinterpret_cast<const unsigned*>(k + off);
+      vw[i] = *reinterpret_cast<const unsigned*>(v + off);
     }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 8 * e8 + i;
+      *reinterpret_cast<unsigned*>(sm.u.in.Q + r * PQ + 2 * cp) = qw[i];
+      *reinterpret_cast<unsigned*>(sm.u.in.K + r * PQ + 2 * cp) = kw[i];
+    }
+    u32x4 k0, k1, v0, v1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      k0[i] = (kw[2 * i] & 0xffffu) | (kw[2 * i + 1] << 16);
+      k1[i] = (kw[2 * i] >> 16) | (kw[2 * i + 1] & 0xffff0000u);
+      v0[i] = (vw[2 * i] & 0xffffu) | (vw[2 * i + 1] << 16);
+      v1[i] = (vw[2 * i] >> 16) | (vw[2 * i + 1] & 0xffff0000u);
+    }
+    *reinterpret_cast<u32x4*>(sm.Kt + (2 * cp) * PC + 8 * e8) = k0;
+    *reinterpret_cast<u32x4*>(sm.Kt + (2 * cp + 1) * PC + 8 * e8) = k1;
+    *reinterpret_cast<u32x4*>(sm.Vt + (2 * cp) * PC + 8 * e8) = v0;
+    *reinterpret_cast<u32x4*>(sm.Vt + (2 * cp + 1) * PC + 8 * e8) = v1;
   }
   if (wave == 0) {
-    const float lgv = wave_scan(__logf(alpha[tok0 + lane]));
-    sm.lg[lane] = lgv;
+    sm.lg[lane] = wave_scan(__logf(alpha[tok0 + lane]));
     sm.bt[lane] = beta[tok0 + lane];
   }
   __syncthreads();
 
-  // ---- Gram k.k and scores q.k, row block = wave, lower tiles; L and A
+  // ---- Gram k.k and scores q.k: wave -> row block (w & 3), column blocks 2(w>>2)+{0,1}
   {
-    const int rb = wave;
+    const int rb = wave & 3;
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
+    for (int cc = 0; cc < 2; ++cc) {
+      const int cb = 2 * (wave >> 2) + cc;
       f32x4 g = {0.f, 0.f, 0.f, 0.f}, s = {0.f, 0.f, 0.f, 0.f};
       if (cb <= rb) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 kb = ld8(sm.K + (cb * 16 + l16) * PQ + ks * 32 + lq * 8);
-          g = mfma(ld8(sm.K + (rb * 16 + l16) * PQ + ks * 32 + lq * 8), kb, g);
-          s = mfma(ld8(sm.Q + (rb * 16 + l16) * PQ + ks * 32 + lq * 8), kb, s);
+          const bf16x8 kb = ld8(sm.u.in.K + (cb * 16 + l16) * PQ + ks * 32 + lq * 8);
+          g = mfma(ld8(sm.u.in.K + (rb * 16 + l16) * PQ + ks * 32 + lq * 8), kb, g);
+          s = mfma(ld8(sm.u.in.Q + (rb * 16 + l16) * PQ + ks * 32 + lq * 8), kb, s);
         }
       }
-      uint16_t* Aw = reinterpret_cast<uint16_t*>(wsc + kWsA);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = rb * 16 + lq * 4 + i, j = cb * 16 + l16;
         const float dec = j <= r ? __expf(sm.lg[r] - sm.lg[j]) : 0.f;
         sm.L[r * PF + j] = j < r ? sm.bt[r] * dec * g[i] : 0.f;
-        Aw[r * C + j] = f32_to_bf16(dec * s[i]);
+        sm.A[r * PC + j] = f32_to_bf16(dec * s[i]);
       }
     }
   }
   __syncthreads();
 
-  // ---- T = (I + L)^-1: diagonal 16 x 16 blocks by column forward substitution
+  // ---- T = (I + L)^-1: diagonal 16 x 16 blocks, one column per thread, in registers
   if (tid < 64) {
     const int b = tid >> 4, c = tid & 15, o = b * 16;
     float x[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
+      const f32x4* Lr = reinterpret_cast<const f32x4*>(sm.L + (o + i) * PF + o);
+      const f32x4 l0 = Lr[0], l1 = Lr[1], l2 = Lr[2], l3 = Lr[3];
+      const float li[16] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w,
+                            l2.x, l2.y, l2.z, l2.w, l3.x, l3.y, l3.z, l3.w};
       float s = i == c ? 1.f : 0.f;
 #pragma unroll
-      for (int j = 0; j < i; ++j) s -= sm.L[(o + i) * PF + o + j] * x[j];
+      for (int j = 0; j < i; ++j) s -= li[j] * x[j];
       x[i] = s;
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) sm.T[(o + i) * PF + o + c] = x[i];
   }
-  // zero the strictly upper blocks
-  for (int e = tid; e < C * C; e += 256) {
+  for (int e = tid; e < C * C; e += NT) {   // strictly upper blocks are zero
     const int r = e >> 6, c = e & 63;
     if ((c >> 4) > (r >> 4)) sm.T[r * PF + c] = 0.f;
   }
   __syncthreads();
   // block rows I = 1..3: M_J = sum_{K=J}^{I-1} L_IK T_KJ, then T_IJ = -D_I M_J
   for (int I = 1; I < 4; ++I) {
-    for (int e = tid; e < I * 256; e += 256) {
+    for (int e = tid; e < I * 256; e += NT) {
       const int J = e >> 8, i = (e >> 4) & 15, j = e & 15;
       float s = 0.f;
-      for (int kk = J * 16; kk < I * 16; ++kk) s += sm.L[(I * 16 + i) * PF + kk] * sm.T[kk * PF + J * 16 + j];
+      for (int kk = J * 16; kk < I * 16; kk += 4) {
+        const f32x4 lv = *reinterpret_cast<const f32x4*>(sm.L + (I * 16 + i) * PF + kk);
+        s += lv.x * sm.T[kk * PF + J * 16 + j] + lv.y * sm.T[(kk + 1) * PF + J * 16 + j] +
+             lv.z * sm.T[(kk + 2) * PF + J * 16 + j] + lv.w * sm.T[(kk + 3) * PF + J * 16 + j];
+      }
       sm.M[J * 272 + i * 17 + j] = s;
     }
     __syncthreads();
-    for (int e = tid; e < I * 256; e += 256) {
+    for (int e = tid; e < I * 256; e += NT) {
       const int J = e >> 8, i = (e >> 4) & 15, j = e & 15;
       float s = 0.f;
 #pragma unroll
@@ -172,38 +207,53 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(
     __syncthreads();
   }
 
-  // ---- T diag(beta g) and T diag(beta) in bf16
-  for (int e = tid; e < C * C; e += 256) {
-    const int r = e >> 6, j = e & 63;
-    const float t = sm.T[r * PF + j];
-    const float bj = sm.bt[j];
-    sm.Tw[r * PC + j] = f32_to_bf16(t * bj * __expf(sm.lg[j]));
-    sm.Tu[r * PC + j] = f32_to_bf16(t * bj);
+  // ---- T diag(beta g) and T diag(beta) in bf16 (pairs of columns)
+  for (int e = tid; e < C * C / 2; e += NT) {
+    const int r = e >> 5, j = 2 * (e & 31);
+    const f32x2 t = *reinterpret_cast<const f32x2*>(sm.T + r * PF + j);
+    const float b0 = sm.bt[j], b1 = sm.bt[j + 1];
+    *reinterpret_cast<unsigned*>(sm.Tw + r * PC + j) =
+        pack_bf16(t.x * b0 * __expf(sm.lg[j]), t.y * b1 * __expf(sm.lg[j + 1]));
+    *reinterpret_cast<unsigned*>(sm.Tu + r * PC + j) = pack_bf16(t.x * b0, t.y * b1);
   }
   __syncthreads();
 
-  // ---- W = Tw K, U~ = Tu V: row block = wave, 8 column blocks, K = 64
+  // ---- W = Tw K, U~ = Tu V: wave -> row block (w & 3), column blocks 4(w>>2)..+4; staged
   {
-    const int rb = wave;
-    uint16_t* Ww = reinterpret_cast<uint16_t*>(wsc + kWsW);
-    uint16_t* Uw = reinterpret_cast<uint16_t*>(wsc + kWsU);
+    const int rb = wave & 3;
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb) {
-      f32x4 w = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
+    for (int cc = 0; cc < 4; ++cc) {
+      const int cb = 4 * (wave >> 2) + cc;
+      f32x4 w = {0.f, 0.f, 0.f, 0.f}, uu = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int js = 0; js < 2; ++js) {
         w = mfma(ld8(sm.Tw + (rb * 16 + l16) * PC + js * 32 + lq * 8),
                  ld8(sm.Kt + (cb * 16 + l16) * PC + js * 32 + lq * 8), w);
-        u = mfma(ld8(sm.Tu + (rb * 16 + l16) * PC + js * 32 + lq * 8),
-                 ld8(sm.Vt + (cb * 16 + l16) * PC + js * 32 + lq * 8), u);
+        uu = mfma(ld8(sm.Tu + (rb * 16 + l16) * PC + js * 32 + lq * 8),
+                  ld8(sm.Vt + (cb * 16 + l16) * PC + js * 32 + lq * 8), uu);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = rb * 16 + lq * 4 + i, c = cb * 16 + l16;
-        Ww[r * kD + c] = f32_to_bf16(w[i]);
-        Uw[r * kD + c] = f32_to_bf16(u[i]);
+        sm.u.out.W[r * PQ + c] = f32_to_bf16(w[i]);
+        sm.u.out.U[r * PQ + c] = f32_to_bf16(uu[i]);
       }
     }
+  }
+  __syncthreads();
+  // ---- W, U~, A to the workspace with 16-byte stores
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int p = tid + NT * i, row = p >> 4, seg = p & 15;
+    *reinterpret_cast<u32x4*>(wsc + kWsW + (size_t)(row * kD + seg * 8) * 2) =
+        *reinterpret_cast<const u32x4*>(sm.u.out.W + row * PQ + seg * 8);
+    *reinterpret_cast<u32x4*>(wsc + kWsU + (size_t)(row * kD + seg * 8) * 2) =
+        *reinterpret_cast<const u32x4*>(sm.u.out.U + row * PQ + seg * 8);
+  }
+  {
+    const int row = tid >> 3, seg = tid & 7;
+    *reinterpret_cast<u32x4*>(wsc + kWsA + (size_t)(row * C + seg * 8) * 2) =
+        *reinterpret_cast<const u32x4*>(sm.A + row * PC + seg * 8);
   }
 }
 
@@ -216,48 +266,57 @@ struct SeqSmem {
   uint16_t Qg[C * PQ];     // diag(g) Q   [r][k]
   uint16_t Kht[kD * PC];   // (diag(g_C/g) K)^T  [k][j]
   uint16_t A[C * PC];      // [r][j]
-  uint16_t Sb[VT * PQ];    // bf16 state tile [v][k]
+  uint16_t Sb[2][VT * PQ]; // bf16 state tile [v][k], double buffered
   uint16_t Ut[VT * PC];    // U^T tile [v][j]
-  float g[C];              // cumulative log-decay of the chunk
 };
 
-}  // namespace gdc
-
-// one chunk's inputs of the sequential pass, held in registers while the previous
-// chunk computes: W, q, k (64 x 128 bf16, 4 x 16 bytes per thread), A (2 x 16 bytes),
-// alpha (lanes of wave 0)
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));   // register-promotable across loops
+// One chunk's inputs of the sequential pass, held in registers while the previous
+// chunk computes: two 16-byte pieces of W and one of A; q and k pairs of key
+// channels (2cp, 2cp+1) for tokens [8e, 8e+8); alpha of token `lane`; and, for the
+// waves that form U, the U~ tile entries in accumulator layout.
+template <int NVB>
 struct Prefetch {
-  u32x4 w[4], q[4], k[4], a[2];
+  u32x4 w[2], a;
+  unsigned q[8], k[8];
   float al;
+  f32x4 ut;
 };
 
-__device__ __forceinline__ void fetch_chunk(Prefetch& pf, const uint16_t* __restrict__ q,
+template <int VT>
+__device__ __forceinline__ void fetch_chunk(Prefetch<VT / 16>& pf, const uint16_t* __restrict__ q,
                                             const uint16_t* __restrict__ k,
                                             const float* __restrict__ alpha,
                                             const uint8_t* __restrict__ ws, int n, int nc, int ci,
-                                            int T) {
-  using namespace gdc;
-  const int tid = threadIdx.x;
+                                            int T, int v0) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cp = tid & 63, e8 = tid >> 6, l16 = lane & 15, lq = lane >> 4;
   const size_t tok0 = (size_t)n * T + (size_t)ci * C;
   const uint8_t* wsc = ws + ((size_t)n * nc + ci) * kWsChunk;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int p = tid + 256 * i, row = p >> 4, seg = p & 15;
-    pf.w[i] = *reinterpret_cast<const u32x4*>(wsc + kWsW + (size_t)(row * kD + seg * 8) * 2);
-    pf.q[i] = *reinterpret_cast<const u32x4*>(q + (tok0 + row) * kD + seg * 8);
-    pf.k[i] = *reinterpret_cast<const u32x4*>(k + (tok0 + row) * kD + seg * 8);
-  }
-#pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int p = tid + 256 * i, row = p >> 3, seg = p & 7;
-    pf.a[i] = *reinterpret_cast<const u32x4*>(wsc + kWsA + (size_t)(row * C + seg * 8) * 2);
+    const int p = tid + NT * i, row = p >> 4, seg = p & 15;
+    pf.w[i] = *reinterpret_cast<const u32x4*>(wsc + kWsW + (size_t)(row * kD + seg * 8) * 2);
   }
-  pf.al = tid < C ? alpha[tok0 + tid] : 1.f;
+  pf.a = *reinterpret_cast<const u32x4*>(wsc + kWsA + (size_t)((tid >> 3) * C + (tid & 7) * 8) * 2);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const size_t off = (tok0 + 8 * e8 + i) * kD + 2 * cp;
+    pf.q[i] = *reinterpret_cast<const unsigned*>(q + off);
+    pf.k[i] = *reinterpret_cast<const unsigned*>(k + off);
+  }
+  pf.al = alpha[tok0 + lane];
+  if (wave < 4 * (VT / 16)) {
+    const int rb = wave & 3, vb = wave >> 2;
+    const uint16_t* Uw = reinterpret_cast<const uint16_t*>(wsc + kWsU);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pf.ut[i] = bf16_to_f32(Uw[(rb * 16 + lq * 4 + i) * kD + v0 + vb * 16 + l16]);
+  }
 }
 
+}  // namespace gdc
+
 template <int VT>
-__global__ __launch_bounds__(256) void gdn_chunk_seq_kernel(
+__global__ __launch_bounds__(512) void gdn_chunk_seq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ alpha,
     const uint8_t* __restrict__ ws, const float* __restrict__ S0, float* __restrict__ ST,
     uint16_t* __restrict__ o, int N, int T) {
@@ -267,144 +326,115 @@ __global__ __launch_bounds__(256) void gdn_chunk_seq_kernel(
   __shared__ SeqSmem<VT> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lq = lane >> 4;
+  const int cp = tid & 63, e8 = tid >> 6;
   const int n = blockIdx.x / TPS, vt = blockIdx.x % TPS, v0 = vt * VT;
   const int nc = T / C;
+  const int kcol = wave * 16 + l16;      // key column of this wave's state tiles
 
-  // state tiles: value blocks vb < NVB x key blocks {2w, 2w+1}
-  f32x4 Sacc[NVB][2];
+  // state tiles: key block = wave, value blocks vb < NVB; lane holds
+  // S[v0 + vb*16 + lq*4 + i][kcol]
+  f32x4 Sacc[NVB];
 #pragma unroll
   for (int vb = 0; vb < NVB; ++vb)
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int kc = (2 * wave + kk) * 16 + l16;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        Sacc[vb][kk][i] = S0 ? S0[((size_t)n * kD + v0 + vb * 16 + lq * 4 + i) * kD + kc] : 0.f;
+    for (int i = 0; i < 4; ++i) {
+      Sacc[vb][i] = S0 ? S0[((size_t)n * kD + v0 + vb * 16 + lq * 4 + i) * kD + kcol] : 0.f;
+      sm.Sb[0][(vb * 16 + lq * 4 + i) * PQ + kcol] = f32_to_bf16(Sacc[vb][i]);
     }
 
-  // prefetch registers for one chunk
-  Prefetch pf;
-  if (nc > 0) fetch_chunk(pf, q, k, alpha, ws, n, nc, 0, T);
-
+  Prefetch<NVB> pf;
+  if (nc > 0) fetch_chunk<VT>(pf, q, k, alpha, ws, n, nc, 0, T, v0);
+  int cur = 0;
   for (int ci = 0; ci < nc; ++ci) {
     const size_t tok0 = (size_t)n * T + (size_t)ci * C;
-    const uint8_t* wsc = ws + ((size_t)n * nc + ci) * kWsChunk;
-    // ---- decays of this chunk
-    if (wave == 0) sm.g[lane] = wave_scan(__logf(pf.al));   // cumulative log-decay
-    // U~ tile straight into the accumulator layout (row block = wave)
-    f32x4 Ut_acc[NVB];
+    // ---- E: cumulative log-decays (every wave for itself), operands to LDS
+    const float lgl = wave_scan(__logf(pf.al));
+    const float lC = __shfl(lgl, C - 1);
+    const float gC = __expf(lC);
     {
-      const uint16_t* Uw = reinterpret_cast<const uint16_t*>(wsc + kWsU);
+      float kh0[8], kh1[8];
 #pragma unroll
-      for (int vb = 0; vb < NVB; ++vb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          Ut_acc[vb][i] = bf16_to_f32(Uw[(wave * 16 + lq * 4 + i) * kD + v0 + vb * 16 + l16]);
-    }
-    // bf16 copy of the state tile
-#pragma unroll
-    for (int vb = 0; vb < NVB; ++vb)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int kc = (2 * wave + kk) * 16 + l16;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sm.Sb[(vb * 16 + lq * 4 + i) * PQ + kc] = f32_to_bf16(Sacc[vb][kk][i]);
+      for (int i = 0; i < 8; ++i) {
+        const int r = 8 * e8 + i;
+        const float lr = __shfl(lgl, r);
+        const float gr = __expf(lr), kr = __expf(lC - lr);
+        *reinterpret_cast<unsigned*>(sm.Qg + r * PQ + 2 * cp) =
+            pack_bf16(gr * lo_bf(pf.q[i]), gr * hi_bf(pf.q[i]));
+        kh0[i] = kr * lo_bf(pf.k[i]);
+        kh1[i] = kr * hi_bf(pf.k[i]);
       }
-    // W and A to LDS as they are
+      u32x4 w0, w1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int p = tid + 256 * i, row = p >> 4, seg = p & 15;
-      *reinterpret_cast<u32x4*>(sm.W + row * PQ + seg * 8) = pf.w[i];
+      for (int i = 0; i < 4; ++i) {
+        w0[i] = pack_bf16(kh0[2 * i], kh0[2 * i + 1]);
+        w1[i] = pack_bf16(kh1[2 * i], kh1[2 * i + 1]);
+      }
+      *reinterpret_cast<u32x4*>(sm.Kht + (2 * cp) * PC + 8 * e8) = w0;
+      *reinterpret_cast<u32x4*>(sm.Kht + (2 * cp + 1) * PC + 8 * e8) = w1;
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int p = tid + 256 * i, row = p >> 3, seg = p & 7;
-      *reinterpret_cast<u32x4*>(sm.A + row * PC + seg * 8) = pf.a[i];
+      const int p = tid + NT * i, row = p >> 4, seg = p & 15;
+      *reinterpret_cast<u32x4*>(sm.W + row * PQ + seg * 8) = pf.w[i];
     }
-    __syncthreads();   // g ready
-    // diag(g) Q and (diag(g_C/g) K)^T, from cumulative log-decays
-    {
-      const float lC = sm.g[C - 1];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int p = tid + 256 * i, row = p >> 4, seg = p & 15;
-        const float gr = __expf(sm.g[row]), kr = __expf(lC - sm.g[row]);
-        const u32x4 q4 = pf.q[i], k4 = pf.k[i];
-        uint32_t out[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint16_t lo = f32_to_bf16(gr * __uint_as_float(q4[e] << 16));
-          const uint16_t hi = f32_to_bf16(gr * __uint_as_float(q4[e] & 0xffff0000u));
-          out[e] = uint32_t(lo) | (uint32_t(hi) << 16);
-          sm.Kht[(seg * 8 + 2 * e) * PC + row] = f32_to_bf16(kr * __uint_as_float(k4[e] << 16));
-          sm.Kht[(seg * 8 + 2 * e + 1) * PC + row] = f32_to_bf16(kr * __uint_as_float(k4[e] & 0xffff0000u));
-        }
-        *reinterpret_cast<u32x4*>(sm.Qg + row * PQ + seg * 8) = u32x4{out[0], out[1], out[2], out[3]};
-      }
-    }
-    if (ci + 1 < nc) fetch_chunk(pf, q, k, alpha, ws, n, nc, ci + 1, T);   // overlaps the MFMA work below
+    *reinterpret_cast<u32x4*>(sm.A + (tid >> 3) * PC + (tid & 7) * 8) = pf.a;
+    const f32x4 ut = pf.ut;
     __syncthreads();
+    if (ci + 1 < nc) fetch_chunk<VT>(pf, q, k, alpha, ws, n, nc, ci + 1, T, v0);   // overlaps below
 
-    // ---- U = U~ - W S^T (row block = wave), to LDS transposed
-#pragma unroll
-    for (int vb = 0; vb < NVB; ++vb) {
+    // ---- U = U~ - W S^T: wave -> (row block w & 3, value block w >> 2); to LDS transposed
+    if (wave < 4 * NVB) {
+      const int rb = wave & 3, vb = wave >> 2;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        acc = mfma(ld8(sm.W + (wave * 16 + l16) * PQ + ks * 32 + lq * 8),
-                   ld8(sm.Sb + (vb * 16 + l16) * PQ + ks * 32 + lq * 8), acc);
+        acc = mfma(ld8(sm.W + (rb * 16 + l16) * PQ + ks * 32 + lq * 8),
+                   ld8(sm.Sb[cur] + (vb * 16 + l16) * PQ + ks * 32 + lq * 8), acc);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        sm.Ut[(vb * 16 + l16) * PC + wave * 16 + lq * 4 + i] = f32_to_bf16(Ut_acc[vb][i] - acc[i]);
+        sm.Ut[(vb * 16 + l16) * PC + rb * 16 + lq * 4 + i] = f32_to_bf16(ut[i] - acc[i]);
     }
     __syncthreads();
 
-    // ---- O = diag(g) Q S^T + A U (row block = wave)
-#pragma unroll
-    for (int vb = 0; vb < NVB; ++vb) {
+    // ---- O = diag(g) Q S^T + A U (same tile assignment)
+    if (wave < 4 * NVB) {
+      const int rb = wave & 3, vb = wave >> 2;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        acc = mfma(ld8(sm.Qg + (wave * 16 + l16) * PQ + ks * 32 + lq * 8),
-                   ld8(sm.Sb + (vb * 16 + l16) * PQ + ks * 32 + lq * 8), acc);
+        acc = mfma(ld8(sm.Qg + (rb * 16 + l16) * PQ + ks * 32 + lq * 8),
+                   ld8(sm.Sb[cur] + (vb * 16 + l16) * PQ + ks * 32 + lq * 8), acc);
 #pragma unroll
       for (int js = 0; js < 2; ++js)
-        if (js * 32 <= wave * 16 + 15)
-          acc = mfma(ld8(sm.A + (wave * 16 + l16) * PC + js * 32 + lq * 8),
+        if (js * 32 <= rb * 16 + 15)
+          acc = mfma(ld8(sm.A + (rb * 16 + l16) * PC + js * 32 + lq * 8),
                      ld8(sm.Ut + (vb * 16 + l16) * PC + js * 32 + lq * 8), acc);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        o[(tok0 + wave * 16 + lq * 4 + i) * kD + v0 + vb * 16 + l16] = f32_to_bf16(acc[i]);
+        o[(tok0 + rb * 16 + lq * 4 + i) * kD + v0 + vb * 16 + l16] = f32_to_bf16(acc[i]);
     }
 
-    // ---- S <- g_C S + U^T (diag(g_C/g) K)
-    {
-      const float gC = __expf(sm.g[C - 1]);
+    // ---- S <- g_C S + U^T (diag(g_C/g) K): key block = wave; next bf16 copy
 #pragma unroll
-      for (int vb = 0; vb < NVB; ++vb)
+    for (int vb = 0; vb < NVB; ++vb) {
+      f32x4 acc = Sacc[vb] * gC;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const int kb = 2 * wave + kk;
-          f32x4 acc = Sacc[vb][kk] * gC;
+      for (int js = 0; js < 2; ++js)
+        acc = mfma(ld8(sm.Ut + (vb * 16 + l16) * PC + js * 32 + lq * 8),
+                   ld8(sm.Kht + (wave * 16 + l16) * PC + js * 32 + lq * 8), acc);
+      Sacc[vb] = acc;
 #pragma unroll
-          for (int js = 0; js < 2; ++js)
-            acc = mfma(ld8(sm.Ut + (vb * 16 + l16) * PC + js * 32 + lq * 8),
-                       ld8(sm.Kht + (kb * 16 + l16) * PC + js * 32 + lq * 8), acc);
-          Sacc[vb][kk] = acc;
-        }
+      for (int i = 0; i < 4; ++i) sm.Sb[cur ^ 1][(vb * 16 + lq * 4 + i) * PQ + kcol] = f32_to_bf16(acc[i]);
     }
+    cur ^= 1;
     __syncthreads();
   }
 
 #pragma unroll
   for (int vb = 0; vb < NVB; ++vb)
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int kc = (2 * wave + kk) * 16 + l16;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        ST[((size_t)n * kD + v0 + vb * 16 + lq * 4 + i) * kD + kc] = Sacc[vb][kk][i];
-    }
+    for (int i = 0; i < 4; ++i)
+      ST[((size_t)n * kD + v0 + vb * 16 + lq * 4 + i) * kD + kcol] = Sacc[vb][i];
 }
 
 }  // namespace gdnrt
@@ -450,7 +480,7 @@ extern "C" int gdn_chunk_fwd(const void* q, const void* k, const void* v, const 
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   if (T > 0) {
-    hipLaunchKernelGGL(gdn_chunk_prep_kernel, dim3((unsigned)(N * (T / kChunk))), dim3(256), 0, s,
+    hipLaunchKernelGGL(gdn_chunk_prep_kernel, dim3((unsigned)(N * (T / kChunk))), dim3(gdc::NT), 0, s,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), alpha, beta, ws, T);
     int rc = check_launch("gdn_chunk_fwd (prep)");
@@ -458,11 +488,11 @@ extern "C" int gdn_chunk_fwd(const void* q, const void* k, const void* v, const 
   }
   // value tiles of 16 when there are too few sequences to fill the chip with 32
   if (N * 4 < 256)
-    hipLaunchKernelGGL((gdn_chunk_seq_kernel<16>), dim3((unsigned)(N * 8)), dim3(256), 0, s,
+    hipLaunchKernelGGL((gdn_chunk_seq_kernel<16>), dim3((unsigned)(N * 8)), dim3(gdc::NT), 0, s,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), alpha, ws,
                        S0, ST, static_cast<uint16_t*>(o), N, T);
   else
-    hipLaunchKernelGGL((gdn_chunk_seq_kernel<32>), dim3((unsigned)(N * 4)), dim3(256), 0, s,
+    hipLaunchKernelGGL((gdn_chunk_seq_kernel<32>), dim3((unsigned)(N * 4)), dim3(gdc::NT), 0, s,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), alpha, ws,
                        S0, ST, static_cast<uint16_t*>(o), N, T);
   return check_launch("gdn_chunk_fwd");
