@@ -97,6 +97,16 @@ __device__ __forceinline__ float sum64(float x) {
   return x;
 }
 
+// Workgroup barrier that orders LDS only. __syncthreads() also fences global
+// memory, which makes the compiler wait for every outstanding global load -- the
+// register prefetches included -- at each barrier. The kernels here exchange data
+// between threads only through LDS, so an LDS-scoped fence suffices.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <typename T> struct io_traits;
 template <> struct io_traits<float> {
   __device__ static __forceinline__ float ld(const float* p, size_t i) { return p[i]; }

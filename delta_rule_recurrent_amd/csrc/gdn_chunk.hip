@@ -133,7 +133,7 @@ __global__ __launch_bounds__(512) void gdn_chunk_prep_kernel(
     sm.lg[lane] = wave_scan(__logf(alpha[tok0 + lane]));
     sm.bt[lane] = beta[tok0 + lane];
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- Gram k.k and scores q.k: wave -> row block (w & 3), column blocks 2(w>>2)+{0,1}
   {
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(512) void gdn_chunk_prep_kernel(
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- T = (I + L)^-1: diagonal 16 x 16 blocks, one column per thread, in registers
   if (tid < 64) {
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(512) void gdn_chunk_prep_kernel(
     const int r = e >> 6, c = e & 63;
     if ((c >> 4) > (r >> 4)) sm.T[r * PF + c] = 0.f;
   }
-  __syncthreads();
+  lds_barrier();
   // block rows I = 1..3: M_J = sum_{K=J}^{I-1} L_IK T_KJ, then T_IJ = -D_I M_J
   for (int I = 1; I < 4; ++I) {
     for (int e = tid; e < I * 256; e += NT) {
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(512) void gdn_chunk_prep_kernel(
       }
       sm.M[J * 272 + i * 17 + j] = s;
     }
-    __syncthreads();
+    lds_barrier();
     for (int e = tid; e < I * 256; e += NT) {
       const int J = e >> 8, i = (e >> 4) & 15, j = e & 15;
       float s = 0.f;
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(512) void gdn_chunk_prep_kernel(
       for (int kk = 0; kk < 16; ++kk) s -= sm.T[(I * 16 + i) * PF + I * 16 + kk] * sm.M[J * 272 + kk * 17 + j];
       sm.T[(I * 16 + i) * PF + J * 16 + j] = s;
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   // ---- T diag(beta g) and T diag(beta) in bf16 (pairs of columns)
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(512) void gdn_chunk_prep_kernel(
         pack_bf16(t.x * b0 * __expf(sm.lg[j]), t.y * b1 * __expf(sm.lg[j + 1]));
     *reinterpret_cast<unsigned*>(sm.Tu + r * PC + j) = pack_bf16(t.x * b0, t.y * b1);
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- W = Tw K, U~ = Tu V: wave -> row block (w & 3), column blocks 4(w>>2)..+4; staged
   {
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(512) void gdn_chunk_prep_kernel(
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
   // ---- W, U~, A to the workspace with 16-byte stores
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -315,37 +315,24 @@ __device__ __forceinline__ void fetch_chunk(Prefetch<VT / 16>& pf, const uint16_
 
 }  // namespace gdc
 
+// One chunk of the sequential pass: starts the loads of the next chunk into `nx`,
+// then consumes `pf` (this chunk's inputs).
 template <int VT>
-__global__ __launch_bounds__(512) void gdn_chunk_seq_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ alpha,
-    const uint8_t* __restrict__ ws, const float* __restrict__ S0, float* __restrict__ ST,
-    uint16_t* __restrict__ o, int N, int T) {
+__device__ __forceinline__ void gdn_seq_chunk(gdc::SeqSmem<VT>& sm, gdc::Prefetch<VT / 16>& pf,
+                                              gdc::Prefetch<VT / 16>& nx, f32x4 (&Sacc)[VT / 16],
+                                              int& cur, int ci, int nc, int n, int T, int v0,
+                                              const uint16_t* __restrict__ q,
+                                              const uint16_t* __restrict__ k,
+                                              const float* __restrict__ alpha,
+                                              const uint8_t* __restrict__ ws,
+                                              uint16_t* __restrict__ o) {
   using namespace gdc;
-  constexpr int NVB = VT / 16;           // value blocks in the tile
-  constexpr int TPS = kD / VT;           // tiles per sequence
-  __shared__ SeqSmem<VT> sm;
+  constexpr int NVB = VT / 16;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lq = lane >> 4;
   const int cp = tid & 63, e8 = tid >> 6;
-  const int n = blockIdx.x / TPS, vt = blockIdx.x % TPS, v0 = vt * VT;
-  const int nc = T / C;
-  const int kcol = wave * 16 + l16;      // key column of this wave's state tiles
-
-  // state tiles: key block = wave, value blocks vb < NVB; lane holds
-  // S[v0 + vb*16 + lq*4 + i][kcol]
-  f32x4 Sacc[NVB];
-#pragma unroll
-  for (int vb = 0; vb < NVB; ++vb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      Sacc[vb][i] = S0 ? S0[((size_t)n * kD + v0 + vb * 16 + lq * 4 + i) * kD + kcol] : 0.f;
-      sm.Sb[0][(vb * 16 + lq * 4 + i) * PQ + kcol] = f32_to_bf16(Sacc[vb][i]);
-    }
-
-  Prefetch<NVB> pf;
-  if (nc > 0) fetch_chunk<VT>(pf, q, k, alpha, ws, n, nc, 0, T, v0);
-  int cur = 0;
-  for (int ci = 0; ci < nc; ++ci) {
+  const int kcol = wave * 16 + l16;
+  if (ci + 1 < nc) fetch_chunk<VT>(nx, q, k, alpha, ws, n, nc, ci + 1, T, v0);
     const size_t tok0 = (size_t)n * T + (size_t)ci * C;
     // ---- E: cumulative log-decays (every wave for itself), operands to LDS
     const float lgl = wave_scan(__logf(pf.al));
@@ -379,8 +366,7 @@ __global__ __launch_bounds__(512) void gdn_chunk_seq_kernel(
     }
     *reinterpret_cast<u32x4*>(sm.A + (tid >> 3) * PC + (tid & 7) * 8) = pf.a;
     const f32x4 ut = pf.ut;
-    __syncthreads();
-    if (ci + 1 < nc) fetch_chunk<VT>(pf, q, k, alpha, ws, n, nc, ci + 1, T, v0);   // overlaps below
+    lds_barrier();
 
     // ---- U = U~ - W S^T: wave -> (row block w & 3, value block w >> 2); to LDS transposed
     if (wave < 4 * NVB) {
@@ -394,7 +380,7 @@ __global__ __launch_bounds__(512) void gdn_chunk_seq_kernel(
       for (int i = 0; i < 4; ++i)
         sm.Ut[(vb * 16 + l16) * PC + rb * 16 + lq * 4 + i] = f32_to_bf16(ut[i] - acc[i]);
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- O = diag(g) Q S^T + A U (same tile assignment)
     if (wave < 4 * NVB) {
@@ -427,7 +413,42 @@ __global__ __launch_bounds__(512) void gdn_chunk_seq_kernel(
       for (int i = 0; i < 4; ++i) sm.Sb[cur ^ 1][(vb * 16 + lq * 4 + i) * PQ + kcol] = f32_to_bf16(acc[i]);
     }
     cur ^= 1;
-    __syncthreads();
+    lds_barrier();
+}
+
+template <int VT>
+__global__ __launch_bounds__(512) void gdn_chunk_seq_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ alpha,
+    const uint8_t* __restrict__ ws, const float* __restrict__ S0, float* __restrict__ ST,
+    uint16_t* __restrict__ o, int N, int T) {
+  using namespace gdc;
+  constexpr int NVB = VT / 16;           // value blocks in the tile
+  constexpr int TPS = kD / VT;           // tiles per sequence
+  __shared__ SeqSmem<VT> sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int cp = tid & 63, e8 = tid >> 6;
+  const int n = blockIdx.x / TPS, vt = blockIdx.x % TPS, v0 = vt * VT;
+  const int nc = T / C;
+  const int kcol = wave * 16 + l16;      // key column of this wave's state tiles
+
+  // state tiles: key block = wave, value blocks vb < NVB; lane holds
+  // S[v0 + vb*16 + lq*4 + i][kcol]
+  f32x4 Sacc[NVB];
+#pragma unroll
+  for (int vb = 0; vb < NVB; ++vb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      Sacc[vb][i] = S0 ? S0[((size_t)n * kD + v0 + vb * 16 + lq * 4 + i) * kD + kcol] : 0.f;
+      sm.Sb[0][(vb * 16 + lq * 4 + i) * PQ + kcol] = f32_to_bf16(Sacc[vb][i]);
+    }
+
+  Prefetch<NVB> pa, pb;
+  if (nc > 0) fetch_chunk<VT>(pa, q, k, alpha, ws, n, nc, 0, T, v0);
+  int cur = 0;
+  for (int ci = 0; ci < nc; ci += 2) {
+    gdn_seq_chunk<VT>(sm, pa, pb, Sacc, cur, ci, nc, n, T, v0, q, k, alpha, ws, o);
+    if (ci + 1 < nc) gdn_seq_chunk<VT>(sm, pb, pa, Sacc, cur, ci + 1, nc, n, T, v0, q, k, alpha, ws, o);
   }
 
 #pragma unroll

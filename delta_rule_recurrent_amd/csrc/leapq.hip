@@ -120,7 +120,7 @@ __global__ __launch_bounds__(256) void leapq_decode_kernel(
     s_g[m] = g;
     buf_a[(size_t)head * window + m] = a;
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- per-head dot products
 #pragma unroll
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(256) void leapq_decode_kernel(
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- this row
   const uint32_t zz[16] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w,
@@ -271,7 +271,7 @@ __device__ void cholqr_pass(const float* src, float* dst) {
       dst[t * kMaxRank + j] = x[j];
     }
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 template <int NQ, int RANK>
@@ -306,7 +306,7 @@ __global__ __launch_bounds__(128 * NQ) void leapq_flush_kernel(
                          : buf_k[((size_t)head * window + (j - rank)) * kD + c];
     }
     if (tid < kD) sm.col[tid] = ksmooth[hk + tid];
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int i = 0; i < FC; ++i) S[i] = 0.f;
     const float* ba = buf_a + (size_t)head * window;
@@ -350,7 +350,7 @@ __global__ __launch_bounds__(128 * NQ) void leapq_flush_kernel(
   // ---------------------------------------------------------------- compensators
   if constexpr (RANK > 0) {
     for (int i = tid; i < kD * rank; i += NT) sm.Qa[(i / rank) * kMaxRank + (i % rank)] = q0[i];
-    __syncthreads();
+    lds_barrier();
     for (int it = 0; it <= iters; ++it) {
       // Y = S Q from the registers
       float acc[RANK];
@@ -364,9 +364,9 @@ __global__ __launch_bounds__(128 * NQ) void leapq_flush_kernel(
       }
 #pragma unroll
       for (int r = 0; r < RANK; ++r) sm.part[(qd * kD + v) * kMaxRank + r] = acc[r];
-      __syncthreads();
+      lds_barrier();
       combine_parts<NQ, RANK>(sm, sm.Y);
-      __syncthreads();
+      lds_barrier();
       if (it == iters) break;   // final Y = S Q: the compensator values
       // Q = S^T Y from the LDS copy: column c = v over rows [c0, c0 + FC)
 #pragma unroll
@@ -381,9 +381,9 @@ __global__ __launch_bounds__(128 * NQ) void leapq_flush_kernel(
       }
 #pragma unroll
       for (int r = 0; r < RANK; ++r) sm.part[(qd * kD + v) * kMaxRank + r] = acc[r];
-      __syncthreads();
+      lds_barrier();
       combine_parts<NQ, RANK>(sm, sm.Qa);
-      __syncthreads();
+      lds_barrier();
       cholqr_pass<RANK>(sm.Qa, sm.Qb);
       cholqr_pass<RANK>(sm.Qb, sm.Qa);
     }
@@ -398,7 +398,7 @@ __global__ __launch_bounds__(128 * NQ) void leapq_flush_kernel(
         sm.part[tid * kMaxRank + r] = h2f(hy);
       }
     }
-    __syncthreads();
+    lds_barrier();
     // residual R = S - sum_r uh_r kh_r^T
     float yh[RANK];
 #pragma unroll
@@ -411,7 +411,7 @@ __global__ __launch_bounds__(128 * NQ) void leapq_flush_kernel(
       sm.S[v * kP + c0 + i] = S[i];
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---------------------------------------------------------------- smoothing
   {
@@ -422,7 +422,7 @@ __global__ __launch_bounds__(128 * NQ) void leapq_flush_kernel(
       acc += smooth_mode == 1 ? x * x : fabsf(x);
     }
     sm.red[qd * kD + v] = acc;
-    __syncthreads();
+    lds_barrier();
     if (tid < kD) {
       float tot = 0.f;
 #pragma unroll
@@ -431,7 +431,7 @@ __global__ __launch_bounds__(128 * NQ) void leapq_flush_kernel(
       ksmooth[hk + tid] = cf;
       sm.col[tid] = 1.0f / cf;
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   // ---------------------------------------------------------------- scales, codes
@@ -443,7 +443,7 @@ __global__ __launch_bounds__(128 * NQ) void leapq_flush_kernel(
       mx = fmaxf(mx, fabsf(S[i]));
     }
     sm.red[qd * kD + v] = mx;
-    __syncthreads();
+    lds_barrier();
     float s = 0.f;
 #pragma unroll
     for (int p = 0; p < NQ; ++p) s = fmaxf(s, sm.red[p * kD + v]);

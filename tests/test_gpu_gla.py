@@ -22,8 +22,9 @@ def _run_ref(inp, idx, T=None):
                              np64(inp["log_g"][idx, sl]), np64(inp["S0"][idx]))
 
 
-@pytest.mark.parametrize("N,T", [(3, 320), (8, 128), (1, 64)])
+@pytest.mark.parametrize("N,T", [(3, 320), (8, 128), (1, 64), (64, 192)])
 def test_small_ragged(N, T):
+    """Ragged sequence counts (XCD placement only when N % 8 == 0)."""
     dev = need_gpu()
     say(f"gla_chunk_fwd: N={N} T={T}")
     inp = synth.gla_prefill(B=N, H=1, T=T, device="cpu", seed=500 + N)
