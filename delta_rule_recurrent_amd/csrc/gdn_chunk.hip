@@ -12,13 +12,14 @@
 //   O   = diag(g) Q S_0^T + A U,            A[r,j] = (g_r/g_j) q_r.k_j for j <= r, else 0,
 //   S_C = g_C S_0 + U^T diag(g_C/g) K.
 //
-// W, U~ and A do not depend on the state. A first kernel forms them for every
-// chunk in parallel (Gram and score products on bf16 MFMA, the triangular inverse in
-// fp32 by 16 x 16 diagonal blocks and block rows) and writes them, bf16, to the
-// caller's workspace. A second kernel walks the chunks of each sequence in order for
-// a tile of value channels (the value rows of U and S are independent) with only
-// MFMA work per chunk, its state tile in fp32 accumulators, and the next chunk's
-// inputs prefetched into registers.
+// W, U~, A, diag(g) Q and diag(g_C/g) K do not depend on the state. A first kernel
+// forms them for every chunk in parallel (Gram and score products on bf16 MFMA, the
+// triangular inverse in fp32 by 16 x 16 diagonal blocks and block rows) and writes
+// them, bf16, to the caller's workspace. A second kernel walks the chunks of each
+// sequence in order for a tile of value channels (the value rows of U and S are
+// independent): per chunk it only copies the prepared operands into LDS and runs
+// MFMA, its state tile in fp32 accumulators, the next chunk's operands prefetched
+// into registers.
 #include "common.hpp"
 
 namespace gdnrt {
@@ -31,9 +32,11 @@ constexpr int PQ = kD + 8;  // bf16 pitch of 128-wide rows (16-byte aligned, con
 constexpr int PC = C + 8;   // bf16 pitch of 64-wide rows
 constexpr int PF = C + 4;   // fp32 pitch of 64-wide rows (16-byte aligned)
 
-// workspace per chunk: W [64][128] bf16, U~ [64][128] bf16, A [64][64] bf16
+// workspace per chunk, all bf16: W [64][128], U~ [64][128], A [64][64],
+// diag(g) Q [64][128] and (diag(g_C/g) K)^T [128][64]
 constexpr size_t kWsW = 0, kWsU = (size_t)C * kD * 2, kWsA = 2 * (size_t)C * kD * 2;
-constexpr size_t kWsChunk = kWsA + (size_t)C * C * 2;   // 40,960 bytes
+constexpr size_t kWsQ = kWsA + (size_t)C * C * 2, kWsK = kWsQ + (size_t)C * kD * 2;
+constexpr size_t kWsChunk = kWsK + (size_t)kD * C * 2;   // 73,728 bytes
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));   // register-promotable across loops
 
@@ -134,6 +137,34 @@ __global__ __launch_bounds__(512) void gdn_chunk_prep_kernel(
     sm.bt[lane] = beta[tok0 + lane];
   }
   lds_barrier();
+
+  // ---- the sequential pass's decayed operands: diag(g) Q and (diag(g_C/g) K)^T,
+  // this thread's key channels (2cp, 2cp+1) of tokens [8e, 8e+8), from LDS
+  {
+    const float lC = sm.lg[C - 1];
+    uint16_t* Qw = reinterpret_cast<uint16_t*>(wsc + kWsQ);
+    uint16_t* Kw = reinterpret_cast<uint16_t*>(wsc + kWsK);
+    float kh0[8], kh1[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 8 * e8 + i;
+      const float lr = sm.lg[r];
+      const float gr = __expf(lr), kr = __expf(lC - lr);
+      const unsigned qw = *reinterpret_cast<const unsigned*>(sm.u.in.Q + r * PQ + 2 * cp);
+      const unsigned kw = *reinterpret_cast<const unsigned*>(sm.u.in.K + r * PQ + 2 * cp);
+      *reinterpret_cast<unsigned*>(Qw + r * kD + 2 * cp) = pack_bf16(gr * lo_bf(qw), gr * hi_bf(qw));
+      kh0[i] = kr * lo_bf(kw);
+      kh1[i] = kr * hi_bf(kw);
+    }
+    u32x4 w0, w1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      w0[i] = pack_bf16(kh0[2 * i], kh0[2 * i + 1]);
+      w1[i] = pack_bf16(kh1[2 * i], kh1[2 * i + 1]);
+    }
+    *reinterpret_cast<u32x4*>(Kw + (2 * cp) * C + 8 * e8) = w0;
+    *reinterpret_cast<u32x4*>(Kw + (2 * cp + 1) * C + 8 * e8) = w1;
+  }
 
   // ---- Gram k.k and scores q.k: wave -> row block (w & 3), column blocks 2(w>>2)+{0,1}
   {
@@ -270,151 +301,119 @@ struct SeqSmem {
   uint16_t Ut[VT * PC];    // U^T tile [v][j]
 };
 
-// One chunk's inputs of the sequential pass, held in registers while the previous
-// chunk computes: two 16-byte pieces of W and one of A; q and k pairs of key
-// channels (2cp, 2cp+1) for tokens [8e, 8e+8); alpha of token `lane`; and, for the
-// waves that form U, the U~ tile entries in accumulator layout.
-template <int NVB>
+// One chunk's operands, held in registers while the previous chunk computes: 7
+// sixteen-byte pieces per thread of W, A, diag(g) Q and (diag(g_C/g) K)^T (56 KB per
+// chunk), alpha of token `lane`, and, for the waves that form U, the raw bf16 U~
+// entries in accumulator layout (converting them here would make the compiler wait
+// for the loads at once).
 struct Prefetch {
-  u32x4 w[2], a;
-  unsigned q[8], k[8];
+  u32x4 w[2], a, qg[2], kh[2];
   float al;
-  f32x4 ut;
+  unsigned short ut[4];
 };
 
 template <int VT>
-__device__ __forceinline__ void fetch_chunk(Prefetch<VT / 16>& pf, const uint16_t* __restrict__ q,
-                                            const uint16_t* __restrict__ k,
-                                            const float* __restrict__ alpha,
+__device__ __forceinline__ void fetch_chunk(Prefetch& pf, const float* __restrict__ alpha,
                                             const uint8_t* __restrict__ ws, int n, int nc, int ci,
                                             int T, int v0) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int cp = tid & 63, e8 = tid >> 6, l16 = lane & 15, lq = lane >> 4;
+  const int l16 = lane & 15, lq = lane >> 4;
   const size_t tok0 = (size_t)n * T + (size_t)ci * C;
   const uint8_t* wsc = ws + ((size_t)n * nc + ci) * kWsChunk;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int p = tid + NT * i, row = p >> 4, seg = p & 15;
-    pf.w[i] = *reinterpret_cast<const u32x4*>(wsc + kWsW + (size_t)(row * kD + seg * 8) * 2);
+    const size_t o16 = (size_t)(tid + NT * i) * 16;   // 16-byte piece of a 16 KB tile
+    pf.w[i] = *reinterpret_cast<const u32x4*>(wsc + kWsW + o16);
+    pf.qg[i] = *reinterpret_cast<const u32x4*>(wsc + kWsQ + o16);
+    pf.kh[i] = *reinterpret_cast<const u32x4*>(wsc + kWsK + o16);
   }
-  pf.a = *reinterpret_cast<const u32x4*>(wsc + kWsA + (size_t)((tid >> 3) * C + (tid & 7) * 8) * 2);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const size_t off = (tok0 + 8 * e8 + i) * kD + 2 * cp;
-    pf.q[i] = *reinterpret_cast<const unsigned*>(q + off);
-    pf.k[i] = *reinterpret_cast<const unsigned*>(k + off);
-  }
+  pf.a = *reinterpret_cast<const u32x4*>(wsc + kWsA + (size_t)tid * 16);
   pf.al = alpha[tok0 + lane];
-  if (wave < 4 * (VT / 16)) {
-    const int rb = wave & 3, vb = wave >> 2;
-    const uint16_t* Uw = reinterpret_cast<const uint16_t*>(wsc + kWsU);
+  const int rb = wave & 3, vb = (wave >> 2) & (VT / 16 - 1);   // in bounds for every wave
+  const uint16_t* Uw = reinterpret_cast<const uint16_t*>(wsc + kWsU);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pf.ut[i] = bf16_to_f32(Uw[(rb * 16 + lq * 4 + i) * kD + v0 + vb * 16 + l16]);
-  }
+  for (int i = 0; i < 4; ++i) pf.ut[i] = Uw[(rb * 16 + lq * 4 + i) * kD + v0 + vb * 16 + l16];
 }
 
-}  // namespace gdc
-
 // One chunk of the sequential pass: starts the loads of the next chunk into `nx`,
-// then consumes `pf` (this chunk's inputs).
+// then consumes `pf` (this chunk's operands).
 template <int VT>
-__device__ __forceinline__ void gdn_seq_chunk(gdc::SeqSmem<VT>& sm, gdc::Prefetch<VT / 16>& pf,
-                                              gdc::Prefetch<VT / 16>& nx, f32x4 (&Sacc)[VT / 16],
-                                              int& cur, int ci, int nc, int n, int T, int v0,
-                                              const uint16_t* __restrict__ q,
-                                              const uint16_t* __restrict__ k,
-                                              const float* __restrict__ alpha,
+__device__ __forceinline__ void gdn_seq_chunk(SeqSmem<VT>& sm, Prefetch& pf, Prefetch& nx,
+                                              f32x4 (&Sacc)[VT / 16], int& cur, int ci, int nc,
+                                              int n, int T, int v0, const float* __restrict__ alpha,
                                               const uint8_t* __restrict__ ws,
                                               uint16_t* __restrict__ o) {
-  using namespace gdc;
   constexpr int NVB = VT / 16;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lq = lane >> 4;
-  const int cp = tid & 63, e8 = tid >> 6;
   const int kcol = wave * 16 + l16;
-  if (ci + 1 < nc) fetch_chunk<VT>(nx, q, k, alpha, ws, n, nc, ci + 1, T, v0);
-    const size_t tok0 = (size_t)n * T + (size_t)ci * C;
-    // ---- E: cumulative log-decays (every wave for itself), operands to LDS
-    const float lgl = wave_scan(__logf(pf.al));
-    const float lC = __shfl(lgl, C - 1);
-    const float gC = __expf(lC);
-    {
-      float kh0[8], kh1[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = 8 * e8 + i;
-        const float lr = __shfl(lgl, r);
-        const float gr = __expf(lr), kr = __expf(lC - lr);
-        *reinterpret_cast<unsigned*>(sm.Qg + r * PQ + 2 * cp) =
-            pack_bf16(gr * lo_bf(pf.q[i]), gr * hi_bf(pf.q[i]));
-        kh0[i] = kr * lo_bf(pf.k[i]);
-        kh1[i] = kr * hi_bf(pf.k[i]);
-      }
-      u32x4 w0, w1;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        w0[i] = pack_bf16(kh0[2 * i], kh0[2 * i + 1]);
-        w1[i] = pack_bf16(kh1[2 * i], kh1[2 * i + 1]);
-      }
-      *reinterpret_cast<u32x4*>(sm.Kht + (2 * cp) * PC + 8 * e8) = w0;
-      *reinterpret_cast<u32x4*>(sm.Kht + (2 * cp + 1) * PC + 8 * e8) = w1;
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int p = tid + NT * i, row = p >> 4, seg = p & 15;
-      *reinterpret_cast<u32x4*>(sm.W + row * PQ + seg * 8) = pf.w[i];
-    }
-    *reinterpret_cast<u32x4*>(sm.A + (tid >> 3) * PC + (tid & 7) * 8) = pf.a;
-    const f32x4 ut = pf.ut;
-    lds_barrier();
+  const size_t tok0 = (size_t)n * T + (size_t)ci * C;
+  if (ci + 1 < nc) fetch_chunk<VT>(nx, alpha, ws, n, nc, ci + 1, T, v0);
 
-    // ---- U = U~ - W S^T: wave -> (row block w & 3, value block w >> 2); to LDS transposed
-    if (wave < 4 * NVB) {
-      const int rb = wave & 3, vb = wave >> 2;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // ---- copy this chunk's operands into LDS; g_C from the decays (every wave)
+  const float gC = __expf(__shfl(wave_scan(__logf(pf.al)), C - 1));
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        acc = mfma(ld8(sm.W + (rb * 16 + l16) * PQ + ks * 32 + lq * 8),
-                   ld8(sm.Sb[cur] + (vb * 16 + l16) * PQ + ks * 32 + lq * 8), acc);
+  for (int i = 0; i < 2; ++i) {
+    const int p = tid + NT * i;
+    *reinterpret_cast<u32x4*>(sm.W + (p >> 4) * PQ + (p & 15) * 8) = pf.w[i];
+    *reinterpret_cast<u32x4*>(sm.Qg + (p >> 4) * PQ + (p & 15) * 8) = pf.qg[i];
+    *reinterpret_cast<u32x4*>(sm.Kht + (p >> 3) * PC + (p & 7) * 8) = pf.kh[i];
+  }
+  *reinterpret_cast<u32x4*>(sm.A + (tid >> 3) * PC + (tid & 7) * 8) = pf.a;
+  f32x4 ut;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        sm.Ut[(vb * 16 + l16) * PC + rb * 16 + lq * 4 + i] = f32_to_bf16(ut[i] - acc[i]);
-    }
-    lds_barrier();
+  for (int i = 0; i < 4; ++i) ut[i] = bf16_to_f32(pf.ut[i]);
+  lds_barrier();
 
-    // ---- O = diag(g) Q S^T + A U (same tile assignment)
-    if (wave < 4 * NVB) {
-      const int rb = wave & 3, vb = wave >> 2;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // ---- U = U~ - W S^T: wave -> (row block w & 3, value block w >> 2); to LDS transposed
+  if (wave < 4 * NVB) {
+    const int rb = wave & 3, vb = wave >> 2;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        acc = mfma(ld8(sm.Qg + (rb * 16 + l16) * PQ + ks * 32 + lq * 8),
-                   ld8(sm.Sb[cur] + (vb * 16 + l16) * PQ + ks * 32 + lq * 8), acc);
+    for (int ks = 0; ks < 4; ++ks)
+      acc = mfma(ld8(sm.W + (rb * 16 + l16) * PQ + ks * 32 + lq * 8),
+                 ld8(sm.Sb[cur] + (vb * 16 + l16) * PQ + ks * 32 + lq * 8), acc);
 #pragma unroll
-      for (int js = 0; js < 2; ++js)
-        if (js * 32 <= rb * 16 + 15)
-          acc = mfma(ld8(sm.A + (rb * 16 + l16) * PC + js * 32 + lq * 8),
-                     ld8(sm.Ut + (vb * 16 + l16) * PC + js * 32 + lq * 8), acc);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        o[(tok0 + rb * 16 + lq * 4 + i) * kD + v0 + vb * 16 + l16] = f32_to_bf16(acc[i]);
-    }
+    for (int i = 0; i < 4; ++i)
+      sm.Ut[(vb * 16 + l16) * PC + rb * 16 + lq * 4 + i] = f32_to_bf16(ut[i] - acc[i]);
+  }
+  lds_barrier();
 
-    // ---- S <- g_C S + U^T (diag(g_C/g) K): key block = wave; next bf16 copy
+  // ---- O = diag(g) Q S^T + A U (same tile assignment)
+  if (wave < 4 * NVB) {
+    const int rb = wave & 3, vb = wave >> 2;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int vb = 0; vb < NVB; ++vb) {
-      f32x4 acc = Sacc[vb] * gC;
+    for (int ks = 0; ks < 4; ++ks)
+      acc = mfma(ld8(sm.Qg + (rb * 16 + l16) * PQ + ks * 32 + lq * 8),
+                 ld8(sm.Sb[cur] + (vb * 16 + l16) * PQ + ks * 32 + lq * 8), acc);
 #pragma unroll
-      for (int js = 0; js < 2; ++js)
-        acc = mfma(ld8(sm.Ut + (vb * 16 + l16) * PC + js * 32 + lq * 8),
-                   ld8(sm.Kht + (wave * 16 + l16) * PC + js * 32 + lq * 8), acc);
-      Sacc[vb] = acc;
+    for (int js = 0; js < 2; ++js)
+      if (js * 32 <= rb * 16 + 15)
+        acc = mfma(ld8(sm.A + (rb * 16 + l16) * PC + js * 32 + lq * 8),
+                   ld8(sm.Ut + (vb * 16 + l16) * PC + js * 32 + lq * 8), acc);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sm.Sb[cur ^ 1][(vb * 16 + lq * 4 + i) * PQ + kcol] = f32_to_bf16(acc[i]);
-    }
-    cur ^= 1;
-    lds_barrier();
+    for (int i = 0; i < 4; ++i)
+      o[(tok0 + rb * 16 + lq * 4 + i) * kD + v0 + vb * 16 + l16] = f32_to_bf16(acc[i]);
+  }
+
+  // ---- S <- g_C S + U^T (diag(g_C/g) K): key block = wave; next bf16 copy
+#pragma unroll
+  for (int vb = 0; vb < NVB; ++vb) {
+    f32x4 acc = Sacc[vb] * gC;
+#pragma unroll
+    for (int js = 0; js < 2; ++js)
+      acc = mfma(ld8(sm.Ut + (vb * 16 + l16) * PC + js * 32 + lq * 8),
+                 ld8(sm.Kht + (wave * 16 + l16) * PC + js * 32 + lq * 8), acc);
+    Sacc[vb] = acc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sm.Sb[cur ^ 1][(vb * 16 + lq * 4 + i) * PQ + kcol] = f32_to_bf16(acc[i]);
+  }
+  cur ^= 1;
+  lds_barrier();
 }
+
+}  // namespace gdc
 
 template <int VT>
 __global__ __launch_bounds__(512) void gdn_chunk_seq_kernel(
@@ -427,7 +426,6 @@ __global__ __launch_bounds__(512) void gdn_chunk_seq_kernel(
   __shared__ SeqSmem<VT> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lq = lane >> 4;
-  const int cp = tid & 63, e8 = tid >> 6;
   const int n = blockIdx.x / TPS, vt = blockIdx.x % TPS, v0 = vt * VT;
   const int nc = T / C;
   const int kcol = wave * 16 + l16;      // key column of this wave's state tiles
@@ -443,12 +441,12 @@ __global__ __launch_bounds__(512) void gdn_chunk_seq_kernel(
       sm.Sb[0][(vb * 16 + lq * 4 + i) * PQ + kcol] = f32_to_bf16(Sacc[vb][i]);
     }
 
-  Prefetch<NVB> pa, pb;
-  if (nc > 0) fetch_chunk<VT>(pa, q, k, alpha, ws, n, nc, 0, T, v0);
+  Prefetch pa, pb;
+  if (nc > 0) fetch_chunk<VT>(pa, alpha, ws, n, nc, 0, T, v0);
   int cur = 0;
   for (int ci = 0; ci < nc; ci += 2) {
-    gdn_seq_chunk<VT>(sm, pa, pb, Sacc, cur, ci, nc, n, T, v0, q, k, alpha, ws, o);
-    if (ci + 1 < nc) gdn_seq_chunk<VT>(sm, pb, pa, Sacc, cur, ci + 1, nc, n, T, v0, q, k, alpha, ws, o);
+    gdn_seq_chunk<VT>(sm, pa, pb, Sacc, cur, ci, nc, n, T, v0, alpha, ws, o);
+    if (ci + 1 < nc) gdn_seq_chunk<VT>(sm, pb, pa, Sacc, cur, ci + 1, nc, n, T, v0, alpha, ws, o);
   }
 
 #pragma unroll

@@ -87,7 +87,9 @@ __device__ __forceinline__ void fetch(Prefetch<C / NW>& pf, const uint16_t* __re
     pf.g[i] = *reinterpret_cast<const f32x2*>(log_g + row * kD + 2 * cp);
     pf.q[i] = *reinterpret_cast<const unsigned*>(q + row * kD + 2 * cp);
     pf.k[i] = *reinterpret_cast<const unsigned*>(k + row * kD + 2 * cp);
-    pf.v[i] = 2 * cp < VT ? *reinterpret_cast<const unsigned*>(v + row * kD + v0 + 2 * cp) : 0u;
+    // every thread loads (an in-bounds pair when 2cp >= VT, unused): a select on a
+    // loaded value would make the compiler wait for the load right here
+    pf.v[i] = *reinterpret_cast<const unsigned*>(v + row * kD + v0 + ((2 * cp) & (VT - 1)));
   }
 }
 
