@@ -299,7 +299,24 @@ struct SeqSmem {
   uint16_t A[C * PC];      // [r][j]
   uint16_t Sb[2][VT * PQ]; // bf16 state tile [v][k], double buffered
   uint16_t Ut[VT * PC];    // U^T tile [v][j]
+  uint16_t Ob[C * (VT + 8)]; // this chunk's outputs [r][v], stored at the next chunk
 };
+
+// Stores the staged outputs of the chunk starting at token tok0: VT / 8 per thread,
+// the same single store in every thread.
+template <int VT>
+__device__ __forceinline__ void store_o(const SeqSmem<VT>& sm, uint16_t* __restrict__ o,
+                                        size_t tok0, int v0) {
+  constexpr int EPT = VT / 8, OBS = VT + 8;
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  const int tid = threadIdx.x, row = tid >> 3, col = (tid & 7) * EPT;
+  const uint16_t* src = sm.Ob + row * OBS + col;
+  uint16_t* dst = o + (tok0 + row) * kD + v0 + col;
+  if constexpr (EPT == 2)
+    *reinterpret_cast<unsigned*>(dst) = *reinterpret_cast<const unsigned*>(src);
+  else
+    *reinterpret_cast<u32x2*>(dst) = *reinterpret_cast<const u32x2*>(src);
+}
 
 // One chunk's operands, held in registers while the previous chunk computes: 7
 // sixteen-byte pieces per thread of W, A, diag(g) Q and (diag(g_C/g) K)^T (56 KB per
@@ -336,8 +353,12 @@ __device__ __forceinline__ void fetch_chunk(Prefetch& pf, const float* __restric
 }
 
 // One chunk of the sequential pass: starts the loads of the next chunk into `nx`,
-// then consumes `pf` (this chunk's operands).
-template <int VT>
+// stores the previous chunk's staged outputs, then consumes `pf` (this chunk's
+// operands). Every thread issues the same loads and the same store on every chunk
+// (the last chunk loads itself again; the first chunk, FIRST, is a separate copy with
+// nothing to store), so the wait for `pf` counts exactly the memory operations issued
+// after it instead of waiting for them.
+template <int VT, bool FIRST>
 __device__ __forceinline__ void gdn_seq_chunk(SeqSmem<VT>& sm, Prefetch& pf, Prefetch& nx,
                                               f32x4 (&Sacc)[VT / 16], int& cur, int ci, int nc,
                                               int n, int T, int v0, const float* __restrict__ alpha,
@@ -348,7 +369,8 @@ __device__ __forceinline__ void gdn_seq_chunk(SeqSmem<VT>& sm, Prefetch& pf, Pre
   const int l16 = lane & 15, lq = lane >> 4;
   const int kcol = wave * 16 + l16;
   const size_t tok0 = (size_t)n * T + (size_t)ci * C;
-  if (ci + 1 < nc) fetch_chunk<VT>(nx, alpha, ws, n, nc, ci + 1, T, v0);
+  fetch_chunk<VT>(nx, alpha, ws, n, nc, min(ci + 1, nc - 1), T, v0);
+  if constexpr (!FIRST) store_o<VT>(sm, o, tok0 - C, v0);
 
   // ---- copy this chunk's operands into LDS; g_C from the decays (every wave)
   const float gC = __expf(__shfl(wave_scan(__logf(pf.al)), C - 1));
@@ -394,7 +416,7 @@ __device__ __forceinline__ void gdn_seq_chunk(SeqSmem<VT>& sm, Prefetch& pf, Pre
                    ld8(sm.Ut + (vb * 16 + l16) * PC + js * 32 + lq * 8), acc);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      o[(tok0 + rb * 16 + lq * 4 + i) * kD + v0 + vb * 16 + l16] = f32_to_bf16(acc[i]);
+      sm.Ob[(rb * 16 + lq * 4 + i) * (VT + 8) + vb * 16 + l16] = f32_to_bf16(acc[i]);
   }
 
   // ---- S <- g_C S + U^T (diag(g_C/g) K): key block = wave; next bf16 copy
@@ -426,7 +448,20 @@ __global__ __launch_bounds__(512) void gdn_chunk_seq_kernel(
   __shared__ SeqSmem<VT> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lq = lane >> 4;
-  const int n = blockIdx.x / TPS, vt = blockIdx.x % TPS, v0 = vt * VT;
+  // block -> (sequence, value tile); the tiles of one sequence share an XCD (blocks
+  // are dealt to the 8 XCDs round robin), so the chunk operands they all read are
+  // fetched into that XCD's L2 once
+  int n, vt;
+  const int bid = blockIdx.x;
+  if ((N & 7) == 0) {
+    const int xcd = bid & 7, slot = bid >> 3;
+    n = (slot / TPS) * 8 + xcd;
+    vt = slot % TPS;
+  } else {
+    n = bid / TPS;
+    vt = bid % TPS;
+  }
+  const int v0 = vt * VT;
   const int nc = T / C;
   const int kcol = wave * 16 + l16;      // key column of this wave's state tiles
 
@@ -441,12 +476,18 @@ __global__ __launch_bounds__(512) void gdn_chunk_seq_kernel(
       sm.Sb[0][(vb * 16 + lq * 4 + i) * PQ + kcol] = f32_to_bf16(Sacc[vb][i]);
     }
 
-  Prefetch pa, pb;
-  if (nc > 0) fetch_chunk<VT>(pa, alpha, ws, n, nc, 0, T, v0);
-  int cur = 0;
-  for (int ci = 0; ci < nc; ci += 2) {
-    gdn_seq_chunk<VT>(sm, pa, pb, Sacc, cur, ci, nc, n, T, v0, alpha, ws, o);
-    if (ci + 1 < nc) gdn_seq_chunk<VT>(sm, pb, pa, Sacc, cur, ci + 1, nc, n, T, v0, alpha, ws, o);
+  if (nc > 0) {
+    Prefetch pa, pb;
+    int cur = 0;
+    fetch_chunk<VT>(pa, alpha, ws, n, nc, 0, T, v0);
+    gdn_seq_chunk<VT, true>(sm, pa, pb, Sacc, cur, 0, nc, n, T, v0, alpha, ws, o);
+    int ci = 1;
+    for (; ci + 1 < nc; ci += 2) {
+      gdn_seq_chunk<VT, false>(sm, pb, pa, Sacc, cur, ci, nc, n, T, v0, alpha, ws, o);
+      gdn_seq_chunk<VT, false>(sm, pa, pb, Sacc, cur, ci + 1, nc, n, T, v0, alpha, ws, o);
+    }
+    if (ci < nc) gdn_seq_chunk<VT, false>(sm, pb, pa, Sacc, cur, ci, nc, n, T, v0, alpha, ws, o);
+    store_o<VT>(sm, o, (size_t)n * T + (size_t)(nc - 1) * C, v0);
   }
 
 #pragma unroll

@@ -93,6 +93,173 @@ __device__ __forceinline__ void fetch(Prefetch<C / NW>& pf, const uint16_t* __re
   }
 }
 
+// One chunk: E1/E2 form the decayed operands from the prefetched inputs, then the
+// next chunk's inputs are requested and M1/M2 run the contractions.
+template <int VT, int NW>
+__device__ __forceinline__ void gla_step(Smem<VT, NW>& sm, Prefetch<C / NW>& pf,
+                                         f32x4 (&Sacc)[Cfg<VT, NW>::SPW],
+                                         const uint16_t* __restrict__ q,
+                                         const uint16_t* __restrict__ k,
+                                         const uint16_t* __restrict__ v,
+                                         const float* __restrict__ log_g,
+                                         uint16_t* __restrict__ o, size_t seq, int c0, int T,
+                                         int v0, int kcol, int vbase) {
+  using CF = Cfg<VT, NW>;
+  constexpr int TPT = CF::TPT, SPW = CF::SPW, OPW = CF::OPW, APW = CF::APW;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int cp = tid & 63, eg = tid >> 6;
+  // ---- E1: prefix sums of this thread's tokens, group totals to LDS
+  f32x2 b[TPT];
+  b[0] = pf.g[0];
+#pragma unroll
+  for (int i = 1; i < TPT; ++i) b[i] = b[i - 1] + pf.g[i];
+  *reinterpret_cast<f32x2*>(sm.tot + eg * kD + 2 * cp) = b[TPT - 1];
+  lds_barrier();
+
+  // ---- E2: decay factors and operands; the bf16 state copy times e^{b_m}
+  {
+    f32x2 off = {0.f, 0.f}, bm = {0.f, 0.f}, bC = {0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < NW; ++e) {
+      const f32x2 te = *reinterpret_cast<const f32x2*>(sm.tot + e * kD + 2 * cp);
+      if (e < eg) off += te;
+      if (e < NW / 2) bm += te;
+      bC += te;
+    }
+    // one exponential and one reciprocal per element: p = e^{b - b_m};
+    // e^{b_m - b} = 1/p, e^{b_C - b} = e^{b_C - b_m} / p
+    const f32x2 eCm = {__expf(bC.x - bm.x), __expf(bC.y - bm.y)};
+    float kh0[TPT], kh1[TPT], vv0[TPT], vv1[TPT];
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      const int r = TPT * eg + i;
+      const f32x2 bb = b[i] + off;
+      const float p0 = __expf(bb.x - bm.x), p1 = __expf(bb.y - bm.y);
+      const float r0 = __builtin_amdgcn_rcpf(p0), r1 = __builtin_amdgcn_rcpf(p1);
+      const float k0 = __uint_as_float(pf.k[i] << 16), k1 = __uint_as_float(pf.k[i] & 0xffff0000u);
+      *reinterpret_cast<unsigned*>(sm.Qr + r * PQ + 2 * cp) =
+          pack_bf16(__uint_as_float(pf.q[i] << 16) * p0, __uint_as_float(pf.q[i] & 0xffff0000u) * p1);
+      *reinterpret_cast<unsigned*>(sm.Kr + r * PQ + 2 * cp) = pack_bf16(k0 * r0, k1 * r1);
+      kh0[i] = k0 * r0 * eCm.x;
+      kh1[i] = k1 * r1 * eCm.y;
+      vv0[i] = __uint_as_float(pf.v[i] << 16);
+      vv1[i] = __uint_as_float(pf.v[i] & 0xffff0000u);
+    }
+    // transposed rows: TPT consecutive tokens of one key (value) channel
+    if constexpr (TPT == 8) {
+      u32x4 w0, w1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        w0[i] = pack_bf16(kh0[2 * i], kh0[2 * i + 1]);
+        w1[i] = pack_bf16(kh1[2 * i], kh1[2 * i + 1]);
+      }
+      *reinterpret_cast<u32x4*>(sm.Kh + (2 * cp) * PC + TPT * eg) = w0;
+      *reinterpret_cast<u32x4*>(sm.Kh + (2 * cp + 1) * PC + TPT * eg) = w1;
+      {
+        // every thread writes: threads whose channel pair repeats modulo VT hold
+        // the same values (the load wraps the column), so their writes agree;
+        // a branch here would make the compiler wait for every outstanding load
+        const int vc = (2 * cp) & (VT - 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          w0[i] = pack_bf16(vv0[2 * i], vv0[2 * i + 1]);
+          w1[i] = pack_bf16(vv1[2 * i], vv1[2 * i + 1]);
+        }
+        *reinterpret_cast<u32x4*>(sm.Vt + vc * PC + TPT * eg) = w0;
+        *reinterpret_cast<u32x4*>(sm.Vt + (vc + 1) * PC + TPT * eg) = w1;
+      }
+    } else {
+      static_assert(TPT == 4, "4 or 8 tokens per thread");
+      typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+      u32x2 w0 = {pack_bf16(kh0[0], kh0[1]), pack_bf16(kh0[2], kh0[3])};
+      u32x2 w1 = {pack_bf16(kh1[0], kh1[1]), pack_bf16(kh1[2], kh1[3])};
+      *reinterpret_cast<u32x2*>(sm.Kh + (2 * cp) * PC + TPT * eg) = w0;
+      *reinterpret_cast<u32x2*>(sm.Kh + (2 * cp + 1) * PC + TPT * eg) = w1;
+      if (2 * cp < VT) {
+        w0 = u32x2{pack_bf16(vv0[0], vv0[1]), pack_bf16(vv0[2], vv0[3])};
+        w1 = u32x2{pack_bf16(vv1[0], vv1[1]), pack_bf16(vv1[2], vv1[3])};
+        *reinterpret_cast<u32x2*>(sm.Vt + (2 * cp) * PC + TPT * eg) = w0;
+        *reinterpret_cast<u32x2*>(sm.Vt + (2 * cp + 1) * PC + TPT * eg) = w1;
+      }
+    }
+    if (eg == 0) {
+      const f32x2 em = {__expf(bm.x), __expf(bm.y)};
+      sm.eC[2 * cp] = eCm.x * em.x;
+      sm.eC[2 * cp + 1] = eCm.y * em.y;
+    }
+    // this wave's state tiles, scaled by e^{b_m} of their key column
+    float bmk = 0.f;
+#pragma unroll
+    for (int e = 0; e < NW / 2; ++e) bmk += sm.tot[e * kD + kcol];
+    const float emk = __expf(bmk);
+#pragma unroll
+    for (int j = 0; j < SPW; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sm.Sb[((vbase + j) * 16 + lq * 4 + i) * PQ + kcol] = f32_to_bf16(Sacc[j][i] * emk);
+  }
+  lds_barrier();
+  // next chunk's inputs, overlapping the MFMA work; unconditional (the last chunk
+  // loads itself again) so the waits for them count exactly the loads issued after
+  fetch<VT, NW>(pf, q, k, v, log_g, seq + min(c0 + C, T - C), v0);
+
+  // ---- M1: masked intra-chunk scores (APW tiles per wave)
+#pragma unroll
+  for (int j = 0; j < APW; ++j) {
+    const int u = wave * APW + j, rb = u & 3, cb = u >> 2;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (cb <= rb) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        acc = mfma(ld8(sm.Qr + (rb * 16 + l16) * PQ + ks * 32 + lq * 8),
+                   ld8(sm.Kr + (cb * 16 + l16) * PQ + ks * 32 + lq * 8), acc);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = rb * 16 + lq * 4 + i, col = cb * 16 + l16;
+      sm.A[row * PC + col] = f32_to_bf16(col <= row ? acc[i] : 0.f);
+    }
+  }
+  lds_barrier();
+
+  // ---- M2: outputs (OPW tiles per wave) and the state update
+#pragma unroll
+  for (int j = 0; j < OPW; ++j) {
+    const int u = wave * OPW + j, rb = u & 3, vb = u >> 2;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      acc = mfma(ld8(sm.Qr + (rb * 16 + l16) * PQ + ks * 32 + lq * 8),
+                 ld8(sm.Sb + (vb * 16 + l16) * PQ + ks * 32 + lq * 8), acc);
+#pragma unroll
+    for (int js = 0; js < 2; ++js)
+      if (js * 32 <= rb * 16 + 15)
+        acc = mfma(ld8(sm.A + (rb * 16 + l16) * PC + js * 32 + lq * 8),
+                   ld8(sm.Vt + (vb * 16 + l16) * PC + js * 32 + lq * 8), acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = rb * 16 + lq * 4 + i;
+      o[(seq + c0 + row) * kD + v0 + vb * 16 + l16] = f32_to_bf16(acc[i]);
+    }
+  }
+  {
+    const float dec = sm.eC[kcol];
+    const int kb = wave & 7;
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      const int vb = vbase + j;
+      f32x4 acc = Sacc[j] * dec;
+#pragma unroll
+      for (int js = 0; js < 2; ++js)
+        acc = mfma(ld8(sm.Vt + (vb * 16 + l16) * PC + js * 32 + lq * 8),
+                   ld8(sm.Kh + (kb * 16 + l16) * PC + js * 32 + lq * 8), acc);
+      Sacc[j] = acc;
+    }
+  }
+  lds_barrier();
+}
+
 }  // namespace gla
 
 template <int VT, int NW>
@@ -137,151 +304,14 @@ __global__ __launch_bounds__(64 * NW) void gla_chunk_kernel(
 
   const size_t seq = (size_t)n * T;
   Prefetch<TPT> pf;
-  if (T > 0) fetch<VT, NW>(pf, q, k, v, log_g, seq, v0);
-  for (int c0 = 0; c0 < T; c0 += C) {
-    // ---- E1: prefix sums of this thread's tokens, group totals to LDS
-    f32x2 b[TPT];
-    b[0] = pf.g[0];
-#pragma unroll
-    for (int i = 1; i < TPT; ++i) b[i] = b[i - 1] + pf.g[i];
-    *reinterpret_cast<f32x2*>(sm.tot + eg * kD + 2 * cp) = b[TPT - 1];
-    lds_barrier();
-
-    // ---- E2: decay factors and operands; the bf16 state copy times e^{b_m}
-    {
-      f32x2 off = {0.f, 0.f}, bm = {0.f, 0.f}, bC = {0.f, 0.f};
-#pragma unroll
-      for (int e = 0; e < NW; ++e) {
-        const f32x2 te = *reinterpret_cast<const f32x2*>(sm.tot + e * kD + 2 * cp);
-        if (e < eg) off += te;
-        if (e < NW / 2) bm += te;
-        bC += te;
-      }
-      // one exponential and one reciprocal per element: p = e^{b - b_m};
-      // e^{b_m - b} = 1/p, e^{b_C - b} = e^{b_C - b_m} / p
-      const f32x2 eCm = {__expf(bC.x - bm.x), __expf(bC.y - bm.y)};
-      float kh0[TPT], kh1[TPT], vv0[TPT], vv1[TPT];
-#pragma unroll
-      for (int i = 0; i < TPT; ++i) {
-        const int r = TPT * eg + i;
-        const f32x2 bb = b[i] + off;
-        const float p0 = __expf(bb.x - bm.x), p1 = __expf(bb.y - bm.y);
-        const float r0 = __builtin_amdgcn_rcpf(p0), r1 = __builtin_amdgcn_rcpf(p1);
-        const float k0 = __uint_as_float(pf.k[i] << 16), k1 = __uint_as_float(pf.k[i] & 0xffff0000u);
-        *reinterpret_cast<unsigned*>(sm.Qr + r * PQ + 2 * cp) =
-            pack_bf16(__uint_as_float(pf.q[i] << 16) * p0, __uint_as_float(pf.q[i] & 0xffff0000u) * p1);
-        *reinterpret_cast<unsigned*>(sm.Kr + r * PQ + 2 * cp) = pack_bf16(k0 * r0, k1 * r1);
-        kh0[i] = k0 * r0 * eCm.x;
-        kh1[i] = k1 * r1 * eCm.y;
-        vv0[i] = __uint_as_float(pf.v[i] << 16);
-        vv1[i] = __uint_as_float(pf.v[i] & 0xffff0000u);
-      }
-      // transposed rows: TPT consecutive tokens of one key (value) channel
-      if constexpr (TPT == 8) {
-        u32x4 w0, w1;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          w0[i] = pack_bf16(kh0[2 * i], kh0[2 * i + 1]);
-          w1[i] = pack_bf16(kh1[2 * i], kh1[2 * i + 1]);
-        }
-        *reinterpret_cast<u32x4*>(sm.Kh + (2 * cp) * PC + TPT * eg) = w0;
-        *reinterpret_cast<u32x4*>(sm.Kh + (2 * cp + 1) * PC + TPT * eg) = w1;
-        if (2 * cp < VT) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            w0[i] = pack_bf16(vv0[2 * i], vv0[2 * i + 1]);
-            w1[i] = pack_bf16(vv1[2 * i], vv1[2 * i + 1]);
-          }
-          *reinterpret_cast<u32x4*>(sm.Vt + (2 * cp) * PC + TPT * eg) = w0;
-          *reinterpret_cast<u32x4*>(sm.Vt + (2 * cp + 1) * PC + TPT * eg) = w1;
-        }
-      } else {
-        static_assert(TPT == 4, "4 or 8 tokens per thread");
-        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-        u32x2 w0 = {pack_bf16(kh0[0], kh0[1]), pack_bf16(kh0[2], kh0[3])};
-        u32x2 w1 = {pack_bf16(kh1[0], kh1[1]), pack_bf16(kh1[2], kh1[3])};
-        *reinterpret_cast<u32x2*>(sm.Kh + (2 * cp) * PC + TPT * eg) = w0;
-        *reinterpret_cast<u32x2*>(sm.Kh + (2 * cp + 1) * PC + TPT * eg) = w1;
-        if (2 * cp < VT) {
-          w0 = u32x2{pack_bf16(vv0[0], vv0[1]), pack_bf16(vv0[2], vv0[3])};
-          w1 = u32x2{pack_bf16(vv1[0], vv1[1]), pack_bf16(vv1[2], vv1[3])};
-          *reinterpret_cast<u32x2*>(sm.Vt + (2 * cp) * PC + TPT * eg) = w0;
-          *reinterpret_cast<u32x2*>(sm.Vt + (2 * cp + 1) * PC + TPT * eg) = w1;
-        }
-      }
-      if (eg == 0) {
-        const f32x2 em = {__expf(bm.x), __expf(bm.y)};
-        sm.eC[2 * cp] = eCm.x * em.x;
-        sm.eC[2 * cp + 1] = eCm.y * em.y;
-      }
-      // this wave's state tiles, scaled by e^{b_m} of their key column
-      float bmk = 0.f;
-#pragma unroll
-      for (int e = 0; e < NW / 2; ++e) bmk += sm.tot[e * kD + kcol];
-      const float emk = __expf(bmk);
-#pragma unroll
-      for (int j = 0; j < SPW; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sm.Sb[((vbase + j) * 16 + lq * 4 + i) * PQ + kcol] = f32_to_bf16(Sacc[j][i] * emk);
-    }
-    lds_barrier();
-    if (c0 + C < T) fetch<VT, NW>(pf, q, k, v, log_g, seq + c0 + C, v0);   // overlaps the MFMA work
-
-    // ---- M1: masked intra-chunk scores (APW tiles per wave)
-#pragma unroll
-    for (int j = 0; j < APW; ++j) {
-      const int u = wave * APW + j, rb = u & 3, cb = u >> 2;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      if (cb <= rb) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          acc = mfma(ld8(sm.Qr + (rb * 16 + l16) * PQ + ks * 32 + lq * 8),
-                     ld8(sm.Kr + (cb * 16 + l16) * PQ + ks * 32 + lq * 8), acc);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = rb * 16 + lq * 4 + i, col = cb * 16 + l16;
-        sm.A[row * PC + col] = f32_to_bf16(col <= row ? acc[i] : 0.f);
-      }
-    }
-    lds_barrier();
-
-    // ---- M2: outputs (OPW tiles per wave) and the state update
-#pragma unroll
-    for (int j = 0; j < OPW; ++j) {
-      const int u = wave * OPW + j, rb = u & 3, vb = u >> 2;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        acc = mfma(ld8(sm.Qr + (rb * 16 + l16) * PQ + ks * 32 + lq * 8),
-                   ld8(sm.Sb + (vb * 16 + l16) * PQ + ks * 32 + lq * 8), acc);
-#pragma unroll
-      for (int js = 0; js < 2; ++js)
-        if (js * 32 <= rb * 16 + 15)
-          acc = mfma(ld8(sm.A + (rb * 16 + l16) * PC + js * 32 + lq * 8),
-                     ld8(sm.Vt + (vb * 16 + l16) * PC + js * 32 + lq * 8), acc);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = rb * 16 + lq * 4 + i;
-        o[(seq + c0 + row) * kD + v0 + vb * 16 + l16] = f32_to_bf16(acc[i]);
-      }
-    }
-    {
-      const float dec = sm.eC[kcol];
-      const int kb = wave & 7;
-#pragma unroll
-      for (int j = 0; j < SPW; ++j) {
-        const int vb = vbase + j;
-        f32x4 acc = Sacc[j] * dec;
-#pragma unroll
-        for (int js = 0; js < 2; ++js)
-          acc = mfma(ld8(sm.Vt + (vb * 16 + l16) * PC + js * 32 + lq * 8),
-                     ld8(sm.Kh + (kb * 16 + l16) * PC + js * 32 + lq * 8), acc);
-        Sacc[j] = acc;
-      }
-    }
-    lds_barrier();
+  if (T > 0) {
+    fetch<VT, NW>(pf, q, k, v, log_g, seq, v0);
+    // the first chunk is peeled so that the loop is entered, as on every later
+    // iteration, with one chunk of loads and then that chunk's output stores in
+    // flight: the waits for the loads then count the stores and do not wait for them
+    gla_step<VT, NW>(sm, pf, Sacc, q, k, v, log_g, o, seq, 0, T, v0, kcol, vbase);
+    for (int c0 = C; c0 < T; c0 += C)
+      gla_step<VT, NW>(sm, pf, Sacc, q, k, v, log_g, o, seq, c0, T, v0, kcol, vbase);
   }
 
 #pragma unroll
