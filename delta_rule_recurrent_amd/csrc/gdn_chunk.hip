@@ -12,14 +12,19 @@
 //   O   = diag(g) Q S_0^T + A U,            A[r,j] = (g_r/g_j) q_r.k_j for j <= r, else 0,
 //   S_C = g_C S_0 + U^T diag(g_C/g) K.
 //
-// W, U~, A, diag(g) Q and diag(g_C/g) K do not depend on the state. A first kernel
-// forms them for every chunk in parallel (Gram and score products on bf16 MFMA, the
-// triangular inverse in fp32 by 16 x 16 diagonal blocks and block rows) and writes
-// them, bf16, to the caller's workspace. A second kernel walks the chunks of each
-// sequence in order for a tile of value channels (the value rows of U and S are
-// independent): per chunk it only copies the prepared operands into LDS and runs
-// MFMA, its state tile in fp32 accumulators, the next chunk's operands prefetched
-// into registers.
+// Substituting U into O gives O = Q' S_0^T + O~ with Q' = diag(g) Q - A W and
+// O~ = A U~: the outputs of a chunk need only the state the chunk starts from, not
+// this chunk's U. Everything but S_0 (W, U~, Q', O~, K^ = diag(g_C/g) K, g_C) is
+// formed for every chunk in parallel by a first kernel and written, bf16, to the
+// caller's workspace in the exact register order in which the second kernel feeds
+// them to the matrix cores. The second kernel walks the chunks of each sequence in
+// order for a tile of value channels (the value rows of U and S are independent):
+// per chunk, four waves form U = U~ - W S_0^T while the other four form the outputs,
+// then all eight update the state, S_C = g_C S_0 + U^T K^, which stays in fp32 MFMA
+// accumulators; the operands of the next chunk are loaded straight into registers
+// meanwhile. bf16 MFMA (v_mfma_f32_16x16x32_bf16) with fp32 accumulation throughout;
+// the triangular inverse is fp32 (16 x 16 diagonal blocks by substitution, the
+// blocks below by v_mfma_f32_16x16x4_f32).
 #include "common.hpp"
 
 namespace gdnrt {
@@ -32,19 +37,30 @@ constexpr int PQ = kD + 8;  // bf16 pitch of 128-wide rows (16-byte aligned, con
 constexpr int PC = C + 8;   // bf16 pitch of 64-wide rows
 constexpr int PF = C + 4;   // fp32 pitch of 64-wide rows (16-byte aligned)
 
-// workspace per chunk, all bf16: W [64][128], U~ [64][128], A [64][64],
-// diag(g) Q [64][128] and (diag(g_C/g) K)^T [128][64]
-constexpr size_t kWsW = 0, kWsU = (size_t)C * kD * 2, kWsA = 2 * (size_t)C * kD * 2;
-constexpr size_t kWsQ = kWsA + (size_t)C * C * 2, kWsK = kWsQ + (size_t)C * kD * 2;
-constexpr size_t kWsChunk = kWsK + (size_t)kD * C * 2;   // 73,728 bytes
+// Workspace per chunk (bytes). With lane = 16 lq + l16 of a wave:
+//  W, Q' [64 tokens][128 keys]: 16 A-operand fragments (rb, ks) of 1 KB; lane holds
+//        token rb*16 + l16, keys ks*32 + lq*4 + {0..3} then ks*32 + 16 + lq*4 + {0..3}
+//  K^    [64 tokens][128 keys]: 16 B-operand fragments (kb, js); lane holds key
+//        kb*16 + l16, tokens js*32 + lq*8 + {0..7}
+//  U~, O~ [64 tokens][128 values]: 32 accumulator tiles (rb, vb) of 512 B; lane holds
+//        tokens rb*16 + lq*4 + {0..3} of value vb*16 + l16
+//  g_C   16 copies (so that every lane loads it with a vector load)
+constexpr size_t kWsW = 0, kWsQ = 16384, kWsK = 32768, kWsU = 49152, kWsO = 65536;
+constexpr size_t kWsG = 81920, kWsChunk = 81984;
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));   // register-promotable across loops
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
+__device__ __forceinline__ bf16x8 as_bf8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// fp32 16 x 16 x 4: lane l holds A[l%16][l/16], B[l/16][l%16]; D[4(l/16)+i][l%16]
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
 // inclusive prefix sum over the 64 lanes of a wave
@@ -61,372 +77,427 @@ __device__ __forceinline__ float wave_scan(float x) {
 __device__ __forceinline__ float lo_bf(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
 
-struct PrepSmem {
-  union {
-    struct {
-      uint16_t Q[C * PQ];     // [r][k]
-      uint16_t K[C * PQ];     // [j][k]
-    } in;
-    struct {
-      uint16_t W[C * PQ];     // staged W   [r][k]
-      uint16_t U[C * PQ];     // staged U~  [r][v]
-    } out;
-  } u;
-  uint16_t Kt[kD * PC];   // [k][j]
-  uint16_t Vt[kD * PC];   // [v][j]
-  uint16_t A[C * PC];     // masked decayed scores [r][j]
-  float L[C * PF];        // strict lower part of (I + L)
-  float T[C * PF];        // (I + L)^-1
-  float M[3 * 16 * 17];   // block-row partial products
-  uint16_t Tw[C * PC];    // T diag(beta g), bf16
-  uint16_t Tu[C * PC];    // T diag(beta), bf16
-  float lg[C], bt[C];
+// LDS written by some lanes of a wave and read by others of the same wave: the LDS
+// executes a wave's instructions in order, so this only keeps the compiler from
+// reordering the accesses
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
+// value of lane J of this lane's row of 16 (DPP row_newbcast)
+template <int J>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + J, 0xF, 0xF, false));
+}
+
+// Forward substitution for two columns of a unit lower triangular 16 x 16 block,
+// lane i of a row of 16 holding row i: at step J the entry of row J is final and
+// every row below subtracts its multiple (lr[J] is zero for rows i <= J).
+template <int J>
+struct DiagSolve {
+  __device__ static __forceinline__ void run(const float (&lr)[16], float& a0, float& a1) {
+    const float x0 = row_bcast<J>(a0), x1 = row_bcast<J>(a1);
+    a0 = fmaf(-lr[J], x0, a0);
+    a1 = fmaf(-lr[J], x1, a1);
+    DiagSolve<J + 1>::run(lr, a0, a1);
+  }
 };
+template <>
+struct DiagSolve<16> {
+  __device__ static __forceinline__ void run(const float (&)[16], float&, float&) {}
+};
+
+// ------------------------------------------------------------------ per-chunk prep
+
+struct PrepSmem {
+  union {                   // k row-major until the Gram products; inverse scratch; U~^T
+    uint16_t K[C * PQ];     // [j][k]
+    float scr[8][16 * 17];  // one 16 x 16 fp32 tile per wave
+    uint16_t Ut[kD * PC];   // U~^T [v][j]
+  } rk;
+  union {
+    float L[C * PF];        // strict lower part of (I + L), fp32
+    uint16_t Wt[kD * PC];   // W^T [k][j]
+  } rl;
+  uint16_t Q[C * PQ];       // [r][k]
+  uint16_t Kt[kD * PC];     // [k][j]
+  uint16_t Vt[kD * PC];     // [v][j]
+  uint16_t A[C * PC];       // masked decayed scores [r][j]
+  float T[C * PF];          // (I + L)^-1, lower blocks
+  uint16_t Tw[C * PC];      // T diag(beta g)
+  uint16_t Tu[C * PC];      // T diag(beta)
+  float lg[C], g[C], kd[C], bt[C], btg[C];   // log g, g, g_C/g, beta, beta g
+};
+
+// one chunk's inputs for thread (cp = key-channel pair, e8 = token group of 8)
+struct PrepIn {
+  unsigned q[8], k[8], v[8];
+  float al, be;
+};
+
+__device__ __forceinline__ void prep_fetch(PrepIn& in, const uint16_t* __restrict__ q,
+                                           const uint16_t* __restrict__ k,
+                                           const uint16_t* __restrict__ v,
+                                           const float* __restrict__ alpha,
+                                           const float* __restrict__ beta, size_t tok0) {
+  const int tid = threadIdx.x, cp = tid & 63, e8 = tid >> 6;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const size_t off = (tok0 + 8 * e8 + i) * kD + 2 * cp;
+    in.q[i] = *reinterpret_cast<const unsigned*>(q + off);
+    in.k[i] = *reinterpret_cast<const unsigned*>(k + off);
+    in.v[i] = *reinterpret_cast<const unsigned*>(v + off);
+  }
+  in.al = alpha[tok0 + cp];
+  in.be = beta[tok0 + cp];
+}
+
+// lower-triangle 16 x 16 tile pairs (rb, cb), cb <= rb
+__device__ __forceinline__ void tri_pair(int p, int& rb, int& cb) {
+  rb = p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3;
+  cb = p - (rb * (rb + 1)) / 2;
+}
 
 }  // namespace gdc
 
-// ============================================================== kernel 1: per-chunk prep
-//
-// Thread t stages key channels (2cp, 2cp+1) of tokens [8e, 8e+8) (cp = t % 64,
-// e = t / 64): q, k row-major and k, v transposed with 16-byte writes.
+// Persistent: block b handles chunks b, b + grid, ...; the next chunk's inputs are
+// loaded into registers while this one is processed, and every thread issues the
+// same loads and stores on every chunk so that those waits are exact.
 __global__ __launch_bounds__(512) void gdn_chunk_prep_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, uint8_t* __restrict__ ws,
-    int T) {
+    int T, int nchunks) {
   using namespace gdc;
   __shared__ PrepSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lq = lane >> 4;
   const int cp = tid & 63, e8 = tid >> 6;
   const int nc = T / C;
-  const int n = blockIdx.x / nc, ci = blockIdx.x % nc;
-  const size_t tok0 = (size_t)n * T + (size_t)ci * C;
-  uint8_t* wsc = ws + (size_t)blockIdx.x * kWsChunk;
 
-  // ---- stage q, k (row-major), k^T and v^T; cumulative log-decays
-  {
-    unsigned qw[8], kw[8], vw[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const size_t off = (tok0 + 8 * e8 + i) * kD + 2 * cp;
-      qw[i] = *reinterpret_cast<const unsigned*>(q + off);
-      kw[i] = *reinterpret_cast<const unsigned*>(k + off);
-      vw[i] = *reinterpret_cast<const unsigned*>(v + off);
-    }
+  PrepIn in;
+  int cid = blockIdx.x;
+  prep_fetch(in, q, k, v, alpha, beta, (size_t)(cid / nc) * T + (size_t)(cid % nc) * C);
+  for (; cid < nchunks; cid += gridDim.x) {
+    uint8_t* wsc = ws + (size_t)cid * kWsChunk;
+
+    // ---- stage q, k (row-major), k^T and v^T; decays
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int r = 8 * e8 + i;
-      *reinterpret_cast<unsigned*>(sm.u.in.Q + r * PQ + 2 * cp) = qw[i];
-      *reinterpret_cast<unsigned*>(sm.u.in.K + r * PQ + 2 * cp) = kw[i];
+      *reinterpret_cast<unsigned*>(sm.Q + r * PQ + 2 * cp) = in.q[i];
+      *reinterpret_cast<unsigned*>(sm.rk.K + r * PQ + 2 * cp) = in.k[i];
     }
-    u32x4 k0, k1, v0, v1;
+    {
+      u32x4 k0, k1, v0, v1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      k0[i] = (kw[2 * i] & 0xffffu) | (kw[2 * i + 1] << 16);
-      k1[i] = (kw[2 * i] >> 16) | (kw[2 * i + 1] & 0xffff0000u);
-      v0[i] = (vw[2 * i] & 0xffffu) | (vw[2 * i + 1] << 16);
-      v1[i] = (vw[2 * i] >> 16) | (vw[2 * i + 1] & 0xffff0000u);
+      for (int i = 0; i < 4; ++i) {
+        k0[i] = (in.k[2 * i] & 0xffffu) | (in.k[2 * i + 1] << 16);
+        k1[i] = (in.k[2 * i] >> 16) | (in.k[2 * i + 1] & 0xffff0000u);
+        v0[i] = (in.v[2 * i] & 0xffffu) | (in.v[2 * i + 1] << 16);
+        v1[i] = (in.v[2 * i] >> 16) | (in.v[2 * i + 1] & 0xffff0000u);
+      }
+      *reinterpret_cast<u32x4*>(sm.Kt + (2 * cp) * PC + 8 * e8) = k0;
+      *reinterpret_cast<u32x4*>(sm.Kt + (2 * cp + 1) * PC + 8 * e8) = k1;
+      *reinterpret_cast<u32x4*>(sm.Vt + (2 * cp) * PC + 8 * e8) = v0;
+      *reinterpret_cast<u32x4*>(sm.Vt + (2 * cp + 1) * PC + 8 * e8) = v1;
     }
-    *reinterpret_cast<u32x4*>(sm.Kt + (2 * cp) * PC + 8 * e8) = k0;
-    *reinterpret_cast<u32x4*>(sm.Kt + (2 * cp + 1) * PC + 8 * e8) = k1;
-    *reinterpret_cast<u32x4*>(sm.Vt + (2 * cp) * PC + 8 * e8) = v0;
-    *reinterpret_cast<u32x4*>(sm.Vt + (2 * cp + 1) * PC + 8 * e8) = v1;
-  }
-  if (wave == 0) {
-    sm.lg[lane] = wave_scan(__logf(alpha[tok0 + lane]));
-    sm.bt[lane] = beta[tok0 + lane];
-  }
-  lds_barrier();
+    float gCw;   // g_C (every wave computes it)
+    {
+      const float lgv = wave_scan(__logf(in.al));
+      const float lC = __shfl(lgv, C - 1);
+      gCw = __expf(lC);
+      if (wave == 0) {
+        const float gv = __expf(lgv);
+        sm.lg[lane] = lgv;
+        sm.g[lane] = gv;
+        sm.kd[lane] = __expf(lC - lgv);
+        sm.bt[lane] = in.be;
+        sm.btg[lane] = in.be * gv;
+      }
+    }
+    // next chunk's inputs (the last chunk of a block loads itself again)
+    {
+      const int nx = cid + (int)gridDim.x < nchunks ? cid + (int)gridDim.x : cid;
+      prep_fetch(in, q, k, v, alpha, beta, (size_t)(nx / nc) * T + (size_t)(nx % nc) * C);
+    }
+    *reinterpret_cast<float*>(wsc + kWsG + (lane & 15) * 4) = gCw;
+    lds_barrier();
 
-  // ---- the sequential pass's decayed operands: diag(g) Q and (diag(g_C/g) K)^T,
-  // this thread's key channels (2cp, 2cp+1) of tokens [8e, 8e+8), from LDS
-  {
-    const float lC = sm.lg[C - 1];
-    uint16_t* Qw = reinterpret_cast<uint16_t*>(wsc + kWsQ);
-    uint16_t* Kw = reinterpret_cast<uint16_t*>(wsc + kWsK);
-    float kh0[8], kh1[8];
+    // ---- K^ fragments to the workspace: fragment (kb, js) = item >> 6
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = 8 * e8 + i;
-      const float lr = sm.lg[r];
-      const float gr = __expf(lr), kr = __expf(lC - lr);
-      const unsigned qw = *reinterpret_cast<const unsigned*>(sm.u.in.Q + r * PQ + 2 * cp);
-      const unsigned kw = *reinterpret_cast<const unsigned*>(sm.u.in.K + r * PQ + 2 * cp);
-      *reinterpret_cast<unsigned*>(Qw + r * kD + 2 * cp) = pack_bf16(gr * lo_bf(qw), gr * hi_bf(qw));
-      kh0[i] = kr * lo_bf(kw);
-      kh1[i] = kr * hi_bf(kw);
-    }
-    u32x4 w0, w1;
+    for (int h = 0; h < 2; ++h) {
+      const int item = tid + NT * h, f = item >> 6, ln = item & 63;
+      const int kk = (f >> 1) * 16 + (ln & 15), j0 = (f & 1) * 32 + (ln >> 4) * 8;
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(sm.Kt + kk * PC + j0);
+      u32x4 w;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      w0[i] = pack_bf16(kh0[2 * i], kh0[2 * i + 1]);
-      w1[i] = pack_bf16(kh1[2 * i], kh1[2 * i + 1]);
+      for (int e = 0; e < 4; ++e)
+        w[e] = pack_bf16(lo_bf(raw[e]) * sm.kd[j0 + 2 * e], hi_bf(raw[e]) * sm.kd[j0 + 2 * e + 1]);
+      *reinterpret_cast<u32x4*>(wsc + kWsK + (size_t)item * 16) = w;
     }
-    *reinterpret_cast<u32x4*>(Kw + (2 * cp) * C + 8 * e8) = w0;
-    *reinterpret_cast<u32x4*>(Kw + (2 * cp + 1) * C + 8 * e8) = w1;
-  }
+    // ---- Gram k.k -> L and scores q.k -> A: 20 tile products over the lower triangle
+    for (int u = wave; u < 20; u += 8) {
+      int rb, cb;
+      tri_pair(u >> 1, rb, cb);
+      const bool sc = u & 1;
+      const uint16_t* X = sc ? sm.Q : sm.rk.K;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        acc = mfma(ld8(X + (rb * 16 + l16) * PQ + ks * 32 + lq * 8),
+                   ld8(sm.rk.K + (cb * 16 + l16) * PQ + ks * 32 + lq * 8), acc);
+      const int j = cb * 16 + l16;
+      const float lj = sm.lg[j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = rb * 16 + lq * 4 + i;
+        const float dec = j <= r ? __expf(sm.lg[r] - lj) : 0.f;
+        if (sc)
+          sm.A[r * PC + j] = f32_to_bf16(dec * acc[i]);
+        else
+          sm.rl.L[r * PF + j] = j < r ? sm.bt[r] * dec * acc[i] : 0.f;
+      }
+    }
+    {   // the zero upper tiles that the 32-wide contraction slices of A reach: (0,1), (2,3)
+      const int t = tid >> 8, e = tid & 255;
+      sm.A[(t * 32 + (e >> 4)) * PC + t * 32 + 16 + (e & 15)] = 0;
+    }
+    lds_barrier();
 
-  // ---- Gram k.k and scores q.k: wave -> row block (w & 3), column blocks 2(w>>2)+{0,1}
-  {
-    const int rb = wave & 3;
+    // ---- T = (I + L)^-1. Diagonal blocks: wave w -> block w >> 1, columns
+    // (w & 1) * 8 + 2 * (lane >> 4) + {0, 1}; lane & 15 is the row.
+    {
+      const int b = wave >> 1, i = l16;
+      const int c0 = (wave & 1) * 8 + 2 * lq, c1 = c0 + 1;
+      float lr[16];
+      const f32x4* Lrow = reinterpret_cast<const f32x4*>(sm.rl.L + (b * 16 + i) * PF + b * 16);
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      const int cb = 2 * (wave >> 2) + cc;
-      f32x4 g = {0.f, 0.f, 0.f, 0.f}, s = {0.f, 0.f, 0.f, 0.f};
-      if (cb <= rb) {
+      for (int s = 0; s < 4; ++s) {
+        const f32x4 x = Lrow[s];
+        lr[4 * s] = x.x; lr[4 * s + 1] = x.y; lr[4 * s + 2] = x.z; lr[4 * s + 3] = x.w;
+      }
+      float a0 = i == c0 ? 1.f : 0.f, a1 = i == c1 ? 1.f : 0.f;
+      DiagSolve<0>::run(lr, a0, a1);
+      sm.T[(b * 16 + i) * PF + b * 16 + c0] = a0;
+      sm.T[(b * 16 + i) * PF + b * 16 + c1] = a1;
+    }
+    lds_barrier();
+    // Blocks below the diagonal, by distance d = I - J:
+    //   T_IJ = -D_I sum_{K=J}^{I-1} L_IK T_KJ   (D_I = T_II), wave J for J < 4 - d
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 kb = ld8(sm.u.in.K + (cb * 16 + l16) * PQ + ks * 32 + lq * 8);
-          g = mfma(ld8(sm.u.in.K + (rb * 16 + l16) * PQ + ks * 32 + lq * 8), kb, g);
-          s = mfma(ld8(sm.u.in.Q + (rb * 16 + l16) * PQ + ks * 32 + lq * 8), kb, s);
+    for (int d = 1; d < 4; ++d) {
+      if (wave < 4 - d) {
+        const int J = wave, I = J + d;
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+        for (int K = J; K < I; ++K)
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            x = mfma4(sm.rl.L[(I * 16 + l16) * PF + K * 16 + 4 * s + lq],
+                      sm.T[(K * 16 + 4 * s + lq) * PF + J * 16 + l16], x);
+        float* scr = sm.rk.scr[wave];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) scr[(4 * lq + i) * 17 + l16] = x[i];
+        wave_lds_sync();
+        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          y = mfma4(sm.T[(I * 16 + l16) * PF + I * 16 + 4 * s + lq], scr[(4 * s + lq) * 17 + l16], y);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm.T[(I * 16 + 4 * lq + i) * PF + J * 16 + l16] = -y[i];
+      }
+      lds_barrier();
+    }
+
+    // ---- T diag(beta g) and T diag(beta) in bf16 (zero above the diagonal blocks)
+    for (int e = tid; e < C * C / 2; e += NT) {
+      const int r = e >> 5, j = 2 * (e & 31);
+      f32x2 t = {0.f, 0.f};
+      if ((j >> 4) <= (r >> 4)) t = *reinterpret_cast<const f32x2*>(sm.T + r * PF + j);
+      *reinterpret_cast<unsigned*>(sm.Tw + r * PC + j) = pack_bf16(t.x * sm.btg[j], t.y * sm.btg[j + 1]);
+      *reinterpret_cast<unsigned*>(sm.Tu + r * PC + j) = pack_bf16(t.x * sm.bt[j], t.y * sm.bt[j + 1]);
+    }
+    lds_barrier();
+
+    // ---- W = Tw K (to LDS as W^T), W^T fragments and U~ = Tu V (workspace, U~^T to LDS).
+    // Row block rb only reaches tokens j <= 16 rb + 15: contraction slices js <= rb / 2.
+    {
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {   // W tile (rb, kb = wave) -> W^T [k][j]
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int js = 0; js <= rb / 2; ++js)
+          acc = mfma(ld8(sm.Tw + (rb * 16 + l16) * PC + js * 32 + lq * 8),
+                     ld8(sm.Kt + (wave * 16 + l16) * PC + js * 32 + lq * 8), acc);
+        *reinterpret_cast<u32x2*>(sm.rl.Wt + (wave * 16 + l16) * PC + rb * 16 + lq * 4) =
+            u32x2{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {      // W^T fragments (rb, ks): rb pairs {0,3}, {1,2}
+        const int rb = h ? 3 - (wave & 3) : (wave & 3), ks = (wave >> 2) + 2 * h;
+        f32x4 t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
+        for (int js = 0; js <= rb / 2; ++js) {
+          const bf16x8 b = ld8(sm.Tw + (rb * 16 + l16) * PC + js * 32 + lq * 8);
+          t0 = mfma(ld8(sm.Kt + (ks * 32 + l16) * PC + js * 32 + lq * 8), b, t0);
+          t1 = mfma(ld8(sm.Kt + (ks * 32 + 16 + l16) * PC + js * 32 + lq * 8), b, t1);
         }
+        *reinterpret_cast<u32x4*>(wsc + kWsW + ((size_t)(rb * 4 + ks) * 64 + lane) * 16) =
+            u32x4{pack_bf16(t0[0], t0[1]), pack_bf16(t0[2], t0[3]), pack_bf16(t1[0], t1[1]),
+                  pack_bf16(t1[2], t1[3])};
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = rb * 16 + lq * 4 + i, j = cb * 16 + l16;
-        const float dec = j <= r ? __expf(sm.lg[r] - sm.lg[j]) : 0.f;
-        sm.L[r * PF + j] = j < r ? sm.bt[r] * dec * g[i] : 0.f;
-        sm.A[r * PC + j] = f32_to_bf16(dec * s[i]);
+      for (int rb = 0; rb < 4; ++rb) {   // U~ tile (rb, vb = wave)
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int js = 0; js <= rb / 2; ++js)
+          acc = mfma(ld8(sm.Tu + (rb * 16 + l16) * PC + js * 32 + lq * 8),
+                     ld8(sm.Vt + (wave * 16 + l16) * PC + js * 32 + lq * 8), acc);
+        const u32x2 p = {pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
+        *reinterpret_cast<u32x2*>(wsc + kWsU + ((size_t)(rb * 8 + wave) * 64 + lane) * 8) = p;
+        *reinterpret_cast<u32x2*>(sm.rk.Ut + (wave * 16 + l16) * PC + rb * 16 + lq * 4) = p;
       }
-    }
-  }
-  lds_barrier();
-
-  // ---- T = (I + L)^-1: diagonal 16 x 16 blocks, one column per thread, in registers
-  if (tid < 64) {
-    const int b = tid >> 4, c = tid & 15, o = b * 16;
-    float x[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const f32x4* Lr = reinterpret_cast<const f32x4*>(sm.L + (o + i) * PF + o);
-      const f32x4 l0 = Lr[0], l1 = Lr[1], l2 = Lr[2], l3 = Lr[3];
-      const float li[16] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w,
-                            l2.x, l2.y, l2.z, l2.w, l3.x, l3.y, l3.z, l3.w};
-      float s = i == c ? 1.f : 0.f;
-#pragma unroll
-      for (int j = 0; j < i; ++j) s -= li[j] * x[j];
-      x[i] = s;
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sm.T[(o + i) * PF + o + c] = x[i];
-  }
-  for (int e = tid; e < C * C; e += NT) {   // strictly upper blocks are zero
-    const int r = e >> 6, c = e & 63;
-    if ((c >> 4) > (r >> 4)) sm.T[r * PF + c] = 0.f;
-  }
-  lds_barrier();
-  // block rows I = 1..3: M_J = sum_{K=J}^{I-1} L_IK T_KJ, then T_IJ = -D_I M_J
-  for (int I = 1; I < 4; ++I) {
-    for (int e = tid; e < I * 256; e += NT) {
-      const int J = e >> 8, i = (e >> 4) & 15, j = e & 15;
-      float s = 0.f;
-      for (int kk = J * 16; kk < I * 16; kk += 4) {
-        const f32x4 lv = *reinterpret_cast<const f32x4*>(sm.L + (I * 16 + i) * PF + kk);
-        s += lv.x * sm.T[kk * PF + J * 16 + j] + lv.y * sm.T[(kk + 1) * PF + J * 16 + j] +
-             lv.z * sm.T[(kk + 2) * PF + J * 16 + j] + lv.w * sm.T[(kk + 3) * PF + J * 16 + j];
-      }
-      sm.M[J * 272 + i * 17 + j] = s;
     }
     lds_barrier();
-    for (int e = tid; e < I * 256; e += NT) {
-      const int J = e >> 8, i = (e >> 4) & 15, j = e & 15;
-      float s = 0.f;
+
+    // ---- Q'^T = (diag(g) Q)^T - W^T A^T as fragments; O~ = A U~ tiles
+    {
 #pragma unroll
-      for (int kk = 0; kk < 16; ++kk) s -= sm.T[(I * 16 + i) * PF + I * 16 + kk] * sm.M[J * 272 + kk * 17 + j];
-      sm.T[(I * 16 + i) * PF + J * 16 + j] = s;
+      for (int h = 0; h < 2; ++h) {
+        const int rb = h ? 3 - (wave & 3) : (wave & 3), ks = (wave >> 2) + 2 * h;
+        f32x4 t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
+        for (int js = 0; js <= rb / 2; ++js) {
+          const bf16x8 b = ld8(sm.A + (rb * 16 + l16) * PC + js * 32 + lq * 8);
+          t0 = mfma(ld8(sm.rl.Wt + (ks * 32 + l16) * PC + js * 32 + lq * 8), b, t0);
+          t1 = mfma(ld8(sm.rl.Wt + (ks * 32 + 16 + l16) * PC + js * 32 + lq * 8), b, t1);
+        }
+        const int r = rb * 16 + l16;
+        const float gr = sm.g[r];
+        const u32x2 qa = *reinterpret_cast<const u32x2*>(sm.Q + r * PQ + ks * 32 + lq * 4);
+        const u32x2 qb = *reinterpret_cast<const u32x2*>(sm.Q + r * PQ + ks * 32 + 16 + lq * 4);
+        *reinterpret_cast<u32x4*>(wsc + kWsQ + ((size_t)(rb * 4 + ks) * 64 + lane) * 16) =
+            u32x4{pack_bf16(gr * lo_bf(qa.x) - t0[0], gr * hi_bf(qa.x) - t0[1]),
+                  pack_bf16(gr * lo_bf(qa.y) - t0[2], gr * hi_bf(qa.y) - t0[3]),
+                  pack_bf16(gr * lo_bf(qb.x) - t1[0], gr * hi_bf(qb.x) - t1[1]),
+                  pack_bf16(gr * lo_bf(qb.y) - t1[2], gr * hi_bf(qb.y) - t1[3])};
+      }
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {   // O~ tile (rb, vb = wave)
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int js = 0; js <= rb / 2; ++js)
+          acc = mfma(ld8(sm.A + (rb * 16 + l16) * PC + js * 32 + lq * 8),
+                     ld8(sm.rk.Ut + (wave * 16 + l16) * PC + js * 32 + lq * 8), acc);
+        *reinterpret_cast<u32x2*>(wsc + kWsO + ((size_t)(rb * 8 + wave) * 64 + lane) * 8) =
+            u32x2{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
+      }
     }
     lds_barrier();
-  }
-
-  // ---- T diag(beta g) and T diag(beta) in bf16 (pairs of columns)
-  for (int e = tid; e < C * C / 2; e += NT) {
-    const int r = e >> 5, j = 2 * (e & 31);
-    const f32x2 t = *reinterpret_cast<const f32x2*>(sm.T + r * PF + j);
-    const float b0 = sm.bt[j], b1 = sm.bt[j + 1];
-    *reinterpret_cast<unsigned*>(sm.Tw + r * PC + j) =
-        pack_bf16(t.x * b0 * __expf(sm.lg[j]), t.y * b1 * __expf(sm.lg[j + 1]));
-    *reinterpret_cast<unsigned*>(sm.Tu + r * PC + j) = pack_bf16(t.x * b0, t.y * b1);
-  }
-  lds_barrier();
-
-  // ---- W = Tw K, U~ = Tu V: wave -> row block (w & 3), column blocks 4(w>>2)..+4; staged
-  {
-    const int rb = wave & 3;
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      const int cb = 4 * (wave >> 2) + cc;
-      f32x4 w = {0.f, 0.f, 0.f, 0.f}, uu = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int js = 0; js < 2; ++js) {
-        w = mfma(ld8(sm.Tw + (rb * 16 + l16) * PC + js * 32 + lq * 8),
-                 ld8(sm.Kt + (cb * 16 + l16) * PC + js * 32 + lq * 8), w);
-        uu = mfma(ld8(sm.Tu + (rb * 16 + l16) * PC + js * 32 + lq * 8),
-                  ld8(sm.Vt + (cb * 16 + l16) * PC + js * 32 + lq * 8), uu);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = rb * 16 + lq * 4 + i, c = cb * 16 + l16;
-        sm.u.out.W[r * PQ + c] = f32_to_bf16(w[i]);
-        sm.u.out.U[r * PQ + c] = f32_to_bf16(uu[i]);
-      }
-    }
-  }
-  lds_barrier();
-  // ---- W, U~, A to the workspace with 16-byte stores
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int p = tid + NT * i, row = p >> 4, seg = p & 15;
-    *reinterpret_cast<u32x4*>(wsc + kWsW + (size_t)(row * kD + seg * 8) * 2) =
-        *reinterpret_cast<const u32x4*>(sm.u.out.W + row * PQ + seg * 8);
-    *reinterpret_cast<u32x4*>(wsc + kWsU + (size_t)(row * kD + seg * 8) * 2) =
-        *reinterpret_cast<const u32x4*>(sm.u.out.U + row * PQ + seg * 8);
-  }
-  {
-    const int row = tid >> 3, seg = tid & 7;
-    *reinterpret_cast<u32x4*>(wsc + kWsA + (size_t)(row * C + seg * 8) * 2) =
-        *reinterpret_cast<const u32x4*>(sm.A + row * PC + seg * 8);
   }
 }
 
-// ============================================================== kernel 2: sequential pass
+// ------------------------------------------------------------------ sequential pass
 namespace gdc {
 
 template <int VT>
 struct SeqSmem {
-  uint16_t W[C * PQ];      // [r][k]
-  uint16_t Qg[C * PQ];     // diag(g) Q   [r][k]
-  uint16_t Kht[kD * PC];   // (diag(g_C/g) K)^T  [k][j]
-  uint16_t A[C * PC];      // [r][j]
-  uint16_t Sb[2][VT * PQ]; // bf16 state tile [v][k], double buffered
-  uint16_t Ut[VT * PC];    // U^T tile [v][j]
-  uint16_t Ob[C * (VT + 8)]; // this chunk's outputs [r][v], stored at the next chunk
+  uint16_t Sb[2][VT * PQ];   // bf16 state tile [v][k], double buffered
+  uint16_t Ut[VT * PC];      // U^T tile [v][j]
+  uint16_t Ot[2][VT * PC];   // outputs^T [v][r], by chunk parity
 };
+
+// One chunk's operands for this wave: waves 0-3 take W (role U), waves 4-7 take Q'
+// (role O), both for token block rb = wave & 3, with U~ resp. O~ of the block's
+// value tiles; every wave takes the K^ fragments of key block `wave` and g_C.
+template <int NVB>
+struct Prefetch {
+  u32x4 m[4];
+  u32x2 x[NVB];
+  u32x4 kh[2];
+  float gc;
+};
+
+template <int NVB>
+__device__ __forceinline__ void fetch_chunk(Prefetch<NVB>& pf, const uint8_t* __restrict__ wsc,
+                                            int vt) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rb = wave & 3;
+  const bool role_o = wave >= 4;
+  const uint8_t* mb = wsc + (role_o ? kWsQ : kWsW) + (size_t)rb * 4096 + lane * 16;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) pf.m[ks] = *reinterpret_cast<const u32x4*>(mb + ks * 1024);
+  const uint8_t* xb = wsc + (role_o ? kWsO : kWsU) + ((size_t)(rb * 8 + vt * NVB) * 64 + lane) * 8;
+#pragma unroll
+  for (int vb = 0; vb < NVB; ++vb) pf.x[vb] = *reinterpret_cast<const u32x2*>(xb + vb * 512);
+#pragma unroll
+  for (int js = 0; js < 2; ++js)
+    pf.kh[js] = *reinterpret_cast<const u32x4*>(wsc + kWsK + ((size_t)(wave * 2 + js) * 64 + lane) * 16);
+  pf.gc = *reinterpret_cast<const float*>(wsc + kWsG + (lane & 15) * 4);
+}
 
 // Stores the staged outputs of the chunk starting at token tok0: VT / 8 per thread,
 // the same single store in every thread.
 template <int VT>
-__device__ __forceinline__ void store_o(const SeqSmem<VT>& sm, uint16_t* __restrict__ o,
+__device__ __forceinline__ void store_o(const uint16_t* __restrict__ Ot, uint16_t* __restrict__ o,
                                         size_t tok0, int v0) {
-  constexpr int EPT = VT / 8, OBS = VT + 8;
-  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-  const int tid = threadIdx.x, row = tid >> 3, col = (tid & 7) * EPT;
-  const uint16_t* src = sm.Ob + row * OBS + col;
-  uint16_t* dst = o + (tok0 + row) * kD + v0 + col;
-  if constexpr (EPT == 2)
-    *reinterpret_cast<unsigned*>(dst) = *reinterpret_cast<const unsigned*>(src);
-  else
-    *reinterpret_cast<u32x2*>(dst) = *reinterpret_cast<const u32x2*>(src);
-}
-
-// One chunk's operands, held in registers while the previous chunk computes: 7
-// sixteen-byte pieces per thread of W, A, diag(g) Q and (diag(g_C/g) K)^T (56 KB per
-// chunk), alpha of token `lane`, and, for the waves that form U, the raw bf16 U~
-// entries in accumulator layout (converting them here would make the compiler wait
-// for the loads at once).
-struct Prefetch {
-  u32x4 w[2], a, qg[2], kh[2];
-  float al;
-  unsigned short ut[4];
-};
-
-template <int VT>
-__device__ __forceinline__ void fetch_chunk(Prefetch& pf, const float* __restrict__ alpha,
-                                            const uint8_t* __restrict__ ws, int n, int nc, int ci,
-                                            int T, int v0) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l16 = lane & 15, lq = lane >> 4;
-  const size_t tok0 = (size_t)n * T + (size_t)ci * C;
-  const uint8_t* wsc = ws + ((size_t)n * nc + ci) * kWsChunk;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const size_t o16 = (size_t)(tid + NT * i) * 16;   // 16-byte piece of a 16 KB tile
-    pf.w[i] = *reinterpret_cast<const u32x4*>(wsc + kWsW + o16);
-    pf.qg[i] = *reinterpret_cast<const u32x4*>(wsc + kWsQ + o16);
-    pf.kh[i] = *reinterpret_cast<const u32x4*>(wsc + kWsK + o16);
+  constexpr int EPT = VT / 8;
+  const int tid = threadIdx.x, r = tid >> 3, c0 = (tid & 7) * EPT;
+  uint16_t* dst = o + (tok0 + r) * kD + v0 + c0;
+  if constexpr (EPT == 2) {
+    *reinterpret_cast<unsigned*>(dst) = unsigned(Ot[c0 * PC + r]) | (unsigned(Ot[(c0 + 1) * PC + r]) << 16);
+  } else {
+    *reinterpret_cast<u32x2*>(dst) =
+        u32x2{unsigned(Ot[c0 * PC + r]) | (unsigned(Ot[(c0 + 1) * PC + r]) << 16),
+              unsigned(Ot[(c0 + 2) * PC + r]) | (unsigned(Ot[(c0 + 3) * PC + r]) << 16)};
   }
-  pf.a = *reinterpret_cast<const u32x4*>(wsc + kWsA + (size_t)tid * 16);
-  pf.al = alpha[tok0 + lane];
-  const int rb = wave & 3, vb = (wave >> 2) & (VT / 16 - 1);   // in bounds for every wave
-  const uint16_t* Uw = reinterpret_cast<const uint16_t*>(wsc + kWsU);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) pf.ut[i] = Uw[(rb * 16 + lq * 4 + i) * kD + v0 + vb * 16 + l16];
 }
 
-// One chunk of the sequential pass: starts the loads of the next chunk into `nx`,
-// stores the previous chunk's staged outputs, then consumes `pf` (this chunk's
-// operands). Every thread issues the same loads and the same store on every chunk
-// (the last chunk loads itself again; the first chunk, FIRST, is a separate copy with
-// nothing to store), so the wait for `pf` counts exactly the memory operations issued
-// after it instead of waiting for them.
+// One chunk: starts the loads of the next chunk's operands into `nx` and stores the
+// previous chunk's outputs, then consumes `pf`. Every thread issues the same loads
+// and the same store on every chunk (the last chunk loads its own operands again; the
+// first, FIRST, has nothing to store) so that the wait for `pf` counts exactly the
+// memory operations issued after it instead of waiting for them.
 template <int VT, bool FIRST>
-__device__ __forceinline__ void gdn_seq_chunk(SeqSmem<VT>& sm, Prefetch& pf, Prefetch& nx,
-                                              f32x4 (&Sacc)[VT / 16], int& cur, int ci, int nc,
-                                              int n, int T, int v0, const float* __restrict__ alpha,
-                                              const uint8_t* __restrict__ ws,
+__device__ __forceinline__ void gdn_seq_chunk(SeqSmem<VT>& sm, const Prefetch<VT / 16>& pf,
+                                              Prefetch<VT / 16>& nx, f32x4 (&Sacc)[VT / 16],
+                                              int& cur, int ci, int nc, size_t chunk0, size_t tok0,
+                                              int vt, const uint8_t* __restrict__ ws,
                                               uint16_t* __restrict__ o) {
   constexpr int NVB = VT / 16;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, lq = lane >> 4;
-  const int kcol = wave * 16 + l16;
-  const size_t tok0 = (size_t)n * T + (size_t)ci * C;
-  fetch_chunk<VT>(nx, alpha, ws, n, nc, min(ci + 1, nc - 1), T, v0);
-  if constexpr (!FIRST) store_o<VT>(sm, o, tok0 - C, v0);
+  const int rb = wave & 3, kcol = wave * 16 + l16, v0 = vt * VT;
+  const bool role_o = wave >= 4;
+  fetch_chunk<NVB>(nx, ws + (chunk0 + min(ci + 1, nc - 1)) * kWsChunk, vt);
+  if constexpr (!FIRST) store_o<VT>(sm.Ot[(ci - 1) & 1], o, tok0 - C, v0);
 
-  // ---- copy this chunk's operands into LDS; g_C from the decays (every wave)
-  const float gC = __expf(__shfl(wave_scan(__logf(pf.al)), C - 1));
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int p = tid + NT * i;
-    *reinterpret_cast<u32x4*>(sm.W + (p >> 4) * PQ + (p & 15) * 8) = pf.w[i];
-    *reinterpret_cast<u32x4*>(sm.Qg + (p >> 4) * PQ + (p & 15) * 8) = pf.qg[i];
-    *reinterpret_cast<u32x4*>(sm.Kht + (p >> 3) * PC + (p & 7) * 8) = pf.kh[i];
-  }
-  *reinterpret_cast<u32x4*>(sm.A + (tid >> 3) * PC + (tid & 7) * 8) = pf.a;
-  f32x4 ut;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) ut[i] = bf16_to_f32(pf.ut[i]);
-  lds_barrier();
-
-  // ---- U = U~ - W S^T: wave -> (row block w & 3, value block w >> 2); to LDS transposed
-  if (wave < 4 * NVB) {
-    const int rb = wave & 3, vb = wave >> 2;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      acc = mfma(ld8(sm.W + (rb * 16 + l16) * PQ + ks * 32 + lq * 8),
-                 ld8(sm.Sb[cur] + (vb * 16 + l16) * PQ + ks * 32 + lq * 8), acc);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      sm.Ut[(vb * 16 + l16) * PC + rb * 16 + lq * 4 + i] = f32_to_bf16(ut[i] - acc[i]);
-  }
-  lds_barrier();
-
-  // ---- O = diag(g) Q S^T + A U (same tile assignment)
-  if (wave < 4 * NVB) {
-    const int rb = wave & 3, vb = wave >> 2;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      acc = mfma(ld8(sm.Qg + (rb * 16 + l16) * PQ + ks * 32 + lq * 8),
-                 ld8(sm.Sb[cur] + (vb * 16 + l16) * PQ + ks * 32 + lq * 8), acc);
-#pragma unroll
-    for (int js = 0; js < 2; ++js)
-      if (js * 32 <= rb * 16 + 15)
-        acc = mfma(ld8(sm.A + (rb * 16 + l16) * PC + js * 32 + lq * 8),
-                   ld8(sm.Ut + (vb * 16 + l16) * PC + js * 32 + lq * 8), acc);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      sm.Ob[(rb * 16 + lq * 4 + i) * (VT + 8) + vb * 16 + l16] = f32_to_bf16(acc[i]);
-  }
-
-  // ---- S <- g_C S + U^T (diag(g_C/g) K): key block = wave; next bf16 copy
+  // ---- role U: U = U~ - W S^T; role O: O = O~ + Q' S^T (to LDS, transposed)
+  const float sgn = role_o ? 1.f : -1.f;
+  uint16_t* dst = (role_o ? sm.Ot[ci & 1] : sm.Ut) + l16 * PC + rb * 16 + lq * 4;
 #pragma unroll
   for (int vb = 0; vb < NVB; ++vb) {
-    f32x4 acc = Sacc[vb] * gC;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint16_t* sp = sm.Sb[cur] + (vb * 16 + l16) * PQ + ks * 32 + lq * 4;
+      const u32x2 lo = *reinterpret_cast<const u32x2*>(sp);
+      const u32x2 hi = *reinterpret_cast<const u32x2*>(sp + 16);
+      acc = mfma(as_bf8(pf.m[ks]), as_bf8(u32x4{lo.x, lo.y, hi.x, hi.y}), acc);
+    }
+    const u32x2 xv = pf.x[vb];
+    *reinterpret_cast<u32x2*>(dst + vb * 16 * PC) =
+        u32x2{pack_bf16(lo_bf(xv.x) + sgn * acc[0], hi_bf(xv.x) + sgn * acc[1]),
+              pack_bf16(lo_bf(xv.y) + sgn * acc[2], hi_bf(xv.y) + sgn * acc[3])};
+  }
+  lds_barrier();
+
+  // ---- S <- g_C S + U^T K^: key block = wave; next bf16 copy
+#pragma unroll
+  for (int vb = 0; vb < NVB; ++vb) {
+    f32x4 acc = Sacc[vb] * pf.gc;
 #pragma unroll
     for (int js = 0; js < 2; ++js)
-      acc = mfma(ld8(sm.Ut + (vb * 16 + l16) * PC + js * 32 + lq * 8),
-                 ld8(sm.Kht + (wave * 16 + l16) * PC + js * 32 + lq * 8), acc);
+      acc = mfma(ld8(sm.Ut + (vb * 16 + l16) * PC + js * 32 + lq * 8), as_bf8(pf.kh[js]), acc);
     Sacc[vb] = acc;
 #pragma unroll
     for (int i = 0; i < 4; ++i) sm.Sb[cur ^ 1][(vb * 16 + lq * 4 + i) * PQ + kcol] = f32_to_bf16(acc[i]);
@@ -439,7 +510,6 @@ __device__ __forceinline__ void gdn_seq_chunk(SeqSmem<VT>& sm, Prefetch& pf, Pre
 
 template <int VT>
 __global__ __launch_bounds__(512) void gdn_chunk_seq_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ alpha,
     const uint8_t* __restrict__ ws, const float* __restrict__ S0, float* __restrict__ ST,
     uint16_t* __restrict__ o, int N, int T) {
   using namespace gdc;
@@ -477,17 +547,21 @@ __global__ __launch_bounds__(512) void gdn_chunk_seq_kernel(
     }
 
   if (nc > 0) {
-    Prefetch pa, pb;
+    const size_t chunk0 = (size_t)n * nc, tokn = (size_t)n * T;
+    Prefetch<NVB> pa, pb;
     int cur = 0;
-    fetch_chunk<VT>(pa, alpha, ws, n, nc, 0, T, v0);
-    gdn_seq_chunk<VT, true>(sm, pa, pb, Sacc, cur, 0, nc, n, T, v0, alpha, ws, o);
+    fetch_chunk<NVB>(pa, ws + chunk0 * kWsChunk, vt);
+    lds_barrier();
+    gdn_seq_chunk<VT, true>(sm, pa, pb, Sacc, cur, 0, nc, chunk0, tokn, vt, ws, o);
     int ci = 1;
     for (; ci + 1 < nc; ci += 2) {
-      gdn_seq_chunk<VT, false>(sm, pb, pa, Sacc, cur, ci, nc, n, T, v0, alpha, ws, o);
-      gdn_seq_chunk<VT, false>(sm, pa, pb, Sacc, cur, ci + 1, nc, n, T, v0, alpha, ws, o);
+      gdn_seq_chunk<VT, false>(sm, pb, pa, Sacc, cur, ci, nc, chunk0, tokn + (size_t)ci * C, vt, ws, o);
+      gdn_seq_chunk<VT, false>(sm, pa, pb, Sacc, cur, ci + 1, nc, chunk0, tokn + (size_t)(ci + 1) * C,
+                               vt, ws, o);
     }
-    if (ci < nc) gdn_seq_chunk<VT, false>(sm, pb, pa, Sacc, cur, ci, nc, n, T, v0, alpha, ws, o);
-    store_o<VT>(sm, o, (size_t)n * T + (size_t)(nc - 1) * C, v0);
+    if (ci < nc)
+      gdn_seq_chunk<VT, false>(sm, pb, pa, Sacc, cur, ci, nc, chunk0, tokn + (size_t)ci * C, vt, ws, o);
+    store_o<VT>(sm.Ot[(nc - 1) & 1], o, tokn + (size_t)(nc - 1) * C, v0);
   }
 
 #pragma unroll
@@ -521,7 +595,8 @@ extern "C" int gdn_chunk_fwd(const void* q, const void* k, const void* v, const 
   if (N == 0) return clear_error();
   if (!ST || (T > 0 && (!q || !k || !v || !alpha || !beta || !o)))
     return set_error(GDNRT_EINVAL, "gdn_chunk_fwd: null pointer argument");
-  const size_t need = T > 0 ? (size_t)N * (T / kChunk) * gdc::kWsChunk : 0;
+  const size_t nchunks = (size_t)N * (T / kChunk);
+  const size_t need = nchunks * gdc::kWsChunk;
   if (ws_bytes < need || (need && !workspace))
     return set_error(GDNRT_EINVAL, "gdn_chunk_fwd: workspace of %zu bytes needed, %zu given", need, ws_bytes);
   if ((T > 0 && (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(workspace) ||
@@ -540,20 +615,20 @@ extern "C" int gdn_chunk_fwd(const void* q, const void* k, const void* v, const 
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   if (T > 0) {
-    hipLaunchKernelGGL(gdn_chunk_prep_kernel, dim3((unsigned)(N * (T / kChunk))), dim3(gdc::NT), 0, s,
+    // one persistent block per CU (the LDS of a block fills most of one)
+    const unsigned grid = (unsigned)(nchunks < 256 ? nchunks : 256);
+    hipLaunchKernelGGL(gdn_chunk_prep_kernel, dim3(grid), dim3(gdc::NT), 0, s,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                       static_cast<const uint16_t*>(v), alpha, beta, ws, T);
+                       static_cast<const uint16_t*>(v), alpha, beta, ws, T, (int)nchunks);
     int rc = check_launch("gdn_chunk_fwd (prep)");
     if (rc != GDNRT_OK) return rc;
   }
   // value tiles of 16 when there are too few sequences to fill the chip with 32
   if (N * 4 < 256)
-    hipLaunchKernelGGL((gdn_chunk_seq_kernel<16>), dim3((unsigned)(N * 8)), dim3(gdc::NT), 0, s,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), alpha, ws,
-                       S0, ST, static_cast<uint16_t*>(o), N, T);
+    hipLaunchKernelGGL((gdn_chunk_seq_kernel<16>), dim3((unsigned)(N * 8)), dim3(gdc::NT), 0, s, ws, S0,
+                       ST, static_cast<uint16_t*>(o), N, T);
   else
-    hipLaunchKernelGGL((gdn_chunk_seq_kernel<32>), dim3((unsigned)(N * 4)), dim3(gdc::NT), 0, s,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), alpha, ws,
-                       S0, ST, static_cast<uint16_t*>(o), N, T);
+    hipLaunchKernelGGL((gdn_chunk_seq_kernel<32>), dim3((unsigned)(N * 4)), dim3(gdc::NT), 0, s, ws, S0,
+                       ST, static_cast<uint16_t*>(o), N, T);
   return check_launch("gdn_chunk_fwd");
 }

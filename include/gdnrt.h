@@ -103,8 +103,9 @@ GDNRT_API int gla_chunk_fwd(const void* q, const void* k, const void* v, const f
  *   alpha (in (0,1)), beta [N][T] fp32.   S0 [N][dv][dk] fp32 or NULL (zero).
  *   ST [N][dv][dk] fp32 final state (may equal S0).
  *   workspace: caller-owned device memory of gdn_chunk_fwd_workspace_bytes() bytes,
- *   16-byte aligned, overwritten (the per-chunk state-independent operands W, U~, A,
- *   diag(g) Q and (diag(g_C/g) K)^T in bf16, 73,728 bytes per chunk).
+ *   16-byte aligned, overwritten (the per-chunk state-independent operands in bf16:
+ *   W, U~, Q' = diag(g) Q - A W, O~ = A U~ and diag(g_C/g) K, plus g_C; 81,984 bytes
+ *   per chunk).
  * T must be a multiple of chunk (64).
  */
 GDNRT_API int gdn_chunk_fwd(const void* q, const void* k, const void* v,

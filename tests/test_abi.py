@@ -69,7 +69,7 @@ def test_chunk_validation(lib):
     assert g(p, p, p, p, None, p, p, 2, 128, 128, 128, 32, 1, None) == ESHAPE     # chunk
     assert g(p, p, p, p, None, p, p, 2, 128, 128, 128, 64, 0, None) == EDTYPE     # fp32 io
     d = lib.gdn_chunk_fwd
-    assert lib.gdn_chunk_fwd_workspace_bytes(32, 16384, 128, 128, 64) == 32 * 256 * 73728
+    assert lib.gdn_chunk_fwd_workspace_bytes(32, 16384, 128, 128, 64) == 32 * 256 * 81984
     assert lib.gdn_chunk_fwd_workspace_bytes(32, 100, 128, 128, 64) == 0
     assert d(p, p, p, p, p, None, p, p, 2, 128, 128, 128, 64, 1, p, 10, None) == EINVAL  # workspace
 
