@@ -111,29 +111,50 @@ struct DiagSolve<16> {
 
 // ------------------------------------------------------------------ per-chunk prep
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// MFMA operand from a row-major [contraction][column] bf16 matrix in LDS, through
+// the transposing LDS read (ds_read_b64_tr_b16): lane (l16, lq) receives
+// X[c0 + 8 lq + e][n0 + l16], e = 0..7. Within a group of 16 lanes, lane 4a + b of
+// the result takes element b of the rows addressed by lanes a, a + 4, a + 8, a + 12,
+// so lane j of group g addresses row c0 + 8g + j/4 (+4 for the second half) at
+// column n0 + 4 (j % 4).
+__device__ __forceinline__ bf16x8 ld_tr8(const uint16_t* X, int pitch, int c0, int n0) {
+  const int lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
+  const uint16_t* p = X + (c0 + 8 * g + (j >> 2)) * pitch + n0 + 4 * (j & 3);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * pitch));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 struct PrepSmem {
-  union {                   // k row-major until the Gram products; inverse scratch; U~^T
-    uint16_t K[C * PQ];     // [j][k]
-    float scr[8][16 * 17];  // one 16 x 16 fp32 tile per wave
-    uint16_t Ut[kD * PC];   // U~^T [v][j]
-  } rk;
+  uint16_t Q[C * PQ];       // [r][k]
+  uint16_t K[C * PQ];       // [j][k]
+  uint16_t V[C * PQ];       // [j][v]
+  uint16_t A[C * PC];       // masked decayed scores [r][j]
   union {
     float L[C * PF];        // strict lower part of (I + L), fp32
     uint16_t Wt[kD * PC];   // W^T [k][j]
   } rl;
-  uint16_t Q[C * PQ];       // [r][k]
-  uint16_t Kt[kD * PC];     // [k][j]
-  uint16_t Vt[kD * PC];     // [v][j]
-  uint16_t A[C * PC];       // masked decayed scores [r][j]
-  float T[C * PF];          // (I + L)^-1, lower blocks
-  uint16_t Tw[C * PC];      // T diag(beta g)
-  uint16_t Tu[C * PC];      // T diag(beta)
+  union {
+    float T[C * PF];        // (I + L)^-1, lower blocks
+    uint16_t Ut[kD * PC];   // U~^T [v][j]
+  } rt;
+  union {
+    float scr[8][16 * 17];  // one 16 x 16 fp32 tile per wave (inverse)
+    struct {
+      uint16_t Tw[C * PC];  // T diag(beta g)
+      uint16_t Tu[C * PC];  // T diag(beta)
+    } t;
+  } rw;
   float lg[C], g[C], kd[C], bt[C], btg[C];   // log g, g, g_C/g, beta, beta g
 };
 
-// one chunk's inputs for thread (cp = key-channel pair, e8 = token group of 8)
+// one chunk's inputs for this thread: 16-byte pieces p = tid + 512 h (h = 0, 1) of
+// q, k, v (token p >> 4, channels 8 (p & 15) ..), and alpha, beta of token tid % 64
 struct PrepIn {
-  unsigned q[8], k[8], v[8];
+  u32x4 q[2], k[2], v[2];
   float al, be;
 };
 
@@ -142,16 +163,17 @@ __device__ __forceinline__ void prep_fetch(PrepIn& in, const uint16_t* __restric
                                            const uint16_t* __restrict__ v,
                                            const float* __restrict__ alpha,
                                            const float* __restrict__ beta, size_t tok0) {
-  const int tid = threadIdx.x, cp = tid & 63, e8 = tid >> 6;
+  const int tid = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const size_t off = (tok0 + 8 * e8 + i) * kD + 2 * cp;
-    in.q[i] = *reinterpret_cast<const unsigned*>(q + off);
-    in.k[i] = *reinterpret_cast<const unsigned*>(k + off);
-    in.v[i] = *reinterpret_cast<const unsigned*>(v + off);
+  for (int h = 0; h < 2; ++h) {
+    const int p = tid + NT * h;
+    const size_t off = (tok0 + (p >> 4)) * kD + (p & 15) * 8;
+    in.q[h] = *reinterpret_cast<const u32x4*>(q + off);
+    in.k[h] = *reinterpret_cast<const u32x4*>(k + off);
+    in.v[h] = *reinterpret_cast<const u32x4*>(v + off);
   }
-  in.al = alpha[tok0 + cp];
-  in.be = beta[tok0 + cp];
+  in.al = alpha[tok0 + (tid & 63)];
+  in.be = beta[tok0 + (tid & 63)];
 }
 
 // lower-triangle 16 x 16 tile pairs (rb, cb), cb <= rb
@@ -173,7 +195,6 @@ __global__ __launch_bounds__(512) void gdn_chunk_prep_kernel(
   __shared__ PrepSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lq = lane >> 4;
-  const int cp = tid & 63, e8 = tid >> 6;
   const int nc = T / C;
 
   PrepIn in;
@@ -182,26 +203,13 @@ __global__ __launch_bounds__(512) void gdn_chunk_prep_kernel(
   for (; cid < nchunks; cid += gridDim.x) {
     uint8_t* wsc = ws + (size_t)cid * kWsChunk;
 
-    // ---- stage q, k (row-major), k^T and v^T; decays
+    // ---- stage q, k, v (row-major); decays
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = 8 * e8 + i;
-      *reinterpret_cast<unsigned*>(sm.Q + r * PQ + 2 * cp) = in.q[i];
-      *reinterpret_cast<unsigned*>(sm.rk.K + r * PQ + 2 * cp) = in.k[i];
-    }
-    {
-      u32x4 k0, k1, v0, v1;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        k0[i] = (in.k[2 * i] & 0xffffu) | (in.k[2 * i + 1] << 16);
-        k1[i] = (in.k[2 * i] >> 16) | (in.k[2 * i + 1] & 0xffff0000u);
-        v0[i] = (in.v[2 * i] & 0xffffu) | (in.v[2 * i + 1] << 16);
-        v1[i] = (in.v[2 * i] >> 16) | (in.v[2 * i + 1] & 0xffff0000u);
-      }
-      *reinterpret_cast<u32x4*>(sm.Kt + (2 * cp) * PC + 8 * e8) = k0;
-      *reinterpret_cast<u32x4*>(sm.Kt + (2 * cp + 1) * PC + 8 * e8) = k1;
-      *reinterpret_cast<u32x4*>(sm.Vt + (2 * cp) * PC + 8 * e8) = v0;
-      *reinterpret_cast<u32x4*>(sm.Vt + (2 * cp + 1) * PC + 8 * e8) = v1;
+    for (int h = 0; h < 2; ++h) {
+      const int p = tid + NT * h, o = (p >> 4) * PQ + (p & 15) * 8;
+      *reinterpret_cast<u32x4*>(sm.Q + o) = in.q[h];
+      *reinterpret_cast<u32x4*>(sm.K + o) = in.k[h];
+      *reinterpret_cast<u32x4*>(sm.V + o) = in.v[h];
     }
     float gCw;   // g_C (every wave computes it)
     {
@@ -225,29 +233,28 @@ __global__ __launch_bounds__(512) void gdn_chunk_prep_kernel(
     *reinterpret_cast<float*>(wsc + kWsG + (lane & 15) * 4) = gCw;
     lds_barrier();
 
-    // ---- K^ fragments to the workspace: fragment (kb, js) = item >> 6
+    // ---- K^ fragments (kb, js) = (f >> 1, f & 1), f = wave + 8 h, to the workspace
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int item = tid + NT * h, f = item >> 6, ln = item & 63;
-      const int kk = (f >> 1) * 16 + (ln & 15), j0 = (f & 1) * 32 + (ln >> 4) * 8;
-      const u32x4 raw = *reinterpret_cast<const u32x4*>(sm.Kt + kk * PC + j0);
+      const int f = wave + 8 * h, j0 = (f & 1) * 32 + lq * 8;
+      const u32x4 raw = __builtin_bit_cast(u32x4, ld_tr8(sm.K, PQ, (f & 1) * 32, (f >> 1) * 16));
       u32x4 w;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         w[e] = pack_bf16(lo_bf(raw[e]) * sm.kd[j0 + 2 * e], hi_bf(raw[e]) * sm.kd[j0 + 2 * e + 1]);
-      *reinterpret_cast<u32x4*>(wsc + kWsK + (size_t)item * 16) = w;
+      *reinterpret_cast<u32x4*>(wsc + kWsK + ((size_t)f * 64 + lane) * 16) = w;
     }
     // ---- Gram k.k -> L and scores q.k -> A: 20 tile products over the lower triangle
     for (int u = wave; u < 20; u += 8) {
       int rb, cb;
       tri_pair(u >> 1, rb, cb);
       const bool sc = u & 1;
-      const uint16_t* X = sc ? sm.Q : sm.rk.K;
+      const uint16_t* X = sc ? sm.Q : sm.K;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
         acc = mfma(ld8(X + (rb * 16 + l16) * PQ + ks * 32 + lq * 8),
-                   ld8(sm.rk.K + (cb * 16 + l16) * PQ + ks * 32 + lq * 8), acc);
+                   ld8(sm.K + (cb * 16 + l16) * PQ + ks * 32 + lq * 8), acc);
       const int j = cb * 16 + l16;
       const float lj = sm.lg[j];
 #pragma unroll
@@ -280,8 +287,8 @@ __global__ __launch_bounds__(512) void gdn_chunk_prep_kernel(
       }
       float a0 = i == c0 ? 1.f : 0.f, a1 = i == c1 ? 1.f : 0.f;
       DiagSolve<0>::run(lr, a0, a1);
-      sm.T[(b * 16 + i) * PF + b * 16 + c0] = a0;
-      sm.T[(b * 16 + i) * PF + b * 16 + c1] = a1;
+      sm.rt.T[(b * 16 + i) * PF + b * 16 + c0] = a0;
+      sm.rt.T[(b * 16 + i) * PF + b * 16 + c1] = a1;
     }
     lds_barrier();
     // Blocks below the diagonal, by distance d = I - J:
@@ -295,17 +302,17 @@ __global__ __launch_bounds__(512) void gdn_chunk_prep_kernel(
 #pragma unroll
           for (int s = 0; s < 4; ++s)
             x = mfma4(sm.rl.L[(I * 16 + l16) * PF + K * 16 + 4 * s + lq],
-                      sm.T[(K * 16 + 4 * s + lq) * PF + J * 16 + l16], x);
-        float* scr = sm.rk.scr[wave];
+                      sm.rt.T[(K * 16 + 4 * s + lq) * PF + J * 16 + l16], x);
+        float* scr = sm.rw.scr[wave];
 #pragma unroll
         for (int i = 0; i < 4; ++i) scr[(4 * lq + i) * 17 + l16] = x[i];
         wave_lds_sync();
         f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-          y = mfma4(sm.T[(I * 16 + l16) * PF + I * 16 + 4 * s + lq], scr[(4 * s + lq) * 17 + l16], y);
+          y = mfma4(sm.rt.T[(I * 16 + l16) * PF + I * 16 + 4 * s + lq], scr[(4 * s + lq) * 17 + l16], y);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sm.T[(I * 16 + 4 * lq + i) * PF + J * 16 + l16] = -y[i];
+        for (int i = 0; i < 4; ++i) sm.rt.T[(I * 16 + 4 * lq + i) * PF + J * 16 + l16] = -y[i];
       }
       lds_barrier();
     }
@@ -314,9 +321,9 @@ __global__ __launch_bounds__(512) void gdn_chunk_prep_kernel(
     for (int e = tid; e < C * C / 2; e += NT) {
       const int r = e >> 5, j = 2 * (e & 31);
       f32x2 t = {0.f, 0.f};
-      if ((j >> 4) <= (r >> 4)) t = *reinterpret_cast<const f32x2*>(sm.T + r * PF + j);
-      *reinterpret_cast<unsigned*>(sm.Tw + r * PC + j) = pack_bf16(t.x * sm.btg[j], t.y * sm.btg[j + 1]);
-      *reinterpret_cast<unsigned*>(sm.Tu + r * PC + j) = pack_bf16(t.x * sm.bt[j], t.y * sm.bt[j + 1]);
+      if ((j >> 4) <= (r >> 4)) t = *reinterpret_cast<const f32x2*>(sm.rt.T + r * PF + j);
+      *reinterpret_cast<unsigned*>(sm.rw.t.Tw + r * PC + j) = pack_bf16(t.x * sm.btg[j], t.y * sm.btg[j + 1]);
+      *reinterpret_cast<unsigned*>(sm.rw.t.Tu + r * PC + j) = pack_bf16(t.x * sm.bt[j], t.y * sm.bt[j + 1]);
     }
     lds_barrier();
 
@@ -328,8 +335,8 @@ __global__ __launch_bounds__(512) void gdn_chunk_prep_kernel(
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int js = 0; js <= rb / 2; ++js)
-          acc = mfma(ld8(sm.Tw + (rb * 16 + l16) * PC + js * 32 + lq * 8),
-                     ld8(sm.Kt + (wave * 16 + l16) * PC + js * 32 + lq * 8), acc);
+          acc = mfma(ld8(sm.rw.t.Tw + (rb * 16 + l16) * PC + js * 32 + lq * 8),
+                     ld_tr8(sm.K, PQ, js * 32, wave * 16), acc);
         *reinterpret_cast<u32x2*>(sm.rl.Wt + (wave * 16 + l16) * PC + rb * 16 + lq * 4) =
             u32x2{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
       }
@@ -338,9 +345,9 @@ __global__ __launch_bounds__(512) void gdn_chunk_prep_kernel(
         const int rb = h ? 3 - (wave & 3) : (wave & 3), ks = (wave >> 2) + 2 * h;
         f32x4 t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
         for (int js = 0; js <= rb / 2; ++js) {
-          const bf16x8 b = ld8(sm.Tw + (rb * 16 + l16) * PC + js * 32 + lq * 8);
-          t0 = mfma(ld8(sm.Kt + (ks * 32 + l16) * PC + js * 32 + lq * 8), b, t0);
-          t1 = mfma(ld8(sm.Kt + (ks * 32 + 16 + l16) * PC + js * 32 + lq * 8), b, t1);
+          const bf16x8 b = ld8(sm.rw.t.Tw + (rb * 16 + l16) * PC + js * 32 + lq * 8);
+          t0 = mfma(ld_tr8(sm.K, PQ, js * 32, ks * 32), b, t0);
+          t1 = mfma(ld_tr8(sm.K, PQ, js * 32, ks * 32 + 16), b, t1);
         }
         *reinterpret_cast<u32x4*>(wsc + kWsW + ((size_t)(rb * 4 + ks) * 64 + lane) * 16) =
             u32x4{pack_bf16(t0[0], t0[1]), pack_bf16(t0[2], t0[3]), pack_bf16(t1[0], t1[1]),
@@ -351,11 +358,11 @@ __global__ __launch_bounds__(512) void gdn_chunk_prep_kernel(
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int js = 0; js <= rb / 2; ++js)
-          acc = mfma(ld8(sm.Tu + (rb * 16 + l16) * PC + js * 32 + lq * 8),
-                     ld8(sm.Vt + (wave * 16 + l16) * PC + js * 32 + lq * 8), acc);
+          acc = mfma(ld8(sm.rw.t.Tu + (rb * 16 + l16) * PC + js * 32 + lq * 8),
+                     ld_tr8(sm.V, PQ, js * 32, wave * 16), acc);
         const u32x2 p = {pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
         *reinterpret_cast<u32x2*>(wsc + kWsU + ((size_t)(rb * 8 + wave) * 64 + lane) * 8) = p;
-        *reinterpret_cast<u32x2*>(sm.rk.Ut + (wave * 16 + l16) * PC + rb * 16 + lq * 4) = p;
+        *reinterpret_cast<u32x2*>(sm.rt.Ut + (wave * 16 + l16) * PC + rb * 16 + lq * 4) = p;
       }
     }
     lds_barrier();
@@ -387,7 +394,7 @@ __global__ __launch_bounds__(512) void gdn_chunk_prep_kernel(
 #pragma unroll
         for (int js = 0; js <= rb / 2; ++js)
           acc = mfma(ld8(sm.A + (rb * 16 + l16) * PC + js * 32 + lq * 8),
-                     ld8(sm.rk.Ut + (wave * 16 + l16) * PC + js * 32 + lq * 8), acc);
+                     ld8(sm.rt.Ut + (wave * 16 + l16) * PC + js * 32 + lq * 8), acc);
         *reinterpret_cast<u32x2*>(wsc + kWsO + ((size_t)(rb * 8 + wave) * 64 + lane) * 8) =
             u32x2{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
       }
@@ -398,6 +405,9 @@ __global__ __launch_bounds__(512) void gdn_chunk_prep_kernel(
 
 // ------------------------------------------------------------------ sequential pass
 namespace gdc {
+
+constexpr int kAhead = 2;   // chunks of operands in flight ahead of the one in use
+constexpr int kWarm = 2;    // chunks between the L2 warm-up of a chunk and its loads
 
 template <int VT>
 struct SeqSmem {
@@ -415,17 +425,24 @@ struct Prefetch {
   u32x2 x[NVB];
   u32x4 kh[2];
   float gc;
+  unsigned warm;   // one word of a line touched to bring it into L2 early (unused)
 };
 
-template <int NVB>
+// The loads of a set are issued in two parts (PART 0: the W or Q' fragments; PART 1:
+// the rest) at two points of a chunk, so that the address units work through them
+// while the waves compute instead of holding the waves at a burst of loads.
+template <int NVB, int PART>
 __device__ __forceinline__ void fetch_chunk(Prefetch<NVB>& pf, const uint8_t* __restrict__ wsc,
-                                            int vt) {
+                                            const uint8_t* __restrict__ warm, int vt) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rb = wave & 3;
   const bool role_o = wave >= 4;
-  const uint8_t* mb = wsc + (role_o ? kWsQ : kWsW) + (size_t)rb * 4096 + lane * 16;
+  if constexpr (PART == 0) {
+    const uint8_t* mb = wsc + (role_o ? kWsQ : kWsW) + (size_t)rb * 4096 + lane * 16;
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) pf.m[ks] = *reinterpret_cast<const u32x4*>(mb + ks * 1024);
+    for (int ks = 0; ks < 4; ++ks) pf.m[ks] = *reinterpret_cast<const u32x4*>(mb + ks * 1024);
+    return;
+  }
   const uint8_t* xb = wsc + (role_o ? kWsO : kWsU) + ((size_t)(rb * 8 + vt * NVB) * 64 + lane) * 8;
 #pragma unroll
   for (int vb = 0; vb < NVB; ++vb) pf.x[vb] = *reinterpret_cast<const u32x2*>(xb + vb * 512);
@@ -433,6 +450,21 @@ __device__ __forceinline__ void fetch_chunk(Prefetch<NVB>& pf, const uint8_t* __
   for (int js = 0; js < 2; ++js)
     pf.kh[js] = *reinterpret_cast<const u32x4*>(wsc + kWsK + ((size_t)(wave * 2 + js) * 64 + lane) * 16);
   pf.gc = *reinterpret_cast<const float*>(wsc + kWsG + (lane & 15) * 4);
+  // L2 warm-up of a later chunk: the 8 / NVB value tiles of one sequence split its 384
+  // lines of W, Q' and K^ (48 NVB each) and each touches the 32 NVB lines of its own
+  // U~, O~; the remaining threads all touch one line
+  {
+    const int t = threadIdx.x;
+    size_t off = 0;
+    if (t < 48 * NVB) {
+      off = (size_t)(vt * 48 * NVB + t) * 128;
+    } else if (t < 80 * NVB) {
+      const int j = t - 48 * NVB, reg = j / (16 * NVB), w = j % (16 * NVB);
+      off = (reg ? kWsO : kWsU) + (size_t)(((w >> 2) / NVB) * 8 + vt * NVB + (w >> 2) % NVB) * 512 +
+            (w & 3) * 128;
+    }
+    pf.warm = *reinterpret_cast<const unsigned*>(warm + off);
+  }
 }
 
 // Stores the staged outputs of the chunk starting at token tok0: VT / 8 per thread,
@@ -452,24 +484,32 @@ __device__ __forceinline__ void store_o(const uint16_t* __restrict__ Ot, uint16_
   }
 }
 
-// One chunk: starts the loads of the next chunk's operands into `nx` and stores the
-// previous chunk's outputs, then consumes `pf`. Every thread issues the same loads
-// and the same store on every chunk (the last chunk loads its own operands again; the
-// first, FIRST, has nothing to store) so that the wait for `pf` counts exactly the
-// memory operations issued after it instead of waiting for them.
+// One chunk: starts the loads of the operands of the chunk kAhead chunks later into
+// `nx` and stores the previous chunk's outputs, then consumes `pf`. Every thread
+// issues the same loads and the same store on every chunk (past the end the last
+// chunk's operands are loaded again; the first chunk, FIRST, has nothing to store) so
+// that the wait for `pf` counts exactly the memory operations issued after it instead
+// of waiting for them.
 template <int VT, bool FIRST>
 __device__ __forceinline__ void gdn_seq_chunk(SeqSmem<VT>& sm, const Prefetch<VT / 16>& pf,
                                               Prefetch<VT / 16>& nx, f32x4 (&Sacc)[VT / 16],
-                                              int& cur, int ci, int nc, size_t chunk0, size_t tok0,
-                                              int vt, const uint8_t* __restrict__ ws,
+                                              int& cur, unsigned& sink, int ci, int nc, size_t chunk0,
+                                              size_t tok0, int vt, const uint8_t* __restrict__ ws,
                                               uint16_t* __restrict__ o) {
   constexpr int NVB = VT / 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, lq = lane >> 4;
   const int rb = wave & 3, kcol = wave * 16 + l16, v0 = vt * VT;
   const bool role_o = wave >= 4;
-  fetch_chunk<NVB>(nx, ws + (chunk0 + min(ci + 1, nc - 1)) * kWsChunk, vt);
+  const uint8_t* nxc = ws + (chunk0 + min(ci + kAhead, nc - 1)) * kWsChunk;
+  const uint8_t* wmc = ws + (chunk0 + min(ci + kAhead + kWarm, nc - 1)) * kWsChunk;
+  fetch_chunk<NVB, 0>(nx, nxc, wmc, vt);
+  sink ^= pf.warm;
   if constexpr (!FIRST) store_o<VT>(sm.Ot[(ci - 1) & 1], o, tok0 - C, v0);
+
+  // keeps the unpacking of the operand sets still in flight from being moved up to
+  // here, where it would have to wait for their loads
+  __builtin_amdgcn_sched_barrier(0);
 
   // ---- role U: U = U~ - W S^T; role O: O = O~ + Q' S^T (to LDS, transposed)
   const float sgn = role_o ? 1.f : -1.f;
@@ -489,6 +529,7 @@ __device__ __forceinline__ void gdn_seq_chunk(SeqSmem<VT>& sm, const Prefetch<VT
         u32x2{pack_bf16(lo_bf(xv.x) + sgn * acc[0], hi_bf(xv.x) + sgn * acc[1]),
               pack_bf16(lo_bf(xv.y) + sgn * acc[2], hi_bf(xv.y) + sgn * acc[3])};
   }
+  fetch_chunk<NVB, 1>(nx, nxc, wmc, vt);
   lds_barrier();
 
   // ---- S <- g_C S + U^T K^: key block = wave; next bf16 copy
@@ -548,20 +589,39 @@ __global__ __launch_bounds__(512) void gdn_chunk_seq_kernel(
 
   if (nc > 0) {
     const size_t chunk0 = (size_t)n * nc, tokn = (size_t)n * T;
-    Prefetch<NVB> pa, pb;
+    // three operand sets in rotation: chunk ci uses set ci % 3 and loads chunk ci + 2
+    // into set (ci + 2) % 3
+    static_assert(kAhead == 2, "three-set rotation");
+    Prefetch<NVB> p0, p1, p2;
     int cur = 0;
-    fetch_chunk<NVB>(pa, ws + chunk0 * kWsChunk, vt);
+    unsigned sink = 0;
+    {
+      const uint8_t* c0 = ws + chunk0 * kWsChunk;
+      const uint8_t* c1 = ws + (chunk0 + min(1, nc - 1)) * kWsChunk;
+      const uint8_t* w0 = ws + (chunk0 + min(2, nc - 1)) * kWsChunk;
+      const uint8_t* w1 = ws + (chunk0 + min(3, nc - 1)) * kWsChunk;
+      fetch_chunk<NVB, 0>(p0, c0, w0, vt);
+      fetch_chunk<NVB, 1>(p0, c0, w0, vt);
+      fetch_chunk<NVB, 0>(p1, c1, w1, vt);
+      fetch_chunk<NVB, 1>(p1, c1, w1, vt);
+    }
     lds_barrier();
-    gdn_seq_chunk<VT, true>(sm, pa, pb, Sacc, cur, 0, nc, chunk0, tokn, vt, ws, o);
+    gdn_seq_chunk<VT, true>(sm, p0, p2, Sacc, cur, sink, 0, nc, chunk0, tokn, vt, ws, o);
     int ci = 1;
-    for (; ci + 1 < nc; ci += 2) {
-      gdn_seq_chunk<VT, false>(sm, pb, pa, Sacc, cur, ci, nc, chunk0, tokn + (size_t)ci * C, vt, ws, o);
-      gdn_seq_chunk<VT, false>(sm, pa, pb, Sacc, cur, ci + 1, nc, chunk0, tokn + (size_t)(ci + 1) * C,
+    for (; ci + 2 < nc; ci += 3) {
+      gdn_seq_chunk<VT, false>(sm, p1, p0, Sacc, cur, sink, ci, nc, chunk0, tokn + (size_t)ci * C, vt, ws, o);
+      gdn_seq_chunk<VT, false>(sm, p2, p1, Sacc, cur, sink, ci + 1, nc, chunk0, tokn + (size_t)(ci + 1) * C,
+                               vt, ws, o);
+      gdn_seq_chunk<VT, false>(sm, p0, p2, Sacc, cur, sink, ci + 2, nc, chunk0, tokn + (size_t)(ci + 2) * C,
                                vt, ws, o);
     }
     if (ci < nc)
-      gdn_seq_chunk<VT, false>(sm, pb, pa, Sacc, cur, ci, nc, chunk0, tokn + (size_t)ci * C, vt, ws, o);
+      gdn_seq_chunk<VT, false>(sm, p1, p0, Sacc, cur, sink, ci, nc, chunk0, tokn + (size_t)ci * C, vt, ws, o);
+    if (ci + 1 < nc)
+      gdn_seq_chunk<VT, false>(sm, p2, p1, Sacc, cur, sink, ci + 1, nc, chunk0, tokn + (size_t)(ci + 1) * C,
+                               vt, ws, o);
     store_o<VT>(sm.Ot[(nc - 1) & 1], o, tokn + (size_t)(nc - 1) * C, v0);
+    asm volatile("" ::"v"(sink));   // keeps the warm-up loads
   }
 
 #pragma unroll
