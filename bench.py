@@ -90,7 +90,7 @@ def bench_decode(K, W, gen_steps=256):
                 wall_s=wall), inp
 
 
-def cpu_baseline_decode(inp, target_s=10.0):
+def cpu_baseline_decode(inp, target_s=15.0):
     """The fp64 oracle recurrence on a bounded sample of heads (every 8th head of
     the batch, slow and fast heads alike) over all generated steps, reported as
     stream-tokens per second (head-steps per second / 32 heads). numpy's einsum
@@ -108,8 +108,8 @@ def cpu_baseline_decode(inp, target_s=10.0):
         gdn.gdn_recurrent(*args, S0)
         return time.perf_counter() - t0
 
-    probe = torch.arange(0, N, 8)[:64]
-    per_head_step = run(probe, 16) / (len(probe) * 16)
+    probe = torch.arange(0, N, 8)[:16]       # calibration at the full step count
+    per_head_step = run(probe, steps) / (len(probe) * steps)
     n_heads = int(min(N // 8, max(64, target_s / max(per_head_step * steps, 1e-12))))
     heads = torch.arange(0, N, 8)[:n_heads]
     dt = run(heads, steps)
@@ -318,18 +318,23 @@ def main():
         torch.cuda.empty_cache()
     if "gla" in rows:
         r = bench_gla()
+        r["traffic_bytes"] = counter_traffic("gla_chunk_kernel")
         out_rows["gla"] = r
         log(f"[gla] {r['ms']*1e3:.1f} us  {r['tflops']:.1f} TFLOP/s ({r['frac_mfma']*100:.1f}% MFMA)  "
             f"{r['achieved_gbs']:.0f} GB/s ({r['frac_hbm']*100:.1f}% HBM)  {r['tokens_per_s']/1e6:.2f} M tok/s")
         torch.cuda.empty_cache()
     if "gdn" in rows:
         r = bench_gdn_chunk()
+        tp, ts = counter_traffic("gdn_chunk_prep_kernel"), counter_traffic("gdn_chunk_seq_kernel")
+        r["traffic_bytes"] = tp + ts if tp is not None and ts is not None else None
         out_rows["gdn_chunk"] = r
         log(f"[gdn_chunk] {r['ms']*1e3:.1f} us  {r['tflops']:.1f} TFLOP/s ({r['frac_mfma']*100:.1f}% MFMA)  "
             f"{r['achieved_gbs']:.0f} GB/s ({r['frac_hbm']*100:.1f}% HBM)  {r['tokens_per_s']/1e6:.2f} M tok/s")
         torch.cuda.empty_cache()
     if "leapq" in rows:
         r = bench_leapq()
+        r["traffic_bytes_decode_kernel"] = counter_traffic("leapq_decode_kernel")
+        r["traffic_bytes_flush_kernel"] = counter_traffic("leapq_flush_kernel")
         r["speedup_vs_fp32_decode"] = res["ms_per_step"] / r["ms_per_step"] if res else None
         out_rows["leapq"] = r
         log(f"[leapq] {r['ms_per_step']*1e3:.1f} us/step ({r['decode_kernel_ms']*1e3:.1f} us decode "
