@@ -31,29 +31,50 @@ __device__ __forceinline__ float sb(uint32_t w, int b) { return (float)((int32_t
 // The token then gives u = b (v - a S_m k), o = a S_m q + u (k . q), and its record
 // is appended at slot m.
 //
-// One 256-thread block per head; thread (row = tid/2, half = tid%2) owns 64 codes
-// of one value row. Every global load that does not depend on another (codes,
-// this row's buffered corrections and compensator values, the key vectors of the
-// dot products) is issued before the first barrier, so a block waits for memory
-// once. 16-lane groups form the per-head dot products of q and k with the
-// compensator keys, the buffered keys and k itself.
+// The value rows of a head are independent given the per-head dot products, so a
+// head is split over blocks of 128 threads, each taking 32 RPT rows (the blocks of
+// one head on one XCD, so that the vectors they all read come from one L2). Thread
+// (rq = tid / 4, quarter qt = tid % 4) owns 32 codes of each of its RPT rows
+// part * 32 RPT + 32 i + rq, and their buffered and compensator values of slots
+// = qt (mod 4). Each block forms the per-head dot products of q and k with the
+// compensator keys, the buffered keys and k itself (16-lane groups, 8 entries per
+// lane). Every global load that depends on no other is issued before the first
+// barrier; more rows per thread keep more bytes in flight per block.
 
-template <typename IO>
-__global__ __launch_bounds__(256) void leapq_decode_kernel(
+constexpr int kDecodeRPT = 2;   // value rows per thread of a decode block
+
+template <typename IO, int RPT>
+__global__ __launch_bounds__(128) void leapq_decode_kernel(
     const int8_t* __restrict__ codes, const float* __restrict__ vscale,
     const float* __restrict__ ksmooth, const uint16_t* __restrict__ ct_k,
     const uint16_t* __restrict__ ct_u, float* __restrict__ buf_k, float* __restrict__ buf_u,
     float* __restrict__ buf_a, int rank, int window, int m,
     const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
-    const float* __restrict__ alpha, const float* __restrict__ beta, IO* __restrict__ o) {
+    const float* __restrict__ alpha, const float* __restrict__ beta, IO* __restrict__ o, int N) {
+  constexpr int NT = 128;                                      // threads
+  constexpr int RPB = 32 * RPT;                                // rows per block
+  constexpr int PPH = kD / RPB;                                // blocks per head
+  constexpr int NG = NT / 16;                                  // 16-lane groups
+  constexpr int NP = (kMaxRank + kMaxWindow + NG - 1) / NG;    // dot vectors per group
   __shared__ f32x4 s_x4[2][kD / 4];            // ksmooth o k, ksmooth o q
   __shared__ float s_k[kD], s_q[kD];
-  __shared__ float s_dk[32], s_dq[32];
+  __shared__ float s_dk[kMaxRank + kMaxWindow], s_dq[kMaxRank + kMaxWindow];
   __shared__ float s_g[kMaxWindow + 1];        // s_g[j] = G_j for j < m, s_g[m] = G0
 
   const int tid = threadIdx.x;
-  const int head = blockIdx.x;
-  const int row = tid >> 1, hf = tid & 1;
+  int head, part;
+  {
+    const int bid = blockIdx.x;
+    if ((N & 7) == 0) {
+      const int xcd = bid & 7, slot = bid >> 3;
+      head = (slot / PPH) * 8 + xcd;
+      part = slot % PPH;
+    } else {
+      head = bid / PPH;
+      part = bid % PPH;
+    }
+  }
+  const int rq = tid >> 2, qt = tid & 3;
   const size_t hk = (size_t)head * kD;
   float* bk = buf_k + (size_t)head * window * kD;
   float* bu = buf_u + (size_t)head * window * kD;
@@ -61,29 +82,34 @@ __global__ __launch_bounds__(256) void leapq_decode_kernel(
   const int nv = rank + m + 1;   // dot-product vectors: compensators, buffered keys, k
 
   // ---- independent loads
-  const uint4* zp = reinterpret_cast<const uint4*>(codes + (hk + row) * kD + hf * 64);
-  const uint4 z0 = zp[0], z1 = zp[1], z2 = zp[2], z3 = zp[3];
-  float bur[kMaxWindow / 2];
+  uint4 z[RPT][2];
+  float bur[RPT][kMaxWindow / 4], cur[RPT][kMaxRank / 4], vrow[RPT], vs[RPT];
 #pragma unroll
-  for (int i = 0; i < kMaxWindow / 2; ++i) {
-    const int j = 2 * i + hf;
-    bur[i] = j < m ? bu[(size_t)j * kD + row] : 0.f;
-  }
-  float cur[kMaxRank / 2];
+  for (int i = 0; i < RPT; ++i) {
+    const int row = part * RPB + 32 * i + rq;
+    const uint4* zp = reinterpret_cast<const uint4*>(codes + (hk + row) * kD + qt * 32);
+    z[i][0] = zp[0];
+    z[i][1] = zp[1];
 #pragma unroll
-  for (int i = 0; i < kMaxRank / 2; ++i) {
-    const int r = 2 * i + hf;
-    cur[i] = r < rank ? h2f(ct_u[((size_t)head * rank + r) * kD + row]) : 0.f;
+    for (int jj = 0; jj < kMaxWindow / 4; ++jj) {
+      const int j = 4 * jj + qt;
+      bur[i][jj] = j < m ? bu[(size_t)j * kD + row] : 0.f;
+    }
+#pragma unroll
+    for (int rr = 0; rr < kMaxRank / 4; ++rr) {
+      const int r = 4 * rr + qt;
+      cur[i][rr] = r < rank ? h2f(ct_u[((size_t)head * rank + r) * kD + row]) : 0.f;
+    }
+    vrow[i] = io_traits<IO>::ld(v, hk + row);
+    vs[i] = vscale[hk + row];
   }
-  const float vrow = io_traits<IO>::ld(v, hk + row);
-  const float vs = vscale[hk + row];
   const float a = alpha[head];
   const float b = beta[head];
   const int grp = tid >> 4, l16 = tid & 15, c0 = l16 * 8;
-  float w[2][8];
+  float w[NP][8];
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int vi = grp + 16 * p;
+  for (int p = 0; p < NP; ++p) {
+    const int vi = grp + NG * p;
     if (vi < rank) {
       const uint4 raw = *reinterpret_cast<const uint4*>(ct_k + ((size_t)head * rank + vi) * kD + c0);
       const uint32_t r4[4] = {raw.x, raw.y, raw.z, raw.w};
@@ -102,7 +128,7 @@ __global__ __launch_bounds__(256) void leapq_decode_kernel(
       for (int e = 0; e < 8; ++e) w[p][e] = 0.f;
     }
   }
-  if (tid < kD) {
+  {   // one thread per key channel
     const float kv = io_traits<IO>::ld(k, hk + tid);
     const float qv = io_traits<IO>::ld(q, hk + tid);
     const float c = ksmooth[hk + tid];
@@ -110,22 +136,23 @@ __global__ __launch_bounds__(256) void leapq_decode_kernel(
     s_q[tid] = qv;
     reinterpret_cast<float*>(s_x4[0])[tid] = c * kv;
     reinterpret_cast<float*>(s_x4[1])[tid] = c * qv;
-    bk[(size_t)m * kD + tid] = kv;          // append this token's key
-  } else if (tid == kD) {
+    if (part == 0) bk[(size_t)m * kD + tid] = kv;   // append this token's key
+  }
+  if (tid == 0) {
     float g = 1.f;
     for (int j = m - 1; j >= 0; --j) {      // suffix products of the buffered decays
       s_g[j] = g;
       g *= ba[j];
     }
     s_g[m] = g;
-    buf_a[(size_t)head * window + m] = a;
+    if (part == 0) buf_a[(size_t)head * window + m] = a;
   }
   lds_barrier();
 
   // ---- per-head dot products
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int vi = grp + 16 * p;
+  for (int p = 0; p < NP; ++p) {
+    const int vi = grp + NG * p;
     if (vi < nv) {
       float pk = 0.f, pq = 0.f;
 #pragma unroll
@@ -144,47 +171,54 @@ __global__ __launch_bounds__(256) void leapq_decode_kernel(
   }
   lds_barrier();
 
-  // ---- this row
-  const uint32_t zz[16] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w,
-                           z2.x, z2.y, z2.z, z2.w, z3.x, z3.y, z3.z, z3.w};
-  float yk = 0.f, yq = 0.f;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const f32x4 xk = s_x4[0][hf * 16 + e];
-    const f32x4 xq = s_x4[1][hf * 16 + e];
-    const float z_0 = sb(zz[e], 0), z_1 = sb(zz[e], 1), z_2 = sb(zz[e], 2), z_3 = sb(zz[e], 3);
-    yk += z_0 * xk.x + z_1 * xk.y + z_2 * xk.z + z_3 * xk.w;
-    yq += z_0 * xq.x + z_1 * xq.y + z_2 * xq.z + z_3 * xq.w;
-  }
-  float ck = 0.f, cq = 0.f, tk = 0.f, tq = 0.f;
-#pragma unroll
-  for (int i = 0; i < kMaxRank / 2; ++i) {
-    const int r = 2 * i + hf;
-    if (r < rank) {
-      ck += cur[i] * s_dk[r];
-      cq += cur[i] * s_dq[r];
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < kMaxWindow / 2; ++i) {
-    const int j = 2 * i + hf;
-    if (j < m) {
-      const float wj = s_g[j] * bur[i];
-      tk += wj * s_dk[rank + j];
-      tq += wj * s_dq[rank + j];
-    }
-  }
+  // ---- the rows: each quarter's share, then the four quarters summed
   const float g0 = s_g[m];
-  const float sv = vs * (1.0f / 127.0f);
-  float Sk = g0 * (sv * yk + ck) + tk;     // this half-row's share; linear in the parts
-  float Sq = g0 * (sv * yq + cq) + tq;
-  Sk += dpp<0xB1>(Sk);                     // add the other half (adjacent lane)
-  Sq += dpp<0xB1>(Sq);
-  const float u = b * (vrow - a * Sk);
-  const float oi = a * Sq + u * s_dq[rank + m];
-  if (hf == 0) {
-    bu[(size_t)m * kD + row] = u;
-    io_traits<IO>::st(o, hk + row, oi);
+  const float kq = s_dq[rank + m];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const uint32_t zz[8] = {z[i][0].x, z[i][0].y, z[i][0].z, z[i][0].w,
+                            z[i][1].x, z[i][1].y, z[i][1].z, z[i][1].w};
+    float yk = 0.f, yq = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const f32x4 xk = s_x4[0][qt * 8 + e];
+      const f32x4 xq = s_x4[1][qt * 8 + e];
+      const float z_0 = sb(zz[e], 0), z_1 = sb(zz[e], 1), z_2 = sb(zz[e], 2), z_3 = sb(zz[e], 3);
+      yk += z_0 * xk.x + z_1 * xk.y + z_2 * xk.z + z_3 * xk.w;
+      yq += z_0 * xq.x + z_1 * xq.y + z_2 * xq.z + z_3 * xq.w;
+    }
+    float ck = 0.f, cq = 0.f, tk = 0.f, tq = 0.f;
+#pragma unroll
+    for (int rr = 0; rr < kMaxRank / 4; ++rr) {
+      const int r = 4 * rr + qt;
+      if (r < rank) {
+        ck += cur[i][rr] * s_dk[r];
+        cq += cur[i][rr] * s_dq[r];
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < kMaxWindow / 4; ++jj) {
+      const int j = 4 * jj + qt;
+      if (j < m) {
+        const float wj = s_g[j] * bur[i][jj];
+        tk += wj * s_dk[rank + j];
+        tq += wj * s_dq[rank + j];
+      }
+    }
+    const float sv = vs[i] * (1.0f / 127.0f);
+    float Sk = g0 * (sv * yk + ck) + tk;   // this quarter's share; linear in the parts
+    float Sq = g0 * (sv * yq + cq) + tq;
+    Sk += dpp<0xB1>(Sk);                   // quarters 0+1, 2+3
+    Sq += dpp<0xB1>(Sq);
+    Sk += dpp<0x4E>(Sk);                   // all four
+    Sq += dpp<0x4E>(Sq);
+    const float u = b * (vrow[i] - a * Sk);
+    const float oi = a * Sq + u * kq;
+    if (qt == 0) {
+      const int row = part * RPB + 32 * i + rq;
+      bu[(size_t)m * kD + row] = u;
+      io_traits<IO>::st(o, hk + row, oi);
+    }
   }
 }
 
@@ -475,7 +509,7 @@ static int check_state(const leapq_state* st, const char* fn) {
     return set_error(GDNRT_ESHAPE, "%s: rank=%d must be in [0, %d]", fn, st->rank, kMaxRank);
   if (st->window < 1 || st->window > kMaxWindow)
     return set_error(GDNRT_ESHAPE, "%s: window=%d must be in [1, %d]", fn, st->window, kMaxWindow);
-  if ((size_t)st->N > 0x7fffffffu) return set_error(GDNRT_ESHAPE, "%s: N too large", fn);
+  if ((size_t)st->N * 4 > 0x7fffffffu) return set_error(GDNRT_ESHAPE, "%s: N too large", fn);
   if (st->N == 0) return GDNRT_OK;
   if (!st->codes || !st->vscale || !st->ksmooth || !st->buf_k || !st->buf_u || !st->buf_a ||
       (st->rank > 0 && (!st->ct_k || !st->ct_u)))
@@ -511,18 +545,19 @@ extern "C" int leapq_decode_step(const leapq_state* st, int pos, const void* q, 
       overlaps(o, nIO, st->codes, N * kD * kD))
     return set_error(GDNRT_EINVAL, "leapq_decode_step: o overlaps another buffer");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid((unsigned)N), block(256);
+  constexpr int RPT = kDecodeRPT;
+  const dim3 grid((unsigned)(N * (kD / (32 * RPT)))), block(128);
   if (io == GDNRT_F32)
-    hipLaunchKernelGGL(leapq_decode_kernel<float>, grid, block, 0, s, st->codes, st->vscale,
+    hipLaunchKernelGGL((leapq_decode_kernel<float, RPT>), grid, block, 0, s, st->codes, st->vscale,
                        st->ksmooth, st->ct_k, st->ct_u, st->buf_k, st->buf_u, st->buf_a, st->rank,
                        st->window, pos, static_cast<const float*>(q), static_cast<const float*>(k),
-                       static_cast<const float*>(v), alpha, beta, static_cast<float*>(o));
+                       static_cast<const float*>(v), alpha, beta, static_cast<float*>(o), (int)N);
   else
-    hipLaunchKernelGGL(leapq_decode_kernel<uint16_t>, grid, block, 0, s, st->codes, st->vscale,
+    hipLaunchKernelGGL((leapq_decode_kernel<uint16_t, RPT>), grid, block, 0, s, st->codes, st->vscale,
                        st->ksmooth, st->ct_k, st->ct_u, st->buf_k, st->buf_u, st->buf_a, st->rank,
                        st->window, pos, static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), alpha,
-                       beta, static_cast<uint16_t*>(o));
+                       beta, static_cast<uint16_t*>(o), (int)N);
   return check_launch("leapq_decode_step");
 }
 
