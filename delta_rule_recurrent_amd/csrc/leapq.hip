@@ -230,83 +230,122 @@ __global__ __launch_bounds__(128) void leapq_decode_kernel(
 // serves the column operations. Steps: rebuild (eq. 4) or load `dense`;
 // compensator fit by subspace iteration with CholeskyQR2; subtract the
 // fp16-rounded pieces; smoothing factors; value-channel scales; codes.
+// Per-head vectors in LDS are [r][128] (rank-major), so lane-indexed accesses are
+// consecutive and column-indexed ones are broadcasts.
 
 constexpr int kP = kD + 1;
 constexpr int kFlushNQ = 8;   // 1024 threads per flush block, 16 key columns each
 
 template <int NQ>
-struct FlushSmem {
+struct alignas(16) FlushSmem {
   float S[kD * kP];
-  float K[(kMaxRank + kMaxWindow) * kD];   // keys of the rank-one terms (rebuild)
-  float Qa[kD * kMaxRank];                 // [c][r]
-  float Qb[kD * kMaxRank];
-  float Y[kD * kMaxRank];                  // [v][r]
-  float part[NQ * kD * kMaxRank];
+  float K[(kMaxRank + kMaxWindow) * kD];   // keys of the rank-one terms: compensators, records
+  float U[(kMaxRank + kMaxWindow) * kD];   // their value-side vectors
+  float Qa[kMaxRank * kD];                 // [r][c]
+  float Qb[kMaxRank * kD];
+  float Y[kMaxRank * kD];                  // [r][v]
+  float part[NQ * kMaxRank * kD];          // [p][r][x]
+  double gram[2][2][kMaxRank * kMaxRank];  // [pass][wave 0, 1] partial Gram matrices
   float col[kD];
+  float dec[kMaxWindow + 1];               // dec[j] = G_j for j < m, dec[m] = G0
   float red[NQ * kD];
 };
 
-// Y[x][r] = sum over the NQ partial sums (threads t < 128 combine)
+// dst[r][x] = sum over the NQ partial sums, returned to threads t < 128 (row t)
 template <int NQ, int RANK>
-__device__ __forceinline__ void combine_parts(FlushSmem<NQ>& sm, float* dst) {
+__device__ __forceinline__ void combine_parts(const FlushSmem<NQ>& sm, float (&x)[RANK]) {
   const int t = threadIdx.x;
-  if (t < kD) {
 #pragma unroll
-    for (int r = 0; r < RANK; ++r) {
-      float acc = 0.f;
+  for (int r = 0; r < RANK; ++r) {
+    float acc = 0.f;
 #pragma unroll
-      for (int p = 0; p < NQ; ++p) acc += sm.part[(p * kD + t) * kMaxRank + r];
-      dst[t * kMaxRank + r] = acc;
-    }
+    for (int p = 0; p < NQ; ++p) acc += sm.part[(p * kMaxRank + r) * kD + t];
+    x[r] = acc;
   }
 }
 
-// One CholeskyQR pass: dst = src L^{-T}, L L^T = src^T src + (1e-6 tr + 1e-30) I.
-// Every wave forms the Gram matrix itself (two rows per lane, wave sums), so the
-// only barrier is the one after the rows are written.
+// DPP move of an fp64 value (both 32-bit halves)
+template <int CTRL>
+__device__ __forceinline__ double dpp64(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+// lane L's fp64 value, wave-uniform
+__device__ __forceinline__ double lane64(double x, int L) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)u, L);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), L);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+// sum over the 64 lanes of a wave, fp64: within rows of 16 by DPP, then the four
+// row totals (wave-uniform)
+__device__ __forceinline__ double wave_sum_f64(double x) {
+  x += dpp64<0x140>(x);
+  x += dpp64<0x141>(x);
+  x += dpp64<0x4E>(x);
+  x += dpp64<0xB1>(x);
+  return (lane64(x, 0) + lane64(x, 16)) + (lane64(x, 32) + lane64(x, 48));
+}
+
+// Waves 0 and 1 (rows t < 128, x in registers): this wave's share of the Gram
+// matrix x^T x (upper triangle) to g. The fit is ill-conditioned on states with
+// outlier channels, so the Gram matrix, the Cholesky factor and the triangular
+// solve are formed in fp64 (products of fp32 values are exact there).
 template <int RANK>
-__device__ void cholqr_pass(const float* src, float* dst) {
+__device__ __forceinline__ void partial_gram(const float (&x)[RANK], double* g) {
   const int lane = threadIdx.x & 63;
-  float x0[RANK], x1[RANK];
-#pragma unroll
-  for (int i = 0; i < RANK; ++i) {
-    x0[i] = src[(2 * lane) * kMaxRank + i];
-    x1[i] = src[(2 * lane + 1) * kMaxRank + i];
-  }
-  float G[RANK][RANK];
 #pragma unroll
   for (int i = 0; i < RANK; ++i)
 #pragma unroll
-    for (int j = i; j < RANK; ++j) G[i][j] = sum64(x0[i] * x0[j] + x1[i] * x1[j]);
-  float tr = 0.f;
+    for (int j = i; j < RANK; ++j) {
+      const double s = wave_sum_f64((double)x[i] * (double)x[j]);
+      if (lane == 0) g[i * kMaxRank + j] = s;
+    }
+}
+
+// One CholeskyQR step on row x (threads t < 128): x <- x L^{-T} with
+// L L^T = G + (1e-6 tr G + 1e-30) I, G the sum of the two partial Gram matrices
+// (read from LDS as needed). L is kept packed, row by row, and 1 / diag(L) apart.
+template <int RANK>
+__device__ __forceinline__ void chol_solve(float (&x)[RANK], const double* g0, const double* g1) {
+  auto G = [&](int i, int j) { return g0[i * kMaxRank + j] + g1[i * kMaxRank + j]; };   // i <= j
+  double tr = 0.0;
 #pragma unroll
-  for (int i = 0; i < RANK; ++i) tr += G[i][i];
-  const float sh = 1e-6f * tr + 1e-30f;
-  float L[RANK][RANK];
+  for (int i = 0; i < RANK; ++i) tr += G(i, i);
+  const double sh = 1e-6 * tr + 1e-30;
+  double L[RANK * (RANK + 1) / 2], rd[RANK];   // L[i][j] at i (i + 1) / 2 + j
 #pragma unroll
   for (int i = 0; i < RANK; ++i) {
 #pragma unroll
     for (int j = 0; j <= i; ++j) {
-      float s = G[j][i] + (i == j ? sh : 0.f);
+      double s = G(j, i) + (i == j ? sh : 0.0);
 #pragma unroll
-      for (int p = 0; p < j; ++p) s -= L[i][p] * L[j][p];
-      L[i][j] = i == j ? sqrtf(fmaxf(s, 0.f)) : s / L[j][j];
+      for (int p = 0; p < j; ++p) s -= L[i * (i + 1) / 2 + p] * L[j * (j + 1) / 2 + p];
+      if (i == j) {
+        const double d = sqrt(fmax(s, 0.0));
+        L[i * (i + 1) / 2 + i] = d;
+        rd[i] = 1.0 / d;
+      } else {
+        L[i * (i + 1) / 2 + j] = s * rd[j];
+      }
     }
   }
-  const int t = threadIdx.x;
-  if (t < kD) {   // row t: solve x L^T = src[t, :]
-    float x[RANK];
+  double y[RANK];
 #pragma unroll
-    for (int j = 0; j < RANK; ++j) {
-      float s = src[t * kMaxRank + j];
+  for (int j = 0; j < RANK; ++j) {
+    double s = x[j];
 #pragma unroll
-      for (int p = 0; p < j; ++p) s -= x[p] * L[j][p];
-      x[j] = s / L[j][j];
-      dst[t * kMaxRank + j] = x[j];
-    }
+    for (int p = 0; p < j; ++p) s -= y[p] * L[j * (j + 1) / 2 + p];
+    y[j] = s * rd[j];
   }
-  lds_barrier();
+#pragma unroll
+  for (int j = 0; j < RANK; ++j) x[j] = (float)y[j];
 }
+
+// four consecutive floats of LDS as a vector (16-byte aligned)
+__device__ __forceinline__ f32x4 lds4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 
 template <int NQ, int RANK>
 __global__ __launch_bounds__(128 * NQ) void leapq_flush_kernel(
@@ -316,6 +355,7 @@ __global__ __launch_bounds__(128 * NQ) void leapq_flush_kernel(
     const float* __restrict__ dense, const float* __restrict__ q0, int iters, int smooth_mode,
     float* __restrict__ pre_round) {
   constexpr int NT = 128 * NQ, FC = kD / NQ;
+  static_assert(FC == 16, "16 key columns per thread");
   constexpr int rank = RANK;
   __shared__ FlushSmem<NQ> sm;
   const int tid = threadIdx.x;
@@ -333,49 +373,57 @@ __global__ __launch_bounds__(128 * NQ) void leapq_flush_kernel(
       S[4 * i] = x.x; S[4 * i + 1] = x.y; S[4 * i + 2] = x.z; S[4 * i + 3] = x.w;
     }
   } else {
+    // every input of the rebuild is requested before the one wait: this row's codes
+    // and scale, the rank-one terms (keys and value vectors) and decays to LDS
+    const uint4 zw = *reinterpret_cast<const uint4*>(codes + (hk + v) * kD + c0);
+    const float vsv = vscale[hk + v];
     const int nt = rank + m;
-    for (int i = tid; i < nt * kD; i += NT) {
-      const int j = i / kD, c = i % kD;
-      sm.K[i] = j < rank ? h2f(ct_k[((size_t)head * rank + j) * kD + c])
-                         : buf_k[((size_t)head * window + (j - rank)) * kD + c];
+    {   // one piece of four entries of K and of U per thread (nt <= 24 rows of 32)
+      const int j = tid >> 5, c = (tid & 31) * 4;
+      if (j < rank) {
+        const uint2 hk4 = *reinterpret_cast<const uint2*>(ct_k + ((size_t)head * rank + j) * kD + c);
+        const uint2 hu4 = *reinterpret_cast<const uint2*>(ct_u + ((size_t)head * rank + j) * kD + c);
+        *reinterpret_cast<f32x4*>(sm.K + j * kD + c) =
+            f32x4{h2f(uint16_t(hk4.x)), h2f(uint16_t(hk4.x >> 16)), h2f(uint16_t(hk4.y)), h2f(uint16_t(hk4.y >> 16))};
+        *reinterpret_cast<f32x4*>(sm.U + j * kD + c) =
+            f32x4{h2f(uint16_t(hu4.x)), h2f(uint16_t(hu4.x >> 16)), h2f(uint16_t(hu4.y)), h2f(uint16_t(hu4.y >> 16))};
+      } else if (j < nt) {
+        const size_t off = ((size_t)head * window + (j - rank)) * kD + c;
+        *reinterpret_cast<f32x4*>(sm.K + j * kD + c) = *reinterpret_cast<const f32x4*>(buf_k + off);
+        *reinterpret_cast<f32x4*>(sm.U + j * kD + c) = *reinterpret_cast<const f32x4*>(buf_u + off);
+      }
     }
     if (tid < kD) sm.col[tid] = ksmooth[hk + tid];
+    if (tid == 0) {   // suffix products of the buffered decays, newest first
+      const float* ba = buf_a + (size_t)head * window;
+      float g = 1.f;
+      for (int j = m - 1; j >= 0; --j) {
+        sm.dec[j] = g;
+        g *= ba[j];
+      }
+      sm.dec[m] = g;
+    }
     lds_barrier();
 #pragma unroll
     for (int i = 0; i < FC; ++i) S[i] = 0.f;
-    const float* ba = buf_a + (size_t)head * window;
-    float g = 1.f;
-    for (int j = m - 1; j >= 0; --j) {       // newest record first: suffix-product decays
-      const float cj = g * buf_u[((size_t)head * window + j) * kD + v];
-      const f32x4* Kj = reinterpret_cast<const f32x4*>(sm.K + (rank + j) * kD + c0);
+    for (int j = 0; j < nt; ++j) {   // compensators (decay G0), then records (G_j)
+      const float cj = (j < rank ? sm.dec[m] : sm.dec[j - rank]) * sm.U[j * kD + v];
+      const float* Kj = sm.K + j * kD + c0;
 #pragma unroll
       for (int i = 0; i < FC / 4; ++i) {
-        const f32x4 kk = Kj[i];
+        const f32x4 kk = lds4(Kj + 4 * i);
         S[4 * i] += cj * kk.x; S[4 * i + 1] += cj * kk.y; S[4 * i + 2] += cj * kk.z; S[4 * i + 3] += cj * kk.w;
       }
-      g *= ba[j];
     }
-    const float g0 = g;
-    for (int r = 0; r < rank; ++r) {
-      const float cr = g0 * h2f(ct_u[((size_t)head * rank + r) * kD + v]);
-      const f32x4* Kr = reinterpret_cast<const f32x4*>(sm.K + r * kD + c0);
+    const float sv = sm.dec[m] * vsv * (1.0f / 127.0f);
+    const uint32_t z4[4] = {zw.x, zw.y, zw.z, zw.w};
 #pragma unroll
-      for (int i = 0; i < FC / 4; ++i) {
-        const f32x4 kk = Kr[i];
-        S[4 * i] += cr * kk.x; S[4 * i + 1] += cr * kk.y; S[4 * i + 2] += cr * kk.z; S[4 * i + 3] += cr * kk.w;
-      }
-    }
-    const float sv = g0 * vscale[hk + v] * (1.0f / 127.0f);
-    const uint4* zp = reinterpret_cast<const uint4*>(codes + (hk + v) * kD + c0);
-#pragma unroll
-    for (int c16 = 0; c16 < FC / 16; ++c16) {
-      const uint4 zw = zp[c16];
-      const uint32_t z4[4] = {zw.x, zw.y, zw.z, zw.w};
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int i = 16 * c16 + e;
-        S[i] += sv * sb(z4[e >> 2], e & 3) * sm.col[c0 + i];
-      }
+    for (int i4 = 0; i4 < FC / 4; ++i4) {
+      const f32x4 cc = lds4(sm.col + c0 + 4 * i4);
+      S[4 * i4] += sv * sb(z4[i4], 0) * cc.x;
+      S[4 * i4 + 1] += sv * sb(z4[i4], 1) * cc.y;
+      S[4 * i4 + 2] += sv * sb(z4[i4], 2) * cc.z;
+      S[4 * i4 + 3] += sv * sb(z4[i4], 3) * cc.w;
     }
   }
 #pragma unroll
@@ -383,67 +431,101 @@ __global__ __launch_bounds__(128 * NQ) void leapq_flush_kernel(
 
   // ---------------------------------------------------------------- compensators
   if constexpr (RANK > 0) {
-    for (int i = tid; i < kD * rank; i += NT) sm.Qa[(i / rank) * kMaxRank + (i % rank)] = q0[i];
+    for (int i = tid; i < kD * rank; i += NT) sm.Qa[(i % rank) * kD + i / rank] = q0[i];
     lds_barrier();
+    // the state is read back from its LDS copy below, so that its registers are free
+    // during the fit
     for (int it = 0; it <= iters; ++it) {
-      // Y = S Q from the registers
+      // Y = S Q (this thread's row segment)
       float acc[RANK];
 #pragma unroll
       for (int r = 0; r < RANK; ++r) acc[r] = 0.f;
 #pragma unroll
-      for (int i = 0; i < FC; ++i) {
-        const float* qr = sm.Qa + (c0 + i) * kMaxRank;
+      for (int i4 = 0; i4 < FC / 4; ++i4) {
+        const float* sr = sm.S + v * kP + c0 + 4 * i4;
+        const float s0 = sr[0], s1 = sr[1], s2 = sr[2], s3 = sr[3];
 #pragma unroll
-        for (int r = 0; r < RANK; ++r) acc[r] += S[i] * qr[r];
+        for (int r = 0; r < RANK; ++r) {
+          const f32x4 qq = lds4(sm.Qa + r * kD + c0 + 4 * i4);
+          acc[r] += s0 * qq.x + s1 * qq.y + s2 * qq.z + s3 * qq.w;
+        }
       }
 #pragma unroll
-      for (int r = 0; r < RANK; ++r) sm.part[(qd * kD + v) * kMaxRank + r] = acc[r];
+      for (int r = 0; r < RANK; ++r) sm.part[(qd * kMaxRank + r) * kD + v] = acc[r];
       lds_barrier();
-      combine_parts<NQ, RANK>(sm, sm.Y);
+      if (tid < kD) {
+        float y[RANK];
+        combine_parts<NQ, RANK>(sm, y);
+#pragma unroll
+        for (int r = 0; r < RANK; ++r) sm.Y[r * kD + tid] = y[r];
+      }
       lds_barrier();
       if (it == iters) break;   // final Y = S Q: the compensator values
       // Q = S^T Y from the LDS copy: column c = v over rows [c0, c0 + FC)
 #pragma unroll
       for (int r = 0; r < RANK; ++r) acc[r] = 0.f;
 #pragma unroll
-      for (int i = 0; i < FC; ++i) {
-        const int vv = c0 + i;
-        const float sc = sm.S[vv * kP + v];
-        const float* yr = sm.Y + vv * kMaxRank;
+      for (int i4 = 0; i4 < FC / 4; ++i4) {
+        const int vv = c0 + 4 * i4;
+        const float s0 = sm.S[vv * kP + v], s1 = sm.S[(vv + 1) * kP + v];
+        const float s2 = sm.S[(vv + 2) * kP + v], s3 = sm.S[(vv + 3) * kP + v];
 #pragma unroll
-        for (int r = 0; r < RANK; ++r) acc[r] += sc * yr[r];
+        for (int r = 0; r < RANK; ++r) {
+          const f32x4 yy = lds4(sm.Y + r * kD + vv);
+          acc[r] += s0 * yy.x + s1 * yy.y + s2 * yy.z + s3 * yy.w;
+        }
       }
 #pragma unroll
-      for (int r = 0; r < RANK; ++r) sm.part[(qd * kD + v) * kMaxRank + r] = acc[r];
+      for (int r = 0; r < RANK; ++r) sm.part[(qd * kMaxRank + r) * kD + v] = acc[r];
       lds_barrier();
-      combine_parts<NQ, RANK>(sm, sm.Qa);
+      // CholeskyQR2 on the rows of Q, carried by threads t < 128 in registers
+      float x[RANK];
+      if (tid < kD) {
+        combine_parts<NQ, RANK>(sm, x);
+        partial_gram<RANK>(x, sm.gram[0][tid >> 6]);
+      }
       lds_barrier();
-      cholqr_pass<RANK>(sm.Qa, sm.Qb);
-      cholqr_pass<RANK>(sm.Qb, sm.Qa);
+      if (tid < kD) {
+        chol_solve<RANK>(x, sm.gram[0][0], sm.gram[0][1]);
+        partial_gram<RANK>(x, sm.gram[1][tid >> 6]);
+      }
+      lds_barrier();
+      if (tid < kD) {
+        chol_solve<RANK>(x, sm.gram[1][0], sm.gram[1][1]);
+#pragma unroll
+        for (int r = 0; r < RANK; ++r) sm.Qa[r * kD + tid] = x[r];
+      }
+      lds_barrier();
     }
     // round to fp16, store, keep the rounded values for the residual
     if (tid < kD) {
-      for (int r = 0; r < rank; ++r) {
-        const uint16_t hq = f2h(sm.Qa[tid * kMaxRank + r]);
-        const uint16_t hy = f2h(sm.Y[tid * kMaxRank + r]);
+#pragma unroll
+      for (int r = 0; r < RANK; ++r) {
+        const uint16_t hq = f2h(sm.Qa[r * kD + tid]);
+        const uint16_t hy = f2h(sm.Y[r * kD + tid]);
         ct_k[((size_t)head * rank + r) * kD + tid] = hq;
         ct_u[((size_t)head * rank + r) * kD + tid] = hy;
-        sm.Qb[tid * kMaxRank + r] = h2f(hq);
-        sm.part[tid * kMaxRank + r] = h2f(hy);
+        sm.Qb[r * kD + tid] = h2f(hq);
+        sm.part[r * kD + tid] = h2f(hy);
       }
     }
     lds_barrier();
     // residual R = S - sum_r uh_r kh_r^T
+#pragma unroll
+    for (int i = 0; i < FC; ++i) S[i] = sm.S[v * kP + c0 + i];
     float yh[RANK];
 #pragma unroll
-    for (int r = 0; r < RANK; ++r) yh[r] = sm.part[v * kMaxRank + r];
+    for (int r = 0; r < RANK; ++r) yh[r] = sm.part[r * kD + v];
 #pragma unroll
-    for (int i = 0; i < FC; ++i) {
-      const float* qr = sm.Qb + (c0 + i) * kMaxRank;
+    for (int r = 0; r < RANK; ++r)
 #pragma unroll
-      for (int r = 0; r < RANK; ++r) S[i] -= yh[r] * qr[r];
-      sm.S[v * kP + c0 + i] = S[i];
-    }
+      for (int i4 = 0; i4 < FC / 4; ++i4) {
+        const f32x4 kh = lds4(sm.Qb + r * kD + c0 + 4 * i4);
+        S[4 * i4] -= yh[r] * kh.x; S[4 * i4 + 1] -= yh[r] * kh.y;
+        S[4 * i4 + 2] -= yh[r] * kh.z; S[4 * i4 + 3] -= yh[r] * kh.w;
+      }
+#pragma unroll
+    for (int i = 0; i < FC; ++i) sm.S[v * kP + c0 + i] = S[i];
   }
   lds_barrier();
 
@@ -472,10 +554,12 @@ __global__ __launch_bounds__(128 * NQ) void leapq_flush_kernel(
   {
     float mx = 0.f;
 #pragma unroll
-    for (int i = 0; i < FC; ++i) {
-      S[i] *= sm.col[c0 + i];
-      mx = fmaxf(mx, fabsf(S[i]));
+    for (int i4 = 0; i4 < FC / 4; ++i4) {
+      const f32x4 cc = lds4(sm.col + c0 + 4 * i4);
+      S[4 * i4] *= cc.x; S[4 * i4 + 1] *= cc.y; S[4 * i4 + 2] *= cc.z; S[4 * i4 + 3] *= cc.w;
     }
+#pragma unroll
+    for (int i = 0; i < FC; ++i) mx = fmaxf(mx, fabsf(S[i]));
     sm.red[qd * kD + v] = mx;
     lds_barrier();
     float s = 0.f;
