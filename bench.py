@@ -192,11 +192,12 @@ def bench_gla(K=20, W=3, B=4, H=16, T=4096):
     N = B * H
     log(f"[gla] generating B={B} H={H} T={T}")
     inp = synth.gla_prefill(B=B, H=H, T=T, device="cuda")
+    ws = m.gla_chunk_workspace(N, T)
     ST = torch.empty_like(inp["S0"])
     o = torch.empty_like(inp["q"])
 
     def run(i):
-        m.gla_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_g"], inp["S0"], ST, o)
+        m.gla_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_g"], inp["S0"], ST, o, ws)
 
     ms, wall = timed(run, K, W)
     alg, dense = gla_chunk_work()
@@ -207,12 +208,13 @@ def bench_gla(K=20, W=3, B=4, H=16, T=4096):
                         f"fp32 incoming state",
                ms=ms, tokens_per_s=B * T / (ms * 1e-3), gflop=flops / 1e9, gflop_dense=dflops / 1e9,
                tflops=flops / (ms * 1e-3) / 1e12, tflops_dense=dflops / (ms * 1e-3) / 1e12,
-               bytes=byts, achieved_gbs=byts / (ms * 1e-3) / 1e9, wall_s=wall)
+               bytes=byts, achieved_gbs=byts / (ms * 1e-3) / 1e9,
+               workspace_bytes=int(ws.numel()), wall_s=wall)
     res["frac_hbm"] = res["achieved_gbs"] / PEAK_HBM_GBS
     res["frac_mfma"] = res["tflops"] / PEAK_BF16_TFLOPS
     res["frac_mfma_dense"] = res["tflops_dense"] / PEAK_BF16_TFLOPS
     res["roofline_bound"] = "hbm"
-    del inp
+    del inp, ws
     return res
 
 
@@ -318,7 +320,8 @@ def main():
         torch.cuda.empty_cache()
     if "gla" in rows:
         r = bench_gla()
-        r["traffic_bytes"] = counter_traffic("gla_chunk_kernel")
+        tp, ts = counter_traffic("gla_chunk_prep_kernel"), counter_traffic("gla_chunk_seq_kernel")
+        r["traffic_bytes"] = tp + ts if tp is not None and ts is not None else None
         out_rows["gla"] = r
         log(f"[gla] {r['ms']*1e3:.1f} us  {r['tflops']:.1f} TFLOP/s ({r['frac_mfma']*100:.1f}% MFMA)  "
             f"{r['achieved_gbs']:.0f} GB/s ({r['frac_hbm']*100:.1f}% HBM)  {r['tokens_per_s']/1e6:.2f} M tok/s")

@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     gdn_chunk_workspace,
     gdn_decode_step,
     gla_chunk_fwd,
+    gla_chunk_workspace,
     leapq_decode_step,
     leapq_window_flush,
     lib,

@@ -34,7 +34,8 @@ class LeapqState(ctypes.Structure):
 # exported symbol -> (argtypes, restype); mirrors include/gdnrt.h
 SIGNATURES = {
     "gdn_decode_step": ([_vp] * 7 + [_c_int] * 5 + [_vp], _c_int),
-    "gla_chunk_fwd": ([_vp] * 7 + [_c_int] * 6 + [_vp], _c_int),
+    "gla_chunk_fwd": ([_vp] * 7 + [_c_int] * 6 + [_vp, ctypes.c_size_t, _vp], _c_int),
+    "gla_chunk_fwd_workspace_bytes": ([_c_int] * 5, ctypes.c_size_t),
     "gdn_chunk_fwd": ([_vp] * 8 + [_c_int] * 6 + [_vp, ctypes.c_size_t, _vp], _c_int),
     "gdn_chunk_fwd_workspace_bytes": ([_c_int] * 5, ctypes.c_size_t),
     "leapq_decode_step": ([ctypes.POINTER(LeapqState), _c_int] + [_vp] * 6 + [_c_int, _vp], _c_int),
@@ -128,11 +129,18 @@ def gdn_decode_step(S, q, k, v, alpha, beta, o=None):
     return o
 
 
-def gla_chunk_fwd(q, k, v, log_g, S0=None, ST=None, o=None, chunk=CHUNK):
+def gla_chunk_workspace(N, T, device="cuda", chunk=CHUNK):
+    """Allocate the workspace gla_chunk_fwd needs for N sequences of T tokens."""
+    nb = lib().gla_chunk_fwd_workspace_bytes(N, T, D, D, chunk)
+    return torch.empty(max(nb, 16), dtype=torch.uint8, device=device)
+
+
+def gla_chunk_fwd(q, k, v, log_g, S0=None, ST=None, o=None, workspace=None, chunk=CHUNK):
     """Gated linear attention chunkwise forward from an incoming state.
 
     q, k, v [N][T][128] bf16; log_g [N][T][128] fp32; S0 [N][128][128] fp32 or
-    None. Returns (o [N][T][128] bf16, ST [N][128][128] fp32)."""
+    None; workspace from gla_chunk_workspace (allocated here if None).
+    Returns (o [N][T][128] bf16, ST [N][128][128] fp32)."""
     N, T, _ = q.shape
     for n_, t_ in (("q", q), ("k", k), ("v", v)):
         _need(t_, n_, torch.bfloat16, (N, T, D))
@@ -145,9 +153,12 @@ def gla_chunk_fwd(q, k, v, log_g, S0=None, ST=None, o=None, chunk=CHUNK):
     if o is None:
         o = torch.empty((N, T, D), dtype=torch.bfloat16, device=q.device)
     _need(o, "o", torch.bfloat16, (N, T, D))
+    if workspace is None:
+        workspace = gla_chunk_workspace(N, T, q.device, chunk)
+    _need(workspace, "workspace", torch.uint8)
     _check("gla_chunk_fwd", lib().gla_chunk_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(S0), _ptr(ST), _ptr(o),
-        N, T, D, D, chunk, BF16, _stream()))
+        N, T, D, D, chunk, BF16, _ptr(workspace), workspace.numel(), _stream()))
     return o, ST
 
 

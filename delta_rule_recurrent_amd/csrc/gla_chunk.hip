@@ -6,21 +6,20 @@
 // Algorithm" (the intra-chunk keys are divided by Lambda). In the [d_v][d_k] state
 // layout, with b the inclusive cumulative log-gate inside a chunk of C = 64 tokens:
 //
-//   O   = (Q o e^b) S^T + [ ((Q o e^b)(K o e^-b)^T) o M ] V,     M lower incl. diag,
+//   O   = (Q o e^b) S^T + O~,   O~ = [ ((Q o e^b)(K o e^-b)^T) o M ] V,   M lower incl. diag,
 //   S  <- e^{b_C} (on key columns) o S + V^T (K o e^{b_C - b}).
 //
-// The value rows of S evolve independently, so a block owns one sequence and a tile
-// of value channels (the tiles of one sequence are placed on one XCD so their
-// shared q/k/g reads hit the same L2) and walks the chunks in order with its state
-// tile resident in MFMA accumulators (fp32). Per chunk, bf16 MFMA
-// (v_mfma_f32_16x16x32_bf16, fp32 accumulation) forms the three contractions.
-// The intra-chunk factors are taken relative to the chunk's middle token m,
-// Q o e^{b - b_m} and K o e^{b_m - b}, which halves their dynamic range; the
-// matching e^{b_m} is folded into the bf16 copy of the state used for Q S^T.
-// For the elementwise work each thread owns two adjacent key channels of a few
-// consecutive tokens, whose log-gates, q, k and v are prefetched into registers
-// while the previous chunk's MFMA work runs; the cumulative sums are formed in
-// registers with one exchange of per-group totals.
+// Everything but the state is per chunk. A first kernel forms, for every chunk in
+// parallel, Q^ = Q o e^b, K^ = K o e^{b_C - b}, e^{b_C} and the intra-chunk output O~
+// (its score factors taken relative to the chunk's middle token m, Q o e^{b - b_m} and
+// K o e^{b_m - b}, which halves their range), and writes them to the caller's
+// workspace, in bf16 and in the register order in which the second kernel feeds them
+// to the matrix cores. The second kernel walks the chunks of each sequence in order
+// for a tile of value channels (the value rows of S evolve independently; the tiles of
+// a sequence share an XCD, so the operands they all read come from one L2): per chunk,
+// O = O~ + Q^ S^T and S <- e^{b_C} o S + V^T K^, the state in fp32 MFMA accumulators,
+// one barrier per chunk, the operands of the chunk two ahead in flight. bf16 MFMA
+// (v_mfma_f32_16x16x32_bf16) with fp32 accumulation throughout.
 #include "common.hpp"
 
 namespace gdnrt {
@@ -28,334 +27,455 @@ namespace gdnrt {
 namespace gla {
 
 constexpr int C = kChunk;   // 64 tokens
-constexpr int PQ = kD + 8;  // LDS pitch (bf16) of 128-wide rows: conflict-free 16-byte reads
-constexpr int PC = C + 8;   // LDS pitch (bf16) of 64-wide rows
+constexpr int NT = 512;     // threads per block, both kernels
+constexpr int PQ = kD + 8;  // bf16 pitch of 128-wide rows (conflict-free 16-byte reads)
+constexpr int PC = C + 8;   // bf16 pitch of 64-wide rows
+constexpr int PB = kD + 4;  // fp32 pitch of 128-wide rows
+
+// Workspace per chunk (bytes). With lane = 16 lq + l16 of a wave:
+//  Q^  [64 tokens][128 keys]: 16 A-operand fragments (rb, ks) of 1 KB; the lane holds
+//      token 16 rb + l16, keys 32 ks + 4 lq + {0..3} then 32 ks + 16 + 4 lq + {0..3}
+//      (a permutation of the contraction index that the state reads repeat)
+//  K^  [64 tokens][128 keys]: 16 B-operand fragments (kb, js); the lane holds key
+//      16 kb + l16, tokens 32 js + 8 lq + {0..7}
+//  O~  [64 tokens][128 values]: 32 accumulator tiles (rb, vb) of 512 B; the lane holds
+//      tokens 16 rb + 4 lq + {0..3} of value 16 vb + l16
+//  eC  e^{b_C} per key, fp32
+constexpr size_t kWQ = 0, kWK = 16384, kWO = 32768, kWE = 49152, kWChunk = 49664;
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-
-// VT value channels per block, NW waves. Elementwise work: thread t owns key
-// channels (2cp, 2cp+1), cp = t % 64, of TPT = 64 / NW consecutive tokens.
-template <int VT, int NW>
-struct Cfg {
-  static constexpr int NT = 64 * NW;
-  static constexpr int TPT = C / NW;           // tokens per thread
-  static constexpr int NVB = VT / 16;          // value blocks
-  static constexpr int SPW = 8 * NVB / NW;     // state tiles per wave
-  static constexpr int OPW = 4 * NVB / NW;     // output tiles per wave
-  static constexpr int APW = 16 / NW;          // score tiles per wave
-  static_assert(SPW >= 1 && OPW >= 1 && APW >= 1, "tile split");
-};
-
-template <int VT, int NW>
-struct Smem {
-  uint16_t Qr[C * PQ];      // q o e^{b - b_m}     [r][k]
-  uint16_t Kr[C * PQ];      // k o e^{b_m - b}     [j][k]
-  uint16_t Kh[kD * PC];     // (k o e^{b_C - b})^T [k][j]
-  uint16_t Vt[VT * PC];     // v tile transposed   [v][j]
-  uint16_t A[C * PC];       // masked scores       [r][j]
-  uint16_t Sb[VT * PQ];     // bf16 state tile times e^{b_m} (per key column) [v][k]
-  float tot[NW * kD];       // per token-group log-gate sums
-  float eC[kD];
-};
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 __device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
-
+__device__ __forceinline__ bf16x8 as_bf8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ float lo_bf(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
 
-// One chunk's inputs for this thread: log-gates, q, k pairs of its TPT tokens and,
-// when 2cp < VT, the pair of value channels v0 + 2cp, +1.
-template <int TPT>
-struct Prefetch {
-  f32x2 g[TPT];
-  unsigned q[TPT], k[TPT], v[TPT];
+// MFMA operand from a row-major [contraction][column] bf16 matrix in LDS through the
+// transposing LDS read (ds_read_b64_tr_b16): lane (l16, lq) receives
+// X[c0 + 8 lq + e][n0 + l16], e = 0..7.
+__device__ __forceinline__ bf16x8 ld_tr8(const uint16_t* X, int pitch, int c0, int n0) {
+  const int lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
+  const uint16_t* p = X + (c0 + 8 * g + (j >> 2)) * pitch + n0 + 4 * (j & 3);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * pitch));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// lower-triangle 16 x 16 tile pairs (rb, cb), cb <= rb, numbered row by row
+__device__ __forceinline__ void tri_pair(int p, int& rb, int& cb) {
+  rb = p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3;
+  cb = p - (rb * (rb + 1)) / 2;
+}
+
+// ------------------------------------------------------------------ per-chunk prep
+
+struct PrepSmem {
+  uint16_t Q[C * PQ];       // raw q [t][k], then Q^ = q o e^b in place
+  uint16_t K[C * PQ];       // raw k, then K^ = k o e^{b_C - b} in place
+  uint16_t V[C * PQ];       // raw v [t][v]
+  uint16_t Qr[C * PQ];      // q o e^{b - b_m}
+  uint16_t Kr[C * PQ];      // k o e^{b_m - b}
+  float G[C * PB];          // log-gates [t][k]
+  uint16_t A[C * PC];       // masked scores [r][j]
+  float tot[8 * kD];        // log-gate sums of each group of 8 tokens
 };
 
-template <int VT, int NW>
-__device__ __forceinline__ void fetch(Prefetch<C / NW>& pf, const uint16_t* __restrict__ q,
-                                      const uint16_t* __restrict__ k,
-                                      const uint16_t* __restrict__ v,
-                                      const float* __restrict__ log_g, size_t tok0, int v0) {
-  constexpr int TPT = C / NW;
-  const int t = threadIdx.x, cp = t & 63, e = t >> 6;
+// One chunk's inputs in 16-byte pieces: piece p = tid + 512 h of q, k, v (token p / 16,
+// channels 8 (p % 16) ..) and of the log-gates (token p / 32, channels 4 (p % 32) ..).
+struct PrepIn {
+  u32x4 q[2], k[2], v[2];
+  f32x4 g[4];
+};
+
+__device__ __forceinline__ void prep_fetch(PrepIn& in, const uint16_t* __restrict__ q,
+                                           const uint16_t* __restrict__ k,
+                                           const uint16_t* __restrict__ v,
+                                           const float* __restrict__ log_g, size_t tok0) {
+  const int t = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < TPT; ++i) {
-    const size_t row = tok0 + TPT * e + i;
-    pf.g[i] = *reinterpret_cast<const f32x2*>(log_g + row * kD + 2 * cp);
-    pf.q[i] = *reinterpret_cast<const unsigned*>(q + row * kD + 2 * cp);
-    pf.k[i] = *reinterpret_cast<const unsigned*>(k + row * kD + 2 * cp);
-    // every thread loads (an in-bounds pair when 2cp >= VT, unused): a select on a
-    // loaded value would make the compiler wait for the load right here
-    pf.v[i] = *reinterpret_cast<const unsigned*>(v + row * kD + v0 + ((2 * cp) & (VT - 1)));
+  for (int h = 0; h < 2; ++h) {
+    const int p = t + NT * h;
+    const size_t off = (tok0 + (p >> 4)) * kD + (p & 15) * 8;
+    in.q[h] = *reinterpret_cast<const u32x4*>(q + off);
+    in.k[h] = *reinterpret_cast<const u32x4*>(k + off);
+    in.v[h] = *reinterpret_cast<const u32x4*>(v + off);
+  }
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const int p = t + NT * h;
+    in.g[h] = *reinterpret_cast<const f32x4*>(log_g + (tok0 + (p >> 5)) * kD + (p & 31) * 4);
   }
 }
 
-// One chunk: E1/E2 form the decayed operands from the prefetched inputs, then the
-// next chunk's inputs are requested and M1/M2 run the contractions.
-template <int VT, int NW>
-__device__ __forceinline__ void gla_step(Smem<VT, NW>& sm, Prefetch<C / NW>& pf,
-                                         f32x4 (&Sacc)[Cfg<VT, NW>::SPW],
-                                         const uint16_t* __restrict__ q,
-                                         const uint16_t* __restrict__ k,
-                                         const uint16_t* __restrict__ v,
-                                         const float* __restrict__ log_g,
-                                         uint16_t* __restrict__ o, size_t seq, int c0, int T,
-                                         int v0, int kcol, int vbase) {
-  using CF = Cfg<VT, NW>;
-  constexpr int TPT = CF::TPT, SPW = CF::SPW, OPW = CF::OPW, APW = CF::APW;
+}  // namespace gla
+
+// Persistent: block b handles chunks b, b + grid, ...; the next chunk's inputs are
+// loaded into registers while this one is processed, and every thread issues the
+// same global loads and stores on every chunk so that the waits for them are exact.
+__global__ __launch_bounds__(512) void gla_chunk_prep_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ log_g, uint8_t* __restrict__ ws, int T, int nchunks) {
+  using namespace gla;
+  __shared__ PrepSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lq = lane >> 4;
-  const int cp = tid & 63, eg = tid >> 6;
-  // ---- E1: prefix sums of this thread's tokens, group totals to LDS
-  f32x2 b[TPT];
-  b[0] = pf.g[0];
-#pragma unroll
-  for (int i = 1; i < TPT; ++i) b[i] = b[i - 1] + pf.g[i];
-  *reinterpret_cast<f32x2*>(sm.tot + eg * kD + 2 * cp) = b[TPT - 1];
-  lds_barrier();
+  const int cp = tid & 63, eg = tid >> 6;   // elementwise: key-channel pair, token group of 8
+  const int nc = T / C;
 
-  // ---- E2: decay factors and operands; the bf16 state copy times e^{b_m}
-  {
-    f32x2 off = {0.f, 0.f}, bm = {0.f, 0.f}, bC = {0.f, 0.f};
-#pragma unroll
-    for (int e = 0; e < NW; ++e) {
-      const f32x2 te = *reinterpret_cast<const f32x2*>(sm.tot + e * kD + 2 * cp);
-      if (e < eg) off += te;
-      if (e < NW / 2) bm += te;
-      bC += te;
-    }
-    // one exponential and one reciprocal per element: p = e^{b - b_m};
-    // e^{b_m - b} = 1/p, e^{b_C - b} = e^{b_C - b_m} / p
-    const f32x2 eCm = {__expf(bC.x - bm.x), __expf(bC.y - bm.y)};
-    float kh0[TPT], kh1[TPT], vv0[TPT], vv1[TPT];
-#pragma unroll
-    for (int i = 0; i < TPT; ++i) {
-      const int r = TPT * eg + i;
-      const f32x2 bb = b[i] + off;
-      const float p0 = __expf(bb.x - bm.x), p1 = __expf(bb.y - bm.y);
-      const float r0 = __builtin_amdgcn_rcpf(p0), r1 = __builtin_amdgcn_rcpf(p1);
-      const float k0 = __uint_as_float(pf.k[i] << 16), k1 = __uint_as_float(pf.k[i] & 0xffff0000u);
-      *reinterpret_cast<unsigned*>(sm.Qr + r * PQ + 2 * cp) =
-          pack_bf16(__uint_as_float(pf.q[i] << 16) * p0, __uint_as_float(pf.q[i] & 0xffff0000u) * p1);
-      *reinterpret_cast<unsigned*>(sm.Kr + r * PQ + 2 * cp) = pack_bf16(k0 * r0, k1 * r1);
-      kh0[i] = k0 * r0 * eCm.x;
-      kh1[i] = k1 * r1 * eCm.y;
-      vv0[i] = __uint_as_float(pf.v[i] << 16);
-      vv1[i] = __uint_as_float(pf.v[i] & 0xffff0000u);
-    }
-    // transposed rows: TPT consecutive tokens of one key (value) channel
-    if constexpr (TPT == 8) {
-      u32x4 w0, w1;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        w0[i] = pack_bf16(kh0[2 * i], kh0[2 * i + 1]);
-        w1[i] = pack_bf16(kh1[2 * i], kh1[2 * i + 1]);
-      }
-      *reinterpret_cast<u32x4*>(sm.Kh + (2 * cp) * PC + TPT * eg) = w0;
-      *reinterpret_cast<u32x4*>(sm.Kh + (2 * cp + 1) * PC + TPT * eg) = w1;
-      {
-        // every thread writes: threads whose channel pair repeats modulo VT hold
-        // the same values (the load wraps the column), so their writes agree;
-        // a branch here would make the compiler wait for every outstanding load
-        const int vc = (2 * cp) & (VT - 1);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          w0[i] = pack_bf16(vv0[2 * i], vv0[2 * i + 1]);
-          w1[i] = pack_bf16(vv1[2 * i], vv1[2 * i + 1]);
-        }
-        *reinterpret_cast<u32x4*>(sm.Vt + vc * PC + TPT * eg) = w0;
-        *reinterpret_cast<u32x4*>(sm.Vt + (vc + 1) * PC + TPT * eg) = w1;
-      }
-    } else {
-      static_assert(TPT == 4, "4 or 8 tokens per thread");
-      typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-      u32x2 w0 = {pack_bf16(kh0[0], kh0[1]), pack_bf16(kh0[2], kh0[3])};
-      u32x2 w1 = {pack_bf16(kh1[0], kh1[1]), pack_bf16(kh1[2], kh1[3])};
-      *reinterpret_cast<u32x2*>(sm.Kh + (2 * cp) * PC + TPT * eg) = w0;
-      *reinterpret_cast<u32x2*>(sm.Kh + (2 * cp + 1) * PC + TPT * eg) = w1;
-      if (2 * cp < VT) {
-        w0 = u32x2{pack_bf16(vv0[0], vv0[1]), pack_bf16(vv0[2], vv0[3])};
-        w1 = u32x2{pack_bf16(vv1[0], vv1[1]), pack_bf16(vv1[2], vv1[3])};
-        *reinterpret_cast<u32x2*>(sm.Vt + (2 * cp) * PC + TPT * eg) = w0;
-        *reinterpret_cast<u32x2*>(sm.Vt + (2 * cp + 1) * PC + TPT * eg) = w1;
-      }
-    }
-    if (eg == 0) {
-      const f32x2 em = {__expf(bm.x), __expf(bm.y)};
-      sm.eC[2 * cp] = eCm.x * em.x;
-      sm.eC[2 * cp + 1] = eCm.y * em.y;
-    }
-    // this wave's state tiles, scaled by e^{b_m} of their key column
-    float bmk = 0.f;
-#pragma unroll
-    for (int e = 0; e < NW / 2; ++e) bmk += sm.tot[e * kD + kcol];
-    const float emk = __expf(bmk);
-#pragma unroll
-    for (int j = 0; j < SPW; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        sm.Sb[((vbase + j) * 16 + lq * 4 + i) * PQ + kcol] = f32_to_bf16(Sacc[j][i] * emk);
-  }
-  lds_barrier();
-  // next chunk's inputs, overlapping the MFMA work; unconditional (the last chunk
-  // loads itself again) so the waits for them count exactly the loads issued after
-  fetch<VT, NW>(pf, q, k, v, log_g, seq + min(c0 + C, T - C), v0);
+  PrepIn in;
+  int cid = blockIdx.x;
+  prep_fetch(in, q, k, v, log_g, (size_t)(cid / nc) * T + (size_t)(cid % nc) * C);
+  for (; cid < nchunks; cid += gridDim.x) {
+    uint8_t* wsc = ws + (size_t)cid * kWChunk;
 
-  // ---- M1: masked intra-chunk scores (APW tiles per wave)
+    // ---- stage the raw inputs; request the next chunk's
 #pragma unroll
-  for (int j = 0; j < APW; ++j) {
-    const int u = wave * APW + j, rb = u & 3, cb = u >> 2;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (cb <= rb) {
+    for (int h = 0; h < 2; ++h) {
+      const int p = tid + NT * h, o = (p >> 4) * PQ + (p & 15) * 8;
+      *reinterpret_cast<u32x4*>(sm.Q + o) = in.q[h];
+      *reinterpret_cast<u32x4*>(sm.K + o) = in.k[h];
+      *reinterpret_cast<u32x4*>(sm.V + o) = in.v[h];
+    }
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int p = tid + NT * h;
+      *reinterpret_cast<f32x4*>(sm.G + (p >> 5) * PB + (p & 31) * 4) = in.g[h];
+    }
+    {
+      const int nx = cid + (int)gridDim.x < nchunks ? cid + (int)gridDim.x : cid;
+      prep_fetch(in, q, k, v, log_g, (size_t)(nx / nc) * T + (size_t)(nx % nc) * C);
+    }
+    lds_barrier();
+
+    // ---- prefix sums: thread (cp, eg) owns channels 2cp, 2cp+1 of tokens 8eg .. 8eg+7
+    f32x2 b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const f32x2 gi = *reinterpret_cast<const f32x2*>(sm.G + (8 * eg + i) * PB + 2 * cp);
+      b[i] = i ? b[i - 1] + gi : gi;
+    }
+    *reinterpret_cast<f32x2*>(sm.tot + eg * kD + 2 * cp) = b[7];
+    lds_barrier();
+
+    // ---- decayed factors of the thread's elements (each read and rewritten by its owner)
+    {
+      f32x2 off = {0.f, 0.f}, bm = {0.f, 0.f}, bC = {0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const f32x2 te = *reinterpret_cast<const f32x2*>(sm.tot + e * kD + 2 * cp);
+        if (e < eg) off += te;
+        if (e < 4) bm += te;   // b at token 31, the middle of the chunk
+        bC += te;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int o = (8 * eg + i) * PQ + 2 * cp;
+        const f32x2 bb = b[i] + off;
+        const unsigned qw = *reinterpret_cast<const unsigned*>(sm.Q + o);
+        const unsigned kw = *reinterpret_cast<const unsigned*>(sm.K + o);
+        const float q0 = lo_bf(qw), q1 = hi_bf(qw), k0 = lo_bf(kw), k1 = hi_bf(kw);
+        *reinterpret_cast<unsigned*>(sm.Qr + o) =
+            pack_bf16(q0 * __expf(bb.x - bm.x), q1 * __expf(bb.y - bm.y));
+        *reinterpret_cast<unsigned*>(sm.Kr + o) =
+            pack_bf16(k0 * __expf(bm.x - bb.x), k1 * __expf(bm.y - bb.y));
+        *reinterpret_cast<unsigned*>(sm.Q + o) = pack_bf16(q0 * __expf(bb.x), q1 * __expf(bb.y));
+        *reinterpret_cast<unsigned*>(sm.K + o) =
+            pack_bf16(k0 * __expf(bC.x - bb.x), k1 * __expf(bC.y - bb.y));
+      }
+      if (eg == 0)
+        *reinterpret_cast<f32x2*>(reinterpret_cast<float*>(wsc + kWE) + 2 * cp) =
+            f32x2{__expf(bC.x), __expf(bC.y)};
+    }
+    lds_barrier();
+
+    // ---- Q^ and K^ fragments to the workspace; masked scores A to LDS
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {   // Q^ fragment (rb, ks) = (wave & 3, (wave >> 2) + 2h)
+      const int rb = wave & 3, ks = (wave >> 2) + 2 * h;
+      const uint16_t* p = sm.Q + (rb * 16 + l16) * PQ + ks * 32 + lq * 4;
+      const u32x2 a = *reinterpret_cast<const u32x2*>(p);
+      const u32x2 c = *reinterpret_cast<const u32x2*>(p + 16);
+      *reinterpret_cast<u32x4*>(wsc + kWQ + ((size_t)(rb * 4 + ks) * 64 + lane) * 16) =
+          u32x4{a.x, a.y, c.x, c.y};
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {   // K^ fragment f = 2 kb + js = wave + 8h
+      const int f = wave + 8 * h;
+      *reinterpret_cast<u32x4*>(wsc + kWK + ((size_t)f * 64 + lane) * 16) =
+          __builtin_bit_cast(u32x4, ld_tr8(sm.K, PQ, (f & 1) * 32, (f >> 1) * 16));
+    }
+    for (int u = wave; u < 10; u += 8) {   // score tiles over the lower triangle
+      int rb, cb;
+      tri_pair(u, rb, cb);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
         acc = mfma(ld8(sm.Qr + (rb * 16 + l16) * PQ + ks * 32 + lq * 8),
                    ld8(sm.Kr + (cb * 16 + l16) * PQ + ks * 32 + lq * 8), acc);
-    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = rb * 16 + lq * 4 + i, col = cb * 16 + l16;
-      sm.A[row * PC + col] = f32_to_bf16(col <= row ? acc[i] : 0.f);
+      for (int i = 0; i < 4; ++i) {
+        const int r = rb * 16 + lq * 4 + i, j = cb * 16 + l16;
+        sm.A[r * PC + j] = f32_to_bf16(j <= r ? acc[i] : 0.f);
+      }
     }
-  }
-  lds_barrier();
+    {   // the zero upper tiles that the 32-wide contraction slices of A reach: (0,1), (2,3)
+      const int t = tid >> 8, e = tid & 255;
+      sm.A[(t * 32 + (e >> 4)) * PC + t * 32 + 16 + (e & 15)] = 0;
+    }
+    lds_barrier();
 
-  // ---- M2: outputs (OPW tiles per wave) and the state update
+    // ---- O~ = A V: tiles (rb, vb = wave); row block rb reaches tokens <= 16 rb + 15
 #pragma unroll
-  for (int j = 0; j < OPW; ++j) {
-    const int u = wave * OPW + j, rb = u & 3, vb = u >> 2;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int rb = 0; rb < 4; ++rb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      acc = mfma(ld8(sm.Qr + (rb * 16 + l16) * PQ + ks * 32 + lq * 8),
-                 ld8(sm.Sb + (vb * 16 + l16) * PQ + ks * 32 + lq * 8), acc);
+      for (int js = 0; js <= rb / 2; ++js)
+        acc = mfma(ld8(sm.A + (rb * 16 + l16) * PC + js * 32 + lq * 8),
+                   ld_tr8(sm.V, PQ, js * 32, wave * 16), acc);
+      *reinterpret_cast<u32x2*>(wsc + kWO + ((size_t)(rb * 8 + wave) * 64 + lane) * 8) =
+          u32x2{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
+    }
+    lds_barrier();
+  }
+}
+
+// ------------------------------------------------------------------ sequential pass
+namespace gla {
+
+template <int VT>
+struct SeqSmem {
+  static constexpr int PV = VT == 16 ? 16 : 48;   // value-tile pitch (bf16)
+  uint16_t Sb[2][VT * PQ];    // bf16 copy of the state tile [v][k], by chunk parity
+  uint16_t Vs[2][C * PV];     // the chunk's value tile [t][v], by chunk parity
+};
+
+// One chunk's operands for this wave: a 16-byte piece of the value tile (loaded first:
+// it is needed a chunk before the rest), the Q^ fragments of token block rb = wave & 3
+// and the O~ tile (rb, value block (wave >> 2) % NVB) for the output tile, the K^
+// fragments of key block `wave` and e^{b_C} of the lane's key for the state tiles.
+struct SeqIn {
+  u32x4 vp;
+  u32x4 m[4];
+  u32x2 x;
+  u32x4 kh[2];
+  float ec;
+};
+
+template <int VT>
+__device__ __forceinline__ void seq_fetch(SeqIn& in, const uint8_t* __restrict__ wsc,
+                                          const uint16_t* __restrict__ v, size_t tok0, int vt) {
+  constexpr int NVB = VT / 16, PPT = VT / 8, NP = C * PPT;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rb = wave & 3, vbl = (wave >> 2) % NVB;
+  const int pv = tid % NP;   // value tile [64][VT] in 16-byte pieces, VT / 8 per token
+  in.vp = *reinterpret_cast<const u32x4*>(v + (tok0 + pv / PPT) * kD + vt * VT + (pv % PPT) * 8);
+  const uint8_t* mb = wsc + kWQ + (size_t)rb * 4096 + lane * 16;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) in.m[ks] = *reinterpret_cast<const u32x4*>(mb + ks * 1024);
+  in.x = *reinterpret_cast<const u32x2*>(wsc + kWO + ((size_t)(rb * 8 + vt * NVB + vbl) * 64 + lane) * 8);
+#pragma unroll
+  for (int js = 0; js < 2; ++js)
+    in.kh[js] = *reinterpret_cast<const u32x4*>(wsc + kWK + ((size_t)(wave * 2 + js) * 64 + lane) * 16);
+  in.ec = reinterpret_cast<const float*>(wsc + kWE)[wave * 16 + (lane & 15)];
+}
+
+template <int VT>
+__device__ __forceinline__ void stage_v(SeqSmem<VT>& sm, const SeqIn& in, int buf) {
+  constexpr int PPT = VT / 8, NP = C * PPT, PV = SeqSmem<VT>::PV;
+  const int tid = threadIdx.x;
+  if (tid < NP) *reinterpret_cast<u32x4*>(sm.Vs[buf] + (tid / PPT) * PV + (tid % PPT) * 8) = in.vp;
+}
+
+// One chunk: requests the operands of the chunk two ahead into `nx`, forms this
+// chunk's output tile from `pf`, stages the next chunk's value tile (from `nv`, loaded
+// a chunk ago) and updates the state. Every thread issues the same global loads and
+// stores on every chunk (past the end the last chunk is loaded again), so the waits
+// for `pf` and `nv` count exactly the memory operations issued after them.
+template <int VT>
+__device__ __forceinline__ void gla_seq_chunk(SeqSmem<VT>& sm, const SeqIn& pf, const SeqIn& nv,
+                                              SeqIn& nx, f32x4 (&Sacc)[VT / 16], int ci, int nc,
+                                              size_t chunk0, size_t tokn, int vt,
+                                              const uint8_t* __restrict__ ws,
+                                              const uint16_t* __restrict__ v,
+                                              uint16_t* __restrict__ o) {
+  constexpr int NVB = VT / 16, PV = SeqSmem<VT>::PV;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int rb = wave & 3, vbl = (wave >> 2) % NVB, kcol = wave * 16 + l16;
+  const int cur = ci & 1;
+  {
+    const int c2 = min(ci + 2, nc - 1);
+    seq_fetch<VT>(nx, ws + (chunk0 + c2) * kWChunk, v, tokn + (size_t)c2 * C, vt);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- output tile (rb, vbl): O = O~ + Q^ S^T (waves w and w + 4 coincide when NVB = 1)
+  {
+    f32x4 acc = {lo_bf(pf.x.x), hi_bf(pf.x.x), lo_bf(pf.x.y), hi_bf(pf.x.y)};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint16_t* sp = sm.Sb[cur] + (vbl * 16 + l16) * PQ + ks * 32 + lq * 4;
+      const u32x2 lo = *reinterpret_cast<const u32x2*>(sp);
+      const u32x2 hi = *reinterpret_cast<const u32x2*>(sp + 16);
+      acc = mfma(as_bf8(pf.m[ks]), as_bf8(u32x4{lo.x, lo.y, hi.x, hi.y}), acc);
+    }
+    uint16_t* op = o + (tokn + (size_t)ci * C + rb * 16 + lq * 4) * kD + vt * VT + vbl * 16 + l16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) op[(size_t)i * kD] = f32_to_bf16(acc[i]);
+  }
+  stage_v<VT>(sm, nv, cur ^ 1);
+
+  // ---- state tiles (vb, kb = wave): S <- e^{b_C} o S + V^T K^, and its next bf16 copy
+#pragma unroll
+  for (int vb = 0; vb < NVB; ++vb) {
+    f32x4 acc = Sacc[vb] * pf.ec;
 #pragma unroll
     for (int js = 0; js < 2; ++js)
-      if (js * 32 <= rb * 16 + 15)
-        acc = mfma(ld8(sm.A + (rb * 16 + l16) * PC + js * 32 + lq * 8),
-                   ld8(sm.Vt + (vb * 16 + l16) * PC + js * 32 + lq * 8), acc);
+      acc = mfma(ld_tr8(sm.Vs[cur], PV, js * 32, vb * 16), as_bf8(pf.kh[js]), acc);
+    Sacc[vb] = acc;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = rb * 16 + lq * 4 + i;
-      o[(seq + c0 + row) * kD + v0 + vb * 16 + l16] = f32_to_bf16(acc[i]);
-    }
-  }
-  {
-    const float dec = sm.eC[kcol];
-    const int kb = wave & 7;
-#pragma unroll
-    for (int j = 0; j < SPW; ++j) {
-      const int vb = vbase + j;
-      f32x4 acc = Sacc[j] * dec;
-#pragma unroll
-      for (int js = 0; js < 2; ++js)
-        acc = mfma(ld8(sm.Vt + (vb * 16 + l16) * PC + js * 32 + lq * 8),
-                   ld8(sm.Kh + (kb * 16 + l16) * PC + js * 32 + lq * 8), acc);
-      Sacc[j] = acc;
-    }
+    for (int i = 0; i < 4; ++i) sm.Sb[cur ^ 1][(vb * 16 + lq * 4 + i) * PQ + kcol] = f32_to_bf16(acc[i]);
   }
   lds_barrier();
 }
 
 }  // namespace gla
 
-template <int VT, int NW>
-__global__ __launch_bounds__(64 * NW) void gla_chunk_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ log_g, const float* __restrict__ S0, float* __restrict__ ST,
-    uint16_t* __restrict__ o, int N, int T) {
+template <int VT>
+__global__ __launch_bounds__(512) void gla_chunk_seq_kernel(
+    const uint8_t* __restrict__ ws, const uint16_t* __restrict__ v, const float* __restrict__ S0,
+    float* __restrict__ ST, uint16_t* __restrict__ o, int N, int T) {
   using namespace gla;
-  using CF = Cfg<VT, NW>;
-  constexpr int TPT = CF::TPT, NVB = CF::NVB, SPW = CF::SPW, OPW = CF::OPW, APW = CF::APW;
-  constexpr int TPS = kD / VT;   // value tiles per sequence
-  __shared__ Smem<VT, NW> sm;
+  constexpr int NVB = VT / 16;           // value blocks of 16 in the tile
+  constexpr int TPS = kD / VT;           // tiles per sequence
+  __shared__ SeqSmem<VT> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lq = lane >> 4;
-  const int cp = tid & 63, eg = tid >> 6;   // elementwise: key-channel pair, token group
-
   // block -> (sequence, value tile); the tiles of one sequence share an XCD
   int n, vt;
-  const int bid = blockIdx.x;
-  if (TPS > 1 && (N & 7) == 0) {
-    const int xcd = bid & 7, slot = bid >> 3;
-    n = (slot / TPS) * 8 + xcd;
-    vt = slot % TPS;
-  } else {
-    n = bid / TPS;
-    vt = bid % TPS;
+  {
+    const int bid = blockIdx.x;
+    if ((N & 7) == 0) {
+      const int xcd = bid & 7, slot = bid >> 3;
+      n = (slot / TPS) * 8 + xcd;
+      vt = slot % TPS;
+    } else {
+      n = bid / TPS;
+      vt = bid % TPS;
+    }
   }
   const int v0 = vt * VT;
+  const int nc = T / C;
+  const int kcol = wave * 16 + l16;
 
-  // state tiles: key block kb = wave % 8, value blocks (wave / 8) * SPW + j; lane holds
-  // S[v0 + vb*16 + lq*4 + i][kb*16 + l16]
-  const int kcol = (wave & 7) * 16 + l16;
-  const int vbase = (wave >> 3) * SPW;
-  f32x4 Sacc[SPW];
+  // state tiles: key block = wave, value blocks vb < NVB; the lane holds
+  // S[v0 + 16 vb + 4 lq + i][kcol]
+  f32x4 Sacc[NVB];
 #pragma unroll
-  for (int j = 0; j < SPW; ++j)
+  for (int vb = 0; vb < NVB; ++vb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int vrow = v0 + (vbase + j) * 16 + lq * 4 + i;
-      Sacc[j][i] = S0 ? S0[((size_t)n * kD + vrow) * kD + kcol] : 0.f;
+      Sacc[vb][i] = S0 ? S0[((size_t)n * kD + v0 + vb * 16 + lq * 4 + i) * kD + kcol] : 0.f;
+      sm.Sb[0][(vb * 16 + lq * 4 + i) * PQ + kcol] = f32_to_bf16(Sacc[vb][i]);
     }
 
-  const size_t seq = (size_t)n * T;
-  Prefetch<TPT> pf;
-  if (T > 0) {
-    fetch<VT, NW>(pf, q, k, v, log_g, seq, v0);
-    // the first chunk is peeled so that the loop is entered, as on every later
-    // iteration, with one chunk of loads and then that chunk's output stores in
-    // flight: the waits for the loads then count the stores and do not wait for them
-    gla_step<VT, NW>(sm, pf, Sacc, q, k, v, log_g, o, seq, 0, T, v0, kcol, vbase);
-    for (int c0 = C; c0 < T; c0 += C)
-      gla_step<VT, NW>(sm, pf, Sacc, q, k, v, log_g, o, seq, c0, T, v0, kcol, vbase);
+  if (nc > 0) {
+    const size_t chunk0 = (size_t)n * nc, tokn = (size_t)n * T;
+    // three operand sets in rotation: chunk ci computes from set ci % 3, stages the
+    // value tile of set (ci + 1) % 3 and loads chunk ci + 2 into set (ci + 2) % 3
+    SeqIn p0, p1, p2;
+    seq_fetch<VT>(p0, ws + chunk0 * kWChunk, v, tokn, vt);
+    {
+      const int c1 = min(1, nc - 1);
+      seq_fetch<VT>(p1, ws + (chunk0 + c1) * kWChunk, v, tokn + (size_t)c1 * C, vt);
+    }
+    stage_v<VT>(sm, p0, 0);
+    lds_barrier();
+    int ci = 0;
+    for (; ci + 2 < nc; ci += 3) {
+      gla_seq_chunk<VT>(sm, p0, p1, p2, Sacc, ci, nc, chunk0, tokn, vt, ws, v, o);
+      gla_seq_chunk<VT>(sm, p1, p2, p0, Sacc, ci + 1, nc, chunk0, tokn, vt, ws, v, o);
+      gla_seq_chunk<VT>(sm, p2, p0, p1, Sacc, ci + 2, nc, chunk0, tokn, vt, ws, v, o);
+    }
+    if (ci < nc) gla_seq_chunk<VT>(sm, p0, p1, p2, Sacc, ci, nc, chunk0, tokn, vt, ws, v, o);
+    if (ci + 1 < nc) gla_seq_chunk<VT>(sm, p1, p2, p0, Sacc, ci + 1, nc, chunk0, tokn, vt, ws, v, o);
   }
 
 #pragma unroll
-  for (int j = 0; j < SPW; ++j)
+  for (int vb = 0; vb < NVB; ++vb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int vrow = v0 + (vbase + j) * 16 + lq * 4 + i;
-      ST[((size_t)n * kD + vrow) * kD + kcol] = Sacc[j][i];
-    }
+    for (int i = 0; i < 4; ++i)
+      ST[((size_t)n * kD + v0 + vb * 16 + lq * 4 + i) * kD + kcol] = Sacc[vb][i];
 }
 
 }  // namespace gdnrt
 
 using namespace gdnrt;
 
+extern "C" size_t gla_chunk_fwd_workspace_bytes(int N, int T, int dk, int dv, int chunk) {
+  if (N <= 0 || T <= 0 || dk != kD || dv != kD || chunk != kChunk || T % kChunk) return 0;
+  return (size_t)N * (T / kChunk) * gla::kWChunk;
+}
+
 extern "C" int gla_chunk_fwd(const void* q, const void* k, const void* v, const float* log_g,
                              const float* S0, float* ST, void* o, int N, int T, int dk, int dv,
-                             int chunk, int io, void* stream) {
+                             int chunk, int io, void* workspace, size_t ws_bytes, void* stream) {
   if (N < 0 || T < 0) return set_error(GDNRT_ESHAPE, "gla_chunk_fwd: N=%d T=%d must be >= 0", N, T);
   if (dk != kD || dv != kD)
     return set_error(GDNRT_ESHAPE, "gla_chunk_fwd: d_k=%d d_v=%d, only 128 is supported", dk, dv);
   if (chunk != kChunk) return set_error(GDNRT_ESHAPE, "gla_chunk_fwd: chunk=%d, only 64 is supported", chunk);
   if (T % kChunk) return set_error(GDNRT_ESHAPE, "gla_chunk_fwd: T=%d is not a multiple of 64", T);
   if (io != GDNRT_BF16) return set_error(GDNRT_EDTYPE, "gla_chunk_fwd: io must be GDNRT_BF16");
-  if ((size_t)N * 4 > 0x7fffffffu) return set_error(GDNRT_ESHAPE, "gla_chunk_fwd: N too large");
+  if ((size_t)N * (T / kChunk) > 0x7fffffffu || (size_t)N * 8 > 0x7fffffffu)
+    return set_error(GDNRT_ESHAPE, "gla_chunk_fwd: N=%d T=%d too large", N, T);
   if (N == 0) return clear_error();
   if (!ST || (T > 0 && (!q || !k || !v || !log_g || !o)))
     return set_error(GDNRT_EINVAL, "gla_chunk_fwd: null pointer argument");
-  if ((T > 0 && (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_g) || !aligned16(o))) ||
+  const size_t nchunks = (size_t)N * (T / kChunk);
+  const size_t need = nchunks * gla::kWChunk;
+  if (ws_bytes < need || (need && !workspace))
+    return set_error(GDNRT_EINVAL, "gla_chunk_fwd: workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  if ((T > 0 && (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_g) || !aligned16(o) ||
+                 !aligned16(workspace))) ||
       !aligned4(ST) || (S0 && !aligned4(S0)))
-    return set_error(GDNRT_EALIGN, "gla_chunk_fwd: q, k, v, log_g, o must be 16-byte aligned");
+    return set_error(GDNRT_EALIGN, "gla_chunk_fwd: q, k, v, log_g, o, workspace must be 16-byte aligned");
   const size_t ntok = (size_t)N * T, nIO = ntok * kD * 2, nG = ntok * kD * 4, nS = (size_t)N * kD * kD * 4;
   if (overlaps(o, nIO, q, nIO) || overlaps(o, nIO, k, nIO) || overlaps(o, nIO, v, nIO) ||
       overlaps(o, nIO, log_g, nG) || overlaps(o, nIO, ST, nS) || overlaps(o, nIO, S0, nS) ||
+      overlaps(o, nIO, workspace, need) ||
       overlaps(ST, nS, q, nIO) || overlaps(ST, nS, k, nIO) || overlaps(ST, nS, v, nIO) ||
-      overlaps(ST, nS, log_g, nG) || (S0 && S0 != ST && overlaps(ST, nS, S0, nS)))
-    return set_error(GDNRT_EINVAL, "gla_chunk_fwd: output buffers overlap inputs (ST may equal S0)");
-  // T == 0 launches too: the kernel then copies the incoming state (or zeros) to ST
-  // four 32-channel value tiles per sequence, 8 waves each: measured on MI355X at
-  // 64 sequences x 4096 tokens, this beats 64- and 128-channel tiles, whose MFMA
-  // operands re-read from LDS saturate a single CU's LDS bandwidth
-  hipLaunchKernelGGL((gla_chunk_kernel<32, 8>), dim3((unsigned)(N * 4)), dim3(512), 0,
-                     static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(q),
-                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), log_g, S0,
-                     ST, static_cast<uint16_t*>(o), N, T);
+      overlaps(ST, nS, log_g, nG) || overlaps(ST, nS, workspace, need) ||
+      (S0 && S0 != ST && overlaps(ST, nS, S0, nS)) ||
+      overlaps(workspace, need, q, nIO) || overlaps(workspace, need, k, nIO) ||
+      overlaps(workspace, need, v, nIO) || overlaps(workspace, need, log_g, nG) ||
+      overlaps(workspace, need, S0, nS))
+    return set_error(GDNRT_EINVAL, "gla_chunk_fwd: buffers overlap (only ST may equal S0)");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  if (T > 0) {
+    // one persistent block per CU (a block's LDS fills most of one)
+    const unsigned grid = (unsigned)(nchunks < 256 ? nchunks : 256);
+    hipLaunchKernelGGL(gla_chunk_prep_kernel, dim3(grid), dim3(gla::NT), 0, s,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                       static_cast<const uint16_t*>(v), log_g, ws, T, (int)nchunks);
+    int rc = check_launch("gla_chunk_fwd (prep)");
+    if (rc != GDNRT_OK) return rc;
+  }
+  // T == 0 launches too: the kernel then copies the incoming state (or zeros) to ST.
+  // Value tiles of 16 when there are too few sequences to fill the chip with 32.
+  if (N * 4 < 256)
+    hipLaunchKernelGGL((gla_chunk_seq_kernel<16>), dim3((unsigned)(N * 8)), dim3(gla::NT), 0, s, ws,
+                       static_cast<const uint16_t*>(v), S0, ST, static_cast<uint16_t*>(o), N, T);
+  else
+    hipLaunchKernelGGL((gla_chunk_seq_kernel<32>), dim3((unsigned)(N * 4)), dim3(gla::NT), 0, s, ws,
+                       static_cast<const uint16_t*>(v), S0, ST, static_cast<uint16_t*>(o), N, T);
   return check_launch("gla_chunk_fwd");
 }

@@ -83,11 +83,21 @@ GDNRT_API int gdn_decode_step(float* S, const void* q, const void* k, const void
  *   q, k   [N][T][dk] bf16.   v, o [N][T][dv] bf16.   log_g [N][T][dk] fp32 (<= 0).
  *   S0     [N][dv][dk] fp32 incoming state, or NULL for zero.
  *   ST     [N][dv][dk] fp32 final state (may equal S0: read before written).
+ *   workspace: caller-owned device memory of gla_chunk_fwd_workspace_bytes() bytes,
+ *   16-byte aligned, overwritten (the per-chunk state-independent operands in bf16:
+ *   Q o e^b, K o e^{b_C - b} and the intra-chunk output, plus e^{b_C} in fp32, b the
+ *   cumulative log-gate within the chunk; 49,664 bytes per chunk). May be NULL when
+ *   T = 0.
  * T must be a multiple of chunk (64).
  */
 GDNRT_API int gla_chunk_fwd(const void* q, const void* k, const void* v, const float* log_g,
                   const float* S0, float* ST, void* o,
-                  int N, int T, int dk, int dv, int chunk, int io, void* stream);
+                  int N, int T, int dk, int dv, int chunk, int io,
+                  void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace bytes gla_chunk_fwd needs for this shape (0 if the shape is unsupported
+ * or empty). */
+GDNRT_API size_t gla_chunk_fwd_workspace_bytes(int N, int T, int dk, int dv, int chunk);
 
 /*
  * Gated DeltaNet chunkwise forward (prefill): the same recurrence as

@@ -32,7 +32,8 @@ def declared():
 def test_header_declares_the_five_entry_points():
     names = set(declared())
     for n in ("gdn_decode_step", "gla_chunk_fwd", "gdn_chunk_fwd", "leapq_decode_step",
-              "leapq_window_flush", "gdnrt_last_error", "gdn_chunk_fwd_workspace_bytes"):
+              "leapq_window_flush", "gdnrt_last_error", "gdn_chunk_fwd_workspace_bytes",
+              "gla_chunk_fwd_workspace_bytes"):
         assert n in names, n
 
 
@@ -65,9 +66,12 @@ def test_decode_validation(lib):
 def test_chunk_validation(lib):
     p = ctypes.c_void_p(4096)
     g = lib.gla_chunk_fwd
-    assert g(p, p, p, p, None, p, p, 2, 100, 128, 128, 64, 1, None) == ESHAPE     # T % 64
-    assert g(p, p, p, p, None, p, p, 2, 128, 128, 128, 32, 1, None) == ESHAPE     # chunk
-    assert g(p, p, p, p, None, p, p, 2, 128, 128, 128, 64, 0, None) == EDTYPE     # fp32 io
+    assert g(p, p, p, p, None, p, p, 2, 100, 128, 128, 64, 1, p, 1 << 30, None) == ESHAPE  # T % 64
+    assert g(p, p, p, p, None, p, p, 2, 128, 128, 128, 32, 1, p, 1 << 30, None) == ESHAPE  # chunk
+    assert g(p, p, p, p, None, p, p, 2, 128, 128, 128, 64, 0, p, 1 << 30, None) == EDTYPE  # fp32 io
+    assert g(p, p, p, p, None, p, p, 2, 128, 128, 128, 64, 1, p, 10, None) == EINVAL       # workspace
+    assert lib.gla_chunk_fwd_workspace_bytes(64, 4096, 128, 128, 64) == 64 * 64 * 49664
+    assert lib.gla_chunk_fwd_workspace_bytes(64, 100, 128, 128, 64) == 0
     d = lib.gdn_chunk_fwd
     assert lib.gdn_chunk_fwd_workspace_bytes(32, 16384, 128, 128, 64) == 32 * 256 * 81984
     assert lib.gdn_chunk_fwd_workspace_bytes(32, 100, 128, 128, 64) == 0
