@@ -253,68 +253,104 @@ namespace gla {
 template <int VT>
 struct SeqSmem {
   static constexpr int PV = VT == 16 ? 16 : 48;   // value-tile pitch (bf16)
-  uint16_t Sb[2][VT * PQ];    // bf16 copy of the state tile [v][k], by chunk parity
-  uint16_t Vs[2][C * PV];     // the chunk's value tile [t][v], by chunk parity
+  static constexpr int PO = VT + 4;               // output-tile pitch (bf16)
+  uint16_t Sb[2][VT * PQ];       // bf16 copy of the state tile [v][k], by chunk parity
+  uint16_t Vs[2][C * PV];        // the chunk's value tile [t][v], by chunk parity
+  uint16_t Qs[2][16 * 64 * 8];   // the chunk's Q^ fragments, by chunk parity
+  uint16_t Os[2][C * PO];        // the chunk's output tile [t][v], stored a chunk later
 };
 
-// One chunk's operands for this wave: a 16-byte piece of the value tile (loaded first:
-// it is needed a chunk before the rest), the Q^ fragments of token block rb = wave & 3
-// and the O~ tile (rb, value block (wave >> 2) % NVB) for the output tile, the K^
-// fragments of key block `wave` and e^{b_C} of the lane's key for the state tiles.
+// VT / 8 bf16 of one token row: a thread's share of a [64][VT] tile (token tid / 8)
+template <int VT>
+using piece_t = typename std::conditional<VT == 32, u32x2, unsigned>::type;
+
+// One chunk's operands for this wave, loaded two chunks ahead in three parts spread
+// over the chunk's work (a burst of all of them would stall the waves' issue). Staged
+// through LDS a chunk ahead (so loaded first): the thread's piece of the value tile and
+// Q^ fragments `wave` and `wave + 8`, which the waves then read in the order of their
+// output tiles. Kept in registers: the O~ tile (rb = wave & 3, value block
+// (wave >> 2) % NVB) of the output tile, and the K^ fragments of key block `wave` with
+// e^{b_C} of the lane's key for the state tiles.
+template <int VT>
 struct SeqIn {
-  u32x4 vp;
-  u32x4 m[4];
+  piece_t<VT> vp;
+  u32x4 mq[2];
   u32x2 x;
   u32x4 kh[2];
   float ec;
 };
 
-template <int VT>
-__device__ __forceinline__ void seq_fetch(SeqIn& in, const uint8_t* __restrict__ wsc,
+template <int VT, int PART>
+__device__ __forceinline__ void seq_fetch(SeqIn<VT>& in, const uint8_t* __restrict__ wsc,
                                           const uint16_t* __restrict__ v, size_t tok0, int vt) {
-  constexpr int NVB = VT / 16, PPT = VT / 8, NP = C * PPT;
+  constexpr int NVB = VT / 16;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rb = wave & 3, vbl = (wave >> 2) % NVB;
-  const int pv = tid % NP;   // value tile [64][VT] in 16-byte pieces, VT / 8 per token
-  in.vp = *reinterpret_cast<const u32x4*>(v + (tok0 + pv / PPT) * kD + vt * VT + (pv % PPT) * 8);
-  const uint8_t* mb = wsc + kWQ + (size_t)rb * 4096 + lane * 16;
+  if constexpr (PART == 0) {
+    in.vp = *reinterpret_cast<const piece_t<VT>*>(v + (tok0 + (tid >> 3)) * kD + vt * VT + (tid & 7) * (VT / 8));
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) in.m[ks] = *reinterpret_cast<const u32x4*>(mb + ks * 1024);
-  in.x = *reinterpret_cast<const u32x2*>(wsc + kWO + ((size_t)(rb * 8 + vt * NVB + vbl) * 64 + lane) * 8);
-#pragma unroll
-  for (int js = 0; js < 2; ++js)
-    in.kh[js] = *reinterpret_cast<const u32x4*>(wsc + kWK + ((size_t)(wave * 2 + js) * 64 + lane) * 16);
-  in.ec = reinterpret_cast<const float*>(wsc + kWE)[wave * 16 + (lane & 15)];
+    for (int h = 0; h < 2; ++h)
+      in.mq[h] = *reinterpret_cast<const u32x4*>(wsc + kWQ + ((size_t)(wave + 8 * h) * 64 + lane) * 16);
+  } else if constexpr (PART == 1) {
+    in.x = *reinterpret_cast<const u32x2*>(wsc + kWO + ((size_t)(rb * 8 + vt * NVB + vbl) * 64 + lane) * 8);
+    in.kh[0] = *reinterpret_cast<const u32x4*>(wsc + kWK + ((size_t)(wave * 2) * 64 + lane) * 16);
+  } else {
+    in.kh[1] = *reinterpret_cast<const u32x4*>(wsc + kWK + ((size_t)(wave * 2 + 1) * 64 + lane) * 16);
+    in.ec = reinterpret_cast<const float*>(wsc + kWE)[wave * 16 + (lane & 15)];
+  }
 }
 
 template <int VT>
-__device__ __forceinline__ void stage_v(SeqSmem<VT>& sm, const SeqIn& in, int buf) {
-  constexpr int PPT = VT / 8, NP = C * PPT, PV = SeqSmem<VT>::PV;
+__device__ __forceinline__ void seq_fetch_all(SeqIn<VT>& in, const uint8_t* __restrict__ wsc,
+                                              const uint16_t* __restrict__ v, size_t tok0, int vt) {
+  seq_fetch<VT, 0>(in, wsc, v, tok0, vt);
+  seq_fetch<VT, 1>(in, wsc, v, tok0, vt);
+  seq_fetch<VT, 2>(in, wsc, v, tok0, vt);
+}
+
+template <int VT>
+__device__ __forceinline__ void stage(SeqSmem<VT>& sm, const SeqIn<VT>& in, int buf) {
+  constexpr int PV = SeqSmem<VT>::PV;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  *reinterpret_cast<piece_t<VT>*>(sm.Vs[buf] + (tid >> 3) * PV + (tid & 7) * (VT / 8)) = in.vp;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    *reinterpret_cast<u32x4*>(sm.Qs[buf] + ((wave + 8 * h) * 64 + lane) * 8) = in.mq[h];
+}
+
+// Stores the output tile staged in Os[buf] for the chunk starting at token tok0.
+template <int VT>
+__device__ __forceinline__ void store_o(const SeqSmem<VT>& sm, uint16_t* __restrict__ o, size_t tok0,
+                                        int vt, int buf) {
+  constexpr int PO = SeqSmem<VT>::PO;
   const int tid = threadIdx.x;
-  if (tid < NP) *reinterpret_cast<u32x4*>(sm.Vs[buf] + (tid / PPT) * PV + (tid % PPT) * 8) = in.vp;
+  *reinterpret_cast<piece_t<VT>*>(o + (tok0 + (tid >> 3)) * kD + vt * VT + (tid & 7) * (VT / 8)) =
+      *reinterpret_cast<const piece_t<VT>*>(sm.Os[buf] + (tid >> 3) * PO + (tid & 7) * (VT / 8));
 }
 
-// One chunk: requests the operands of the chunk two ahead into `nx`, forms this
-// chunk's output tile from `pf`, stages the next chunk's value tile (from `nv`, loaded
-// a chunk ago) and updates the state. Every thread issues the same global loads and
-// stores on every chunk (past the end the last chunk is loaded again), so the waits
-// for `pf` and `nv` count exactly the memory operations issued after them.
-template <int VT>
-__device__ __forceinline__ void gla_seq_chunk(SeqSmem<VT>& sm, const SeqIn& pf, const SeqIn& nv,
-                                              SeqIn& nx, f32x4 (&Sacc)[VT / 16], int ci, int nc,
+// One chunk: requests the operands of chunk ci + 2 into `nx` (in three parts), stores
+// the previous chunk's output tile, forms this chunk's output tile into LDS, stages the
+// next chunk's value tile and Q^ (from `nv`, loaded a chunk ago) and updates the state
+// from `pf`. Every thread issues the same global loads and stores on every chunk (past
+// the end the last chunk is loaded again; the first chunk is peeled), so the waits for
+// `pf` and `nv` count exactly the memory operations issued after them.
+template <int VT, bool FIRST>
+__device__ __forceinline__ void gla_seq_chunk(SeqSmem<VT>& sm, const SeqIn<VT>& pf, const SeqIn<VT>& nv,
+                                              SeqIn<VT>& nx, f32x4 (&Sacc)[VT / 16], int ci, int nc,
                                               size_t chunk0, size_t tokn, int vt,
                                               const uint8_t* __restrict__ ws,
                                               const uint16_t* __restrict__ v,
                                               uint16_t* __restrict__ o) {
-  constexpr int NVB = VT / 16, PV = SeqSmem<VT>::PV;
+  constexpr int NVB = VT / 16, PV = SeqSmem<VT>::PV, PO = SeqSmem<VT>::PO;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, lq = lane >> 4;
   const int rb = wave & 3, vbl = (wave >> 2) % NVB, kcol = wave * 16 + l16;
   const int cur = ci & 1;
-  {
-    const int c2 = min(ci + 2, nc - 1);
-    seq_fetch<VT>(nx, ws + (chunk0 + c2) * kWChunk, v, tokn + (size_t)c2 * C, vt);
-  }
+  const int c2 = min(ci + 2, nc - 1);
+  const uint8_t* wsc = ws + (chunk0 + c2) * kWChunk;
+  const size_t tok2 = tokn + (size_t)c2 * C;
+  seq_fetch<VT, 0>(nx, wsc, v, tok2, vt);
+  if constexpr (!FIRST) store_o<VT>(sm, o, tokn + (size_t)(ci - 1) * C, vt, cur ^ 1);
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- output tile (rb, vbl): O = O~ + Q^ S^T (waves w and w + 4 coincide when NVB = 1)
@@ -325,13 +361,18 @@ __device__ __forceinline__ void gla_seq_chunk(SeqSmem<VT>& sm, const SeqIn& pf, 
       const uint16_t* sp = sm.Sb[cur] + (vbl * 16 + l16) * PQ + ks * 32 + lq * 4;
       const u32x2 lo = *reinterpret_cast<const u32x2*>(sp);
       const u32x2 hi = *reinterpret_cast<const u32x2*>(sp + 16);
-      acc = mfma(as_bf8(pf.m[ks]), as_bf8(u32x4{lo.x, lo.y, hi.x, hi.y}), acc);
+      acc = mfma(ld8(sm.Qs[cur] + ((rb * 4 + ks) * 64 + lane) * 8), as_bf8(u32x4{lo.x, lo.y, hi.x, hi.y}),
+                 acc);
     }
-    uint16_t* op = o + (tokn + (size_t)ci * C + rb * 16 + lq * 4) * kD + vt * VT + vbl * 16 + l16;
+    if (NVB == 2 || wave < 4) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) op[(size_t)i * kD] = f32_to_bf16(acc[i]);
+      for (int i = 0; i < 4; ++i) sm.Os[cur][(rb * 16 + lq * 4 + i) * PO + vbl * 16 + l16] = f32_to_bf16(acc[i]);
+    }
   }
-  stage_v<VT>(sm, nv, cur ^ 1);
+  __builtin_amdgcn_sched_barrier(0);
+  seq_fetch<VT, 1>(nx, wsc, v, tok2, vt);
+  __builtin_amdgcn_sched_barrier(0);
+  stage<VT>(sm, nv, cur ^ 1);
 
   // ---- state tiles (vb, kb = wave): S <- e^{b_C} o S + V^T K^, and its next bf16 copy
 #pragma unroll
@@ -344,6 +385,8 @@ __device__ __forceinline__ void gla_seq_chunk(SeqSmem<VT>& sm, const SeqIn& pf, 
 #pragma unroll
     for (int i = 0; i < 4; ++i) sm.Sb[cur ^ 1][(vb * 16 + lq * 4 + i) * PQ + kcol] = f32_to_bf16(acc[i]);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  seq_fetch<VT, 2>(nx, wsc, v, tok2, vt);
   lds_barrier();
 }
 
@@ -389,24 +432,27 @@ __global__ __launch_bounds__(512) void gla_chunk_seq_kernel(
 
   if (nc > 0) {
     const size_t chunk0 = (size_t)n * nc, tokn = (size_t)n * T;
+    const uint8_t* wsn = ws + chunk0 * kWChunk;
     // three operand sets in rotation: chunk ci computes from set ci % 3, stages the
-    // value tile of set (ci + 1) % 3 and loads chunk ci + 2 into set (ci + 2) % 3
-    SeqIn p0, p1, p2;
-    seq_fetch<VT>(p0, ws + chunk0 * kWChunk, v, tokn, vt);
+    // LDS operands of set (ci + 1) % 3 and loads chunk ci + 2 into set (ci + 2) % 3
+    SeqIn<VT> p0, p1, p2;
+    seq_fetch_all<VT>(p0, wsn, v, tokn, vt);
     {
       const int c1 = min(1, nc - 1);
-      seq_fetch<VT>(p1, ws + (chunk0 + c1) * kWChunk, v, tokn + (size_t)c1 * C, vt);
+      seq_fetch_all<VT>(p1, wsn + c1 * kWChunk, v, tokn + (size_t)c1 * C, vt);
     }
-    stage_v<VT>(sm, p0, 0);
+    stage<VT>(sm, p0, 0);
     lds_barrier();
-    int ci = 0;
+    gla_seq_chunk<VT, true>(sm, p0, p1, p2, Sacc, 0, nc, chunk0, tokn, vt, ws, v, o);
+    int ci = 1;
     for (; ci + 2 < nc; ci += 3) {
-      gla_seq_chunk<VT>(sm, p0, p1, p2, Sacc, ci, nc, chunk0, tokn, vt, ws, v, o);
-      gla_seq_chunk<VT>(sm, p1, p2, p0, Sacc, ci + 1, nc, chunk0, tokn, vt, ws, v, o);
-      gla_seq_chunk<VT>(sm, p2, p0, p1, Sacc, ci + 2, nc, chunk0, tokn, vt, ws, v, o);
+      gla_seq_chunk<VT, false>(sm, p1, p2, p0, Sacc, ci, nc, chunk0, tokn, vt, ws, v, o);
+      gla_seq_chunk<VT, false>(sm, p2, p0, p1, Sacc, ci + 1, nc, chunk0, tokn, vt, ws, v, o);
+      gla_seq_chunk<VT, false>(sm, p0, p1, p2, Sacc, ci + 2, nc, chunk0, tokn, vt, ws, v, o);
     }
-    if (ci < nc) gla_seq_chunk<VT>(sm, p0, p1, p2, Sacc, ci, nc, chunk0, tokn, vt, ws, v, o);
-    if (ci + 1 < nc) gla_seq_chunk<VT>(sm, p1, p2, p0, Sacc, ci + 1, nc, chunk0, tokn, vt, ws, v, o);
+    if (ci < nc) gla_seq_chunk<VT, false>(sm, p1, p2, p0, Sacc, ci, nc, chunk0, tokn, vt, ws, v, o);
+    if (ci + 1 < nc) gla_seq_chunk<VT, false>(sm, p2, p0, p1, Sacc, ci + 1, nc, chunk0, tokn, vt, ws, v, o);
+    store_o<VT>(sm, o, tokn + (size_t)(nc - 1) * C, vt, (nc - 1) & 1);
   }
 
 #pragma unroll
