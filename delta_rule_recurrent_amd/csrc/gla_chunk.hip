@@ -28,14 +28,13 @@ namespace gla {
 
 constexpr int C = kChunk;   // 64 tokens
 constexpr int NT = 512;     // threads per block, both kernels
-constexpr int PQ = kD + 8;  // bf16 pitch of 128-wide rows (conflict-free 16-byte reads)
-constexpr int PC = C + 8;   // bf16 pitch of 64-wide rows
-constexpr int PB = kD + 4;  // fp32 pitch of 128-wide rows
+constexpr int PQ = kD + 8;   // bf16 pitch of 128-wide rows read by rows (conflict-free 16-byte reads)
+constexpr int PT = kD + 16;  // bf16 pitch of 128-wide rows read transposed (conflict-free ds_read_b64_tr_b16)
+constexpr int PC = C + 8;    // bf16 pitch of 64-wide rows
 
 // Workspace per chunk (bytes). With lane = 16 lq + l16 of a wave:
 //  Q^  [64 tokens][128 keys]: 16 A-operand fragments (rb, ks) of 1 KB; the lane holds
-//      token 16 rb + l16, keys 32 ks + 4 lq + {0..3} then 32 ks + 16 + 4 lq + {0..3}
-//      (a permutation of the contraction index that the state reads repeat)
+//      token 16 rb + l16, keys 32 ks + 8 lq + {0..7}
 //  K^  [64 tokens][128 keys]: 16 B-operand fragments (kb, js); the lane holds key
 //      16 kb + l16, tokens 32 js + 8 lq + {0..7}
 //  O~  [64 tokens][128 values]: 32 accumulator tiles (rb, vb) of 512 B; the lane holds
@@ -79,20 +78,20 @@ __device__ __forceinline__ void tri_pair(int p, int& rb, int& cb) {
 
 struct PrepSmem {
   uint16_t Q[C * PQ];       // raw q [t][k], then Q^ = q o e^b in place
-  uint16_t K[C * PQ];       // raw k, then K^ = k o e^{b_C - b} in place
-  uint16_t V[C * PQ];       // raw v [t][v]
+  uint16_t K[C * PT];       // raw k, then K^ = k o e^{b_C - b} in place
+  uint16_t V[C * PT];       // raw v [t][v]
   uint16_t Qr[C * PQ];      // q o e^{b - b_m}
   uint16_t Kr[C * PQ];      // k o e^{b_m - b}
-  float G[C * PB];          // log-gates [t][k]
   uint16_t A[C * PC];       // masked scores [r][j]
   float tot[8 * kD];        // log-gate sums of each group of 8 tokens
 };
 
-// One chunk's inputs in 16-byte pieces: piece p = tid + 512 h of q, k, v (token p / 16,
-// channels 8 (p % 16) ..) and of the log-gates (token p / 32, channels 4 (p % 32) ..).
+// One chunk's inputs: 16-byte pieces p = tid + 512 h of q, k, v (token p / 16, channels
+// 8 (p % 16) ..), and the log-gates of the thread's elementwise share (channels 2 cp,
+// 2 cp + 1 of tokens 8 eg .. 8 eg + 7, cp = tid % 64, eg = tid / 64).
 struct PrepIn {
   u32x4 q[2], k[2], v[2];
-  f32x4 g[4];
+  f32x2 g[8];
 };
 
 __device__ __forceinline__ void prep_fetch(PrepIn& in, const uint16_t* __restrict__ q,
@@ -109,10 +108,8 @@ __device__ __forceinline__ void prep_fetch(PrepIn& in, const uint16_t* __restric
     in.v[h] = *reinterpret_cast<const u32x4*>(v + off);
   }
 #pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    const int p = t + NT * h;
-    in.g[h] = *reinterpret_cast<const f32x4*>(log_g + (tok0 + (p >> 5)) * kD + (p & 31) * 4);
-  }
+  for (int i = 0; i < 8; ++i)
+    in.g[i] = *reinterpret_cast<const f32x2*>(log_g + (tok0 + 8 * (t >> 6) + i) * kD + 2 * (t & 63));
 }
 
 }  // namespace gla
@@ -136,33 +133,23 @@ __global__ __launch_bounds__(512) void gla_chunk_prep_kernel(
   for (; cid < nchunks; cid += gridDim.x) {
     uint8_t* wsc = ws + (size_t)cid * kWChunk;
 
-    // ---- stage the raw inputs; request the next chunk's
+    // ---- stage the raw inputs, prefix sums of the thread's log-gates (thread (cp, eg)
+    // owns channels 2cp, 2cp+1 of tokens 8eg .. 8eg+7); request the next chunk's inputs
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int p = tid + NT * h, o = (p >> 4) * PQ + (p & 15) * 8;
-      *reinterpret_cast<u32x4*>(sm.Q + o) = in.q[h];
-      *reinterpret_cast<u32x4*>(sm.K + o) = in.k[h];
-      *reinterpret_cast<u32x4*>(sm.V + o) = in.v[h];
+      const int p = tid + NT * h, r = p >> 4, c = (p & 15) * 8;
+      *reinterpret_cast<u32x4*>(sm.Q + r * PQ + c) = in.q[h];
+      *reinterpret_cast<u32x4*>(sm.K + r * PT + c) = in.k[h];
+      *reinterpret_cast<u32x4*>(sm.V + r * PT + c) = in.v[h];
     }
+    f32x2 b[8];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const int p = tid + NT * h;
-      *reinterpret_cast<f32x4*>(sm.G + (p >> 5) * PB + (p & 31) * 4) = in.g[h];
-    }
+    for (int i = 0; i < 8; ++i) b[i] = i ? b[i - 1] + in.g[i] : in.g[i];
+    *reinterpret_cast<f32x2*>(sm.tot + eg * kD + 2 * cp) = b[7];
     {
       const int nx = cid + (int)gridDim.x < nchunks ? cid + (int)gridDim.x : cid;
       prep_fetch(in, q, k, v, log_g, (size_t)(nx / nc) * T + (size_t)(nx % nc) * C);
     }
-    lds_barrier();
-
-    // ---- prefix sums: thread (cp, eg) owns channels 2cp, 2cp+1 of tokens 8eg .. 8eg+7
-    f32x2 b[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const f32x2 gi = *reinterpret_cast<const f32x2*>(sm.G + (8 * eg + i) * PB + 2 * cp);
-      b[i] = i ? b[i - 1] + gi : gi;
-    }
-    *reinterpret_cast<f32x2*>(sm.tot + eg * kD + 2 * cp) = b[7];
     lds_barrier();
 
     // ---- decayed factors of the thread's elements (each read and rewritten by its owner)
@@ -177,17 +164,17 @@ __global__ __launch_bounds__(512) void gla_chunk_prep_kernel(
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int o = (8 * eg + i) * PQ + 2 * cp;
+        const int o = (8 * eg + i) * PQ + 2 * cp, ok = (8 * eg + i) * PT + 2 * cp;
         const f32x2 bb = b[i] + off;
         const unsigned qw = *reinterpret_cast<const unsigned*>(sm.Q + o);
-        const unsigned kw = *reinterpret_cast<const unsigned*>(sm.K + o);
+        const unsigned kw = *reinterpret_cast<const unsigned*>(sm.K + ok);
         const float q0 = lo_bf(qw), q1 = hi_bf(qw), k0 = lo_bf(kw), k1 = hi_bf(kw);
         *reinterpret_cast<unsigned*>(sm.Qr + o) =
             pack_bf16(q0 * __expf(bb.x - bm.x), q1 * __expf(bb.y - bm.y));
         *reinterpret_cast<unsigned*>(sm.Kr + o) =
             pack_bf16(k0 * __expf(bm.x - bb.x), k1 * __expf(bm.y - bb.y));
         *reinterpret_cast<unsigned*>(sm.Q + o) = pack_bf16(q0 * __expf(bb.x), q1 * __expf(bb.y));
-        *reinterpret_cast<unsigned*>(sm.K + o) =
+        *reinterpret_cast<unsigned*>(sm.K + ok) =
             pack_bf16(k0 * __expf(bC.x - bb.x), k1 * __expf(bC.y - bb.y));
       }
       if (eg == 0)
@@ -200,17 +187,14 @@ __global__ __launch_bounds__(512) void gla_chunk_prep_kernel(
 #pragma unroll
     for (int h = 0; h < 2; ++h) {   // Q^ fragment (rb, ks) = (wave & 3, (wave >> 2) + 2h)
       const int rb = wave & 3, ks = (wave >> 2) + 2 * h;
-      const uint16_t* p = sm.Q + (rb * 16 + l16) * PQ + ks * 32 + lq * 4;
-      const u32x2 a = *reinterpret_cast<const u32x2*>(p);
-      const u32x2 c = *reinterpret_cast<const u32x2*>(p + 16);
       *reinterpret_cast<u32x4*>(wsc + kWQ + ((size_t)(rb * 4 + ks) * 64 + lane) * 16) =
-          u32x4{a.x, a.y, c.x, c.y};
+          *reinterpret_cast<const u32x4*>(sm.Q + (rb * 16 + l16) * PQ + ks * 32 + lq * 8);
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {   // K^ fragment f = 2 kb + js = wave + 8h
       const int f = wave + 8 * h;
       *reinterpret_cast<u32x4*>(wsc + kWK + ((size_t)f * 64 + lane) * 16) =
-          __builtin_bit_cast(u32x4, ld_tr8(sm.K, PQ, (f & 1) * 32, (f >> 1) * 16));
+          __builtin_bit_cast(u32x4, ld_tr8(sm.K, PT, (f & 1) * 32, (f >> 1) * 16));
     }
     for (int u = wave; u < 10; u += 8) {   // score tiles over the lower triangle
       int rb, cb;
@@ -239,7 +223,7 @@ __global__ __launch_bounds__(512) void gla_chunk_prep_kernel(
 #pragma unroll
       for (int js = 0; js <= rb / 2; ++js)
         acc = mfma(ld8(sm.A + (rb * 16 + l16) * PC + js * 32 + lq * 8),
-                   ld_tr8(sm.V, PQ, js * 32, wave * 16), acc);
+                   ld_tr8(sm.V, PT, js * 32, wave * 16), acc);
       *reinterpret_cast<u32x2*>(wsc + kWO + ((size_t)(rb * 8 + wave) * 64 + lane) * 8) =
           u32x2{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
     }
@@ -358,11 +342,8 @@ __device__ __forceinline__ void gla_seq_chunk(SeqSmem<VT>& sm, const SeqIn<VT>& 
     f32x4 acc = {lo_bf(pf.x.x), hi_bf(pf.x.x), lo_bf(pf.x.y), hi_bf(pf.x.y)};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const uint16_t* sp = sm.Sb[cur] + (vbl * 16 + l16) * PQ + ks * 32 + lq * 4;
-      const u32x2 lo = *reinterpret_cast<const u32x2*>(sp);
-      const u32x2 hi = *reinterpret_cast<const u32x2*>(sp + 16);
-      acc = mfma(ld8(sm.Qs[cur] + ((rb * 4 + ks) * 64 + lane) * 8), as_bf8(u32x4{lo.x, lo.y, hi.x, hi.y}),
-                 acc);
+      acc = mfma(ld8(sm.Qs[cur] + ((rb * 4 + ks) * 64 + lane) * 8),
+                 ld8(sm.Sb[cur] + (vbl * 16 + l16) * PQ + ks * 32 + lq * 8), acc);
     }
     if (NVB == 2 || wave < 4) {
 #pragma unroll
