@@ -128,7 +128,7 @@ __device__ __forceinline__ bf16x8 ld_tr8(const uint16_t* X, int pitch, int c0, i
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-struct PrepSmem {
+struct alignas(16) PrepSmem {
   uint16_t Q[C * PQ];       // [r][k]
   uint16_t K[C * PQ];       // [j][k]
   uint16_t V[C * PQ];       // [j][v]
@@ -184,223 +184,237 @@ __device__ __forceinline__ void tri_pair(int p, int& rb, int& cb) {
 
 }  // namespace gdc
 
+namespace gdc {
+
+// One chunk of the prep: stages the inputs held in `in`, requests the next chunk's into
+// `in`, and writes the chunk's operands to the workspace.
+__device__ __forceinline__ void prep_chunk(PrepSmem& sm, PrepIn& in, int cid, const uint16_t* __restrict__ q,
+                                           const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                           const float* __restrict__ alpha, const float* __restrict__ beta,
+                                           uint8_t* __restrict__ ws, int T, int nchunks) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int nc = T / C;
+  uint8_t* wsc = ws + (size_t)cid * kWsChunk;
+
+  // ---- stage q, k, v (row-major); decays
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int p = tid + NT * h, o = (p >> 4) * PQ + (p & 15) * 8;
+    *reinterpret_cast<u32x4*>(sm.Q + o) = in.q[h];
+    *reinterpret_cast<u32x4*>(sm.K + o) = in.k[h];
+    *reinterpret_cast<u32x4*>(sm.V + o) = in.v[h];
+  }
+  float gCw;   // g_C (every wave computes it)
+  {
+    const float lgv = wave_scan(__logf(in.al));
+    const float lC = __shfl(lgv, C - 1);
+    gCw = __expf(lC);
+    if (wave == 0) {
+      const float gv = __expf(lgv);
+      sm.lg[lane] = lgv;
+      sm.g[lane] = gv;
+      sm.kd[lane] = __expf(lC - lgv);
+      sm.bt[lane] = in.be;
+      sm.btg[lane] = in.be * gv;
+    }
+  }
+  // next chunk's inputs (the last chunk of a block loads itself again)
+  {
+    const int nx = cid + (int)gridDim.x < nchunks ? cid + (int)gridDim.x : cid;
+    prep_fetch(in, q, k, v, alpha, beta, (size_t)(nx / nc) * T + (size_t)(nx % nc) * C);
+  }
+  *reinterpret_cast<float*>(wsc + kWsG + (lane & 15) * 4) = gCw;
+  lds_barrier();
+
+  // ---- K^ fragments (kb, js) = (f >> 1, f & 1), f = wave + 8 h, to the workspace
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int f = wave + 8 * h, j0 = (f & 1) * 32 + lq * 8;
+    const u32x4 raw = __builtin_bit_cast(u32x4, ld_tr8(sm.K, PQ, (f & 1) * 32, (f >> 1) * 16));
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = pack_bf16(lo_bf(raw[e]) * sm.kd[j0 + 2 * e], hi_bf(raw[e]) * sm.kd[j0 + 2 * e + 1]);
+    *reinterpret_cast<u32x4*>(wsc + kWsK + ((size_t)f * 64 + lane) * 16) = w;
+  }
+  // ---- Gram k.k -> L and scores q.k -> A: 20 tile products over the lower triangle
+  for (int u = wave; u < 20; u += 8) {
+    int rb, cb;
+    tri_pair(u >> 1, rb, cb);
+    const bool sc = u & 1;
+    const uint16_t* X = sc ? sm.Q : sm.K;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      acc = mfma(ld8(X + (rb * 16 + l16) * PQ + ks * 32 + lq * 8),
+                 ld8(sm.K + (cb * 16 + l16) * PQ + ks * 32 + lq * 8), acc);
+    const int j = cb * 16 + l16;
+    const float lj = sm.lg[j];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = rb * 16 + lq * 4 + i;
+      const float dec = j <= r ? __expf(sm.lg[r] - lj) : 0.f;
+      if (sc)
+        sm.A[r * PC + j] = f32_to_bf16(dec * acc[i]);
+      else
+        sm.rl.L[r * PF + j] = j < r ? sm.bt[r] * dec * acc[i] : 0.f;
+    }
+  }
+  {   // the zero upper tiles that the 32-wide contraction slices of A reach: (0,1), (2,3)
+    const int t = tid >> 8, e = tid & 255;
+    sm.A[(t * 32 + (e >> 4)) * PC + t * 32 + 16 + (e & 15)] = 0;
+  }
+  lds_barrier();
+
+  // ---- T = (I + L)^-1. Diagonal blocks: wave w -> block w >> 1, columns
+  // (w & 1) * 8 + 2 * (lane >> 4) + {0, 1}; lane & 15 is the row.
+  {
+    const int b = wave >> 1, i = l16;
+    const int c0 = (wave & 1) * 8 + 2 * lq, c1 = c0 + 1;
+    float lr[16];
+    const f32x4* Lrow = reinterpret_cast<const f32x4*>(sm.rl.L + (b * 16 + i) * PF + b * 16);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const f32x4 x = Lrow[s];
+      lr[4 * s] = x.x; lr[4 * s + 1] = x.y; lr[4 * s + 2] = x.z; lr[4 * s + 3] = x.w;
+    }
+    float a0 = i == c0 ? 1.f : 0.f, a1 = i == c1 ? 1.f : 0.f;
+    DiagSolve<0>::run(lr, a0, a1);
+    sm.rt.T[(b * 16 + i) * PF + b * 16 + c0] = a0;
+    sm.rt.T[(b * 16 + i) * PF + b * 16 + c1] = a1;
+  }
+  lds_barrier();
+  // Blocks below the diagonal, by distance d = I - J:
+  //   T_IJ = -D_I sum_{K=J}^{I-1} L_IK T_KJ   (D_I = T_II), wave J for J < 4 - d
+#pragma unroll
+  for (int d = 1; d < 4; ++d) {
+    if (wave < 4 - d) {
+      const int J = wave, I = J + d;
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+      for (int K = J; K < I; ++K)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          x = mfma4(sm.rl.L[(I * 16 + l16) * PF + K * 16 + 4 * s + lq],
+                    sm.rt.T[(K * 16 + 4 * s + lq) * PF + J * 16 + l16], x);
+      float* scr = sm.rw.scr[wave];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) scr[(4 * lq + i) * 17 + l16] = x[i];
+      wave_lds_sync();
+      f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        y = mfma4(sm.rt.T[(I * 16 + l16) * PF + I * 16 + 4 * s + lq], scr[(4 * s + lq) * 17 + l16], y);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm.rt.T[(I * 16 + 4 * lq + i) * PF + J * 16 + l16] = -y[i];
+    }
+    lds_barrier();
+  }
+
+  // ---- T diag(beta g) and T diag(beta) in bf16 (zero above the diagonal blocks)
+  for (int e = tid; e < C * C / 2; e += NT) {
+    const int r = e >> 5, j = 2 * (e & 31);
+    f32x2 t = {0.f, 0.f};
+    if ((j >> 4) <= (r >> 4)) t = *reinterpret_cast<const f32x2*>(sm.rt.T + r * PF + j);
+    *reinterpret_cast<unsigned*>(sm.rw.t.Tw + r * PC + j) = pack_bf16(t.x * sm.btg[j], t.y * sm.btg[j + 1]);
+    *reinterpret_cast<unsigned*>(sm.rw.t.Tu + r * PC + j) = pack_bf16(t.x * sm.bt[j], t.y * sm.bt[j + 1]);
+  }
+  lds_barrier();
+
+  // ---- W = Tw K (to LDS as W^T), W^T fragments and U~ = Tu V (workspace, U~^T to LDS).
+  // Row block rb only reaches tokens j <= 16 rb + 15: contraction slices js <= rb / 2.
+  {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {   // W tile (rb, kb = wave) -> W^T [k][j]
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int js = 0; js <= rb / 2; ++js)
+        acc = mfma(ld8(sm.rw.t.Tw + (rb * 16 + l16) * PC + js * 32 + lq * 8),
+                   ld_tr8(sm.K, PQ, js * 32, wave * 16), acc);
+      *reinterpret_cast<u32x2*>(sm.rl.Wt + (wave * 16 + l16) * PC + rb * 16 + lq * 4) =
+          u32x2{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {      // W^T fragments (rb, ks): rb pairs {0,3}, {1,2}
+      const int rb = h ? 3 - (wave & 3) : (wave & 3), ks = (wave >> 2) + 2 * h;
+      f32x4 t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
+      for (int js = 0; js <= rb / 2; ++js) {
+        const bf16x8 b = ld8(sm.rw.t.Tw + (rb * 16 + l16) * PC + js * 32 + lq * 8);
+        t0 = mfma(ld_tr8(sm.K, PQ, js * 32, ks * 32), b, t0);
+        t1 = mfma(ld_tr8(sm.K, PQ, js * 32, ks * 32 + 16), b, t1);
+      }
+      *reinterpret_cast<u32x4*>(wsc + kWsW + ((size_t)(rb * 4 + ks) * 64 + lane) * 16) =
+          u32x4{pack_bf16(t0[0], t0[1]), pack_bf16(t0[2], t0[3]), pack_bf16(t1[0], t1[1]),
+                pack_bf16(t1[2], t1[3])};
+    }
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {   // U~ tile (rb, vb = wave)
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int js = 0; js <= rb / 2; ++js)
+        acc = mfma(ld8(sm.rw.t.Tu + (rb * 16 + l16) * PC + js * 32 + lq * 8),
+                   ld_tr8(sm.V, PQ, js * 32, wave * 16), acc);
+      const u32x2 p = {pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
+      *reinterpret_cast<u32x2*>(wsc + kWsU + ((size_t)(rb * 8 + wave) * 64 + lane) * 8) = p;
+      *reinterpret_cast<u32x2*>(sm.rt.Ut + (wave * 16 + l16) * PC + rb * 16 + lq * 4) = p;
+    }
+  }
+  lds_barrier();
+
+  // ---- Q'^T = (diag(g) Q)^T - W^T A^T as fragments; O~ = A U~ tiles
+  {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int rb = h ? 3 - (wave & 3) : (wave & 3), ks = (wave >> 2) + 2 * h;
+      f32x4 t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
+      for (int js = 0; js <= rb / 2; ++js) {
+        const bf16x8 b = ld8(sm.A + (rb * 16 + l16) * PC + js * 32 + lq * 8);
+        t0 = mfma(ld8(sm.rl.Wt + (ks * 32 + l16) * PC + js * 32 + lq * 8), b, t0);
+        t1 = mfma(ld8(sm.rl.Wt + (ks * 32 + 16 + l16) * PC + js * 32 + lq * 8), b, t1);
+      }
+      const int r = rb * 16 + l16;
+      const float gr = sm.g[r];
+      const u32x2 qa = *reinterpret_cast<const u32x2*>(sm.Q + r * PQ + ks * 32 + lq * 4);
+      const u32x2 qb = *reinterpret_cast<const u32x2*>(sm.Q + r * PQ + ks * 32 + 16 + lq * 4);
+      *reinterpret_cast<u32x4*>(wsc + kWsQ + ((size_t)(rb * 4 + ks) * 64 + lane) * 16) =
+          u32x4{pack_bf16(gr * lo_bf(qa.x) - t0[0], gr * hi_bf(qa.x) - t0[1]),
+                pack_bf16(gr * lo_bf(qa.y) - t0[2], gr * hi_bf(qa.y) - t0[3]),
+                pack_bf16(gr * lo_bf(qb.x) - t1[0], gr * hi_bf(qb.x) - t1[1]),
+                pack_bf16(gr * lo_bf(qb.y) - t1[2], gr * hi_bf(qb.y) - t1[3])};
+    }
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {   // O~ tile (rb, vb = wave)
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int js = 0; js <= rb / 2; ++js)
+        acc = mfma(ld8(sm.A + (rb * 16 + l16) * PC + js * 32 + lq * 8),
+                   ld8(sm.rt.Ut + (wave * 16 + l16) * PC + js * 32 + lq * 8), acc);
+      *reinterpret_cast<u32x2*>(wsc + kWsO + ((size_t)(rb * 8 + wave) * 64 + lane) * 8) =
+          u32x2{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
+    }
+  }
+  lds_barrier();
+}
+
+}  // namespace gdc
+
 // Persistent: block b handles chunks b, b + grid, ...; the next chunk's inputs are
 // loaded into registers while this one is processed, and every thread issues the
-// same loads and stores on every chunk so that those waits are exact.
+// same loads and stores on every chunk so that those waits are exact (the first chunk
+// is peeled, so that the loop's waits do not also serve the loads issued before it).
 __global__ __launch_bounds__(512) void gdn_chunk_prep_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, uint8_t* __restrict__ ws,
     int T, int nchunks) {
   using namespace gdc;
   __shared__ PrepSmem sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l16 = lane & 15, lq = lane >> 4;
   const int nc = T / C;
-
   PrepIn in;
-  int cid = blockIdx.x;
+  int cid = blockIdx.x;   // the grid never exceeds nchunks
   prep_fetch(in, q, k, v, alpha, beta, (size_t)(cid / nc) * T + (size_t)(cid % nc) * C);
-  for (; cid < nchunks; cid += gridDim.x) {
-    uint8_t* wsc = ws + (size_t)cid * kWsChunk;
-
-    // ---- stage q, k, v (row-major); decays
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int p = tid + NT * h, o = (p >> 4) * PQ + (p & 15) * 8;
-      *reinterpret_cast<u32x4*>(sm.Q + o) = in.q[h];
-      *reinterpret_cast<u32x4*>(sm.K + o) = in.k[h];
-      *reinterpret_cast<u32x4*>(sm.V + o) = in.v[h];
-    }
-    float gCw;   // g_C (every wave computes it)
-    {
-      const float lgv = wave_scan(__logf(in.al));
-      const float lC = __shfl(lgv, C - 1);
-      gCw = __expf(lC);
-      if (wave == 0) {
-        const float gv = __expf(lgv);
-        sm.lg[lane] = lgv;
-        sm.g[lane] = gv;
-        sm.kd[lane] = __expf(lC - lgv);
-        sm.bt[lane] = in.be;
-        sm.btg[lane] = in.be * gv;
-      }
-    }
-    // next chunk's inputs (the last chunk of a block loads itself again)
-    {
-      const int nx = cid + (int)gridDim.x < nchunks ? cid + (int)gridDim.x : cid;
-      prep_fetch(in, q, k, v, alpha, beta, (size_t)(nx / nc) * T + (size_t)(nx % nc) * C);
-    }
-    *reinterpret_cast<float*>(wsc + kWsG + (lane & 15) * 4) = gCw;
-    lds_barrier();
-
-    // ---- K^ fragments (kb, js) = (f >> 1, f & 1), f = wave + 8 h, to the workspace
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int f = wave + 8 * h, j0 = (f & 1) * 32 + lq * 8;
-      const u32x4 raw = __builtin_bit_cast(u32x4, ld_tr8(sm.K, PQ, (f & 1) * 32, (f >> 1) * 16));
-      u32x4 w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        w[e] = pack_bf16(lo_bf(raw[e]) * sm.kd[j0 + 2 * e], hi_bf(raw[e]) * sm.kd[j0 + 2 * e + 1]);
-      *reinterpret_cast<u32x4*>(wsc + kWsK + ((size_t)f * 64 + lane) * 16) = w;
-    }
-    // ---- Gram k.k -> L and scores q.k -> A: 20 tile products over the lower triangle
-    for (int u = wave; u < 20; u += 8) {
-      int rb, cb;
-      tri_pair(u >> 1, rb, cb);
-      const bool sc = u & 1;
-      const uint16_t* X = sc ? sm.Q : sm.K;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        acc = mfma(ld8(X + (rb * 16 + l16) * PQ + ks * 32 + lq * 8),
-                   ld8(sm.K + (cb * 16 + l16) * PQ + ks * 32 + lq * 8), acc);
-      const int j = cb * 16 + l16;
-      const float lj = sm.lg[j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = rb * 16 + lq * 4 + i;
-        const float dec = j <= r ? __expf(sm.lg[r] - lj) : 0.f;
-        if (sc)
-          sm.A[r * PC + j] = f32_to_bf16(dec * acc[i]);
-        else
-          sm.rl.L[r * PF + j] = j < r ? sm.bt[r] * dec * acc[i] : 0.f;
-      }
-    }
-    {   // the zero upper tiles that the 32-wide contraction slices of A reach: (0,1), (2,3)
-      const int t = tid >> 8, e = tid & 255;
-      sm.A[(t * 32 + (e >> 4)) * PC + t * 32 + 16 + (e & 15)] = 0;
-    }
-    lds_barrier();
-
-    // ---- T = (I + L)^-1. Diagonal blocks: wave w -> block w >> 1, columns
-    // (w & 1) * 8 + 2 * (lane >> 4) + {0, 1}; lane & 15 is the row.
-    {
-      const int b = wave >> 1, i = l16;
-      const int c0 = (wave & 1) * 8 + 2 * lq, c1 = c0 + 1;
-      float lr[16];
-      const f32x4* Lrow = reinterpret_cast<const f32x4*>(sm.rl.L + (b * 16 + i) * PF + b * 16);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const f32x4 x = Lrow[s];
-        lr[4 * s] = x.x; lr[4 * s + 1] = x.y; lr[4 * s + 2] = x.z; lr[4 * s + 3] = x.w;
-      }
-      float a0 = i == c0 ? 1.f : 0.f, a1 = i == c1 ? 1.f : 0.f;
-      DiagSolve<0>::run(lr, a0, a1);
-      sm.rt.T[(b * 16 + i) * PF + b * 16 + c0] = a0;
-      sm.rt.T[(b * 16 + i) * PF + b * 16 + c1] = a1;
-    }
-    lds_barrier();
-    // Blocks below the diagonal, by distance d = I - J:
-    //   T_IJ = -D_I sum_{K=J}^{I-1} L_IK T_KJ   (D_I = T_II), wave J for J < 4 - d
-#pragma unroll
-    for (int d = 1; d < 4; ++d) {
-      if (wave < 4 - d) {
-        const int J = wave, I = J + d;
-        f32x4 x = {0.f, 0.f, 0.f, 0.f};
-        for (int K = J; K < I; ++K)
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-            x = mfma4(sm.rl.L[(I * 16 + l16) * PF + K * 16 + 4 * s + lq],
-                      sm.rt.T[(K * 16 + 4 * s + lq) * PF + J * 16 + l16], x);
-        float* scr = sm.rw.scr[wave];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) scr[(4 * lq + i) * 17 + l16] = x[i];
-        wave_lds_sync();
-        f32x4 y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          y = mfma4(sm.rt.T[(I * 16 + l16) * PF + I * 16 + 4 * s + lq], scr[(4 * s + lq) * 17 + l16], y);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sm.rt.T[(I * 16 + 4 * lq + i) * PF + J * 16 + l16] = -y[i];
-      }
-      lds_barrier();
-    }
-
-    // ---- T diag(beta g) and T diag(beta) in bf16 (zero above the diagonal blocks)
-    for (int e = tid; e < C * C / 2; e += NT) {
-      const int r = e >> 5, j = 2 * (e & 31);
-      f32x2 t = {0.f, 0.f};
-      if ((j >> 4) <= (r >> 4)) t = *reinterpret_cast<const f32x2*>(sm.rt.T + r * PF + j);
-      *reinterpret_cast<unsigned*>(sm.rw.t.Tw + r * PC + j) = pack_bf16(t.x * sm.btg[j], t.y * sm.btg[j + 1]);
-      *reinterpret_cast<unsigned*>(sm.rw.t.Tu + r * PC + j) = pack_bf16(t.x * sm.bt[j], t.y * sm.bt[j + 1]);
-    }
-    lds_barrier();
-
-    // ---- W = Tw K (to LDS as W^T), W^T fragments and U~ = Tu V (workspace, U~^T to LDS).
-    // Row block rb only reaches tokens j <= 16 rb + 15: contraction slices js <= rb / 2.
-    {
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {   // W tile (rb, kb = wave) -> W^T [k][j]
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int js = 0; js <= rb / 2; ++js)
-          acc = mfma(ld8(sm.rw.t.Tw + (rb * 16 + l16) * PC + js * 32 + lq * 8),
-                     ld_tr8(sm.K, PQ, js * 32, wave * 16), acc);
-        *reinterpret_cast<u32x2*>(sm.rl.Wt + (wave * 16 + l16) * PC + rb * 16 + lq * 4) =
-            u32x2{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {      // W^T fragments (rb, ks): rb pairs {0,3}, {1,2}
-        const int rb = h ? 3 - (wave & 3) : (wave & 3), ks = (wave >> 2) + 2 * h;
-        f32x4 t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
-        for (int js = 0; js <= rb / 2; ++js) {
-          const bf16x8 b = ld8(sm.rw.t.Tw + (rb * 16 + l16) * PC + js * 32 + lq * 8);
-          t0 = mfma(ld_tr8(sm.K, PQ, js * 32, ks * 32), b, t0);
-          t1 = mfma(ld_tr8(sm.K, PQ, js * 32, ks * 32 + 16), b, t1);
-        }
-        *reinterpret_cast<u32x4*>(wsc + kWsW + ((size_t)(rb * 4 + ks) * 64 + lane) * 16) =
-            u32x4{pack_bf16(t0[0], t0[1]), pack_bf16(t0[2], t0[3]), pack_bf16(t1[0], t1[1]),
-                  pack_bf16(t1[2], t1[3])};
-      }
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {   // U~ tile (rb, vb = wave)
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int js = 0; js <= rb / 2; ++js)
-          acc = mfma(ld8(sm.rw.t.Tu + (rb * 16 + l16) * PC + js * 32 + lq * 8),
-                     ld_tr8(sm.V, PQ, js * 32, wave * 16), acc);
-        const u32x2 p = {pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
-        *reinterpret_cast<u32x2*>(wsc + kWsU + ((size_t)(rb * 8 + wave) * 64 + lane) * 8) = p;
-        *reinterpret_cast<u32x2*>(sm.rt.Ut + (wave * 16 + l16) * PC + rb * 16 + lq * 4) = p;
-      }
-    }
-    lds_barrier();
-
-    // ---- Q'^T = (diag(g) Q)^T - W^T A^T as fragments; O~ = A U~ tiles
-    {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int rb = h ? 3 - (wave & 3) : (wave & 3), ks = (wave >> 2) + 2 * h;
-        f32x4 t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
-        for (int js = 0; js <= rb / 2; ++js) {
-          const bf16x8 b = ld8(sm.A + (rb * 16 + l16) * PC + js * 32 + lq * 8);
-          t0 = mfma(ld8(sm.rl.Wt + (ks * 32 + l16) * PC + js * 32 + lq * 8), b, t0);
-          t1 = mfma(ld8(sm.rl.Wt + (ks * 32 + 16 + l16) * PC + js * 32 + lq * 8), b, t1);
-        }
-        const int r = rb * 16 + l16;
-        const float gr = sm.g[r];
-        const u32x2 qa = *reinterpret_cast<const u32x2*>(sm.Q + r * PQ + ks * 32 + lq * 4);
-        const u32x2 qb = *reinterpret_cast<const u32x2*>(sm.Q + r * PQ + ks * 32 + 16 + lq * 4);
-        *reinterpret_cast<u32x4*>(wsc + kWsQ + ((size_t)(rb * 4 + ks) * 64 + lane) * 16) =
-            u32x4{pack_bf16(gr * lo_bf(qa.x) - t0[0], gr * hi_bf(qa.x) - t0[1]),
-                  pack_bf16(gr * lo_bf(qa.y) - t0[2], gr * hi_bf(qa.y) - t0[3]),
-                  pack_bf16(gr * lo_bf(qb.x) - t1[0], gr * hi_bf(qb.x) - t1[1]),
-                  pack_bf16(gr * lo_bf(qb.y) - t1[2], gr * hi_bf(qb.y) - t1[3])};
-      }
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {   // O~ tile (rb, vb = wave)
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int js = 0; js <= rb / 2; ++js)
-          acc = mfma(ld8(sm.A + (rb * 16 + l16) * PC + js * 32 + lq * 8),
-                     ld8(sm.rt.Ut + (wave * 16 + l16) * PC + js * 32 + lq * 8), acc);
-        *reinterpret_cast<u32x2*>(wsc + kWsO + ((size_t)(rb * 8 + wave) * 64 + lane) * 8) =
-            u32x2{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
-      }
-    }
-    lds_barrier();
-  }
+  prep_chunk(sm, in, cid, q, k, v, alpha, beta, ws, T, nchunks);
+  for (cid += gridDim.x; cid < nchunks; cid += gridDim.x)
+    prep_chunk(sm, in, cid, q, k, v, alpha, beta, ws, T, nchunks);
 }
 
 // ------------------------------------------------------------------ sequential pass
@@ -410,7 +424,7 @@ constexpr int kAhead = 2;   // chunks of operands in flight ahead of the one in 
 constexpr int kWarm = 2;    // chunks between the L2 warm-up of a chunk and its loads
 
 template <int VT>
-struct SeqSmem {
+struct alignas(16) SeqSmem {
   uint16_t Sb[2][VT * PQ];   // bf16 state tile [v][k], double buffered
   uint16_t Ut[VT * PC];      // U^T tile [v][j]
   uint16_t Ot[2][VT * PC];   // outputs^T [v][r], by chunk parity

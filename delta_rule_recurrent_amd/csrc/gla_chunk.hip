@@ -76,7 +76,7 @@ __device__ __forceinline__ void tri_pair(int p, int& rb, int& cb) {
 
 // ------------------------------------------------------------------ per-chunk prep
 
-struct PrepSmem {
+struct alignas(16) PrepSmem {
   uint16_t Q[C * PQ];       // raw q [t][k], then Q^ = q o e^b in place
   uint16_t K[C * PT];       // raw k, then K^ = k o e^{b_C - b} in place
   uint16_t V[C * PT];       // raw v [t][v]
@@ -114,128 +114,142 @@ __device__ __forceinline__ void prep_fetch(PrepIn& in, const uint16_t* __restric
 
 }  // namespace gla
 
+namespace gla {
+
+// One chunk of the prep: stages the inputs held in `in`, requests the next chunk's into
+// `in`, and writes the chunk's operands to the workspace.
+__device__ __forceinline__ void prep_chunk(PrepSmem& sm, PrepIn& in, int cid, const uint16_t* __restrict__ q,
+                                           const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                           const float* __restrict__ log_g, uint8_t* __restrict__ ws, int T,
+                                           int nchunks) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int cp = tid & 63, eg = tid >> 6;   // elementwise: key-channel pair, token group of 8
+  const int nc = T / C;
+  uint8_t* wsc = ws + (size_t)cid * kWChunk;
+
+  // ---- stage the raw inputs, prefix sums of the thread's log-gates (thread (cp, eg)
+  // owns channels 2cp, 2cp+1 of tokens 8eg .. 8eg+7); request the next chunk's inputs
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int p = tid + NT * h, r = p >> 4, c = (p & 15) * 8;
+    *reinterpret_cast<u32x4*>(sm.Q + r * PQ + c) = in.q[h];
+    *reinterpret_cast<u32x4*>(sm.K + r * PT + c) = in.k[h];
+    *reinterpret_cast<u32x4*>(sm.V + r * PT + c) = in.v[h];
+  }
+  f32x2 b[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) b[i] = i ? b[i - 1] + in.g[i] : in.g[i];
+  *reinterpret_cast<f32x2*>(sm.tot + eg * kD + 2 * cp) = b[7];
+  {
+    const int nx = cid + (int)gridDim.x < nchunks ? cid + (int)gridDim.x : cid;
+    prep_fetch(in, q, k, v, log_g, (size_t)(nx / nc) * T + (size_t)(nx % nc) * C);
+  }
+  lds_barrier();
+
+  // ---- decayed factors of the thread's elements (each read and rewritten by its owner)
+  {
+    f32x2 off = {0.f, 0.f}, bm = {0.f, 0.f}, bC = {0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const f32x2 te = *reinterpret_cast<const f32x2*>(sm.tot + e * kD + 2 * cp);
+      if (e < eg) off += te;
+      if (e < 4) bm += te;   // b at token 31, the middle of the chunk
+      bC += te;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int o = (8 * eg + i) * PQ + 2 * cp, ok = (8 * eg + i) * PT + 2 * cp;
+      const f32x2 bb = b[i] + off;
+      const unsigned qw = *reinterpret_cast<const unsigned*>(sm.Q + o);
+      const unsigned kw = *reinterpret_cast<const unsigned*>(sm.K + ok);
+      const float q0 = lo_bf(qw), q1 = hi_bf(qw), k0 = lo_bf(kw), k1 = hi_bf(kw);
+      *reinterpret_cast<unsigned*>(sm.Qr + o) =
+          pack_bf16(q0 * __expf(bb.x - bm.x), q1 * __expf(bb.y - bm.y));
+      *reinterpret_cast<unsigned*>(sm.Kr + o) =
+          pack_bf16(k0 * __expf(bm.x - bb.x), k1 * __expf(bm.y - bb.y));
+      *reinterpret_cast<unsigned*>(sm.Q + o) = pack_bf16(q0 * __expf(bb.x), q1 * __expf(bb.y));
+      *reinterpret_cast<unsigned*>(sm.K + ok) =
+          pack_bf16(k0 * __expf(bC.x - bb.x), k1 * __expf(bC.y - bb.y));
+    }
+    if (eg == 0)
+      *reinterpret_cast<f32x2*>(reinterpret_cast<float*>(wsc + kWE) + 2 * cp) =
+          f32x2{__expf(bC.x), __expf(bC.y)};
+  }
+  lds_barrier();
+
+  // ---- Q^ and K^ fragments to the workspace; masked scores A to LDS
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {   // Q^ fragment (rb, ks) = (wave & 3, (wave >> 2) + 2h)
+    const int rb = wave & 3, ks = (wave >> 2) + 2 * h;
+    *reinterpret_cast<u32x4*>(wsc + kWQ + ((size_t)(rb * 4 + ks) * 64 + lane) * 16) =
+        *reinterpret_cast<const u32x4*>(sm.Q + (rb * 16 + l16) * PQ + ks * 32 + lq * 8);
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {   // K^ fragment f = 2 kb + js = wave + 8h
+    const int f = wave + 8 * h;
+    *reinterpret_cast<u32x4*>(wsc + kWK + ((size_t)f * 64 + lane) * 16) =
+        __builtin_bit_cast(u32x4, ld_tr8(sm.K, PT, (f & 1) * 32, (f >> 1) * 16));
+  }
+  for (int u = wave; u < 10; u += 8) {   // score tiles over the lower triangle
+    int rb, cb;
+    tri_pair(u, rb, cb);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      acc = mfma(ld8(sm.Qr + (rb * 16 + l16) * PQ + ks * 32 + lq * 8),
+                 ld8(sm.Kr + (cb * 16 + l16) * PQ + ks * 32 + lq * 8), acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = rb * 16 + lq * 4 + i, j = cb * 16 + l16;
+      sm.A[r * PC + j] = f32_to_bf16(j <= r ? acc[i] : 0.f);
+    }
+  }
+  {   // the zero upper tiles that the 32-wide contraction slices of A reach: (0,1), (2,3)
+    const int t = tid >> 8, e = tid & 255;
+    sm.A[(t * 32 + (e >> 4)) * PC + t * 32 + 16 + (e & 15)] = 0;
+  }
+  lds_barrier();
+
+  // ---- O~ = A V: tiles (rb, vb = wave); row block rb reaches tokens <= 16 rb + 15
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int js = 0; js <= rb / 2; ++js)
+      acc = mfma(ld8(sm.A + (rb * 16 + l16) * PC + js * 32 + lq * 8),
+                 ld_tr8(sm.V, PT, js * 32, wave * 16), acc);
+    *reinterpret_cast<u32x2*>(wsc + kWO + ((size_t)(rb * 8 + wave) * 64 + lane) * 8) =
+        u32x2{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
+  }
+  lds_barrier();
+}
+
+}  // namespace gla
+
 // Persistent: block b handles chunks b, b + grid, ...; the next chunk's inputs are
 // loaded into registers while this one is processed, and every thread issues the
-// same global loads and stores on every chunk so that the waits for them are exact.
+// same global loads and stores on every chunk so that the waits for them are exact
+// (the first chunk is peeled, so that the loop's waits do not also serve the loads
+// issued before it).
 __global__ __launch_bounds__(512) void gla_chunk_prep_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ log_g, uint8_t* __restrict__ ws, int T, int nchunks) {
   using namespace gla;
   __shared__ PrepSmem sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l16 = lane & 15, lq = lane >> 4;
-  const int cp = tid & 63, eg = tid >> 6;   // elementwise: key-channel pair, token group of 8
   const int nc = T / C;
-
   PrepIn in;
-  int cid = blockIdx.x;
+  int cid = blockIdx.x;   // the grid never exceeds nchunks
   prep_fetch(in, q, k, v, log_g, (size_t)(cid / nc) * T + (size_t)(cid % nc) * C);
-  for (; cid < nchunks; cid += gridDim.x) {
-    uint8_t* wsc = ws + (size_t)cid * kWChunk;
-
-    // ---- stage the raw inputs, prefix sums of the thread's log-gates (thread (cp, eg)
-    // owns channels 2cp, 2cp+1 of tokens 8eg .. 8eg+7); request the next chunk's inputs
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int p = tid + NT * h, r = p >> 4, c = (p & 15) * 8;
-      *reinterpret_cast<u32x4*>(sm.Q + r * PQ + c) = in.q[h];
-      *reinterpret_cast<u32x4*>(sm.K + r * PT + c) = in.k[h];
-      *reinterpret_cast<u32x4*>(sm.V + r * PT + c) = in.v[h];
-    }
-    f32x2 b[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) b[i] = i ? b[i - 1] + in.g[i] : in.g[i];
-    *reinterpret_cast<f32x2*>(sm.tot + eg * kD + 2 * cp) = b[7];
-    {
-      const int nx = cid + (int)gridDim.x < nchunks ? cid + (int)gridDim.x : cid;
-      prep_fetch(in, q, k, v, log_g, (size_t)(nx / nc) * T + (size_t)(nx % nc) * C);
-    }
-    lds_barrier();
-
-    // ---- decayed factors of the thread's elements (each read and rewritten by its owner)
-    {
-      f32x2 off = {0.f, 0.f}, bm = {0.f, 0.f}, bC = {0.f, 0.f};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const f32x2 te = *reinterpret_cast<const f32x2*>(sm.tot + e * kD + 2 * cp);
-        if (e < eg) off += te;
-        if (e < 4) bm += te;   // b at token 31, the middle of the chunk
-        bC += te;
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int o = (8 * eg + i) * PQ + 2 * cp, ok = (8 * eg + i) * PT + 2 * cp;
-        const f32x2 bb = b[i] + off;
-        const unsigned qw = *reinterpret_cast<const unsigned*>(sm.Q + o);
-        const unsigned kw = *reinterpret_cast<const unsigned*>(sm.K + ok);
-        const float q0 = lo_bf(qw), q1 = hi_bf(qw), k0 = lo_bf(kw), k1 = hi_bf(kw);
-        *reinterpret_cast<unsigned*>(sm.Qr + o) =
-            pack_bf16(q0 * __expf(bb.x - bm.x), q1 * __expf(bb.y - bm.y));
-        *reinterpret_cast<unsigned*>(sm.Kr + o) =
-            pack_bf16(k0 * __expf(bm.x - bb.x), k1 * __expf(bm.y - bb.y));
-        *reinterpret_cast<unsigned*>(sm.Q + o) = pack_bf16(q0 * __expf(bb.x), q1 * __expf(bb.y));
-        *reinterpret_cast<unsigned*>(sm.K + ok) =
-            pack_bf16(k0 * __expf(bC.x - bb.x), k1 * __expf(bC.y - bb.y));
-      }
-      if (eg == 0)
-        *reinterpret_cast<f32x2*>(reinterpret_cast<float*>(wsc + kWE) + 2 * cp) =
-            f32x2{__expf(bC.x), __expf(bC.y)};
-    }
-    lds_barrier();
-
-    // ---- Q^ and K^ fragments to the workspace; masked scores A to LDS
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {   // Q^ fragment (rb, ks) = (wave & 3, (wave >> 2) + 2h)
-      const int rb = wave & 3, ks = (wave >> 2) + 2 * h;
-      *reinterpret_cast<u32x4*>(wsc + kWQ + ((size_t)(rb * 4 + ks) * 64 + lane) * 16) =
-          *reinterpret_cast<const u32x4*>(sm.Q + (rb * 16 + l16) * PQ + ks * 32 + lq * 8);
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {   // K^ fragment f = 2 kb + js = wave + 8h
-      const int f = wave + 8 * h;
-      *reinterpret_cast<u32x4*>(wsc + kWK + ((size_t)f * 64 + lane) * 16) =
-          __builtin_bit_cast(u32x4, ld_tr8(sm.K, PT, (f & 1) * 32, (f >> 1) * 16));
-    }
-    for (int u = wave; u < 10; u += 8) {   // score tiles over the lower triangle
-      int rb, cb;
-      tri_pair(u, rb, cb);
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        acc = mfma(ld8(sm.Qr + (rb * 16 + l16) * PQ + ks * 32 + lq * 8),
-                   ld8(sm.Kr + (cb * 16 + l16) * PQ + ks * 32 + lq * 8), acc);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = rb * 16 + lq * 4 + i, j = cb * 16 + l16;
-        sm.A[r * PC + j] = f32_to_bf16(j <= r ? acc[i] : 0.f);
-      }
-    }
-    {   // the zero upper tiles that the 32-wide contraction slices of A reach: (0,1), (2,3)
-      const int t = tid >> 8, e = tid & 255;
-      sm.A[(t * 32 + (e >> 4)) * PC + t * 32 + 16 + (e & 15)] = 0;
-    }
-    lds_barrier();
-
-    // ---- O~ = A V: tiles (rb, vb = wave); row block rb reaches tokens <= 16 rb + 15
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int js = 0; js <= rb / 2; ++js)
-        acc = mfma(ld8(sm.A + (rb * 16 + l16) * PC + js * 32 + lq * 8),
-                   ld_tr8(sm.V, PT, js * 32, wave * 16), acc);
-      *reinterpret_cast<u32x2*>(wsc + kWO + ((size_t)(rb * 8 + wave) * 64 + lane) * 8) =
-          u32x2{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
-    }
-    lds_barrier();
-  }
+  prep_chunk(sm, in, cid, q, k, v, log_g, ws, T, nchunks);
+  for (cid += gridDim.x; cid < nchunks; cid += gridDim.x) prep_chunk(sm, in, cid, q, k, v, log_g, ws, T, nchunks);
 }
 
 // ------------------------------------------------------------------ sequential pass
 namespace gla {
 
 template <int VT>
-struct SeqSmem {
+struct alignas(16) SeqSmem {
   static constexpr int PV = VT == 16 ? 16 : 48;   // value-tile pitch (bf16)
   static constexpr int PO = VT + 4;               // output-tile pitch (bf16)
   uint16_t Sb[2][VT * PQ];       // bf16 copy of the state tile [v][k], by chunk parity
