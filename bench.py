@@ -1,6 +1,6 @@
 """Benchmark of the gated delta-rule hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--rows decode,leapq,gla,gdn]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--rows decode,kda,leapq,gla,gdn]
 
 Headline (`value`): Gated DeltaNet decode of one layer, 512 streams x 32 heads,
 d_k = d_v = 128, fp32 state resident in HBM, bf16 q/k/v; one step = one token for
@@ -88,6 +88,34 @@ def bench_decode(K, W, gen_steps=256):
                 ms_per_step=ms, tokens_per_s=B / (ms * 1e-3), head_steps=N,
                 bytes_per_launch=bytes_launch, achieved_gbs=gbs, frac_hbm=gbs / PEAK_HBM_GBS,
                 wall_s=wall), inp
+
+
+def bench_kda(K, W, gen_steps=256):
+    """Kimi Delta Attention decode (one decay per key channel) at the GDN decode
+    shape: one kda_decode_step launch over 16,384 heads per step."""
+    B, H = DECODE_B, DECODE_H
+    N = B * H
+    log(f"[kda] generating B={B} H={H} steps={gen_steps}")
+    inp = synth.kda_decode(B=B, H=H, steps=gen_steps, device="cuda")
+    S = inp["S0"].clone()
+    o = torch.empty((N, 1, D), dtype=torch.bfloat16, device="cuda")
+    q, k, v, a, b = (inp[n] for n in ("q", "k", "v", "alpha", "beta"))
+
+    def step(i):
+        t = i % gen_steps
+        m.kda_decode_step(S, q[t, :, None], k[t, :, None], v[t, :, None],
+                          a[t, :, None], b[t, :, None], o)
+
+    ms, wall = timed(step, K, W)
+    per_head = decode_bytes_per_head_step() + (D - 1) * 4     # alpha is a d_k vector
+    bytes_launch = per_head * N
+    gbs = bytes_launch / (ms * 1e-3) / 1e9
+    del inp, S, q, k, v, a, b
+    return dict(workload="kda_decode B=512 H=32 d_k=d_v=128 fp32 state, bf16 q/k/v, fp32 per-key-channel "
+                         "decays, T=1 per launch",
+                ms_per_step=ms, tokens_per_s=B / (ms * 1e-3), head_steps=N,
+                bytes_per_launch=bytes_launch, achieved_gbs=gbs, frac_hbm=gbs / PEAK_HBM_GBS,
+                wall_s=wall)
 
 
 def cpu_baseline_decode(inp, target_s=15.0):
@@ -277,6 +305,31 @@ def counter_traffic(kernel):
     return rec["traffic_bytes"]
 
 
+# ------------------------------------------------------------------- ceilings
+
+def measure_ceilings(reps=20):
+    """Ceilings measured on this GPU, reported beside the published peaks: a plain
+    2 GiB device-to-device copy (HBM read + write) and an 8192^3 bf16 matrix product
+    through torch's BLAS (dense MFMA). Neither is part of the hot path."""
+    n = 1 << 29
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    ms, _ = timed(lambda i: dst.copy_(src), reps, 3)
+    copy_gbs = 2 * n * 4 / (ms * 1e-3) / 1e9
+    del src, dst
+    M = 8192
+    g = torch.Generator(device="cuda").manual_seed(7)
+    a = torch.randn((M, M), generator=g, device="cuda").to(torch.bfloat16).contiguous()
+    b = torch.randn((M, M), generator=g, device="cuda").to(torch.bfloat16).contiguous()
+    ms, _ = timed(lambda i: torch.matmul(a, b), reps, 3)
+    gemm_tflops = 2 * M ** 3 / (ms * 1e-3) / 1e12
+    del a, b
+    torch.cuda.empty_cache()
+    return {"hbm_copy_gbs": copy_gbs, "bf16_gemm_tflops": gemm_tflops,
+            "how": "torch copy_ of 2 GiB fp32 (bytes read + written); torch.matmul 8192^3 bf16",
+            "published_hbm_gbs": PEAK_HBM_GBS, "published_bf16_tflops": PEAK_BF16_TFLOPS}
+
+
 # ------------------------------------------------------------------- main
 
 def main():
@@ -284,8 +337,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--rows", default="decode,leapq,gla,gdn")
+    ap.add_argument("--rows", default="decode,kda,leapq,gla,gdn")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the measured HBM-copy and bf16-GEMM ceilings")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -318,6 +373,13 @@ def main():
             cpu = cpu_baseline_decode(inp)
         del inp
         torch.cuda.empty_cache()
+    if "kda" in rows:
+        r = bench_kda(args.steps, args.warmup)
+        r["traffic_bytes"] = counter_traffic("gdn_decode_kernel<kda>")
+        out_rows["kda"] = r
+        log(f"[kda] {r['ms_per_step']*1e3:.1f} us/step  {r['achieved_gbs']:.0f} GB/s  "
+            f"{r['tokens_per_s']/1e6:.3f} M tok/s")
+        torch.cuda.empty_cache()
     if "gla" in rows:
         r = bench_gla()
         tp, ts = counter_traffic("gla_chunk_prep_kernel"), counter_traffic("gla_chunk_seq_kernel")
@@ -344,6 +406,15 @@ def main():
             f"+ {r['flush_kernel_ms']*1e3:.1f} us flush per window)  {r['achieved_gbs']:.0f} GB/s  "
             f"{r['tokens_per_s']/1e6:.3f} M tok/s")
         torch.cuda.empty_cache()
+    ceil = None
+    if not args.no_ceilings:
+        ceil = measure_ceilings()
+        log(f"[ceilings] copy {ceil['hbm_copy_gbs']:.0f} GB/s, bf16 GEMM {ceil['bf16_gemm_tflops']:.0f} TFLOP/s")
+        for r in out_rows.values():
+            if "achieved_gbs" in r:
+                r["frac_hbm_of_measured_copy"] = r["achieved_gbs"] / ceil["hbm_copy_gbs"]
+            if "tflops" in r:
+                r["frac_mfma_of_measured_gemm"] = r["tflops"] / ceil["bf16_gemm_tflops"]
     line = {
         "metric": "GDN decode tokens/s at B=512 (one layer, 32 heads, d=128)",
         "value": res["tokens_per_s"] if res else None,
@@ -363,6 +434,7 @@ def main():
                       "unit": "GB/s", "frac": res["frac_hbm"],
                       "traffic": counter_traffic("gdn_decode_kernel")} if res else None),
         "cpu_baseline": cpu,
+        "ceilings": ceil,
         "rows": out_rows,
         "host": {"cpus": os.cpu_count(), "machine": platform.processor() or platform.machine(),
                  "torch": torch.__version__, "hip": torch.version.hip},

@@ -1,8 +1,8 @@
 """MI355X-native gated delta-rule recurrent state update.
 
-Five entry points over the gdnrt HIP library (C ABI in include/gdnrt.h):
-``gdn_decode_step``, ``gla_chunk_fwd``, ``gdn_chunk_fwd``, ``leapq_decode_step``
-and ``leapq_window_flush``. ``synth`` draws the seeded synthetic workloads.
+Entry points over the gdnrt HIP library (C ABI in include/gdnrt.h):
+``gdn_decode_step``, ``gla_chunk_fwd``, ``gdn_chunk_fwd``, ``leapq_decode_step``,
+``leapq_window_flush`` and ``kda_decode_step``. ``synth`` draws the seeded synthetic workloads.
 """
 from .binding import (  # noqa: F401
     GdnrtError,
@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     gdn_decode_step,
     gla_chunk_fwd,
     gla_chunk_workspace,
+    kda_decode_step,
     leapq_decode_step,
     leapq_window_flush,
     lib,

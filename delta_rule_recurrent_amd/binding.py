@@ -34,6 +34,7 @@ class LeapqState(ctypes.Structure):
 # exported symbol -> (argtypes, restype); mirrors include/gdnrt.h
 SIGNATURES = {
     "gdn_decode_step": ([_vp] * 7 + [_c_int] * 5 + [_vp], _c_int),
+    "kda_decode_step": ([_vp] * 7 + [_c_int] * 5 + [_vp], _c_int),
     "gla_chunk_fwd": ([_vp] * 7 + [_c_int] * 6 + [_vp, ctypes.c_size_t, _vp], _c_int),
     "gla_chunk_fwd_workspace_bytes": ([_c_int] * 5, ctypes.c_size_t),
     "gdn_chunk_fwd": ([_vp] * 8 + [_c_int] * 6 + [_vp, ctypes.c_size_t, _vp], _c_int),
@@ -124,6 +125,28 @@ def gdn_decode_step(S, q, k, v, alpha, beta, o=None):
         o = torch.empty((N, T, D), dtype=q.dtype, device=q.device)
     _need(o, "o", q.dtype, (N, T, D))
     _check("gdn_decode_step", lib().gdn_decode_step(
+        _ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(o),
+        N, T, D, D, io, _stream()))
+    return o
+
+
+def kda_decode_step(S, q, k, v, alpha, beta, o=None):
+    """Kimi Delta Attention recurrent step(s) (one decay per key channel), state
+    updated in place.
+
+    S [N][128][128] fp32; q, k, v [N][T][128] (fp32 or bf16, one dtype);
+    alpha [N][T][128] fp32; beta [N][T] fp32. Returns o [N][T][128] in the dtype of q."""
+    N, T, _ = q.shape
+    io = _io(q.dtype)
+    _need(S, "S", torch.float32, (N, D, D))
+    for n_, t_ in (("q", q), ("k", k), ("v", v)):
+        _need(t_, n_, q.dtype, (N, T, D))
+    _need(alpha, "alpha", torch.float32, (N, T, D))
+    _need(beta, "beta", torch.float32, (N, T))
+    if o is None:
+        o = torch.empty((N, T, D), dtype=q.dtype, device=q.device)
+    _need(o, "o", q.dtype, (N, T, D))
+    _check("kda_decode_step", lib().kda_decode_step(
         _ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(o),
         N, T, D, D, io, _stream()))
     return o

@@ -20,11 +20,18 @@
 // keep more rows in flight per wave (and beat a plain copy kernel), which is why
 // the block is this small. Row sums use DPP inside 16-lane rows plus one swizzle
 // across the two halves of a 32-lane group.
+//
+// Kimi Delta Attention (same section: the decay becomes a vector alpha_t, one factor
+// per key channel, eq. 1) runs through the same kernel: with the decay folded into
+// the two read vectors,
+//
+//     u_i = b (v_i - S_i.(a o k)),   o_i = S_i.(a o q) + u_i (k.q),   S_i <- a o S_i + u_i k.
 #include "common.hpp"
 
 namespace gdnrt {
 
-template <typename IO>
+// VEC: alpha is [N][T][d_k] (one decay per key channel, KDA) instead of [N][T].
+template <typename IO, bool VEC>
 __global__ __launch_bounds__(256) void gdn_decode_kernel(
     float* __restrict__ S, const IO* __restrict__ q, const IO* __restrict__ k,
     const IO* __restrict__ v, const float* __restrict__ alpha, const float* __restrict__ beta,
@@ -44,25 +51,36 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(
     const size_t tok = (size_t)head * T + t;
     const f32x4 k4 = io_traits<IO>::ld4(k, tok * kD + col);
     const f32x4 q4 = io_traits<IO>::ld4(q, tok * kD + col);
-    const float a = alpha[tok];
     const float b = beta[tok];
     const float vi = io_traits<IO>::ld(v, tok * kD + row);
     const float kq = sum32(k4.x * q4.x + k4.y * q4.y + k4.z * q4.z + k4.w * q4.w);
-    const float pk = sum32(s.x * k4.x + s.y * k4.y + s.z * k4.z + s.w * k4.w);
-    const float pq = sum32(s.x * q4.x + s.y * q4.y + s.z * q4.z + s.w * q4.w);
-    const float u = b * (vi - a * pk);
-    const float oi = a * pq + u * kq;
-    s = a * s + u * k4;
+    float u, oi;
+    if constexpr (VEC) {
+      const f32x4 a4 = *reinterpret_cast<const f32x4*>(alpha + tok * kD + col);
+      const f32x4 ak = a4 * k4, aq = a4 * q4;
+      const float pk = sum32(s.x * ak.x + s.y * ak.y + s.z * ak.z + s.w * ak.w);
+      const float pq = sum32(s.x * aq.x + s.y * aq.y + s.z * aq.z + s.w * aq.w);
+      u = b * (vi - pk);
+      oi = pq + u * kq;
+      s = a4 * s + u * k4;
+    } else {
+      const float a = alpha[tok];
+      const float pk = sum32(s.x * k4.x + s.y * k4.y + s.z * k4.z + s.w * k4.w);
+      const float pq = sum32(s.x * q4.x + s.y * q4.y + s.z * q4.z + s.w * q4.w);
+      u = b * (vi - a * pk);
+      oi = a * pq + u * kq;
+      s = a * s + u * k4;
+    }
     if ((lane & 31) == 0) io_traits<IO>::st(o, tok * kD + row, oi);
   }
   __builtin_nontemporal_store(s, Sp);
 }
 
-template <typename IO>
+template <typename IO, bool VEC>
 static void launch_decode(float* S, const void* q, const void* k, const void* v,
                           const float* alpha, const float* beta, void* o, int N, int T,
                           hipStream_t stream) {
-  hipLaunchKernelGGL((gdn_decode_kernel<IO>), dim3(N * (kD / 8)), dim3(256), 0, stream, S,
+  hipLaunchKernelGGL((gdn_decode_kernel<IO, VEC>), dim3(N * (kD / 8)), dim3(256), 0, stream, S,
                      static_cast<const IO*>(q), static_cast<const IO*>(k),
                      static_cast<const IO*>(v), alpha, beta, static_cast<IO*>(o), T);
 }
@@ -71,33 +89,50 @@ static void launch_decode(float* S, const void* q, const void* k, const void* v,
 
 using namespace gdnrt;
 
+// Shared by the scalar-decay (GDN) and per-channel-decay (KDA) entry points; `vec`
+// selects the decay layout ([N][T] or [N][T][d_k]).
+static int decode_step(const char* fn, bool vec, float* S, const void* q, const void* k, const void* v,
+                       const float* alpha, const float* beta, void* o, int N, int T, int dk, int dv,
+                       int io, void* stream) {
+  if (N < 0 || T < 0) return set_error(GDNRT_ESHAPE, "%s: N=%d T=%d must be >= 0", fn, N, T);
+  if (dk != kD || dv != kD)
+    return set_error(GDNRT_ESHAPE, "%s: d_k=%d d_v=%d, only 128 is supported", fn, dk, dv);
+  if (io != GDNRT_F32 && io != GDNRT_BF16) return set_error(GDNRT_EDTYPE, "%s: io=%d", fn, io);
+  if (N == 0 || T == 0) return clear_error();
+  if (!S || !q || !k || !v || !alpha || !beta || !o)
+    return set_error(GDNRT_EINVAL, "%s: null pointer argument", fn);
+  if ((size_t)N * (kD / 8) > 0x7fffffffu || (size_t)N * (size_t)T > ((size_t)1 << 36))
+    return set_error(GDNRT_ESHAPE, "%s: N=%d T=%d too large", fn, N, T);
+  if (!aligned16(S) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (vec ? !aligned16(alpha) : !aligned4(alpha)) || !aligned4(beta))
+    return set_error(GDNRT_EALIGN, vec ? "%s: S, q, k, v, o, alpha must be 16-byte aligned, beta 4-byte"
+                                       : "%s: S, q, k, v, o must be 16-byte aligned, gates 4-byte", fn);
+  const size_t es = io == GDNRT_F32 ? 4 : 2;
+  const size_t ntok = (size_t)N * T;
+  const size_t nS = (size_t)N * kD * kD * 4, nIO = ntok * kD * es, nG = ntok * 4, nA = vec ? ntok * kD * 4 : nG;
+  if (overlaps(o, nIO, S, nS) || overlaps(o, nIO, q, nIO) || overlaps(o, nIO, k, nIO) ||
+      overlaps(o, nIO, v, nIO) || overlaps(o, nIO, alpha, nA) || overlaps(o, nIO, beta, nG) ||
+      overlaps(S, nS, q, nIO) || overlaps(S, nS, k, nIO) || overlaps(S, nS, v, nIO) ||
+      overlaps(S, nS, alpha, nA) || overlaps(S, nS, beta, nG))
+    return set_error(GDNRT_EINVAL, "%s: S or o overlaps another buffer", fn);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (io == GDNRT_F32)
+    vec ? launch_decode<float, true>(S, q, k, v, alpha, beta, o, N, T, s)
+        : launch_decode<float, false>(S, q, k, v, alpha, beta, o, N, T, s);
+  else
+    vec ? launch_decode<uint16_t, true>(S, q, k, v, alpha, beta, o, N, T, s)
+        : launch_decode<uint16_t, false>(S, q, k, v, alpha, beta, o, N, T, s);
+  return check_launch(fn);
+}
+
 extern "C" int gdn_decode_step(float* S, const void* q, const void* k, const void* v,
                                const float* alpha, const float* beta, void* o, int N, int T,
                                int dk, int dv, int io, void* stream) {
-  if (N < 0 || T < 0) return set_error(GDNRT_ESHAPE, "gdn_decode_step: N=%d T=%d must be >= 0", N, T);
-  if (dk != kD || dv != kD)
-    return set_error(GDNRT_ESHAPE, "gdn_decode_step: d_k=%d d_v=%d, only 128 is supported", dk, dv);
-  if (io != GDNRT_F32 && io != GDNRT_BF16) return set_error(GDNRT_EDTYPE, "gdn_decode_step: io=%d", io);
-  if (N == 0 || T == 0) return clear_error();
-  if (!S || !q || !k || !v || !alpha || !beta || !o)
-    return set_error(GDNRT_EINVAL, "gdn_decode_step: null pointer argument");
-  if ((size_t)N * (kD / 8) > 0x7fffffffu || (size_t)N * (size_t)T > ((size_t)1 << 36))
-    return set_error(GDNRT_ESHAPE, "gdn_decode_step: N=%d T=%d too large", N, T);
-  if (!aligned16(S) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
-      !aligned4(alpha) || !aligned4(beta))
-    return set_error(GDNRT_EALIGN, "gdn_decode_step: S, q, k, v, o must be 16-byte aligned, gates 4-byte");
-  const size_t es = io == GDNRT_F32 ? 4 : 2;
-  const size_t ntok = (size_t)N * T;
-  const size_t nS = (size_t)N * kD * kD * 4, nIO = ntok * kD * es, nG = ntok * 4;
-  if (overlaps(o, nIO, S, nS) || overlaps(o, nIO, q, nIO) || overlaps(o, nIO, k, nIO) ||
-      overlaps(o, nIO, v, nIO) || overlaps(o, nIO, alpha, nG) || overlaps(o, nIO, beta, nG) ||
-      overlaps(S, nS, q, nIO) || overlaps(S, nS, k, nIO) || overlaps(S, nS, v, nIO) ||
-      overlaps(S, nS, alpha, nG) || overlaps(S, nS, beta, nG))
-    return set_error(GDNRT_EINVAL, "gdn_decode_step: S or o overlaps another buffer");
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (io == GDNRT_F32)
-    launch_decode<float>(S, q, k, v, alpha, beta, o, N, T, s);
-  else
-    launch_decode<uint16_t>(S, q, k, v, alpha, beta, o, N, T, s);
-  return check_launch("gdn_decode_step");
+  return decode_step("gdn_decode_step", false, S, q, k, v, alpha, beta, o, N, T, dk, dv, io, stream);
+}
+
+extern "C" int kda_decode_step(float* S, const void* q, const void* k, const void* v,
+                               const float* alpha, const float* beta, void* o, int N, int T,
+                               int dk, int dv, int io, void* stream) {
+  return decode_step("kda_decode_step", true, S, q, k, v, alpha, beta, o, N, T, dk, dv, io, stream);
 }

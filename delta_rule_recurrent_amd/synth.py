@@ -131,6 +131,45 @@ def gdn_decode(B=512, H=32, steps=256, d=D, device="cpu", seed=1003, io=torch.bf
     return dict(q=q, k=k, v=v, alpha=alpha, beta=beta, S0=S0)
 
 
+def _decode_gates_vec(steps, B, H, d, g, device):
+    """Per-key-channel decays: heads h < H/2 are slow heads with alpha = 0.999 on
+    every channel and token; the rest draw alpha = sigmoid(N(2,1)) per (stream,
+    token, key channel), in chunks of 256 steps."""
+    N = B * H
+    a = torch.empty((steps, N, d), device=device, dtype=torch.float32)
+    for s0 in range(0, steps, CHUNK_STEPS):
+        s1 = min(steps, s0 + CHUNK_STEPS)
+        a[s0:s1] = torch.sigmoid(_randn((s1 - s0, N, d), g, device, 2.0, 1.0))
+    slow = (torch.arange(N, device=device) % H) < (H // 2)
+    a[:, slow] = 0.999
+    return a
+
+
+def kda_decode(B=512, H=32, steps=256, d=D, device="cpu", seed=1005, io=torch.bfloat16):
+    """Kimi Delta Attention decode of one layer: the GDN decode workload's shape and
+    draws, with one decay per key channel (``alpha`` is ``[steps][N][d_k]``)."""
+    g = _gen(device, seed)
+    N = B * H
+    q, k, v = _decode_tokens(steps, N, d, g, device, io)
+    alpha = _decode_gates_vec(steps, B, H, d, g, device)
+    beta = torch.sigmoid(_randn((steps, N), g, device, 0.0, 1.0))
+    S0 = _randn((N, d, d), g, device, 0.0, 0.05)
+    return dict(q=q, k=k, v=v, alpha=alpha, beta=beta, S0=S0)
+
+
+def kda_small(T=64, d=D, device="cpu", seed=1006):
+    """One KDA head, fp32 throughout: q, k L2-normalised, alpha = sigmoid(N(4,1))
+    per key channel and token, beta = sigmoid(N(0,1)), zero initial state."""
+    g = _gen(device, seed)
+    q = _l2n(_randn((1, T, d), g, device))
+    k = _l2n(_randn((1, T, d), g, device))
+    v = _randn((1, T, d), g, device)
+    alpha = torch.sigmoid(_randn((1, T, d), g, device, 4.0, 1.0))
+    beta = torch.sigmoid(_randn((1, T), g, device, 0.0, 1.0))
+    S0 = torch.zeros((1, d, d), device=device, dtype=torch.float32)
+    return dict(q=q, k=k, v=v, alpha=alpha, beta=beta, S0=S0)
+
+
 def leapq_decode(B=512, H=32, steps=4096, d=D, device="cpu", seed=1004,
                  outlier_scale=50.0, n_outliers=2):
     """LeapQuant windowed 8-bit decode: the decode workload above plus two

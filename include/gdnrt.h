@@ -72,6 +72,21 @@ GDNRT_API int gdn_decode_step(float* S, const void* q, const void* k, const void
                     int N, int T, int dk, int dv, int io, void* stream);
 
 /*
+ * Kimi Delta Attention recurrent step: the same delta rule with the decay a vector,
+ * one factor per key channel ("LeapQuant: an 8-bit recurrent state that stops
+ * rounding every token", section "The state, from the update rule up", eq. 1 and
+ * eq. 3). In the [d_v][d_k] layout, per head and token:
+ *
+ *     u_t = beta_t (v_t - S_{t-1} (alpha_t o k_t)),
+ *     S_t = S_{t-1} Diag(alpha_t) + u_t k_t^T,   o_t = S_t q_t.
+ *
+ * Arguments as gdn_decode_step except alpha: [N][T][dk] fp32, 16-byte aligned.
+ */
+GDNRT_API int kda_decode_step(float* S, const void* q, const void* k, const void* v,
+                    const float* alpha, const float* beta, void* o,
+                    int N, int T, int dk, int dv, int io, void* stream);
+
+/*
  * Gated linear attention, chunkwise forward of one sequence shard that starts
  * from an incoming state ("ZeCO: Zero Communication Overhead Sequence Parallelism
  * for Linear Attention", section "Gated Linear Attention (GLA) Formulation" for

@@ -29,11 +29,11 @@ def declared():
     return re.findall(r"GDNRT_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
 
 
-def test_header_declares_the_five_entry_points():
+def test_header_declares_the_entry_points():
     names = set(declared())
     for n in ("gdn_decode_step", "gla_chunk_fwd", "gdn_chunk_fwd", "leapq_decode_step",
               "leapq_window_flush", "gdnrt_last_error", "gdn_chunk_fwd_workspace_bytes",
-              "gla_chunk_fwd_workspace_bytes"):
+              "gla_chunk_fwd_workspace_bytes", "kda_decode_step"):
         assert n in names, n
 
 
@@ -61,6 +61,21 @@ def test_decode_validation(lib):
     big = ctypes.c_void_p(1 << 40)
     # o overlapping the state
     assert f(big, p, p, p, p, p, big, 4, 1, 128, 128, 1, None) == EINVAL
+
+
+def test_kda_decode_validation(lib):
+    f = lib.kda_decode_step
+    p = ctypes.c_void_p(4096)
+    assert f(p, p, p, p, p, p, p, 4, 1, 128, 64, 1, None) == ESHAPE and "kda_decode_step" in _err(lib)
+    assert f(p, p, p, p, p, p, p, 4, 1, 128, 128, 3, None) == EDTYPE
+    assert f(p, p, p, p, None, p, p, 4, 1, 128, 128, 1, None) == EINVAL
+    # the per-channel decays are read 16 bytes at a time: 4-byte alignment is not enough
+    assert f(p, p, p, p, ctypes.c_void_p(4100), p, p, 4, 1, 128, 128, 1, None) == EALIGN
+    assert lib.gdn_decode_step(p, p, p, p, ctypes.c_void_p(4100), p, ctypes.c_void_p(1 << 40),
+                               4, 1, 128, 128, 1, None) != EALIGN
+    # alpha spans N*T*d_k floats: an o placed inside that span overlaps it
+    assert f(p, ctypes.c_void_p(1 << 41), p, p, ctypes.c_void_p(1 << 40), p,
+             ctypes.c_void_p((1 << 40) + 1024), 4, 1, 128, 128, 1, None) == EINVAL
 
 
 def test_chunk_validation(lib):
