@@ -3,7 +3,7 @@
     python -m delta_rule_recurrent_amd.build
 
 hipcc cross-compiles for gfx950 without a GPU. Packed fp32 VALU instructions are
-disabled for every device compilation.
+disabled for every device compilation; MFMA instructions use their VGPR form.
 """
 from __future__ import annotations
 
@@ -37,6 +37,10 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
            "-fvisibility=hidden", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           # MFMA accumulators in ordinary VGPRs: kernels that also work on the
+           # accumulators with VALU code then hold one copy instead of an AGPR copy
+           # plus a VGPR copy
+           "-mllvm", "-amdgpu-mfma-vgpr-form",
            "-I", os.path.join(ROOT, "include"), "-o", tmp] + sources()
     if verbose:
         print(" ".join(cmd), flush=True)

@@ -224,45 +224,79 @@ __global__ __launch_bounds__(128) void leapq_decode_kernel(
 
 // ============================================================== window flush
 //
-// One block of 128*NQ threads per head. Thread t owns value row v = t % 128 and
-// key columns [c0, c0 + 128/NQ), c0 = (t / 128) * 128/NQ, of the dense state in
-// registers; a copy in LDS ([128][129] fp32, conflict-free by rows and columns)
-// serves the column operations. Steps: rebuild (eq. 4) or load `dense`;
-// compensator fit by subspace iteration with CholeskyQR2; subtract the
-// fp16-rounded pieces; smoothing factors; value-channel scales; codes.
-// Per-head vectors in LDS are [r][128] (rank-major), so lane-indexed accesses are
-// consecutive and column-indexed ones are broadcasts.
+// One block of 256 threads (four waves) per head; the dense 128 x 128 state stays in
+// fp32 MFMA accumulators from the rebuild to the codes. Wave w holds value rows
+// [32 w, 32 w + 32) as two tiles t of 16 rows; lane (n = lane % 16, g = lane / 16)
+// holds rows 32 w + 16 t + n and the 32 contiguous key channels [32 g, 32 g + 32):
+// register e of accumulator tile (t, tc) is S[32 w + 16 t + n][32 g + 4 tc + e].
+// For v_mfma_f32_16x16x4f32 the tile (t, tc) is the block D = S^T with its rows
+// (key channels) permuted: D row i of tile tc is channel 32 (i / 4) + 4 tc + i % 4.
+//
+//  * rebuild (eq. 4): D starts as the decayed dequantised residual, then the
+//    compensators and buffered records, four rank-one terms per MFMA:
+//    A[i][k] = key of term k at channel i, B[k][j] = coefficient x value vector;
+//  * compensator fit (eq. 5, subspace iteration with CholeskyQR2): Y = S Q is
+//    summed within a lane over its 32 channels and across the four lanes of a
+//    row; S^T Y within a lane over its two rows, across the 16 lanes of a DPP
+//    row by a reduce-scatter, and across the four waves through LDS; one wave
+//    orthonormalises in fp64;
+//  * residual, smoothing factors (eq. 7), value-channel scales and codes, each
+//    lane writing its 32 codes of a row as two 16-byte stores.
 
-constexpr int kP = kD + 1;
-constexpr int kFlushNQ = 8;   // 1024 threads per flush block, 16 key columns each
+constexpr int kFlushNT = 256;
+constexpr int kRP = kD + 16;   // fp32 pitch of staged rank-one rows: the rows read by the
+                               // two half-waves of an MFMA operand load fall in other banks
+constexpr int kMaxTerms = kMaxRank + kMaxWindow;
 
-template <int NQ>
+template <int RQ>
 struct alignas(16) FlushSmem {
-  float S[kD * kP];
-  float K[(kMaxRank + kMaxWindow) * kD];   // keys of the rank-one terms: compensators, records
-  float U[(kMaxRank + kMaxWindow) * kD];   // their value-side vectors
-  float Qa[kMaxRank * kD];                 // [r][c]
-  float Qb[kMaxRank * kD];
-  float Y[kMaxRank * kD];                  // [r][v]
-  float part[NQ * kMaxRank * kD];          // [p][r][x]
-  double gram[2][2][kMaxRank * kMaxRank];  // [pass][wave 0, 1] partial Gram matrices
-  float col[kD];
-  float dec[kMaxWindow + 1];               // dec[j] = G_j for j < m, dec[m] = G0
-  float red[NQ * kD];
+  union {
+    struct {
+      float K[kMaxTerms * kRP];   // term keys, channels permuted as the D rows of a tile
+      float U[kMaxTerms * kRP];   // term value vectors
+    } rb;
+    float red[4 * kD * RQ];       // per-wave partial S^T Y, [wave][channel][r]
+  } u;
+  float Q[kD * RQ];               // subspace block, [channel][r] (r >= rank: zero)
+  float Kh[kD * RQ];              // fp16-rounded compensator keys, [channel][r]
+  float col[kD];                  // stored smoothing factors, then 1 / the new ones
+  float cred[4 * kD];             // per-wave column statistics
+  float dec[kMaxWindow + 1];      // dec[j] = G_j for j < m, dec[m] = G0
 };
 
-// dst[r][x] = sum over the NQ partial sums, returned to threads t < 128 (row t)
-template <int NQ, int RANK>
-__device__ __forceinline__ void combine_parts(const FlushSmem<NQ>& sm, float (&x)[RANK]) {
-  const int t = threadIdx.x;
+// fp32 16 x 16 x 4 MFMA: lane l holds A[l%16][l/16], B[l/16][l%16]; D[4(l/16)+e][l%16]
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// One halving step of a reduce-scatter inside a 16-lane DPP row: x[0, M) becomes
+// x[0, M/2), the half selected by `upper`, plus the partner lane's copy of that half.
+// The partner (DPP control CTRL) differs from this lane in the bit that sets `upper`.
+template <int M, int CTRL>
+__device__ __forceinline__ void rs_step(float* x, bool upper) {
 #pragma unroll
-  for (int r = 0; r < RANK; ++r) {
-    float acc = 0.f;
-#pragma unroll
-    for (int p = 0; p < NQ; ++p) acc += sm.part[(p * kMaxRank + r) * kD + t];
-    x[r] = acc;
+  for (int i = 0; i < M / 2; ++i) {
+    const float keep = upper ? x[M / 2 + i] : x[i];
+    const float give = upper ? x[i] : x[M / 2 + i];
+    x[i] = keep + dpp<CTRL>(give);
   }
 }
+
+// Reduce-scatter over the 16 lanes of a DPP row: on entry each lane holds NV values;
+// on return lane n holds, in x[0, NV/16), the row sums of values [n NV/16, (n+1) NV/16).
+// Partners: row_ror:8 (n ^ 8), row_half_mirror (7 - n within 8: bit 2 differs),
+// quad_perm(3,2,1,0) (bit 1 differs), quad_perm(1,0,3,2) (n ^ 1).
+template <int NV>
+__device__ __forceinline__ void reduce_scatter16(float (&x)[NV], int n) {
+  static_assert(NV >= 16 && NV % 16 == 0, "16 lanes");
+  rs_step<NV, 0x128>(x, n & 8);
+  rs_step<NV / 2, 0x141>(x, n & 4);
+  rs_step<NV / 4, 0x1B>(x, n & 2);
+  rs_step<NV / 8, 0xB1>(x, n & 1);
+}
+
+// lane-to-lane move within a wave: value of lane (lane ^ M)
+__device__ __forceinline__ float xor_lane(float x, int m) { return __shfl_xor(x, m); }
 
 // DPP move of an fp64 value (both 32-bit halves)
 template <int CTRL>
@@ -289,298 +323,331 @@ __device__ __forceinline__ double wave_sum_f64(double x) {
   return (lane64(x, 0) + lane64(x, 16)) + (lane64(x, 32) + lane64(x, 48));
 }
 
-// Waves 0 and 1 (rows t < 128, x in registers): this wave's share of the Gram
-// matrix x^T x (upper triangle) to g. The fit is ill-conditioned on states with
-// outlier channels, so the Gram matrix, the Cholesky factor and the triangular
-// solve are formed in fp64 (products of fp32 values are exact there).
+// CholeskyQR2 of a 128 x RANK block held by one wave, rows lane and lane + 64:
+// twice x <- x L^{-T} with L L^T = x^T x + (1e-6 tr + 1e-30) I. The fit is
+// ill-conditioned on states with outlier channels, so the Gram matrix, the factor
+// and the solve are fp64 (products of fp32 values are exact there).
 template <int RANK>
-__device__ __forceinline__ void partial_gram(const float (&x)[RANK], double* g) {
-  const int lane = threadIdx.x & 63;
+__device__ __forceinline__ void cholqr2_wave(float (&x)[2][RANK]) {
 #pragma unroll
-  for (int i = 0; i < RANK; ++i)
+  for (int pass = 0; pass < 2; ++pass) {
+    double G[RANK][RANK];
 #pragma unroll
-    for (int j = i; j < RANK; ++j) {
-      const double s = wave_sum_f64((double)x[i] * (double)x[j]);
-      if (lane == 0) g[i * kMaxRank + j] = s;
-    }
-}
-
-// One CholeskyQR step on row x (threads t < 128): x <- x L^{-T} with
-// L L^T = G + (1e-6 tr G + 1e-30) I, G the sum of the two partial Gram matrices
-// (read from LDS as needed). L is kept packed, row by row, and 1 / diag(L) apart.
-template <int RANK>
-__device__ __forceinline__ void chol_solve(float (&x)[RANK], const double* g0, const double* g1) {
-  auto G = [&](int i, int j) { return g0[i * kMaxRank + j] + g1[i * kMaxRank + j]; };   // i <= j
-  double tr = 0.0;
+    for (int i = 0; i < RANK; ++i)
 #pragma unroll
-  for (int i = 0; i < RANK; ++i) tr += G(i, i);
-  const double sh = 1e-6 * tr + 1e-30;
-  double L[RANK * (RANK + 1) / 2], rd[RANK];   // L[i][j] at i (i + 1) / 2 + j
+      for (int j = i; j < RANK; ++j)
+        G[i][j] = wave_sum_f64((double)x[0][i] * (double)x[0][j] + (double)x[1][i] * (double)x[1][j]);
+    double tr = 0.0;
 #pragma unroll
-  for (int i = 0; i < RANK; ++i) {
+    for (int i = 0; i < RANK; ++i) tr += G[i][i];
+    const double sh = 1e-6 * tr + 1e-30;
+    double L[RANK * (RANK + 1) / 2], rd[RANK];   // L[i][j] at i (i + 1) / 2 + j
 #pragma unroll
-    for (int j = 0; j <= i; ++j) {
-      double s = G(j, i) + (i == j ? sh : 0.0);
+    for (int i = 0; i < RANK; ++i) {
 #pragma unroll
-      for (int p = 0; p < j; ++p) s -= L[i * (i + 1) / 2 + p] * L[j * (j + 1) / 2 + p];
-      if (i == j) {
-        const double d = sqrt(fmax(s, 0.0));
-        L[i * (i + 1) / 2 + i] = d;
-        rd[i] = 1.0 / d;
-      } else {
-        L[i * (i + 1) / 2 + j] = s * rd[j];
+      for (int j = 0; j <= i; ++j) {
+        double s = G[j][i] + (i == j ? sh : 0.0);
+#pragma unroll
+        for (int p = 0; p < j; ++p) s -= L[i * (i + 1) / 2 + p] * L[j * (j + 1) / 2 + p];
+        if (i == j) {
+          const double d = sqrt(fmax(s, 0.0));
+          L[i * (i + 1) / 2 + i] = d;
+          rd[i] = 1.0 / d;
+        } else {
+          L[i * (i + 1) / 2 + j] = s * rd[j];
+        }
       }
     }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      double y[RANK];
+#pragma unroll
+      for (int j = 0; j < RANK; ++j) {
+        double s = x[h][j];
+#pragma unroll
+        for (int p = 0; p < j; ++p) s -= y[p] * L[j * (j + 1) / 2 + p];
+        y[j] = s * rd[j];
+      }
+#pragma unroll
+      for (int j = 0; j < RANK; ++j) x[h][j] = (float)y[j];
+    }
   }
-  double y[RANK];
-#pragma unroll
-  for (int j = 0; j < RANK; ++j) {
-    double s = x[j];
-#pragma unroll
-    for (int p = 0; p < j; ++p) s -= y[p] * L[j * (j + 1) / 2 + p];
-    y[j] = s * rd[j];
-  }
-#pragma unroll
-  for (int j = 0; j < RANK; ++j) x[j] = (float)y[j];
 }
 
 // four consecutive floats of LDS as a vector (16-byte aligned)
 __device__ __forceinline__ f32x4 lds4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 
-template <int NQ, int RANK>
-__global__ __launch_bounds__(128 * NQ) void leapq_flush_kernel(
+template <int RANK>
+__global__ __launch_bounds__(kFlushNT) __attribute__((amdgpu_waves_per_eu(RANK <= 5 ? 3 : 2))) void leapq_flush_kernel(
     int8_t* __restrict__ codes, float* __restrict__ vscale, float* __restrict__ ksmooth,
     uint16_t* __restrict__ ct_k, uint16_t* __restrict__ ct_u, const float* __restrict__ buf_k,
     const float* __restrict__ buf_u, const float* __restrict__ buf_a, int window, int m,
     const float* __restrict__ dense, const float* __restrict__ q0, int iters, int smooth_mode,
     float* __restrict__ pre_round) {
-  constexpr int NT = 128 * NQ, FC = kD / NQ;
-  static_assert(FC == 16, "16 key columns per thread");
-  constexpr int rank = RANK;
-  __shared__ FlushSmem<NQ> sm;
-  const int tid = threadIdx.x;
+  constexpr int RQ = RANK <= 4 ? 4 : 8;   // padded rank of the LDS blocks
+  __shared__ FlushSmem<RQ> sm;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
   const int head = blockIdx.x;
   const size_t hk = (size_t)head * kD;
-  const int v = tid & (kD - 1), qd = tid >> 7, c0 = qd * FC;
-  float S[FC];
+  const int vrow[2] = {32 * w + n, 32 * w + 16 + n};
+  f32x4 acc[2][8];
 
-  // ---------------------------------------------------------------- dense state
-  if (dense) {
-    const f32x4* Dp = reinterpret_cast<const f32x4*>(dense + (hk + v) * kD + c0);
-#pragma unroll
-    for (int i = 0; i < FC / 4; ++i) {
-      const f32x4 x = Dp[i];
-      S[4 * i] = x.x; S[4 * i + 1] = x.y; S[4 * i + 2] = x.z; S[4 * i + 3] = x.w;
+  // ---------------------------------------------------------------- inputs
+  if constexpr (RANK > 0) {
+    for (int i = tid; i < kD * RQ; i += kFlushNT) {
+      const int c = i / RQ, r = i % RQ;
+      sm.Q[i] = r < RANK ? q0[c * RANK + r] : 0.f;
     }
+  }
+  const int nt = dense ? 0 : RANK + m;   // rank-one terms of the rebuild
+  const int ns = (nt + 3) >> 2;          // MFMA steps of four terms
+  uint4 z[2][2];
+  float vs[2];
+  if (dense) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int tc = 0; tc < 8; ++tc)
+        acc[t][tc] = *reinterpret_cast<const f32x4*>(dense + (hk + vrow[t]) * kD + 32 * g + 4 * tc);
   } else {
-    // every input of the rebuild is requested before the one wait: this row's codes
-    // and scale, the rank-one terms (keys and value vectors) and decays to LDS
-    const uint4 zw = *reinterpret_cast<const uint4*>(codes + (hk + v) * kD + c0);
-    const float vsv = vscale[hk + v];
-    const int nt = rank + m;
-    {   // one piece of four entries of K and of U per thread (nt <= 24 rows of 32)
-      const int j = tid >> 5, c = (tid & 31) * 4;
-      if (j < rank) {
-        const uint2 hk4 = *reinterpret_cast<const uint2*>(ct_k + ((size_t)head * rank + j) * kD + c);
-        const uint2 hu4 = *reinterpret_cast<const uint2*>(ct_u + ((size_t)head * rank + j) * kD + c);
-        *reinterpret_cast<f32x4*>(sm.K + j * kD + c) =
-            f32x4{h2f(uint16_t(hk4.x)), h2f(uint16_t(hk4.x >> 16)), h2f(uint16_t(hk4.y)), h2f(uint16_t(hk4.y >> 16))};
-        *reinterpret_cast<f32x4*>(sm.U + j * kD + c) =
-            f32x4{h2f(uint16_t(hu4.x)), h2f(uint16_t(hu4.x >> 16)), h2f(uint16_t(hu4.y)), h2f(uint16_t(hu4.y >> 16))};
+    // every input of the rebuild is requested before the one wait
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint4* zp = reinterpret_cast<const uint4*>(codes + (hk + vrow[t]) * kD + 32 * g);
+      z[t][0] = zp[0];
+      z[t][1] = zp[1];
+      vs[t] = vscale[hk + vrow[t]];
+    }
+    // term rows (compensators, then records; zero up to a multiple of four): piece q
+    // of a row is channels [4 q, 4 q + 4); keys go to D-row order, values as they are
+    for (int idx = tid; idx < ns * 4 * 32; idx += kFlushNT) {
+      const int j = idx >> 5, q = idx & 31;
+      f32x4 kk = {0.f, 0.f, 0.f, 0.f}, uu = {0.f, 0.f, 0.f, 0.f};
+      if (j < RANK) {
+        const uint2 hk4 = *reinterpret_cast<const uint2*>(ct_k + ((size_t)head * RANK + j) * kD + 4 * q);
+        const uint2 hu4 = *reinterpret_cast<const uint2*>(ct_u + ((size_t)head * RANK + j) * kD + 4 * q);
+        kk = f32x4{h2f(uint16_t(hk4.x)), h2f(uint16_t(hk4.x >> 16)), h2f(uint16_t(hk4.y)), h2f(uint16_t(hk4.y >> 16))};
+        uu = f32x4{h2f(uint16_t(hu4.x)), h2f(uint16_t(hu4.x >> 16)), h2f(uint16_t(hu4.y)), h2f(uint16_t(hu4.y >> 16))};
       } else if (j < nt) {
-        const size_t off = ((size_t)head * window + (j - rank)) * kD + c;
-        *reinterpret_cast<f32x4*>(sm.K + j * kD + c) = *reinterpret_cast<const f32x4*>(buf_k + off);
-        *reinterpret_cast<f32x4*>(sm.U + j * kD + c) = *reinterpret_cast<const f32x4*>(buf_u + off);
+        const size_t off = ((size_t)head * window + (j - RANK)) * kD + 4 * q;
+        kk = *reinterpret_cast<const f32x4*>(buf_k + off);
+        uu = *reinterpret_cast<const f32x4*>(buf_u + off);
       }
+      *reinterpret_cast<f32x4*>(sm.u.rb.K + j * kRP + 16 * (q & 7) + 4 * (q >> 3)) = kk;
+      *reinterpret_cast<f32x4*>(sm.u.rb.U + j * kRP + 4 * q) = uu;
     }
     if (tid < kD) sm.col[tid] = ksmooth[hk + tid];
     if (tid == 0) {   // suffix products of the buffered decays, newest first
       const float* ba = buf_a + (size_t)head * window;
-      float g = 1.f;
+      float gg = 1.f;
       for (int j = m - 1; j >= 0; --j) {
-        sm.dec[j] = g;
-        g *= ba[j];
+        sm.dec[j] = gg;
+        gg *= ba[j];
       }
-      sm.dec[m] = g;
-    }
-    lds_barrier();
-#pragma unroll
-    for (int i = 0; i < FC; ++i) S[i] = 0.f;
-    for (int j = 0; j < nt; ++j) {   // compensators (decay G0), then records (G_j)
-      const float cj = (j < rank ? sm.dec[m] : sm.dec[j - rank]) * sm.U[j * kD + v];
-      const float* Kj = sm.K + j * kD + c0;
-#pragma unroll
-      for (int i = 0; i < FC / 4; ++i) {
-        const f32x4 kk = lds4(Kj + 4 * i);
-        S[4 * i] += cj * kk.x; S[4 * i + 1] += cj * kk.y; S[4 * i + 2] += cj * kk.z; S[4 * i + 3] += cj * kk.w;
-      }
-    }
-    const float sv = sm.dec[m] * vsv * (1.0f / 127.0f);
-    const uint32_t z4[4] = {zw.x, zw.y, zw.z, zw.w};
-#pragma unroll
-    for (int i4 = 0; i4 < FC / 4; ++i4) {
-      const f32x4 cc = lds4(sm.col + c0 + 4 * i4);
-      S[4 * i4] += sv * sb(z4[i4], 0) * cc.x;
-      S[4 * i4 + 1] += sv * sb(z4[i4], 1) * cc.y;
-      S[4 * i4 + 2] += sv * sb(z4[i4], 2) * cc.z;
-      S[4 * i4 + 3] += sv * sb(z4[i4], 3) * cc.w;
+      sm.dec[m] = gg;
     }
   }
+  lds_barrier();
+
+  // ---------------------------------------------------------------- rebuild
+  if (!dense) {
+    const float g0 = sm.dec[m];
 #pragma unroll
-  for (int i = 0; i < FC; ++i) sm.S[v * kP + c0 + i] = S[i];
+    for (int t = 0; t < 2; ++t) {
+      const float sv = g0 * vs[t] * (1.0f / 127.0f);
+      const uint32_t zw[8] = {z[t][0].x, z[t][0].y, z[t][0].z, z[t][0].w,
+                              z[t][1].x, z[t][1].y, z[t][1].z, z[t][1].w};
+#pragma unroll
+      for (int tc = 0; tc < 8; ++tc) {
+        const f32x4 cc = lds4(sm.col + 32 * g + 4 * tc);
+        acc[t][tc] = f32x4{sv * sb(zw[tc], 0) * cc.x, sv * sb(zw[tc], 1) * cc.y,
+                           sv * sb(zw[tc], 2) * cc.z, sv * sb(zw[tc], 3) * cc.w};
+      }
+    }
+    for (int s = 0; s < ns; ++s) {
+      const int j = 4 * s + g;   // this lane's term (the k index of its A and B entries)
+      const float cj = j < RANK ? g0 : (j < nt ? sm.dec[j - RANK] : 0.f);
+      const float b0 = cj * sm.u.rb.U[j * kRP + 32 * w + n];
+      const float b1 = cj * sm.u.rb.U[j * kRP + 32 * w + 16 + n];
+#pragma unroll
+      for (int tc = 0; tc < 8; ++tc) {
+        const float a = sm.u.rb.K[j * kRP + 16 * tc + n];
+        acc[0][tc] = mfma4(a, b0, acc[0][tc]);
+        acc[1][tc] = mfma4(a, b1, acc[1][tc]);
+      }
+    }
+  }
 
   // ---------------------------------------------------------------- compensators
   if constexpr (RANK > 0) {
-    for (int i = tid; i < kD * rank; i += NT) sm.Qa[(i % rank) * kD + i / rank] = q0[i];
-    lds_barrier();
-    // the state is read back from its LDS copy below, so that its registers are free
-    // during the fit
-    for (int it = 0; it <= iters; ++it) {
-      // Y = S Q (this thread's row segment)
-      float acc[RANK];
+    lds_barrier();   // the term rows share LDS with the S^T Y partials
+    float y[2][RANK];
+    for (int it = 0;; ++it) {
+      // Y = S Q: this lane's 32 channels, then the four lanes of the row
 #pragma unroll
-      for (int r = 0; r < RANK; ++r) acc[r] = 0.f;
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int i4 = 0; i4 < FC / 4; ++i4) {
-        const float* sr = sm.S + v * kP + c0 + 4 * i4;
-        const float s0 = sr[0], s1 = sr[1], s2 = sr[2], s3 = sr[3];
+        for (int r = 0; r < RANK; ++r) y[t][r] = 0.f;
+#pragma unroll
+      for (int tc = 0; tc < 8; ++tc)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float qv[RQ];
+#pragma unroll
+          for (int r4 = 0; r4 < RQ / 4; ++r4) {
+            const f32x4 q4 = lds4(sm.Q + (32 * g + 4 * tc + e) * RQ + 4 * r4);
+            qv[4 * r4] = q4.x; qv[4 * r4 + 1] = q4.y; qv[4 * r4 + 2] = q4.z; qv[4 * r4 + 3] = q4.w;
+          }
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < RANK; ++r) y[t][r] += acc[t][tc][e] * qv[r];
+        }
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int r = 0; r < RANK; ++r) {
-          const f32x4 qq = lds4(sm.Qa + r * kD + c0 + 4 * i4);
-          acc[r] += s0 * qq.x + s1 * qq.y + s2 * qq.z + s3 * qq.w;
+          y[t][r] += xor_lane(y[t][r], 16);
+          y[t][r] += xor_lane(y[t][r], 32);
         }
-      }
-#pragma unroll
-      for (int r = 0; r < RANK; ++r) sm.part[(qd * kMaxRank + r) * kD + v] = acc[r];
-      lds_barrier();
-      if (tid < kD) {
-        float y[RANK];
-        combine_parts<NQ, RANK>(sm, y);
-#pragma unroll
-        for (int r = 0; r < RANK; ++r) sm.Y[r * kD + tid] = y[r];
-      }
-      lds_barrier();
       if (it == iters) break;   // final Y = S Q: the compensator values
-      // Q = S^T Y from the LDS copy: column c = v over rows [c0, c0 + FC)
+      // S^T Y: this lane's two rows, then the 16 rows of the DPP row, then the waves
 #pragma unroll
-      for (int r = 0; r < RANK; ++r) acc[r] = 0.f;
+      for (int tc = 0; tc < 8; ++tc) {
+        float p[4 * RQ];
 #pragma unroll
-      for (int i4 = 0; i4 < FC / 4; ++i4) {
-        const int vv = c0 + 4 * i4;
-        const float s0 = sm.S[vv * kP + v], s1 = sm.S[(vv + 1) * kP + v];
-        const float s2 = sm.S[(vv + 2) * kP + v], s3 = sm.S[(vv + 3) * kP + v];
+        for (int e = 0; e < 4; ++e) {
 #pragma unroll
-        for (int r = 0; r < RANK; ++r) {
-          const f32x4 yy = lds4(sm.Y + r * kD + vv);
-          acc[r] += s0 * yy.x + s1 * yy.y + s2 * yy.z + s3 * yy.w;
+          for (int r = 0; r < RANK; ++r) p[e * RQ + r] = acc[0][tc][e] * y[0][r] + acc[1][tc][e] * y[1][r];
+#pragma unroll
+          for (int r = RANK; r < RQ; ++r) p[e * RQ + r] = 0.f;
         }
-      }
+        reduce_scatter16<4 * RQ>(p, n);
+        float* dst = sm.u.red + w * kD * RQ + (32 * g + 4 * tc) * RQ + n * (RQ / 4);
 #pragma unroll
-      for (int r = 0; r < RANK; ++r) sm.part[(qd * kMaxRank + r) * kD + v] = acc[r];
-      lds_barrier();
-      // CholeskyQR2 on the rows of Q, carried by threads t < 128 in registers
-      float x[RANK];
-      if (tid < kD) {
-        combine_parts<NQ, RANK>(sm, x);
-        partial_gram<RANK>(x, sm.gram[0][tid >> 6]);
+        for (int k2 = 0; k2 < RQ / 4; ++k2) dst[k2] = p[k2];
       }
       lds_barrier();
-      if (tid < kD) {
-        chol_solve<RANK>(x, sm.gram[0][0], sm.gram[0][1]);
-        partial_gram<RANK>(x, sm.gram[1][tid >> 6]);
-      }
-      lds_barrier();
-      if (tid < kD) {
-        chol_solve<RANK>(x, sm.gram[1][0], sm.gram[1][1]);
+      if (w == 0) {
+        float x[2][RANK];
 #pragma unroll
-        for (int r = 0; r < RANK; ++r) sm.Qa[r * kD + tid] = x[r];
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int r = 0; r < RANK; ++r) {
+            const int o = (lane + 64 * h) * RQ + r;
+            x[h][r] = (sm.u.red[o] + sm.u.red[kD * RQ + o]) + (sm.u.red[2 * kD * RQ + o] + sm.u.red[3 * kD * RQ + o]);
+          }
+        cholqr2_wave<RANK>(x);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int r = 0; r < RANK; ++r) sm.Q[(lane + 64 * h) * RQ + r] = x[h][r];
       }
       lds_barrier();
     }
-    // round to fp16, store, keep the rounded values for the residual
-    if (tid < kD) {
+    // fp16 pieces: stored, and their rounded values kept for the residual
+    float yh[2][RANK];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < RANK; ++r) {
-        const uint16_t hq = f2h(sm.Qa[r * kD + tid]);
-        const uint16_t hy = f2h(sm.Y[r * kD + tid]);
-        ct_k[((size_t)head * rank + r) * kD + tid] = hq;
-        ct_u[((size_t)head * rank + r) * kD + tid] = hy;
-        sm.Qb[r * kD + tid] = h2f(hq);
-        sm.part[r * kD + tid] = h2f(hy);
+        const uint16_t hy = f2h(y[t][r]);
+        yh[t][r] = h2f(hy);
+        if (g == 0) ct_u[((size_t)head * RANK + r) * kD + vrow[t]] = hy;
+      }
+    if (tid < kD) {
+#pragma unroll
+      for (int r = 0; r < RQ; ++r) {
+        float kh = 0.f;
+        if (r < RANK) {
+          const uint16_t hq = f2h(sm.Q[tid * RQ + r]);
+          ct_k[((size_t)head * RANK + r) * kD + tid] = hq;
+          kh = h2f(hq);
+        }
+        sm.Kh[tid * RQ + r] = kh;
       }
     }
     lds_barrier();
     // residual R = S - sum_r uh_r kh_r^T
 #pragma unroll
-    for (int i = 0; i < FC; ++i) S[i] = sm.S[v * kP + c0 + i];
-    float yh[RANK];
+    for (int tc = 0; tc < 8; ++tc)
 #pragma unroll
-    for (int r = 0; r < RANK; ++r) yh[r] = sm.part[r * kD + v];
+      for (int e = 0; e < 4; ++e) {
+        float kv[RQ];
 #pragma unroll
-    for (int r = 0; r < RANK; ++r)
+        for (int r4 = 0; r4 < RQ / 4; ++r4) {
+          const f32x4 k4 = lds4(sm.Kh + (32 * g + 4 * tc + e) * RQ + 4 * r4);
+          kv[4 * r4] = k4.x; kv[4 * r4 + 1] = k4.y; kv[4 * r4 + 2] = k4.z; kv[4 * r4 + 3] = k4.w;
+        }
 #pragma unroll
-      for (int i4 = 0; i4 < FC / 4; ++i4) {
-        const f32x4 kh = lds4(sm.Qb + r * kD + c0 + 4 * i4);
-        S[4 * i4] -= yh[r] * kh.x; S[4 * i4 + 1] -= yh[r] * kh.y;
-        S[4 * i4 + 2] -= yh[r] * kh.z; S[4 * i4 + 3] -= yh[r] * kh.w;
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int r = 0; r < RANK; ++r) acc[t][tc][e] -= yh[t][r] * kv[r];
       }
+  }
+
+  // ---------------------------------------------------------------- smoothing
+  if (smooth_mode != 2) {
 #pragma unroll
-    for (int i = 0; i < FC; ++i) sm.S[v * kP + c0 + i] = S[i];
+    for (int hf = 0; hf < 2; ++hf) {   // channels 32 g + 16 hf + [0, 16)
+      float cs[16];
+#pragma unroll
+      for (int tc = 0; tc < 4; ++tc)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float a0 = acc[0][4 * hf + tc][e], a1 = acc[1][4 * hf + tc][e];
+          cs[4 * tc + e] = smooth_mode == 1 ? a0 * a0 + a1 * a1 : fabsf(a0) + fabsf(a1);
+        }
+      reduce_scatter16<16>(cs, n);   // lane n: channel 32 g + 16 hf + n
+      sm.cred[w * kD + 32 * g + 16 * hf + n] = cs[0];
+    }
+  }
+  lds_barrier();
+  if (tid < kD) {
+    float cf = 1.f;
+    if (smooth_mode != 2) {
+      const float tot = (sm.cred[tid] + sm.cred[kD + tid]) + (sm.cred[2 * kD + tid] + sm.cred[3 * kD + tid]);
+      cf = fmaxf(sqrtf(tot * (1.0f / kD)), 1e-12f);
+    }
+    ksmooth[hk + tid] = cf;
+    sm.col[tid] = 1.0f / cf;
   }
   lds_barrier();
 
-  // ---------------------------------------------------------------- smoothing
-  {
-    float acc = 0.f;
-#pragma unroll
-    for (int i = 0; i < FC; ++i) {
-      const float x = sm.S[(c0 + i) * kP + v];   // column v, rows [c0, c0 + FC)
-      acc += smooth_mode == 1 ? x * x : fabsf(x);
-    }
-    sm.red[qd * kD + v] = acc;
-    lds_barrier();
-    if (tid < kD) {
-      float tot = 0.f;
-#pragma unroll
-      for (int p = 0; p < NQ; ++p) tot += sm.red[p * kD + tid];
-      const float cf = smooth_mode == 2 ? 1.f : fmaxf(sqrtf(tot * (1.0f / kD)), 1e-12f);
-      ksmooth[hk + tid] = cf;
-      sm.col[tid] = 1.0f / cf;
-    }
-    lds_barrier();
-  }
-
   // ---------------------------------------------------------------- scales, codes
-  {
+#pragma unroll
+  for (int tc = 0; tc < 8; ++tc) {
+    const f32x4 cc = lds4(sm.col + 32 * g + 4 * tc);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) acc[t][tc] *= cc;
+  }
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
     float mx = 0.f;
 #pragma unroll
-    for (int i4 = 0; i4 < FC / 4; ++i4) {
-      const f32x4 cc = lds4(sm.col + c0 + 4 * i4);
-      S[4 * i4] *= cc.x; S[4 * i4 + 1] *= cc.y; S[4 * i4 + 2] *= cc.z; S[4 * i4 + 3] *= cc.w;
-    }
+    for (int tc = 0; tc < 8; ++tc)
 #pragma unroll
-    for (int i = 0; i < FC; ++i) mx = fmaxf(mx, fabsf(S[i]));
-    sm.red[qd * kD + v] = mx;
-    lds_barrier();
-    float s = 0.f;
+      for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fabsf(acc[t][tc][e]));
+    mx = fmaxf(mx, xor_lane(mx, 16));
+    mx = fmaxf(mx, xor_lane(mx, 32));
+    if (g == 0) vscale[hk + vrow[t]] = mx;
+    const float sc = mx > 0.f ? 127.0f / mx : 0.f;
+    uint32_t wd[8];
 #pragma unroll
-    for (int p = 0; p < NQ; ++p) s = fmaxf(s, sm.red[p * kD + v]);
-    if (qd == 0) vscale[hk + v] = s;
-    const float sc = s > 0.f ? 127.0f / s : 0.f;
-    uint4* zr = reinterpret_cast<uint4*>(codes + (hk + v) * kD + c0);
-    float* pr = pre_round ? pre_round + (hk + v) * kD + c0 : nullptr;
+    for (int tc = 0; tc < 8; ++tc) {
+      const f32x4 x = acc[t][tc] * sc;
+      if (pre_round) *reinterpret_cast<f32x4*>(pre_round + (hk + vrow[t]) * kD + 32 * g + 4 * tc) = x;
+      uint32_t word = 0;
 #pragma unroll
-    for (int c16 = 0; c16 < FC / 16; ++c16) {
-      uint32_t w[4] = {0, 0, 0, 0};
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float x = S[16 * c16 + e] * sc;
-        if (pr) pr[16 * c16 + e] = x;
-        const float qz = fminf(fmaxf(rintf(x), -127.f), 127.f);
-        w[e >> 2] |= (uint32_t)((int32_t)qz & 0xff) << (8 * (e & 3));
+      for (int e = 0; e < 4; ++e) {
+        const float qz = fminf(fmaxf(rintf(x[e]), -127.f), 127.f);
+        word |= (uint32_t)((int32_t)qz & 0xff) << (8 * e);
       }
-      zr[c16] = make_uint4(w[0], w[1], w[2], w[3]);
+      wd[tc] = word;
     }
+    uint4* zr = reinterpret_cast<uint4*>(codes + (hk + vrow[t]) * kD + 32 * g);
+    zr[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    zr[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
   }
 }
 
@@ -667,7 +734,7 @@ extern "C" int leapq_window_flush(const leapq_state* st, int pos, const float* d
   switch (st->rank) {
 #define GDNRT_FLUSH(R)                                                                            \
   case R:                                                                                         \
-    hipLaunchKernelGGL((leapq_flush_kernel<kFlushNQ, R>), dim3((unsigned)N), dim3(128 * kFlushNQ), \
+    hipLaunchKernelGGL((leapq_flush_kernel<R>), dim3((unsigned)N), dim3(kFlushNT),               \
                        0, s, st->codes, st->vscale, st->ksmooth, st->ct_k, st->ct_u, st->buf_k,   \
                        st->buf_u, st->buf_a, st->window, pos, dense, q0, iters, smooth_mode,      \
                        pre_round);                                                                \

@@ -39,17 +39,40 @@ def buffer(st, pos, heads=None):
     return [(bk[:, j], bu[:, j], ba[:, j]) for j in range(pos)]
 
 
-def compare_flush(st, ref, what):
-    """Compare a GPU flush result with the oracle's; returns the code flips.
+def compare_flush(st, ref, what, S, mode=0):
+    """Compare a GPU flush of the dense state S with the oracle's; returns the code
+    flips.
 
     The compensator fit runs the same procedure in fp32 on the GPU and fp64 in
     the oracle; on states with large outliers its Gram matrix is ill-conditioned
     (kappa ~ 1e5), so a compensator entry may land one fp16 step away and the
     residual, scales and codes follow. Checked: pieces within 2 fp16 steps of
-    each vector's largest entry, smoothing factors 1e-4 and scales 1e-3 of their
-    maximum, every code within one step of the oracle's."""
-    assert_rel(np64(st.ksmooth), ref["c"], 1e-4, f"{what} ksmooth")
+    each vector's largest entry; scales 1e-3 of their maximum; every code within
+    one step of the oracle's; smoothing factors within what the difference of the
+    two sets of pieces does to the residual. With dR bounding |R_gpu - R_ref| per
+    entry (the two sets of subtracted pieces, plus fp32 rounding of the rebuild
+    and the subtraction, 8 ulps of |S| + sum_r |uc_r| |kc_r|), the factor of
+    eq. 7, c = sqrt(mean_v |R|), moves by |a - b| / (sqrt a + sqrt b) <=
+    mean_v dR / (c_gpu + c_ref); the root-mean-square variant by at most
+    sqrt(mean_v dR^2) (triangle inequality)."""
     assert_rel(np64(st.vscale), ref["s"], 1e-3, f"{what} vscale")
+    c_g, c_r = np64(st.ksmooth), ref["c"]
+    mag = np.abs(S)
+    dR = np.zeros_like(mag)
+    if st.rank > 0:
+        ug, kg = np.swapaxes(np64(st.ct_u), -1, -2), np64(st.ct_k)
+        dR = np.abs(ug @ kg - np.swapaxes(ref["ut"], -1, -2) @ ref["kt"])
+        mag = mag + np.abs(ug) @ np.abs(kg)
+    dR = dR + 8 * 2.0 ** -24 * mag
+    if mode == 0:
+        bound = dR.mean(axis=1) / (c_g + c_r)
+    elif mode == 1:
+        bound = np.sqrt((dR ** 2).mean(axis=1))
+    else:
+        bound = np.zeros_like(c_r)
+    err = np.abs(c_g - c_r)
+    worst = float(np.max(err / (1.25 * bound + 1e-6 * c_r)))
+    assert worst <= 1.0, f"{what} ksmooth: {worst:.2f}x the propagated bound"
     if st.rank > 0:
         for key, name in (("kt", "ct_k"), ("ut", "ct_u")):
             g, r = np64(getattr(st, name)), ref[key]
@@ -58,9 +81,21 @@ def compare_flush(st, ref, what):
         kt = np64(st.ct_k)
         gram = kt @ np.swapaxes(kt, -1, -2)
         assert np.abs(gram - np.eye(st.rank)).max() < 5e-3, f"{what}: compensator keys not orthonormal"
+    # codes: each side is within half a step of its own residual, the residuals
+    # differ by at most dR, and the steps s_v c_k / 127 by their own difference,
+    # so |Z_gpu - Z_ref| <= 1 + dR / step + 127 |1 - step_ref / step_gpu|. Where the
+    # pieces agree this is one step; on outlier channels (c_k ~ 1e-3 after the
+    # pieces take the outliers out) a one-step fp16 difference in a piece is
+    # several code steps.
     Z = st.codes.cpu().numpy().astype(np.int32)
     flips = Z != ref["Z"].astype(np.int32)
-    assert np.all(np.abs(Z - ref["Z"])[flips] == 1), f"{what}: a code moved by more than one step"
+    step_g = np64(st.vscale)[:, :, None] * c_g[:, None, :] / 127.0
+    step_r = ref["s"][:, :, None] * c_r[:, None, :] / 127.0
+    with np.errstate(divide="ignore", invalid="ignore"):
+        allow = 1 + 1.25 * (dR / step_g + 127 * np.abs(1 - step_r / step_g))
+    allow = np.where(step_g > 0, allow, 1)
+    assert np.all(np.abs(Z - ref["Z"]) <= allow), f"{what}: a code moved beyond its propagated bound"
+    assert flips.mean() < 1e-2, f"{what}: {flips.mean():.1e} of the codes differ"
     return int(flips.sum())
 
 
@@ -102,7 +137,7 @@ def test_flush_dense_matches_oracle(mode):
     m.leapq_window_flush(st, Q0.to(dev), dense=S0.to(dev), smooth_mode=mode, pre_round=pre)
     torch.cuda.synchronize()
     ref = leapq.flush(np64(S0), np64(Q0), rank=4, iters=1, smooth_mode=mode)
-    flips = compare_flush(st, ref, f"mode {mode}")
+    flips = compare_flush(st, ref, f"mode {mode}", np64(S0), mode)
     # the INT8 decision on the GPU's own pre-rounding values is the oracle's
     assert np.array_equal(leapq.round_codes(pre.cpu().numpy()), st.codes.cpu().numpy())
     # smoothing, scales and pre-rounding values of the residual left by the GPU's
@@ -175,10 +210,11 @@ def test_teacher_forced_windows(io):
         assert_rel(u_gpu, u_ref, TOL_F32, f"window {w} corrections")
         assert_rel(np64(o), o_ref, TOL_F32 if io == torch.float32 else TOL_BF16, f"window {w} outputs")
         # flush from the GPU's own stored state and buffer, oracle on the same
-        ref = leapq.flush(leapq.rebuild(start, buffer(st, W)), np64(inp["Q0"]), rank=4)
+        S_w = leapq.rebuild(start, buffer(st, W))
+        ref = leapq.flush(S_w, np64(inp["Q0"]), rank=4)
         m.leapq_window_flush(st, Q0)
         torch.cuda.synchronize()
-        flips = compare_flush(st, ref, f"window {w} flush")
+        flips = compare_flush(st, ref, f"window {w} flush", S_w)
         say(f"  window {w}: u err {rel_err(u_gpu, u_ref):.2e}, code flips {flips}")
 
 
