@@ -31,193 +31,274 @@ __device__ __forceinline__ float sb(uint32_t w, int b) { return (float)((int32_t
 // The token then gives u = b (v - a S_m k), o = a S_m q + u (k . q), and its record
 // is appended at slot m.
 //
-// The value rows of a head are independent given the per-head dot products, so a
-// head is split over blocks of 128 threads, each taking 32 RPT rows (the blocks of
-// one head on one XCD, so that the vectors they all read come from one L2). Thread
-// (rq = tid / 4, quarter qt = tid % 4) owns 32 codes of each of its RPT rows
-// part * 32 RPT + 32 i + rq, and their buffered and compensator values of slots
-// = qt (mod 4). Each block forms the per-head dot products of q and k with the
-// compensator keys, the buffered keys and k itself (16-lane groups, 8 entries per
-// lane). Every global load that depends on no other is issued before the first
-// barrier; more rows per thread keep more bytes in flight per block.
+// One block of 256 threads (four waves) per head; wave w owns value rows
+// [32 w, 32 w + 32) as two tiles of 16. The products Z x_k and Z x_q run on the
+// int8 matrix cores with the stored codes as they are: each wave writes the two read
+// vectors x = ksmooth o k, ksmooth o q as 22-bit fixed point relative to their
+// largest entry (x ~= X 2^(e-22), |X| < 2^22), split into three signed int8 digits
+// (X = 2^16 d0 + 2^8 d1 + d2, each in [-128, 127]), and v_mfma_i32_16x16x64_i8 forms
+// the exact integer products of the digits with the code rows. The only rounding of
+// the read-out is the fixed-point rounding of x (2^-23 of its largest entry) and the
+// fp32 arithmetic after the integer sums. Everything else a row needs (compensator
+// and buffered terms) comes from per-head dot products formed by 16-lane groups
+// before the block's one barrier.
 
-constexpr int kDecodeRPT = 2;   // value rows per thread of a decode block
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-template <typename IO, int RPT>
-__global__ __launch_bounds__(128) void leapq_decode_kernel(
+// LDS written by some lanes of a wave and read by others of the same wave: the LDS
+// executes a wave's instructions in order, so this only keeps the compiler from
+// reordering the accesses
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
+// largest value over the 16 lanes of a DPP row (every lane receives it)
+__device__ __forceinline__ float max16(float x) {
+  x = fmaxf(x, dpp<0x140>(x));
+  x = fmaxf(x, dpp<0x141>(x));
+  x = fmaxf(x, dpp<0x4E>(x));
+  x = fmaxf(x, dpp<0xB1>(x));
+  return x;
+}
+
+// Fixed-point digits of 8 values sharing the scale of `mx` (the largest magnitude
+// of the vector): X = rint(x 2^(22 - e)), mx = f 2^e with f in [0.5, 1), so
+// |X| < 2^22; balanced base-256 digits d0 (|d0| <= 64), d1, d2 in [-128, 127],
+// packed 8 to a uint2 per digit. Returns e (0 for a zero vector).
+__device__ __forceinline__ int fixed_digits(const float (&x)[8], float mx, uint2 (&d)[3]) {
+  int e = 0;
+  if (mx > 0.f) (void)frexpf(mx, &e);
+  if (e < -100) e = 0, mx = 0.f;   // nothing measurable: a zero vector
+  const float sc = mx > 0.f ? ldexpf(1.0f, 22 - e) : 0.f;
+  uint32_t w[3][2] = {{0, 0}, {0, 0}, {0, 0}};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int X = (int)rintf(x[i] * sc);
+    const int lo = ((X + 128) & 0xff) - 128;
+    const int X1 = (X - lo) >> 8;
+    const int mid = ((X1 + 128) & 0xff) - 128;
+    const int hi = (X1 - mid) >> 8;
+    w[0][i >> 2] |= (uint32_t)(hi & 0xff) << (8 * (i & 3));
+    w[1][i >> 2] |= (uint32_t)(mid & 0xff) << (8 * (i & 3));
+    w[2][i >> 2] |= (uint32_t)(lo & 0xff) << (8 * (i & 3));
+  }
+#pragma unroll
+  for (int t = 0; t < 3; ++t) d[t] = make_uint2(w[t][0], w[t][1]);
+  return e;
+}
+
+template <typename IO>
+__global__ __launch_bounds__(256) void leapq_decode_kernel(
     const int8_t* __restrict__ codes, const float* __restrict__ vscale,
     const float* __restrict__ ksmooth, const uint16_t* __restrict__ ct_k,
     const uint16_t* __restrict__ ct_u, float* __restrict__ buf_k, float* __restrict__ buf_u,
     float* __restrict__ buf_a, int rank, int window, int m,
     const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
-    const float* __restrict__ alpha, const float* __restrict__ beta, IO* __restrict__ o, int N) {
-  constexpr int NT = 128;                                      // threads
-  constexpr int RPB = 32 * RPT;                                // rows per block
-  constexpr int PPH = kD / RPB;                                // blocks per head
-  constexpr int NG = NT / 16;                                  // 16-lane groups
-  constexpr int NP = (kMaxRank + kMaxWindow + NG - 1) / NG;    // dot vectors per group
-  __shared__ f32x4 s_x4[2][kD / 4];            // ksmooth o k, ksmooth o q
-  __shared__ float s_k[kD], s_q[kD];
-  __shared__ float s_dk[kMaxRank + kMaxWindow], s_dq[kMaxRank + kMaxWindow];
-  __shared__ float s_g[kMaxWindow + 1];        // s_g[j] = G_j for j < m, s_g[m] = G0
+    const float* __restrict__ alpha, const float* __restrict__ beta, IO* __restrict__ o) {
+  constexpr int NV = kMaxRank + kMaxWindow;   // dot-product vectors: compensators, records, k
+  __shared__ __attribute__((aligned(16))) uint2 s_dig[4][8][kD / 8];   // per wave: digit rows
+                                                                      // (x_k 0-2, x_q 3-5, 6-7 zero)
+  __shared__ float s_dk[NV], s_dq[NV];
+  __shared__ float s_g[kMaxWindow + 1];       // s_g[j] = G_j for j < m, s_g[m] = G0
 
-  const int tid = threadIdx.x;
-  int head, part;
-  {
-    const int bid = blockIdx.x;
-    if ((N & 7) == 0) {
-      const int xcd = bid & 7, slot = bid >> 3;
-      head = (slot / PPH) * 8 + xcd;
-      part = slot % PPH;
-    } else {
-      head = bid / PPH;
-      part = bid % PPH;
-    }
-  }
-  const int rq = tid >> 2, qt = tid & 3;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
+  const int head = blockIdx.x;
   const size_t hk = (size_t)head * kD;
   float* bk = buf_k + (size_t)head * window * kD;
   float* bu = buf_u + (size_t)head * window * kD;
   const float* ba = buf_a + (size_t)head * window;
-  const int nv = rank + m + 1;   // dot-product vectors: compensators, buffered keys, k
+  const int nv = rank + m;   // vectors before k itself
+  const int row[2] = {32 * w + n, 32 * w + 16 + n};
 
   // ---- independent loads
-  uint4 z[RPT][2];
-  float bur[RPT][kMaxWindow / 4], cur[RPT][kMaxRank / 4], vrow[RPT], vs[RPT];
+  // code rows of this wave's tiles as MFMA B operands: row 32 w + 16 T + n, bytes 64 s + 16 g
+  i32x4 zb[2][2];
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    const int row = part * RPB + 32 * i + rq;
-    const uint4* zp = reinterpret_cast<const uint4*>(codes + (hk + row) * kD + qt * 32);
-    z[i][0] = zp[0];
-    z[i][1] = zp[1];
+  for (int T = 0; T < 2; ++T)
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      zb[T][s] = *reinterpret_cast<const i32x4*>(codes + (hk + row[T]) * kD + 64 * s + 16 * g);
+  // buffered corrections and compensator values of this lane's rows, slots = g (mod 4)
+  float bur[2][kMaxWindow / 4], cur[2][kMaxRank / 4], vrow[2], vsr[2];
+#pragma unroll
+  for (int T = 0; T < 2; ++T) {
 #pragma unroll
     for (int jj = 0; jj < kMaxWindow / 4; ++jj) {
-      const int j = 4 * jj + qt;
-      bur[i][jj] = j < m ? bu[(size_t)j * kD + row] : 0.f;
+      const int j = 4 * jj + g;
+      bur[T][jj] = j < m ? bu[(size_t)j * kD + row[T]] : 0.f;
     }
 #pragma unroll
     for (int rr = 0; rr < kMaxRank / 4; ++rr) {
-      const int r = 4 * rr + qt;
-      cur[i][rr] = r < rank ? h2f(ct_u[((size_t)head * rank + r) * kD + row]) : 0.f;
+      const int r = 4 * rr + g;
+      cur[T][rr] = r < rank ? h2f(ct_u[((size_t)head * rank + r) * kD + row[T]]) : 0.f;
     }
-    vrow[i] = io_traits<IO>::ld(v, hk + row);
-    vs[i] = vscale[hk + row];
+    vrow[T] = io_traits<IO>::ld(v, hk + row[T]);
+    vsr[T] = vscale[hk + row[T]];
   }
-  const float a = alpha[head];
-  const float b = beta[head];
-  const int grp = tid >> 4, l16 = tid & 15, c0 = l16 * 8;
-  float w[NP][8];
+  // this lane's key channels 8 n .. 8 n + 7 of k, q and the smoothing factors
+  float kx[8], qx[8], cx[8];
+  {
+    const int c0 = 8 * n;
+    const f32x4 k0 = io_traits<IO>::ld4(k, hk + c0), k1 = io_traits<IO>::ld4(k, hk + c0 + 4);
+    const f32x4 q0 = io_traits<IO>::ld4(q, hk + c0), q1 = io_traits<IO>::ld4(q, hk + c0 + 4);
+    const f32x4 s0 = *reinterpret_cast<const f32x4*>(ksmooth + hk + c0);
+    const f32x4 s1 = *reinterpret_cast<const f32x4*>(ksmooth + hk + c0 + 4);
 #pragma unroll
-  for (int p = 0; p < NP; ++p) {
-    const int vi = grp + NG * p;
+    for (int e = 0; e < 4; ++e) {
+      kx[e] = k0[e]; kx[4 + e] = k1[e];
+      qx[e] = q0[e]; qx[4 + e] = q1[e];
+      cx[e] = s0[e]; cx[4 + e] = s1[e];
+    }
+  }
+  // dot vectors of 16-lane group 4 w + g: indices 4 w + g and 4 w + g + 16
+  float wv[2][8];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int vi = 4 * w + g + 16 * p;
     if (vi < rank) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(ct_k + ((size_t)head * rank + vi) * kD + c0);
+      const uint4 raw = *reinterpret_cast<const uint4*>(ct_k + ((size_t)head * rank + vi) * kD + 8 * n);
       const uint32_t r4[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        w[p][2 * e] = h2f(uint16_t(r4[e] & 0xffffu));
-        w[p][2 * e + 1] = h2f(uint16_t(r4[e] >> 16));
+        wv[p][2 * e] = h2f(uint16_t(r4[e] & 0xffffu));
+        wv[p][2 * e + 1] = h2f(uint16_t(r4[e] >> 16));
       }
-    } else if (vi < rank + m) {
-      const f32x4* pp = reinterpret_cast<const f32x4*>(bk + (size_t)(vi - rank) * kD + c0);
+    } else if (vi < nv) {
+      const f32x4* pp = reinterpret_cast<const f32x4*>(bk + (size_t)(vi - rank) * kD + 8 * n);
       const f32x4 x0 = pp[0], x1 = pp[1];
-      w[p][0] = x0.x; w[p][1] = x0.y; w[p][2] = x0.z; w[p][3] = x0.w;
-      w[p][4] = x1.x; w[p][5] = x1.y; w[p][6] = x1.z; w[p][7] = x1.w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        wv[p][e] = x0[e];
+        wv[p][4 + e] = x1[e];
+      }
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) w[p][e] = 0.f;
+      for (int e = 0; e < 8; ++e) wv[p][e] = kx[e];   // k itself (vi == nv) or unused
     }
   }
-  {   // one thread per key channel
-    const float kv = io_traits<IO>::ld(k, hk + tid);
-    const float qv = io_traits<IO>::ld(q, hk + tid);
-    const float c = ksmooth[hk + tid];
-    s_k[tid] = kv;
-    s_q[tid] = qv;
-    reinterpret_cast<float*>(s_x4[0])[tid] = c * kv;
-    reinterpret_cast<float*>(s_x4[1])[tid] = c * qv;
-    if (part == 0) bk[(size_t)m * kD + tid] = kv;   // append this token's key
-  }
+  const float a = alpha[head];
+  const float b = beta[head];
+
+  // ---- decays, appends
   if (tid == 0) {
-    float g = 1.f;
-    for (int j = m - 1; j >= 0; --j) {      // suffix products of the buffered decays
-      s_g[j] = g;
-      g *= ba[j];
+    float gg = 1.f;
+    for (int j = m - 1; j >= 0; --j) {   // suffix products of the buffered decays
+      s_g[j] = gg;
+      gg *= ba[j];
     }
-    s_g[m] = g;
-    if (part == 0) buf_a[(size_t)head * window + m] = a;
+    s_g[m] = gg;
+    buf_a[(size_t)head * window + m] = a;
   }
-  lds_barrier();
+  if (w == 0 && g == 0) {   // this token's key as record m
+    f32x4* dst = reinterpret_cast<f32x4*>(bk + (size_t)m * kD + 8 * n);
+    dst[0] = f32x4{kx[0], kx[1], kx[2], kx[3]};
+    dst[1] = f32x4{kx[4], kx[5], kx[6], kx[7]};
+  }
 
   // ---- per-head dot products
 #pragma unroll
-  for (int p = 0; p < NP; ++p) {
-    const int vi = grp + NG * p;
-    if (vi < nv) {
+  for (int p = 0; p < 2; ++p) {
+    const int vi = 4 * w + g + 16 * p;
+    if (vi <= nv) {
       float pk = 0.f, pq = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float we = vi == rank + m ? s_k[c0 + e] : w[p][e];
-        pk += we * s_k[c0 + e];
-        pq += we * s_q[c0 + e];
+        pk += wv[p][e] * kx[e];
+        pq += wv[p][e] * qx[e];
       }
       pk = sum16(pk);
       pq = sum16(pq);
-      if (l16 == 0) {
+      if (n == 0) {
         s_dk[vi] = pk;
         s_dq[vi] = pq;
       }
     }
   }
-  lds_barrier();
 
-  // ---- the rows: each quarter's share, then the four quarters summed
-  const float g0 = s_g[m];
-  const float kq = s_dq[rank + m];
-#pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    const uint32_t zz[8] = {z[i][0].x, z[i][0].y, z[i][0].z, z[i][0].w,
-                            z[i][1].x, z[i][1].y, z[i][1].z, z[i][1].w};
-    float yk = 0.f, yq = 0.f;
+  // ---- read vectors as fixed-point digits (every row of 16 lanes holds all 128
+  // channels; row 0 of the wave writes the wave's copy)
+  int ek, eq;
+  {
+    float xk[8], xq[8], mk = 0.f, mq = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const f32x4 xk = s_x4[0][qt * 8 + e];
-      const f32x4 xq = s_x4[1][qt * 8 + e];
-      const float z_0 = sb(zz[e], 0), z_1 = sb(zz[e], 1), z_2 = sb(zz[e], 2), z_3 = sb(zz[e], 3);
-      yk += z_0 * xk.x + z_1 * xk.y + z_2 * xk.z + z_3 * xk.w;
-      yq += z_0 * xq.x + z_1 * xq.y + z_2 * xq.z + z_3 * xq.w;
+      xk[e] = cx[e] * kx[e];
+      xq[e] = cx[e] * qx[e];
+      mk = fmaxf(mk, fabsf(xk[e]));
+      mq = fmaxf(mq, fabsf(xq[e]));
     }
+    mk = max16(mk);
+    mq = max16(mq);
+    uint2 dk3[3], dq3[3];
+    ek = fixed_digits(xk, mk, dk3);
+    eq = fixed_digits(xq, mq, dq3);
+    if (g == 0) {
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        s_dig[w][t][n] = dk3[t];
+        s_dig[w][3 + t][n] = dq3[t];
+      }
+      s_dig[w][6][n] = make_uint2(0, 0);
+      s_dig[w][7][n] = make_uint2(0, 0);
+    }
+  }
+  wave_lds_sync();
+
+  // ---- Z x on the int8 matrix cores: A = digit rows (M), B = code rows (N)
+  i32x4 acc[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    i32x4 ad = {0, 0, 0, 0};
+    if (n < 8) ad = *reinterpret_cast<const i32x4*>(&s_dig[w][n][8 * s + 2 * g]);
+#pragma unroll
+    for (int T = 0; T < 2; ++T) acc[T] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ad, zb[T][s], acc[T], 0, 0, 0);
+  }
+  // lane (n, 0) holds digits 0-3 of row 16 T + n, lane (n, 1) digits 4-7
+  float yk[2], yq[2];
+#pragma unroll
+  for (int T = 0; T < 2; ++T) {
+    const int t4 = __shfl_xor(acc[T][0], 16), t5 = __shfl_xor(acc[T][1], 16);
+    yk[T] = ldexpf(((float)acc[T][0] * 65536.0f + (float)acc[T][1] * 256.0f) + (float)acc[T][2], ek - 22);
+    yq[T] = ldexpf(((float)acc[T][3] * 65536.0f + (float)t4 * 256.0f) + (float)t5, eq - 22);
+  }
+  lds_barrier();
+
+  // ---- rows: compensator and buffered terms (slots = g mod 4), summed over the
+  // four lanes of a row, then lane (n, 0) finishes rows 32 w + 16 T + n
+  const float g0 = s_g[m];
+  const float kq = s_dq[nv];
+#pragma unroll
+  for (int T = 0; T < 2; ++T) {
     float ck = 0.f, cq = 0.f, tk = 0.f, tq = 0.f;
 #pragma unroll
     for (int rr = 0; rr < kMaxRank / 4; ++rr) {
-      const int r = 4 * rr + qt;
+      const int r = 4 * rr + g;
       if (r < rank) {
-        ck += cur[i][rr] * s_dk[r];
-        cq += cur[i][rr] * s_dq[r];
+        ck += cur[T][rr] * s_dk[r];
+        cq += cur[T][rr] * s_dq[r];
       }
     }
 #pragma unroll
     for (int jj = 0; jj < kMaxWindow / 4; ++jj) {
-      const int j = 4 * jj + qt;
+      const int j = 4 * jj + g;
       if (j < m) {
-        const float wj = s_g[j] * bur[i][jj];
+        const float wj = s_g[j] * bur[T][jj];
         tk += wj * s_dk[rank + j];
         tq += wj * s_dq[rank + j];
       }
     }
-    const float sv = vs[i] * (1.0f / 127.0f);
-    float Sk = g0 * (sv * yk + ck) + tk;   // this quarter's share; linear in the parts
-    float Sq = g0 * (sv * yq + cq) + tq;
-    Sk += dpp<0xB1>(Sk);                   // quarters 0+1, 2+3
-    Sq += dpp<0xB1>(Sq);
-    Sk += dpp<0x4E>(Sk);                   // all four
-    Sq += dpp<0x4E>(Sq);
-    const float u = b * (vrow[i] - a * Sk);
-    const float oi = a * Sq + u * kq;
-    if (qt == 0) {
-      const int row = part * RPB + 32 * i + rq;
-      bu[(size_t)m * kD + row] = u;
-      io_traits<IO>::st(o, hk + row, oi);
+    ck += __shfl_xor(ck, 16); cq += __shfl_xor(cq, 16); tk += __shfl_xor(tk, 16); tq += __shfl_xor(tq, 16);
+    ck += __shfl_xor(ck, 32); cq += __shfl_xor(cq, 32); tk += __shfl_xor(tk, 32); tq += __shfl_xor(tq, 32);
+    if (g == 0) {
+      const float sv = vsr[T] * (1.0f / 127.0f);
+      const float Sk = g0 * (sv * yk[T] + ck) + tk;
+      const float Sq = g0 * (sv * yq[T] + cq) + tq;
+      const float u = b * (vrow[T] - a * Sk);
+      const float oi = a * Sq + u * kq;
+      bu[(size_t)m * kD + row[T]] = u;
+      io_traits<IO>::st(o, hk + row[T], oi);
     }
   }
 }
@@ -666,9 +747,9 @@ static int check_state(const leapq_state* st, const char* fn) {
       (st->rank > 0 && (!st->ct_k || !st->ct_u)))
     return set_error(GDNRT_EINVAL, "%s: null buffer in leapq_state", fn);
   if (!aligned16(st->codes) || !aligned16(st->buf_k) || !aligned16(st->buf_u) ||
-      !aligned4(st->vscale) || !aligned4(st->ksmooth) || !aligned4(st->buf_a) ||
+      !aligned4(st->vscale) || !aligned16(st->ksmooth) || !aligned4(st->buf_a) ||
       (st->rank > 0 && (!aligned16(st->ct_k) || !aligned16(st->ct_u))))
-    return set_error(GDNRT_EALIGN, "%s: codes, buf_k, buf_u, ct_k, ct_u must be 16-byte aligned", fn);
+    return set_error(GDNRT_EALIGN, "%s: codes, ksmooth, buf_k, buf_u, ct_k, ct_u must be 16-byte aligned", fn);
   return GDNRT_OK;
 }
 
@@ -687,8 +768,8 @@ extern "C" int leapq_decode_step(const leapq_state* st, int pos, const void* q, 
   if (st->N == 0) return clear_error();
   if (!q || !k || !v || !alpha || !beta || !o)
     return set_error(GDNRT_EINVAL, "leapq_decode_step: null pointer argument");
-  if (!aligned4(q) || !aligned4(k) || !aligned4(v) || !aligned4(o) || !aligned4(alpha) || !aligned4(beta))
-    return set_error(GDNRT_EALIGN, "leapq_decode_step: q, k, v, o, alpha, beta must be 4-byte aligned");
+  if (!aligned16(q) || !aligned16(k) || !aligned4(v) || !aligned4(o) || !aligned4(alpha) || !aligned4(beta))
+    return set_error(GDNRT_EALIGN, "leapq_decode_step: q, k must be 16-byte aligned, v, o, alpha, beta 4-byte");
   const size_t es = io == GDNRT_F32 ? 4 : 2;
   const size_t N = st->N, nIO = N * kD * es, nB = N * st->window * kD * 4;
   if (overlaps(o, nIO, q, nIO) || overlaps(o, nIO, k, nIO) || overlaps(o, nIO, v, nIO) ||
@@ -696,19 +777,18 @@ extern "C" int leapq_decode_step(const leapq_state* st, int pos, const void* q, 
       overlaps(o, nIO, st->codes, N * kD * kD))
     return set_error(GDNRT_EINVAL, "leapq_decode_step: o overlaps another buffer");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  constexpr int RPT = kDecodeRPT;
-  const dim3 grid((unsigned)(N * (kD / (32 * RPT)))), block(128);
+  const dim3 grid((unsigned)N), block(256);
   if (io == GDNRT_F32)
-    hipLaunchKernelGGL((leapq_decode_kernel<float, RPT>), grid, block, 0, s, st->codes, st->vscale,
+    hipLaunchKernelGGL((leapq_decode_kernel<float>), grid, block, 0, s, st->codes, st->vscale,
                        st->ksmooth, st->ct_k, st->ct_u, st->buf_k, st->buf_u, st->buf_a, st->rank,
                        st->window, pos, static_cast<const float*>(q), static_cast<const float*>(k),
-                       static_cast<const float*>(v), alpha, beta, static_cast<float*>(o), (int)N);
+                       static_cast<const float*>(v), alpha, beta, static_cast<float*>(o));
   else
-    hipLaunchKernelGGL((leapq_decode_kernel<uint16_t, RPT>), grid, block, 0, s, st->codes, st->vscale,
+    hipLaunchKernelGGL((leapq_decode_kernel<uint16_t>), grid, block, 0, s, st->codes, st->vscale,
                        st->ksmooth, st->ct_k, st->ct_u, st->buf_k, st->buf_u, st->buf_a, st->rank,
                        st->window, pos, static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), alpha,
-                       beta, static_cast<uint16_t*>(o), (int)N);
+                       beta, static_cast<uint16_t*>(o));
   return check_launch("leapq_decode_step");
 }
 

@@ -159,6 +159,9 @@ GDNRT_API size_t gdn_chunk_fwd_workspace_bytes(int N, int T, int dk, int dv, int
  *   buf_k   [N][window][dk] fp32, buf_u [N][window][dv] fp32, buf_a [N][window] fp32:
  *                              the open window's records (k_t, u_t, alpha_t)
  *
+ * Alignment: codes, ksmooth, ct_k, ct_u, buf_k, buf_u 16 bytes; vscale, buf_a 4
+ * bytes (GDNRT_EALIGN otherwise).
+ *
  * The stored state is S_hat[v,k] = vscale[v] * codes[v,k] / 127 * ksmooth[k]
  *                                   + sum_r ct_u[r][v] ct_k[r][k].
  * The compensator tokens enter the window ahead of the real tokens with decay 1,
@@ -184,7 +187,8 @@ typedef struct {
  *     u_t = beta_t (v_t - alpha_t S_pos k_t),   o_t = alpha_t S_pos q_t + u_t (k_t . q_t),
  *
  * then appends (k_t, u_t, alpha_t) at buffer slot pos. Writes no state.
- *   q, k [N][dk], v, o [N][dv] io dtype; alpha, beta [N] fp32.
+ *   q, k [N][dk], v, o [N][dv] io dtype; alpha, beta [N] fp32. q and k are read 16
+ *   bytes at a time and must be 16-byte aligned; v, o, alpha, beta 4-byte aligned.
  * pos outside [0, window) returns GDNRT_ESTATE.
  */
 GDNRT_API int leapq_decode_step(const leapq_state* st, int pos,
