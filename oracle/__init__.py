@@ -25,4 +25,4 @@ write ``d_k x d_v``; their formulas are used transposed.
 Parity status of each function is stated in its docstring; the only function
 without a pin is ``leapq.toy_error_trend`` (a trend, "parity unpinned").
 """
-from . import gdn, gla, leapq  # noqa: F401
+from . import gdn, gla, kda, kda_leapq, leapq  # noqa: F401
