@@ -1,6 +1,6 @@
 """Benchmark of the gated delta-rule hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--rows decode,kda,leapq,gla,gdn]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--rows decode,kda,leapq,kda_leapq,gla,gdn]
 
 Headline (`value`): Gated DeltaNet decode of one layer, 512 streams x 32 heads,
 d_k = d_v = 128, fp32 state resident in HBM, bf16 q/k/v; one step = one token for
@@ -148,54 +148,64 @@ def cpu_baseline_decode(inp, target_s=15.0):
 
 # ------------------------------------------------------------------- LeapQuant
 
-def leapq_bytes_per_head_window(W=16, rank=4):
+def leapq_bytes_per_head_window(W=16, rank=4, kda=False):
     """Algorithmic bytes of one head over one window (W decode steps + flush).
     Step at position m reads codes 16,384 + scales 1,024 + compensators 4*r*128
     + m buffered records (k, u fp32 and a) + q, k, v (bf16) and alpha, beta; it
     writes one record and o (bf16). The flush reads the stored state and the W
-    records and writes the stored state."""
+    records and writes the stored state. With ``kda`` every decay is a 128-long
+    fp32 vector (the token's alpha and each record's)."""
     stored = D * D + 2 * D * 4 + rank * 2 * D * 2          # 19,456 at r = 4
-    rec = 2 * D * 4 + 4                                   # 1,028
-    io_in, io_out = 3 * D * 2 + 2 * 4, D * 2
+    a_b = D * 4 if kda else 4
+    rec = 2 * D * 4 + a_b                                 # 1,028 (KDA 1,536)
+    io_in, io_out = 3 * D * 2 + a_b + 4, D * 2
     steps = sum(stored + m * rec + io_in + rec + io_out for m in range(W))
     flush = stored + W * rec + stored
     return steps + flush
 
 
-def bench_leapq(tokens=4096, B=DECODE_B, H=DECODE_H, W=16, rank=4):
+def bench_leapq(tokens=4096, B=DECODE_B, H=DECODE_H, W=16, rank=4, kda=False):
+    """The windowed INT8 state over ``tokens`` decode steps (every window: W decode
+    launches and one flush). With ``kda``: one decay per key channel (inputs are
+    drawn for 256 steps and reused cyclically)."""
     N = B * H
-    log(f"[leapq] generating B={B} H={H} steps={tokens}")
-    inp = synth.leapq_decode(B=B, H=H, steps=tokens, device="cuda")
-    st = m.LeapqBuffers(N, rank=rank, window=W)
+    tag = "kda_leapq" if kda else "leapq"
+    gen = min(tokens, 256) if kda else tokens
+    log(f"[{tag}] generating B={B} H={H} steps={gen}")
+    inp = (synth.kda_leapq_decode if kda else synth.leapq_decode)(B=B, H=H, steps=gen, device="cuda")
+    st = m.LeapqBuffers(N, rank=rank, window=W, kda=kda)
     Q0 = inp["Q0"].cuda()
     q, k, v, a, b = (inp[n] for n in ("q", "k", "v", "alpha", "beta"))
     o = torch.empty((N, D), dtype=torch.bfloat16, device="cuda")
+    step = m.kda_leapq_decode_step if kda else m.leapq_decode_step
+    flush = m.kda_leapq_window_flush if kda else m.leapq_window_flush
 
     def run_window(w):
         for j in range(W):
-            t = (w * W + j) % tokens
-            m.leapq_decode_step(st, q[t], k[t], v[t], a[t], b[t], o)
-        m.leapq_window_flush(st, Q0)
+            t = (w * W + j) % gen
+            step(st, q[t], k[t], v[t], a[t], b[t], o)
+        flush(st, Q0)
 
-    m.leapq_window_flush(st, Q0, dense=inp["S0"])      # encode the initial state
+    flush(st, Q0, dense=inp["S0"])      # encode the initial state
     n_win = tokens // W
     ms_win, wall = timed(run_window, n_win, 1)
     ms_step = ms_win / W
-    bpw = leapq_bytes_per_head_window(W, rank) * N
+    bpw = leapq_bytes_per_head_window(W, rank, kda) * N
     # per-kernel split from events around each launch of one window
     s = torch.cuda.current_stream()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(W + 2)]
     ev[0].record(s)
     for j in range(W):
-        m.leapq_decode_step(st, q[j], k[j], v[j], a[j], b[j], o)
+        step(st, q[j], k[j], v[j], a[j], b[j], o)
         ev[j + 1].record(s)
-    m.leapq_window_flush(st, Q0)
+    flush(st, Q0)
     ev[W + 1].record(s)
     torch.cuda.synchronize()
     dec_ms = ev[0].elapsed_time(ev[W]) / W
     flush_ms = ev[W].elapsed_time(ev[W + 1])
-    res = dict(workload=f"leapq_decode B={B} H={H} d=128, INT8 residual + fp32 scales + {rank} fp16 "
-                        f"compensators, {W}-token fp32 buffer, {tokens} tokens",
+    res = dict(workload=f"{tag}_decode B={B} H={H} d=128, INT8 residual + fp32 scales + {rank} fp16 "
+                        f"compensators, {W}-token fp32 buffer"
+                        f"{' with per-channel fp32 decays' if kda else ''}, {tokens} tokens",
                ms_per_step=ms_step, tokens_per_s=B / (ms_step * 1e-3),
                bytes_per_head_step=bpw / N / W, achieved_gbs=bpw / (ms_win * 1e-3) / 1e9,
                decode_kernel_ms=dec_ms, flush_kernel_ms=flush_ms, wall_s=wall,
@@ -337,7 +347,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--rows", default="decode,kda,leapq,gla,gdn")
+    ap.add_argument("--rows", default="decode,kda,leapq,kda_leapq,gla,gdn")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the measured HBM-copy and bf16-GEMM ceilings")
@@ -403,6 +413,15 @@ def main():
         r["speedup_vs_fp32_decode"] = res["ms_per_step"] / r["ms_per_step"] if res else None
         out_rows["leapq"] = r
         log(f"[leapq] {r['ms_per_step']*1e3:.1f} us/step ({r['decode_kernel_ms']*1e3:.1f} us decode "
+            f"+ {r['flush_kernel_ms']*1e3:.1f} us flush per window)  {r['achieved_gbs']:.0f} GB/s  "
+            f"{r['tokens_per_s']/1e6:.3f} M tok/s")
+        torch.cuda.empty_cache()
+    if "kda_leapq" in rows:
+        r = bench_leapq(tokens=256, kda=True)
+        kda_row = out_rows.get("kda")
+        r["speedup_vs_fp32_kda_decode"] = kda_row["ms_per_step"] / r["ms_per_step"] if kda_row else None
+        out_rows["kda_leapq"] = r
+        log(f"[kda_leapq] {r['ms_per_step']*1e3:.1f} us/step ({r['decode_kernel_ms']*1e3:.1f} us decode "
             f"+ {r['flush_kernel_ms']*1e3:.1f} us flush per window)  {r['achieved_gbs']:.0f} GB/s  "
             f"{r['tokens_per_s']/1e6:.3f} M tok/s")
         torch.cuda.empty_cache()

@@ -2,7 +2,8 @@
 
 Entry points over the gdnrt HIP library (C ABI in include/gdnrt.h):
 ``gdn_decode_step``, ``gla_chunk_fwd``, ``gdn_chunk_fwd``, ``leapq_decode_step``,
-``leapq_window_flush`` and ``kda_decode_step``. ``synth`` draws the seeded synthetic workloads.
+``leapq_window_flush``, ``kda_decode_step``, ``kda_leapq_decode_step`` and
+``kda_leapq_window_flush``. ``synth`` draws the seeded synthetic workloads.
 """
 from .binding import (  # noqa: F401
     GdnrtError,
@@ -13,6 +14,8 @@ from .binding import (  # noqa: F401
     gla_chunk_fwd,
     gla_chunk_workspace,
     kda_decode_step,
+    kda_leapq_decode_step,
+    kda_leapq_window_flush,
     leapq_decode_step,
     leapq_window_flush,
     lib,

@@ -42,6 +42,9 @@ SIGNATURES = {
     "leapq_decode_step": ([ctypes.POINTER(LeapqState), _c_int] + [_vp] * 6 + [_c_int, _vp], _c_int),
     "leapq_window_flush": ([ctypes.POINTER(LeapqState), _c_int, _vp, _vp, _c_int, _c_int, _vp, _vp],
                            _c_int),
+    "kda_leapq_decode_step": ([ctypes.POINTER(LeapqState), _c_int] + [_vp] * 6 + [_c_int, _vp], _c_int),
+    "kda_leapq_window_flush": ([ctypes.POINTER(LeapqState), _c_int, _vp, _vp, _c_int, _c_int, _vp, _vp],
+                               _c_int),
     "gdnrt_last_error": ([], ctypes.c_char_p),
 }
 
@@ -223,8 +226,8 @@ class LeapqBuffers:
     """Caller-owned device memory of a LeapQuant state for N heads (see
     ``leapq_state`` in include/gdnrt.h). Allocated once by torch."""
 
-    def __init__(self, N, rank=4, window=16, device="cuda"):
-        self.N, self.rank, self.window = N, rank, window
+    def __init__(self, N, rank=4, window=16, device="cuda", kda=False):
+        self.N, self.rank, self.window, self.kda = N, rank, window, kda
         f = dict(dtype=torch.float32, device=device)
         self.codes = torch.zeros((N, D, D), dtype=torch.int8, device=device)
         self.vscale = torch.zeros((N, D), **f)
@@ -234,7 +237,8 @@ class LeapqBuffers:
         self.ct_u = torch.zeros((N, max(rank, 1), D), dtype=torch.float16, device=device)
         self.buf_k = torch.zeros((N, window, D), **f)
         self.buf_u = torch.zeros((N, window, D), **f)
-        self.buf_a = torch.zeros((N, window), **f)
+        # Gated DeltaNet: one decay per buffered token; KDA: one per key channel
+        self.buf_a = torch.zeros((N, window, D) if kda else (N, window), **f)
         self.pos = 0
         self._st = LeapqState(
             _ptr(self.codes), _ptr(self.vscale), _ptr(self.ksmooth), _ptr(self.ct_k),
@@ -246,33 +250,61 @@ class LeapqBuffers:
         return self._st
 
 
-def leapq_window_flush(st: LeapqBuffers, q0, dense=None, iters=1, smooth_mode=0, pre_round=None):
-    """Rebuild (or take ``dense``), fit compensator tokens, smooth, round once.
-    Resets the window position to 0."""
+def _flush(name, st, q0, dense, iters, smooth_mode, pre_round):
     _need(q0, "q0", torch.float32, (D, st.rank) if st.rank > 0 else None)
     if dense is not None:
         _need(dense, "dense", torch.float32, (st.N, D, D))
     if pre_round is not None:
         _need(pre_round, "pre_round", torch.float32, (st.N, D, D))
-    _check("leapq_window_flush", lib().leapq_window_flush(
+    _check(name, getattr(lib(), name)(
         ctypes.byref(st.struct), st.pos, _ptr(dense), _ptr(q0), iters, smooth_mode,
         _ptr(pre_round), _stream()))
     st.pos = 0
 
 
-def leapq_decode_step(st: LeapqBuffers, q, k, v, alpha, beta, o=None):
-    """One token per head inside the open window; appends its record."""
+def _decode(name, st, q, k, v, alpha, beta, o, alpha_shape):
     N = st.N
     io = _io(q.dtype)
     for n_, t_ in (("q", q), ("k", k), ("v", v)):
         _need(t_, n_, q.dtype, (N, D))
-    _need(alpha, "alpha", torch.float32, (N,))
+    _need(alpha, "alpha", torch.float32, alpha_shape)
     _need(beta, "beta", torch.float32, (N,))
     if o is None:
         o = torch.empty((N, D), dtype=q.dtype, device=q.device)
     _need(o, "o", q.dtype, (N, D))
-    _check("leapq_decode_step", lib().leapq_decode_step(
+    _check(name, getattr(lib(), name)(
         ctypes.byref(st.struct), st.pos, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
         _ptr(o), io, _stream()))
     st.pos += 1
     return o
+
+
+def leapq_window_flush(st: LeapqBuffers, q0, dense=None, iters=1, smooth_mode=0, pre_round=None):
+    """Rebuild (or take ``dense``), fit compensator tokens, smooth, round once.
+    Resets the window position to 0."""
+    if st.kda:
+        raise ValueError("leapq_window_flush: the buffers hold per-channel decays (use kda_leapq_window_flush)")
+    _flush("leapq_window_flush", st, q0, dense, iters, smooth_mode, pre_round)
+
+
+def leapq_decode_step(st: LeapqBuffers, q, k, v, alpha, beta, o=None):
+    """One token per head inside the open window; appends its record."""
+    if st.kda:
+        raise ValueError("leapq_decode_step: the buffers hold per-channel decays (use kda_leapq_decode_step)")
+    return _decode("leapq_decode_step", st, q, k, v, alpha, beta, o, (st.N,))
+
+
+def kda_leapq_window_flush(st: LeapqBuffers, q0, dense=None, iters=1, smooth_mode=0, pre_round=None):
+    """KDA windowed state: rebuild with per-channel decays (or take ``dense``),
+    fit compensator tokens, smooth, round once. Resets the window position to 0."""
+    if not st.kda:
+        raise ValueError("kda_leapq_window_flush: allocate the buffers with kda=True")
+    _flush("kda_leapq_window_flush", st, q0, dense, iters, smooth_mode, pre_round)
+
+
+def kda_leapq_decode_step(st: LeapqBuffers, q, k, v, alpha, beta, o=None):
+    """KDA windowed state: one token per head (alpha [N][128], one decay per key
+    channel) inside the open window; appends its record."""
+    if not st.kda:
+        raise ValueError("kda_leapq_decode_step: allocate the buffers with kda=True")
+    return _decode("kda_leapq_decode_step", st, q, k, v, alpha, beta, o, (st.N, D))

@@ -22,6 +22,26 @@ __device__ __forceinline__ uint16_t f2h(float x) { return __builtin_bit_cast(uin
 // sign-extend byte b of w to float
 __device__ __forceinline__ float sb(uint32_t w, int b) { return (float)((int32_t)(w << (24 - 8 * b)) >> 24); }
 
+// Suffix products of the m buffered decays a_0 .. a_{m-1} of one channel (stride
+// floats apart): put(j, prod_{j<i<m} a_i) for j < m, then put(m, prod_{i<m} a_i),
+// multiplied newest first. Every decay is requested before the first product, so
+// the loads overlap instead of each waiting for the one before.
+template <typename Put>
+__device__ __forceinline__ void suffix_products(const float* __restrict__ a, size_t stride, int m, Put&& put) {
+  float av[kMaxWindow];
+#pragma unroll
+  for (int j = 0; j < kMaxWindow; ++j) av[j] = j < m ? a[(size_t)j * stride] : 1.f;
+  float gg = 1.f;
+#pragma unroll
+  for (int j = kMaxWindow - 1; j >= 0; --j) {
+    if (j < m) {
+      put(j, gg);
+      gg *= av[j];
+    }
+  }
+  put(m, gg);
+}
+
 // ============================================================== decode step
 //
 // Per head, with m = pos buffered records (k_j, u_j, a_j) and compensator pairs
@@ -89,7 +109,7 @@ __device__ __forceinline__ int fixed_digits(const float (&x)[8], float mx, uint2
   return e;
 }
 
-template <typename IO>
+template <typename IO, bool KDA>
 __global__ __launch_bounds__(256) void leapq_decode_kernel(
     const int8_t* __restrict__ codes, const float* __restrict__ vscale,
     const float* __restrict__ ksmooth, const uint16_t* __restrict__ ct_k,
@@ -102,6 +122,8 @@ __global__ __launch_bounds__(256) void leapq_decode_kernel(
                                                                       // (x_k 0-2, x_q 3-5, 6-7 zero)
   __shared__ float s_dk[NV], s_dq[NV];
   __shared__ float s_g[kMaxWindow + 1];       // s_g[j] = G_j for j < m, s_g[m] = G0
+  // KDA: the same products per key channel, s_gv[j][c] = prod_{j<i<m} a_i[c], s_gv[m] = G0
+  __shared__ float s_gv[KDA ? kMaxWindow + 1 : 1][KDA ? kD : 1];
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
   const int head = blockIdx.x;
@@ -178,23 +200,53 @@ __global__ __launch_bounds__(256) void leapq_decode_kernel(
       for (int e = 0; e < 8; ++e) wv[p][e] = kx[e];   // k itself (vi == nv) or unused
     }
   }
-  const float a = alpha[head];
   const float b = beta[head];
+  // GDN: one decay per head; KDA: this lane's channels of the per-channel decay
+  float a = 0.f, ax[8];
+  if constexpr (KDA) {
+    const f32x4 a0 = *reinterpret_cast<const f32x4*>(alpha + hk + 8 * n);
+    const f32x4 a1 = *reinterpret_cast<const f32x4*>(alpha + hk + 8 * n + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ax[e] = a0[e];
+      ax[4 + e] = a1[e];
+    }
+  } else {
+    a = alpha[head];
+  }
 
   // ---- decays, appends
-  if (tid == 0) {
-    float gg = 1.f;
-    for (int j = m - 1; j >= 0; --j) {   // suffix products of the buffered decays
-      s_g[j] = gg;
-      gg *= ba[j];
+  if constexpr (KDA) {
+    if (tid < kD)   // suffix products of channel tid's buffered decays
+      suffix_products(buf_a + (size_t)head * window * kD + tid, kD, m,
+                      [&](int j, float x) { s_gv[j][tid] = x; });
+    if (w == 0 && g == 0) {   // this token's decays as record m
+      f32x4* dst = reinterpret_cast<f32x4*>(buf_a + ((size_t)head * window + m) * kD + 8 * n);
+      dst[0] = f32x4{ax[0], ax[1], ax[2], ax[3]};
+      dst[1] = f32x4{ax[4], ax[5], ax[6], ax[7]};
     }
-    s_g[m] = gg;
-    buf_a[(size_t)head * window + m] = a;
+    lds_barrier();
+  } else {
+    if (tid == 0) {   // suffix products of the buffered decays
+      suffix_products(ba, 1, m, [&](int j, float x) { s_g[j] = x; });
+      buf_a[(size_t)head * window + m] = a;
+    }
   }
   if (w == 0 && g == 0) {   // this token's key as record m
     f32x4* dst = reinterpret_cast<f32x4*>(bk + (size_t)m * kD + 8 * n);
     dst[0] = f32x4{kx[0], kx[1], kx[2], kx[3]};
     dst[1] = f32x4{kx[4], kx[5], kx[6], kx[7]};
+  }
+  // KDA: the vectors the state is applied to are yk = a o k, yq = a o q; the
+  // compensators and the stored residual see them decayed by G0, record j by G_j
+  float g0x[8], yk8[8], yq8[8];
+  if constexpr (KDA) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      g0x[e] = s_gv[m][8 * n + e];
+      yk8[e] = ax[e] * kx[e];
+      yq8[e] = ax[e] * qx[e];
+    }
   }
 
   // ---- per-head dot products
@@ -203,10 +255,19 @@ __global__ __launch_bounds__(256) void leapq_decode_kernel(
     const int vi = 4 * w + g + 16 * p;
     if (vi <= nv) {
       float pk = 0.f, pq = 0.f;
+      if (KDA && vi < nv) {   // (decayed a o k) . key of the compensator or record
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pk += wv[p][e] * kx[e];
-        pq += wv[p][e] * qx[e];
+        for (int e = 0; e < 8; ++e) {
+          const float d = vi < rank ? g0x[e] : s_gv[vi - rank][8 * n + e];
+          pk += wv[p][e] * (d * yk8[e]);
+          pq += wv[p][e] * (d * yq8[e]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pk += wv[p][e] * kx[e];
+          pq += wv[p][e] * qx[e];
+        }
       }
       pk = sum16(pk);
       pq = sum16(pq);
@@ -224,8 +285,13 @@ __global__ __launch_bounds__(256) void leapq_decode_kernel(
     float xk[8], xq[8], mk = 0.f, mq = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      xk[e] = cx[e] * kx[e];
-      xq[e] = cx[e] * qx[e];
+      if constexpr (KDA) {
+        xk[e] = cx[e] * (g0x[e] * yk8[e]);
+        xq[e] = cx[e] * (g0x[e] * yq8[e]);
+      } else {
+        xk[e] = cx[e] * kx[e];
+        xq[e] = cx[e] * qx[e];
+      }
       mk = fmaxf(mk, fabsf(xk[e]));
       mq = fmaxf(mq, fabsf(xq[e]));
     }
@@ -267,7 +333,7 @@ __global__ __launch_bounds__(256) void leapq_decode_kernel(
 
   // ---- rows: compensator and buffered terms (slots = g mod 4), summed over the
   // four lanes of a row, then lane (n, 0) finishes rows 32 w + 16 T + n
-  const float g0 = s_g[m];
+  const float g0 = KDA ? 1.f : s_g[m];
   const float kq = s_dq[nv];
 #pragma unroll
   for (int T = 0; T < 2; ++T) {
@@ -284,7 +350,7 @@ __global__ __launch_bounds__(256) void leapq_decode_kernel(
     for (int jj = 0; jj < kMaxWindow / 4; ++jj) {
       const int j = 4 * jj + g;
       if (j < m) {
-        const float wj = s_g[j] * bur[T][jj];
+        const float wj = KDA ? bur[T][jj] : s_g[j] * bur[T][jj];
         tk += wj * s_dk[rank + j];
         tq += wj * s_dq[rank + j];
       }
@@ -295,8 +361,8 @@ __global__ __launch_bounds__(256) void leapq_decode_kernel(
       const float sv = vsr[T] * (1.0f / 127.0f);
       const float Sk = g0 * (sv * yk[T] + ck) + tk;
       const float Sq = g0 * (sv * yq[T] + cq) + tq;
-      const float u = b * (vrow[T] - a * Sk);
-      const float oi = a * Sq + u * kq;
+      const float u = KDA ? b * (vrow[T] - Sk) : b * (vrow[T] - a * Sk);
+      const float oi = KDA ? Sq + u * kq : a * Sq + u * kq;
       bu[(size_t)m * kD + row[T]] = u;
       io_traits<IO>::st(o, hk + row[T], oi);
     }
@@ -343,6 +409,16 @@ struct alignas(16) FlushSmem {
   float col[kD];                  // stored smoothing factors, then 1 / the new ones
   float cred[4 * kD];             // per-wave column statistics
   float dec[kMaxWindow + 1];      // dec[j] = G_j for j < m, dec[m] = G0
+};
+
+// KDA: the decays per key channel, gv[j][c] = prod_{j<i<m} a_i[c], gv[m] = G0
+template <bool KDA>
+struct alignas(16) FlushDecays {
+  float gv[kMaxWindow + 1][kD];
+};
+template <>
+struct alignas(16) FlushDecays<false> {   // Gated DeltaNet: scalar decays (FlushSmem::dec)
+  float gv[1][4];
 };
 
 // fp32 16 x 16 x 4 MFMA: lane l holds A[l%16][l/16], B[l/16][l%16]; D[4(l/16)+e][l%16]
@@ -458,7 +534,7 @@ __device__ __forceinline__ void cholqr2_wave(float (&x)[2][RANK]) {
 // four consecutive floats of LDS as a vector (16-byte aligned)
 __device__ __forceinline__ f32x4 lds4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 
-template <int RANK>
+template <int RANK, bool KDA>
 __global__ __launch_bounds__(kFlushNT) __attribute__((amdgpu_waves_per_eu(RANK <= 5 ? 3 : 2))) void leapq_flush_kernel(
     int8_t* __restrict__ codes, float* __restrict__ vscale, float* __restrict__ ksmooth,
     uint16_t* __restrict__ ct_k, uint16_t* __restrict__ ct_u, const float* __restrict__ buf_k,
@@ -467,6 +543,7 @@ __global__ __launch_bounds__(kFlushNT) __attribute__((amdgpu_waves_per_eu(RANK <
     float* __restrict__ pre_round) {
   constexpr int RQ = RANK <= 4 ? 4 : 8;   // padded rank of the LDS blocks
   __shared__ FlushSmem<RQ> sm;
+  __shared__ FlushDecays<KDA> dk_[1];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
   const int head = blockIdx.x;
   const size_t hk = (size_t)head * kD;
@@ -475,10 +552,14 @@ __global__ __launch_bounds__(kFlushNT) __attribute__((amdgpu_waves_per_eu(RANK <
 
   // ---------------------------------------------------------------- inputs
   if constexpr (RANK > 0) {
-    for (int i = tid; i < kD * RQ; i += kFlushNT) {
-      const int c = i / RQ, r = i % RQ;
-      sm.Q[i] = r < RANK ? q0[c * RANK + r] : 0.f;
+    float qs[kD * RQ / kFlushNT];   // all requested before the first is stored
+#pragma unroll
+    for (int it = 0; it < kD * RQ / kFlushNT; ++it) {
+      const int i = tid + kFlushNT * it, c = i / RQ, r = i % RQ;
+      qs[it] = r < RANK ? q0[c * RANK + r] : 0.f;
     }
+#pragma unroll
+    for (int it = 0; it < kD * RQ / kFlushNT; ++it) sm.Q[tid + kFlushNT * it] = qs[it];
   }
   const int nt = dense ? 0 : RANK + m;   // rank-one terms of the rebuild
   const int ns = (nt + 3) >> 2;          // MFMA steps of four terms
@@ -500,32 +581,54 @@ __global__ __launch_bounds__(kFlushNT) __attribute__((amdgpu_waves_per_eu(RANK <
       vs[t] = vscale[hk + vrow[t]];
     }
     // term rows (compensators, then records; zero up to a multiple of four): piece q
-    // of a row is channels [4 q, 4 q + 4); keys go to D-row order, values as they are
-    for (int idx = tid; idx < ns * 4 * 32; idx += kFlushNT) {
-      const int j = idx >> 5, q = idx & 31;
-      f32x4 kk = {0.f, 0.f, 0.f, 0.f}, uu = {0.f, 0.f, 0.f, 0.f};
+    // of a row is channels [4 q, 4 q + 4); keys go to D-row order, values as they are.
+    // At most three pieces per thread (24 rows of 32 pieces over 256 threads).
+    f32x4 kk[3], uu[3];
+#pragma unroll
+    for (int it = 0; it < 3; ++it) {
+      const int idx = tid + kFlushNT * it, j = idx >> 5, q = idx & 31;
+      kk[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+      uu[it] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (j < RANK) {
         const uint2 hk4 = *reinterpret_cast<const uint2*>(ct_k + ((size_t)head * RANK + j) * kD + 4 * q);
         const uint2 hu4 = *reinterpret_cast<const uint2*>(ct_u + ((size_t)head * RANK + j) * kD + 4 * q);
-        kk = f32x4{h2f(uint16_t(hk4.x)), h2f(uint16_t(hk4.x >> 16)), h2f(uint16_t(hk4.y)), h2f(uint16_t(hk4.y >> 16))};
-        uu = f32x4{h2f(uint16_t(hu4.x)), h2f(uint16_t(hu4.x >> 16)), h2f(uint16_t(hu4.y)), h2f(uint16_t(hu4.y >> 16))};
+        kk[it] = f32x4{h2f(uint16_t(hk4.x)), h2f(uint16_t(hk4.x >> 16)), h2f(uint16_t(hk4.y)), h2f(uint16_t(hk4.y >> 16))};
+        uu[it] = f32x4{h2f(uint16_t(hu4.x)), h2f(uint16_t(hu4.x >> 16)), h2f(uint16_t(hu4.y)), h2f(uint16_t(hu4.y >> 16))};
       } else if (j < nt) {
         const size_t off = ((size_t)head * window + (j - RANK)) * kD + 4 * q;
-        kk = *reinterpret_cast<const f32x4*>(buf_k + off);
-        uu = *reinterpret_cast<const f32x4*>(buf_u + off);
+        kk[it] = *reinterpret_cast<const f32x4*>(buf_k + off);
+        uu[it] = *reinterpret_cast<const f32x4*>(buf_u + off);
       }
-      *reinterpret_cast<f32x4*>(sm.u.rb.K + j * kRP + 16 * (q & 7) + 4 * (q >> 3)) = kk;
-      *reinterpret_cast<f32x4*>(sm.u.rb.U + j * kRP + 4 * q) = uu;
     }
-    if (tid < kD) sm.col[tid] = ksmooth[hk + tid];
-    if (tid == 0) {   // suffix products of the buffered decays, newest first
-      const float* ba = buf_a + (size_t)head * window;
-      float gg = 1.f;
-      for (int j = m - 1; j >= 0; --j) {
-        sm.dec[j] = gg;
-        gg *= ba[j];
+    if constexpr (KDA) {
+      // suffix products of channel tid's buffered decays, newest first; the stored
+      // residual's smoothing factors carry G0, so the dequantised term decays with it
+      if (tid < kD) {
+        suffix_products(buf_a + (size_t)head * window * kD + tid, kD, m,
+                        [&](int j, float x) { dk_[0].gv[j][tid] = x; });
+        sm.col[tid] = ksmooth[hk + tid] * dk_[0].gv[m][tid];
       }
-      sm.dec[m] = gg;
+      if (tid == 0) {
+#pragma unroll
+        for (int j = 0; j <= kMaxWindow; ++j) sm.dec[j] = 1.f;
+      }
+      lds_barrier();
+    } else {
+      if (tid < kD) sm.col[tid] = ksmooth[hk + tid];
+      if (tid == 0)   // suffix products of the buffered decays
+        suffix_products(buf_a + (size_t)head * window, 1, m, [&](int j, float x) { sm.dec[j] = x; });
+    }
+#pragma unroll
+    for (int it = 0; it < 3; ++it) {
+      const int idx = tid + kFlushNT * it, j = idx >> 5, q = idx & 31;
+      if (idx < ns * 4 * 32) {
+        f32x4 kv = kk[it];
+        if constexpr (KDA) {   // KDA: the key of a term carries its decay (G0 for compensators)
+          if (j < nt) kv *= *reinterpret_cast<const f32x4*>(&dk_[0].gv[j < RANK ? m : j - RANK][4 * q]);
+        }
+        *reinterpret_cast<f32x4*>(sm.u.rb.K + j * kRP + 16 * (q & 7) + 4 * (q >> 3)) = kv;
+        *reinterpret_cast<f32x4*>(sm.u.rb.U + j * kRP + 4 * q) = uu[it];
+      }
     }
   }
   lds_barrier();
@@ -757,64 +860,67 @@ static int check_state(const leapq_state* st, const char* fn) {
 
 using namespace gdnrt;
 
-extern "C" int leapq_decode_step(const leapq_state* st, int pos, const void* q, const void* k,
-                                 const void* v, const float* alpha, const float* beta, void* o,
-                                 int io, void* stream) {
-  int rc = check_state(st, "leapq_decode_step");
+namespace {
+
+template <bool KDA>
+int decode_step(const char* fn, const leapq_state* st, int pos, const void* q, const void* k,
+                const void* v, const float* alpha, const float* beta, void* o, int io, void* stream) {
+  int rc = check_state(st, fn);
   if (rc != GDNRT_OK) return rc;
-  if (io != GDNRT_F32 && io != GDNRT_BF16) return set_error(GDNRT_EDTYPE, "leapq_decode_step: io=%d", io);
+  if (io != GDNRT_F32 && io != GDNRT_BF16) return set_error(GDNRT_EDTYPE, "%s: io=%d", fn, io);
   if (pos < 0 || pos >= st->window)
-    return set_error(GDNRT_ESTATE, "leapq_decode_step: pos=%d outside [0, window=%d)", pos, st->window);
+    return set_error(GDNRT_ESTATE, "%s: pos=%d outside [0, window=%d)", fn, pos, st->window);
   if (st->N == 0) return clear_error();
-  if (!q || !k || !v || !alpha || !beta || !o)
-    return set_error(GDNRT_EINVAL, "leapq_decode_step: null pointer argument");
-  if (!aligned16(q) || !aligned16(k) || !aligned4(v) || !aligned4(o) || !aligned4(alpha) || !aligned4(beta))
-    return set_error(GDNRT_EALIGN, "leapq_decode_step: q, k must be 16-byte aligned, v, o, alpha, beta 4-byte");
+  if (!q || !k || !v || !alpha || !beta || !o) return set_error(GDNRT_EINVAL, "%s: null pointer argument", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned4(v) || !aligned4(o) || !aligned4(beta) ||
+      (KDA ? !aligned16(alpha) : !aligned4(alpha)))
+    return set_error(GDNRT_EALIGN, KDA ? "%s: q, k, alpha must be 16-byte aligned, v, o, beta 4-byte"
+                                       : "%s: q, k must be 16-byte aligned, v, o, alpha, beta 4-byte", fn);
   const size_t es = io == GDNRT_F32 ? 4 : 2;
   const size_t N = st->N, nIO = N * kD * es, nB = N * st->window * kD * 4;
   if (overlaps(o, nIO, q, nIO) || overlaps(o, nIO, k, nIO) || overlaps(o, nIO, v, nIO) ||
       overlaps(o, nIO, st->buf_k, nB) || overlaps(o, nIO, st->buf_u, nB) ||
       overlaps(o, nIO, st->codes, N * kD * kD))
-    return set_error(GDNRT_EINVAL, "leapq_decode_step: o overlaps another buffer");
+    return set_error(GDNRT_EINVAL, "%s: o overlaps another buffer", fn);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid((unsigned)N), block(256);
   if (io == GDNRT_F32)
-    hipLaunchKernelGGL((leapq_decode_kernel<float>), grid, block, 0, s, st->codes, st->vscale,
+    hipLaunchKernelGGL((leapq_decode_kernel<float, KDA>), grid, block, 0, s, st->codes, st->vscale,
                        st->ksmooth, st->ct_k, st->ct_u, st->buf_k, st->buf_u, st->buf_a, st->rank,
                        st->window, pos, static_cast<const float*>(q), static_cast<const float*>(k),
                        static_cast<const float*>(v), alpha, beta, static_cast<float*>(o));
   else
-    hipLaunchKernelGGL((leapq_decode_kernel<uint16_t>), grid, block, 0, s, st->codes, st->vscale,
+    hipLaunchKernelGGL((leapq_decode_kernel<uint16_t, KDA>), grid, block, 0, s, st->codes, st->vscale,
                        st->ksmooth, st->ct_k, st->ct_u, st->buf_k, st->buf_u, st->buf_a, st->rank,
                        st->window, pos, static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), alpha,
                        beta, static_cast<uint16_t*>(o));
-  return check_launch("leapq_decode_step");
+  return check_launch(fn);
 }
 
-extern "C" int leapq_window_flush(const leapq_state* st, int pos, const float* dense,
-                                  const float* q0, int iters, int smooth_mode, float* pre_round,
-                                  void* stream) {
-  int rc = check_state(st, "leapq_window_flush");
+template <bool KDA>
+int window_flush(const char* fn, const leapq_state* st, int pos, const float* dense, const float* q0,
+                 int iters, int smooth_mode, float* pre_round, void* stream) {
+  int rc = check_state(st, fn);
   if (rc != GDNRT_OK) return rc;
   if (pos < 0 || pos > st->window)
-    return set_error(GDNRT_ESTATE, "leapq_window_flush: pos=%d outside [0, window=%d]", pos, st->window);
-  if (smooth_mode < 0 || smooth_mode > 2)
-    return set_error(GDNRT_EINVAL, "leapq_window_flush: smooth_mode=%d", smooth_mode);
-  if (iters < 0 || iters > 64) return set_error(GDNRT_EINVAL, "leapq_window_flush: iters=%d", iters);
+    return set_error(GDNRT_ESTATE, "%s: pos=%d outside [0, window=%d]", fn, pos, st->window);
+  if (smooth_mode < 0 || smooth_mode > 2) return set_error(GDNRT_EINVAL, "%s: smooth_mode=%d", fn, smooth_mode);
+  if (iters < 0 || iters > 64) return set_error(GDNRT_EINVAL, "%s: iters=%d", fn, iters);
   if (st->N == 0) return clear_error();
-  if (st->rank > 0 && !q0) return set_error(GDNRT_EINVAL, "leapq_window_flush: q0 is null");
-  if ((dense && !aligned16(dense)) || (pre_round && !aligned16(pre_round)) || (q0 && !aligned4(q0)))
-    return set_error(GDNRT_EALIGN, "leapq_window_flush: dense, pre_round must be 16-byte aligned");
+  if (st->rank > 0 && !q0) return set_error(GDNRT_EINVAL, "%s: q0 is null", fn);
+  if ((dense && !aligned16(dense)) || (pre_round && !aligned16(pre_round)) || (q0 && !aligned4(q0)) ||
+      (KDA && !aligned16(st->buf_a)))
+    return set_error(GDNRT_EALIGN, "%s: dense, pre_round%s must be 16-byte aligned", fn, KDA ? ", buf_a" : "");
   const size_t N = st->N, nS = N * kD * kD * 4;
   if ((dense && (overlaps(dense, nS, st->codes, N * kD * kD) || overlaps(dense, nS, pre_round, nS))) ||
       (pre_round && overlaps(pre_round, nS, st->codes, N * kD * kD)))
-    return set_error(GDNRT_EINVAL, "leapq_window_flush: dense / pre_round overlap the state");
+    return set_error(GDNRT_EINVAL, "%s: dense / pre_round overlap the state", fn);
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (st->rank) {
 #define GDNRT_FLUSH(R)                                                                            \
   case R:                                                                                         \
-    hipLaunchKernelGGL((leapq_flush_kernel<R>), dim3((unsigned)N), dim3(kFlushNT),               \
+    hipLaunchKernelGGL((leapq_flush_kernel<R, KDA>), dim3((unsigned)N), dim3(kFlushNT),          \
                        0, s, st->codes, st->vscale, st->ksmooth, st->ct_k, st->ct_u, st->buf_k,   \
                        st->buf_u, st->buf_a, st->window, pos, dense, q0, iters, smooth_mode,      \
                        pre_round);                                                                \
@@ -823,5 +929,32 @@ extern "C" int leapq_window_flush(const leapq_state* st, int pos, const float* d
     GDNRT_FLUSH(5) GDNRT_FLUSH(6) GDNRT_FLUSH(7) GDNRT_FLUSH(8)
 #undef GDNRT_FLUSH
   }
-  return check_launch("leapq_window_flush");
+  return check_launch(fn);
+}
+
+}  // namespace
+
+extern "C" int leapq_decode_step(const leapq_state* st, int pos, const void* q, const void* k,
+                                 const void* v, const float* alpha, const float* beta, void* o,
+                                 int io, void* stream) {
+  return decode_step<false>("leapq_decode_step", st, pos, q, k, v, alpha, beta, o, io, stream);
+}
+
+extern "C" int leapq_window_flush(const leapq_state* st, int pos, const float* dense,
+                                  const float* q0, int iters, int smooth_mode, float* pre_round,
+                                  void* stream) {
+  return window_flush<false>("leapq_window_flush", st, pos, dense, q0, iters, smooth_mode, pre_round, stream);
+}
+
+extern "C" int kda_leapq_decode_step(const leapq_state* st, int pos, const void* q, const void* k,
+                                     const void* v, const float* alpha, const float* beta, void* o,
+                                     int io, void* stream) {
+  return decode_step<true>("kda_leapq_decode_step", st, pos, q, k, v, alpha, beta, o, io, stream);
+}
+
+extern "C" int kda_leapq_window_flush(const leapq_state* st, int pos, const float* dense,
+                                      const float* q0, int iters, int smooth_mode, float* pre_round,
+                                      void* stream) {
+  return window_flush<true>("kda_leapq_window_flush", st, pos, dense, q0, iters, smooth_mode, pre_round,
+                            stream);
 }

@@ -191,6 +191,25 @@ def leapq_decode(B=512, H=32, steps=4096, d=D, device="cpu", seed=1004,
                 Q0=compensator_start(d))
 
 
+def kda_leapq_decode(B=512, H=32, steps=256, d=D, device="cpu", seed=1007,
+                     outlier_scale=50.0, n_outliers=2):
+    """KDA in the windowed 8-bit state: the KDA decode workload (one decay per key
+    channel, slow heads at 0.999) with the LeapQuant initial state's two outlier key
+    channels per head at 50x, and the compensator start block ``Q0``."""
+    g = _gen(device, seed)
+    N = B * H
+    q, k, v = _decode_tokens(steps, N, d, g, device, torch.bfloat16)
+    alpha = _decode_gates_vec(steps, B, H, d, g, device)
+    beta = torch.sigmoid(_randn((steps, N), g, device, 0.0, 1.0))
+    S0 = _randn((N, d, d), g, device, 0.0, 0.05)
+    cols = torch.argsort(torch.rand((N, d), generator=g, device=device), dim=1)[:, :n_outliers]
+    scale = torch.ones((N, d), device=device)
+    scale.scatter_(1, cols, outlier_scale)
+    S0.mul_(scale[:, None, :])
+    return dict(q=q, k=k, v=v, alpha=alpha, beta=beta, S0=S0, outlier_cols=cols,
+                Q0=compensator_start(d))
+
+
 def compensator_start(d=D, r=4, seed=0):
     """Fixed random start block of the compensator-token subspace iteration:
     ``[d_k][r]`` fp32 entries N(0,1) from seed 0 (always drawn on the CPU)."""

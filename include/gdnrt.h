@@ -218,6 +218,37 @@ GDNRT_API int leapq_window_flush(const leapq_state* st, int pos, const float* de
                        const float* q0, int iters, int smooth_mode,
                        float* pre_round, void* stream);
 
+/*
+ * Kimi Delta Attention (one decay per key channel) in the windowed 8-bit state:
+ * "LeapQuant: an 8-bit recurrent state that stops rounding every token", section
+ * "The state, from the update rule up" for the update, section "Fix one: leap over a
+ * window" (eq. 4 and eq. 10 with diagonal decays, which accumulate per channel) and
+ * section "What 1.19 bytes buys" for the buffered per-channel decays. Same stored
+ * state and buffer as leapq_decode_step except buf_a: [N][window][dk] fp32, 16-byte
+ * aligned, one decay vector per buffered token. With Gamma_{a:b} = Diag(alpha_a ...
+ * alpha_b) and S_pos y = S_hat_0 (Gamma_{1:pos} y) + sum_j u_j (k_j . Gamma_{j+1:pos} y)
+ * (the compensator tokens decay with the residual by Gamma_{1:pos}),
+ *
+ *     u_t = beta_t (v_t - S_pos (alpha_t o k_t)),   o_t = S_pos (alpha_t o q_t) + u_t (k_t . q_t),
+ *
+ * then appends (k_t, u_t, alpha_t) at slot pos. alpha [N][dk] fp32 (16-byte aligned).
+ * Errors as leapq_decode_step.
+ */
+GDNRT_API int kda_leapq_decode_step(const leapq_state* st, int pos,
+                      const void* q, const void* k, const void* v,
+                      const float* alpha, const float* beta, void* o,
+                      int io, void* stream);
+
+/*
+ * Window flush of the KDA windowed state: as leapq_window_flush, with the rebuild
+ * S_pos = S_hat_0 Gamma_{1:pos} + sum_j u_j k_j^T Gamma_{j+1:pos} (eq. 4 with diagonal
+ * decays) from buf_a [N][window][dk]. The fit, subtraction, smoothing and rounding are
+ * those of leapq_window_flush; with `dense` the two are the same operation.
+ */
+GDNRT_API int kda_leapq_window_flush(const leapq_state* st, int pos, const float* dense,
+                       const float* q0, int iters, int smooth_mode,
+                       float* pre_round, void* stream);
+
 /* Message for the calling thread's last non-OK status ("" if none). */
 GDNRT_API const char* gdnrt_last_error(void);
 

@@ -33,7 +33,8 @@ def test_header_declares_the_entry_points():
     names = set(declared())
     for n in ("gdn_decode_step", "gla_chunk_fwd", "gdn_chunk_fwd", "leapq_decode_step",
               "leapq_window_flush", "gdnrt_last_error", "gdn_chunk_fwd_workspace_bytes",
-              "gla_chunk_fwd_workspace_bytes", "kda_decode_step"):
+              "gla_chunk_fwd_workspace_bytes", "kda_decode_step", "kda_leapq_decode_step",
+              "kda_leapq_window_flush"):
         assert n in names, n
 
 
@@ -115,3 +116,20 @@ def test_leapq_validation(lib):
     assert fl(ctypes.byref(st), 17, None, p, 1, 0, None, None) == ESTATE
     assert fl(ctypes.byref(st), 0, None, p, 1, 3, None, None) == EINVAL      # smooth_mode
     assert fl(ctypes.byref(st), 0, None, None, 1, 0, None, None) == EINVAL   # q0 missing
+
+
+def test_kda_leapq_validation(lib):
+    """The KDA windowed entry points validate as the GDN ones, and read the
+    per-channel decays 16 bytes at a time."""
+    p = ctypes.c_void_p(4096)
+    st = _state(lib)
+    f = lib.kda_leapq_decode_step
+    assert f(ctypes.byref(st), 16, p, p, p, p, p, p, 1, None) == ESTATE
+    assert f(ctypes.byref(_state(lib, rank=9)), 0, p, p, p, p, p, p, 1, None) == ESHAPE
+    assert f(ctypes.byref(st), 0, p, p, p, ctypes.c_void_p(4100), p, p, 1, None) == EALIGN
+    assert "kda_leapq_decode_step" in _err(lib)
+    assert f(None, 0, p, p, p, p, p, p, 1, None) == EINVAL
+    fl = lib.kda_leapq_window_flush
+    assert fl(ctypes.byref(st), 17, None, p, 1, 0, None, None) == ESTATE
+    assert fl(ctypes.byref(st), 0, None, None, 1, 0, None, None) == EINVAL   # q0 missing
+    assert fl(ctypes.byref(_state(lib, buf_a=4100)), 0, None, p, 1, 0, None, None) == EALIGN
