@@ -418,6 +418,8 @@ def main():
         torch.cuda.empty_cache()
     if "kda_leapq" in rows:
         r = bench_leapq(tokens=256, kda=True)
+        r["traffic_bytes_decode_kernel"] = counter_traffic("leapq_decode_kernel<kda>")
+        r["traffic_bytes_flush_kernel"] = counter_traffic("leapq_flush_kernel<kda>")
         kda_row = out_rows.get("kda")
         r["speedup_vs_fp32_kda_decode"] = kda_row["ms_per_step"] / r["ms_per_step"] if kda_row else None
         out_rows["kda_leapq"] = r

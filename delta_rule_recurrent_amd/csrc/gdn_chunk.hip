@@ -420,7 +420,7 @@ __global__ __launch_bounds__(512) void gdn_chunk_prep_kernel(
 // ------------------------------------------------------------------ sequential pass
 namespace gdc {
 
-constexpr int kAhead = 2;   // chunks of operands in flight ahead of the one in use
+constexpr int kAhead = 2;   // chunks of operands in flight ahead of the one in use (4 measured no faster)
 constexpr int kWarm = 2;    // chunks between the L2 warm-up of a chunk and its loads
 
 template <int VT>
@@ -603,37 +603,34 @@ __global__ __launch_bounds__(512) void gdn_chunk_seq_kernel(
 
   if (nc > 0) {
     const size_t chunk0 = (size_t)n * nc, tokn = (size_t)n * T;
-    // three operand sets in rotation: chunk ci uses set ci % 3 and loads chunk ci + 2
-    // into set (ci + 2) % 3
-    static_assert(kAhead == 2, "three-set rotation");
-    Prefetch<NVB> p0, p1, p2;
+    // kAhead + 1 operand sets in rotation: chunk ci uses set ci % NS and loads chunk
+    // ci + kAhead into set (ci + kAhead) % NS (every index below is a constant after
+    // unrolling, so the sets stay in registers)
+    constexpr int NS = kAhead + 1;
+    Prefetch<NVB> P[NS];
     int cur = 0;
     unsigned sink = 0;
-    {
-      const uint8_t* c0 = ws + chunk0 * kWsChunk;
-      const uint8_t* c1 = ws + (chunk0 + min(1, nc - 1)) * kWsChunk;
-      const uint8_t* w0 = ws + (chunk0 + min(2, nc - 1)) * kWsChunk;
-      const uint8_t* w1 = ws + (chunk0 + min(3, nc - 1)) * kWsChunk;
-      fetch_chunk<NVB, 0>(p0, c0, w0, vt);
-      fetch_chunk<NVB, 1>(p0, c0, w0, vt);
-      fetch_chunk<NVB, 0>(p1, c1, w1, vt);
-      fetch_chunk<NVB, 1>(p1, c1, w1, vt);
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) {
+      const uint8_t* ci_ = ws + (chunk0 + min(i, nc - 1)) * kWsChunk;
+      const uint8_t* wi_ = ws + (chunk0 + min(i + kWarm, nc - 1)) * kWsChunk;
+      fetch_chunk<NVB, 0>(P[i], ci_, wi_, vt);
+      fetch_chunk<NVB, 1>(P[i], ci_, wi_, vt);
     }
     lds_barrier();
-    gdn_seq_chunk<VT, true>(sm, p0, p2, Sacc, cur, sink, 0, nc, chunk0, tokn, vt, ws, o);
+    gdn_seq_chunk<VT, true>(sm, P[0], P[kAhead], Sacc, cur, sink, 0, nc, chunk0, tokn, vt, ws, o);
     int ci = 1;
-    for (; ci + 2 < nc; ci += 3) {
-      gdn_seq_chunk<VT, false>(sm, p1, p0, Sacc, cur, sink, ci, nc, chunk0, tokn + (size_t)ci * C, vt, ws, o);
-      gdn_seq_chunk<VT, false>(sm, p2, p1, Sacc, cur, sink, ci + 1, nc, chunk0, tokn + (size_t)(ci + 1) * C,
-                               vt, ws, o);
-      gdn_seq_chunk<VT, false>(sm, p0, p2, Sacc, cur, sink, ci + 2, nc, chunk0, tokn + (size_t)(ci + 2) * C,
-                               vt, ws, o);
+    for (; ci + NS - 1 < nc; ci += NS) {
+#pragma unroll
+      for (int u = 0; u < NS; ++u)
+        gdn_seq_chunk<VT, false>(sm, P[(1 + u) % NS], P[(1 + u + kAhead) % NS], Sacc, cur, sink, ci + u, nc,
+                                 chunk0, tokn + (size_t)(ci + u) * C, vt, ws, o);
     }
-    if (ci < nc)
-      gdn_seq_chunk<VT, false>(sm, p1, p0, Sacc, cur, sink, ci, nc, chunk0, tokn + (size_t)ci * C, vt, ws, o);
-    if (ci + 1 < nc)
-      gdn_seq_chunk<VT, false>(sm, p2, p1, Sacc, cur, sink, ci + 1, nc, chunk0, tokn + (size_t)(ci + 1) * C,
-                               vt, ws, o);
+#pragma unroll
+    for (int u = 0; u < NS - 1; ++u)
+      if (ci + u < nc)
+        gdn_seq_chunk<VT, false>(sm, P[(1 + u) % NS], P[(1 + u + kAhead) % NS], Sacc, cur, sink, ci + u, nc,
+                                 chunk0, tokn + (size_t)(ci + u) * C, vt, ws, o);
     store_o<VT>(sm.Ot[(nc - 1) & 1], o, tokn + (size_t)(nc - 1) * C, v0);
     asm volatile("" ::"v"(sink));   // keeps the warm-up loads
   }
