@@ -87,3 +87,54 @@ def kda_recurrent_explicit(q, k, v, alpha, beta, S0=None):
             o[n, t] = (Sk.T @ qt).reshape(dv)
         S_out[n] = Sk.T
     return o, S_out
+
+
+def kda_chunk_wy(q, k, v, alpha, beta, S0=None, chunk=64):
+    """Chunkwise form of the KDA recurrence (UT-transform reading; the pages print
+    no chunk form). Unrolling eq. 3 with per-channel decays inside a chunk, with
+    local positions r, j, b_r = sum_{i<=r} log alpha_i (a vector over key channels)
+    and Gamma_r = exp(b_r), rows of K, V, Q, U being tokens:
+
+        (I + L) U = diag(beta) V - diag(beta) (K o Gamma) S_0^T,
+            L[r, j] = beta_r sum_c k_r[c] k_j[c] exp(b_r[c] - b_j[c]) for j < r,
+        O   = (Q o Gamma) S_0^T + A U,
+            A[r, j] = sum_c q_r[c] k_j[c] exp(b_r[c] - b_j[c]) for j <= r,
+        S_C = S_0 Diag(Gamma_C) + U^T (K o exp(b_C - b)).
+
+    This is the Gated DeltaNet chunk form with the decay moved inside the key and
+    query products, as gated linear attention carries it. Not used for GPU parity
+    (the recurrence is the definition); a test checks it equals ``kda_recurrent``.
+    T must be a multiple of ``chunk``.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    alpha = np.asarray(alpha, np.float64)
+    beta = np.asarray(beta, np.float64)
+    N, T, dk = k.shape
+    dv = v.shape[2]
+    if T % chunk:
+        raise ValueError("T must be a multiple of chunk")
+    o = np.empty((N, T, dv))
+    S_out = np.empty((N, dv, dk))
+    I = np.eye(chunk)
+    for n in range(N):
+        S = np.zeros((dv, dk)) if S0 is None else np.array(S0[n], dtype=np.float64)
+        for c0 in range(0, T, chunk):
+            sl = slice(c0, c0 + chunk)
+            K, V, Q = k[n, sl], v[n, sl], q[n, sl]
+            bt = beta[n, sl]
+            b = np.cumsum(np.log(alpha[n, sl]), axis=0)           # [C][d_k]
+            diff = b[:, None, :] - b[None, :, :]                   # b_r - b_j
+            low = np.tril(np.ones((chunk, chunk), bool))
+            E = np.where(low[:, :, None], np.exp(np.minimum(diff, 0.0)), 0.0)   # j <= r only
+            G = np.einsum("rc,jc,rjc->rj", K, K, E)
+            L = np.tril(bt[:, None] * G, -1)
+            A = np.einsum("rc,jc,rjc->rj", Q, K, E)
+            Gam = np.exp(b)
+            rhs = bt[:, None] * V - bt[:, None] * ((K * Gam) @ S.T)
+            U = np.linalg.solve(I + L, rhs)
+            o[n, sl] = (Q * Gam) @ S.T + A @ U
+            S = S * Gam[-1][None, :] + U.T @ (K * np.exp(b[-1] - b))
+        S_out[n] = S
+    return o, S_out

@@ -119,3 +119,18 @@ def test_unit_decay_is_the_delta_rule():
         S = S + u[:, :, None] * k[:, t][:, None, :]
         np.testing.assert_allclose(o[:, t], np.einsum("nvk,nk->nv", S, q[:, t]), rtol=0, atol=1e-12)
     np.testing.assert_allclose(ST, S, rtol=0, atol=1e-12)
+
+
+def test_chunk_form_equals_recurrence():
+    """The UT-transform chunk reading with per-channel decays inside the products
+    equals the token-by-token recurrence for several chunk sizes, from zero and
+    from a nonzero state."""
+    rng = np.random.default_rng(31)
+    N, T, d = 2, 64, 16
+    q, k, v, a, b = _rand(rng, N, T, d)
+    S0 = 0.3 * rng.standard_normal((N, d, d))
+    o_r, S_r = kda.kda_recurrent(q, k, v, a, b, S0)
+    for C in (1, 16, 64):
+        o_c, S_c = kda.kda_chunk_wy(q, k, v, a, b, S0, chunk=C)
+        np.testing.assert_allclose(o_c, o_r, rtol=0, atol=1e-11 * np.abs(o_r).max())
+        np.testing.assert_allclose(S_c, S_r, rtol=0, atol=1e-11 * np.abs(S_r).max())
