@@ -1,6 +1,6 @@
 """Benchmark of the gated delta-rule hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--rows decode,kda,leapq,kda_leapq,gla,gdn]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--rows decode,kda,leapq,kda_leapq,gla,gdn,kda_chunk]
 
 Headline (`value`): Gated DeltaNet decode of one layer, 512 streams x 32 heads,
 d_k = d_v = 128, fp32 state resident in HBM, bf16 q/k/v; one step = one token for
@@ -269,24 +269,30 @@ def gdn_chunk_work(C=64):
     return alg, dense
 
 
-def bench_gdn_chunk(K=10, W=2, B=1, H=32, T=16384):
+def bench_gdn_chunk(K=10, W=2, B=1, H=32, T=16384, kda=False):
+    """Chunkwise prefill of the Gated DeltaNet workload; with ``kda`` the same shape
+    with one decay per key channel and token (kda_chunk_fwd). The FLOP count is the
+    GDN one (the per-channel decays only rescale operands)."""
     N = B * H
-    log(f"[gdn_chunk] generating B={B} H={H} T={T}")
-    inp = synth.gdn_prefill(B=B, H=H, T=T, device="cuda")
-    ws = m.gdn_chunk_workspace(N, T)
+    tag = "kda_chunk" if kda else "gdn_chunk"
+    log(f"[{tag}] generating B={B} H={H} T={T}")
+    inp = (synth.kda_prefill if kda else synth.gdn_prefill)(B=B, H=H, T=T, device="cuda")
+    ws = (m.kda_chunk_workspace if kda else m.gdn_chunk_workspace)(N, T)
+    fwd = m.kda_chunk_fwd if kda else m.gdn_chunk_fwd
     ST = torch.empty((N, D, D), device="cuda")
     o = torch.empty_like(inp["q"])
 
     def run(i):
-        m.gdn_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], None, ST, o, ws)
+        fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], None, ST, o, ws)
 
     ms, wall = timed(run, K, W)
     alg, dense = gdn_chunk_work()
     chunks = N * T // 64
     flops, dflops = alg * chunks, dense * chunks
-    byts = N * T * (3 * D * 2 + 2 * 4 + D * 2) + N * D * D * 4   # q,k,v, alpha,beta, o, ST
-    res = dict(workload=f"gdn_chunk_fwd B={B} H={H} T={T} d=128 chunk 64, bf16 q/k/v (q, k "
-                        f"L2-normalised), fp32 gates, zero initial state",
+    a_b = D * 4 if kda else 4
+    byts = N * T * (3 * D * 2 + a_b + 4 + D * 2) + N * D * D * 4   # q,k,v, alpha,beta, o, ST
+    res = dict(workload=f"{tag}_fwd B={B} H={H} T={T} d=128 chunk 64, bf16 q/k/v (q, k "
+                        f"L2-normalised), fp32 {'per-channel ' if kda else ''}gates, zero initial state",
                ms=ms, tokens_per_s=B * T / (ms * 1e-3), gflop=flops / 1e9, gflop_dense=dflops / 1e9,
                tflops=flops / (ms * 1e-3) / 1e12, tflops_dense=dflops / (ms * 1e-3) / 1e12,
                bytes=byts, achieved_gbs=byts / (ms * 1e-3) / 1e9,
@@ -347,7 +353,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--rows", default="decode,kda,leapq,kda_leapq,gla,gdn")
+    ap.add_argument("--rows", default="decode,kda,leapq,kda_leapq,gla,gdn,kda_chunk")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the measured HBM-copy and bf16-GEMM ceilings")
@@ -404,6 +410,12 @@ def main():
         r["traffic_bytes"] = tp + ts if tp is not None and ts is not None else None
         out_rows["gdn_chunk"] = r
         log(f"[gdn_chunk] {r['ms']*1e3:.1f} us  {r['tflops']:.1f} TFLOP/s ({r['frac_mfma']*100:.1f}% MFMA)  "
+            f"{r['achieved_gbs']:.0f} GB/s ({r['frac_hbm']*100:.1f}% HBM)  {r['tokens_per_s']/1e6:.2f} M tok/s")
+        torch.cuda.empty_cache()
+    if "kda_chunk" in rows:
+        r = bench_gdn_chunk(kda=True)
+        out_rows["kda_chunk"] = r
+        log(f"[kda_chunk] {r['ms']*1e3:.1f} us  {r['tflops']:.1f} TFLOP/s ({r['frac_mfma']*100:.1f}% MFMA)  "
             f"{r['achieved_gbs']:.0f} GB/s ({r['frac_hbm']*100:.1f}% HBM)  {r['tokens_per_s']/1e6:.2f} M tok/s")
         torch.cuda.empty_cache()
     if "leapq" in rows:

@@ -2,8 +2,8 @@
 
 Entry points over the gdnrt HIP library (C ABI in include/gdnrt.h):
 ``gdn_decode_step``, ``gla_chunk_fwd``, ``gdn_chunk_fwd``, ``leapq_decode_step``,
-``leapq_window_flush``, ``kda_decode_step``, ``kda_leapq_decode_step`` and
-``kda_leapq_window_flush``. ``synth`` draws the seeded synthetic workloads.
+``leapq_window_flush``, ``kda_decode_step``, ``kda_chunk_fwd``,
+``kda_leapq_decode_step`` and ``kda_leapq_window_flush``. ``synth`` draws the seeded synthetic workloads.
 """
 from .binding import (  # noqa: F401
     GdnrtError,
@@ -13,6 +13,8 @@ from .binding import (  # noqa: F401
     gdn_decode_step,
     gla_chunk_fwd,
     gla_chunk_workspace,
+    kda_chunk_fwd,
+    kda_chunk_workspace,
     kda_decode_step,
     kda_leapq_decode_step,
     kda_leapq_window_flush,

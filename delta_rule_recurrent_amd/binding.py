@@ -39,6 +39,8 @@ SIGNATURES = {
     "gla_chunk_fwd_workspace_bytes": ([_c_int] * 5, ctypes.c_size_t),
     "gdn_chunk_fwd": ([_vp] * 8 + [_c_int] * 6 + [_vp, ctypes.c_size_t, _vp], _c_int),
     "gdn_chunk_fwd_workspace_bytes": ([_c_int] * 5, ctypes.c_size_t),
+    "kda_chunk_fwd": ([_vp] * 8 + [_c_int] * 6 + [_vp, ctypes.c_size_t, _vp], _c_int),
+    "kda_chunk_fwd_workspace_bytes": ([_c_int] * 5, ctypes.c_size_t),
     "leapq_decode_step": ([ctypes.POINTER(LeapqState), _c_int] + [_vp] * 6 + [_c_int, _vp], _c_int),
     "leapq_window_flush": ([ctypes.POINTER(LeapqState), _c_int, _vp, _vp, _c_int, _c_int, _vp, _vp],
                            _c_int),
@@ -194,16 +196,37 @@ def gdn_chunk_workspace(N, T, device="cuda", chunk=CHUNK):
     return torch.empty(max(nb, 16), dtype=torch.uint8, device=device)
 
 
+def kda_chunk_workspace(N, T, device="cuda", chunk=CHUNK):
+    """Allocate the workspace kda_chunk_fwd needs for N sequences of T tokens."""
+    nb = lib().kda_chunk_fwd_workspace_bytes(N, T, D, D, chunk)
+    return torch.empty(max(nb, 16), dtype=torch.uint8, device=device)
+
+
+def kda_chunk_fwd(q, k, v, alpha, beta, S0=None, ST=None, o=None, workspace=None, chunk=CHUNK):
+    """Kimi Delta Attention chunkwise forward (prefill), one decay per key channel.
+
+    q, k, v [N][T][128] bf16; alpha [N][T][128] fp32; beta [N][T] fp32; S0
+    [N][128][128] fp32 or None; workspace from kda_chunk_workspace (allocated here
+    if None). Returns (o [N][T][128] bf16, ST [N][128][128] fp32)."""
+    return _chunk_fwd("kda_chunk_fwd", kda_chunk_workspace, (q.shape[0], q.shape[1], D),
+                      q, k, v, alpha, beta, S0, ST, o, workspace, chunk)
+
+
 def gdn_chunk_fwd(q, k, v, alpha, beta, S0=None, ST=None, o=None, workspace=None, chunk=CHUNK):
     """Gated DeltaNet chunkwise forward (prefill).
 
     q, k, v [N][T][128] bf16; alpha, beta [N][T] fp32; S0 [N][128][128] fp32 or
     None; workspace from gdn_chunk_workspace (allocated here if None).
     Returns (o [N][T][128] bf16, ST [N][128][128] fp32)."""
+    return _chunk_fwd("gdn_chunk_fwd", gdn_chunk_workspace, (q.shape[0], q.shape[1]),
+                      q, k, v, alpha, beta, S0, ST, o, workspace, chunk)
+
+
+def _chunk_fwd(name, alloc, alpha_shape, q, k, v, alpha, beta, S0, ST, o, workspace, chunk):
     N, T, _ = q.shape
     for n_, t_ in (("q", q), ("k", k), ("v", v)):
         _need(t_, n_, torch.bfloat16, (N, T, D))
-    _need(alpha, "alpha", torch.float32, (N, T))
+    _need(alpha, "alpha", torch.float32, alpha_shape)
     _need(beta, "beta", torch.float32, (N, T))
     if S0 is not None:
         _need(S0, "S0", torch.float32, (N, D, D))
@@ -214,9 +237,9 @@ def gdn_chunk_fwd(q, k, v, alpha, beta, S0=None, ST=None, o=None, workspace=None
         o = torch.empty((N, T, D), dtype=torch.bfloat16, device=q.device)
     _need(o, "o", torch.bfloat16, (N, T, D))
     if workspace is None:
-        workspace = gdn_chunk_workspace(N, T, q.device, chunk)
+        workspace = alloc(N, T, q.device, chunk)
     _need(workspace, "workspace", torch.uint8)
-    _check("gdn_chunk_fwd", lib().gdn_chunk_fwd(
+    _check(name, getattr(lib(), name)(
         _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(ST), _ptr(o),
         N, T, D, D, chunk, BF16, _ptr(workspace), workspace.numel(), _stream()))
     return o, ST

@@ -47,6 +47,10 @@ constexpr int PF = C + 4;   // fp32 pitch of 64-wide rows (16-byte aligned)
 //  g_C   16 copies (so that every lane loads it with a vector load)
 constexpr size_t kWsW = 0, kWsQ = 16384, kWsK = 32768, kWsU = 49152, kWsO = 65536;
 constexpr size_t kWsG = 81920, kWsChunk = 81984;
+// KDA: the chunk's state decay is a vector over key channels (128 fp32 at kWsG)
+constexpr size_t kWsChunkKda = kWsG + kD * 4;
+template <bool KDA>
+constexpr size_t ws_chunk() { return KDA ? kWsChunkKda : kWsChunk; }
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));   // register-promotable across loops
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -153,12 +157,16 @@ struct alignas(16) PrepSmem {
 
 // one chunk's inputs for this thread: 16-byte pieces p = tid + 512 h (h = 0, 1) of
 // q, k, v (token p >> 4, channels 8 (p & 15) ..), and alpha, beta of token tid % 64
+// KDA: the per-channel decays of tokens 4 (tid >> 5) .. + 3, channels 4 (tid & 31) .. + 3
+template <bool KDA>
 struct PrepIn {
   u32x4 q[2], k[2], v[2];
   float al, be;
+  f32x4 a4[KDA ? 4 : 1];
 };
 
-__device__ __forceinline__ void prep_fetch(PrepIn& in, const uint16_t* __restrict__ q,
+template <bool KDA>
+__device__ __forceinline__ void prep_fetch(PrepIn<KDA>& in, const uint16_t* __restrict__ q,
                                            const uint16_t* __restrict__ k,
                                            const uint16_t* __restrict__ v,
                                            const float* __restrict__ alpha,
@@ -172,9 +180,29 @@ __device__ __forceinline__ void prep_fetch(PrepIn& in, const uint16_t* __restric
     in.k[h] = *reinterpret_cast<const u32x4*>(k + off);
     in.v[h] = *reinterpret_cast<const u32x4*>(v + off);
   }
-  in.al = alpha[tok0 + (tid & 63)];
+  if constexpr (KDA) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      in.a4[i] = *reinterpret_cast<const f32x4*>(alpha + (tok0 + 4 * (tid >> 5) + i) * kD + 4 * (tid & 31));
+  } else {
+    in.al = alpha[tok0 + (tid & 63)];
+  }
   in.be = beta[tok0 + (tid & 63)];
 }
+
+// KDA: the extra LDS of the prep. Km = K o exp(b_m - b) (bf16, the second operand of
+// the Gram matrix and the scores), per-group totals of the cumulative log-decays and
+// per-channel exp(b_m), exp(b_C - b_m), b_m the cumulative log-decay at token 31.
+template <bool KDA>
+struct alignas(16) KdaPrepSmem {
+  uint16_t Km[C * PQ];
+  float tot[16][kD];
+  float em[kD], ecm[kD];
+};
+template <>
+struct alignas(16) KdaPrepSmem<false> {
+  float unused[4];
+};
 
 // lower-triangle 16 x 16 tile pairs (rb, cb), cb <= rb
 __device__ __forceinline__ void tri_pair(int p, int& rb, int& cb) {
@@ -188,14 +216,16 @@ namespace gdc {
 
 // One chunk of the prep: stages the inputs held in `in`, requests the next chunk's into
 // `in`, and writes the chunk's operands to the workspace.
-__device__ __forceinline__ void prep_chunk(PrepSmem& sm, PrepIn& in, int cid, const uint16_t* __restrict__ q,
+template <bool KDA>
+__device__ __forceinline__ void prep_chunk(PrepSmem& sm, KdaPrepSmem<KDA>& xs, PrepIn<KDA>& in, int cid,
+                                           const uint16_t* __restrict__ q,
                                            const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                            const float* __restrict__ alpha, const float* __restrict__ beta,
                                            uint8_t* __restrict__ ws, int T, int nchunks) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lq = lane >> 4;
   const int nc = T / C;
-  uint8_t* wsc = ws + (size_t)cid * kWsChunk;
+  uint8_t* wsc = ws + (size_t)cid * ws_chunk<KDA>();
 
   // ---- stage q, k, v (row-major); decays
 #pragma unroll
@@ -205,8 +235,22 @@ __device__ __forceinline__ void prep_chunk(PrepSmem& sm, PrepIn& in, int cid, co
     *reinterpret_cast<u32x4*>(sm.K + o) = in.k[h];
     *reinterpret_cast<u32x4*>(sm.V + o) = in.v[h];
   }
-  float gCw;   // g_C (every wave computes it)
-  {
+  float gCw = 0.f;   // GDN: g_C (every wave computes it)
+  // KDA: cumulative log-decays of this thread's 4 tokens x 4 channels, within its group
+  f32x4 pre[KDA ? 4 : 1];
+  if constexpr (KDA) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 a = in.a4[i];
+      const f32x4 la = {__logf(a.x), __logf(a.y), __logf(a.z), __logf(a.w)};
+      pre[i] = i == 0 ? la : pre[i - 1] + la;
+    }
+    *reinterpret_cast<f32x4*>(&xs.tot[tid >> 5][4 * (tid & 31)]) = pre[3];
+    if (wave == 0) {
+      sm.bt[lane] = in.be;
+      sm.btg[lane] = in.be;   // the decays sit in the key operand of W
+    }
+  } else {
     const float lgv = wave_scan(__logf(in.al));
     const float lC = __shfl(lgv, C - 1);
     gCw = __expf(lC);
@@ -222,20 +266,75 @@ __device__ __forceinline__ void prep_chunk(PrepSmem& sm, PrepIn& in, int cid, co
   // next chunk's inputs (the last chunk of a block loads itself again)
   {
     const int nx = cid + (int)gridDim.x < nchunks ? cid + (int)gridDim.x : cid;
-    prep_fetch(in, q, k, v, alpha, beta, (size_t)(nx / nc) * T + (size_t)(nx % nc) * C);
+    prep_fetch<KDA>(in, q, k, v, alpha, beta, (size_t)(nx / nc) * T + (size_t)(nx % nc) * C);
   }
-  *reinterpret_cast<float*>(wsc + kWsG + (lane & 15) * 4) = gCw;
+  if constexpr (KDA) {
+    // b = cumulative log-decay per channel; with b_m its value at token 31 (the middle),
+    // Q <- Q o exp(b - b_m), K <- K o exp(b - b_m), Km = K o exp(b_m - b): the Gram
+    // matrix and the scores then carry exp(b_r - b_j) inside their products, and no
+    // factor exceeds exp(32 max|log alpha|)
+    lds_barrier();
+    const int tq = tid >> 5, c0 = 4 * (tid & 31);
+    f32x4 base = {0.f, 0.f, 0.f, 0.f}, bm = {0.f, 0.f, 0.f, 0.f}, bC = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      const f32x4 t4 = *reinterpret_cast<const f32x4*>(&xs.tot[g][c0]);
+      if (g < tq) base += t4;
+      if (g < 8) bm += t4;
+      bC += t4;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 4 * tq + i;
+      const f32x4 b = base + pre[i];
+      f32x4 fp, fm;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        fp[e] = __expf(b[e] - bm[e]);
+        fm[e] = __expf(bm[e] - b[e]);
+      }
+      u32x2* qp = reinterpret_cast<u32x2*>(sm.Q + t * PQ + c0);
+      u32x2* kp = reinterpret_cast<u32x2*>(sm.K + t * PQ + c0);
+      const u32x2 qw = *qp, kw = *kp;
+      *qp = u32x2{pack_bf16(lo_bf(qw.x) * fp[0], hi_bf(qw.x) * fp[1]), pack_bf16(lo_bf(qw.y) * fp[2], hi_bf(qw.y) * fp[3])};
+      *kp = u32x2{pack_bf16(lo_bf(kw.x) * fp[0], hi_bf(kw.x) * fp[1]), pack_bf16(lo_bf(kw.y) * fp[2], hi_bf(kw.y) * fp[3])};
+      *reinterpret_cast<u32x2*>(xs.Km + t * PQ + c0) =
+          u32x2{pack_bf16(lo_bf(kw.x) * fm[0], hi_bf(kw.x) * fm[1]), pack_bf16(lo_bf(kw.y) * fm[2], hi_bf(kw.y) * fm[3])};
+    }
+    if (tq == 0) {
+      f32x4 em, ecm, gc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        em[e] = __expf(bm[e]);
+        ecm[e] = __expf(bC[e] - bm[e]);
+        gc[e] = __expf(bC[e]);
+      }
+      *reinterpret_cast<f32x4*>(&xs.em[c0]) = em;
+      *reinterpret_cast<f32x4*>(&xs.ecm[c0]) = ecm;
+      *reinterpret_cast<f32x4*>(wsc + kWsG + c0 * 4) = gc;
+    }
+  } else {
+    *reinterpret_cast<float*>(wsc + kWsG + (lane & 15) * 4) = gCw;
+  }
   lds_barrier();
 
   // ---- K^ fragments (kb, js) = (f >> 1, f & 1), f = wave + 8 h, to the workspace
+  // (KDA: K^ = Km o exp(b_C - b_m), one channel per lane)
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int f = wave + 8 * h, j0 = (f & 1) * 32 + lq * 8;
-    const u32x4 raw = __builtin_bit_cast(u32x4, ld_tr8(sm.K, PQ, (f & 1) * 32, (f >> 1) * 16));
     u32x4 w;
+    if constexpr (KDA) {
+      const u32x4 raw = __builtin_bit_cast(u32x4, ld_tr8(xs.Km, PQ, (f & 1) * 32, (f >> 1) * 16));
+      const float fc = xs.ecm[(f >> 1) * 16 + l16];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      w[e] = pack_bf16(lo_bf(raw[e]) * sm.kd[j0 + 2 * e], hi_bf(raw[e]) * sm.kd[j0 + 2 * e + 1]);
+      for (int e = 0; e < 4; ++e) w[e] = pack_bf16(lo_bf(raw[e]) * fc, hi_bf(raw[e]) * fc);
+    } else {
+      const u32x4 raw = __builtin_bit_cast(u32x4, ld_tr8(sm.K, PQ, (f & 1) * 32, (f >> 1) * 16));
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = pack_bf16(lo_bf(raw[e]) * sm.kd[j0 + 2 * e], hi_bf(raw[e]) * sm.kd[j0 + 2 * e + 1]);
+    }
     *reinterpret_cast<u32x4*>(wsc + kWsK + ((size_t)f * 64 + lane) * 16) = w;
   }
   // ---- Gram k.k -> L and scores q.k -> A: 20 tile products over the lower triangle
@@ -244,21 +343,24 @@ __device__ __forceinline__ void prep_chunk(PrepSmem& sm, PrepIn& in, int cid, co
     tri_pair(u >> 1, rb, cb);
     const bool sc = u & 1;
     const uint16_t* X = sc ? sm.Q : sm.K;
+    const uint16_t* Y = sm.K;
+    if constexpr (KDA) Y = xs.Km;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      acc = mfma(ld8(X + (rb * 16 + l16) * PQ + ks * 32 + lq * 8),
-                 ld8(sm.K + (cb * 16 + l16) * PQ + ks * 32 + lq * 8), acc);
+    for (int kk = 0; kk < 4; ++kk)
+      acc = mfma(ld8(X + (rb * 16 + l16) * PQ + kk * 32 + lq * 8),
+                 ld8(Y + (cb * 16 + l16) * PQ + kk * 32 + lq * 8), acc);
     const int j = cb * 16 + l16;
-    const float lj = sm.lg[j];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = rb * 16 + lq * 4 + i;
-      const float dec = j <= r ? __expf(sm.lg[r] - lj) : 0.f;
+      // KDA: the decay is already inside the product; above the diagonal the product
+      // is not a decayed one, so it is dropped by selection, never multiplied by 0
+      const float val = KDA ? (j <= r ? acc[i] : 0.f) : (j <= r ? __expf(sm.lg[r] - sm.lg[j]) : 0.f) * acc[i];
       if (sc)
-        sm.A[r * PC + j] = f32_to_bf16(dec * acc[i]);
+        sm.A[r * PC + j] = f32_to_bf16(val);
       else
-        sm.rl.L[r * PF + j] = j < r ? sm.bt[r] * dec * acc[i] : 0.f;
+        sm.rl.L[r * PF + j] = j < r ? sm.bt[r] * val : 0.f;
     }
   }
   {   // the zero upper tiles that the 32-wide contraction slices of A reach: (0,1), (2,3)
@@ -266,6 +368,16 @@ __device__ __forceinline__ void prep_chunk(PrepSmem& sm, PrepIn& in, int cid, co
     sm.A[(t * 32 + (e >> 4)) * PC + t * 32 + 16 + (e & 15)] = 0;
   }
   lds_barrier();
+  if constexpr (KDA) {   // K <- K o exp(b) (the key operand of W), this thread's 4 x 4 block
+    const int tq = tid >> 5, c0 = 4 * (tid & 31);
+    const f32x4 em = *reinterpret_cast<const f32x4*>(&xs.em[c0]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      u32x2* kp = reinterpret_cast<u32x2*>(sm.K + (4 * tq + i) * PQ + c0);
+      const u32x2 kw = *kp;
+      *kp = u32x2{pack_bf16(lo_bf(kw.x) * em[0], hi_bf(kw.x) * em[1]), pack_bf16(lo_bf(kw.y) * em[2], hi_bf(kw.y) * em[3])};
+    }
+  }
 
   // ---- T = (I + L)^-1. Diagonal blocks: wave w -> block w >> 1, columns
   // (w & 1) * 8 + 2 * (lane >> 4) + {0, 1}; lane & 15 is the row.
@@ -373,14 +485,23 @@ __device__ __forceinline__ void prep_chunk(PrepSmem& sm, PrepIn& in, int cid, co
         t1 = mfma(ld8(sm.rl.Wt + (ks * 32 + 16 + l16) * PC + js * 32 + lq * 8), b, t1);
       }
       const int r = rb * 16 + l16;
-      const float gr = sm.g[r];
       const u32x2 qa = *reinterpret_cast<const u32x2*>(sm.Q + r * PQ + ks * 32 + lq * 4);
       const u32x2 qb = *reinterpret_cast<const u32x2*>(sm.Q + r * PQ + ks * 32 + 16 + lq * 4);
+      // GDN: g_r per token; KDA: exp(b_m) per channel (Q holds Q o exp(b - b_m))
+      f32x4 fa, fb;
+      if constexpr (KDA) {
+        fa = *reinterpret_cast<const f32x4*>(&xs.em[ks * 32 + lq * 4]);
+        fb = *reinterpret_cast<const f32x4*>(&xs.em[ks * 32 + 16 + lq * 4]);
+      } else {
+        const float gr = sm.g[r];
+        fa = f32x4{gr, gr, gr, gr};
+        fb = fa;
+      }
       *reinterpret_cast<u32x4*>(wsc + kWsQ + ((size_t)(rb * 4 + ks) * 64 + lane) * 16) =
-          u32x4{pack_bf16(gr * lo_bf(qa.x) - t0[0], gr * hi_bf(qa.x) - t0[1]),
-                pack_bf16(gr * lo_bf(qa.y) - t0[2], gr * hi_bf(qa.y) - t0[3]),
-                pack_bf16(gr * lo_bf(qb.x) - t1[0], gr * hi_bf(qb.x) - t1[1]),
-                pack_bf16(gr * lo_bf(qb.y) - t1[2], gr * hi_bf(qb.y) - t1[3])};
+          u32x4{pack_bf16(fa[0] * lo_bf(qa.x) - t0[0], fa[1] * hi_bf(qa.x) - t0[1]),
+                pack_bf16(fa[2] * lo_bf(qa.y) - t0[2], fa[3] * hi_bf(qa.y) - t0[3]),
+                pack_bf16(fb[0] * lo_bf(qb.x) - t1[0], fb[1] * hi_bf(qb.x) - t1[1]),
+                pack_bf16(fb[2] * lo_bf(qb.y) - t1[2], fb[3] * hi_bf(qb.y) - t1[3])};
     }
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {   // O~ tile (rb, vb = wave)
@@ -402,19 +523,21 @@ __device__ __forceinline__ void prep_chunk(PrepSmem& sm, PrepIn& in, int cid, co
 // loaded into registers while this one is processed, and every thread issues the
 // same loads and stores on every chunk so that those waits are exact (the first chunk
 // is peeled, so that the loop's waits do not also serve the loads issued before it).
+template <bool KDA>
 __global__ __launch_bounds__(512) void gdn_chunk_prep_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, uint8_t* __restrict__ ws,
     int T, int nchunks) {
   using namespace gdc;
   __shared__ PrepSmem sm;
+  __shared__ KdaPrepSmem<KDA> xs;
   const int nc = T / C;
-  PrepIn in;
+  PrepIn<KDA> in;
   int cid = blockIdx.x;   // the grid never exceeds nchunks
-  prep_fetch(in, q, k, v, alpha, beta, (size_t)(cid / nc) * T + (size_t)(cid % nc) * C);
-  prep_chunk(sm, in, cid, q, k, v, alpha, beta, ws, T, nchunks);
+  prep_fetch<KDA>(in, q, k, v, alpha, beta, (size_t)(cid / nc) * T + (size_t)(cid % nc) * C);
+  prep_chunk<KDA>(sm, xs, in, cid, q, k, v, alpha, beta, ws, T, nchunks);
   for (cid += gridDim.x; cid < nchunks; cid += gridDim.x)
-    prep_chunk(sm, in, cid, q, k, v, alpha, beta, ws, T, nchunks);
+    prep_chunk<KDA>(sm, xs, in, cid, q, k, v, alpha, beta, ws, T, nchunks);
 }
 
 // ------------------------------------------------------------------ sequential pass
@@ -445,7 +568,7 @@ struct Prefetch {
 // The loads of a set are issued in two parts (PART 0: the W or Q' fragments; PART 1:
 // the rest) at two points of a chunk, so that the address units work through them
 // while the waves compute instead of holding the waves at a burst of loads.
-template <int NVB, int PART>
+template <int NVB, int PART, bool KDA>
 __device__ __forceinline__ void fetch_chunk(Prefetch<NVB>& pf, const uint8_t* __restrict__ wsc,
                                             const uint8_t* __restrict__ warm, int vt) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -463,7 +586,8 @@ __device__ __forceinline__ void fetch_chunk(Prefetch<NVB>& pf, const uint8_t* __
 #pragma unroll
   for (int js = 0; js < 2; ++js)
     pf.kh[js] = *reinterpret_cast<const u32x4*>(wsc + kWsK + ((size_t)(wave * 2 + js) * 64 + lane) * 16);
-  pf.gc = *reinterpret_cast<const float*>(wsc + kWsG + (lane & 15) * 4);
+  // the state decay of this lane's key column (GDN: one value, stored 16 times)
+  pf.gc = *reinterpret_cast<const float*>(wsc + kWsG + (KDA ? wave * 16 + (lane & 15) : (lane & 15)) * 4);
   // L2 warm-up of a later chunk: the 8 / NVB value tiles of one sequence split its 384
   // lines of W, Q' and K^ (48 NVB each) and each touches the 32 NVB lines of its own
   // U~, O~; the remaining threads all touch one line
@@ -504,7 +628,7 @@ __device__ __forceinline__ void store_o(const uint16_t* __restrict__ Ot, uint16_
 // chunk's operands are loaded again; the first chunk, FIRST, has nothing to store) so
 // that the wait for `pf` counts exactly the memory operations issued after it instead
 // of waiting for them.
-template <int VT, bool FIRST>
+template <int VT, bool FIRST, bool KDA>
 __device__ __forceinline__ void gdn_seq_chunk(SeqSmem<VT>& sm, const Prefetch<VT / 16>& pf,
                                               Prefetch<VT / 16>& nx, f32x4 (&Sacc)[VT / 16],
                                               int& cur, unsigned& sink, int ci, int nc, size_t chunk0,
@@ -515,9 +639,9 @@ __device__ __forceinline__ void gdn_seq_chunk(SeqSmem<VT>& sm, const Prefetch<VT
   const int l16 = lane & 15, lq = lane >> 4;
   const int rb = wave & 3, kcol = wave * 16 + l16, v0 = vt * VT;
   const bool role_o = wave >= 4;
-  const uint8_t* nxc = ws + (chunk0 + min(ci + kAhead, nc - 1)) * kWsChunk;
-  const uint8_t* wmc = ws + (chunk0 + min(ci + kAhead + kWarm, nc - 1)) * kWsChunk;
-  fetch_chunk<NVB, 0>(nx, nxc, wmc, vt);
+  const uint8_t* nxc = ws + (chunk0 + min(ci + kAhead, nc - 1)) * ws_chunk<KDA>();
+  const uint8_t* wmc = ws + (chunk0 + min(ci + kAhead + kWarm, nc - 1)) * ws_chunk<KDA>();
+  fetch_chunk<NVB, 0, KDA>(nx, nxc, wmc, vt);
   sink ^= pf.warm;
   if constexpr (!FIRST) store_o<VT>(sm.Ot[(ci - 1) & 1], o, tok0 - C, v0);
 
@@ -543,7 +667,7 @@ __device__ __forceinline__ void gdn_seq_chunk(SeqSmem<VT>& sm, const Prefetch<VT
         u32x2{pack_bf16(lo_bf(xv.x) + sgn * acc[0], hi_bf(xv.x) + sgn * acc[1]),
               pack_bf16(lo_bf(xv.y) + sgn * acc[2], hi_bf(xv.y) + sgn * acc[3])};
   }
-  fetch_chunk<NVB, 1>(nx, nxc, wmc, vt);
+  fetch_chunk<NVB, 1, KDA>(nx, nxc, wmc, vt);
   lds_barrier();
 
   // ---- S <- g_C S + U^T K^: key block = wave; next bf16 copy
@@ -563,7 +687,7 @@ __device__ __forceinline__ void gdn_seq_chunk(SeqSmem<VT>& sm, const Prefetch<VT
 
 }  // namespace gdc
 
-template <int VT>
+template <int VT, bool KDA>
 __global__ __launch_bounds__(512) void gdn_chunk_seq_kernel(
     const uint8_t* __restrict__ ws, const float* __restrict__ S0, float* __restrict__ ST,
     uint16_t* __restrict__ o, int N, int T) {
@@ -612,24 +736,24 @@ __global__ __launch_bounds__(512) void gdn_chunk_seq_kernel(
     unsigned sink = 0;
 #pragma unroll
     for (int i = 0; i < kAhead; ++i) {
-      const uint8_t* ci_ = ws + (chunk0 + min(i, nc - 1)) * kWsChunk;
-      const uint8_t* wi_ = ws + (chunk0 + min(i + kWarm, nc - 1)) * kWsChunk;
-      fetch_chunk<NVB, 0>(P[i], ci_, wi_, vt);
-      fetch_chunk<NVB, 1>(P[i], ci_, wi_, vt);
+      const uint8_t* ci_ = ws + (chunk0 + min(i, nc - 1)) * ws_chunk<KDA>();
+      const uint8_t* wi_ = ws + (chunk0 + min(i + kWarm, nc - 1)) * ws_chunk<KDA>();
+      fetch_chunk<NVB, 0, KDA>(P[i], ci_, wi_, vt);
+      fetch_chunk<NVB, 1, KDA>(P[i], ci_, wi_, vt);
     }
     lds_barrier();
-    gdn_seq_chunk<VT, true>(sm, P[0], P[kAhead], Sacc, cur, sink, 0, nc, chunk0, tokn, vt, ws, o);
+    gdn_seq_chunk<VT, true, KDA>(sm, P[0], P[kAhead], Sacc, cur, sink, 0, nc, chunk0, tokn, vt, ws, o);
     int ci = 1;
     for (; ci + NS - 1 < nc; ci += NS) {
 #pragma unroll
       for (int u = 0; u < NS; ++u)
-        gdn_seq_chunk<VT, false>(sm, P[(1 + u) % NS], P[(1 + u + kAhead) % NS], Sacc, cur, sink, ci + u, nc,
+        gdn_seq_chunk<VT, false, KDA>(sm, P[(1 + u) % NS], P[(1 + u + kAhead) % NS], Sacc, cur, sink, ci + u, nc,
                                  chunk0, tokn + (size_t)(ci + u) * C, vt, ws, o);
     }
 #pragma unroll
     for (int u = 0; u < NS - 1; ++u)
       if (ci + u < nc)
-        gdn_seq_chunk<VT, false>(sm, P[(1 + u) % NS], P[(1 + u + kAhead) % NS], Sacc, cur, sink, ci + u, nc,
+        gdn_seq_chunk<VT, false, KDA>(sm, P[(1 + u) % NS], P[(1 + u + kAhead) % NS], Sacc, cur, sink, ci + u, nc,
                                  chunk0, tokn + (size_t)(ci + u) * C, vt, ws, o);
     store_o<VT>(sm.Ot[(nc - 1) & 1], o, tokn + (size_t)(nc - 1) * C, v0);
     asm volatile("" ::"v"(sink));   // keeps the warm-up loads
@@ -646,60 +770,92 @@ __global__ __launch_bounds__(512) void gdn_chunk_seq_kernel(
 
 using namespace gdnrt;
 
-extern "C" size_t gdn_chunk_fwd_workspace_bytes(int N, int T, int dk, int dv, int chunk) {
+namespace {
+
+template <bool KDA>
+size_t chunk_workspace_bytes(int N, int T, int dk, int dv, int chunk) {
   if (N <= 0 || T <= 0 || dk != kD || dv != kD || chunk != kChunk || T % kChunk) return 0;
-  return (size_t)N * (T / kChunk) * gdc::kWsChunk;
+  return (size_t)N * (T / kChunk) * gdc::ws_chunk<KDA>();
+}
+
+template <bool KDA>
+int chunk_fwd(const char* fn, const void* q, const void* k, const void* v, const float* alpha,
+              const float* beta, const float* S0, float* ST, void* o, int N, int T, int dk, int dv,
+              int chunk, int io, void* workspace, size_t ws_bytes, void* stream) {
+  if (N < 0 || T < 0) return set_error(GDNRT_ESHAPE, "%s: N=%d T=%d must be >= 0", fn, N, T);
+  if (dk != kD || dv != kD)
+    return set_error(GDNRT_ESHAPE, "%s: d_k=%d d_v=%d, only 128 is supported", fn, dk, dv);
+  if (chunk != kChunk) return set_error(GDNRT_ESHAPE, "%s: chunk=%d, only 64 is supported", fn, chunk);
+  if (T % kChunk) return set_error(GDNRT_ESHAPE, "%s: T=%d is not a multiple of 64", fn, T);
+  if (io != GDNRT_BF16) return set_error(GDNRT_EDTYPE, "%s: io must be GDNRT_BF16", fn);
+  if ((size_t)N * (T / kChunk) > 0x7fffffffu || (size_t)N * 8 > 0x7fffffffu)
+    return set_error(GDNRT_ESHAPE, "%s: N=%d T=%d too large", fn, N, T);
+  if (N == 0) return clear_error();
+  if (!ST || (T > 0 && (!q || !k || !v || !alpha || !beta || !o)))
+    return set_error(GDNRT_EINVAL, "%s: null pointer argument", fn);
+  const size_t nchunks = (size_t)N * (T / kChunk);
+  const size_t need = nchunks * gdc::ws_chunk<KDA>();
+  if (ws_bytes < need || (need && !workspace))
+    return set_error(GDNRT_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
+  if ((T > 0 && (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(workspace) ||
+                 (KDA ? !aligned16(alpha) : !aligned4(alpha)) || !aligned4(beta))) ||
+      !aligned4(ST) || (S0 && !aligned4(S0)))
+    return set_error(GDNRT_EALIGN, KDA ? "%s: q, k, v, o, alpha, workspace must be 16-byte aligned"
+                                       : "%s: q, k, v, o, workspace must be 16-byte aligned", fn);
+  const size_t ntok = (size_t)N * T, nIO = ntok * kD * 2, nG = ntok * 4 * (KDA ? kD : 1),
+               nS = (size_t)N * kD * kD * 4;
+  if (overlaps(o, nIO, q, nIO) || overlaps(o, nIO, k, nIO) || overlaps(o, nIO, v, nIO) ||
+      overlaps(o, nIO, alpha, nG) || overlaps(o, nIO, beta, ntok * 4) || overlaps(o, nIO, ST, nS) ||
+      overlaps(o, nIO, S0, nS) || overlaps(o, nIO, workspace, need) ||
+      overlaps(ST, nS, q, nIO) || overlaps(ST, nS, k, nIO) || overlaps(ST, nS, v, nIO) ||
+      overlaps(ST, nS, workspace, need) || (S0 && S0 != ST && overlaps(ST, nS, S0, nS)) ||
+      overlaps(workspace, need, q, nIO) || overlaps(workspace, need, k, nIO) ||
+      overlaps(workspace, need, v, nIO) || overlaps(workspace, need, S0, nS) ||
+      overlaps(workspace, need, alpha, nG))
+    return set_error(GDNRT_EINVAL, "%s: buffers overlap (only ST may equal S0)", fn);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  if (T > 0) {
+    // one persistent block per CU (the LDS of a block fills most of one)
+    const unsigned grid = (unsigned)(nchunks < 256 ? nchunks : 256);
+    hipLaunchKernelGGL(gdn_chunk_prep_kernel<KDA>, dim3(grid), dim3(gdc::NT), 0, s,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                       static_cast<const uint16_t*>(v), alpha, beta, ws, T, (int)nchunks);
+    int rc = check_launch(fn);
+    if (rc != GDNRT_OK) return rc;
+  }
+  // value tiles of 16 when there are too few sequences to fill the chip with 32
+  if (N * 4 < 256)
+    hipLaunchKernelGGL((gdn_chunk_seq_kernel<16, KDA>), dim3((unsigned)(N * 8)), dim3(gdc::NT), 0, s, ws, S0,
+                       ST, static_cast<uint16_t*>(o), N, T);
+  else
+    hipLaunchKernelGGL((gdn_chunk_seq_kernel<32, KDA>), dim3((unsigned)(N * 4)), dim3(gdc::NT), 0, s, ws, S0,
+                       ST, static_cast<uint16_t*>(o), N, T);
+  return check_launch(fn);
+}
+
+}  // namespace
+
+extern "C" size_t gdn_chunk_fwd_workspace_bytes(int N, int T, int dk, int dv, int chunk) {
+  return chunk_workspace_bytes<false>(N, T, dk, dv, chunk);
 }
 
 extern "C" int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
                              const float* beta, const float* S0, float* ST, void* o, int N, int T,
                              int dk, int dv, int chunk, int io, void* workspace, size_t ws_bytes,
                              void* stream) {
-  if (N < 0 || T < 0) return set_error(GDNRT_ESHAPE, "gdn_chunk_fwd: N=%d T=%d must be >= 0", N, T);
-  if (dk != kD || dv != kD)
-    return set_error(GDNRT_ESHAPE, "gdn_chunk_fwd: d_k=%d d_v=%d, only 128 is supported", dk, dv);
-  if (chunk != kChunk) return set_error(GDNRT_ESHAPE, "gdn_chunk_fwd: chunk=%d, only 64 is supported", chunk);
-  if (T % kChunk) return set_error(GDNRT_ESHAPE, "gdn_chunk_fwd: T=%d is not a multiple of 64", T);
-  if (io != GDNRT_BF16) return set_error(GDNRT_EDTYPE, "gdn_chunk_fwd: io must be GDNRT_BF16");
-  if ((size_t)N * (T / kChunk) > 0x7fffffffu || (size_t)N * 8 > 0x7fffffffu)
-    return set_error(GDNRT_ESHAPE, "gdn_chunk_fwd: N=%d T=%d too large", N, T);
-  if (N == 0) return clear_error();
-  if (!ST || (T > 0 && (!q || !k || !v || !alpha || !beta || !o)))
-    return set_error(GDNRT_EINVAL, "gdn_chunk_fwd: null pointer argument");
-  const size_t nchunks = (size_t)N * (T / kChunk);
-  const size_t need = nchunks * gdc::kWsChunk;
-  if (ws_bytes < need || (need && !workspace))
-    return set_error(GDNRT_EINVAL, "gdn_chunk_fwd: workspace of %zu bytes needed, %zu given", need, ws_bytes);
-  if ((T > 0 && (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(workspace) ||
-                 !aligned4(alpha) || !aligned4(beta))) ||
-      !aligned4(ST) || (S0 && !aligned4(S0)))
-    return set_error(GDNRT_EALIGN, "gdn_chunk_fwd: q, k, v, o, workspace must be 16-byte aligned");
-  const size_t ntok = (size_t)N * T, nIO = ntok * kD * 2, nG = ntok * 4, nS = (size_t)N * kD * kD * 4;
-  if (overlaps(o, nIO, q, nIO) || overlaps(o, nIO, k, nIO) || overlaps(o, nIO, v, nIO) ||
-      overlaps(o, nIO, alpha, nG) || overlaps(o, nIO, beta, nG) || overlaps(o, nIO, ST, nS) ||
-      overlaps(o, nIO, S0, nS) || overlaps(o, nIO, workspace, need) ||
-      overlaps(ST, nS, q, nIO) || overlaps(ST, nS, k, nIO) || overlaps(ST, nS, v, nIO) ||
-      overlaps(ST, nS, workspace, need) || (S0 && S0 != ST && overlaps(ST, nS, S0, nS)) ||
-      overlaps(workspace, need, q, nIO) || overlaps(workspace, need, k, nIO) ||
-      overlaps(workspace, need, v, nIO) || overlaps(workspace, need, S0, nS))
-    return set_error(GDNRT_EINVAL, "gdn_chunk_fwd: buffers overlap (only ST may equal S0)");
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  if (T > 0) {
-    // one persistent block per CU (the LDS of a block fills most of one)
-    const unsigned grid = (unsigned)(nchunks < 256 ? nchunks : 256);
-    hipLaunchKernelGGL(gdn_chunk_prep_kernel, dim3(grid), dim3(gdc::NT), 0, s,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                       static_cast<const uint16_t*>(v), alpha, beta, ws, T, (int)nchunks);
-    int rc = check_launch("gdn_chunk_fwd (prep)");
-    if (rc != GDNRT_OK) return rc;
-  }
-  // value tiles of 16 when there are too few sequences to fill the chip with 32
-  if (N * 4 < 256)
-    hipLaunchKernelGGL((gdn_chunk_seq_kernel<16>), dim3((unsigned)(N * 8)), dim3(gdc::NT), 0, s, ws, S0,
-                       ST, static_cast<uint16_t*>(o), N, T);
-  else
-    hipLaunchKernelGGL((gdn_chunk_seq_kernel<32>), dim3((unsigned)(N * 4)), dim3(gdc::NT), 0, s, ws, S0,
-                       ST, static_cast<uint16_t*>(o), N, T);
-  return check_launch("gdn_chunk_fwd");
+  return chunk_fwd<false>("gdn_chunk_fwd", q, k, v, alpha, beta, S0, ST, o, N, T, dk, dv, chunk, io,
+                          workspace, ws_bytes, stream);
+}
+
+extern "C" size_t kda_chunk_fwd_workspace_bytes(int N, int T, int dk, int dv, int chunk) {
+  return chunk_workspace_bytes<true>(N, T, dk, dv, chunk);
+}
+
+extern "C" int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
+                             const float* beta, const float* S0, float* ST, void* o, int N, int T,
+                             int dk, int dv, int chunk, int io, void* workspace, size_t ws_bytes,
+                             void* stream) {
+  return chunk_fwd<true>("kda_chunk_fwd", q, k, v, alpha, beta, S0, ST, o, N, T, dk, dv, chunk, io,
+                         workspace, ws_bytes, stream);
 }

@@ -94,6 +94,30 @@ def gdn_prefill(B=1, H=32, T=16384, d=D, device="cpu", seed=1002, S0_std=0.0):
 CHUNK_STEPS = 256
 
 
+def kda_prefill(B=1, H=32, T=16384, d=D, device="cpu", seed=1008, S0_std=0.0):
+    """Kimi Delta Attention chunkwise prefill: the GDN prefill workload's shape and
+    draws, with one decay per key channel and token, alpha = sigmoid(N(4,1))
+    ([N][T][d_k] fp32, drawn 1024 tokens at a time)."""
+    g = _gen(device, seed)
+    N = B * H
+    q = torch.empty((N, T, d), dtype=torch.bfloat16, device=device)
+    k = torch.empty_like(q)
+    v = torch.empty_like(q)
+    for x, norm in ((q, True), (k, True), (v, False)):
+        for t0 in range(0, T, 1024):
+            t1 = min(T, t0 + 1024)
+            c = _randn((N, t1 - t0, d), g, device)
+            x[:, t0:t1] = (_l2n(c) if norm else c).to(torch.bfloat16)
+    alpha = torch.empty((N, T, d), dtype=torch.float32, device=device)
+    for t0 in range(0, T, 1024):
+        t1 = min(T, t0 + 1024)
+        alpha[:, t0:t1] = torch.sigmoid(_randn((N, t1 - t0, d), g, device, 4.0, 1.0))
+    beta = torch.sigmoid(_randn((N, T), g, device, 0.0, 1.0))
+    S0 = (_randn((N, d, d), g, device, 0.0, S0_std) if S0_std > 0
+          else torch.zeros((N, d, d), device=device, dtype=torch.float32))
+    return dict(q=q, k=k, v=v, alpha=alpha, beta=beta, S0=S0)
+
+
 def _decode_tokens(steps, N, d, g, device, io):
     """q, k (L2-normalised) and v for ``steps`` decode steps, drawn in chunks of
     256 steps (q chunks, then k chunks, then v chunks) so that long runs need no

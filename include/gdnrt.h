@@ -144,6 +144,37 @@ GDNRT_API int gdn_chunk_fwd(const void* q, const void* k, const void* v,
 GDNRT_API size_t gdn_chunk_fwd_workspace_bytes(int N, int T, int dk, int dv, int chunk);
 
 /*
+ * Kimi Delta Attention chunkwise forward (prefill): the recurrence of
+ * kda_decode_step (one decay per key channel; LeapQuant page, section "The state,
+ * from the update rule up", eq. 1 / eq. 3) over T tokens, per chunk of 64 tokens
+ * through the UT form of gdn_chunk_fwd with the decay inside the key and query
+ * products (derived by unrolling eq. 3 within a chunk; the pages print no chunk
+ * form). With b_r the cumulative log-decay per key channel within the chunk and
+ * Gamma_r = exp(b_r):
+ *   (I + L) U = diag(beta) V - diag(beta) (K o Gamma) S_0^T,
+ *       L[r,j] = beta_r sum_c k_r[c] k_j[c] exp(b_r[c] - b_j[c]) (j < r),
+ *   O = (Q o Gamma) S_0^T + A U,  A[r,j] = sum_c q_r[c] k_j[c] exp(b_r[c] - b_j[c]) (j <= r),
+ *   S_C = S_0 Diag(Gamma_C) + U^T (K o exp(b_C - b)).
+ *
+ *   q, k [N][T][dk] bf16, v, o [N][T][dv] bf16 (as gdn_chunk_fwd).
+ *   alpha [N][T][dk] fp32 in (0, 1), 16-byte aligned; beta [N][T] fp32.
+ *   S0, ST, workspace as gdn_chunk_fwd, workspace of kda_chunk_fwd_workspace_bytes()
+ *   bytes (82,432 per chunk: the per-channel chunk decay Gamma_C takes 512 bytes).
+ * The products are formed relative to the chunk's middle token, so exp(|b_r - b_m|)
+ * must stay within fp32 range: the log-decays of any 32 consecutive tokens of a
+ * channel must sum to more than -88 (e.g. every alpha above 0.064).
+ * T must be a multiple of chunk (64).
+ */
+GDNRT_API int kda_chunk_fwd(const void* q, const void* k, const void* v,
+                            const float* alpha, const float* beta,
+                            const float* S0, float* ST, void* o,
+                            int N, int T, int dk, int dv, int chunk, int io,
+                            void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace bytes kda_chunk_fwd needs for this shape (0 if unsupported or empty). */
+GDNRT_API size_t kda_chunk_fwd_workspace_bytes(int N, int T, int dk, int dv, int chunk);
+
+/*
  * LeapQuant windowed 8-bit state ("LeapQuant: an 8-bit recurrent state that stops
  * rounding every token": section "Fix one: leap over a window" eq. 4 and eq. 10,
  * section "Fix two: pull the outliers out as tokens" eq. 5, section "Fix three:

@@ -34,7 +34,7 @@ def test_header_declares_the_entry_points():
     for n in ("gdn_decode_step", "gla_chunk_fwd", "gdn_chunk_fwd", "leapq_decode_step",
               "leapq_window_flush", "gdnrt_last_error", "gdn_chunk_fwd_workspace_bytes",
               "gla_chunk_fwd_workspace_bytes", "kda_decode_step", "kda_leapq_decode_step",
-              "kda_leapq_window_flush"):
+              "kda_leapq_window_flush", "kda_chunk_fwd", "kda_chunk_fwd_workspace_bytes"):
         assert n in names, n
 
 
@@ -133,3 +133,16 @@ def test_kda_leapq_validation(lib):
     assert fl(ctypes.byref(st), 17, None, p, 1, 0, None, None) == ESTATE
     assert fl(ctypes.byref(st), 0, None, None, 1, 0, None, None) == EINVAL   # q0 missing
     assert fl(ctypes.byref(_state(lib, buf_a=4100)), 0, None, p, 1, 0, None, None) == EALIGN
+
+
+def test_kda_chunk_validation(lib):
+    p = ctypes.c_void_p(4096)
+    f = lib.kda_chunk_fwd
+    assert lib.kda_chunk_fwd_workspace_bytes(32, 16384, 128, 128, 64) == 32 * 256 * 82432
+    assert lib.kda_chunk_fwd_workspace_bytes(32, 100, 128, 128, 64) == 0
+    assert f(p, p, p, p, p, None, p, p, 2, 128, 128, 128, 64, 1, p, 10, None) == EINVAL      # workspace
+    assert f(p, p, p, p, p, None, p, p, 2, 96, 128, 128, 64, 1, p, 1 << 30, None) == ESHAPE  # T % 64
+    # the per-channel decays are read 16 bytes at a time
+    assert f(p, p, p, ctypes.c_void_p(4100), p, None, p, p, 2, 128, 128, 128, 64, 1, p, 1 << 30,
+             None) == EALIGN
+    assert "kda_chunk_fwd" in _err(lib)
