@@ -23,6 +23,10 @@ Pins (tests/test_oracle_gla.py): with zero log-gates the output is the textbook
 causal linear attention tril(Q K^T) V + Q S_0^T; eq. 6 (final state from S_0 is
 the decayed S_0 plus the state from zero); the decay acts on key columns; one
 token from zero gives v (k . q); chunk form == recurrence for C in {1, 16, 64}.
+``gla_recurrent_bwd`` (reverse mode through the recurrence) is pinned by torch
+autograd of a separately written forward, by central differences, by the textbook
+gradients of causal linear attention at zero log-gates, and by ZeCO's chunk-level
+state-gradient recurrence and the gate-gradient identity.
 """
 from __future__ import annotations
 
@@ -73,3 +77,52 @@ def gla_chunk(q, k, v, log_g, S0=None, chunk=64):
         o[:, sl] = np.einsum("nrk,nvk->nrv", Qt, S) + np.einsum("nrj,njv->nrv", A, v[:, sl])
         S = np.exp(b[:, -1])[:, None, :] * S + np.einsum("njv,njk->nvk", v[:, sl], Kg)
     return o, S
+
+
+def gla_recurrent_bwd(q, k, v, log_g, S0, dO, dST=None, ckpt=64):
+    """Gradients of the per-token recurrence ``gla_recurrent`` by reverse-mode
+    differentiation token by token, in fp64: for the scalar
+    L = sum(dO o o) + sum(dST o S_T), returns (dq, dk, dv, dlog_g, dS0).
+
+    Going backward with dS the gradient of L with respect to S_t:
+        dS   += do_t q_t^T                    (o_t = S_t q_t)
+        dq_t  = S_t^T do_t
+        dv_t  = dS k_t,   dk_t = dS^T v_t     (S_t = ... + v_t k_t^T)
+        dg_t  = sum_v dS o exp(g_t) o S_{t-1} (per key column)
+        dS    = exp(g_t) o dS                 (-> gradient with respect to S_{t-1})
+    and dS0 is the final dS. The states S_{t-1}, S_t are recomputed forward from
+    checkpoints every ``ckpt`` tokens (no division by decays). ZeCO's backward
+    (section "The Backward Algorithm and Gradient Flow") states the chunk-level
+    form of the dS recurrence, dS = gamma o dS + Q~^T dO; a test checks it.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    lg = np.asarray(log_g, np.float64)
+    dO = np.asarray(dO, np.float64)
+    N, T, dk = k.shape
+    dv = v.shape[2]
+    S = np.zeros((N, dv, dk)) if S0 is None else np.array(S0, dtype=np.float64, copy=True)
+    marks = {}
+    for t in range(T):
+        if t % ckpt == 0:
+            marks[t] = S.copy()
+        S = np.exp(lg[:, t])[:, None, :] * S + v[:, t][:, :, None] * k[:, t][:, None, :]
+    dS = np.zeros((N, dv, dk)) if dST is None else np.array(dST, dtype=np.float64, copy=True)
+    dq, dk_, dv_, dg = (np.empty_like(q), np.empty_like(k), np.empty_like(v), np.empty_like(lg))
+    for c0 in (range(((T - 1) // ckpt) * ckpt, -1, -ckpt) if T else ()):
+        c1 = min(T, c0 + ckpt)
+        states = [marks[c0]]                              # S_{c0-1}, S_{c0}, ..., S_{c1-1}
+        for t in range(c0, c1):
+            states.append(np.exp(lg[:, t])[:, None, :] * states[-1]
+                          + v[:, t][:, :, None] * k[:, t][:, None, :])
+        for t in range(c1 - 1, c0 - 1, -1):
+            St, Sp = states[t - c0 + 1], states[t - c0]
+            dS = dS + dO[:, t][:, :, None] * q[:, t][:, None, :]
+            dq[:, t] = np.einsum("nvk,nv->nk", St, dO[:, t])
+            dv_[:, t] = np.einsum("nvk,nk->nv", dS, k[:, t])
+            dk_[:, t] = np.einsum("nvk,nv->nk", dS, v[:, t])
+            e = np.exp(lg[:, t])
+            dg[:, t] = np.einsum("nvk,nvk->nk", dS, Sp) * e
+            dS = e[:, None, :] * dS
+    return dq, dk_, dv_, dg, dS

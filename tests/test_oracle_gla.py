@@ -99,3 +99,104 @@ def test_shards_chain_like_one_call():
     ob, Sb = gla.gla_recurrent(q[:, h:], k[:, h:], v[:, h:], lg[:, h:], Sa)
     np.testing.assert_allclose(np.concatenate([oa, ob], 1), o, atol=1e-12)
     np.testing.assert_allclose(Sb, S, atol=1e-12)
+
+
+# ------------------------------------------------------------------ backward
+
+def _loss_grads_torch(q, k, v, lg, S0, dO, dST):
+    """Gradients by torch autograd (float64, CPU) of a separately written torch
+    forward of the recurrence: an independent derivation of the same gradients."""
+    import torch
+    t = [torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v, lg, S0)]
+    tq, tk, tv, tg, tS = t
+    S = tS
+    outs = []
+    for i in range(q.shape[1]):
+        S = torch.exp(tg[:, i])[:, None, :] * S + tv[:, i][:, :, None] * tk[:, i][:, None, :]
+        outs.append(torch.einsum("nvk,nk->nv", S, tq[:, i]))
+    o = torch.stack(outs, 1)
+    L = (o * torch.tensor(dO)).sum() + (S * torch.tensor(dST)).sum()
+    L.backward()
+    return [x.grad.numpy() for x in t]
+
+
+def test_backward_equals_autograd():
+    rng = np.random.default_rng(41)
+    N, T, d = 2, 40, 8
+    q, k, v, lg = _rand(rng, N, T, d)
+    S0, dST = rng.standard_normal((2, N, d, d))
+    dO = rng.standard_normal((N, T, d))
+    got = gla.gla_recurrent_bwd(q, k, v, lg, S0, dO, dST, ckpt=16)
+    ref = _loss_grads_torch(q, k, v, lg, S0, dO, dST)
+    for g_, r_, name in zip(got, ref, ("dq", "dk", "dv", "dg", "dS0")):
+        np.testing.assert_allclose(g_, r_, rtol=0, atol=1e-10 * np.abs(r_).max(), err_msg=name)
+
+
+def test_backward_finite_differences():
+    """Central differences of L = sum(dO o o) + sum(dST o S_T) on a tiny case."""
+    rng = np.random.default_rng(42)
+    N, T, d = 1, 6, 3
+    q, k, v, lg = _rand(rng, N, T, d)
+    S0, dST = rng.standard_normal((2, N, d, d))
+    dO = rng.standard_normal((N, T, d))
+
+    def L(q_, k_, v_, g_, S_):
+        o, ST = gla.gla_recurrent(q_, k_, v_, g_, S_)
+        return float((o * dO).sum() + (ST * dST).sum())
+
+    grads = gla.gla_recurrent_bwd(q, k, v, lg, S0, dO, dST)
+    args = [q, k, v, lg, S0]
+    h = 1e-6
+    for ai, g_ in enumerate(grads):
+        x = args[ai]
+        num = np.empty_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            ap, am = list(args), list(args)
+            ap[ai], am[ai] = xp, xm
+            num[idx] = (L(*ap) - L(*am)) / (2 * h)
+        np.testing.assert_allclose(g_, num, rtol=0, atol=1e-6 * max(1.0, np.abs(num).max()))
+
+
+def test_backward_zero_gates_textbook():
+    """g = 0: O = tril(Q K^T) V + Q S0^T, so dQ = tril(dO V^T) K + dO S0,
+    dK = tril(dO V^T)^T Q, dV = tril(Q K^T)^T dO, dS0 = dO^T Q (dST = 0)."""
+    rng = np.random.default_rng(43)
+    N, T, d = 2, 24, 8
+    q, k, v, _ = _rand(rng, N, T, d)
+    S0 = rng.standard_normal((N, d, d))
+    dO = rng.standard_normal((N, T, d))
+    dq, dk, dv, dg, dS0 = gla.gla_recurrent_bwd(q, k, v, np.zeros((N, T, d)), S0, dO)
+    P = np.tril(np.einsum("ntv,njv->ntj", dO, v))
+    np.testing.assert_allclose(dq, P @ k + np.einsum("ntv,nvk->ntk", dO, S0), atol=1e-10)
+    np.testing.assert_allclose(dk, np.swapaxes(P, 1, 2) @ q, atol=1e-10)
+    np.testing.assert_allclose(dv, np.swapaxes(np.tril(np.einsum("ntk,njk->ntj", q, k)), 1, 2) @ dO, atol=1e-10)
+    np.testing.assert_allclose(dS0, np.einsum("ntv,ntk->nvk", dO, q), atol=1e-10)
+
+
+def test_backward_zeco_chunk_state_gradient():
+    """ZeCO's backward, phase 1: per chunk in reverse, dS <- gamma o dS + Q~^T dO
+    (in this orientation dS <- exp(b_C) o dS + dO^T (Q o exp(b))) gives the
+    gradient with respect to the incoming state; and the gate gradient follows
+    from dq and dk: with b the cumulative log-gate over the sequence, q o exp(b)
+    and k o exp(-b) are what b enters, so dL/db_t = q_t o dq_t - k_t o dk_t
+    (+ sum_v dST o S_T at the last token) and dg is its reverse cumulative sum."""
+    rng = np.random.default_rng(44)
+    N, T, d, C = 2, 128, 8, 32
+    q, k, v, lg = _rand(rng, N, T, d)
+    S0, dST = rng.standard_normal((2, N, d, d))
+    dO = rng.standard_normal((N, T, d))
+    dq, dk, dv, dg, dS0 = gla.gla_recurrent_bwd(q, k, v, lg, S0, dO, dST)
+    dS = dST.copy()
+    for c0 in range(T - C, -1, -C):
+        sl = slice(c0, c0 + C)
+        b = np.cumsum(lg[:, sl], axis=1)
+        dS = np.exp(b[:, -1])[:, None, :] * dS + np.einsum("ntv,ntk->nvk", dO[:, sl], q[:, sl] * np.exp(b))
+    np.testing.assert_allclose(dS0, dS, rtol=0, atol=1e-10 * np.abs(dS).max())
+    _, ST = gla.gla_recurrent(q, k, v, lg, S0)
+    db = q * dq - k * dk
+    db[:, -1] += np.einsum("nvk,nvk->nk", dST, ST)
+    np.testing.assert_allclose(dg, np.cumsum(db[:, ::-1], axis=1)[:, ::-1], rtol=0,
+                               atol=1e-9 * np.abs(dg).max())
