@@ -1,6 +1,6 @@
 """Benchmark of the gated delta-rule hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--rows decode,kda,leapq,kda_leapq,gla,gdn,kda_chunk]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--rows decode,kda,leapq,kda_leapq,gla,gla_bwd,gdn,kda_chunk]
 
 Headline (`value`): Gated DeltaNet decode of one layer, 512 streams x 32 heads,
 d_k = d_v = 128, fp32 state resident in HBM, bf16 q/k/v; one step = one token for
@@ -256,6 +256,46 @@ def bench_gla(K=20, W=3, B=4, H=16, T=4096):
     return res
 
 
+def gla_bwd_work(C=64):
+    """Algorithmic FLOPs of one chunk of the GLA backward: the forward state recompute
+    (V^T K^) and the state-gradient scan (dO^T Q^), then A and dA (lower), dQ^ = dO S_b,
+    dQ~ = dA K~ and dK~ = dA^T Q~ (triangular), dK^ = V dS_a, dV = A^T dO + K^ dS_a^T."""
+    tri = C * (C + 1) // 2
+    full, low = 2 * C * D * D, 2 * tri * D
+    return 2 * full + (2 * low + full + 2 * low + full + low + full)
+
+
+def bench_gla_bwd(K=10, W=2, B=4, H=16, T=4096):
+    N = B * H
+    log(f"[gla_bwd] generating B={B} H={H} T={T}")
+    inp = synth.gla_prefill(B=B, H=H, T=T, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(77)
+    dO = torch.randn(inp["q"].shape, generator=g, device="cuda").to(torch.bfloat16)
+    dST = 0.1 * torch.randn(inp["S0"].shape, generator=g, device="cuda")
+    ws = m.gla_chunk_bwd_workspace(N, T)
+    out = (torch.empty_like(inp["q"]), torch.empty_like(inp["k"]), torch.empty_like(inp["v"]),
+           torch.empty_like(inp["log_g"]), torch.empty_like(inp["S0"]))
+
+    def run(i):
+        m.gla_chunk_bwd(inp["q"], inp["k"], inp["v"], inp["log_g"], dO, inp["S0"], dST, ws, out)
+
+    ms, wall = timed(run, K, W)
+    chunks = N * T // 64
+    flops = gla_bwd_work() * chunks
+    # reads q, k, v, dO (bf16), gates (fp32), S0, dST; writes dq, dk, dv (bf16), d gates, dS0
+    byts = N * T * D * (4 * 2 + 4 + 3 * 2 + 4) + 3 * N * D * D * 4
+    res = dict(workload=f"gla_chunk_bwd B={B} H={H} T={T} d=128 chunk 64: gradients of q, k, v, log-gates "
+                        f"and the incoming state, bf16 in and out, fp32 gates",
+               ms=ms, tokens_per_s=B * T / (ms * 1e-3), gflop=flops / 1e9,
+               tflops=flops / (ms * 1e-3) / 1e12, bytes=byts, achieved_gbs=byts / (ms * 1e-3) / 1e9,
+               workspace_bytes=int(ws.numel()), wall_s=wall)
+    res["frac_hbm"] = res["achieved_gbs"] / PEAK_HBM_GBS
+    res["frac_mfma"] = res["tflops"] / PEAK_BF16_TFLOPS
+    res["roofline_bound"] = "hbm"
+    del inp, ws, out
+    return res
+
+
 def gdn_chunk_work(C=64):
     """Algorithmic FLOPs of one chunk of one head in the UT / WY form: Gram k.k
     (strict lower), triangular inverse (C^3/3 multiply-adds), scores q.k (lower),
@@ -353,7 +393,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--rows", default="decode,kda,leapq,kda_leapq,gla,gdn,kda_chunk")
+    ap.add_argument("--rows", default="decode,kda,leapq,kda_leapq,gla,gla_bwd,gdn,kda_chunk")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the measured HBM-copy and bf16-GEMM ceilings")
@@ -410,6 +450,12 @@ def main():
         r["traffic_bytes"] = tp + ts if tp is not None and ts is not None else None
         out_rows["gdn_chunk"] = r
         log(f"[gdn_chunk] {r['ms']*1e3:.1f} us  {r['tflops']:.1f} TFLOP/s ({r['frac_mfma']*100:.1f}% MFMA)  "
+            f"{r['achieved_gbs']:.0f} GB/s ({r['frac_hbm']*100:.1f}% HBM)  {r['tokens_per_s']/1e6:.2f} M tok/s")
+        torch.cuda.empty_cache()
+    if "gla_bwd" in rows:
+        r = bench_gla_bwd()
+        out_rows["gla_bwd"] = r
+        log(f"[gla_bwd] {r['ms']*1e3:.1f} us  {r['tflops']:.1f} TFLOP/s ({r['frac_mfma']*100:.1f}% MFMA)  "
             f"{r['achieved_gbs']:.0f} GB/s ({r['frac_hbm']*100:.1f}% HBM)  {r['tokens_per_s']/1e6:.2f} M tok/s")
         torch.cuda.empty_cache()
     if "kda_chunk" in rows:

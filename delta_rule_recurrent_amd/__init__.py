@@ -1,7 +1,7 @@
 """MI355X-native gated delta-rule recurrent state update.
 
 Entry points over the gdnrt HIP library (C ABI in include/gdnrt.h):
-``gdn_decode_step``, ``gla_chunk_fwd``, ``gdn_chunk_fwd``, ``leapq_decode_step``,
+``gdn_decode_step``, ``gla_chunk_fwd``, ``gla_chunk_bwd``, ``gdn_chunk_fwd``, ``leapq_decode_step``,
 ``leapq_window_flush``, ``kda_decode_step``, ``kda_chunk_fwd``,
 ``kda_leapq_decode_step`` and ``kda_leapq_window_flush``. ``synth`` draws the seeded synthetic workloads.
 """
@@ -11,6 +11,8 @@ from .binding import (  # noqa: F401
     gdn_chunk_fwd,
     gdn_chunk_workspace,
     gdn_decode_step,
+    gla_chunk_bwd,
+    gla_chunk_bwd_workspace,
     gla_chunk_fwd,
     gla_chunk_workspace,
     kda_chunk_fwd,

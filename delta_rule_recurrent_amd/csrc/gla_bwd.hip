@@ -1,0 +1,419 @@
+// Gated linear attention, chunkwise backward of one sequence shard.
+//
+// Method: "ZeCO: Zero Communication Overhead Sequence Parallelism for Linear
+// Attention", section "The Backward Algorithm and Gradient Flow": the state gradient
+// runs backward over the chunks, dS <- gamma o dS + Q~^T dO, and each chunk's
+// gradients combine an intra-chunk part (through its attention matrix) and an
+// inter-chunk part (through the states). In the [d_v][d_k] layout, with b the
+// inclusive cumulative log-gate inside a chunk of C = 64 tokens, b_m its value at
+// token 31 and b_C at token 63, the forward of a chunk is
+//
+//   Q^ = Q o e^b, K^ = K o e^{b_C - b}, Q~ = Q o e^{b - b_m}, K~ = K o e^{b_m - b},
+//   A = (Q~ K~^T) o M,  O = Q^ S_b^T + A V,  S_a = e^{b_C} o S_b + V^T K^
+//
+// (S_b the state before the chunk, S_a after), so with dS_a the gradient with respect
+// to S_a and dO given:
+//
+//   dS_b = e^{b_C} o dS_a + dO^T Q^                         (the backward state scan)
+//   dA = (dO V^T) o M,  dQ^ = dO S_b,  dQ~ = dA K~,  dK~ = dA^T Q~,  dK^ = V dS_a,
+//   dq = (dQ^ e^{b_m} + dQ~) e^{b - b_m},   dk = (dK~ + dK^ e^{b_C - b_m}) e^{b_m - b},
+//   dv = A^T dO + K^ dS_a^T.
+//
+// The gate gradient uses that b enters only through q o e^B and k o e^{-B} (B the
+// cumulative log-gate over the whole sequence): dL/dB_t = q_t o dq_t - k_t o dk_t,
+// plus sum_v dS_T o S_T at the last token, and d log_g is its reverse cumulative sum.
+//
+// Six kernels: a per-chunk prep (cumulative gates, the scaled operands), a forward
+// state scan (the state before every chunk), a backward state scan (the gradient after
+// every chunk, and dS_0), a per-chunk gradient kernel (bf16 MFMA, fp32 accumulation),
+// and the reverse cumulative sum for the gates in two per-chunk passes.
+#include "common.hpp"
+
+namespace gdnrt {
+
+namespace glab {
+
+constexpr int C = kChunk;    // 64
+constexpr int PT = kD + 16;  // bf16 pitch of 128-wide rows read transposed
+constexpr int PA = C + 16;   // bf16 pitch of 64-wide rows read transposed
+constexpr int PX = 16 + 16;  // bf16 pitch of 16-wide rows (one value tile) read transposed
+
+// Workspace per chunk (bytes): bf16 [64][128] Q^, K^, Q~, K~; fp32 [64][128]
+// E = e^{b - b_m}; fp32 [128] e^{b_C}, e^{b_m}, e^{b_C - b_m}; bf16 [128][128] the
+// state before the chunk and the state gradient after it. Then per sequence the fp32
+// final state of the recomputed forward.
+constexpr size_t kQh = 0, kKh = 16384, kQt = 32768, kKt = 49152, kE = 65536, kEC = 98304,
+                 kEm = 98816, kECm = 99328, kSb = 99840, kdS = 132608, kChunkB = 165376;
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// MFMA operand from a row-major [contraction][column] bf16 matrix in LDS through the
+// transposing LDS read: lane (l16, lq) receives X[c0 + 8 lq + e][n0 + l16], e = 0..7.
+__device__ __forceinline__ bf16x8 ld_tr8(const uint16_t* X, int pitch, int c0, int n0) {
+  const int lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
+  const uint16_t* p = X + (c0 + 8 * g + (j >> 2)) * pitch + n0 + 4 * (j & 3);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * pitch));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+}  // namespace glab
+
+// ------------------------------------------------------------------ prep
+// One block of 256 threads per chunk: thread (c = tid % 128, h = tid / 128) sums the
+// log-gates of channel c over tokens 32 h .. 32 h + 31.
+__global__ __launch_bounds__(256) void gla_bwd_prep_kernel(const uint16_t* __restrict__ q,
+                                                           const uint16_t* __restrict__ k,
+                                                           const float* __restrict__ log_g,
+                                                           uint8_t* __restrict__ ws, int T) {
+  using namespace glab;
+  __shared__ float tot[2][kD];
+  const int tid = threadIdx.x, c = tid & (kD - 1), h = tid >> 7;
+  const int nc = T / C, cid = blockIdx.x;
+  const size_t tok0 = (size_t)(cid / nc) * T + (size_t)(cid % nc) * C + 32 * h;
+  uint8_t* wsc = ws + (size_t)cid * kChunkB;
+  float gv[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) gv[i] = log_g[(tok0 + i) * kD + c];
+  float run = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    run += gv[i];
+    gv[i] = run;   // prefix within the half
+  }
+  tot[h][c] = run;
+  lds_barrier();
+  const float base = h ? tot[0][c] : 0.f, bm = tot[0][c], bC = tot[0][c] + tot[1][c];
+  uint16_t* Qh = reinterpret_cast<uint16_t*>(wsc + kQh);
+  uint16_t* Kh = reinterpret_cast<uint16_t*>(wsc + kKh);
+  uint16_t* Qt = reinterpret_cast<uint16_t*>(wsc + kQt);
+  uint16_t* Kt = reinterpret_cast<uint16_t*>(wsc + kKt);
+  float* E = reinterpret_cast<float*>(wsc + kE);
+#pragma unroll 8
+  for (int i = 0; i < 32; ++i) {
+    const int t = 32 * h + i;
+    const float b = base + gv[i];
+    const float qv = bf16_to_f32(q[(tok0 + i) * kD + c]), kv = bf16_to_f32(k[(tok0 + i) * kD + c]);
+    const float e = __expf(b - bm);
+    Qh[t * kD + c] = f32_to_bf16(qv * __expf(b));
+    Kh[t * kD + c] = f32_to_bf16(kv * __expf(bC - b));
+    Qt[t * kD + c] = f32_to_bf16(qv * e);
+    Kt[t * kD + c] = f32_to_bf16(kv * __expf(bm - b));
+    E[t * kD + c] = e;
+  }
+  if (h == 0) {
+    reinterpret_cast<float*>(wsc + kEC)[c] = __expf(bC);
+    reinterpret_cast<float*>(wsc + kEm)[c] = __expf(bm);
+    reinterpret_cast<float*>(wsc + kECm)[c] = __expf(bC - bm);
+  }
+}
+
+// ------------------------------------------------------------------ state scans
+// One block of 256 threads per (sequence, value tile of 16 rows); wave w owns key
+// columns [32 w, 32 w + 32) as two 16 x 16 accumulator tiles (lane holds rows
+// 4 lq + i, column 32 w + 16 j + l16). Per chunk (forward: first to last; reverse: last
+// to first) the state is stored in bf16 to the workspace, then
+//   forward:  S  <- e^{b_C} o S  + V^T K^     (X = V,  Y = K^)
+//   reverse:  dS <- e^{b_C} o dS + dO^T Q^    (X = dO, Y = Q^).
+// The next chunk's X and Y are loaded into registers while this one is computed.
+template <bool REV>
+__global__ __launch_bounds__(256) void gla_bwd_scan_kernel(const uint16_t* __restrict__ X,
+                                                           uint8_t* __restrict__ ws,
+                                                           const float* __restrict__ Sinit,
+                                                           float* __restrict__ Sout, int T) {
+  using namespace glab;
+  __shared__ __attribute__((aligned(16))) uint16_t sx[C * PX];
+  __shared__ __attribute__((aligned(16))) uint16_t sy[C * PT];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, lq = lane >> 4;
+  const int n = blockIdx.x >> 3, v0 = (blockIdx.x & 7) * 16;
+  const int nc = T / C;
+  const size_t chunk0 = (size_t)n * nc;
+  const size_t soff = REV ? kQh : kKh;   // Y: Q^ (reverse) or K^ (forward)
+  f32x4 acc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc[j][i] = Sinit ? Sinit[((size_t)n * kD + v0 + 4 * lq + i) * kD + 32 * w + 16 * j + l16] : 0.f;
+
+  // thread's pieces: X row tid / 4, values 4 (tid % 4) ..; Y 16-byte pieces tid + 256 p
+  auto load = [&](int ci, u32x2& xr, u32x4 (&yr)[4], float (&ec)[2]) {
+    const size_t tok = (size_t)n * T + (size_t)ci * C;
+    xr = *reinterpret_cast<const u32x2*>(X + (tok + (tid >> 2)) * kD + v0 + 4 * (tid & 3));
+    const uint8_t* wsc = ws + (chunk0 + ci) * kChunkB;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) yr[p] = *reinterpret_cast<const u32x4*>(wsc + soff + (size_t)(tid + 256 * p) * 16);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) ec[j] = reinterpret_cast<const float*>(wsc + kEC)[32 * w + 16 * j + l16];
+  };
+  u32x2 xr;
+  u32x4 yr[4];
+  float ec[2];
+  if (nc > 0) load(REV ? nc - 1 : 0, xr, yr, ec);
+  for (int s = 0; s < nc; ++s) {
+    const int ci = REV ? nc - 1 - s : s;
+    // this chunk's state (forward) or state gradient (reverse), in bf16
+    uint16_t* dst = reinterpret_cast<uint16_t*>(ws + (chunk0 + ci) * kChunkB + (REV ? kdS : kSb));
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[(v0 + 4 * lq + i) * kD + 32 * w + 16 * j + l16] = f32_to_bf16(acc[j][i]);
+    *reinterpret_cast<u32x2*>(sx + (tid >> 2) * PX + 4 * (tid & 3)) = xr;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int e = (tid + 256 * p) * 8;   // element index in [64][128]
+      *reinterpret_cast<u32x4*>(sy + (e >> 7) * PT + (e & 127)) = yr[p];
+    }
+    const float e0 = ec[0], e1 = ec[1];
+    if (s + 1 < nc) load(REV ? ci - 1 : ci + 1, xr, yr, ec);
+    lds_barrier();
+    acc[0] *= e0;
+    acc[1] *= e1;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 a = ld_tr8(sx, PX, 32 * ks, 0);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[j] = mfma(a, ld_tr8(sy, PT, 32 * ks, 32 * w + 16 * j), acc[j]);
+    }
+    lds_barrier();
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Sout[((size_t)n * kD + v0 + 4 * lq + i) * kD + 32 * w + 16 * j + l16] = acc[j][i];
+}
+
+// ------------------------------------------------------------------ gradients
+// One block of 512 threads (8 waves) per chunk.
+struct alignas(16) GradSmem {
+  uint16_t Qt[kChunk * glab::PT], Kt[kChunk * glab::PT], dO[kChunk * glab::PT];   // [t][128]
+  uint16_t Sb[kD * glab::PT], dS[kD * glab::PT];                                 // [v][c]
+  uint16_t A[kChunk * glab::PA], dA[kChunk * glab::PA];                          // [r][j], upper tiles zero
+};
+
+__global__ __launch_bounds__(512) void gla_bwd_grad_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dO, const uint8_t* __restrict__ ws, uint16_t* __restrict__ dq,
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, float* __restrict__ db, int T) {
+  using namespace glab;
+  __shared__ GradSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, lq = lane >> 4;
+  const int nc = T / C, cid = blockIdx.x;
+  const size_t tok0 = (size_t)(cid / nc) * T + (size_t)(cid % nc) * C;
+  const uint8_t* wsc = ws + (size_t)cid * kChunkB;
+
+  // ---- stage: Q~, K~, dO rows ([64][128]: 1024 pieces of 16 bytes each), the state
+  // before the chunk and the gradient after it ([128][128]: 2048 pieces each); zeros
+  // for A and dA
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int e = (tid + 512 * p) * 8, r = e >> 7, cc = e & 127;
+    *reinterpret_cast<u32x4*>(sm.Qt + r * PT + cc) = *reinterpret_cast<const u32x4*>(wsc + kQt + (size_t)e * 2);
+    *reinterpret_cast<u32x4*>(sm.Kt + r * PT + cc) = *reinterpret_cast<const u32x4*>(wsc + kKt + (size_t)e * 2);
+    *reinterpret_cast<u32x4*>(sm.dO + r * PT + cc) = *reinterpret_cast<const u32x4*>(dO + (tok0 + r) * kD + cc);
+  }
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int e = (tid + 512 * p) * 8, r = e >> 7, cc = e & 127;
+    *reinterpret_cast<u32x4*>(sm.Sb + r * PT + cc) = *reinterpret_cast<const u32x4*>(wsc + kSb + (size_t)e * 2);
+    *reinterpret_cast<u32x4*>(sm.dS + r * PT + cc) = *reinterpret_cast<const u32x4*>(wsc + kdS + (size_t)e * 2);
+  }
+  for (int e = tid; e < C * PA / 2; e += 512) {
+    reinterpret_cast<uint32_t*>(sm.A)[e] = 0u;
+    reinterpret_cast<uint32_t*>(sm.dA)[e] = 0u;
+  }
+  lds_barrier();
+
+  // ---- A = (Q~ K~^T) o M and dA = (dO V^T) o M: 10 lower tiles each
+  for (int u = w; u < 20; u += 8) {
+    const int p = u >> 1;
+    const int rb = p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3, cb = p - (rb * (rb + 1)) / 2;
+    const bool grad = u & 1;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (grad)
+        acc = mfma(ld8(sm.dO + (16 * rb + l16) * PT + 32 * ks + 8 * lq),
+                   ld8(v + (tok0 + 16 * cb + l16) * kD + 32 * ks + 8 * lq), acc);
+      else
+        acc = mfma(ld8(sm.Qt + (16 * rb + l16) * PT + 32 * ks + 8 * lq),
+                   ld8(sm.Kt + (16 * cb + l16) * PT + 32 * ks + 8 * lq), acc);
+    }
+    uint16_t* dst = grad ? sm.dA : sm.A;
+    const int j = 16 * cb + l16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * rb + 4 * lq + i;
+      dst[r * PA + j] = f32_to_bf16(j <= r ? acc[i] : 0.f);
+    }
+  }
+  lds_barrier();
+
+  // ---- output tiles (rb, cb): rows t = 16 rb + 4 lq + i, columns 16 cb + l16
+  const float* E = reinterpret_cast<const float*>(wsc + kE);
+  const float* em = reinterpret_cast<const float*>(wsc + kEm);
+  const float* ecm = reinterpret_cast<const float*>(wsc + kECm);
+  const uint16_t* Kh = reinterpret_cast<const uint16_t*>(wsc + kKh);
+  const int rb = w & 3;
+#pragma unroll 1
+  for (int u = 0; u < 4; ++u) {
+    const int cb = (w >> 2) * 4 + u;
+    const int col = 16 * cb + l16;
+    f32x4 dQh = {0.f, 0.f, 0.f, 0.f}, dQt = dQh, dKt = dQh, dKh = dQh, dV = dQh;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      dQh = mfma(ld8(sm.dO + (16 * rb + l16) * PT + 32 * ks + 8 * lq), ld_tr8(sm.Sb, PT, 32 * ks, 16 * cb), dQh);
+      dKh = mfma(ld8(v + (tok0 + 16 * rb + l16) * kD + 32 * ks + 8 * lq), ld_tr8(sm.dS, PT, 32 * ks, 16 * cb), dKh);
+      dV = mfma(ld8(Kh + (16 * rb + l16) * kD + 32 * ks + 8 * lq), ld8(sm.dS + (16 * cb + l16) * PT + 32 * ks + 8 * lq), dV);
+    }
+#pragma unroll
+    for (int js = 0; js < 2; ++js) {
+      if (js <= rb / 2)   // dA[t][j] is zero for j > t
+        dQt = mfma(ld8(sm.dA + (16 * rb + l16) * PA + 32 * js + 8 * lq), ld_tr8(sm.Kt, PT, 32 * js, 16 * cb), dQt);
+      if (32 * js + 31 >= 16 * rb) {   // dA[r][t], A[r][t] are zero for r < t
+        dKt = mfma(ld_tr8(sm.dA, PA, 32 * js, 16 * rb), ld_tr8(sm.Qt, PT, 32 * js, 16 * cb), dKt);
+        dV = mfma(ld_tr8(sm.A, PA, 32 * js, 16 * rb), ld_tr8(sm.dO, PT, 32 * js, 16 * cb), dV);
+      }
+    }
+    const float emc = em[col], ecmc = ecm[col];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * rb + 4 * lq + i;
+      const size_t g = (tok0 + t) * kD + col;
+      const float e = E[t * kD + col];
+      const float gq = (dQh[i] * emc + dQt[i]) * e;
+      const float gk = (dKt[i] + dKh[i] * ecmc) / e;
+      dq[g] = f32_to_bf16(gq);
+      dk[g] = f32_to_bf16(gk);
+      dv[g] = f32_to_bf16(dV[i]);
+      db[g] = bf16_to_f32(q[g]) * gq - bf16_to_f32(k[g]) * gk;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ gate gradient
+// d log_g is the reverse cumulative sum over the sequence of dL/dB (in place), the last
+// token also carrying sum_v dS_T o S_T. Two passes of one block of 128 threads (one per
+// key channel) per chunk: the reverse sums within the chunk and the chunk's total, then
+// every later chunk's total added.
+__global__ __launch_bounds__(128) void gla_bwd_gate_chunk_kernel(float* __restrict__ dg,
+                                                                 float* __restrict__ totals,
+                                                                 const float* __restrict__ dST,
+                                                                 const float* __restrict__ ST, int T) {
+  const int c = threadIdx.x, nc = T / kChunk, cid = blockIdx.x, n = cid / nc, ci = cid % nc;
+  float acc = 0.f;
+  if (dST && ci == nc - 1) {
+    const size_t base = (size_t)n * kD * kD + c;
+#pragma unroll 8
+    for (int r = 0; r < kD; ++r) acc += dST[base + (size_t)r * kD] * ST[base + (size_t)r * kD];
+  }
+  float* p = dg + ((size_t)n * T + (size_t)ci * kChunk) * kD + c;
+  float x[kChunk];
+#pragma unroll
+  for (int t = 0; t < kChunk; ++t) x[t] = p[(size_t)t * kD];
+#pragma unroll
+  for (int t = kChunk - 1; t >= 0; --t) {
+    acc += x[t];
+    p[(size_t)t * kD] = acc;
+  }
+  totals[(size_t)cid * kD + c] = acc;
+}
+
+__global__ __launch_bounds__(128) void gla_bwd_gate_offset_kernel(float* __restrict__ dg,
+                                                                  const float* __restrict__ totals, int T) {
+  const int c = threadIdx.x, nc = T / kChunk, cid = blockIdx.x, n = cid / nc, ci = cid % nc;
+  float off = 0.f;
+  for (int j = nc - 1; j > ci; --j) off += totals[((size_t)n * nc + j) * kD + c];
+  if (ci == nc - 1) return;
+  float* p = dg + ((size_t)n * T + (size_t)ci * kChunk) * kD + c;
+#pragma unroll 16
+  for (int t = 0; t < kChunk; ++t) p[(size_t)t * kD] += off;
+}
+
+}  // namespace gdnrt
+
+using namespace gdnrt;
+
+extern "C" size_t gla_chunk_bwd_workspace_bytes(int N, int T, int dk, int dv, int chunk) {
+  if (N <= 0 || T <= 0 || dk != kD || dv != kD || chunk != kChunk || T % kChunk) return 0;
+  // per chunk the operands and states, then per sequence the recomputed final state,
+  // then per chunk the gate-gradient totals
+  return (size_t)N * (T / kChunk) * (glab::kChunkB + kD * 4) + (size_t)N * kD * kD * 4;
+}
+
+extern "C" int gla_chunk_bwd(const void* q, const void* k, const void* v, const float* log_g,
+                             const float* S0, const void* dO, const float* dST, void* dq, void* dk,
+                             void* dv, float* dlog_g, float* dS0, int N, int T, int dk_, int dv_,
+                             int chunk, int io, void* workspace, size_t ws_bytes, void* stream) {
+  const char* fn = "gla_chunk_bwd";
+  if (N < 0 || T < 0) return set_error(GDNRT_ESHAPE, "%s: N=%d T=%d must be >= 0", fn, N, T);
+  if (dk_ != kD || dv_ != kD) return set_error(GDNRT_ESHAPE, "%s: d_k=%d d_v=%d, only 128 is supported", fn, dk_, dv_);
+  if (chunk != kChunk) return set_error(GDNRT_ESHAPE, "%s: chunk=%d, only 64 is supported", fn, chunk);
+  if (T % kChunk) return set_error(GDNRT_ESHAPE, "%s: T=%d is not a multiple of 64", fn, T);
+  if (io != GDNRT_BF16) return set_error(GDNRT_EDTYPE, "%s: io must be GDNRT_BF16", fn);
+  if ((size_t)N * (T / kChunk) > 0x7fffffffu) return set_error(GDNRT_ESHAPE, "%s: N=%d T=%d too large", fn, N, T);
+  if (N == 0) return clear_error();
+  if (!dS0 || (T > 0 && (!q || !k || !v || !log_g || !dO || !dq || !dk || !dv || !dlog_g)))
+    return set_error(GDNRT_EINVAL, "%s: null pointer argument", fn);
+  const size_t nchunks = (size_t)N * (T / kChunk);
+  const size_t need = nchunks * (glab::kChunkB + kD * 4) + (size_t)N * kD * kD * 4;
+  if (ws_bytes < need || !workspace)
+    return set_error(GDNRT_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
+  if ((T > 0 && (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned16(log_g) ||
+                 !aligned4(dq) || !aligned4(dk) || !aligned4(dv) || !aligned4(dlog_g))) ||
+      !aligned16(workspace) || !aligned4(dS0) || (S0 && !aligned4(S0)) || (dST && !aligned4(dST)))
+    return set_error(GDNRT_EALIGN, "%s: q, k, v, dO, log_g, workspace must be 16-byte aligned", fn);
+  const size_t ntok = (size_t)N * T, nIO = ntok * kD * 2, nG = ntok * kD * 4, nS = (size_t)N * kD * kD * 4;
+  const void* ins[] = {q, k, v, dO};
+  const void* outs[] = {dq, dk, dv};
+  for (const void* a : outs) {
+    for (const void* b : ins)
+      if (overlaps(a, nIO, b, nIO)) return set_error(GDNRT_EINVAL, "%s: a gradient overlaps an input", fn);
+    for (const void* b : outs)
+      if (a != b && overlaps(a, nIO, b, nIO)) return set_error(GDNRT_EINVAL, "%s: gradients overlap", fn);
+    if (overlaps(a, nIO, dlog_g, nG) || overlaps(a, nIO, workspace, need) || overlaps(a, nIO, log_g, nG))
+      return set_error(GDNRT_EINVAL, "%s: buffers overlap", fn);
+  }
+  for (const void* b : ins)
+    if (overlaps(dlog_g, nG, b, nIO) || overlaps(workspace, need, b, nIO) || overlaps(dS0, nS, b, nIO))
+      return set_error(GDNRT_EINVAL, "%s: buffers overlap", fn);
+  if (overlaps(dlog_g, nG, log_g, nG) || overlaps(dlog_g, nG, workspace, need) ||
+      overlaps(workspace, need, log_g, nG) || overlaps(dS0, nS, workspace, need) ||
+      overlaps(dS0, nS, dlog_g, nG) || overlaps(workspace, need, S0, nS) || overlaps(workspace, need, dST, nS))
+    return set_error(GDNRT_EINVAL, "%s: buffers overlap", fn);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* ST = reinterpret_cast<float*>(ws + nchunks * glab::kChunkB);   // recomputed final states
+  if (T > 0) {
+    hipLaunchKernelGGL(gla_bwd_prep_kernel, dim3((unsigned)nchunks), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), log_g, ws, T);
+    int rc = check_launch(fn);
+    if (rc != GDNRT_OK) return rc;
+  }
+  hipLaunchKernelGGL(gla_bwd_scan_kernel<false>, dim3((unsigned)(N * 8)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(v), ws, S0, ST, T);
+  hipLaunchKernelGGL(gla_bwd_scan_kernel<true>, dim3((unsigned)(N * 8)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(dO), ws, dST, dS0, T);
+  if (T > 0) {
+    hipLaunchKernelGGL(gla_bwd_grad_kernel, dim3((unsigned)nchunks), dim3(512), 0, s,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dO), ws,
+                       static_cast<uint16_t*>(dq), static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv),
+                       dlog_g, T);
+    float* totals = ST + (size_t)N * kD * kD;
+    hipLaunchKernelGGL(gla_bwd_gate_chunk_kernel, dim3((unsigned)nchunks), dim3(128), 0, s, dlog_g, totals,
+                       dST, ST, T);
+    hipLaunchKernelGGL(gla_bwd_gate_offset_kernel, dim3((unsigned)nchunks), dim3(128), 0, s, dlog_g,
+                       totals, T);
+  }
+  return check_launch(fn);
+}

@@ -115,6 +115,32 @@ GDNRT_API int gla_chunk_fwd(const void* q, const void* k, const void* v, const f
 GDNRT_API size_t gla_chunk_fwd_workspace_bytes(int N, int T, int dk, int dv, int chunk);
 
 /*
+ * Gated linear attention, chunkwise backward of one sequence shard ("ZeCO: Zero
+ * Communication Overhead Sequence Parallelism for Linear Attention", section "The
+ * Backward Algorithm and Gradient Flow": the state gradient flows backward over the
+ * chunks, dS <- gamma o dS + Q~^T dO, and each chunk combines its intra-chunk and
+ * inter-chunk gradients). For the forward of gla_chunk_fwd from S0 and the scalar
+ * L = sum(dO o o) + sum(dST o S_T), writes
+ *   dq, dk [N][T][dk], dv [N][T][dv] (bf16), dlog_g [N][T][dk] (fp32) and dS0
+ *   [N][dv][dk] (fp32, the gradient with respect to the incoming state).
+ *   q, k, v, dO [N][T][d] bf16 and log_g fp32: 16-byte aligned. S0, dST may be NULL
+ *   (zero). workspace: gla_chunk_bwd_workspace_bytes() bytes, 16-byte aligned,
+ *   overwritten (per chunk the scaled operands, the state before the chunk and the
+ *   state gradient after it, in bf16, and the gate-gradient totals: 165,888 bytes; per
+ *   sequence the recomputed final state).
+ * The gate gradient is the reverse cumulative sum of q o dq - k o dk (plus dST o S_T
+ * summed over value channels at the last token). T must be a multiple of 64.
+ */
+GDNRT_API int gla_chunk_bwd(const void* q, const void* k, const void* v, const float* log_g,
+                            const float* S0, const void* dO, const float* dST,
+                            void* dq, void* dk, void* dv, float* dlog_g, float* dS0,
+                            int N, int T, int dk_, int dv_, int chunk, int io,
+                            void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace bytes gla_chunk_bwd needs for this shape (0 if unsupported or empty). */
+GDNRT_API size_t gla_chunk_bwd_workspace_bytes(int N, int T, int dk, int dv, int chunk);
+
+/*
  * Gated DeltaNet chunkwise forward (prefill): the same recurrence as
  * gdn_decode_step over T tokens, computed per chunk of 64 tokens through the
  * UT / WY form of the intra-chunk delta rule (derived from eq. 3 of the LeapQuant

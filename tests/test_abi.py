@@ -34,7 +34,8 @@ def test_header_declares_the_entry_points():
     for n in ("gdn_decode_step", "gla_chunk_fwd", "gdn_chunk_fwd", "leapq_decode_step",
               "leapq_window_flush", "gdnrt_last_error", "gdn_chunk_fwd_workspace_bytes",
               "gla_chunk_fwd_workspace_bytes", "kda_decode_step", "kda_leapq_decode_step",
-              "kda_leapq_window_flush", "kda_chunk_fwd", "kda_chunk_fwd_workspace_bytes"):
+              "kda_leapq_window_flush", "kda_chunk_fwd", "kda_chunk_fwd_workspace_bytes",
+              "gla_chunk_bwd", "gla_chunk_bwd_workspace_bytes"):
         assert n in names, n
 
 
@@ -146,3 +147,18 @@ def test_kda_chunk_validation(lib):
     assert f(p, p, p, ctypes.c_void_p(4100), p, None, p, p, 2, 128, 128, 128, 64, 1, p, 1 << 30,
              None) == EALIGN
     assert "kda_chunk_fwd" in _err(lib)
+
+
+def test_gla_bwd_validation(lib):
+    p = ctypes.c_void_p(4096)
+    f = lib.gla_chunk_bwd
+    assert lib.gla_chunk_bwd_workspace_bytes(64, 4096, 128, 128, 64) == 64 * 64 * (165376 + 512) + 64 * 65536
+    assert lib.gla_chunk_bwd_workspace_bytes(64, 100, 128, 128, 64) == 0
+    args = lambda T, ws_bytes, **kw: [kw.get(n, p) for n in ("q", "k", "v", "g", "S0", "dO", "dST", "dq", "dk",
+                                                          "dv", "dg", "dS0")] + [2, T, 128, 128, 64, 1, p,
+                                                                                 ws_bytes, None]
+    assert f(*args(128, 10)) == EINVAL                                   # workspace too small
+    assert f(*args(96, 1 << 34)) == ESHAPE                               # T % 64
+    assert f(*args(128, 1 << 34, q=ctypes.c_void_p(4098))) == EALIGN
+    assert f(*args(128, 1 << 34, dS0=None)) == EINVAL
+    assert "gla_chunk_bwd" in _err(lib)
