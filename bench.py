@@ -345,6 +345,10 @@ def bench_gdn_chunk(K=10, W=2, B=1, H=32, T=16384, kda=False):
     return res
 
 
+GLA_BWD_KERNELS = ("gla_bwd_prep_kernel", "gla_bwd_scan_kernel<fwd>", "gla_bwd_scan_kernel<rev>",
+                   "gla_bwd_grad_kernel", "gla_bwd_gate_offset_kernel")
+
+
 def counter_traffic(kernel):
     """HBM bytes per launch measured by rocprofv3 counters (profiles/counters.json),
     or None if the kernel's sources changed since they were taken."""
@@ -454,12 +458,16 @@ def main():
         torch.cuda.empty_cache()
     if "gla_bwd" in rows:
         r = bench_gla_bwd()
+        parts = [counter_traffic(k) for k in GLA_BWD_KERNELS]
+        r["traffic_bytes"] = sum(parts) if None not in parts else None
         out_rows["gla_bwd"] = r
         log(f"[gla_bwd] {r['ms']*1e3:.1f} us  {r['tflops']:.1f} TFLOP/s ({r['frac_mfma']*100:.1f}% MFMA)  "
             f"{r['achieved_gbs']:.0f} GB/s ({r['frac_hbm']*100:.1f}% HBM)  {r['tokens_per_s']/1e6:.2f} M tok/s")
         torch.cuda.empty_cache()
     if "kda_chunk" in rows:
         r = bench_gdn_chunk(kda=True)
+        tp, ts = counter_traffic("gdn_chunk_prep_kernel<kda>"), counter_traffic("gdn_chunk_seq_kernel<kda>")
+        r["traffic_bytes"] = tp + ts if tp is not None and ts is not None else None
         out_rows["kda_chunk"] = r
         log(f"[kda_chunk] {r['ms']*1e3:.1f} us  {r['tflops']:.1f} TFLOP/s ({r['frac_mfma']*100:.1f}% MFMA)  "
             f"{r['achieved_gbs']:.0f} GB/s ({r['frac_hbm']*100:.1f}% HBM)  {r['tokens_per_s']/1e6:.2f} M tok/s")

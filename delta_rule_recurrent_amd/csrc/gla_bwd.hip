@@ -23,10 +23,11 @@
 // cumulative log-gate over the whole sequence): dL/dB_t = q_t o dq_t - k_t o dk_t,
 // plus sum_v dS_T o S_T at the last token, and d log_g is its reverse cumulative sum.
 //
-// Six kernels: a per-chunk prep (cumulative gates, the scaled operands), a forward
+// Five kernels: a per-chunk prep (cumulative gates, the scaled operands), a forward
 // state scan (the state before every chunk), a backward state scan (the gradient after
-// every chunk, and dS_0), a per-chunk gradient kernel (bf16 MFMA, fp32 accumulation),
-// and the reverse cumulative sum for the gates in two per-chunk passes.
+// every chunk, and dS_0), a per-chunk gradient kernel (bf16 MFMA, fp32 accumulation;
+// also the gates' reverse cumulative sum within the chunk), and the later chunks'
+// totals added to the gate gradient.
 #include "common.hpp"
 
 namespace gdnrt {
@@ -38,12 +39,12 @@ constexpr int PT = kD + 16;  // bf16 pitch of 128-wide rows read transposed
 constexpr int PA = C + 16;   // bf16 pitch of 64-wide rows read transposed
 constexpr int PX = 16 + 16;  // bf16 pitch of 16-wide rows (one value tile) read transposed
 
-// Workspace per chunk (bytes): bf16 [64][128] Q^, K^, Q~, K~; fp32 [64][128]
-// E = e^{b - b_m}; fp32 [128] e^{b_C}, e^{b_m}, e^{b_C - b_m}; bf16 [128][128] the
-// state before the chunk and the state gradient after it. Then per sequence the fp32
-// final state of the recomputed forward.
-constexpr size_t kQh = 0, kKh = 16384, kQt = 32768, kKt = 49152, kE = 65536, kEC = 98304,
-                 kEm = 98816, kECm = 99328, kSb = 99840, kdS = 132608, kChunkB = 165376;
+// Workspace per chunk (bytes): bf16 [64][128] Q^, K^; fp32 [64][128] E = e^{b - b_m};
+// fp32 [128] e^{b_C}, e^{b_m}, e^{b_C - b_m}; bf16 [128][128] the state before the
+// chunk and the state gradient after it. Then per sequence the fp32 final state of the
+// recomputed forward, and per chunk the fp32 [128] totals of the gate gradient.
+constexpr size_t kQh = 0, kKh = 16384, kE = 32768, kEC = 65536, kEm = 66048, kECm = 66560,
+                 kSb = 67072, kdS = 99840, kChunkB = 132608;
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -69,51 +70,74 @@ __device__ __forceinline__ bf16x8 ld_tr8(const uint16_t* X, int pitch, int c0, i
 }  // namespace glab
 
 // ------------------------------------------------------------------ prep
-// One block of 256 threads per chunk: thread (c = tid % 128, h = tid / 128) sums the
-// log-gates of channel c over tokens 32 h .. 32 h + 31.
+// One block of 256 threads per chunk: thread (cq = tid % 32, h = tid / 32) covers key
+// channels 4 cq .. 4 cq + 3 over tokens 8 h .. 8 h + 7.
 __global__ __launch_bounds__(256) void gla_bwd_prep_kernel(const uint16_t* __restrict__ q,
                                                            const uint16_t* __restrict__ k,
                                                            const float* __restrict__ log_g,
                                                            uint8_t* __restrict__ ws, int T) {
   using namespace glab;
-  __shared__ float tot[2][kD];
-  const int tid = threadIdx.x, c = tid & (kD - 1), h = tid >> 7;
+  __shared__ f32x4 tot[8][32];
+  const int tid = threadIdx.x, cq = tid & 31, h = tid >> 5, c0 = 4 * cq;
   const int nc = T / C, cid = blockIdx.x;
-  const size_t tok0 = (size_t)(cid / nc) * T + (size_t)(cid % nc) * C + 32 * h;
+  const size_t tok0 = (size_t)(cid / nc) * T + (size_t)(cid % nc) * C + 8 * h;
   uint8_t* wsc = ws + (size_t)cid * kChunkB;
-  float gv[32];
+  f32x4 gv[8];
+  u32x2 qv[8], kv[8];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) gv[i] = log_g[(tok0 + i) * kD + c];
-  float run = 0.f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    run += gv[i];
-    gv[i] = run;   // prefix within the half
+  for (int i = 0; i < 8; ++i) {
+    gv[i] = *reinterpret_cast<const f32x4*>(log_g + (tok0 + i) * kD + c0);
+    qv[i] = *reinterpret_cast<const u32x2*>(q + (tok0 + i) * kD + c0);
+    kv[i] = *reinterpret_cast<const u32x2*>(k + (tok0 + i) * kD + c0);
   }
-  tot[h][c] = run;
+  f32x4 run = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    run += gv[i];
+    gv[i] = run;   // prefix within the segment
+  }
+  tot[h][cq] = run;
   lds_barrier();
-  const float base = h ? tot[0][c] : 0.f, bm = tot[0][c], bC = tot[0][c] + tot[1][c];
+  f32x4 base = {0.f, 0.f, 0.f, 0.f}, bm = base, bC;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const f32x4 x = tot[j][cq];
+    if (j < h) base += x;
+    if (j < 4) bm += x;
+  }
+  bC = bm + tot[4][cq] + tot[5][cq] + tot[6][cq] + tot[7][cq];
   uint16_t* Qh = reinterpret_cast<uint16_t*>(wsc + kQh);
   uint16_t* Kh = reinterpret_cast<uint16_t*>(wsc + kKh);
-  uint16_t* Qt = reinterpret_cast<uint16_t*>(wsc + kQt);
-  uint16_t* Kt = reinterpret_cast<uint16_t*>(wsc + kKt);
   float* E = reinterpret_cast<float*>(wsc + kE);
-#pragma unroll 8
-  for (int i = 0; i < 32; ++i) {
-    const int t = 32 * h + i;
-    const float b = base + gv[i];
-    const float qv = bf16_to_f32(q[(tok0 + i) * kD + c]), kv = bf16_to_f32(k[(tok0 + i) * kD + c]);
-    const float e = __expf(b - bm);
-    Qh[t * kD + c] = f32_to_bf16(qv * __expf(b));
-    Kh[t * kD + c] = f32_to_bf16(kv * __expf(bC - b));
-    Qt[t * kD + c] = f32_to_bf16(qv * e);
-    Kt[t * kD + c] = f32_to_bf16(kv * __expf(bm - b));
-    E[t * kD + c] = e;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int t = 8 * h + i;
+    float qh[4], kh[4];
+    f32x4 e;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float b = base[j] + gv[i][j];
+      const float qf = bf16_to_f32(uint16_t(qv[i][j >> 1] >> (16 * (j & 1))));
+      const float kf = bf16_to_f32(uint16_t(kv[i][j >> 1] >> (16 * (j & 1))));
+      e[j] = __expf(b - bm[j]);
+      qh[j] = qf * __expf(b);
+      kh[j] = kf * __expf(bC[j] - b);
+    }
+    *reinterpret_cast<u32x2*>(Qh + t * kD + c0) = u32x2{pack_bf16(qh[0], qh[1]), pack_bf16(qh[2], qh[3])};
+    *reinterpret_cast<u32x2*>(Kh + t * kD + c0) = u32x2{pack_bf16(kh[0], kh[1]), pack_bf16(kh[2], kh[3])};
+    *reinterpret_cast<f32x4*>(E + t * kD + c0) = e;
   }
   if (h == 0) {
-    reinterpret_cast<float*>(wsc + kEC)[c] = __expf(bC);
-    reinterpret_cast<float*>(wsc + kEm)[c] = __expf(bm);
-    reinterpret_cast<float*>(wsc + kECm)[c] = __expf(bC - bm);
+    f32x4 ec, em, ecm;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ec[j] = __expf(bC[j]);
+      em[j] = __expf(bm[j]);
+      ecm[j] = __expf(bC[j] - bm[j]);
+    }
+    *reinterpret_cast<f32x4*>(wsc + kEC + 4 * c0) = ec;
+    *reinterpret_cast<f32x4*>(wsc + kEm + 4 * c0) = em;
+    *reinterpret_cast<f32x4*>(wsc + kECm + 4 * c0) = ecm;
   }
 }
 
@@ -134,7 +158,19 @@ __global__ __launch_bounds__(256) void gla_bwd_scan_kernel(const uint16_t* __res
   __shared__ __attribute__((aligned(16))) uint16_t sx[C * PX];
   __shared__ __attribute__((aligned(16))) uint16_t sy[C * PT];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, lq = lane >> 4;
-  const int n = blockIdx.x >> 3, v0 = (blockIdx.x & 7) * 16;
+  // block -> (sequence, value tile); the 8 tiles of one sequence share an XCD (blocks
+  // are dealt to the 8 XCDs round robin), so the scaled keys or queries they all read
+  // are fetched into that XCD's L2 once
+  const int bid = blockIdx.x;
+  int n, vt;
+  if ((gridDim.x & 63) == 0) {
+    n = (bid >> 6) * 8 + (bid & 7);
+    vt = (bid >> 3) & 7;
+  } else {
+    n = bid >> 3;
+    vt = bid & 7;
+  }
+  const int v0 = vt * 16;
   const int nc = T / C;
   const size_t chunk0 = (size_t)n * nc;
   const size_t soff = REV ? kQh : kKh;   // Y: Q^ (reverse) or K^ (forward)
@@ -202,8 +238,9 @@ struct alignas(16) GradSmem {
 
 __global__ __launch_bounds__(512) void gla_bwd_grad_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ dO, const uint8_t* __restrict__ ws, uint16_t* __restrict__ dq,
-    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, float* __restrict__ db, int T) {
+    const uint16_t* __restrict__ dO, const uint8_t* __restrict__ ws, const float* __restrict__ dST,
+    const float* __restrict__ ST, uint16_t* __restrict__ dq, uint16_t* __restrict__ dk,
+    uint16_t* __restrict__ dv, float* __restrict__ dg, float* __restrict__ totals, int T) {
   using namespace glab;
   __shared__ GradSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, lq = lane >> 4;
@@ -211,14 +248,25 @@ __global__ __launch_bounds__(512) void gla_bwd_grad_kernel(
   const size_t tok0 = (size_t)(cid / nc) * T + (size_t)(cid % nc) * C;
   const uint8_t* wsc = ws + (size_t)cid * kChunkB;
 
-  // ---- stage: Q~, K~, dO rows ([64][128]: 1024 pieces of 16 bytes each), the state
-  // before the chunk and the gradient after it ([128][128]: 2048 pieces each); zeros
-  // for A and dA
+  // ---- stage: Q~ = Q o E, K~ = K / E and dO rows ([64][128]: 1024 pieces of 8
+  // elements each), the state before the chunk and the gradient after it ([128][128]:
+  // 2048 pieces each); zeros for A and dA
+  const float* E = reinterpret_cast<const float*>(wsc + kE);
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     const int e = (tid + 512 * p) * 8, r = e >> 7, cc = e & 127;
-    *reinterpret_cast<u32x4*>(sm.Qt + r * PT + cc) = *reinterpret_cast<const u32x4*>(wsc + kQt + (size_t)e * 2);
-    *reinterpret_cast<u32x4*>(sm.Kt + r * PT + cc) = *reinterpret_cast<const u32x4*>(wsc + kKt + (size_t)e * 2);
+    const u32x4 qq = *reinterpret_cast<const u32x4*>(q + (tok0 + r) * kD + cc);
+    const u32x4 kk = *reinterpret_cast<const u32x4*>(k + (tok0 + r) * kD + cc);
+    const f32x4 e0 = *reinterpret_cast<const f32x4*>(E + e), e1 = *reinterpret_cast<const f32x4*>(E + e + 4);
+    u32x4 qt, kt;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float ea = j < 2 ? e0[2 * j] : e1[2 * j - 4], eb = j < 2 ? e0[2 * j + 1] : e1[2 * j - 3];
+      qt[j] = pack_bf16(bf16_to_f32(uint16_t(qq[j])) * ea, bf16_to_f32(uint16_t(qq[j] >> 16)) * eb);
+      kt[j] = pack_bf16(bf16_to_f32(uint16_t(kk[j])) / ea, bf16_to_f32(uint16_t(kk[j] >> 16)) / eb);
+    }
+    *reinterpret_cast<u32x4*>(sm.Qt + r * PT + cc) = qt;
+    *reinterpret_cast<u32x4*>(sm.Kt + r * PT + cc) = kt;
     *reinterpret_cast<u32x4*>(sm.dO + r * PT + cc) = *reinterpret_cast<const u32x4*>(dO + (tok0 + r) * kD + cc);
   }
 #pragma unroll
@@ -259,11 +307,11 @@ __global__ __launch_bounds__(512) void gla_bwd_grad_kernel(
   lds_barrier();
 
   // ---- output tiles (rb, cb): rows t = 16 rb + 4 lq + i, columns 16 cb + l16
-  const float* E = reinterpret_cast<const float*>(wsc + kE);
   const float* em = reinterpret_cast<const float*>(wsc + kEm);
   const float* ecm = reinterpret_cast<const float*>(wsc + kECm);
   const uint16_t* Kh = reinterpret_cast<const uint16_t*>(wsc + kKh);
   const int rb = w & 3;
+  float dB[4][4];   // dL/dB of this lane's tile elements
 #pragma unroll 1
   for (int u = 0; u < 4; ++u) {
     const int cb = (w >> 2) * 4 + u;
@@ -295,48 +343,71 @@ __global__ __launch_bounds__(512) void gla_bwd_grad_kernel(
       dq[g] = f32_to_bf16(gq);
       dk[g] = f32_to_bf16(gk);
       dv[g] = f32_to_bf16(dV[i]);
-      db[g] = bf16_to_f32(q[g]) * gq - bf16_to_f32(k[g]) * gk;
+      const float x = bf16_to_f32(q[g]) * gq - bf16_to_f32(k[g]) * gk;
+#pragma unroll
+      for (int uu = 0; uu < 4; ++uu)   // constant register index under the rolled tile loop
+        if (uu == u) dB[uu][i] = x;
     }
   }
+
+  // ---- d log_g inside the chunk: the reverse cumulative sum of dL/dB over its tokens
+  // (fp32 [64][132] over the state tiles, 16-token segment totals over A), starting at
+  // sum_v dS_T o S_T in the sequence's last chunk; the chunk total goes to `totals`
+  constexpr int PG = kD + 4;
+  float* G = reinterpret_cast<float*>(sm.Sb);
+  float* seg = reinterpret_cast<float*>(sm.A);   // [4][128] segment totals, [128] start
+  lds_barrier();
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) G[(16 * rb + 4 * lq + i) * PG + 16 * ((w >> 2) * 4 + u) + l16] = dB[u][i];
+  const int c = tid & (kD - 1), h = tid >> 7;
+  const bool last = dST && (cid % nc) == nc - 1;
+  float start = 0.f;
+  if (last) {   // rows 32 h .. 32 h + 31 of the final state
+    const size_t base = (size_t)(cid / nc) * kD * kD + c;
+#pragma unroll 8
+    for (int r = 32 * h; r < 32 * h + 32; ++r) start += dST[base + (size_t)r * kD] * ST[base + (size_t)r * kD];
+    seg[4 * kD + h * kD + c] = start;
+  }
+  lds_barrier();
+  float run = 0.f, x[16];
+#pragma unroll
+  for (int t = 15; t >= 0; --t) {
+    run += G[(16 * h + t) * PG + c];
+    x[t] = run;
+  }
+  seg[h * kD + c] = run;
+  lds_barrier();
+  float off = 0.f;
+  if (last) off = seg[4 * kD + c] + seg[5 * kD + c] + seg[6 * kD + c] + seg[7 * kD + c];
+  for (int j = 3; j > h; --j) off += seg[j * kD + c];
+  float* p = dg + (tok0 + 16 * h) * kD + c;
+#pragma unroll
+  for (int t = 0; t < 16; ++t) p[(size_t)t * kD] = x[t] + off;
+  if (h == 0) totals[(size_t)cid * kD + c] = off + run;
 }
 
 // ------------------------------------------------------------------ gate gradient
-// d log_g is the reverse cumulative sum over the sequence of dL/dB (in place), the last
-// token also carrying sum_v dS_T o S_T. Two passes of one block of 128 threads (one per
-// key channel) per chunk: the reverse sums within the chunk and the chunk's total, then
-// every later chunk's total added.
-__global__ __launch_bounds__(128) void gla_bwd_gate_chunk_kernel(float* __restrict__ dg,
-                                                                 float* __restrict__ totals,
-                                                                 const float* __restrict__ dST,
-                                                                 const float* __restrict__ ST, int T) {
+// d log_g is the reverse cumulative sum over the sequence of dL/dB; the gradient
+// kernel leaves the sums within each chunk and the chunk totals, and one block of 128
+// threads (one per key channel) per chunk adds every later chunk's total.
+__global__ __launch_bounds__(128) void gla_bwd_gate_offset_kernel(float* __restrict__ dg,
+                                                                  const float* __restrict__ totals, int T) {
   const int c = threadIdx.x, nc = T / kChunk, cid = blockIdx.x, n = cid / nc, ci = cid % nc;
-  float acc = 0.f;
-  if (dST && ci == nc - 1) {
-    const size_t base = (size_t)n * kD * kD + c;
-#pragma unroll 8
-    for (int r = 0; r < kD; ++r) acc += dST[base + (size_t)r * kD] * ST[base + (size_t)r * kD];
-  }
+  if (ci == nc - 1) return;
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int j0 = ci + 1; j0 < nc; j0 += 8)
+#pragma unroll
+    for (int u = 0; u < 8; ++u)   // eight independent loads in flight
+      if (j0 + u < nc) o[u] += totals[((size_t)n * nc + j0 + u) * kD + c];
+  const float off = ((o[0] + o[1]) + (o[2] + o[3])) + ((o[4] + o[5]) + (o[6] + o[7]));
   float* p = dg + ((size_t)n * T + (size_t)ci * kChunk) * kD + c;
   float x[kChunk];
 #pragma unroll
   for (int t = 0; t < kChunk; ++t) x[t] = p[(size_t)t * kD];
 #pragma unroll
-  for (int t = kChunk - 1; t >= 0; --t) {
-    acc += x[t];
-    p[(size_t)t * kD] = acc;
-  }
-  totals[(size_t)cid * kD + c] = acc;
-}
-
-__global__ __launch_bounds__(128) void gla_bwd_gate_offset_kernel(float* __restrict__ dg,
-                                                                  const float* __restrict__ totals, int T) {
-  const int c = threadIdx.x, nc = T / kChunk, cid = blockIdx.x, n = cid / nc, ci = cid % nc;
-  float off = 0.f;
-  for (int j = nc - 1; j > ci; --j) off += totals[((size_t)n * nc + j) * kD + c];
-  if (ci == nc - 1) return;
-  float* p = dg + ((size_t)n * T + (size_t)ci * kChunk) * kD + c;
-#pragma unroll 16
-  for (int t = 0; t < kChunk; ++t) p[(size_t)t * kD] += off;
+  for (int t = 0; t < kChunk; ++t) p[(size_t)t * kD] = x[t] + off;
 }
 
 }  // namespace gdnrt
@@ -393,6 +464,7 @@ extern "C" int gla_chunk_bwd(const void* q, const void* k, const void* v, const 
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   float* ST = reinterpret_cast<float*>(ws + nchunks * glab::kChunkB);   // recomputed final states
+  float* totals = ST + (size_t)N * kD * kD;                             // per chunk, d log_g totals
   if (T > 0) {
     hipLaunchKernelGGL(gla_bwd_prep_kernel, dim3((unsigned)nchunks), dim3(256), 0, s,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), log_g, ws, T);
@@ -406,12 +478,9 @@ extern "C" int gla_chunk_bwd(const void* q, const void* k, const void* v, const 
   if (T > 0) {
     hipLaunchKernelGGL(gla_bwd_grad_kernel, dim3((unsigned)nchunks), dim3(512), 0, s,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dO), ws,
+                       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dO), ws, dST, ST,
                        static_cast<uint16_t*>(dq), static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv),
-                       dlog_g, T);
-    float* totals = ST + (size_t)N * kD * kD;
-    hipLaunchKernelGGL(gla_bwd_gate_chunk_kernel, dim3((unsigned)nchunks), dim3(128), 0, s, dlog_g, totals,
-                       dST, ST, T);
+                       dlog_g, totals, T);
     hipLaunchKernelGGL(gla_bwd_gate_offset_kernel, dim3((unsigned)nchunks), dim3(128), 0, s, dlog_g,
                        totals, T);
   }

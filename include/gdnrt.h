@@ -126,7 +126,7 @@ GDNRT_API size_t gla_chunk_fwd_workspace_bytes(int N, int T, int dk, int dv, int
  *   q, k, v, dO [N][T][d] bf16 and log_g fp32: 16-byte aligned. S0, dST may be NULL
  *   (zero). workspace: gla_chunk_bwd_workspace_bytes() bytes, 16-byte aligned,
  *   overwritten (per chunk the scaled operands, the state before the chunk and the
- *   state gradient after it, in bf16, and the gate-gradient totals: 165,888 bytes; per
+ *   state gradient after it, in bf16, and the gate-gradient totals: 133,120 bytes; per
  *   sequence the recomputed final state).
  * The gate gradient is the reverse cumulative sum of q o dq - k o dk (plus dST o S_T
  * summed over value channels at the last token). T must be a multiple of 64.
