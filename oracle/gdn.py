@@ -20,6 +20,13 @@ beta = 1 with a unit key stores v exactly along k; alpha = 1, beta = 0 leaves
 the state unchanged; beta = 0 is pure decay; orthonormal keys with
 alpha = beta = 1 recall every stored value; the page's own d_k x d_v forms of
 the delta rule and of eq. 1.
+
+``gdn_recurrent_bwd`` (reverse mode through the rank-one form) is pinned by torch
+autograd of a separately written forward (the explicit matrix form), by central
+differences, and by the closed form at alpha = 1, beta = 0 (a constant state).
+``gdn_chunk_wy_bwd`` is the chunk-form backward that the GPU follows (pages
+silent; derived from the chunk form below), pinned by equality with the
+reverse-mode gradients.
 """
 from __future__ import annotations
 
@@ -121,3 +128,151 @@ def gdn_chunk_wy(q, k, v, alpha, beta, S0=None, chunk=64):
             S = gC * S + U.T @ (np.exp(lg[-1] - lg)[:, None] * K)
         S_out[n] = S
     return o, S_out
+
+
+def gdn_recurrent_bwd(q, k, v, alpha, beta, S0, dO, dST=None, ckpt=64):
+    """Gradients of ``gdn_recurrent`` by reverse-mode differentiation token by token,
+    in fp64: for the scalar L = sum(dO o o) + sum(dST o S_T), returns
+    (dq, dk, dv, dalpha, dbeta, dS0).
+
+    Forward step (rank-one form): y = S_{t-1} k_t, u_t = beta_t (v_t - alpha_t y),
+    S_t = alpha_t S_{t-1} + u_t k_t^T, o_t = S_t q_t. Going backward with dS the
+    gradient with respect to S_t:
+        dS    += do_t q_t^T;           dq_t = S_t^T do_t
+        du     = dS k_t;               dk_t = dS^T u_t
+        dv_t   = beta_t du;            dbeta_t = du . (v_t - alpha_t y)
+        dy     = -alpha_t beta_t du;   dk_t += S_{t-1}^T dy
+        dalpha_t = sum(dS o S_{t-1}) - beta_t du . y
+        dS     = alpha_t dS + dy k_t^T   (-> gradient with respect to S_{t-1})
+    The states are recomputed forward from checkpoints every ``ckpt`` tokens.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    alpha = np.asarray(alpha, np.float64)
+    beta = np.asarray(beta, np.float64)
+    dO = np.asarray(dO, np.float64)
+    N, T, dk = k.shape
+    dv = v.shape[2]
+
+    def step(S, t):
+        y = np.einsum("nvk,nk->nv", S, k[:, t])
+        u = beta[:, t][:, None] * (v[:, t] - alpha[:, t][:, None] * y)
+        return alpha[:, t][:, None, None] * S + u[:, :, None] * k[:, t][:, None, :], y, u
+
+    S = np.zeros((N, dv, dk)) if S0 is None else np.array(S0, dtype=np.float64, copy=True)
+    marks = {}
+    for t in range(T):
+        if t % ckpt == 0:
+            marks[t] = S.copy()
+        S = step(S, t)[0]
+    dS = np.zeros((N, dv, dk)) if dST is None else np.array(dST, dtype=np.float64, copy=True)
+    dq, dk_, dv_ = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+    da, db = np.empty_like(alpha), np.empty_like(beta)
+    for c0 in (range(((T - 1) // ckpt) * ckpt, -1, -ckpt) if T else ()):
+        c1 = min(T, c0 + ckpt)
+        states, ys, us = [marks[c0]], [], []
+        for t in range(c0, c1):
+            Sn, y, u = step(states[-1], t)
+            states.append(Sn)
+            ys.append(y)
+            us.append(u)
+        for t in range(c1 - 1, c0 - 1, -1):
+            i = t - c0
+            St, Sp, y, u = states[i + 1], states[i], ys[i], us[i]
+            a, b = alpha[:, t][:, None], beta[:, t][:, None]
+            dS = dS + dO[:, t][:, :, None] * q[:, t][:, None, :]
+            dq[:, t] = np.einsum("nvk,nv->nk", St, dO[:, t])
+            du = np.einsum("nvk,nk->nv", dS, k[:, t])
+            dk_[:, t] = np.einsum("nvk,nv->nk", dS, u)
+            dv_[:, t] = b * du
+            db[:, t] = np.einsum("nv,nv->n", du, v[:, t] - a * y)
+            dy = -a * b * du
+            dk_[:, t] += np.einsum("nvk,nv->nk", Sp, dy)
+            da[:, t] = np.einsum("nvk,nvk->n", dS, Sp) - beta[:, t] * np.einsum("nv,nv->n", du, y)
+            dS = a[:, :, None] * dS + dy[:, :, None] * k[:, t][:, None, :]
+    return dq, dk_, dv_, da, db, dS
+
+
+def gdn_chunk_wy_bwd(q, k, v, alpha, beta, S0, dO, dST=None, chunk=64):
+    """Chunk-form backward of ``gdn_chunk_wy`` (the pages give none; derived here).
+
+    Per chunk, with the forward's T, W, U~, U = U~ - W S_0^T, A = M o (g_r/g_j) o QK^T
+    and K^ = diag(g_C/g) K, and dS the gradient with respect to the state after the
+    chunk:
+        dU  = A^T dO + K^ dS^T
+        dA  = (dO U^T) o M,   dA' = dA o (g_r/g_j)
+        dQ  = dA' K + diag(g) dO S_0
+        dK  = dA'^T Q + diag(g_C/g) U dS + diag(beta g) T^T dW + dL' K + dL'^T K
+        dW  = -dU S_0,  dV = diag(beta) T^T dU
+        dL  = -(T^T dW W^T + T^T dU U~^T) o strict_lower,  dL' = dL o (g_r/g_j) o beta_r
+        dbeta = g o rowdot(T^T dW, K) + rowdot(T^T dU, V) + rowsum(dL o (g_r/g_j) o KK^T)
+        dS_0 = g_C dS + dO^T diag(g) Q - dU^T W        (the state-gradient scan)
+    The decay enters the recurrence only through q_t e^{B_t} and v_t e^{-B_t} (B the
+    cumulative log-decay over the sequence; dividing S_t by e^{B_t} removes the decay),
+    so dL/dB_t = q_t . dq_t - v_t . dv_t (+ sum(dST o S_T) at the last token),
+    d log alpha is its reverse cumulative sum and dalpha = d log alpha / alpha.
+    Returns (dq, dk, dv, dalpha, dbeta, dS0). T must be a multiple of ``chunk``.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    alpha = np.asarray(alpha, np.float64)
+    beta = np.asarray(beta, np.float64)
+    dO = np.asarray(dO, np.float64)
+    N, T, dk = k.shape
+    dv = v.shape[2]
+    if T % chunk:
+        raise ValueError("T must be a multiple of chunk")
+    M = np.tril(np.ones((chunk, chunk)))
+    Ms = np.tril(np.ones((chunk, chunk)), -1)
+    I = np.eye(chunk)
+    dq, dk_, dv_ = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+    dlog, dbeta = np.empty_like(alpha), np.empty_like(beta)
+    dS0 = np.empty((N, dv, dk))
+    for n in range(N):
+        S = np.zeros((dv, dk)) if S0 is None else np.array(S0[n], dtype=np.float64)
+        starts = []
+        for c0 in range(0, T, chunk):      # forward: the state before every chunk
+            starts.append(S)
+            sl = slice(c0, c0 + chunk)
+            K, V, bt = k[n, sl], v[n, sl], beta[n, sl]
+            lg = np.cumsum(np.log(alpha[n, sl]))
+            g = np.exp(lg)
+            Gam = np.exp(np.minimum(lg[:, None] - lg[None, :], 0.0))
+            Tm = np.linalg.inv(I + Ms * bt[:, None] * Gam * (K @ K.T))
+            U = Tm @ (bt[:, None] * V) - Tm @ ((bt * g)[:, None] * K) @ S.T
+            S = g[-1] * S + U.T @ (np.exp(lg[-1] - lg)[:, None] * K)
+        ST = S
+        dS = np.zeros((dv, dk)) if dST is None else np.array(dST[n], dtype=np.float64)
+        for ci in range(T // chunk - 1, -1, -1):
+            sl = slice(ci * chunk, ci * chunk + chunk)
+            Q, K, V, bt, dOc, Sb = q[n, sl], k[n, sl], v[n, sl], beta[n, sl], dO[n, sl], starts[ci]
+            lg = np.cumsum(np.log(alpha[n, sl]))
+            g = np.exp(lg)
+            Gam = np.exp(np.minimum(lg[:, None] - lg[None, :], 0.0))
+            KK = K @ K.T
+            Tm = np.linalg.inv(I + Ms * bt[:, None] * Gam * KK)
+            W = Tm @ ((bt * g)[:, None] * K)
+            Ut = Tm @ (bt[:, None] * V)
+            U = Ut - W @ Sb.T
+            A = M * Gam * (Q @ K.T)
+            Kh = np.exp(lg[-1] - lg)[:, None] * K
+            dU = A.T @ dOc + Kh @ dS.T
+            dAg = M * (dOc @ U.T) * Gam
+            dQ = dAg @ K + g[:, None] * (dOc @ Sb)
+            dW = -dU @ Sb
+            dXW, dXU = Tm.T @ dW, Tm.T @ dU
+            dL = -Ms * (dXW @ W.T + dXU @ Ut.T)
+            dLb = dL * Gam * bt[:, None]
+            dK = dAg.T @ Q + np.exp(lg[-1] - lg)[:, None] * (U @ dS) + (bt * g)[:, None] * dXW + dLb @ K + dLb.T @ K
+            dV = bt[:, None] * dXU
+            dbeta[n, sl] = g * np.einsum("rc,rc->r", dXW, K) + np.einsum("rv,rv->r", dXU, V) + (dL * Gam * KK).sum(1)
+            dq[n, sl], dk_[n, sl], dv_[n, sl] = dQ, dK, dV
+            dS = g[-1] * dS + dOc.T @ (g[:, None] * Q) - dU.T @ W
+        dS0[n] = dS
+        dB = np.einsum("tk,tk->t", q[n], dq[n]) - np.einsum("tv,tv->t", v[n], dv_[n])
+        if dST is not None and T:
+            dB[-1] += float((dST[n] * ST).sum())
+        dlog[n] = np.cumsum(dB[::-1])[::-1]
+    return dq, dk_, dv_, dlog / alpha, dbeta, dS0

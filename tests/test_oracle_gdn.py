@@ -153,3 +153,103 @@ def test_chunk_wy_affine_in_incoming_state():
     o3, S3 = f(2 * A1 - 3 * A2)
     np.testing.assert_allclose(o3 - o0, 2 * (o1 - o0) - 3 * (o2 - o0), atol=1e-10)
     np.testing.assert_allclose(S3 - S0_, 2 * (S1 - S0_) - 3 * (S2 - S0_), atol=1e-10)
+
+
+# ------------------------------------------------------------------ backward
+
+def _torch_grads(q, k, v, a, b, S0, dO, dST):
+    """Gradients by torch autograd (float64, CPU) of a separately written forward:
+    the explicit matrix form S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T."""
+    import torch
+    t = [torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v, a, b, S0)]
+    tq, tk, tv, ta, tb, tS = t
+    S = tS
+    eye = torch.eye(q.shape[2], dtype=torch.float64)
+    outs = []
+    for i in range(q.shape[1]):
+        kt = tk[:, i][:, :, None]
+        P = eye - tb[:, i][:, None, None] * (kt @ kt.transpose(1, 2))
+        S = ta[:, i][:, None, None] * (S @ P) + tb[:, i][:, None, None] * (tv[:, i][:, :, None] @ kt.transpose(1, 2))
+        outs.append((S @ tq[:, i][:, :, None])[..., 0])
+    o = torch.stack(outs, 1)
+    L = (o * torch.tensor(dO)).sum() + (S * torch.tensor(dST)).sum()
+    L.backward()
+    return [x.grad.numpy() for x in t]
+
+
+def _bwd_case(rng, N, T, d):
+    q, k, v, a, b = _rand(rng, N, T, d)
+    S0, dST = rng.standard_normal((2, N, d, d))
+    dO = rng.standard_normal((N, T, d))
+    return q, k, v, a, b, S0, dO, dST
+
+
+NAMES = ("dq", "dk", "dv", "dalpha", "dbeta", "dS0")
+
+
+def test_backward_equals_autograd_of_explicit_form():
+    rng = np.random.default_rng(51)
+    q, k, v, a, b, S0, dO, dST = _bwd_case(rng, 2, 40, 8)
+    got = gdn.gdn_recurrent_bwd(q, k, v, a, b, S0, dO, dST, ckpt=16)
+    ref = _torch_grads(q, k, v, a, b, S0, dO, dST)
+    for g_, r_, name in zip(got, ref, NAMES):
+        np.testing.assert_allclose(g_, r_, rtol=0, atol=1e-10 * np.abs(r_).max(), err_msg=name)
+
+
+def test_backward_finite_differences():
+    """Central differences of L = sum(dO o o) + sum(dST o S_T) on a tiny case."""
+    rng = np.random.default_rng(52)
+    q, k, v, a, b, S0, dO, dST = _bwd_case(rng, 1, 6, 3)
+
+    def L(*args):
+        o, ST = gdn.gdn_recurrent(*args)
+        return float((o * dO).sum() + (ST * dST).sum())
+
+    args = [q, k, v, a, b, S0]
+    grads = gdn.gdn_recurrent_bwd(q, k, v, a, b, S0, dO, dST)
+    h = 1e-6
+    for ai, g_ in enumerate(grads):
+        x = args[ai]
+        num = np.empty_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            ap, am = list(args), list(args)
+            ap[ai], am[ai] = xp, xm
+            num[idx] = (L(*ap) - L(*am)) / (2 * h)
+        np.testing.assert_allclose(g_, num, rtol=0, atol=1e-6 * max(1.0, np.abs(num).max()), err_msg=NAMES[ai])
+
+
+def test_backward_constant_state_closed_form():
+    """alpha = 1, beta = 0: S_t = S0 and o_t = S0 q_t, so with D_t = dST + sum_{s>=t}
+    do_s q_s^T: dq_t = S0^T do_t, dk = dv = 0, dbeta_t = (D_t k_t) . (v_t - S0 k_t),
+    dalpha_t = sum(D_t o S0), dS0 = D_0."""
+    rng = np.random.default_rng(53)
+    N, T, d = 2, 12, 5
+    q, k, v, _, _, S0, dO, dST = _bwd_case(rng, N, T, d)
+    dq, dk, dv, da, db, dS0 = gdn.gdn_recurrent_bwd(q, k, v, np.ones((N, T)), np.zeros((N, T)), S0, dO, dST)
+    D = dST[:, None] + np.cumsum(np.einsum("ntv,ntk->ntvk", dO, q)[:, ::-1], axis=1)[:, ::-1]
+    np.testing.assert_allclose(dq, np.einsum("nvk,ntv->ntk", S0, dO), atol=1e-12)
+    np.testing.assert_allclose(dk, 0, atol=1e-12)
+    np.testing.assert_allclose(dv, 0, atol=1e-12)
+    Dk = np.einsum("ntvk,ntk->ntv", D, k)
+    np.testing.assert_allclose(db, np.einsum("ntv,ntv->nt", Dk, v - np.einsum("nvk,ntk->ntv", S0, k)), atol=1e-11)
+    np.testing.assert_allclose(da, np.einsum("ntvk,nvk->nt", D, S0), atol=1e-11)
+    np.testing.assert_allclose(dS0, D[:, 0], atol=1e-12)
+
+
+@pytest.mark.parametrize("C", [1, 16, 64])
+def test_chunk_backward_equals_reverse_mode(C):
+    """The chunk-form backward (WY gradients, the state-gradient scan and the gate
+    gradient from q . dq - v . dv) equals reverse mode through the recurrence."""
+    rng = np.random.default_rng(60 + C)
+    q, k, v, a, b, S0, dO, dST = _bwd_case(rng, 2, 128, 8)
+    ref = gdn.gdn_recurrent_bwd(q, k, v, a, b, S0, dO, dST, ckpt=32)
+    got = gdn.gdn_chunk_wy_bwd(q, k, v, a, b, S0, dO, dST, chunk=C)
+    for g_, r_, name in zip(got, ref, NAMES):
+        np.testing.assert_allclose(g_, r_, rtol=0, atol=1e-11 * np.abs(r_).max(), err_msg=name)
+    got = gdn.gdn_chunk_wy_bwd(q, k, v, a, b, None, dO, None, chunk=C)
+    ref = gdn.gdn_recurrent_bwd(q, k, v, a, b, None, dO, None)
+    for g_, r_, name in zip(got, ref, NAMES):
+        np.testing.assert_allclose(g_, r_, rtol=0, atol=1e-11 * np.abs(r_).max(), err_msg=name)
