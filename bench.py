@@ -296,6 +296,51 @@ def bench_gla_bwd(K=10, W=2, B=4, H=16, T=4096):
     return res
 
 
+def gdn_bwd_work(C=64):
+    """Algorithmic FLOPs of one chunk of one head in the GDN chunk-form backward: the
+    forward's chunk operands (as gdn_chunk_work, without the state products), the state
+    recompute (W S^T, U^T K^), the state-gradient scan (K^ dS^T, dO^T Q', dU^T W), then
+    A and dA (lower), U, dU = A^T dO + K^ dS^T, dq = dA' K + dO S_b, dA'^T Q + U dS_a,
+    dW = dU S_b, T^T dW and T^T dU (lower T), dL (strict lower, with the Gram matrix)
+    and (dL' + dL'^T) K."""
+    tri, stri = C * (C + 1) // 2, C * (C - 1) // 2
+    full, low, slow = 2 * C * D * D, 2 * tri * D, 2 * stri * D
+    fwd_ops = slow + 2 * C ** 3 // 3 + low + 2 * low + low   # Gram, inverse, A, W and U~, Q' (A W)
+    scans = 2 * full + 3 * full
+    grad1 = low + full + (low + full) + low + (low + full) + (low + full)
+    grad2 = full + 2 * low + 3 * slow + 2 * C * C * D
+    return fwd_ops + scans + grad1 + grad2
+
+
+def bench_gdn_bwd(K=10, W=2, B=1, H=32, T=16384):
+    N = B * H
+    log(f"[gdn_bwd] generating B={B} H={H} T={T}")
+    inp = synth.gdn_prefill(B=B, H=H, T=T, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(91)
+    dO = torch.randn(inp["q"].shape, generator=g, device="cuda").to(torch.bfloat16)
+    ws = m.gdn_chunk_bwd_workspace(N, T)
+    out = (torch.empty_like(inp["q"]), torch.empty_like(inp["k"]), torch.empty_like(inp["v"]),
+           torch.empty_like(inp["alpha"]), torch.empty_like(inp["beta"]), torch.empty_like(inp["S0"]))
+
+    def run(i):
+        m.gdn_chunk_bwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], dO, None, None, ws, out)
+
+    ms, wall = timed(run, K, W)
+    flops = gdn_bwd_work() * (N * T // 64)
+    # reads q, k, v, dO (bf16), alpha, beta; writes dq, dk, dv (bf16), dalpha, dbeta, dS0
+    byts = N * T * (D * 4 * 2 + 2 * 4 + D * 3 * 2 + 2 * 4) + N * D * D * 4
+    res = dict(workload=f"gdn_chunk_bwd B={B} H={H} T={T} d=128 chunk 64: gradients of q, k, v, alpha, beta "
+                        f"and the incoming state, bf16 in and out, fp32 gates, zero initial state",
+               ms=ms, tokens_per_s=B * T / (ms * 1e-3), gflop=flops / 1e9,
+               tflops=flops / (ms * 1e-3) / 1e12, bytes=byts, achieved_gbs=byts / (ms * 1e-3) / 1e9,
+               workspace_bytes=int(ws.numel()), wall_s=wall)
+    res["frac_hbm"] = res["achieved_gbs"] / PEAK_HBM_GBS
+    res["frac_mfma"] = res["tflops"] / PEAK_BF16_TFLOPS
+    res["roofline_bound"] = "mfma (at the knee)"
+    del inp, ws, out
+    return res
+
+
 def gdn_chunk_work(C=64):
     """Algorithmic FLOPs of one chunk of one head in the UT / WY form: Gram k.k
     (strict lower), triangular inverse (C^3/3 multiply-adds), scores q.k (lower),
@@ -346,7 +391,11 @@ def bench_gdn_chunk(K=10, W=2, B=1, H=32, T=16384, kda=False):
 
 
 GLA_BWD_KERNELS = ("gla_bwd_prep_kernel", "gla_bwd_scan_kernel<fwd>", "gla_bwd_scan_kernel<rev>",
-                   "gla_bwd_grad_kernel", "gla_bwd_gate_offset_kernel")
+                   "gla_bwd_grad_kernel")
+
+
+GDN_BWD_KERNELS = ("gdn_chunk_prep_kernel<bwd>", "gdn_bwd_fscan_kernel", "gdn_bwd_rscan_kernel",
+                   "gdn_bwd_grad1_kernel", "gdn_bwd_grad2_kernel")
 
 
 def counter_traffic(kernel):
@@ -397,7 +446,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--rows", default="decode,kda,leapq,kda_leapq,gla,gla_bwd,gdn,kda_chunk")
+    ap.add_argument("--rows", default="decode,kda,leapq,kda_leapq,gla,gla_bwd,gdn,gdn_bwd,kda_chunk")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the measured HBM-copy and bf16-GEMM ceilings")
@@ -462,6 +511,14 @@ def main():
         r["traffic_bytes"] = sum(parts) if None not in parts else None
         out_rows["gla_bwd"] = r
         log(f"[gla_bwd] {r['ms']*1e3:.1f} us  {r['tflops']:.1f} TFLOP/s ({r['frac_mfma']*100:.1f}% MFMA)  "
+            f"{r['achieved_gbs']:.0f} GB/s ({r['frac_hbm']*100:.1f}% HBM)  {r['tokens_per_s']/1e6:.2f} M tok/s")
+        torch.cuda.empty_cache()
+    if "gdn_bwd" in rows:
+        r = bench_gdn_bwd()
+        parts = [counter_traffic(k) for k in GDN_BWD_KERNELS]
+        r["traffic_bytes"] = sum(parts) if None not in parts else None
+        out_rows["gdn_bwd"] = r
+        log(f"[gdn_bwd] {r['ms']*1e3:.1f} us  {r['tflops']:.1f} TFLOP/s ({r['frac_mfma']*100:.1f}% MFMA)  "
             f"{r['achieved_gbs']:.0f} GB/s ({r['frac_hbm']*100:.1f}% HBM)  {r['tokens_per_s']/1e6:.2f} M tok/s")
         torch.cuda.empty_cache()
     if "kda_chunk" in rows:

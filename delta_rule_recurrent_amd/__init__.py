@@ -1,13 +1,16 @@
 """MI355X-native gated delta-rule recurrent state update.
 
 Entry points over the gdnrt HIP library (C ABI in include/gdnrt.h):
-``gdn_decode_step``, ``gla_chunk_fwd``, ``gla_chunk_bwd``, ``gdn_chunk_fwd``, ``leapq_decode_step``,
+``gdn_decode_step``, ``gla_chunk_fwd``, ``gla_chunk_bwd``, ``gdn_chunk_fwd``, ``gdn_chunk_bwd``,
+``leapq_decode_step``,
 ``leapq_window_flush``, ``kda_decode_step``, ``kda_chunk_fwd``,
 ``kda_leapq_decode_step`` and ``kda_leapq_window_flush``. ``synth`` draws the seeded synthetic workloads.
 """
 from .binding import (  # noqa: F401
     GdnrtError,
     LeapqBuffers,
+    gdn_chunk_bwd,
+    gdn_chunk_bwd_workspace,
     gdn_chunk_fwd,
     gdn_chunk_workspace,
     gdn_decode_step,

@@ -42,6 +42,8 @@ SIGNATURES = {
     "kda_chunk_fwd": ([_vp] * 8 + [_c_int] * 6 + [_vp, ctypes.c_size_t, _vp], _c_int),
     "gla_chunk_bwd": ([_vp] * 12 + [_c_int] * 6 + [_vp, ctypes.c_size_t, _vp], _c_int),
     "gla_chunk_bwd_workspace_bytes": ([_c_int] * 5, ctypes.c_size_t),
+    "gdn_chunk_bwd": ([_vp] * 14 + [_c_int] * 6 + [_vp, ctypes.c_size_t, _vp], _c_int),
+    "gdn_chunk_bwd_workspace_bytes": ([_c_int] * 5, ctypes.c_size_t),
     "kda_chunk_fwd_workspace_bytes": ([_c_int] * 5, ctypes.c_size_t),
     "leapq_decode_step": ([ctypes.POINTER(LeapqState), _c_int] + [_vp] * 6 + [_c_int, _vp], _c_int),
     "leapq_window_flush": ([ctypes.POINTER(LeapqState), _c_int, _vp, _vp, _c_int, _c_int, _vp, _vp],
@@ -229,6 +231,40 @@ def gla_chunk_bwd(q, k, v, log_g, dO, S0=None, dST=None, workspace=None, out=Non
         _ptr(dv), _ptr(dg), _ptr(dS0), N, T, D, D, chunk, BF16, _ptr(workspace), workspace.numel(),
         _stream()))
     return dq, dk, dv, dg, dS0
+
+
+def gdn_chunk_bwd_workspace(N, T, device="cuda", chunk=CHUNK):
+    """Allocate the workspace gdn_chunk_bwd needs for N sequences of T tokens."""
+    nb = lib().gdn_chunk_bwd_workspace_bytes(N, max(T, CHUNK), D, D, chunk)
+    return torch.empty(max(nb, 16), dtype=torch.uint8, device=device)
+
+
+def gdn_chunk_bwd(q, k, v, alpha, beta, dO, S0=None, dST=None, workspace=None, out=None, chunk=CHUNK):
+    """Gated DeltaNet chunkwise backward: gradients of sum(dO * o) + sum(dST * S_T)
+    for the forward of gdn_chunk_fwd.
+
+    q, k, v, dO [N][T][128] bf16; alpha, beta [N][T] fp32; S0, dST [N][128][128]
+    fp32 or None. Returns (dq, dk, dv (bf16), dalpha, dbeta, dS0 (fp32))."""
+    N, T, _ = q.shape
+    for n_, t_ in (("q", q), ("k", k), ("v", v), ("dO", dO)):
+        _need(t_, n_, torch.bfloat16, (N, T, D))
+    for n_, t_ in (("alpha", alpha), ("beta", beta)):
+        _need(t_, n_, torch.float32, (N, T))
+    for n_, t_ in (("S0", S0), ("dST", dST)):
+        if t_ is not None:
+            _need(t_, n_, torch.float32, (N, D, D))
+    if out is None:
+        out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(alpha),
+               torch.empty_like(beta), torch.empty((N, D, D), dtype=torch.float32, device=q.device))
+    dq, dk, dv, da, db, dS0 = out
+    if workspace is None:
+        workspace = gdn_chunk_bwd_workspace(N, T, q.device, chunk)
+    _need(workspace, "workspace", torch.uint8)
+    _check("gdn_chunk_bwd", lib().gdn_chunk_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(dO), _ptr(dST), _ptr(dq),
+        _ptr(dk), _ptr(dv), _ptr(da), _ptr(db), _ptr(dS0), N, T, D, D, chunk, BF16, _ptr(workspace),
+        workspace.numel(), _stream()))
+    return dq, dk, dv, da, db, dS0
 
 
 def kda_chunk_workspace(N, T, device="cuda", chunk=CHUNK):

@@ -1,0 +1,751 @@
+// Gated DeltaNet chunkwise backward of one sequence shard.
+//
+// The recurrence is the one of "LeapQuant: an 8-bit recurrent state that stops
+// rounding every token", section "The state, from the update rule up" (eq. 3); the
+// pages print no chunk form and no backward for it. The forward's chunk form (UT /
+// WY, state [d_v][d_k], C = 64 tokens, g_r = prod_{i<=r} alpha_i inside the chunk):
+//
+//   T = (I + L)^-1,  L[r,j] = beta_r (g_r/g_j) k_r.k_j (j < r),
+//   W = T diag(beta g) K,  U~ = T diag(beta) V,  U = U~ - W S_b^T,
+//   A = M o (g_r/g_j) o Q K^T,  O = diag(g) Q S_b^T + A U,
+//   S_a = g_C S_b + U^T K^,  K^ = diag(g_C/g) K,   Q' = diag(g) Q - A W,
+//
+// (S_b the state before the chunk, S_a after). Differentiating it, with dS_a given:
+//
+//   dS_b = g_C dS_a + dO^T Q' - (K^ dS_a^T)^T W              (backward state scan)
+//   dU   = A^T dO + K^ dS_a^T,   dA' = (dO U^T) o M o (g_r/g_j)
+//   dq   = dA' K + diag(g) dO S_b
+//   dk   = dA'^T Q + diag(g_C/g) U dS_a + (T diag(beta g))^T dW + dL' K + dL'^T K
+//   dW   = -dU S_b,   dv = (T diag(beta))^T dU
+//   dL   = -(T^T dW W^T + T^T dU U~^T) o strict_lower,  dL' = dL o (g_r/g_j) o beta_r
+//   dbeta = g o rowdot(T^T dW, K) + rowdot(T^T dU, V) + rowsum(dL o (g_r/g_j) o K K^T)
+//
+// and the decay gradient from the fact that, with B_t the cumulative log-decay over
+// the sequence, S_t e^{-B_t} follows the undecayed delta rule driven by v_t e^{-B_t}
+// and read by q_t e^{B_t}: dL/dB_t = q_t.dq_t - v_t.dv_t and d log alpha_t =
+// sum_{s >= t} dL/dB_s. Shifting B on every token after a chunk scales the state the
+// next chunk starts from, so the part of that sum beyond the chunk is sum(dS_a o S_a)
+// (dST o S_T after the last chunk); the rest is a sum over at most 64 tokens, and no
+// rounding error accumulates along the sequence. dalpha = d log alpha / alpha.
+//
+// Kernels: the forward's chunk prep (which also stores T), a forward state scan (the
+// state before every chunk, bf16), the backward state scan (the gradient after every
+// chunk, bf16, dS_0 and the chunks' sum(dS_a o S_a)), and two per-chunk gradient
+// kernels (bf16 MFMA, fp32 accumulation).
+#include "common.hpp"
+#include "gdn_chunk_layout.hpp"
+
+namespace gdnrt {
+
+void gdn_chunk_prep_with_inverse(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                 const float* alpha, const float* beta, uint8_t* ws, uint16_t* Tout,
+                                 int T, int nchunks, hipStream_t s);
+
+namespace gdb {
+
+using namespace gdc;
+constexpr int C = kChunk;    // 64
+constexpr int PT = kD + 16;  // bf16 pitch of 128-wide rows
+constexpr int PA = C + 16;   // bf16 pitch of 64-wide rows
+constexpr int PX = 16 + 16;  // bf16 pitch of 16-wide rows
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ bf16x8 as_bf(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+__device__ __forceinline__ bf16x8 ld8(const uint16_t* p) { return as_bf(*reinterpret_cast<const u32x4*>(p)); }
+// 8 keys of a row in the prep fragments' order: 4 at c, 4 at c + 16
+__device__ __forceinline__ bf16x8 ld8_split(const uint16_t* p) {
+  const u32x2 a = *reinterpret_cast<const u32x2*>(p), b = *reinterpret_cast<const u32x2*>(p + 16);
+  return as_bf(u32x4{a.x, a.y, b.x, b.y});
+}
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// MFMA operand from a row-major [contraction][column] bf16 matrix in LDS through the
+// transposing LDS read: lane (l16, lq) receives X[c0 + 8 lq + e][n0 + l16], e = 0..7.
+__device__ __forceinline__ bf16x8 ld_tr8(const uint16_t* X, int pitch, int c0, int n0) {
+  const int lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
+  const uint16_t* p = X + (c0 + 8 * g + (j >> 2)) * pitch + n0 + 4 * (j & 3);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * pitch));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+__device__ __forceinline__ float lo_bf(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float wave_scan(float x) {   // inclusive prefix sum over 64 lanes
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+// lower-triangle 16 x 16 tile pairs (rb, cb), cb <= rb
+__device__ __forceinline__ void tri_pair(int p, int& rb, int& cb) {
+  rb = p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3;
+  cb = p - (rb * (rb + 1)) / 2;
+}
+// block -> (sequence, value tile of 16); the 8 tiles of one sequence share an XCD
+// (blocks are dealt to the 8 XCDs round robin), so the chunk operands they all read
+// are fetched into that XCD's L2 once
+__device__ __forceinline__ void seq_tile(int& n, int& vt) {
+  const int bid = blockIdx.x;
+  if ((gridDim.x & 63) == 0) {
+    n = (bid >> 6) * 8 + (bid & 7);
+    vt = (bid >> 3) & 7;
+  } else {
+    n = bid >> 3;
+    vt = bid & 7;
+  }
+}
+
+// Workspace regions of the backward, each an array over chunks (then sequences).
+struct Ws {
+  uint8_t* prep;   // the forward prep's operands, kWsChunk bytes per chunk
+  uint16_t* T;     // (I + L)^-1, bf16 [64][64]
+  uint16_t* Sb;    // state before the chunk, bf16 [128][128]
+  uint16_t* dSa;   // state gradient after the chunk, bf16 [128][128]
+  uint16_t* dU;    // dU, bf16 [64][128]
+  float* dK1;      // dA'^T Q + diag(g_C/g) U dS_a, fp32 [64][128]
+  float* qdq;      // q_t . dq_t, fp32 [64]
+  float* bnd;      // sum(dS_a o S_a) in 32 parts (value tile, wave), fp32
+  float* ST;       // per sequence, the recomputed final state, fp32 [128][128]
+};
+
+}  // namespace gdb
+
+// ------------------------------------------------------------------ forward state scan
+// One block of 256 threads per (sequence, value tile of 16 rows); wave w owns key
+// columns [32 w, 32 w + 32) of the state (lane holds rows 4 lq + i, columns
+// 32 w + 16 j + l16) and token block w of U. Per chunk: store the state (bf16), then
+// U = U~ - W S^T for this tile's values and S <- g_C S + U^T K^, with the prep's
+// fragments as MFMA operands straight from registers (next chunk's loaded ahead).
+__global__ __launch_bounds__(256) void gdn_bwd_fscan_kernel(const uint8_t* __restrict__ prep,
+                                                            const float* __restrict__ S0,
+                                                            uint16_t* __restrict__ Sb,
+                                                            float* __restrict__ ST, int T) {
+  using namespace gdb;
+  __shared__ __attribute__((aligned(16))) uint16_t sS[16 * PT];
+  __shared__ __attribute__((aligned(16))) uint16_t sU[16 * PA];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, lq = lane >> 4;
+  int n, vt;
+  seq_tile(n, vt);
+  const int v0 = 16 * vt, nc = T / C;
+  const size_t chunk0 = (size_t)n * nc;
+  f32x4 acc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc[j][i] = S0 ? S0[((size_t)n * kD + v0 + 4 * lq + i) * kD + 32 * w + 16 * j + l16] : 0.f;
+  struct Ops {
+    u32x4 w[4], kh[4];
+    u32x2 u;
+    float gc;
+  };
+  auto load = [&](size_t cid, Ops& o) {
+    const uint8_t* pc = prep + cid * kWsChunk;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      o.w[ks] = *reinterpret_cast<const u32x4*>(pc + kWsW + ((size_t)(w * 4 + ks) * 64 + lane) * 16);
+#pragma unroll
+    for (int f = 0; f < 4; ++f)   // K^ fragments (kb, js) = (2 w + f / 2, f % 2)
+      o.kh[f] = *reinterpret_cast<const u32x4*>(pc + kWsK + ((size_t)(4 * w + f) * 64 + lane) * 16);
+    o.u = *reinterpret_cast<const u32x2*>(pc + kWsU + ((size_t)(w * 8 + vt) * 64 + lane) * 8);
+    o.gc = *reinterpret_cast<const float*>(pc + kWsG + l16 * 4);
+  };
+  Ops cur, nxt;
+  if (nc > 0) load(chunk0, nxt);
+  for (int s = 0; s < nc; ++s) {
+    cur = nxt;
+    if (s + 1 < nc) load(chunk0 + s + 1, nxt);
+    uint16_t* dst = Sb + (chunk0 + s) * kD * kD;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint16_t b = f32_to_bf16(acc[j][i]);
+        const int r = 4 * lq + i, c = 32 * w + 16 * j + l16;
+        dst[(size_t)(v0 + r) * kD + c] = b;
+        sS[r * PT + c] = b;
+      }
+    lds_barrier();
+    f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) p = mfma(as_bf(cur.w[ks]), ld8_split(sS + l16 * PT + 32 * ks + 4 * lq), p);
+    const float u0 = lo_bf(cur.u.x) - p[0], u1 = hi_bf(cur.u.x) - p[1];
+    const float u2 = lo_bf(cur.u.y) - p[2], u3 = hi_bf(cur.u.y) - p[3];
+    *reinterpret_cast<u32x2*>(sU + l16 * PA + 16 * w + 4 * lq) = u32x2{pack_bf16(u0, u1), pack_bf16(u2, u3)};
+    lds_barrier();
+    acc[0] *= cur.gc;
+    acc[1] *= cur.gc;
+#pragma unroll
+    for (int js = 0; js < 2; ++js) {
+      const bf16x8 a = ld8(sU + l16 * PA + 32 * js + 8 * lq);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[j] = mfma(a, as_bf(cur.kh[2 * j + js]), acc[j]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ST[((size_t)n * kD + v0 + 4 * lq + i) * kD + 32 * w + 16 * j + l16] = acc[j][i];
+}
+
+// ------------------------------------------------------------------ backward state scan
+// One block of 256 threads per (sequence, value tile of 16 rows), chunks last to
+// first; wave w owns key columns [32 w, 32 w + 32) of dS and token block w of
+// K^ dS^T. Per chunk: store dS (bf16, the gradient after the chunk) and this tile's
+// part of sum(dS o S) with S the state after the chunk, stage K^ (as K^^T), Q', W and
+// this tile's dO in LDS, then
+//   dS <- g_C dS + dO^T Q' - (K^ dS^T)^T W.
+__global__ __launch_bounds__(256) void gdn_bwd_rscan_kernel(const uint8_t* __restrict__ prep,
+                                                            const uint16_t* __restrict__ dO,
+                                                            const float* __restrict__ dST,
+                                                            const uint16_t* __restrict__ Sb,
+                                                            const float* __restrict__ ST,
+                                                            uint16_t* __restrict__ dSa,
+                                                            float* __restrict__ bnd,
+                                                            float* __restrict__ dS0, int T) {
+  using namespace gdb;
+  __shared__ __attribute__((aligned(16))) uint16_t sD[16 * PT];
+  __shared__ __attribute__((aligned(16))) uint16_t sKt[kD * PA];
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[C * PT];
+  __shared__ __attribute__((aligned(16))) uint16_t sW[C * PT];
+  __shared__ __attribute__((aligned(16))) uint16_t sO[C * PX];
+  __shared__ __attribute__((aligned(16))) uint16_t sdU[16 * PA];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, lq = lane >> 4;
+  int n, vt;
+  seq_tile(n, vt);
+  const int v0 = 16 * vt, nc = T / C;
+  const size_t chunk0 = (size_t)n * nc;
+  f32x4 acc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc[j][i] = dST ? dST[((size_t)n * kD + v0 + 4 * lq + i) * kD + 32 * w + 16 * j + l16] : 0.f;
+  struct Ops {
+    u32x4 kh[4], qp[4], w[4];
+    u32x2 o;
+    float gc;
+    float sa[2][4];   // this lane's entries of the state after the chunk
+  };
+  // fragment f = w + 4 p of each 16-fragment operand, this lane's 16 bytes
+  auto load = [&](int ci, Ops& o) {
+    const uint8_t* pc = prep + (chunk0 + ci) * kWsChunk;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const size_t e = (size_t)(v0 + 4 * lq + i) * kD + 32 * w + 16 * j + l16;
+        o.sa[j][i] = ci + 1 < nc ? bf16_to_f32(Sb[(chunk0 + ci + 1) * kD * kD + e]) : ST[(size_t)n * kD * kD + e];
+      }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const size_t off = ((size_t)(w + 4 * p) * 64 + lane) * 16;
+      o.kh[p] = *reinterpret_cast<const u32x4*>(pc + kWsK + off);
+      o.qp[p] = *reinterpret_cast<const u32x4*>(pc + kWsQ + off);
+      o.w[p] = *reinterpret_cast<const u32x4*>(pc + kWsW + off);
+    }
+    o.o = *reinterpret_cast<const u32x2*>(dO + ((size_t)n * T + (size_t)ci * C + (tid >> 2)) * kD + v0 + 4 * (tid & 3));
+    o.gc = *reinterpret_cast<const float*>(pc + kWsG + l16 * 4);
+  };
+  Ops cur, nxt;
+  if (nc > 0) load(nc - 1, nxt);
+  for (int s = 0; s < nc; ++s) {
+    const int ci = nc - 1 - s;
+    cur = nxt;
+    if (s + 1 < nc) load(ci - 1, nxt);
+    uint16_t* dst = dSa + (chunk0 + ci) * kD * kD;
+    float part = 0.f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint16_t b = f32_to_bf16(acc[j][i]);
+        const int r = 4 * lq + i, c = 32 * w + 16 * j + l16;
+        dst[(size_t)(v0 + r) * kD + c] = b;
+        sD[r * PT + c] = b;
+        part += acc[j][i] * cur.sa[j][i];
+      }
+    part = sum64(part);
+    if (lane == 0) bnd[(chunk0 + ci) * 32 + 4 * vt + w] = part;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int f = w + 4 * p;
+      // K^ fragment (kb, js) = (f / 2, f % 2): key kb*16 + l16, tokens js*32 + lq*8 ..
+      *reinterpret_cast<u32x4*>(sKt + ((f >> 1) * 16 + l16) * PA + (f & 1) * 32 + lq * 8) = cur.kh[p];
+      // W, Q' fragments (rb, ks) = (f / 4, f % 4): token rb*16 + l16, keys split by 16
+      const int ro = ((f >> 2) * 16 + l16) * PT + (f & 3) * 32 + lq * 4;
+      *reinterpret_cast<u32x2*>(sW + ro) = u32x2{cur.w[p].x, cur.w[p].y};
+      *reinterpret_cast<u32x2*>(sW + ro + 16) = u32x2{cur.w[p].z, cur.w[p].w};
+      *reinterpret_cast<u32x2*>(sQ + ro) = u32x2{cur.qp[p].x, cur.qp[p].y};
+      *reinterpret_cast<u32x2*>(sQ + ro + 16) = u32x2{cur.qp[p].z, cur.qp[p].w};
+    }
+    *reinterpret_cast<u32x2*>(sO + (tid >> 2) * PX + 4 * (tid & 3)) = cur.o;
+    lds_barrier();
+    // -(K^ dS^T)^T for tokens 16 w .. 16 w + 15: [v][t]
+    f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) x = mfma(ld8(sD + l16 * PT + 32 * ks + 8 * lq), ld_tr8(sKt, PA, 32 * ks, 16 * w), x);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sdU[(4 * lq + i) * PA + 16 * w + l16] = f32_to_bf16(-x[i]);
+    lds_barrier();
+    acc[0] *= cur.gc;
+    acc[1] *= cur.gc;
+#pragma unroll
+    for (int js = 0; js < 2; ++js) {
+      const bf16x8 ao = ld_tr8(sO, PX, 32 * js, 0);
+      const bf16x8 au = ld8(sdU + l16 * PA + 32 * js + 8 * lq);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        acc[j] = mfma(ao, ld_tr8(sQ, PT, 32 * js, 32 * w + 16 * j), acc[j]);
+        acc[j] = mfma(au, ld_tr8(sW, PT, 32 * js, 32 * w + 16 * j), acc[j]);
+      }
+    }
+    lds_barrier();
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dS0[((size_t)n * kD + v0 + 4 * lq + i) * kD + 32 * w + 16 * j + l16] = acc[j][i];
+}
+
+// ------------------------------------------------------------------ gradients, part 1
+// One block of 512 threads (8 waves) per chunk: U, A, dU (to the workspace), dA', dq
+// (final, with q_t . dq_t) and dK1 = dA'^T Q + diag(g_C/g) U dS_a (to the workspace).
+// Output tiles (rb, cb): wave w takes token block rb = w % 4 and column blocks
+// cb = 4 (w / 4) .. + 3; lane holds rows 16 rb + 4 lq + i of column 16 cb + l16.
+struct alignas(16) G1Smem {
+  uint16_t Q[kChunk * gdb::PT], K[kChunk * gdb::PT], O[kChunk * gdb::PT];   // [t][128]
+  uint16_t S[kD * gdb::PT], D[kD * gdb::PT];                                 // S_b, dS_a [v][c]
+  uint16_t U[kChunk * gdb::PT];                                              // [t][v]
+  uint16_t A[kChunk * gdb::PA];                                              // A, then dA' [r][j]
+  float lg[kChunk], g[kChunk], kd[kChunk], qdq[kChunk];
+};
+
+__global__ __launch_bounds__(512) void gdn_bwd_grad1_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ dO,
+    const float* __restrict__ alpha, gdb::Ws ws, uint16_t* __restrict__ dq, int T) {
+  using namespace gdb;
+  __shared__ G1Smem sm;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, lq = lane >> 4;
+  const int nc = T / C, cid = blockIdx.x;
+  const size_t tok0 = (size_t)(cid / nc) * T + (size_t)(cid % nc) * C;
+  const uint8_t* pc = ws.prep + (size_t)cid * kWsChunk;
+
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int e = (tid + 512 * p) * 8, r = e >> 7, cc = e & 127;
+    const size_t gi = (tok0 + r) * kD + cc;
+    *reinterpret_cast<u32x4*>(sm.Q + r * PT + cc) = *reinterpret_cast<const u32x4*>(q + gi);
+    *reinterpret_cast<u32x4*>(sm.K + r * PT + cc) = *reinterpret_cast<const u32x4*>(k + gi);
+    *reinterpret_cast<u32x4*>(sm.O + r * PT + cc) = *reinterpret_cast<const u32x4*>(dO + gi);
+  }
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int e = (tid + 512 * p) * 8, r = e >> 7, cc = e & 127;
+    *reinterpret_cast<u32x4*>(sm.S + r * PT + cc) = *reinterpret_cast<const u32x4*>(ws.Sb + (size_t)cid * kD * kD + e);
+    *reinterpret_cast<u32x4*>(sm.D + r * PT + cc) = *reinterpret_cast<const u32x4*>(ws.dSa + (size_t)cid * kD * kD + e);
+  }
+  for (int e = tid; e < C * PA / 2; e += 512) reinterpret_cast<uint32_t*>(sm.A)[e] = 0u;
+  if (w == 0) {
+    const float lgv = wave_scan(__logf(alpha[tok0 + lane]));
+    const float lC = __shfl(lgv, C - 1);
+    sm.lg[lane] = lgv;
+    sm.g[lane] = __expf(lgv);
+    sm.kd[lane] = __expf(lC - lgv);
+    sm.qdq[lane] = 0.f;
+  }
+  lds_barrier();
+
+  const int rb = w & 3;
+  // ---- A = M o (g_r/g_j) o Q K^T (lower tiles) and U = U~ - W S_b^T
+  for (int t = w; t < 10; t += 8) {
+    int ab, cb;
+    tri_pair(t, ab, cb);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      acc = mfma(ld8(sm.Q + (16 * ab + l16) * PT + 32 * ks + 8 * lq), ld8(sm.K + (16 * cb + l16) * PT + 32 * ks + 8 * lq), acc);
+    const int j = 16 * cb + l16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * ab + 4 * lq + i;
+      sm.A[r * PA + j] = f32_to_bf16(j <= r ? __expf(sm.lg[r] - sm.lg[j]) * acc[i] : 0.f);
+    }
+  }
+  {
+    u32x4 wf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      wf[ks] = *reinterpret_cast<const u32x4*>(pc + kWsW + ((size_t)(rb * 4 + ks) * 64 + lane) * 16);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int vb = (w >> 2) * 4 + u;
+      const u32x2 ut = *reinterpret_cast<const u32x2*>(pc + kWsU + ((size_t)(rb * 8 + vb) * 64 + lane) * 8);
+      f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) p = mfma(as_bf(wf[ks]), ld8_split(sm.S + (16 * vb + l16) * PT + 32 * ks + 4 * lq), p);
+      const float uu[4] = {lo_bf(ut.x) - p[0], hi_bf(ut.x) - p[1], lo_bf(ut.y) - p[2], hi_bf(ut.y) - p[3]};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm.U[(16 * rb + 4 * lq + i) * PT + 16 * vb + l16] = f32_to_bf16(uu[i]);
+    }
+  }
+  lds_barrier();
+
+  // ---- dU = A^T dO + diag(g_C/g) K dS_a^T (to the workspace); dO U^T on the lower tiles
+  uint16_t* dUw = ws.dU + (size_t)cid * C * kD;
+#pragma unroll 1
+  for (int u = 0; u < 4; ++u) {
+    const int vb = (w >> 2) * 4 + u;
+    f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = a1;
+#pragma unroll
+    for (int js = 0; js < 2; ++js)
+      if (32 * js + 31 >= 16 * rb)   // A[j][r] is zero for j < r
+        a1 = mfma(ld_tr8(sm.A, PA, 32 * js, 16 * rb), ld_tr8(sm.O, PT, 32 * js, 16 * vb), a1);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      a2 = mfma(ld8(sm.K + (16 * rb + l16) * PT + 32 * ks + 8 * lq), ld8(sm.D + (16 * vb + l16) * PT + 32 * ks + 8 * lq), a2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * rb + 4 * lq + i;
+      dUw[r * kD + 16 * vb + l16] = f32_to_bf16(a1[i] + sm.kd[r] * a2[i]);
+    }
+  }
+  f32x4 da[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    da[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (w + 8 * h < 10) {
+      int ab, cb;
+      tri_pair(w + 8 * h, ab, cb);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        da[h] = mfma(ld8(sm.O + (16 * ab + l16) * PT + 32 * ks + 8 * lq), ld8(sm.U + (16 * cb + l16) * PT + 32 * ks + 8 * lq), da[h]);
+    }
+  }
+  lds_barrier();
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    if (w + 8 * h < 10) {
+      int ab, cb;
+      tri_pair(w + 8 * h, ab, cb);
+      const int j = 16 * cb + l16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * ab + 4 * lq + i;
+        sm.A[r * PA + j] = f32_to_bf16(j <= r ? __expf(sm.lg[r] - sm.lg[j]) * da[h][i] : 0.f);
+      }
+    }
+  lds_barrier();
+
+  // ---- dq = dA' K + diag(g) dO S_b;  dK1 = dA'^T Q + diag(g_C/g) U dS_a
+  float* dK1 = ws.dK1 + (size_t)cid * C * kD;
+#pragma unroll 1
+  for (int u = 0; u < 4; ++u) {
+    const int kb = (w >> 2) * 4 + u;
+    f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = a1, a3 = a1, a4 = a1;
+#pragma unroll
+    for (int js = 0; js < 2; ++js) {
+      if (js <= rb / 2)   // dA'[r][j] is zero for j > r
+        a1 = mfma(ld8(sm.A + (16 * rb + l16) * PA + 32 * js + 8 * lq), ld_tr8(sm.K, PT, 32 * js, 16 * kb), a1);
+      if (32 * js + 31 >= 16 * rb)   // dA'[i][r] is zero for i < r
+        a3 = mfma(ld_tr8(sm.A, PA, 32 * js, 16 * rb), ld_tr8(sm.Q, PT, 32 * js, 16 * kb), a3);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      a2 = mfma(ld8(sm.O + (16 * rb + l16) * PT + 32 * ks + 8 * lq), ld_tr8(sm.S, PT, 32 * ks, 16 * kb), a2);
+      a4 = mfma(ld8(sm.U + (16 * rb + l16) * PT + 32 * ks + 8 * lq), ld_tr8(sm.D, PT, 32 * ks, 16 * kb), a4);
+    }
+    const int col = 16 * kb + l16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * rb + 4 * lq + i;
+      const float gq = a1[i] + sm.g[r] * a2[i];
+      dq[(tok0 + r) * kD + col] = f32_to_bf16(gq);
+      dK1[r * kD + col] = a3[i] + sm.kd[r] * a4[i];
+      const float s = sum16(bf16_to_f32(sm.Q[r * PT + col]) * gq);
+      if (l16 == 0) atomicAdd(&sm.qdq[r], s);
+    }
+  }
+  lds_barrier();
+  if (tid < C) ws.qdq[(size_t)cid * C + tid] = sm.qdq[tid];
+}
+
+// ------------------------------------------------------------------ gradients, part 2
+// One block of 512 threads per chunk: dW = -dU S_b, the WY gradients T^T dW and
+// T^T dU, dv, dL, dk (with dK1), dbeta, and dalpha from dL/dB_t = q_t.dq_t - v_t.dv_t
+// summed in reverse inside the chunk plus the chunk's sum(dS_a o S_a).
+struct alignas(16) G2Smem {
+  uint16_t K[kChunk * gdb::PT], V[kChunk * gdb::PT], dU[kChunk * gdb::PT], dW[kChunk * gdb::PT];
+  uint16_t Ut[kChunk * gdb::PT];   // U~ [t][v]
+  uint16_t S[kD * gdb::PT];        // S_b [v][c], then T^T dW [t][c] and T^T dU [t][v]
+  uint16_t T[kChunk * gdb::PA];    // (I + L)^-1 [r][j]
+  uint16_t L[kChunk * gdb::PA];    // dL o (g_r/g_j) o beta_r and its transpose [r][j]
+  float lg[kChunk], g[kChunk], bt[kChunk], dbW[kChunk], dbU[kChunk], dbL[kChunk];
+};
+
+__global__ __launch_bounds__(512) void gdn_bwd_grad2_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ alpha,
+    const float* __restrict__ beta, gdb::Ws ws, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
+    float* __restrict__ dbeta, float* __restrict__ dalpha, int T) {
+  using namespace gdb;
+  __shared__ G2Smem sm;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, lq = lane >> 4;
+  const int nc = T / C, cid = blockIdx.x, n = cid / nc;
+  const size_t tok0 = (size_t)n * T + (size_t)(cid % nc) * C;
+  const uint8_t* pc = ws.prep + (size_t)cid * kWsChunk;
+  uint16_t* XW = sm.S;             // T^T dW, after dW is formed
+  uint16_t* XU = sm.S + C * PT;    // T^T dU
+
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int e = (tid + 512 * p) * 8, r = e >> 7, cc = e & 127;
+    const size_t gi = (tok0 + r) * kD + cc;
+    *reinterpret_cast<u32x4*>(sm.K + r * PT + cc) = *reinterpret_cast<const u32x4*>(k + gi);
+    *reinterpret_cast<u32x4*>(sm.V + r * PT + cc) = *reinterpret_cast<const u32x4*>(v + gi);
+    *reinterpret_cast<u32x4*>(sm.dU + r * PT + cc) = *reinterpret_cast<const u32x4*>(ws.dU + (size_t)cid * C * kD + e);
+  }
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int e = (tid + 512 * p) * 8, r = e >> 7, cc = e & 127;
+    *reinterpret_cast<u32x4*>(sm.S + r * PT + cc) = *reinterpret_cast<const u32x4*>(ws.Sb + (size_t)cid * kD * kD + e);
+    // U~ tile f = w + 8 p (rb, vb) = (f / 8, f % 8): tokens rb*16 + lq*4 + i of value vb*16 + l16
+    const int f = w + 8 * p, ub = f >> 3, vb = f & 7;
+    const u32x2 ut = *reinterpret_cast<const u32x2*>(pc + kWsU + ((size_t)f * 64 + lane) * 8);
+    const float uv[4] = {lo_bf(ut.x), hi_bf(ut.x), lo_bf(ut.y), hi_bf(ut.y)};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sm.Ut[(16 * ub + 4 * lq + i) * PT + 16 * vb + l16] = f32_to_bf16(uv[i]);
+  }
+  {
+    const int e = tid * 8, r = e >> 6, cc = e & 63;
+    *reinterpret_cast<u32x4*>(sm.T + r * PA + cc) = *reinterpret_cast<const u32x4*>(ws.T + (size_t)cid * C * C + e);
+  }
+  for (int e = tid; e < C * PA / 2; e += 512) reinterpret_cast<uint32_t*>(sm.L)[e] = 0u;
+  if (w == 0) {
+    const float lgv = wave_scan(__logf(alpha[tok0 + lane]));
+    sm.lg[lane] = lgv;
+    sm.g[lane] = __expf(lgv);
+    sm.bt[lane] = beta[tok0 + lane];
+    sm.dbW[lane] = 0.f;
+    sm.dbU[lane] = 0.f;
+    sm.dbL[lane] = 0.f;
+  }
+  lds_barrier();
+
+  const int rb = w & 3;
+  // ---- dW = -dU S_b
+#pragma unroll 1
+  for (int u = 0; u < 4; ++u) {
+    const int kb = (w >> 2) * 4 + u;
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      a = mfma(ld8(sm.dU + (16 * rb + l16) * PT + 32 * ks + 8 * lq), ld_tr8(sm.S, PT, 32 * ks, 16 * kb), a);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sm.dW[(16 * rb + 4 * lq + i) * PT + 16 * kb + l16] = f32_to_bf16(-a[i]);
+  }
+  lds_barrier();
+
+  // ---- T^T dW and T^T dU; dv = beta o T^T dU; dK_W = beta g o T^T dW (kept)
+  f32x4 kw[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int cb = (w >> 2) * 4 + u;
+    f32x4 xw = {0.f, 0.f, 0.f, 0.f}, xu = xw;
+#pragma unroll
+    for (int js = 0; js < 2; ++js)
+      if (32 * js + 31 >= 16 * rb) {   // T[j][r] is zero for j < r
+        const bf16x8 tt = ld_tr8(sm.T, PA, 32 * js, 16 * rb);
+        xw = mfma(tt, ld_tr8(sm.dW, PT, 32 * js, 16 * cb), xw);
+        xu = mfma(tt, ld_tr8(sm.dU, PT, 32 * js, 16 * cb), xu);
+      }
+    const int col = 16 * cb + l16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * rb + 4 * lq + i;
+      XW[r * PT + col] = f32_to_bf16(xw[i]);
+      XU[r * PT + col] = f32_to_bf16(xu[i]);
+      dv[(tok0 + r) * kD + col] = f32_to_bf16(sm.bt[r] * xu[i]);
+      kw[u][i] = sm.bt[r] * sm.g[r] * xw[i];
+      const float su = sum16(xu[i] * bf16_to_f32(sm.V[r * PT + col]));
+      const float sw = sum16(xw[i] * bf16_to_f32(sm.K[r * PT + col]));
+      if (l16 == 0) {
+        atomicAdd(&sm.dbU[r], su);
+        atomicAdd(&sm.dbW[r], sw);
+      }
+    }
+  }
+  lds_barrier();
+
+  // ---- dL = -(T^T dW W^T + T^T dU U~^T) on the strict lower part; with the Gram
+  // matrix K K^T for dbeta; dL o (g_r/g_j) o beta_r and its transpose to LDS
+  for (int t = w; t < 10; t += 8) {
+    int ab, cb;
+    tri_pair(t, ab, cb);
+    f32x4 a = {0.f, 0.f, 0.f, 0.f}, gk = a;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const u32x4 wfr = *reinterpret_cast<const u32x4*>(pc + kWsW + ((size_t)(cb * 4 + ks) * 64 + lane) * 16);
+      a = mfma(ld8_split(XW + (16 * ab + l16) * PT + 32 * ks + 4 * lq), as_bf(wfr), a);
+      a = mfma(ld8(XU + (16 * ab + l16) * PT + 32 * ks + 8 * lq), ld8(sm.Ut + (16 * cb + l16) * PT + 32 * ks + 8 * lq), a);
+      gk = mfma(ld8(sm.K + (16 * ab + l16) * PT + 32 * ks + 8 * lq), ld8(sm.K + (16 * cb + l16) * PT + 32 * ks + 8 * lq), gk);
+    }
+    const int j = 16 * cb + l16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * ab + 4 * lq + i;
+      float x = 0.f, y = 0.f;
+      if (j < r) {
+        const float dl = -a[i] * __expf(sm.lg[r] - sm.lg[j]);
+        x = dl * sm.bt[r];
+        y = dl * gk[i];
+        const uint16_t xb = f32_to_bf16(x);
+        sm.L[r * PA + j] = xb;
+        sm.L[j * PA + r] = xb;
+      }
+      const float sy = sum16(y);
+      if (l16 == 0) atomicAdd(&sm.dbL[r], sy);
+    }
+  }
+  lds_barrier();
+
+  // ---- dk = dK1 + dK_W + (dL' + dL'^T) K
+  const float* dK1 = ws.dK1 + (size_t)cid * C * kD;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int kb = (w >> 2) * 4 + u;
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int js = 0; js < 2; ++js)
+      a = mfma(ld8(sm.L + (16 * rb + l16) * PA + 32 * js + 8 * lq), ld_tr8(sm.K, PT, 32 * js, 16 * kb), a);
+    const int col = 16 * kb + l16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * rb + 4 * lq + i;
+      dk[(tok0 + r) * kD + col] = f32_to_bf16(dK1[r * kD + col] + kw[u][i] + a[i]);
+    }
+  }
+  lds_barrier();
+  if (w == 0) {
+    const int t = lane;
+    dbeta[tok0 + t] = sm.g[t] * sm.dbW[t] + sm.dbU[t] + sm.dbL[t];
+    const float dB = ws.qdq[(size_t)cid * C + t] - sm.bt[t] * sm.dbU[t];
+    const float off = sum64(t < 32 ? ws.bnd[(size_t)cid * 32 + t] : 0.f);
+    // reverse inclusive sum inside the chunk: lane l scans token 63 - l
+    const float rs = wave_scan(__shfl(dB, C - 1 - lane));
+    dalpha[tok0 + t] = (__shfl(rs, C - 1 - t) + off) / alpha[tok0 + t];
+  }
+}
+
+}  // namespace gdnrt
+
+using namespace gdnrt;
+
+namespace {
+
+struct BwdLayout {
+  size_t prep, T, Sb, dSa, dU, dK1, qdq, bnd, ST, total;
+};
+
+BwdLayout bwd_layout(size_t N, size_t nchunks) {
+  auto a16 = [](size_t x) { return (x + 15) & ~size_t(15); };
+  BwdLayout L;
+  L.prep = 0;
+  L.T = L.prep + nchunks * gdc::kWsChunk;
+  L.Sb = L.T + nchunks * kChunk * kChunk * 2;
+  L.dSa = L.Sb + nchunks * kD * kD * 2;
+  L.dU = L.dSa + nchunks * kD * kD * 2;
+  L.dK1 = L.dU + nchunks * kChunk * kD * 2;
+  L.qdq = L.dK1 + nchunks * kChunk * kD * 4;
+  L.bnd = L.qdq + nchunks * kChunk * 4;
+  L.ST = a16(L.bnd + nchunks * 32 * 4);
+  L.total = L.ST + N * kD * kD * 4;
+  return L;
+}
+
+}  // namespace
+
+extern "C" size_t gdn_chunk_bwd_workspace_bytes(int N, int T, int dk, int dv, int chunk) {
+  if (N <= 0 || T <= 0 || dk != kD || dv != kD || chunk != kChunk || T % kChunk) return 0;
+  return bwd_layout((size_t)N, (size_t)N * (T / kChunk)).total;
+}
+
+extern "C" int gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* alpha,
+                             const float* beta, const float* S0, const void* dO, const float* dST,
+                             void* dq, void* dk, void* dv, float* dalpha, float* dbeta, float* dS0, int N,
+                             int T, int dk_, int dv_, int chunk, int io, void* workspace, size_t ws_bytes,
+                             void* stream) {
+  const char* fn = "gdn_chunk_bwd";
+  if (N < 0 || T < 0) return set_error(GDNRT_ESHAPE, "%s: N=%d T=%d must be >= 0", fn, N, T);
+  if (dk_ != kD || dv_ != kD) return set_error(GDNRT_ESHAPE, "%s: d_k=%d d_v=%d, only 128 is supported", fn, dk_, dv_);
+  if (chunk != kChunk) return set_error(GDNRT_ESHAPE, "%s: chunk=%d, only 64 is supported", fn, chunk);
+  if (T % kChunk) return set_error(GDNRT_ESHAPE, "%s: T=%d is not a multiple of 64", fn, T);
+  if (io != GDNRT_BF16) return set_error(GDNRT_EDTYPE, "%s: io must be GDNRT_BF16", fn);
+  if ((size_t)N * (T / kChunk) > 0x7fffffffu || (size_t)N * 8 > 0x7fffffffu)
+    return set_error(GDNRT_ESHAPE, "%s: N=%d T=%d too large", fn, N, T);
+  if (N == 0) return clear_error();
+  if (!dS0 || (T > 0 && (!q || !k || !v || !alpha || !beta || !dO || !dq || !dk || !dv || !dalpha || !dbeta)))
+    return set_error(GDNRT_EINVAL, "%s: null pointer argument", fn);
+  const size_t nchunks = (size_t)N * (T / kChunk);
+  const BwdLayout lay = bwd_layout((size_t)N, nchunks);
+  const size_t need = T > 0 ? lay.total : 0;
+  if (ws_bytes < need || (need && !workspace))
+    return set_error(GDNRT_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
+  if ((T > 0 && (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned16(workspace) ||
+                 !aligned4(alpha) || !aligned4(beta) || !aligned4(dq) || !aligned4(dk) || !aligned4(dv) ||
+                 !aligned4(dalpha) || !aligned4(dbeta))) ||
+      !aligned4(dS0) || (S0 && !aligned4(S0)) || (dST && !aligned4(dST)))
+    return set_error(GDNRT_EALIGN, "%s: q, k, v, dO, workspace must be 16-byte aligned", fn);
+  const size_t ntok = (size_t)N * T, nIO = ntok * kD * 2, nG = ntok * 4, nS = (size_t)N * kD * kD * 4;
+  struct Buf {
+    const void* p;
+    size_t n;
+  };
+  const Buf ins[] = {{q, nIO}, {k, nIO}, {v, nIO}, {dO, nIO}, {alpha, nG}, {beta, nG}, {S0, nS}, {dST, nS}};
+  const Buf outs[] = {{dq, nIO}, {dk, nIO}, {dv, nIO}, {dalpha, nG}, {dbeta, nG}, {dS0, nS}, {workspace, need}};
+  for (const Buf& a : outs) {
+    for (const Buf& b : ins)
+      if (overlaps(a.p, a.n, b.p, b.n)) return set_error(GDNRT_EINVAL, "%s: an output overlaps an input", fn);
+    for (const Buf& b : outs)
+      if (a.p != b.p && overlaps(a.p, a.n, b.p, b.n)) return set_error(GDNRT_EINVAL, "%s: outputs overlap", fn);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 0) {   // no tokens: the state gradient passes through
+    hipLaunchKernelGGL(gdn_bwd_rscan_kernel, dim3((unsigned)(N * 8)), dim3(256), 0, s, nullptr, nullptr, dST,
+                       nullptr, nullptr, nullptr, nullptr, dS0, 0);
+    return check_launch(fn);
+  }
+  uint8_t* base = static_cast<uint8_t*>(workspace);
+  gdb::Ws ws;
+  ws.prep = base + lay.prep;
+  ws.T = reinterpret_cast<uint16_t*>(base + lay.T);
+  ws.Sb = reinterpret_cast<uint16_t*>(base + lay.Sb);
+  ws.dSa = reinterpret_cast<uint16_t*>(base + lay.dSa);
+  ws.dU = reinterpret_cast<uint16_t*>(base + lay.dU);
+  ws.dK1 = reinterpret_cast<float*>(base + lay.dK1);
+  ws.qdq = reinterpret_cast<float*>(base + lay.qdq);
+  ws.bnd = reinterpret_cast<float*>(base + lay.bnd);
+  ws.ST = reinterpret_cast<float*>(base + lay.ST);
+  const uint16_t* q16 = static_cast<const uint16_t*>(q);
+  const uint16_t* k16 = static_cast<const uint16_t*>(k);
+  const uint16_t* v16 = static_cast<const uint16_t*>(v);
+  const uint16_t* o16 = static_cast<const uint16_t*>(dO);
+  gdn_chunk_prep_with_inverse(q16, k16, v16, alpha, beta, ws.prep, ws.T, T, (int)nchunks, s);
+  int rc = check_launch(fn);
+  if (rc != GDNRT_OK) return rc;
+  hipLaunchKernelGGL(gdn_bwd_fscan_kernel, dim3((unsigned)(N * 8)), dim3(256), 0, s, ws.prep, S0, ws.Sb, ws.ST, T);
+  hipLaunchKernelGGL(gdn_bwd_rscan_kernel, dim3((unsigned)(N * 8)), dim3(256), 0, s, ws.prep, o16, dST, ws.Sb,
+                     ws.ST, ws.dSa, ws.bnd, dS0, T);
+  hipLaunchKernelGGL(gdn_bwd_grad1_kernel, dim3((unsigned)nchunks), dim3(512), 0, s, q16, k16, o16, alpha, ws,
+                     static_cast<uint16_t*>(dq), T);
+  hipLaunchKernelGGL(gdn_bwd_grad2_kernel, dim3((unsigned)nchunks), dim3(512), 0, s, k16, v16, alpha, beta, ws,
+                     static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), dbeta, dalpha, T);
+  return check_launch(fn);
+}

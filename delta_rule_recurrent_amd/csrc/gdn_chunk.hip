@@ -26,6 +26,7 @@
 // the triangular inverse is fp32 (16 x 16 diagonal blocks by substitution, the
 // blocks below by v_mfma_f32_16x16x4_f32).
 #include "common.hpp"
+#include "gdn_chunk_layout.hpp"
 
 namespace gdnrt {
 
@@ -37,16 +38,7 @@ constexpr int PQ = kD + 8;  // bf16 pitch of 128-wide rows (16-byte aligned, con
 constexpr int PC = C + 8;   // bf16 pitch of 64-wide rows
 constexpr int PF = C + 4;   // fp32 pitch of 64-wide rows (16-byte aligned)
 
-// Workspace per chunk (bytes). With lane = 16 lq + l16 of a wave:
-//  W, Q' [64 tokens][128 keys]: 16 A-operand fragments (rb, ks) of 1 KB; lane holds
-//        token rb*16 + l16, keys ks*32 + lq*4 + {0..3} then ks*32 + 16 + lq*4 + {0..3}
-//  K^    [64 tokens][128 keys]: 16 B-operand fragments (kb, js); lane holds key
-//        kb*16 + l16, tokens js*32 + lq*8 + {0..7}
-//  U~, O~ [64 tokens][128 values]: 32 accumulator tiles (rb, vb) of 512 B; lane holds
-//        tokens rb*16 + lq*4 + {0..3} of value vb*16 + l16
-//  g_C   16 copies (so that every lane loads it with a vector load)
-constexpr size_t kWsW = 0, kWsQ = 16384, kWsK = 32768, kWsU = 49152, kWsO = 65536;
-constexpr size_t kWsG = 81920, kWsChunk = 81984;
+// Workspace per chunk: gdn_chunk_layout.hpp (kWsW .. kWsChunk).
 // KDA: the chunk's state decay is a vector over key channels (128 fp32 at kWsG)
 constexpr size_t kWsChunkKda = kWsG + kD * 4;
 template <bool KDA>
@@ -216,12 +208,13 @@ namespace gdc {
 
 // One chunk of the prep: stages the inputs held in `in`, requests the next chunk's into
 // `in`, and writes the chunk's operands to the workspace.
-template <bool KDA>
+template <bool KDA, bool STORE_T>
 __device__ __forceinline__ void prep_chunk(PrepSmem& sm, KdaPrepSmem<KDA>& xs, PrepIn<KDA>& in, int cid,
                                            const uint16_t* __restrict__ q,
                                            const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                            const float* __restrict__ alpha, const float* __restrict__ beta,
-                                           uint8_t* __restrict__ ws, int T, int nchunks) {
+                                           uint8_t* __restrict__ ws, uint16_t* __restrict__ Tout, int T,
+                                           int nchunks) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lq = lane >> 4;
   const int nc = T / C;
@@ -430,6 +423,9 @@ __device__ __forceinline__ void prep_chunk(PrepSmem& sm, KdaPrepSmem<KDA>& xs, P
     if ((j >> 4) <= (r >> 4)) t = *reinterpret_cast<const f32x2*>(sm.rt.T + r * PF + j);
     *reinterpret_cast<unsigned*>(sm.rw.t.Tw + r * PC + j) = pack_bf16(t.x * sm.btg[j], t.y * sm.btg[j + 1]);
     *reinterpret_cast<unsigned*>(sm.rw.t.Tu + r * PC + j) = pack_bf16(t.x * sm.bt[j], t.y * sm.bt[j + 1]);
+    if constexpr (STORE_T)   // T itself for the backward, bf16 [r][j], zero above the diagonal
+      *reinterpret_cast<unsigned*>(Tout + (size_t)cid * C * C + r * C + j) =
+          pack_bf16(j <= r ? t.x : 0.f, j + 1 <= r ? t.y : 0.f);
   }
   lds_barrier();
 
@@ -523,11 +519,13 @@ __device__ __forceinline__ void prep_chunk(PrepSmem& sm, KdaPrepSmem<KDA>& xs, P
 // loaded into registers while this one is processed, and every thread issues the
 // same loads and stores on every chunk so that those waits are exact (the first chunk
 // is peeled, so that the loop's waits do not also serve the loads issued before it).
-template <bool KDA>
+// With STORE_T the chunk's (I + L)^-1 is also written (bf16 [64][64] per chunk, to
+// Tout) for the chunkwise backward.
+template <bool KDA, bool STORE_T>
 __global__ __launch_bounds__(512) void gdn_chunk_prep_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, uint8_t* __restrict__ ws,
-    int T, int nchunks) {
+    uint16_t* __restrict__ Tout, int T, int nchunks) {
   using namespace gdc;
   __shared__ PrepSmem sm;
   __shared__ KdaPrepSmem<KDA> xs;
@@ -535,9 +533,9 @@ __global__ __launch_bounds__(512) void gdn_chunk_prep_kernel(
   PrepIn<KDA> in;
   int cid = blockIdx.x;   // the grid never exceeds nchunks
   prep_fetch<KDA>(in, q, k, v, alpha, beta, (size_t)(cid / nc) * T + (size_t)(cid % nc) * C);
-  prep_chunk<KDA>(sm, xs, in, cid, q, k, v, alpha, beta, ws, T, nchunks);
+  prep_chunk<KDA, STORE_T>(sm, xs, in, cid, q, k, v, alpha, beta, ws, Tout, T, nchunks);
   for (cid += gridDim.x; cid < nchunks; cid += gridDim.x)
-    prep_chunk<KDA>(sm, xs, in, cid, q, k, v, alpha, beta, ws, T, nchunks);
+    prep_chunk<KDA, STORE_T>(sm, xs, in, cid, q, k, v, alpha, beta, ws, Tout, T, nchunks);
 }
 
 // ------------------------------------------------------------------ sequential pass
@@ -818,9 +816,9 @@ int chunk_fwd(const char* fn, const void* q, const void* k, const void* v, const
   if (T > 0) {
     // one persistent block per CU (the LDS of a block fills most of one)
     const unsigned grid = (unsigned)(nchunks < 256 ? nchunks : 256);
-    hipLaunchKernelGGL(gdn_chunk_prep_kernel<KDA>, dim3(grid), dim3(gdc::NT), 0, s,
+    hipLaunchKernelGGL((gdn_chunk_prep_kernel<KDA, false>), dim3(grid), dim3(gdc::NT), 0, s,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                       static_cast<const uint16_t*>(v), alpha, beta, ws, T, (int)nchunks);
+                       static_cast<const uint16_t*>(v), alpha, beta, ws, nullptr, T, (int)nchunks);
     int rc = check_launch(fn);
     if (rc != GDNRT_OK) return rc;
   }
@@ -835,6 +833,19 @@ int chunk_fwd(const char* fn, const void* q, const void* k, const void* v, const
 }
 
 }  // namespace
+
+namespace gdnrt {
+// The GDN chunk prep for the chunkwise backward: the forward's operands (at the
+// forward's per-chunk stride) and each chunk's (I + L)^-1. T > 0, shapes checked by
+// the caller.
+void gdn_chunk_prep_with_inverse(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                 const float* alpha, const float* beta, uint8_t* ws, uint16_t* Tout,
+                                 int T, int nchunks, hipStream_t s) {
+  const unsigned grid = (unsigned)(nchunks < 256 ? nchunks : 256);
+  hipLaunchKernelGGL((gdn_chunk_prep_kernel<false, true>), dim3(grid), dim3(gdc::NT), 0, s, q, k, v, alpha,
+                     beta, ws, Tout, T, nchunks);
+}
+}  // namespace gdnrt
 
 extern "C" size_t gdn_chunk_fwd_workspace_bytes(int N, int T, int dk, int dv, int chunk) {
   return chunk_workspace_bytes<false>(N, T, dk, dv, chunk);

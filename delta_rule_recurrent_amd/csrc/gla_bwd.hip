@@ -21,13 +21,16 @@
 //
 // The gate gradient uses that b enters only through q o e^B and k o e^{-B} (B the
 // cumulative log-gate over the whole sequence): dL/dB_t = q_t o dq_t - k_t o dk_t,
-// plus sum_v dS_T o S_T at the last token, and d log_g is its reverse cumulative sum.
+// and d log_g_t = sum_{s >= t} dL/dB_s. Shifting B on every token after a chunk (in one
+// key channel) scales that key column of the state the next chunk starts from, so the
+// part of the sum beyond the chunk is sum_v dS_a o S_a (dST o S_T after the last
+// chunk): only sums over at most 64 tokens remain, and no rounding error accumulates
+// along the sequence.
 //
-// Five kernels: a per-chunk prep (cumulative gates, the scaled operands), a forward
+// Four kernels: a per-chunk prep (cumulative gates, the scaled operands), a forward
 // state scan (the state before every chunk), a backward state scan (the gradient after
-// every chunk, and dS_0), a per-chunk gradient kernel (bf16 MFMA, fp32 accumulation;
-// also the gates' reverse cumulative sum within the chunk), and the later chunks'
-// totals added to the gate gradient.
+// every chunk, dS_0 and the chunks' sum_v dS_a o S_a), and a per-chunk gradient kernel
+// (bf16 MFMA, fp32 accumulation; also the gate gradient).
 #include "common.hpp"
 
 namespace gdnrt {
@@ -42,7 +45,7 @@ constexpr int PX = 16 + 16;  // bf16 pitch of 16-wide rows (one value tile) read
 // Workspace per chunk (bytes): bf16 [64][128] Q^, K^; fp32 [64][128] E = e^{b - b_m};
 // fp32 [128] e^{b_C}, e^{b_m}, e^{b_C - b_m}; bf16 [128][128] the state before the
 // chunk and the state gradient after it. Then per sequence the fp32 final state of the
-// recomputed forward, and per chunk the fp32 [128] totals of the gate gradient.
+// recomputed forward, and per chunk fp32 [8][128] sum_v dS_a o S_a by value tile.
 constexpr size_t kQh = 0, kKh = 16384, kE = 32768, kEC = 65536, kEm = 66048, kECm = 66560,
                  kSb = 67072, kdS = 99840, kChunkB = 132608;
 
@@ -147,13 +150,17 @@ __global__ __launch_bounds__(256) void gla_bwd_prep_kernel(const uint16_t* __res
 // 4 lq + i, column 32 w + 16 j + l16). Per chunk (forward: first to last; reverse: last
 // to first) the state is stored in bf16 to the workspace, then
 //   forward:  S  <- e^{b_C} o S  + V^T K^     (X = V,  Y = K^)
-//   reverse:  dS <- e^{b_C} o dS + dO^T Q^    (X = dO, Y = Q^).
+//   reverse:  dS <- e^{b_C} o dS + dO^T Q^    (X = dO, Y = Q^);
+// the reverse scan also writes this tile's sum_v dS o S per key channel, S the state
+// after the chunk (the next chunk's stored state, or ST after the last one).
 // The next chunk's X and Y are loaded into registers while this one is computed.
 template <bool REV>
 __global__ __launch_bounds__(256) void gla_bwd_scan_kernel(const uint16_t* __restrict__ X,
                                                            uint8_t* __restrict__ ws,
                                                            const float* __restrict__ Sinit,
-                                                           float* __restrict__ Sout, int T) {
+                                                           float* __restrict__ Sout,
+                                                           const float* __restrict__ ST,
+                                                           float* __restrict__ bnd, int T) {
   using namespace glab;
   __shared__ __attribute__((aligned(16))) uint16_t sx[C * PX];
   __shared__ __attribute__((aligned(16))) uint16_t sy[C * PT];
@@ -182,7 +189,18 @@ __global__ __launch_bounds__(256) void gla_bwd_scan_kernel(const uint16_t* __res
       acc[j][i] = Sinit ? Sinit[((size_t)n * kD + v0 + 4 * lq + i) * kD + 32 * w + 16 * j + l16] : 0.f;
 
   // thread's pieces: X row tid / 4, values 4 (tid % 4) ..; Y 16-byte pieces tid + 256 p
-  auto load = [&](int ci, u32x2& xr, u32x4 (&yr)[4], float (&ec)[2]) {
+  auto load = [&](int ci, u32x2& xr, u32x4 (&yr)[4], float (&ec)[2], float (&sa)[2][4]) {
+    if constexpr (REV) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const size_t e = (size_t)(v0 + 4 * lq + i) * kD + 32 * w + 16 * j + l16;
+          sa[j][i] = ci + 1 < nc
+                         ? bf16_to_f32(reinterpret_cast<const uint16_t*>(ws + (chunk0 + ci + 1) * kChunkB + kSb)[e])
+                         : ST[(size_t)n * kD * kD + e];
+        }
+    }
     const size_t tok = (size_t)n * T + (size_t)ci * C;
     xr = *reinterpret_cast<const u32x2*>(X + (tok + (tid >> 2)) * kD + v0 + 4 * (tid & 3));
     const uint8_t* wsc = ws + (chunk0 + ci) * kChunkB;
@@ -193,8 +211,8 @@ __global__ __launch_bounds__(256) void gla_bwd_scan_kernel(const uint16_t* __res
   };
   u32x2 xr;
   u32x4 yr[4];
-  float ec[2];
-  if (nc > 0) load(REV ? nc - 1 : 0, xr, yr, ec);
+  float ec[2], sa[2][4];
+  if (nc > 0) load(REV ? nc - 1 : 0, xr, yr, ec, sa);
   for (int s = 0; s < nc; ++s) {
     const int ci = REV ? nc - 1 - s : s;
     // this chunk's state (forward) or state gradient (reverse), in bf16
@@ -203,6 +221,15 @@ __global__ __launch_bounds__(256) void gla_bwd_scan_kernel(const uint16_t* __res
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) dst[(v0 + 4 * lq + i) * kD + 32 * w + 16 * j + l16] = f32_to_bf16(acc[j][i]);
+    if constexpr (REV) {   // sum over this tile's 16 value rows of dS o S, per key channel
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        float x = ((acc[j][0] * sa[j][0] + acc[j][1] * sa[j][1]) + (acc[j][2] * sa[j][2] + acc[j][3] * sa[j][3]));
+        x += __shfl_xor(x, 16);
+        x += __shfl_xor(x, 32);
+        if (lq == 0) bnd[((chunk0 + ci) * 8 + vt) * kD + 32 * w + 16 * j + l16] = x;
+      }
+    }
     *reinterpret_cast<u32x2*>(sx + (tid >> 2) * PX + 4 * (tid & 3)) = xr;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -210,7 +237,7 @@ __global__ __launch_bounds__(256) void gla_bwd_scan_kernel(const uint16_t* __res
       *reinterpret_cast<u32x4*>(sy + (e >> 7) * PT + (e & 127)) = yr[p];
     }
     const float e0 = ec[0], e1 = ec[1];
-    if (s + 1 < nc) load(REV ? ci - 1 : ci + 1, xr, yr, ec);
+    if (s + 1 < nc) load(REV ? ci - 1 : ci + 1, xr, yr, ec, sa);
     lds_barrier();
     acc[0] *= e0;
     acc[1] *= e1;
@@ -238,9 +265,9 @@ struct alignas(16) GradSmem {
 
 __global__ __launch_bounds__(512) void gla_bwd_grad_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ dO, const uint8_t* __restrict__ ws, const float* __restrict__ dST,
-    const float* __restrict__ ST, uint16_t* __restrict__ dq, uint16_t* __restrict__ dk,
-    uint16_t* __restrict__ dv, float* __restrict__ dg, float* __restrict__ totals, int T) {
+    const uint16_t* __restrict__ dO, const uint8_t* __restrict__ ws, const float* __restrict__ bnd,
+    uint16_t* __restrict__ dq, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
+    float* __restrict__ dg, int T) {
   using namespace glab;
   __shared__ GradSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, lq = lane >> 4;
@@ -350,26 +377,21 @@ __global__ __launch_bounds__(512) void gla_bwd_grad_kernel(
     }
   }
 
-  // ---- d log_g inside the chunk: the reverse cumulative sum of dL/dB over its tokens
-  // (fp32 [64][132] over the state tiles, 16-token segment totals over A), starting at
-  // sum_v dS_T o S_T in the sequence's last chunk; the chunk total goes to `totals`
+  // ---- d log_g: the reverse cumulative sum of dL/dB over the chunk's tokens (fp32
+  // [64][132] over the state tiles, 16-token segment totals over A) plus the chunk's
+  // sum_v dS_a o S_a (eight value-tile parts)
   constexpr int PG = kD + 4;
   float* G = reinterpret_cast<float*>(sm.Sb);
-  float* seg = reinterpret_cast<float*>(sm.A);   // [4][128] segment totals, [128] start
+  float* seg = reinterpret_cast<float*>(sm.A);   // [4][128] segment totals
   lds_barrier();
 #pragma unroll
   for (int u = 0; u < 4; ++u)
 #pragma unroll
     for (int i = 0; i < 4; ++i) G[(16 * rb + 4 * lq + i) * PG + 16 * ((w >> 2) * 4 + u) + l16] = dB[u][i];
   const int c = tid & (kD - 1), h = tid >> 7;
-  const bool last = dST && (cid % nc) == nc - 1;
   float start = 0.f;
-  if (last) {   // rows 32 h .. 32 h + 31 of the final state
-    const size_t base = (size_t)(cid / nc) * kD * kD + c;
-#pragma unroll 8
-    for (int r = 32 * h; r < 32 * h + 32; ++r) start += dST[base + (size_t)r * kD] * ST[base + (size_t)r * kD];
-    seg[4 * kD + h * kD + c] = start;
-  }
+#pragma unroll
+  for (int p = 0; p < 8; ++p) start += bnd[((size_t)cid * 8 + p) * kD + c];
   lds_barrier();
   float run = 0.f, x[16];
 #pragma unroll
@@ -379,35 +401,11 @@ __global__ __launch_bounds__(512) void gla_bwd_grad_kernel(
   }
   seg[h * kD + c] = run;
   lds_barrier();
-  float off = 0.f;
-  if (last) off = seg[4 * kD + c] + seg[5 * kD + c] + seg[6 * kD + c] + seg[7 * kD + c];
+  float off = start;
   for (int j = 3; j > h; --j) off += seg[j * kD + c];
   float* p = dg + (tok0 + 16 * h) * kD + c;
 #pragma unroll
   for (int t = 0; t < 16; ++t) p[(size_t)t * kD] = x[t] + off;
-  if (h == 0) totals[(size_t)cid * kD + c] = off + run;
-}
-
-// ------------------------------------------------------------------ gate gradient
-// d log_g is the reverse cumulative sum over the sequence of dL/dB; the gradient
-// kernel leaves the sums within each chunk and the chunk totals, and one block of 128
-// threads (one per key channel) per chunk adds every later chunk's total.
-__global__ __launch_bounds__(128) void gla_bwd_gate_offset_kernel(float* __restrict__ dg,
-                                                                  const float* __restrict__ totals, int T) {
-  const int c = threadIdx.x, nc = T / kChunk, cid = blockIdx.x, n = cid / nc, ci = cid % nc;
-  if (ci == nc - 1) return;
-  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j0 = ci + 1; j0 < nc; j0 += 8)
-#pragma unroll
-    for (int u = 0; u < 8; ++u)   // eight independent loads in flight
-      if (j0 + u < nc) o[u] += totals[((size_t)n * nc + j0 + u) * kD + c];
-  const float off = ((o[0] + o[1]) + (o[2] + o[3])) + ((o[4] + o[5]) + (o[6] + o[7]));
-  float* p = dg + ((size_t)n * T + (size_t)ci * kChunk) * kD + c;
-  float x[kChunk];
-#pragma unroll
-  for (int t = 0; t < kChunk; ++t) x[t] = p[(size_t)t * kD];
-#pragma unroll
-  for (int t = 0; t < kChunk; ++t) p[(size_t)t * kD] = x[t] + off;
 }
 
 }  // namespace gdnrt
@@ -417,8 +415,8 @@ using namespace gdnrt;
 extern "C" size_t gla_chunk_bwd_workspace_bytes(int N, int T, int dk, int dv, int chunk) {
   if (N <= 0 || T <= 0 || dk != kD || dv != kD || chunk != kChunk || T % kChunk) return 0;
   // per chunk the operands and states, then per sequence the recomputed final state,
-  // then per chunk the gate-gradient totals
-  return (size_t)N * (T / kChunk) * (glab::kChunkB + kD * 4) + (size_t)N * kD * kD * 4;
+  // then per chunk sum_v dS_a o S_a by value tile
+  return (size_t)N * (T / kChunk) * (glab::kChunkB + 8 * kD * 4) + (size_t)N * kD * kD * 4;
 }
 
 extern "C" int gla_chunk_bwd(const void* q, const void* k, const void* v, const float* log_g,
@@ -436,7 +434,7 @@ extern "C" int gla_chunk_bwd(const void* q, const void* k, const void* v, const 
   if (!dS0 || (T > 0 && (!q || !k || !v || !log_g || !dO || !dq || !dk || !dv || !dlog_g)))
     return set_error(GDNRT_EINVAL, "%s: null pointer argument", fn);
   const size_t nchunks = (size_t)N * (T / kChunk);
-  const size_t need = nchunks * (glab::kChunkB + kD * 4) + (size_t)N * kD * kD * 4;
+  const size_t need = nchunks * (glab::kChunkB + 8 * kD * 4) + (size_t)N * kD * kD * 4;
   if (ws_bytes < need || !workspace)
     return set_error(GDNRT_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
   if ((T > 0 && (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned16(log_g) ||
@@ -464,7 +462,7 @@ extern "C" int gla_chunk_bwd(const void* q, const void* k, const void* v, const 
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   float* ST = reinterpret_cast<float*>(ws + nchunks * glab::kChunkB);   // recomputed final states
-  float* totals = ST + (size_t)N * kD * kD;                             // per chunk, d log_g totals
+  float* bnd = ST + (size_t)N * kD * kD;                                // per chunk, sum_v dS_a o S_a
   if (T > 0) {
     hipLaunchKernelGGL(gla_bwd_prep_kernel, dim3((unsigned)nchunks), dim3(256), 0, s,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), log_g, ws, T);
@@ -472,17 +470,15 @@ extern "C" int gla_chunk_bwd(const void* q, const void* k, const void* v, const 
     if (rc != GDNRT_OK) return rc;
   }
   hipLaunchKernelGGL(gla_bwd_scan_kernel<false>, dim3((unsigned)(N * 8)), dim3(256), 0, s,
-                     static_cast<const uint16_t*>(v), ws, S0, ST, T);
+                     static_cast<const uint16_t*>(v), ws, S0, ST, nullptr, nullptr, T);
   hipLaunchKernelGGL(gla_bwd_scan_kernel<true>, dim3((unsigned)(N * 8)), dim3(256), 0, s,
-                     static_cast<const uint16_t*>(dO), ws, dST, dS0, T);
+                     static_cast<const uint16_t*>(dO), ws, dST, dS0, ST, bnd, T);
   if (T > 0) {
     hipLaunchKernelGGL(gla_bwd_grad_kernel, dim3((unsigned)nchunks), dim3(512), 0, s,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dO), ws, dST, ST,
+                       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dO), ws, bnd,
                        static_cast<uint16_t*>(dq), static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv),
-                       dlog_g, totals, T);
-    hipLaunchKernelGGL(gla_bwd_gate_offset_kernel, dim3((unsigned)nchunks), dim3(128), 0, s, dlog_g,
-                       totals, T);
+                       dlog_g, T);
   }
   return check_launch(fn);
 }

@@ -126,7 +126,7 @@ GDNRT_API size_t gla_chunk_fwd_workspace_bytes(int N, int T, int dk, int dv, int
  *   q, k, v, dO [N][T][d] bf16 and log_g fp32: 16-byte aligned. S0, dST may be NULL
  *   (zero). workspace: gla_chunk_bwd_workspace_bytes() bytes, 16-byte aligned,
  *   overwritten (per chunk the scaled operands, the state before the chunk and the
- *   state gradient after it, in bf16, and the gate-gradient totals: 133,120 bytes; per
+ *   state gradient after it, in bf16, and sum_v dS o S by value tile: 136,704 bytes; per
  *   sequence the recomputed final state).
  * The gate gradient is the reverse cumulative sum of q o dq - k o dk (plus dST o S_T
  * summed over value channels at the last token). T must be a multiple of 64.
@@ -168,6 +168,38 @@ GDNRT_API int gdn_chunk_fwd(const void* q, const void* k, const void* v,
 /* Workspace bytes gdn_chunk_fwd needs for this shape (0 if the shape is unsupported
  * or empty). */
 GDNRT_API size_t gdn_chunk_fwd_workspace_bytes(int N, int T, int dk, int dv, int chunk);
+
+/*
+ * Gated DeltaNet chunkwise backward of one sequence shard: for the forward of
+ * gdn_chunk_fwd from S0 and the scalar L = sum(dO o o) + sum(dST o S_T), writes
+ *   dq, dk [N][T][dk], dv [N][T][dv] (bf16), dalpha, dbeta [N][T] (fp32) and dS0
+ *   [N][dv][dk] (fp32, the gradient with respect to the incoming state).
+ * The pages print no backward for the delta rule; this one differentiates the
+ * forward's chunk form (above): the state gradient runs backward over the chunks,
+ *   dS_b = g_C dS_a + dO^T Q' - (diag(g_C/g) K dS_a^T)^T W,
+ * each chunk's gradients go through U = U~ - W S_b^T, A and the WY factors
+ * (T = (I + L)^-1, W, U~), and the decay gradient follows from the cumulative
+ * log-decay B_t entering only as q_t e^{B_t} and v_t e^{-B_t} once the state is
+ * divided by e^{B_t}: d log alpha_t = sum_{s >= t} (q_s.dq_s - v_s.dv_s), plus
+ * sum(dST o S_T), and dalpha = d log alpha / alpha.
+ *   q, k, v, dO [N][T][d] bf16, 16-byte aligned; alpha (in (0,1)), beta [N][T] fp32.
+ *   S0, dST [N][dv][dk] fp32 or NULL (zero). Outputs must not overlap inputs.
+ *   workspace: gdn_chunk_bwd_workspace_bytes() bytes, 16-byte aligned, overwritten
+ *   (per chunk the forward's operands, (I + L)^-1, the state before the chunk and the
+ *   state gradient after it in bf16, dU, a partial dk, q.dq and the chunk's
+ *   sum(dS o S) in 32 parts: 205,248 bytes; per
+ *   sequence the recomputed final state). May be NULL when T = 0.
+ * T must be a multiple of 64 (chunk).
+ */
+GDNRT_API int gdn_chunk_bwd(const void* q, const void* k, const void* v,
+                            const float* alpha, const float* beta, const float* S0,
+                            const void* dO, const float* dST,
+                            void* dq, void* dk, void* dv, float* dalpha, float* dbeta, float* dS0,
+                            int N, int T, int dk_, int dv_, int chunk, int io,
+                            void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace bytes gdn_chunk_bwd needs for this shape (0 if unsupported or empty). */
+GDNRT_API size_t gdn_chunk_bwd_workspace_bytes(int N, int T, int dk, int dv, int chunk);
 
 /*
  * Kimi Delta Attention chunkwise forward (prefill): the recurrence of

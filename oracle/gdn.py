@@ -210,9 +210,13 @@ def gdn_chunk_wy_bwd(q, k, v, alpha, beta, S0, dO, dST=None, chunk=64):
         dS_0 = g_C dS + dO^T diag(g) Q - dU^T W        (the state-gradient scan)
     The decay enters the recurrence only through q_t e^{B_t} and v_t e^{-B_t} (B the
     cumulative log-decay over the sequence; dividing S_t by e^{B_t} removes the decay),
-    so dL/dB_t = q_t . dq_t - v_t . dv_t (+ sum(dST o S_T) at the last token),
-    d log alpha is its reverse cumulative sum and dalpha = d log alpha / alpha.
-    Returns (dq, dk, dv, dalpha, dbeta, dS0). T must be a multiple of ``chunk``.
+    so dL/dB_t = q_t . dq_t - v_t . dv_t and d log alpha_t = sum_{s >= t} dL/dB_s.
+    The part of that sum beyond the chunk is a shift of B on every later token, i.e.
+    a scaling of the state the next chunk starts from, so it equals sum(dS o S) with S
+    the state after the chunk and dS its gradient (dST o S_T after the last chunk):
+        d log alpha_t = sum_{s >= t in the chunk} (q_s . dq_s - v_s . dv_s) + sum(dS_a o S_a),
+    and dalpha = d log alpha / alpha. Returns (dq, dk, dv, dalpha, dbeta, dS0). T must
+    be a multiple of ``chunk``.
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -243,9 +247,10 @@ def gdn_chunk_wy_bwd(q, k, v, alpha, beta, S0, dO, dST=None, chunk=64):
             Tm = np.linalg.inv(I + Ms * bt[:, None] * Gam * (K @ K.T))
             U = Tm @ (bt[:, None] * V) - Tm @ ((bt * g)[:, None] * K) @ S.T
             S = g[-1] * S + U.T @ (np.exp(lg[-1] - lg)[:, None] * K)
-        ST = S
+        starts.append(S)                    # the final state, after the last chunk
         dS = np.zeros((dv, dk)) if dST is None else np.array(dST[n], dtype=np.float64)
         for ci in range(T // chunk - 1, -1, -1):
+            boundary = float((dS * starts[ci + 1]).sum())
             sl = slice(ci * chunk, ci * chunk + chunk)
             Q, K, V, bt, dOc, Sb = q[n, sl], k[n, sl], v[n, sl], beta[n, sl], dO[n, sl], starts[ci]
             lg = np.cumsum(np.log(alpha[n, sl]))
@@ -269,10 +274,8 @@ def gdn_chunk_wy_bwd(q, k, v, alpha, beta, S0, dO, dST=None, chunk=64):
             dV = bt[:, None] * dXU
             dbeta[n, sl] = g * np.einsum("rc,rc->r", dXW, K) + np.einsum("rv,rv->r", dXU, V) + (dL * Gam * KK).sum(1)
             dq[n, sl], dk_[n, sl], dv_[n, sl] = dQ, dK, dV
+            dB = np.einsum("tk,tk->t", Q, dQ) - np.einsum("tv,tv->t", V, dV)
+            dlog[n, sl] = np.cumsum(dB[::-1])[::-1] + boundary
             dS = g[-1] * dS + dOc.T @ (g[:, None] * Q) - dU.T @ W
         dS0[n] = dS
-        dB = np.einsum("tk,tk->t", q[n], dq[n]) - np.einsum("tv,tv->t", v[n], dv_[n])
-        if dST is not None and T:
-            dB[-1] += float((dST[n] * ST).sum())
-        dlog[n] = np.cumsum(dB[::-1])[::-1]
     return dq, dk_, dv_, dlog / alpha, dbeta, dS0

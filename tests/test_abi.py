@@ -35,7 +35,8 @@ def test_header_declares_the_entry_points():
               "leapq_window_flush", "gdnrt_last_error", "gdn_chunk_fwd_workspace_bytes",
               "gla_chunk_fwd_workspace_bytes", "kda_decode_step", "kda_leapq_decode_step",
               "kda_leapq_window_flush", "kda_chunk_fwd", "kda_chunk_fwd_workspace_bytes",
-              "gla_chunk_bwd", "gla_chunk_bwd_workspace_bytes"):
+              "gla_chunk_bwd", "gla_chunk_bwd_workspace_bytes", "gdn_chunk_bwd",
+              "gdn_chunk_bwd_workspace_bytes"):
         assert n in names, n
 
 
@@ -152,7 +153,7 @@ def test_kda_chunk_validation(lib):
 def test_gla_bwd_validation(lib):
     p = ctypes.c_void_p(4096)
     f = lib.gla_chunk_bwd
-    assert lib.gla_chunk_bwd_workspace_bytes(64, 4096, 128, 128, 64) == 64 * 64 * (132608 + 512) + 64 * 65536
+    assert lib.gla_chunk_bwd_workspace_bytes(64, 4096, 128, 128, 64) == 64 * 64 * (132608 + 4096) + 64 * 65536
     assert lib.gla_chunk_bwd_workspace_bytes(64, 100, 128, 128, 64) == 0
     args = lambda T, ws_bytes, **kw: [kw.get(n, p) for n in ("q", "k", "v", "g", "S0", "dO", "dST", "dq", "dk",
                                                           "dv", "dg", "dS0")] + [2, T, 128, 128, 64, 1, p,
@@ -162,3 +163,19 @@ def test_gla_bwd_validation(lib):
     assert f(*args(128, 1 << 34, q=ctypes.c_void_p(4098))) == EALIGN
     assert f(*args(128, 1 << 34, dS0=None)) == EINVAL
     assert "gla_chunk_bwd" in _err(lib)
+
+
+def test_gdn_bwd_validation(lib):
+    p = ctypes.c_void_p(4096)
+    f = lib.gdn_chunk_bwd
+    per_chunk = 81984 + 8192 + 2 * 32768 + 16384 + 32768 + 256 + 128
+    assert lib.gdn_chunk_bwd_workspace_bytes(32, 16384, 128, 128, 64) == 32 * 256 * per_chunk + 32 * 65536
+    assert lib.gdn_chunk_bwd_workspace_bytes(32, 100, 128, 128, 64) == 0
+    names = ("q", "k", "v", "a", "b", "S0", "dO", "dST", "dq", "dk", "dv", "da", "db", "dS0")
+    args = lambda T, ws_bytes, **kw: [kw.get(n, p) for n in names] + [2, T, 128, 128, 64, 1, p, ws_bytes, None]
+    assert f(*args(128, 10)) == EINVAL                                   # workspace too small
+    assert f(*args(96, 1 << 34)) == ESHAPE                               # T % 64
+    assert f(*args(128, 1 << 34, k=ctypes.c_void_p(4104))) == EALIGN
+    assert f(*args(128, 1 << 34, dS0=None)) == EINVAL
+    assert f(*args(128, 1 << 34)) == EINVAL                              # outputs overlap inputs
+    assert "gdn_chunk_bwd" in _err(lib)

@@ -253,3 +253,25 @@ def test_chunk_backward_equals_reverse_mode(C):
     ref = gdn.gdn_recurrent_bwd(q, k, v, a, b, None, dO, None)
     for g_, r_, name in zip(got, ref, NAMES):
         np.testing.assert_allclose(g_, r_, rtol=0, atol=1e-11 * np.abs(r_).max(), err_msg=name)
+
+
+def test_decay_gradient_sums_and_state_boundary_identity():
+    """d log alpha_t (reverse mode, alpha_t dalpha_t) equals the reverse sum over s >= t
+    of q_s . dq_s - v_s . dv_s (+ sum(dST o S_T)), and its part beyond any token
+    boundary equals sum(dS o S) of the state there and its gradient: scaling alpha_t
+    is scaling the state that token t starts from."""
+    rng = np.random.default_rng(54)
+    N, T, d = 2, 40, 6
+    q, k, v, a, b, S0, dO, dST = _bwd_case(rng, N, T, d)
+    dq, dk, dv, da, db, dS0 = gdn.gdn_recurrent_bwd(q, k, v, a, b, S0, dO, dST)
+    _, ST = gdn.gdn_recurrent(q, k, v, a, b, S0)
+    dB = np.einsum("ntk,ntk->nt", q, dq) - np.einsum("ntv,ntv->nt", v, dv)
+    dB[:, -1] += np.einsum("nvk,nvk->n", dST, ST)
+    dlog = a * da
+    np.testing.assert_allclose(dlog, np.cumsum(dB[:, ::-1], axis=1)[:, ::-1], rtol=0, atol=1e-10 * np.abs(dlog).max())
+    for t0 in (1, 17, 39):   # boundary before token t0: state S_{t0-1} and its gradient
+        _, S_mid = gdn.gdn_recurrent(q[:, :t0], k[:, :t0], v[:, :t0], a[:, :t0], b[:, :t0], S0)
+        *_, dS_mid = gdn.gdn_recurrent_bwd(q[:, t0:], k[:, t0:], v[:, t0:], a[:, t0:], b[:, t0:], S_mid,
+                                           dO[:, t0:], dST)
+        np.testing.assert_allclose(dlog[:, t0], np.einsum("nvk,nvk->n", dS_mid, S_mid), rtol=0,
+                                   atol=1e-10 * np.abs(dlog).max())

@@ -200,3 +200,20 @@ def test_backward_zeco_chunk_state_gradient():
     db[:, -1] += np.einsum("nvk,nvk->nk", dST, ST)
     np.testing.assert_allclose(dg, np.cumsum(db[:, ::-1], axis=1)[:, ::-1], rtol=0,
                                atol=1e-9 * np.abs(dg).max())
+
+
+def test_backward_gate_gradient_beyond_a_boundary():
+    """The part of d log_g_t from tokens after a boundary equals sum_v dS o S (per key
+    channel) of the state there and its gradient: shifting the cumulative log-gate of
+    one channel on every later token scales that key column of the state."""
+    rng = np.random.default_rng(45)
+    N, T, d = 2, 48, 6
+    q, k, v, lg = _rand(rng, N, T, d)
+    S0, dST = rng.standard_normal((2, N, d, d))
+    dO = rng.standard_normal((N, T, d))
+    dq, dk, dv, dg, dS0 = gla.gla_recurrent_bwd(q, k, v, lg, S0, dO, dST)
+    for t0 in (1, 16, 47):
+        _, S_mid = gla.gla_recurrent(q[:, :t0], k[:, :t0], v[:, :t0], lg[:, :t0], S0)
+        *_, dS_mid = gla.gla_recurrent_bwd(q[:, t0:], k[:, t0:], v[:, t0:], lg[:, t0:], S_mid, dO[:, t0:], dST)
+        np.testing.assert_allclose(dg[:, t0], np.einsum("nvk,nvk->nk", dS_mid, S_mid), rtol=0,
+                                   atol=1e-10 * np.abs(dg).max())
