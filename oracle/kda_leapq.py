@@ -56,7 +56,7 @@ def readout(st, buf, y):
     n, dk = y.shape
     x = _suffix(buf, -1, dk, n) * y                                   # Gamma_{1:m} y
     Z = st["Z"].astype(np.float64)
-    out = st["s"] * np.einsum("nvk,nk->nv", Z, st["c"] * x) / 127.0
+    out = st["s"] * np.einsum("nvk,nk->nv", Z, st["c"] * x) / float(st.get("Q", 127))
     out = out + np.einsum("nrv,nr->nv", st["ut"], np.einsum("nrk,nk->nr", st["kt"], x))
     for j, (kj, uj, _) in enumerate(buf):
         out = out + uj * np.sum(kj * (_suffix(buf, j, dk, n) * y), axis=-1)[:, None]

@@ -9,7 +9,9 @@ at the point of storage:
 * codes: symmetric INT8 in [-127, 127], one fp32 scale per value channel, the
   step being the channel's largest magnitude over 127 (section "Fix two", the
   quantiser paragraph, and the dequantised payload (Z/127) B of section "Fix
-  three");
+  three"); ``bits`` = 6 or 4 narrows the grid to [-Q, Q], Q = 2^(bits-1) - 1, in
+  the same int8 container (the widths of section "Fix two"'s compensator-count
+  paragraph, where the paper pairs them with 6 compensator tokens);
 * row smoothing: one fp32 factor per key channel, the square root of that
   channel's mean magnitude over the value channels (section "Fix three", eq. 7),
   clamped below at 1e-12; mode 1 uses the root of the mean square instead and
@@ -66,10 +68,18 @@ def fp32(x):
     return np.asarray(x, np.float64).astype(np.float32).astype(np.float64)
 
 
-def round_codes(x32):
-    """INT8 decision on fp32 pre-rounding values: clamp(rint(x), -127, 127)."""
+def qmax(bits):
+    """Largest code of the symmetric b-bit grid, 2^(b-1) - 1 (127 at 8 bits)."""
+    if not 2 <= bits <= 8:
+        raise ValueError("bits must be in 2..8")
+    return (1 << (bits - 1)) - 1
+
+
+def round_codes(x32, bits=8):
+    """Code decision on fp32 pre-rounding values: clamp(rint(x), -Q, Q)."""
     x32 = np.asarray(x32, np.float32)
-    return np.clip(np.rint(x32), -127, 127).astype(np.int8)
+    Q = qmax(bits)
+    return np.clip(np.rint(x32), -Q, Q).astype(np.int8)
 
 
 def cholqr2(Z):
@@ -119,8 +129,9 @@ def fit_compensators(S, Q0, rank=4, iters=1, svd=False):
     return Q
 
 
-def flush(S, Q0=None, rank=4, iters=1, smooth_mode=0, svd=False):
-    """Encode dense states S ([N][d_v][d_k]) into the stored form.
+def flush(S, Q0=None, rank=4, iters=1, smooth_mode=0, svd=False, bits=8):
+    """Encode dense states S ([N][d_v][d_k]) into the stored form (codes on the
+    symmetric ``bits``-bit grid).
 
     Returns dict(Z int8 [N][dv][dk], s fp32 [N][dv], c fp32 [N][dk],
     kt fp16 [N][r][dk], ut fp16 [N][r][dv], pre fp32 [N][dv][dk]) with the
@@ -137,31 +148,35 @@ def flush(S, Q0=None, rank=4, iters=1, smooth_mode=0, svd=False):
         kt = np.zeros((N, 0, dk))
         ut = np.zeros((N, 0, dv))
         R = S
-    out = encode_residual(R, smooth_mode)
+    out = encode_residual(R, smooth_mode, bits)
     out.update(kt=kt, ut=ut)
     return out
 
 
-def encode_residual(R, smooth_mode=0):
+def encode_residual(R, smooth_mode=0, bits=8):
     """Smooth and round a residual R ([N][d_v][d_k]) once: returns dict(Z, s, c,
     pre) -- codes, value-channel scales, key-channel smoothing factors (fp32) and
-    the fp32 pre-rounding values."""
+    the fp32 pre-rounding values -- and Q. With Q = 2^(bits-1) - 1 (127 at 8 bits)
+    and s_v = max_k |R/c| (fp32): pre = (R/c) (Q/s_v), codes = clamp(rint(pre), -Q, Q);
+    the channel dequantises as s_v Z / Q."""
     R = np.asarray(R, np.float64)
+    Q = qmax(bits)
     c = fp32(smoothing(R, smooth_mode))                        # [N][dk]
     Rc = R / c[:, None, :]
     s = fp32(np.max(np.abs(Rc), axis=-1))                      # [N][dv]
     with np.errstate(divide="ignore", invalid="ignore"):
-        pre = np.where(s[:, :, None] > 0, Rc * (127.0 / s[:, :, None]), 0.0)
+        pre = np.where(s[:, :, None] > 0, Rc * (float(Q) / s[:, :, None]), 0.0)
     pre = pre.astype(np.float32)
-    Z = round_codes(pre)
-    return dict(Z=Z, s=s, c=c, pre=pre)
+    Z = round_codes(pre, bits)
+    return dict(Z=Z, s=s, c=c, pre=pre, Q=Q)
 
 
 def dequant(st):
     """Dense stored state: C-smoothed dequantised residual plus the fp16
-    compensator pieces, S_hat[v,k] = s_v Z[v,k] / 127 c_k + sum_r ut_r[v] kt_r[k]."""
+    compensator pieces, S_hat[v,k] = s_v Z[v,k] / Q c_k + sum_r ut_r[v] kt_r[k]
+    (Q = 127 at 8 bits)."""
     Z = st["Z"].astype(np.float64)
-    S = st["s"][:, :, None] * (Z / 127.0) * st["c"][:, None, :]
+    S = st["s"][:, :, None] * (Z / float(st.get("Q", 127))) * st["c"][:, None, :]
     return S + np.swapaxes(st["ut"], -1, -2) @ st["kt"]
 
 
@@ -180,7 +195,7 @@ def readout(st, buf, x):
     smoothing folded into the vector, as the page describes."""
     x = np.asarray(x, np.float64)
     Z = st["Z"].astype(np.float64)
-    y = st["s"] * np.einsum("nvk,nk->nv", Z, st["c"] * x) / 127.0
+    y = st["s"] * np.einsum("nvk,nk->nv", Z, st["c"] * x) / float(st.get("Q", 127))
     y = y + np.einsum("nrv,nr->nv", st["ut"], np.einsum("nrk,nk->nr", st["kt"], x))
     m = len(buf)
     g = np.ones(x.shape[0])
@@ -205,7 +220,7 @@ def rebuild(st, buf):
 
 
 def decode_run(q, k, v, alpha, beta, S0, Q0, window=16, rank=4, iters=1,
-               smooth_mode=0, buf_dtype=np.float32, collect=False):
+               smooth_mode=0, buf_dtype=np.float32, collect=False, bits=8):
     """The windowed scheme over T tokens for N heads (inputs [T][N][d], gates
     [T][N], S0 [N][d_v][d_k]). The initial state is encoded by one flush before
     the first token; after every ``window`` real tokens the state is rebuilt and
@@ -218,7 +233,7 @@ def decode_run(q, k, v, alpha, beta, S0, Q0, window=16, rank=4, iters=1,
     alpha = np.asarray(alpha, np.float64)
     beta = np.asarray(beta, np.float64)
     T = q.shape[0]
-    st = flush(S0, Q0, rank, iters, smooth_mode)
+    st = flush(S0, Q0, rank, iters, smooth_mode, bits=bits)
     starts = [st] if collect else None
     buf = []
     o = np.empty(v.shape)
@@ -230,7 +245,7 @@ def decode_run(q, k, v, alpha, beta, S0, Q0, window=16, rank=4, iters=1,
         buf.append((k[t], u, a))
         o[t] = readout(st, buf, q[t])
         if len(buf) == window:
-            st = flush(rebuild(st, buf), Q0, rank, iters, smooth_mode)
+            st = flush(rebuild(st, buf), Q0, rank, iters, smooth_mode, bits=bits)
             buf = []
             if collect:
                 starts.append(st)
@@ -260,31 +275,62 @@ def window_run(st, q, k, v, alpha, beta, buf_dtype=np.float32):
 
 # ----------------------------------------------------------------- eq. 2
 
-def per_step_int8(q, k, v, alpha, beta, S0):
+def per_step_int8(q, k, v, alpha, beta, S0, bits=8):
     """Eq. 2 (section "Rounding every token"): the state is requantised after
     every token, S_t = alpha_t S_hat_{t-1} + k_t u_t^T (transposed here) with
-    u_t computed from the stored state, S_hat_t = quant(S_t). Symmetric INT8
-    with one scale per value channel, no smoothing, no compensator tokens.
-    Written independently of the windowed path; returns (o, Z, s)."""
+    u_t computed from the stored state, S_hat_t = quant(S_t). Symmetric b-bit codes
+    (Q = 2^(b-1) - 1) with one scale per value channel, the step being the channel's
+    largest magnitude over Q; no smoothing, no compensator tokens. Written
+    independently of the windowed path; returns (o, Z, m) with m the channels'
+    largest magnitudes (the dequantised state is m Z / Q)."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
+    Q = float(qmax(bits))
 
     def quant(S):
-        s = fp32(np.max(np.abs(S), axis=-1))
+        m = fp32(np.max(np.abs(S), axis=-1))
         with np.errstate(divide="ignore", invalid="ignore"):
-            x = np.where(s[:, :, None] > 0, S * (127.0 / s[:, :, None]), 0.0)
-        Z = round_codes(x.astype(np.float32))
-        return Z, s
+            x = np.where(m[:, :, None] > 0, S * (Q / m[:, :, None]), 0.0)
+        Z = np.clip(np.rint(x.astype(np.float32)), -Q, Q).astype(np.int8)
+        return Z, m
 
-    Z, s = quant(np.asarray(S0, np.float64))
+    Z, m = quant(np.asarray(S0, np.float64))
     o = np.empty(v.shape)
     for t in range(q.shape[0]):
-        Sh = s[:, :, None] * Z.astype(np.float64) / 127.0
+        Sh = m[:, :, None] * Z.astype(np.float64) / Q
         a = np.asarray(alpha[t], np.float64)[:, None]
         b = np.asarray(beta[t], np.float64)[:, None]
         u = b * (v[t] - a * np.einsum("nvk,nk->nv", Sh, k[t]))
         S = a[:, :, None] * Sh + u[:, :, None] * k[t][:, None, :]
         o[t] = np.einsum("nvk,nk->nv", S, q[t])
-        Z, s = quant(S)
-    return o, Z, s
+        Z, m = quant(S)
+    return o, Z, m
+
+
+def bf16(x):
+    """Round to bfloat16, nearest-even, back to fp64 (8 significant bits)."""
+    x32 = np.ascontiguousarray(np.asarray(x, np.float64), dtype=np.float32)
+    u = x32.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def per_step_bf16(q, k, v, alpha, beta, S0):
+    """The state kept in BF16 and re-rounded after every token (section "Rounding
+    every token", the BF16 case): u_t from the stored state, S_t = alpha_t S_{t-1} +
+    u_t k_t^T computed exactly, then rounded to bf16 (nearest even) per entry.
+    Returns (o, S_T)."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    S = bf16(S0)
+    o = np.empty(v.shape)
+    for t in range(q.shape[0]):
+        a = np.asarray(alpha[t], np.float64)[:, None]
+        b = np.asarray(beta[t], np.float64)[:, None]
+        u = b * (v[t] - a * np.einsum("nvk,nk->nv", S, k[t]))
+        Sn = a[:, :, None] * S + u[:, :, None] * k[t][:, None, :]
+        o[t] = np.einsum("nvk,nk->nv", Sn, q[t])
+        S = bf16(Sn)
+    return o, S

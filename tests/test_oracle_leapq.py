@@ -26,16 +26,18 @@ def _tn(x):   # [T][N][d] -> [N][T][d]
     return np.swapaxes(x, 0, 1)
 
 
-def test_window_one_no_extras_equals_per_token_rounding_eq2():
+@pytest.mark.parametrize("bits", [8, 6, 4])
+def test_window_one_no_extras_equals_per_token_rounding_eq2(bits):
     """Eq. 2 rounding after every token, written separately, must equal the
-    windowed scheme with W = 1, no compensator tokens and no smoothing."""
+    windowed scheme with W = 1, no compensator tokens and no smoothing, at every
+    code width."""
     rng = np.random.default_rng(1)
     T, N, d = 24, 3, 16
     q, k, v, a, b = _inputs(rng, T, N, d)
     S0 = 0.05 * rng.standard_normal((N, d, d))
-    o1, Z1, s1 = leapq.per_step_int8(q, k, v, a, b, S0)
+    o1, Z1, s1 = leapq.per_step_int8(q, k, v, a, b, S0, bits=bits)
     r = leapq.decode_run(q, k, v, a, b, S0, None, window=1, rank=0, smooth_mode=2,
-                         buf_dtype=np.float64)
+                         buf_dtype=np.float64, bits=bits)
     np.testing.assert_array_equal(r["st"]["Z"], Z1)
     np.testing.assert_array_equal(r["st"]["s"], s1)
     np.testing.assert_allclose(r["o"], o1, rtol=0, atol=1e-12)
@@ -231,3 +233,78 @@ def test_error_ordering_trend_on_a_toy_head():
                          smooth_mode=0)
     e["full"] = np.linalg.norm(final_dense(r) - S_ex) / np.linalg.norm(S_ex)
     assert e["step"] > e["window"] > e["full"], e
+
+
+# ------------------------------------------------------------------ narrower codes, BF16
+
+@pytest.mark.parametrize("bits", [6, 4])
+def test_narrow_grid_codes_and_half_step_bound(bits):
+    """At b bits the codes stay in [-Q, Q], Q = 2^(b-1) - 1, every nonzero value
+    channel reaches +-Q, and each entry is within half a step s_v / Q c_k."""
+    rng = np.random.default_rng(15)
+    N, d = 3, 32
+    S = rng.standard_normal((N, d, d))
+    S[:, :, 3] *= 50
+    st = leapq.flush(S, rng.standard_normal((d, 6)), rank=6, smooth_mode=0, bits=bits)
+    Q = (1 << (bits - 1)) - 1
+    assert st["Q"] == Q and np.abs(st["Z"]).max() == Q
+    assert np.all(np.abs(st["Z"]).max(axis=-1) == Q)
+    err = np.abs(leapq.dequant(st) - S)
+    step = st["s"][:, :, None] / Q * st["c"][:, None, :]
+    assert np.all(err <= 0.5 * step * (1 + 1e-5) + 1e-12)
+
+
+def test_bf16_rounding_is_torch_bfloat16():
+    rng = np.random.default_rng(16)
+    x = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.uniform(-6, 6, 20000),
+                        [0.0, -0.0, 1.0, 1.00390625, 1.01171875, -3.5]])
+    ref = torch.tensor(x, dtype=torch.float32).to(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(leapq.bf16(x), ref)
+
+
+def test_per_step_bf16_state_freezes_slow_decays():
+    """The page's count: a BF16 state re-rounded after every token does not move
+    under a decay of 0.999 (all values), 0.998 (most) or 0.997 (about a third),
+    for log-uniform values in [0.01, 10] -- through the per-step BF16 baseline with
+    no writes (beta = 0)."""
+    with open(os.path.join(GOLD, "decay_freeze.json")) as f:
+        g = json.load(f)
+    lo, hi = np.log10(g["range"][0]), np.log10(g["range"][1])
+    N, d = 4, 64
+    S0 = leapq.bf16(10.0 ** np.linspace(lo, hi, N * d * d)).reshape(N, d, d)
+    z = np.zeros((1, N, d))
+    for a, want in g["bf16"].items():
+        _, S1 = leapq.per_step_bf16(z, z, z, np.full((1, N), float(a)), np.zeros((1, N)), S0)
+        assert abs(np.mean(S1 == S0) - want) <= 2 * g["tol"] + 2e-3, a
+    _, S100 = leapq.per_step_bf16(np.zeros((100, N, d)), np.zeros((100, N, d)), np.zeros((100, N, d)),
+                                  np.full((100, N), 0.999), np.zeros((100, N)), S0)
+    np.testing.assert_array_equal(S100, S0)
+
+
+@pytest.mark.parametrize("bits", [6, 4])
+def test_error_ordering_trend_at_narrow_widths(bits):
+    """Trend only (parity unpinned): at 6 and 4 bits, with 6 compensator tokens
+    (the paper's pairing), the relative state error still orders as per-token
+    rounding > window > window with compensator tokens and smoothing."""
+    rng = np.random.default_rng(9)
+    T, N, d = 512, 1, 32
+    k = rng.standard_normal((T, N, d))
+    k[..., :2] += 2.0
+    k[..., 2:6] *= 3.0
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    q = k[::-1].copy()
+    v = rng.standard_normal((T, N, d))
+    v[..., :2] += 4.0
+    a = np.full((T, N), 0.995)
+    b = rng.uniform(0.05, 0.15, (T, N))
+    S0 = np.zeros((N, d, d))
+    _, S_ex = gdn.gdn_recurrent(_tn(q), _tn(k), _tn(v), a.T, b.T, S0)
+    rel = lambda X: np.linalg.norm(X - S_ex) / np.linalg.norm(S_ex)
+    _, Zp, mp = leapq.per_step_int8(q, k, v, a, b, S0, bits=bits)
+    e_step = rel(mp[:, :, None] * Zp / leapq.qmax(bits))
+    r = leapq.decode_run(q, k, v, a, b, S0, None, window=16, rank=0, smooth_mode=2, bits=bits)
+    e_win = rel(leapq.rebuild(r["st"], r["buf"]))
+    r = leapq.decode_run(q, k, v, a, b, S0, rng.standard_normal((d, 6)), window=16, rank=6,
+                         smooth_mode=0, bits=bits)
+    e_full = rel(leapq.rebuild(r["st"], r["buf"]))
+    assert e_step > e_win > e_full, (e_step, e_win, e_full)
