@@ -14,6 +14,8 @@ from .binding import (  # noqa: F401
     gdn_chunk_fwd,
     gdn_chunk_workspace,
     gdn_decode_step,
+    gdn_decode_step_bf16_state,
+    gdn_decode_step_int_state,
     gla_chunk_bwd,
     gla_chunk_bwd_workspace,
     gla_chunk_fwd,

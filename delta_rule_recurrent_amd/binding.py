@@ -28,7 +28,7 @@ class LeapqState(ctypes.Structure):
     _fields_ = [("codes", _vp), ("vscale", _vp), ("ksmooth", _vp), ("ct_k", _vp),
                 ("ct_u", _vp), ("buf_k", _vp), ("buf_u", _vp), ("buf_a", _vp),
                 ("N", _c_int), ("dk", _c_int), ("dv", _c_int), ("rank", _c_int),
-                ("window", _c_int)]
+                ("window", _c_int), ("bits", _c_int)]
 
 
 # exported symbol -> (argtypes, restype); mirrors include/gdnrt.h
@@ -42,6 +42,8 @@ SIGNATURES = {
     "kda_chunk_fwd": ([_vp] * 8 + [_c_int] * 6 + [_vp, ctypes.c_size_t, _vp], _c_int),
     "gla_chunk_bwd": ([_vp] * 12 + [_c_int] * 6 + [_vp, ctypes.c_size_t, _vp], _c_int),
     "gla_chunk_bwd_workspace_bytes": ([_c_int] * 5, ctypes.c_size_t),
+    "gdn_decode_step_bf16_state": ([_vp] * 7 + [_c_int] * 5 + [_vp], _c_int),
+    "gdn_decode_step_int_state": ([_vp, _vp, _c_int] + [_vp] * 6 + [_c_int] * 5 + [_vp], _c_int),
     "gdn_chunk_bwd": ([_vp] * 14 + [_c_int] * 6 + [_vp, ctypes.c_size_t, _vp], _c_int),
     "gdn_chunk_bwd_workspace_bytes": ([_c_int] * 5, ctypes.c_size_t),
     "kda_chunk_fwd_workspace_bytes": ([_c_int] * 5, ctypes.c_size_t),
@@ -136,6 +138,38 @@ def gdn_decode_step(S, q, k, v, alpha, beta, o=None):
     _check("gdn_decode_step", lib().gdn_decode_step(
         _ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(o),
         N, T, D, D, io, _stream()))
+    return o
+
+
+def gdn_decode_step_bf16_state(S, q, k, v, alpha, beta, o=None):
+    """Per-step BF16 baseline: gdn_decode_step with S [N][128][128] stored in bf16 and
+    re-rounded after every token (in place). Returns o."""
+    return _lowp_decode("gdn_decode_step_bf16_state", S, None, 0, q, k, v, alpha, beta, o)
+
+
+def gdn_decode_step_int_state(codes, rowmax, bits, q, k, v, alpha, beta, o=None):
+    """Per-step b-bit baseline: the state is rowmax[v] * codes[v,k] / Q (Q = 2^(bits-1)
+    - 1), requantised after every token (codes int8 [N][128][128], rowmax fp32
+    [N][128], in place). Returns o."""
+    return _lowp_decode("gdn_decode_step_int_state", codes, rowmax, bits, q, k, v, alpha, beta, o)
+
+
+def _lowp_decode(name, S, rowmax, bits, q, k, v, alpha, beta, o):
+    N, T = q.shape[0], q.shape[1]
+    _need(S, "S", torch.bfloat16 if rowmax is None else torch.int8, (N, D, D))
+    if rowmax is not None:
+        _need(rowmax, "rowmax", torch.float32, (N, D))
+    for n_, t_ in (("q", q), ("k", k), ("v", v)):
+        _need(t_, n_, q.dtype, (N, T, D))
+    for n_, t_ in (("alpha", alpha), ("beta", beta)):
+        _need(t_, n_, torch.float32, (N, T))
+    if o is None:
+        o = torch.empty_like(v)
+    _need(o, "o", q.dtype, (N, T, D))
+    io = _io(q.dtype)
+    args = (_ptr(S),) if rowmax is None else (_ptr(S), _ptr(rowmax), bits)
+    _check(name, getattr(lib(), name)(*args, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(o),
+                                      N, T, D, D, io, _stream()))
     return o
 
 
@@ -320,8 +354,8 @@ class LeapqBuffers:
     """Caller-owned device memory of a LeapQuant state for N heads (see
     ``leapq_state`` in include/gdnrt.h). Allocated once by torch."""
 
-    def __init__(self, N, rank=4, window=16, device="cuda", kda=False):
-        self.N, self.rank, self.window, self.kda = N, rank, window, kda
+    def __init__(self, N, rank=4, window=16, device="cuda", kda=False, bits=8):
+        self.N, self.rank, self.window, self.kda, self.bits = N, rank, window, kda, bits
         f = dict(dtype=torch.float32, device=device)
         self.codes = torch.zeros((N, D, D), dtype=torch.int8, device=device)
         self.vscale = torch.zeros((N, D), **f)
@@ -337,7 +371,7 @@ class LeapqBuffers:
         self._st = LeapqState(
             _ptr(self.codes), _ptr(self.vscale), _ptr(self.ksmooth), _ptr(self.ct_k),
             _ptr(self.ct_u), _ptr(self.buf_k), _ptr(self.buf_u), _ptr(self.buf_a),
-            N, D, D, rank, window)
+            N, D, D, rank, window, bits)
 
     @property
     def struct(self):

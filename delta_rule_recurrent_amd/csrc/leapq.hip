@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256) void leapq_decode_kernel(
     const int8_t* __restrict__ codes, const float* __restrict__ vscale,
     const float* __restrict__ ksmooth, const uint16_t* __restrict__ ct_k,
     const uint16_t* __restrict__ ct_u, float* __restrict__ buf_k, float* __restrict__ buf_u,
-    float* __restrict__ buf_a, int rank, int window, int m,
+    float* __restrict__ buf_a, int rank, int window, int m, float qinv,
     const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, IO* __restrict__ o) {
   constexpr int NV = kMaxRank + kMaxWindow;   // dot-product vectors: compensators, records, k
@@ -358,7 +358,7 @@ __global__ __launch_bounds__(256) void leapq_decode_kernel(
     ck += __shfl_xor(ck, 16); cq += __shfl_xor(cq, 16); tk += __shfl_xor(tk, 16); tq += __shfl_xor(tq, 16);
     ck += __shfl_xor(ck, 32); cq += __shfl_xor(cq, 32); tk += __shfl_xor(tk, 32); tq += __shfl_xor(tq, 32);
     if (g == 0) {
-      const float sv = vsr[T] * (1.0f / 127.0f);
+      const float sv = vsr[T] * qinv;   // 1 / Q, Q = 127 at 8 bits
       const float Sk = g0 * (sv * yk[T] + ck) + tk;
       const float Sq = g0 * (sv * yq[T] + cq) + tq;
       const float u = KDA ? b * (vrow[T] - Sk) : b * (vrow[T] - a * Sk);
@@ -540,7 +540,7 @@ __global__ __launch_bounds__(kFlushNT) __attribute__((amdgpu_waves_per_eu(RANK <
     uint16_t* __restrict__ ct_k, uint16_t* __restrict__ ct_u, const float* __restrict__ buf_k,
     const float* __restrict__ buf_u, const float* __restrict__ buf_a, int window, int m,
     const float* __restrict__ dense, const float* __restrict__ q0, int iters, int smooth_mode,
-    float* __restrict__ pre_round) {
+    float qf, float qinv, float* __restrict__ pre_round) {
   constexpr int RQ = RANK <= 4 ? 4 : 8;   // padded rank of the LDS blocks
   __shared__ FlushSmem<RQ> sm;
   __shared__ FlushDecays<KDA> dk_[1];
@@ -638,7 +638,7 @@ __global__ __launch_bounds__(kFlushNT) __attribute__((amdgpu_waves_per_eu(RANK <
     const float g0 = sm.dec[m];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const float sv = g0 * vs[t] * (1.0f / 127.0f);
+      const float sv = g0 * vs[t] * qinv;
       const uint32_t zw[8] = {z[t][0].x, z[t][0].y, z[t][0].z, z[t][0].w,
                               z[t][1].x, z[t][1].y, z[t][1].z, z[t][1].w};
 #pragma unroll
@@ -815,7 +815,7 @@ __global__ __launch_bounds__(kFlushNT) __attribute__((amdgpu_waves_per_eu(RANK <
     mx = fmaxf(mx, xor_lane(mx, 16));
     mx = fmaxf(mx, xor_lane(mx, 32));
     if (g == 0) vscale[hk + vrow[t]] = mx;
-    const float sc = mx > 0.f ? 127.0f / mx : 0.f;
+    const float sc = mx > 0.f ? qf / mx : 0.f;   // Q / max, Q = 2^(bits-1) - 1
     uint32_t wd[8];
 #pragma unroll
     for (int tc = 0; tc < 8; ++tc) {
@@ -824,7 +824,7 @@ __global__ __launch_bounds__(kFlushNT) __attribute__((amdgpu_waves_per_eu(RANK <
       uint32_t word = 0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float qz = fminf(fmaxf(rintf(x[e]), -127.f), 127.f);
+        const float qz = fminf(fmaxf(rintf(x[e]), -qf), qf);
         word |= (uint32_t)((int32_t)qz & 0xff) << (8 * e);
       }
       wd[tc] = word;
@@ -835,6 +835,9 @@ __global__ __launch_bounds__(kFlushNT) __attribute__((amdgpu_waves_per_eu(RANK <
   }
 }
 
+// largest code of the state's grid: 2^(bits-1) - 1, bits = 0 meaning 8
+static int code_max(const leapq_state* st) { return (1 << ((st->bits ? st->bits : 8) - 1)) - 1; }
+
 static int check_state(const leapq_state* st, const char* fn) {
   if (!st) return set_error(GDNRT_EINVAL, "%s: null state", fn);
   if (st->dk != kD || st->dv != kD)
@@ -844,6 +847,8 @@ static int check_state(const leapq_state* st, const char* fn) {
     return set_error(GDNRT_ESHAPE, "%s: rank=%d must be in [0, %d]", fn, st->rank, kMaxRank);
   if (st->window < 1 || st->window > kMaxWindow)
     return set_error(GDNRT_ESHAPE, "%s: window=%d must be in [1, %d]", fn, st->window, kMaxWindow);
+  if (st->bits != 0 && (st->bits < 2 || st->bits > 8))
+    return set_error(GDNRT_ESHAPE, "%s: bits=%d must be 0 (8) or in [2, 8]", fn, st->bits);
   if ((size_t)st->N * 4 > 0x7fffffffu) return set_error(GDNRT_ESHAPE, "%s: N too large", fn);
   if (st->N == 0) return GDNRT_OK;
   if (!st->codes || !st->vscale || !st->ksmooth || !st->buf_k || !st->buf_u || !st->buf_a ||
@@ -884,15 +889,16 @@ int decode_step(const char* fn, const leapq_state* st, int pos, const void* q, c
     return set_error(GDNRT_EINVAL, "%s: o overlaps another buffer", fn);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid((unsigned)N), block(256);
+  const float qinv = 1.0f / (float)code_max(st);
   if (io == GDNRT_F32)
     hipLaunchKernelGGL((leapq_decode_kernel<float, KDA>), grid, block, 0, s, st->codes, st->vscale,
                        st->ksmooth, st->ct_k, st->ct_u, st->buf_k, st->buf_u, st->buf_a, st->rank,
-                       st->window, pos, static_cast<const float*>(q), static_cast<const float*>(k),
+                       st->window, pos, qinv, static_cast<const float*>(q), static_cast<const float*>(k),
                        static_cast<const float*>(v), alpha, beta, static_cast<float*>(o));
   else
     hipLaunchKernelGGL((leapq_decode_kernel<uint16_t, KDA>), grid, block, 0, s, st->codes, st->vscale,
                        st->ksmooth, st->ct_k, st->ct_u, st->buf_k, st->buf_u, st->buf_a, st->rank,
-                       st->window, pos, static_cast<const uint16_t*>(q),
+                       st->window, pos, qinv, static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), alpha,
                        beta, static_cast<uint16_t*>(o));
   return check_launch(fn);
@@ -917,13 +923,14 @@ int window_flush(const char* fn, const leapq_state* st, int pos, const float* de
       (pre_round && overlaps(pre_round, nS, st->codes, N * kD * kD)))
     return set_error(GDNRT_EINVAL, "%s: dense / pre_round overlap the state", fn);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const float qf = (float)code_max(st), qinv = 1.0f / qf;
   switch (st->rank) {
 #define GDNRT_FLUSH(R)                                                                            \
   case R:                                                                                         \
     hipLaunchKernelGGL((leapq_flush_kernel<R, KDA>), dim3((unsigned)N), dim3(kFlushNT),          \
                        0, s, st->codes, st->vscale, st->ksmooth, st->ct_k, st->ct_u, st->buf_k,   \
-                       st->buf_u, st->buf_a, st->window, pos, dense, q0, iters, smooth_mode,      \
-                       pre_round);                                                                \
+                       st->buf_u, st->buf_a, st->window, pos, dense, q0, iters, smooth_mode, qf,  \
+                       qinv, pre_round);                                                          \
     break;
     GDNRT_FLUSH(0) GDNRT_FLUSH(1) GDNRT_FLUSH(2) GDNRT_FLUSH(3) GDNRT_FLUSH(4)
     GDNRT_FLUSH(5) GDNRT_FLUSH(6) GDNRT_FLUSH(7) GDNRT_FLUSH(8)

@@ -233,13 +233,41 @@ GDNRT_API int kda_chunk_fwd(const void* q, const void* k, const void* v,
 GDNRT_API size_t kda_chunk_fwd_workspace_bytes(int N, int T, int dk, int dv, int chunk);
 
 /*
+ * Per-step low-precision state baselines ("LeapQuant: an 8-bit recurrent state that
+ * stops rounding every token", section "Rounding every token", eq. 2): gdn_decode_step
+ * with the state stored in a narrow format and re-rounded after every token. Each token
+ * computes u, o and the next state in fp32 from the stored state, then rounds it:
+ *
+ *   gdn_decode_step_bf16_state: S [N][dv][dk] bf16 (16-byte aligned), rounded to
+ *     nearest even per entry.
+ *   gdn_decode_step_int_state: codes [N][dv][dk] int8 in [-Q, Q], Q = 2^(bits-1) - 1
+ *     (bits in 2..8), and rowmax [N][dv] fp32, the value row's largest magnitude; the
+ *     state is rowmax[v] * codes[v,k] / Q; after each token rowmax <- max_k |S[v,k]| and
+ *     codes <- clamp(rint(S * (Q / rowmax)), -Q, Q) (fp32, nearest even). No smoothing
+ *     and no compensator tokens.
+ *
+ * q, k [N][T][dk] (16-byte aligned), v, o [N][T][dv] in the io dtype; alpha, beta [N][T]
+ * fp32. Outputs o_t = S_t q_t from the unrounded S_t. Errors as gdn_decode_step.
+ */
+GDNRT_API int gdn_decode_step_bf16_state(uint16_t* S, const void* q, const void* k, const void* v,
+                                         const float* alpha, const float* beta, void* o,
+                                         int N, int T, int dk, int dv, int io, void* stream);
+GDNRT_API int gdn_decode_step_int_state(int8_t* codes, float* rowmax, int bits,
+                                        const void* q, const void* k, const void* v,
+                                        const float* alpha, const float* beta, void* o,
+                                        int N, int T, int dk, int dv, int io, void* stream);
+
+/*
  * LeapQuant windowed 8-bit state ("LeapQuant: an 8-bit recurrent state that stops
  * rounding every token": section "Fix one: leap over a window" eq. 4 and eq. 10,
  * section "Fix two: pull the outliers out as tokens" eq. 5, section "Fix three:
  * smooth what is left" eq. 7, layout from section "What 1.19 bytes buys").
  * A host struct of caller-owned device pointers, per head n of N:
  *
- *   codes   [N][dv][dk] int8   residual codes Z in [-127, 127]
+ *   codes   [N][dv][dk] int8   residual codes Z in [-Q, Q]: Q = 127 at 8 bits; `bits`
+ *                              = 6 or 4 narrows the grid (Q = 31, 7) in the same
+ *                              int8 container (the narrower widths of section "Fix
+ *                              two", which pairs them with 6 compensator tokens)
  *   vscale  [N][dv]     fp32   one scale per value channel (row): its largest
  *                              smoothed residual magnitude
  *   ksmooth [N][dk]     fp32   one smoothing factor per key channel (column)
@@ -251,7 +279,7 @@ GDNRT_API size_t kda_chunk_fwd_workspace_bytes(int N, int T, int dk, int dv, int
  * Alignment: codes, ksmooth, ct_k, ct_u, buf_k, buf_u 16 bytes; vscale, buf_a 4
  * bytes (GDNRT_EALIGN otherwise).
  *
- * The stored state is S_hat[v,k] = vscale[v] * codes[v,k] / 127 * ksmooth[k]
+ * The stored state is S_hat[v,k] = vscale[v] * codes[v,k] / Q * ksmooth[k]
  *                                   + sum_r ct_u[r][v] ct_k[r][k].
  * The compensator tokens enter the window ahead of the real tokens with decay 1,
  * so they decay together with the residual.
@@ -266,6 +294,7 @@ typedef struct {
   float* buf_u;
   float* buf_a;
   int N, dk, dv, rank, window;
+  int bits;   /* code width: codes on [-Q, Q], Q = 2^(bits-1) - 1; 2..8, or 0 for 8 */
 } leapq_state;
 
 /*
@@ -297,8 +326,8 @@ GDNRT_API int leapq_decode_step(const leapq_state* st, int pos,
  *   3. smoothing per key channel k: smooth_mode 0: sqrt(mean_v |R[v,k]|),
  *      1: sqrt(mean_v R[v,k]^2), 2: none (1); clamped below at 1e-12;
  *   4. vscale[v] = max_k |R[v,k] / ksmooth[k]|;
- *   5. x = (R[v,k] / ksmooth[k]) * (127 / vscale[v]) in fp32 (0 when vscale is 0),
- *      codes = clamp(rint(x), -127, 127), round half to even.
+ *   5. x = (R[v,k] / ksmooth[k]) * (Q / vscale[v]) in fp32 (0 when vscale is 0),
+ *      codes = clamp(rint(x), -Q, Q), round half to even (Q = 127 at 8 bits).
  * The stored state is overwritten; the buffer is then empty (next pos = 0).
  * pre_round, when not NULL ([N][dv][dk] fp32), receives x.
  * pos outside [0, window] returns GDNRT_ESTATE.

@@ -36,7 +36,8 @@ def test_header_declares_the_entry_points():
               "gla_chunk_fwd_workspace_bytes", "kda_decode_step", "kda_leapq_decode_step",
               "kda_leapq_window_flush", "kda_chunk_fwd", "kda_chunk_fwd_workspace_bytes",
               "gla_chunk_bwd", "gla_chunk_bwd_workspace_bytes", "gdn_chunk_bwd",
-              "gdn_chunk_bwd_workspace_bytes"):
+              "gdn_chunk_bwd_workspace_bytes", "gdn_decode_step_bf16_state",
+              "gdn_decode_step_int_state"):
         assert n in names, n
 
 
@@ -118,6 +119,21 @@ def test_leapq_validation(lib):
     assert fl(ctypes.byref(st), 17, None, p, 1, 0, None, None) == ESTATE
     assert fl(ctypes.byref(st), 0, None, p, 1, 3, None, None) == EINVAL      # smooth_mode
     assert fl(ctypes.byref(st), 0, None, None, 1, 0, None, None) == EINVAL   # q0 missing
+    for bad in (1, 9, -1):                                                    # code width
+        assert fl(ctypes.byref(_state(lib, bits=bad)), 0, None, p, 1, 0, None, None) == ESHAPE
+        assert f(ctypes.byref(_state(lib, bits=bad)), 0, p, p, p, p, p, p, 1, None) == ESHAPE
+
+
+def test_per_step_state_validation(lib):
+    p = ctypes.c_void_p(4096)
+    fb, fi = lib.gdn_decode_step_bf16_state, lib.gdn_decode_step_int_state
+    assert fb(p, p, p, p, p, p, p, 2, 4, 96, 128, 1, None) == ESHAPE          # d_k
+    assert fb(p, p, p, p, p, p, p, 2, 4, 128, 128, 7, None) == EDTYPE
+    assert fb(ctypes.c_void_p(4104), p, p, p, p, p, p, 2, 4, 128, 128, 1, None) == EALIGN
+    assert fb(p, p, p, p, p, p, p, 2, 4, 128, 128, 1, None) == EINVAL         # all overlap
+    assert fi(p, p, 9, p, p, p, p, p, p, 2, 4, 128, 128, 1, None) == ESHAPE   # bits
+    assert fi(p, None, 8, p, p, p, p, p, p, 2, 4, 128, 128, 1, None) == EINVAL
+    assert fi(p, p, 4, p, p, p, p, p, p, 0, 4, 128, 128, 1, None) == OK        # empty
 
 
 def test_kda_leapq_validation(lib):

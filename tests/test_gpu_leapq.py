@@ -39,7 +39,7 @@ def buffer(st, pos, heads=None):
     return [(bk[:, j], bu[:, j], ba[:, j]) for j in range(pos)]
 
 
-def compare_flush(st, ref, what, S, mode=0):
+def compare_flush(st, ref, what, S, mode=0, Q=127):
     """Compare a GPU flush of the dense state S with the oracle's; returns the code
     flips.
 
@@ -82,17 +82,17 @@ def compare_flush(st, ref, what, S, mode=0):
         gram = kt @ np.swapaxes(kt, -1, -2)
         assert np.abs(gram - np.eye(st.rank)).max() < 5e-3, f"{what}: compensator keys not orthonormal"
     # codes: each side is within half a step of its own residual, the residuals
-    # differ by at most dR, and the steps s_v c_k / 127 by their own difference,
-    # so |Z_gpu - Z_ref| <= 1 + dR / step + 127 |1 - step_ref / step_gpu|. Where the
+    # differ by at most dR, and the steps s_v c_k / Q by their own difference,
+    # so |Z_gpu - Z_ref| <= 1 + dR / step + Q |1 - step_ref / step_gpu|. Where the
     # pieces agree this is one step; on outlier channels (c_k ~ 1e-3 after the
     # pieces take the outliers out) a one-step fp16 difference in a piece is
     # several code steps.
     Z = st.codes.cpu().numpy().astype(np.int32)
     flips = Z != ref["Z"].astype(np.int32)
-    step_g = np64(st.vscale)[:, :, None] * c_g[:, None, :] / 127.0
-    step_r = ref["s"][:, :, None] * c_r[:, None, :] / 127.0
+    step_g = np64(st.vscale)[:, :, None] * c_g[:, None, :] / Q
+    step_r = ref["s"][:, :, None] * c_r[:, None, :] / Q
     with np.errstate(divide="ignore", invalid="ignore"):
-        allow = 1 + 1.25 * (dR / step_g + 127 * np.abs(1 - step_r / step_g))
+        allow = 1 + 1.25 * (dR / step_g + Q * np.abs(1 - step_r / step_g))
     allow = np.where(step_g > 0, allow, 1)
     assert np.all(np.abs(Z - ref["Z"]) <= allow), f"{what}: a code moved beyond its propagated bound"
     assert flips.mean() < 1e-2, f"{what}: {flips.mean():.1e} of the codes differ"

@@ -1,0 +1,136 @@
+"""GPU parity of the LeapQuant variants against the fp64 oracle: the windowed state
+at 6 and 4 bits with 6 compensator tokens, and the per-step BF16 and b-bit baselines
+(the state re-rounded after every token).
+
+Tolerances: windowed read-outs as the 8-bit path (teacher forced from the GPU's own
+stored state; outputs bf16: 2e-2, corrections fp32: 1e-4); flush pieces, scales and
+codes within the propagated bounds of the 8-bit tests with the step s_v c_k / Q. Per
+step: one token from a given stored state is exact up to the fp32-vs-fp64 decision at
+a rounding tie (bf16 entries within one bf16 step, codes within one code step, on
+< 1e-3 of the entries); longer runs free-run and are compared in aggregate."""
+import numpy as np
+import pytest
+import torch
+
+import delta_rule_recurrent_amd as m
+from delta_rule_recurrent_amd import synth
+from oracle import gdn, leapq
+from helpers import assert_rel, need_gpu, np64, rel_err, say
+from test_gpu_leapq import compare_flush, stored
+
+pytestmark = pytest.mark.gpu
+TOL_F32, TOL_BF16 = 1e-4, 2e-2
+
+
+@pytest.mark.parametrize("bits", [6, 4])
+def test_narrow_width_flush_and_window(bits):
+    """Encode the outlier initial state at b bits with 6 compensator tokens, then one
+    window of 16 decode steps (teacher forced) and the flush that closes it."""
+    dev = need_gpu()
+    say(f"leapq {bits}-bit, rank 6: flush + window")
+    Q = (1 << (bits - 1)) - 1
+    B, H, W = 4, 8, 16
+    N = B * H
+    inp = synth.leapq_decode(B=B, H=H, steps=W, device="cpu")
+    Q0 = synth.compensator_start(r=6)
+    st = m.LeapqBuffers(N, rank=6, window=W, bits=bits)
+    pre = torch.empty((N, 128, 128), device=dev)
+    m.leapq_window_flush(st, Q0.to(dev), dense=inp["S0"].to(dev), pre_round=pre)
+    torch.cuda.synchronize()
+    ref = leapq.flush(np64(inp["S0"]), np64(Q0), rank=6, bits=bits)
+    Z = st.codes.cpu().numpy()
+    assert np.abs(Z).max() == Q
+    assert np.array_equal(leapq.round_codes(pre.cpu().numpy(), bits), Z)
+    flips = compare_flush(st, ref, f"{bits}-bit encode", np64(inp["S0"]), Q=Q)
+    start = stored(st)
+    start["Q"] = Q
+    outs = [m.leapq_decode_step(st, *(inp[n][t].to(dev) for n in ("q", "k", "v", "alpha", "beta")))
+            for t in range(W)]
+    torch.cuda.synchronize()
+    o_ref, buf_ref = leapq.window_run(start, *(np64(inp[n]) for n in ("q", "k", "v", "alpha", "beta")))
+    u_gpu = np64(st.buf_u).transpose(1, 0, 2)
+    assert_rel(u_gpu, np.stack([b[1] for b in buf_ref]), TOL_F32, "corrections")
+    e = assert_rel(np64(torch.stack(outs)), o_ref, TOL_BF16, "outputs")
+    S_w = leapq.rebuild(start, [(np64(st.buf_k)[:, j], np64(st.buf_u)[:, j], np64(st.buf_a)[:, j])
+                                for j in range(W)])
+    ref = leapq.flush(S_w, np64(Q0), rank=6, bits=bits)
+    m.leapq_window_flush(st, Q0.to(dev))
+    torch.cuda.synchronize()
+    f2 = compare_flush(st, ref, f"{bits}-bit window flush", S_w, Q=Q)
+    say(f"  outputs {e:.2e}, code flips {flips} / {f2}")
+
+
+def _tokens(N, T, seed, io=torch.float32):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.nn.functional.normalize(torch.randn((N, T, 128), generator=g), dim=-1).to(io)
+    k = torch.nn.functional.normalize(torch.randn((N, T, 128), generator=g), dim=-1).to(io)
+    v = torch.randn((N, T, 128), generator=g).to(io)
+    a = torch.sigmoid(torch.randn((N, T), generator=g) + 4.0)
+    b = torch.sigmoid(torch.randn((N, T), generator=g))
+    return q, k, v, a, b
+
+
+def test_per_step_bf16_one_token_and_run():
+    dev = need_gpu()
+    say("per-step bf16 state")
+    N = 8
+    q, k, v, a, b = _tokens(N, 64, 31)
+    S0 = (0.05 * torch.randn((N, 128, 128), generator=torch.Generator().manual_seed(32))).to(torch.bfloat16)
+    # one token: the stored state after it equals the oracle's bf16 rounding
+    S = S0.to(dev).clone()
+    o1 = m.gdn_decode_step_bf16_state(S, *(x[:, :1].contiguous().to(dev) for x in (q, k, v, a, b)))
+    torch.cuda.synchronize()
+    ref_o, ref_S = leapq.per_step_bf16(*(np.swapaxes(np64(x[:, :1]), 0, 1) for x in (q, k, v)),
+                                       np64(a[:, :1]).T, np64(b[:, :1]).T, np64(S0))
+    assert_rel(np64(o1), np.swapaxes(ref_o, 0, 1), 1e-5, "one-token outputs")
+    got = np64(S)
+    diff = got != ref_S
+    # one bf16 step of the entry, or the fp32 rounding of a * s + u * k where the two
+    # terms cancel (a few 2^-24 of the state's scale)
+    ulp = np.maximum(np.abs(ref_S) * 2.0 ** -7, 8 * 2.0 ** -24 * np.abs(ref_S).max())
+    bad = diff & (np.abs(got - ref_S) > ulp * 1.01)
+    assert diff.mean() < 1e-3 and not bad.any(), (diff.mean(), got[bad][:4], ref_S[bad][:4])
+    # 64 tokens free running: outputs and final state against the oracle's run
+    S = S0.to(dev).clone()
+    o = m.gdn_decode_step_bf16_state(S, *(x.to(dev) for x in (q, k, v, a, b)))
+    torch.cuda.synchronize()
+    ref_o, ref_S = leapq.per_step_bf16(*(np.swapaxes(np64(x), 0, 1) for x in (q, k, v)), np64(a).T,
+                                       np64(b).T, np64(S0))
+    e1 = assert_rel(np64(o), np.swapaxes(ref_o, 0, 1), 1e-2, "outputs over 64 tokens")
+    e2 = assert_rel(np64(S), ref_S, 1e-2, "state after 64 tokens")
+    say(f"  64 tokens: outputs {e1:.1e}, state {e2:.1e}")
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_per_step_int_one_token_and_run(bits):
+    dev = need_gpu()
+    say(f"per-step {bits}-bit state")
+    Q = (1 << (bits - 1)) - 1
+    N = 8
+    q, k, v, a, b = _tokens(N, 64, 41 + bits)
+    S0 = 0.05 * torch.randn((N, 128, 128), generator=torch.Generator().manual_seed(42))
+    m0 = S0.abs().amax(dim=-1)
+    Z0 = torch.clamp(torch.round(S0 * (Q / m0[:, :, None])), -Q, Q).to(torch.int8)
+    Sd = np64(m0)[:, :, None] * Z0.numpy().astype(np.float64) / Q     # the stored state
+    # one token from the stored state
+    Z, mx = Z0.to(dev).clone(), m0.to(dev).clone()
+    o1 = m.gdn_decode_step_int_state(Z, mx, bits, *(x[:, :1].contiguous().to(dev) for x in (q, k, v, a, b)))
+    torch.cuda.synchronize()
+    ref_o, ref_Z, ref_m = leapq.per_step_int8(*(np.swapaxes(np64(x[:, :1]), 0, 1) for x in (q, k, v)),
+                                              np64(a[:, :1]).T, np64(b[:, :1]).T, Sd, bits=bits)
+    assert_rel(np64(o1), np.swapaxes(ref_o, 0, 1), 1e-5, "one-token outputs")
+    assert_rel(np64(mx), ref_m, 1e-6, "row maxima")
+    dz = Z.cpu().numpy().astype(np.int32) - ref_Z.astype(np.int32)
+    assert np.abs(dz).max() <= 1 and (dz != 0).mean() < 1e-3, (dz != 0).mean()
+    # 64 tokens free running
+    Z, mx = Z0.to(dev).clone(), m0.to(dev).clone()
+    o = m.gdn_decode_step_int_state(Z, mx, bits, *(x.to(dev) for x in (q, k, v, a, b)))
+    torch.cuda.synchronize()
+    ref_o, ref_Z, ref_m = leapq.per_step_int8(*(np.swapaxes(np64(x), 0, 1) for x in (q, k, v)), np64(a).T,
+                                              np64(b).T, Sd, bits=bits)
+    S_gpu = np64(mx)[:, :, None] * Z.cpu().numpy().astype(np.float64) / Q
+    S_ref = ref_m[:, :, None] * ref_Z.astype(np.float64) / Q
+    tol = 2e-2 if bits == 8 else 1e-1
+    e1 = assert_rel(np64(o), np.swapaxes(ref_o, 0, 1), tol, "outputs over 64 tokens")
+    e2 = assert_rel(S_gpu, S_ref, tol, "state after 64 tokens")
+    say(f"  64 tokens: outputs {e1:.1e}, state {e2:.1e}")
