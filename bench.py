@@ -90,6 +90,45 @@ def bench_decode(K, W, gen_steps=256):
                 wall_s=wall), inp
 
 
+def bench_decode_lowp(K, W, bits, gen_steps=256):
+    """The per-step baselines at the GDN decode shape: the state stored in bf16
+    (bits = 16) or as b-bit codes with one fp32 maximum per value row, re-rounded
+    after every token; one launch over 16,384 heads per step."""
+    B, H = DECODE_B, DECODE_H
+    N = B * H
+    name = "bf16_state" if bits == 16 else f"int{bits}_state"
+    log(f"[{name}] generating B={B} H={H} steps={gen_steps}")
+    inp = synth.gdn_decode(B=B, H=H, steps=gen_steps, device="cuda")
+    o = torch.empty((N, 1, D), dtype=torch.bfloat16, device="cuda")
+    q, k, v, a, b = (inp[n] for n in ("q", "k", "v", "alpha", "beta"))
+    if bits == 16:
+        S = inp["S0"].to(torch.bfloat16)
+        state_bytes = D * D * 2
+
+        def step(i):
+            t = i % gen_steps
+            m.gdn_decode_step_bf16_state(S, q[t, :, None], k[t, :, None], v[t, :, None],
+                                         a[t, :, None], b[t, :, None], o)
+    else:
+        Qm = (1 << (bits - 1)) - 1
+        mx = inp["S0"].abs().amax(dim=-1)
+        Z = torch.clamp(torch.round(inp["S0"] * (Qm / mx)[..., None]), -Qm, Qm).to(torch.int8)
+        state_bytes = D * D + D * 4
+
+        def step(i):
+            t = i % gen_steps
+            m.gdn_decode_step_int_state(Z, mx, bits, q[t, :, None], k[t, :, None], v[t, :, None],
+                                        a[t, :, None], b[t, :, None], o)
+    ms, wall = timed(step, K, W)
+    per_head = 2 * state_bytes + decode_bytes_per_head_step() - 2 * D * D * 4
+    gbs = per_head * N / (ms * 1e-3) / 1e9
+    del inp, q, k, v, a, b
+    return dict(workload=f"gdn_decode B=512 H=32 d=128, state {'bf16' if bits == 16 else f'int{bits} + fp32 row max'}"
+                         f" re-rounded every token, bf16 q/k/v, T=1 per launch",
+                ms_per_step=ms, tokens_per_s=B / (ms * 1e-3), bytes_per_head_step=per_head,
+                achieved_gbs=gbs, frac_hbm=gbs / PEAK_HBM_GBS, wall_s=wall)
+
+
 def bench_kda(K, W, gen_steps=256):
     """Kimi Delta Attention decode (one decay per key channel) at the GDN decode
     shape: one kda_decode_step launch over 16,384 heads per step."""
@@ -446,7 +485,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--rows", default="decode,kda,leapq,kda_leapq,gla,gla_bwd,gdn,gdn_bwd,kda_chunk")
+    ap.add_argument("--rows", default="decode,bf16_state,int8_state,kda,leapq,kda_leapq,gla,gla_bwd,gdn,gdn_bwd,"
+                                      "kda_chunk")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the measured HBM-copy and bf16-GEMM ceilings")
@@ -482,6 +522,14 @@ def main():
             cpu = cpu_baseline_decode(inp)
         del inp
         torch.cuda.empty_cache()
+    for bits, key in ((16, "bf16_state"), (8, "int8_state")):
+        if key in rows:
+            r = bench_decode_lowp(args.steps, args.warmup, bits)
+            r["speedup_vs_fp32_decode"] = res["ms_per_step"] / r["ms_per_step"] if res else None
+            out_rows[key] = r
+            log(f"[{key}] {r['ms_per_step']*1e3:.1f} us/step  {r['achieved_gbs']:.0f} GB/s  "
+                f"{r['tokens_per_s']/1e6:.3f} M tok/s")
+            torch.cuda.empty_cache()
     if "kda" in rows:
         r = bench_kda(args.steps, args.warmup)
         r["traffic_bytes"] = counter_traffic("gdn_decode_kernel<kda>")

@@ -12,87 +12,130 @@
 //                m_i <- max |S_i|, Z_i <- clamp(rint(S_i (Q / m_i)), -Q, Q).
 //                No smoothing and no compensator tokens: the page's eq. 2 scheme.
 //
-// Mapping as the fp32 decode kernel: a 256-thread block owns 8 rows of one head, 32
-// lanes per row, four key columns per lane; over T tokens in one launch the row stays
-// in registers and is rounded after every token exactly as a launch per token would.
+// Mapping: every lane holds 16 bytes of its row (8 bf16 entries, or 16 codes), so a
+// row is 16 (bf16) or 8 (codes) consecutive lanes and one wave instruction moves 1 KiB
+// of state, as in the fp32 decode kernel; a 256-thread block owns 16 (bf16) or 32
+// (codes) rows of one head. Over T tokens in one launch the row stays in registers
+// and is rounded after every token exactly as a launch per token would.
 #include "common.hpp"
 
 namespace gdnrt {
 
-// max over the 32 lanes of a row group (DPP inside 16-lane rows, then xor 16)
-__device__ __forceinline__ float max32(float x) {
-  x = fmaxf(x, dpp<0x140>(x));
+// reductions over an aligned group of L = 16 or 8 lanes (DPP inside 16-lane rows)
+template <int L>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (L == 16) return sum16(x);
+  else return sum8(x);
+}
+template <int L>
+__device__ __forceinline__ float group_max(float x) {
+  if constexpr (L == 16) x = fmaxf(x, dpp<0x140>(x));
   x = fmaxf(x, dpp<0x141>(x));
   x = fmaxf(x, dpp<0x4E>(x));
   x = fmaxf(x, dpp<0xB1>(x));
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F)));
   return x;
 }
 
 __device__ __forceinline__ float bf16_round(float x) { return bf16_to_f32(f32_to_bf16(x)); }
+
+// E entries of a q/k row at column c (fp32 or bf16 storage)
+template <typename IO, int E>
+__device__ __forceinline__ void load_vec(const IO* p, float (&x)[E]) {
+#pragma unroll
+  for (int e = 0; e < E; e += 4) {
+    const f32x4 w = io_traits<IO>::ld4(p, e);
+    x[e] = w.x;
+    x[e + 1] = w.y;
+    x[e + 2] = w.z;
+    x[e + 3] = w.w;
+  }
+}
 
 template <typename IO, bool BF16STATE>
 __global__ __launch_bounds__(256) void gdn_decode_lowp_kernel(
     void* __restrict__ Sv, float* __restrict__ rowmax, float qf, float qinv, const IO* __restrict__ q,
     const IO* __restrict__ k, const IO* __restrict__ v, const float* __restrict__ alpha,
     const float* __restrict__ beta, IO* __restrict__ o, int T) {
-  constexpr int kRowsPerBlock = 8;
-  constexpr int BPH = kD / kRowsPerBlock;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int E = BF16STATE ? 8 : 16;   // entries per lane (16 bytes)
+  constexpr int L = kD / E;               // lanes per row
+  constexpr int RPB = 256 / L;            // rows per block
+  constexpr int BPH = kD / RPB;           // blocks per head
+  const int tid = threadIdx.x;
   const int head = blockIdx.x / BPH;
-  const int row = (blockIdx.x % BPH) * kRowsPerBlock + wave * 2 + (lane >> 5);
-  const int col = (lane & 31) * 4;
+  const int row = (blockIdx.x % BPH) * RPB + tid / L;
+  const int col = (tid % L) * E;
   const size_t e0 = (size_t)head * kD * kD + (size_t)row * kD + col;
   const size_t r0 = (size_t)head * kD + row;
+  const bool lead = (tid % L) == 0;
 
-  f32x4 s;
-  uint32_t zw = 0;   // b-bit: this lane's 4 codes
+  float s[E];
   float m = 0.f;
   if constexpr (BF16STATE) {
-    const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(Sv) + e0);
-    s = f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
-              __uint_as_float(w.y & 0xffff0000u)};
+    const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(Sv) + e0);
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      s[2 * j] = __uint_as_float(ww[j] << 16);
+      s[2 * j + 1] = __uint_as_float(ww[j] & 0xffff0000u);
+    }
   } else {
-    zw = *reinterpret_cast<const uint32_t*>(static_cast<const int8_t*>(Sv) + e0);
+    const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const int8_t*>(Sv) + e0);
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
     m = rowmax[r0];
     const float sv = m * qinv;
-    s = f32x4{sv * (float)(int8_t)(zw & 0xff), sv * (float)(int8_t)((zw >> 8) & 0xff),
-              sv * (float)(int8_t)((zw >> 16) & 0xff), sv * (float)(int8_t)(zw >> 24)};
+#pragma unroll
+    for (int e = 0; e < E; ++e) s[e] = sv * (float)(int8_t)((ww[e >> 2] >> (8 * (e & 3))) & 0xff);
   }
+  uint32_t zw[4] = {0u, 0u, 0u, 0u};
 
   for (int t = 0; t < T; ++t) {
     const size_t tok = (size_t)head * T + t;
-    const f32x4 k4 = io_traits<IO>::ld4(k, tok * kD + col);
-    const f32x4 q4 = io_traits<IO>::ld4(q, tok * kD + col);
+    float k4[E], q4[E];
+    load_vec<IO, E>(k + tok * kD + col, k4);
+    load_vec<IO, E>(q + tok * kD + col, q4);
     const float a = alpha[tok], b = beta[tok];
     const float vi = io_traits<IO>::ld(v, tok * kD + row);
-    const float kq = sum32(k4.x * q4.x + k4.y * q4.y + k4.z * q4.z + k4.w * q4.w);
-    const float pk = sum32(s.x * k4.x + s.y * k4.y + s.z * k4.z + s.w * k4.w);
-    const float pq = sum32(s.x * q4.x + s.y * q4.y + s.z * q4.z + s.w * q4.w);
+    float kq = 0.f, pk = 0.f, pq = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      kq += k4[e] * q4[e];
+      pk += s[e] * k4[e];
+      pq += s[e] * q4[e];
+    }
+    kq = group_sum<L>(kq);
+    pk = group_sum<L>(pk);
+    pq = group_sum<L>(pq);
     const float u = b * (vi - a * pk);
     const float oi = a * pq + u * kq;
-    const f32x4 sn = a * s + u * k4;
-    if ((lane & 31) == 0) io_traits<IO>::st(o, tok * kD + row, oi);
-    if constexpr (BF16STATE) {
-      s = f32x4{bf16_round(sn.x), bf16_round(sn.y), bf16_round(sn.z), bf16_round(sn.w)};
-    } else {
-      m = max32(fmaxf(fmaxf(fabsf(sn.x), fabsf(sn.y)), fmaxf(fabsf(sn.z), fabsf(sn.w))));
-      const float sc = m > 0.f ? qf / m : 0.f, sv = m * qinv;
-      zw = 0;
+    if (lead) io_traits<IO>::st(o, tok * kD + row, oi);
+    float sn[E];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < E; ++e) sn[e] = a * s[e] + u * k4[e];
+    if constexpr (BF16STATE) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) s[e] = bf16_round(sn[e]);
+    } else {
+      float mx = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) mx = fmaxf(mx, fabsf(sn[e]));
+      m = group_max<L>(mx);
+      const float sc = m > 0.f ? qf / m : 0.f, sv = m * qinv;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) zw[j] = 0u;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
         const float z = fminf(fmaxf(rintf(sn[e] * sc), -qf), qf);
         s[e] = sv * z;
-        zw |= (uint32_t)((int32_t)z & 0xff) << (8 * e);
+        zw[e >> 2] |= (uint32_t)((int32_t)z & 0xff) << (8 * (e & 3));
       }
     }
   }
   if constexpr (BF16STATE) {
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(Sv) + e0) =
-        make_uint2(pack_bf16(s.x, s.y), pack_bf16(s.z, s.w));
-  } else {
-    *reinterpret_cast<uint32_t*>(static_cast<int8_t*>(Sv) + e0) = zw;
-    if ((lane & 31) == 0) rowmax[r0] = m;
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(Sv) + e0) =
+        make_uint4(pack_bf16(s[0], s[1]), pack_bf16(s[2], s[3]), pack_bf16(s[4], s[5]), pack_bf16(s[6], s[7]));
+  } else if (T > 0) {
+    *reinterpret_cast<uint4*>(static_cast<int8_t*>(Sv) + e0) = make_uint4(zw[0], zw[1], zw[2], zw[3]);
+    if (lead) rowmax[r0] = m;
   }
 }
 
@@ -128,7 +171,8 @@ static int lowp_decode(const char* fn, bool bf16state, void* S, float* rowmax, i
       (rowmax && (overlaps(rowmax, nM, S, nS) || overlaps(rowmax, nM, o, nIO))))
     return set_error(GDNRT_EINVAL, "%s: buffers overlap", fn);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid((unsigned)(N * (kD / 8))), block(256);
+  // blocks per head: 8 (bf16 rows, 16 per block) or 4 (code rows, 32 per block)
+  const dim3 grid((unsigned)(N * (bf16state ? 8 : 4))), block(256);
   const float qf = bf16state ? 0.f : (float)((1 << (bits - 1)) - 1), qinv = bf16state ? 0.f : 1.0f / qf;
 #define GDNRT_LOWP(IOT, B)                                                                              \
   hipLaunchKernelGGL((gdn_decode_lowp_kernel<IOT, B>), grid, block, 0, s, S, rowmax, qf, qinv,         \
