@@ -330,30 +330,58 @@ __device__ __forceinline__ void prep_chunk(PrepSmem& sm, KdaPrepSmem<KDA>& xs, P
     }
     *reinterpret_cast<u32x4*>(wsc + kWsK + ((size_t)f * 64 + lane) * 16) = w;
   }
-  // ---- Gram k.k -> L and scores q.k -> A: 20 tile products over the lower triangle
-  for (int u = wave; u < 20; u += 8) {
-    int rb, cb;
-    tri_pair(u >> 1, rb, cb);
-    const bool sc = u & 1;
-    const uint16_t* X = sc ? sm.Q : sm.K;
-    const uint16_t* Y = sm.K;
-    if constexpr (KDA) Y = xs.Km;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // ---- Gram k.k -> L and scores q.k -> A: 20 tile products over the lower triangle,
+  // up to three per wave, their products issued together (tile index uniform per wave)
+  {
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    f32x4 acc[3];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      acc = mfma(ld8(X + (rb * 16 + l16) * PQ + kk * 32 + lq * 8),
-                 ld8(Y + (cb * 16 + l16) * PQ + kk * 32 + lq * 8), acc);
-    const int j = cb * 16 + l16;
+    for (int t = 0; t < 3; ++t) {
+      const int u = wv + 8 * t;
+      acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (u < 20) {
+        int rb, cb;
+        tri_pair(u >> 1, rb, cb);
+        const uint16_t* X = (u & 1) ? sm.Q : sm.K;
+        const uint16_t* Y = sm.K;
+        if constexpr (KDA) Y = xs.Km;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = rb * 16 + lq * 4 + i;
-      // KDA: the decay is already inside the product; above the diagonal the product
-      // is not a decayed one, so it is dropped by selection, never multiplied by 0
-      const float val = KDA ? (j <= r ? acc[i] : 0.f) : (j <= r ? __expf(sm.lg[r] - sm.lg[j]) : 0.f) * acc[i];
-      if (sc)
-        sm.A[r * PC + j] = f32_to_bf16(val);
-      else
-        sm.rl.L[r * PF + j] = j < r ? sm.bt[r] * val : 0.f;
+        for (int kk = 0; kk < 4; ++kk)
+          acc[t] = mfma(ld8(X + (rb * 16 + l16) * PQ + kk * 32 + lq * 8),
+                        ld8(Y + (cb * 16 + l16) * PQ + kk * 32 + lq * 8), acc[t]);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+      const int u = wv + 8 * t;
+      if (u < 20) {
+        int rb, cb;
+        tri_pair(u >> 1, rb, cb);
+        const int j = cb * 16 + l16, r0 = rb * 16 + lq * 4;
+        f32x4 val;
+        if constexpr (KDA) {
+          // the decay is already inside the product; above the diagonal the product is
+          // not a decayed one, so it is dropped by selection, never multiplied by 0
+#pragma unroll
+          for (int i = 0; i < 4; ++i) val[i] = j <= r0 + i ? acc[t][i] : 0.f;
+        } else {
+          const f32x4 lgr = *reinterpret_cast<const f32x4*>(sm.lg + r0);
+          const float lgj = sm.lg[j];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float x = __expf(lgr[i] - lgj) * acc[t][i];   // g_r / g_j for j <= r
+            val[i] = j <= r0 + i ? x : 0.f;
+          }
+        }
+        if (u & 1) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sm.A[(r0 + i) * PC + j] = f32_to_bf16(val[i]);
+        } else {
+          const f32x4 bt = *reinterpret_cast<const f32x4*>(sm.bt + r0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sm.rl.L[(r0 + i) * PF + j] = j < r0 + i ? bt[i] * val[i] : 0.f;
+        }
+      }
     }
   }
   {   // the zero upper tiles that the 32-wide contraction slices of A reach: (0,1), (2,3)
@@ -416,16 +444,29 @@ __device__ __forceinline__ void prep_chunk(PrepSmem& sm, KdaPrepSmem<KDA>& xs, P
     lds_barrier();
   }
 
-  // ---- T diag(beta g) and T diag(beta) in bf16 (zero above the diagonal blocks)
-  for (int e = tid; e < C * C / 2; e += NT) {
-    const int r = e >> 5, j = 2 * (e & 31);
-    f32x2 t = {0.f, 0.f};
-    if ((j >> 4) <= (r >> 4)) t = *reinterpret_cast<const f32x2*>(sm.rt.T + r * PF + j);
-    *reinterpret_cast<unsigned*>(sm.rw.t.Tw + r * PC + j) = pack_bf16(t.x * sm.btg[j], t.y * sm.btg[j + 1]);
-    *reinterpret_cast<unsigned*>(sm.rw.t.Tu + r * PC + j) = pack_bf16(t.x * sm.bt[j], t.y * sm.bt[j + 1]);
-    if constexpr (STORE_T)   // T itself for the backward, bf16 [r][j], zero above the diagonal
-      *reinterpret_cast<unsigned*>(Tout + (size_t)cid * C * C + r * C + j) =
-          pack_bf16(j <= r ? t.x : 0.f, j + 1 <= r ? t.y : 0.f);
+  // ---- T diag(beta g) and T diag(beta) in bf16 (zero above the diagonal blocks):
+  // thread -> row tid / 8, columns 8 (tid % 8) .. + 7
+  {
+    const int r = tid >> 3, j0 = (tid & 7) * 8;
+    f32x4 t0 = {0.f, 0.f, 0.f, 0.f}, t1 = t0;
+    if ((j0 >> 4) <= (r >> 4)) {
+      t0 = *reinterpret_cast<const f32x4*>(sm.rt.T + r * PF + j0);
+      t1 = *reinterpret_cast<const f32x4*>(sm.rt.T + r * PF + j0 + 4);
+    }
+    const f32x4 g0 = *reinterpret_cast<const f32x4*>(sm.btg + j0), g1 = *reinterpret_cast<const f32x4*>(sm.btg + j0 + 4);
+    const f32x4 b0 = *reinterpret_cast<const f32x4*>(sm.bt + j0), b1 = *reinterpret_cast<const f32x4*>(sm.bt + j0 + 4);
+    const f32x4 w0 = t0 * g0, w1 = t1 * g1, u0 = t0 * b0, u1 = t1 * b1;
+    *reinterpret_cast<u32x4*>(sm.rw.t.Tw + r * PC + j0) =
+        u32x4{pack_bf16(w0.x, w0.y), pack_bf16(w0.z, w0.w), pack_bf16(w1.x, w1.y), pack_bf16(w1.z, w1.w)};
+    *reinterpret_cast<u32x4*>(sm.rw.t.Tu + r * PC + j0) =
+        u32x4{pack_bf16(u0.x, u0.y), pack_bf16(u0.z, u0.w), pack_bf16(u1.x, u1.y), pack_bf16(u1.z, u1.w)};
+    if constexpr (STORE_T) {   // T itself for the backward, bf16 [r][j], zero above the diagonal
+      float tt[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) tt[e] = j0 + e <= r ? tt[e] : 0.f;
+      *reinterpret_cast<u32x4*>(Tout + (size_t)cid * C * C + r * C + j0) =
+          u32x4{pack_bf16(tt[0], tt[1]), pack_bf16(tt[2], tt[3]), pack_bf16(tt[4], tt[5]), pack_bf16(tt[6], tt[7])};
+    }
   }
   lds_barrier();
 
