@@ -90,3 +90,22 @@ def test_full_size_config_sampled():
     for got, r, name in zip(out, ref, ("dq", "dk", "dv", "dlog_g", "dS0")):
         e = assert_rel(np64(got[idx]), r, TOL, name)
         say(f"  {name} err {e:.2e}")
+
+
+@pytest.mark.parametrize("case", ["no_decay", "fast_decay"])
+def test_degenerate_gates(case):
+    """log-gates 0 (plain linear attention, nothing forgotten) and log-gates down to
+    log 0.05 on every channel (the state forgets within a few tokens)."""
+    dev = need_gpu()
+    say(f"gla_chunk_bwd: degenerate gates, {case}")
+    N, T = 2, 128
+    inp, dO, dST = _grads(N, T, dev, 960)
+    if case == "no_decay":
+        inp["log_g"] = torch.zeros_like(inp["log_g"])
+    else:
+        g = torch.Generator().manual_seed(961)
+        inp["log_g"] = torch.log(0.05 + 0.5 * torch.rand(inp["log_g"].shape, generator=g))
+    d = {k_: t.to(dev) for k_, t in inp.items()}
+    out = m.gla_chunk_bwd(d["q"], d["k"], d["v"], d["log_g"], dO.to(dev), S0=d["S0"], dST=dST.to(dev))
+    torch.cuda.synchronize()
+    _check(out, inp, dO, dST, slice(None), case)
