@@ -134,3 +134,48 @@ def test_per_step_int_one_token_and_run(bits):
     e1 = assert_rel(np64(o), np.swapaxes(ref_o, 0, 1), tol, "outputs over 64 tokens")
     e2 = assert_rel(S_gpu, S_ref, tol, "state after 64 tokens")
     say(f"  64 tokens: outputs {e1:.1e}, state {e2:.1e}")
+
+
+def test_per_step_baselines_full_decode_shape_sampled():
+    """512 streams x 32 heads, one token per launch as the benchmark times them:
+    sampled heads of the BF16 and INT8 per-step states after 4 steps against the
+    oracle's per-step schemes run from the same stored states."""
+    dev = need_gpu()
+    B, H, steps = 512, 32, 4
+    N = B * H
+    say(f"per-step baselines: B={B} H={H} steps={steps}")
+    inp = synth.gdn_decode(B=B, H=H, steps=steps, device=dev)
+    heads = torch.tensor([0, 7, 31, 32 * 100 + 3, 32 * 333 + 17, N - 1])
+    S_bf = inp["S0"].to(torch.bfloat16)
+    mx = inp["S0"].abs().amax(dim=-1)
+    Z = torch.clamp(torch.round(inp["S0"] * (127.0 / mx)[..., None]), -127, 127).to(torch.int8)
+    start_bf, start_Z, start_m = S_bf[heads].cpu(), Z[heads].cpu(), mx[heads].cpu()
+    o_bf, o_i8 = [], []
+    for t in range(steps):
+        args = [inp[n_][t, :, None] for n_ in ("q", "k", "v", "alpha", "beta")]
+        o_bf.append(m.gdn_decode_step_bf16_state(S_bf, *args)[:, 0])
+        o_i8.append(m.gdn_decode_step_int_state(Z, mx, 8, *args)[:, 0])
+    torch.cuda.synchronize()
+    sel = lambda x: np64(x[:, heads])
+    ins = [sel(inp[n_]) for n_ in ("q", "k", "v", "alpha", "beta")]
+    ref_o, ref_S = leapq.per_step_bf16(*ins, np64(start_bf))
+    assert_rel(np64(torch.stack(o_bf)[:, heads]), ref_o, TOL_BF16, "bf16 state outputs")
+    assert_rel(np64(S_bf[heads]), ref_S, 1e-2, "bf16 state")
+    Sd = np64(start_m)[:, :, None] * start_Z.numpy().astype(np.float64) / 127.0
+    ref_o, ref_Z, ref_m = leapq.per_step_int8(*ins, Sd)
+    assert_rel(np64(torch.stack(o_i8)[:, heads]), ref_o, TOL_BF16, "int8 state outputs")
+    S_gpu = np64(mx[heads])[:, :, None] * Z[heads].cpu().numpy().astype(np.float64) / 127.0
+    assert_rel(S_gpu, ref_m[:, :, None] * ref_Z.astype(np.float64) / 127.0, 2e-2, "int8 state")
+
+
+def test_error_study_trend_long_memory():
+    """Trend only (parity unpinned): the GPU error study on 1 stream x 32 heads over
+    512 tokens in the long-memory regime orders per-token rounding above the window
+    and the window above the window with compensator tokens and smoothing (8 bits)."""
+    need_gpu()
+    from delta_rule_recurrent_amd import error_study
+    res = error_study.run(streams=1, heads=32, steps=512, every=256, regime="long", log=lambda s: None)
+    e = {k_: v_["ordinary"][-1] for k_, v_ in res["schemes"].items()}
+    say("  " + ", ".join(f"{k_} {100 * v_:.2f}%" for k_, v_ in e.items()))
+    assert e["per-step int8"] > e["window int8"] > e["window int8 + 4 CT + smooth"], e
+    assert e["per-step int4"] > e["window int4 + 6 CT + smooth"], e
