@@ -23,6 +23,12 @@ Pins (tests/test_oracle_gla.py): with zero log-gates the output is the textbook
 causal linear attention tril(Q K^T) V + Q S_0^T; eq. 6 (final state from S_0 is
 the decayed S_0 plus the state from zero); the decay acts on key columns; one
 token from zero gives v (k . q); chunk form == recurrence for C in {1, 16, 64}.
+``zeco_local``, ``zeco_all_scan_step``, ``zeco_output`` and ``zeco_forward``
+take ZeCO's three forward phases in the page's order (local chunk states and
+cumulative decays from zero, the All-Scan update, outputs from the received
+state); they are pinned by the recurrence over the whole sequence for several
+device and block counts, by the closed form of the cumulative decays and by the
+local states at the chunk boundaries.
 ``gla_recurrent_bwd`` (reverse mode through the recurrence) is pinned by torch
 autograd of a separately written forward, by central differences, by the textbook
 gradients of causal linear attention at zero log-gates, and by ZeCO's chunk-level
@@ -77,6 +83,108 @@ def gla_chunk(q, k, v, log_g, S0=None, chunk=64):
         o[:, sl] = np.einsum("nrk,nvk->nrv", Qt, S) + np.einsum("nrj,njv->nrv", A, v[:, sl])
         S = np.exp(b[:, -1])[:, None, :] * S + np.einsum("njv,njk->nvk", v[:, sl], Kg)
     return o, S
+
+
+def zeco_local(k, v, log_g, chunk=64):
+    """Phase 1 of ZeCO's forward on one device (page section "Local State
+    Computation"): from a zero state, the chunk states and the cumulative decays
+
+        S_[n]      = gamma_[n] (on key columns) o S_[n-1] + ((K o Gamma)^T V)^T,
+        gamma~_[n] = gamma~_[n-1] o gamma_[n],      gamma_[n] = exp(b_C of chunk n),
+
+    for n = 1..nc, with S_[0] = 0 and gamma~_[0] = 1. Returns
+    (S [N][nc+1][d_v][d_k], gam [N][nc+1][d_k])."""
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    lg = np.asarray(log_g, np.float64)
+    N, T, dk = k.shape
+    dv = v.shape[2]
+    if T % chunk:
+        raise ValueError("T must be a multiple of chunk")
+    nc = T // chunk
+    S = np.zeros((N, nc + 1, dv, dk))
+    gam = np.ones((N, nc + 1, dk))
+    for n in range(nc):
+        sl = slice(n * chunk, (n + 1) * chunk)
+        b = np.cumsum(lg[:, sl], axis=1)
+        Kg = k[:, sl] * np.exp(b[:, -1:, :] - b)            # K o Gamma
+        gamma = np.exp(b[:, -1])                            # chunk decay per key
+        S[:, n + 1] = gamma[:, None, :] * S[:, n] + np.einsum("njv,njk->nvk", v[:, sl], Kg)
+        gam[:, n + 1] = gam[:, n] * gamma
+    return S, gam
+
+
+def zeco_all_scan_step(S_local, gam_total, S_recv=None, blocks=1):
+    """One device's step of All-Scan (page section "All-Scan Collective
+    Communication"): the key channels are cut into ``blocks`` contiguous blocks,
+    and each block of the state to send is the received block decayed by the
+    device's total cumulative decay plus the local final state's block,
+    S_send = gamma~_[N] (on key columns) o S_recv + S_[N]. The start device has
+    nothing to receive (``S_recv`` None) and sends its local state.
+    S_local, S_recv: [N][d_v][d_k]; gam_total: [N][d_k]."""
+    S_local = np.asarray(S_local, np.float64)
+    if S_recv is None:
+        return S_local.copy()
+    S_recv = np.asarray(S_recv, np.float64)
+    gam_total = np.asarray(gam_total, np.float64)
+    dk = S_local.shape[2]
+    out = np.empty_like(S_local)
+    edges = np.linspace(0, dk, blocks + 1).astype(int)
+    for k0, k1 in zip(edges[:-1], edges[1:]):
+        out[:, :, k0:k1] = gam_total[:, None, k0:k1] * S_recv[:, :, k0:k1] + S_local[:, :, k0:k1]
+    return out
+
+
+def zeco_output(q, k, v, log_g, S_states, gam, S_in=None, chunk=64):
+    """Phase 3 of ZeCO's forward (page section "The Complete Forward Algorithm"):
+    per chunk n, from the local state before it and the received state,
+
+        O_[n] = Q~_[n] (S_[n-1] + gamma~_[n-1] o S_in)^T + P_[n] V_[n],
+        Q~ = Q o Lambda,  P = (Q~ (K / Lambda)^T) o M,
+
+    with Lambda = exp(b), b the inclusive in-chunk cumulative log-gate and M lower
+    triangular including the diagonal (the inclusive read-out o_t = S_t q_t).
+    S_states, gam: as returned by ``zeco_local``; S_in None is a zero state."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    lg = np.asarray(log_g, np.float64)
+    N, T, dk = k.shape
+    dv = v.shape[2]
+    M = np.tril(np.ones((chunk, chunk)))
+    o = np.empty((N, T, dv))
+    for n in range(T // chunk):
+        sl = slice(n * chunk, (n + 1) * chunk)
+        b = np.cumsum(lg[:, sl], axis=1)
+        Qt = q[:, sl] * np.exp(b)
+        Kt = k[:, sl] * np.exp(-b)
+        S = S_states[:, n]
+        if S_in is not None:
+            S = S + gam[:, n][:, None, :] * np.asarray(S_in, np.float64)
+        P = np.einsum("nrk,njk->nrj", Qt, Kt) * M
+        o[:, sl] = np.einsum("nrk,nvk->nrv", Qt, S) + np.einsum("nrj,njv->nrv", P, v[:, sl])
+    return o
+
+
+def zeco_forward(q, k, v, log_g, devices, S0=None, chunk=64, blocks=1):
+    """ZeCO's forward over ``devices`` devices, run one after the other here: the
+    sequence is cut into that many contiguous shards of whole chunks; each runs
+    phase 1 from a zero state; All-Scan passes the states along the devices in
+    order, starting from S0 (None = zero); each device then computes its outputs
+    from the state it received. Returns (o [N][T][d_v], S_T [N][d_v][d_k])."""
+    T = np.asarray(k).shape[1]
+    if T % (devices * chunk):
+        raise ValueError("T must be a multiple of devices * chunk")
+    L = T // devices
+    outs = []
+    S_recv = None if S0 is None else np.asarray(S0, np.float64)
+    for p in range(devices):
+        sl = slice(p * L, (p + 1) * L)
+        Ss, gam = zeco_local(k[:, sl], v[:, sl], log_g[:, sl], chunk)
+        S_send = zeco_all_scan_step(Ss[:, -1], gam[:, -1], S_recv, blocks)
+        outs.append(zeco_output(q[:, sl], k[:, sl], v[:, sl], log_g[:, sl], Ss, gam, S_recv, chunk))
+        S_recv = S_send
+    return np.concatenate(outs, axis=1), S_recv
 
 
 def gla_recurrent_bwd(q, k, v, log_g, S0, dO, dST=None, ckpt=64):

@@ -217,3 +217,49 @@ def test_backward_gate_gradient_beyond_a_boundary():
         *_, dS_mid = gla.gla_recurrent_bwd(q[:, t0:], k[:, t0:], v[:, t0:], lg[:, t0:], S_mid, dO[:, t0:], dST)
         np.testing.assert_allclose(dg[:, t0], np.einsum("nvk,nvk->nk", dS_mid, S_mid), rtol=0,
                                    atol=1e-10 * np.abs(dg).max())
+
+
+@pytest.mark.parametrize("devices,blocks", [(1, 1), (2, 1), (4, 4), (3, 2)])
+def test_zeco_forward_equals_recurrence(devices, blocks):
+    """ZeCO's three phases over several devices (local states from zero, All-Scan
+    in device order with the state cut into key blocks, outputs from the received
+    state) give the recurrence over the whole sequence, from a nonzero S0."""
+    rng = np.random.default_rng(46)
+    N, C, d = 2, 16, 8
+    T = devices * 2 * C
+    q, k, v, lg = _rand(rng, N, T, d, mu=1.0)
+    S0 = rng.standard_normal((N, d, d))
+    o_ref, S_ref = gla.gla_recurrent(q, k, v, lg, S0)
+    o, S = gla.zeco_forward(q, k, v, lg, devices, S0, chunk=C, blocks=blocks)
+    np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-12 * np.abs(o_ref).max())
+    np.testing.assert_allclose(S, S_ref, rtol=0, atol=1e-12 * np.abs(S_ref).max())
+
+
+def test_zeco_local_states_and_decays():
+    """Phase 1: S_[n] is the state from zero after n chunks (the recurrence cut
+    there), and gamma~_[n] is exp of the log-gates summed over those tokens."""
+    rng = np.random.default_rng(47)
+    N, T, d, C = 2, 64, 6, 16
+    q, k, v, lg = _rand(rng, N, T, d)
+    Ss, gam = gla.zeco_local(k, v, lg, C)
+    assert Ss.shape == (N, T // C + 1, d, d) and gam.shape == (N, T // C + 1, d)
+    np.testing.assert_array_equal(Ss[:, 0], 0.0)
+    np.testing.assert_array_equal(gam[:, 0], 1.0)
+    for n in range(1, T // C + 1):
+        _, S_n = gla.gla_recurrent(q[:, :n * C], k[:, :n * C], v[:, :n * C], lg[:, :n * C], None)
+        np.testing.assert_allclose(Ss[:, n], S_n, rtol=0, atol=1e-12 * np.abs(S_n).max())
+        np.testing.assert_allclose(gam[:, n], np.exp(lg[:, :n * C].sum(axis=1)), rtol=1e-13)
+
+
+def test_zeco_all_scan_step_blocks_and_start_device():
+    """All-Scan's update is elementwise along the key channels: cutting the state
+    into 1, 2 or 8 blocks gives the same result bit for bit, and the start device
+    sends its local state unchanged."""
+    rng = np.random.default_rng(48)
+    N, d = 3, 8
+    S_loc, S_recv = rng.standard_normal((2, N, d, d))
+    gam = rng.uniform(0.1, 1.0, (N, d))
+    ref = gam[:, None, :] * S_recv + S_loc
+    for blocks in (1, 2, 8):
+        np.testing.assert_array_equal(gla.zeco_all_scan_step(S_loc, gam, S_recv, blocks), ref)
+    np.testing.assert_array_equal(gla.zeco_all_scan_step(S_loc, gam, None), S_loc)
