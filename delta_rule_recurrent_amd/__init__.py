@@ -4,7 +4,10 @@ Entry points over the gdnrt HIP library (C ABI in include/gdnrt.h):
 ``gdn_decode_step``, ``gla_chunk_fwd``, ``gla_chunk_bwd``, ``gdn_chunk_fwd``, ``gdn_chunk_bwd``,
 ``leapq_decode_step``,
 ``leapq_window_flush``, ``kda_decode_step``, ``kda_chunk_fwd``,
-``kda_leapq_decode_step`` and ``kda_leapq_window_flush``. ``synth`` draws the seeded synthetic workloads.
+``kda_leapq_decode_step``, ``kda_leapq_window_flush``, and the per-device calls of ZeCO's
+sequence-parallel GLA forward: ``gla_shard_local`` (``gla_chunk_fwd`` from zero and
+``gla_shard_decay``), ``gla_all_scan_step`` and ``gla_shard_output_correct``. ``synth``
+draws the seeded synthetic workloads.
 """
 from .binding import (  # noqa: F401
     GdnrtError,
@@ -20,6 +23,10 @@ from .binding import (  # noqa: F401
     gla_chunk_bwd_workspace,
     gla_chunk_fwd,
     gla_chunk_workspace,
+    gla_all_scan_step,
+    gla_shard_decay,
+    gla_shard_local,
+    gla_shard_output_correct,
     kda_chunk_fwd,
     kda_chunk_workspace,
     kda_decode_step,

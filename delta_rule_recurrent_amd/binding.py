@@ -37,6 +37,9 @@ SIGNATURES = {
     "kda_decode_step": ([_vp] * 7 + [_c_int] * 5 + [_vp], _c_int),
     "gla_chunk_fwd": ([_vp] * 7 + [_c_int] * 6 + [_vp, ctypes.c_size_t, _vp], _c_int),
     "gla_chunk_fwd_workspace_bytes": ([_c_int] * 5, ctypes.c_size_t),
+    "gla_shard_decay": ([_vp, ctypes.c_size_t, _vp] + [_c_int] * 4 + [_vp], _c_int),
+    "gla_all_scan_step": ([_vp, _vp, ctypes.c_size_t, _vp, _vp] + [_c_int] * 5 + [_vp], _c_int),
+    "gla_shard_output_correct": ([_vp, ctypes.c_size_t, _vp, _vp, _vp] + [_c_int] * 6 + [_vp], _c_int),
     "gdn_chunk_fwd": ([_vp] * 8 + [_c_int] * 6 + [_vp, ctypes.c_size_t, _vp], _c_int),
     "gdn_chunk_fwd_workspace_bytes": ([_c_int] * 5, ctypes.c_size_t),
     "kda_chunk_fwd": ([_vp] * 8 + [_c_int] * 6 + [_vp, ctypes.c_size_t, _vp], _c_int),
@@ -226,6 +229,69 @@ def gla_chunk_fwd(q, k, v, log_g, S0=None, ST=None, o=None, workspace=None, chun
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(S0), _ptr(ST), _ptr(o),
         N, T, D, D, chunk, BF16, _ptr(workspace), workspace.numel(), _stream()))
     return o, ST
+
+
+def gla_shard_decay(workspace, N, T, gamma=None, chunk=CHUNK):
+    """ZeCO's cumulative decays of a shard from the workspace its gla_chunk_fwd call
+    left: gamma [N][T/chunk + 1][128] fp32, gamma[n][c] = product of the chunk decays
+    e^{b_C} of chunks 0..c-1."""
+    _need(workspace, "workspace", torch.uint8)
+    if gamma is None:
+        gamma = torch.empty((N, T // chunk + 1, D), dtype=torch.float32, device=workspace.device)
+    _need(gamma, "gamma", torch.float32, (N, T // chunk + 1, D))
+    _check("gla_shard_decay", lib().gla_shard_decay(
+        _ptr(workspace), workspace.numel(), _ptr(gamma), N, T, D, chunk, _stream()))
+    return gamma
+
+
+def gla_all_scan_step(S_local, gamma_total=None, S_recv=None, S_send=None, k0=0, k1=D):
+    """One device's All-Scan update of key channels [k0, k1):
+    S_send = gamma_total o S_recv + S_local (S_recv None: S_send = S_local).
+    gamma_total [N][128] fp32 with unit stride along the keys (a view such as
+    gamma[:, -1] of gla_shard_decay's output is accepted). Returns S_send."""
+    N = S_local.shape[0]
+    _need(S_local, "S_local", torch.float32, (N, D, D))
+    if S_send is None:
+        S_send = torch.empty_like(S_local)
+    _need(S_send, "S_send", torch.float32, (N, D, D))
+    stride = D
+    if S_recv is not None:
+        _need(S_recv, "S_recv", torch.float32, (N, D, D))
+        if not isinstance(gamma_total, torch.Tensor) or gamma_total.dtype != torch.float32 or \
+                tuple(gamma_total.shape) != (N, D) or gamma_total.stride(1) != 1 or not gamma_total.is_cuda:
+            raise ValueError("gamma_total must be a [N][128] float32 GPU tensor with unit stride along keys")
+        stride = gamma_total.stride(0) if N > 1 else D
+    _check("gla_all_scan_step", lib().gla_all_scan_step(
+        _ptr(S_recv), None if S_recv is None else gamma_total.data_ptr(), stride, _ptr(S_local),
+        _ptr(S_send), N, D, D, k0, k1, _stream()))
+    return S_send
+
+
+def gla_shard_output_correct(workspace, gamma, S_in, o, chunk=CHUNK):
+    """Adds the received state's share to a shard's outputs (o from gla_chunk_fwd with
+    a zero state, updated in place): o_t += S_in (q_t o e^{b_t} o gamma[c(t)])."""
+    N, T, _ = o.shape
+    _need(o, "o", torch.bfloat16, (N, T, D))
+    _need(workspace, "workspace", torch.uint8)
+    _need(gamma, "gamma", torch.float32, (N, T // chunk + 1, D))
+    if S_in is not None:
+        _need(S_in, "S_in", torch.float32, (N, D, D))
+    _check("gla_shard_output_correct", lib().gla_shard_output_correct(
+        _ptr(workspace), workspace.numel(), _ptr(gamma), _ptr(S_in), _ptr(o), N, T, D, D, chunk, BF16,
+        _stream()))
+    return o
+
+
+def gla_shard_local(q, k, v, log_g, workspace=None, chunk=CHUNK):
+    """ZeCO's first phase on one device: gla_chunk_fwd from a zero state and the
+    cumulative decays. Returns (o_local, S_local, gamma, workspace); the workspace
+    is read again by gla_shard_output_correct."""
+    N, T, _ = q.shape
+    if workspace is None:
+        workspace = gla_chunk_workspace(N, T, q.device, chunk)
+    o, S_local = gla_chunk_fwd(q, k, v, log_g, None, None, None, workspace, chunk)
+    gamma = gla_shard_decay(workspace, N, T, chunk=chunk)
+    return o, S_local, gamma, workspace
 
 
 def gdn_chunk_workspace(N, T, device="cuda", chunk=CHUNK):

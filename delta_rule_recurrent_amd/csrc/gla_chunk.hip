@@ -21,6 +21,7 @@
 // one barrier per chunk, the operands of the chunk two ahead in flight. bf16 MFMA
 // (v_mfma_f32_16x16x32_bf16) with fp32 accumulation throughout.
 #include "common.hpp"
+#include "gla_chunk_layout.hpp"
 
 namespace gdnrt {
 
@@ -32,15 +33,7 @@ constexpr int PQ = kD + 8;   // bf16 pitch of 128-wide rows read by rows (confli
 constexpr int PT = kD + 16;  // bf16 pitch of 128-wide rows read transposed (conflict-free ds_read_b64_tr_b16)
 constexpr int PC = C + 8;    // bf16 pitch of 64-wide rows
 
-// Workspace per chunk (bytes). With lane = 16 lq + l16 of a wave:
-//  Q^  [64 tokens][128 keys]: 16 A-operand fragments (rb, ks) of 1 KB; the lane holds
-//      token 16 rb + l16, keys 32 ks + 8 lq + {0..7}
-//  K^  [64 tokens][128 keys]: 16 B-operand fragments (kb, js); the lane holds key
-//      16 kb + l16, tokens 32 js + 8 lq + {0..7}
-//  O~  [64 tokens][128 values]: 32 accumulator tiles (rb, vb) of 512 B; the lane holds
-//      tokens 16 rb + 4 lq + {0..3} of value 16 vb + l16
-//  eC  e^{b_C} per key, fp32
-constexpr size_t kWQ = 0, kWK = 16384, kWO = 32768, kWE = 49152, kWChunk = 49664;
+// The workspace layout per chunk (Q^, K^, O~ fragments, e^{b_C}) is in gla_chunk_layout.hpp.
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));

@@ -115,6 +115,58 @@ GDNRT_API int gla_chunk_fwd(const void* q, const void* k, const void* v, const f
 GDNRT_API size_t gla_chunk_fwd_workspace_bytes(int N, int T, int dk, int dv, int chunk);
 
 /*
+ * Sequence parallelism for GLA, the per-device calls ("ZeCO: Zero Communication
+ * Overhead Sequence Parallelism for Linear Attention", sections "Local State
+ * Computation", "Global State Update Formula" (eq. 6), "All-Scan Collective
+ * Communication" and "The Complete Forward Algorithm"). The sequence is cut into
+ * contiguous shards of whole chunks, one per device. A device:
+ *   1. runs gla_chunk_fwd on its shard from a zero state (S0 = NULL): local outputs o,
+ *      local final state S_[N] (its ST), and a workspace holding per chunk
+ *      Q o e^b and the chunk decay gamma = e^{b_C};
+ *   2. gla_shard_decay: the cumulative decays gamma~ from that workspace;
+ *   3. gla_all_scan_step, block by block along d_k: receives block k of the state
+ *      from the previous device and forms the block to send to the next one;
+ *   4. gla_shard_output_correct: adds the received state's share to its outputs.
+ * o and the last device's sent state then equal one gla_chunk_fwd over the whole
+ * sequence. Moving the state blocks between devices is the caller's (one
+ * point-to-point send/receive per block); nothing here communicates.
+ *
+ * Between steps 1 and 4 the workspace must hold what gla_chunk_fwd left in it
+ * (same N, T; not reused meanwhile).
+ */
+
+/* gamma [N][T/chunk + 1][dk] fp32, 16-byte aligned: gamma[n][c][k] is the product of
+ * the chunk decays e^{b_C}[k] of chunks 0..c-1 of sequence n (gamma~_[c] of the page;
+ * gamma[n][0] = 1 and gamma[n][T/chunk] is the shard's total decay). workspace,
+ * ws_bytes: as passed to gla_chunk_fwd for this shard (N, T). T = 0 writes the ones. */
+GDNRT_API int gla_shard_decay(const void* workspace, size_t ws_bytes, float* gamma,
+                    int N, int T, int dk, int chunk, void* stream);
+
+/* All-Scan update of key channels [k0, k1) (0 <= k0 <= k1 <= dk):
+ *     S_send[n][v][k] = gamma_n[k] S_recv[n][v][k] + S_local[n][v][k],
+ * gamma_n = gamma + n * gamma_stride (floats, >= dk): the shard's total decay, e.g.
+ * gla_shard_decay's output with offset (T/chunk) * dk and stride (T/chunk + 1) * dk.
+ * S_recv NULL (the first device): S_send = S_local, and gamma may be NULL. States
+ * [N][dv][dk] fp32, 4-byte aligned; S_send may equal S_local or S_recv, other overlaps
+ * are rejected. Channels outside [k0, k1) of S_send are not touched. */
+GDNRT_API int gla_all_scan_step(const float* S_recv, const float* gamma, size_t gamma_stride,
+                      const float* S_local, float* S_send, int N, int dk, int dv, int k0, int k1,
+                      void* stream);
+
+/* Adds to the outputs o [N][T][dv] (bf16, those of gla_chunk_fwd from a zero state)
+ * the share of the received state S_in [N][dv][dk] (fp32):
+ *     o_t += S_in (q_t o e^{b_t} o gamma~_[c]),   token t in chunk c,
+ * b the inclusive cumulative log-gate within the chunk; gamma from gla_shard_decay.
+ * The scaled query is formed in bf16 (from the workspace's bf16 Q o e^b), the state
+ * is rounded to bf16 for the matrix cores, accumulation is fp32 and o is rounded
+ * once. S_in NULL (the first device, or a zero incoming state) does nothing.
+ * workspace, gamma, S_in, o: 16-byte aligned; o must not overlap the others.
+ * io must be GDNRT_BF16. */
+GDNRT_API int gla_shard_output_correct(const void* workspace, size_t ws_bytes, const float* gamma,
+                             const float* S_in, void* o, int N, int T, int dk, int dv, int chunk,
+                             int io, void* stream);
+
+/*
  * Gated linear attention, chunkwise backward of one sequence shard ("ZeCO: Zero
  * Communication Overhead Sequence Parallelism for Linear Attention", section "The
  * Backward Algorithm and Gradient Flow": the state gradient flows backward over the

@@ -37,7 +37,8 @@ def test_header_declares_the_entry_points():
               "kda_leapq_window_flush", "kda_chunk_fwd", "kda_chunk_fwd_workspace_bytes",
               "gla_chunk_bwd", "gla_chunk_bwd_workspace_bytes", "gdn_chunk_bwd",
               "gdn_chunk_bwd_workspace_bytes", "gdn_decode_step_bf16_state",
-              "gdn_decode_step_int_state"):
+              "gdn_decode_step_int_state", "gla_shard_decay", "gla_all_scan_step",
+              "gla_shard_output_correct"):
         assert n in names, n
 
 
@@ -195,3 +196,37 @@ def test_gdn_bwd_validation(lib):
     assert f(*args(128, 1 << 34, dS0=None)) == EINVAL
     assert f(*args(128, 1 << 34)) == EINVAL                              # outputs overlap inputs
     assert "gdn_chunk_bwd" in _err(lib)
+
+
+def test_gla_shard_validation(lib):
+    p = ctypes.c_void_p(4096)
+    ws_need = 2 * 2 * 49664
+    # gla_shard_decay(workspace, ws_bytes, gamma, N, T, dk, chunk, stream)
+    f = lib.gla_shard_decay
+    assert f(p, ws_need - 1, ctypes.c_void_p(1 << 30), 2, 128, 128, 64, None) == EINVAL
+    assert f(p, ws_need, ctypes.c_void_p(1 << 30), 2, 96, 128, 64, None) == ESHAPE
+    assert f(p, ws_need, ctypes.c_void_p((1 << 30) + 4), 2, 128, 128, 64, None) == EALIGN
+    assert f(p, ws_need, None, 2, 128, 128, 64, None) == EINVAL
+    assert f(p, ws_need, p, 2, 128, 128, 64, None) == EINVAL           # gamma overlaps the workspace
+    assert "gla_shard_decay" in _err(lib)
+    assert f(p, 0, None, 0, 128, 128, 64, None) == OK                  # nothing to do
+    # gla_all_scan_step(S_recv, gamma, gamma_stride, S_local, S_send, N, dk, dv, k0, k1, stream)
+    f = lib.gla_all_scan_step
+    a, b, c, g = (ctypes.c_void_p(x << 30) for x in (1, 2, 3, 4))
+    assert f(a, g, 128, b, c, 2, 128, 128, 0, 129, None) == ESHAPE      # key block past d_k
+    assert f(a, g, 128, b, c, 2, 128, 128, 64, 32, None) == ESHAPE     # k1 < k0
+    assert f(a, None, 128, b, c, 2, 128, 128, 0, 128, None) == EINVAL  # S_recv without gamma
+    assert f(a, g, 64, b, c, 2, 128, 128, 0, 128, None) == ESHAPE      # gamma_stride < d_k
+    assert f(a, g, 128, b, ctypes.c_void_p((2 << 30) + 256), 2, 128, 128, 0, 128, None) == EINVAL
+    assert "gla_all_scan_step" in _err(lib)
+    assert f(a, g, 128, b, c, 2, 128, 128, 16, 16, None) == OK          # empty key block
+    assert f(a, g, 128, b, c, 0, 128, 128, 0, 128, None) == OK
+    # gla_shard_output_correct(workspace, ws_bytes, gamma, S_in, o, N, T, dk, dv, chunk, io, stream)
+    f = lib.gla_shard_output_correct
+    assert f(a, ws_need, g, b, c, 2, 128, 128, 128, 64, 0, None) == EDTYPE
+    assert f(a, ws_need, g, None, c, 2, 128, 128, 128, 64, 1, None) == OK   # no incoming state
+    assert f(a, ws_need - 1, g, b, c, 2, 128, 128, 128, 64, 1, None) == EINVAL
+    assert f(a, ws_need, g, b, ctypes.c_void_p((3 << 30) + 8), 2, 128, 128, 128, 64, 1, None) == EALIGN
+    assert f(a, ws_need, g, b, ctypes.c_void_p((1 << 30) + 1024), 2, 128, 128, 128, 64, 1, None) == EINVAL
+    assert f(a, ws_need, g, b, c, 2, 100, 128, 128, 64, 1, None) == ESHAPE
+    assert "gla_shard_output_correct" in _err(lib)
