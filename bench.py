@@ -1,6 +1,7 @@
 """Benchmark of the gated delta-rule hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--rows decode,kda,leapq,kda_leapq,gla,gla_bwd,gdn,kda_chunk]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--rows decode,bf16_state,int8_state,kda,leapq,
+                     kda_leapq,gla,zeco,gla_bwd,gdn,gdn_bwd,kda_chunk]
 
 Headline (`value`): Gated DeltaNet decode of one layer, 512 streams x 32 heads,
 d_k = d_v = 128, fp32 state resident in HBM, bf16 q/k/v; one step = one token for
@@ -54,6 +55,26 @@ def timed(fn, K, W):
     e1.record(s)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / K, time.perf_counter() - t0
+
+
+def timed_graph(fn, K, reps=20):
+    """GPU time per call of a launch-bound call: ``reps`` calls captured in one HIP
+    graph, the graph replayed K times between events (the host's launch cost per call
+    would otherwise exceed the kernels' own time). Returns (ms per call, wall s)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(3):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(reps):
+            fn(i)
+    ms, wall = timed(lambda i: g.replay(), K, 2)
+    del g
+    return ms / reps, wall
 
 
 # ------------------------------------------------------------------- decode
@@ -295,6 +316,58 @@ def bench_gla(K=20, W=3, B=4, H=16, T=4096):
     return res
 
 
+def bench_zeco(K=20, W=3, B=4, H=16, T=4096, blocks=4):
+    """The per-device work that ZeCO's sequence parallelism adds to a GLA prefill
+    shard (one device's share at the prefill shape, receiving the workload's
+    incoming state): the cumulative decays after the local forward, one All-Scan
+    step in ``blocks`` key blocks, and the output correction. Each is timed on its
+    own (the two small ones as graphs of 20 calls, their host launch cost excluded);
+    the local forward from a zero state is timed beside them."""
+    N = B * H
+    log(f"[zeco] generating B={B} H={H} T={T}")
+    inp = synth.gla_prefill(B=B, H=H, T=T, device="cuda")
+    o, S_loc, gam, ws = m.gla_shard_local(inp["q"], inp["k"], inp["v"], inp["log_g"])
+    S_send = torch.empty_like(S_loc)
+    edges = [int(x) for x in np.linspace(0, D, blocks + 1)]
+
+    def local(i):
+        m.gla_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_g"], None, S_loc, o, ws)
+
+    def decay(i):
+        m.gla_shard_decay(ws, N, T, gam)
+
+    def scan(i):
+        for k0, k1 in zip(edges[:-1], edges[1:]):
+            m.gla_all_scan_step(S_loc, gam[:, -1], inp["S0"], S_send, k0, k1)
+
+    def correct(i):
+        m.gla_shard_output_correct(ws, gam, inp["S0"], o)
+
+    ms_local, _ = timed(local, K, W)
+    ms_decay, _ = timed_graph(decay, K)
+    ms_scan, _ = timed_graph(scan, K)
+    ms_corr, wall = timed(correct, K, W)
+    nc = T // 64
+    # correction: per chunk Q o e^b (bf16) and o in and out, one decay row; the state once per sequence
+    corr_bytes = N * nc * (64 * D * 2 * 3 + D * 4) + N * D * D * 4
+    corr_flops = 2 * N * T * D * D
+    scan_bytes = 3 * N * D * D * 4 + N * D * 4
+    decay_bytes = N * nc * D * 4 + N * (nc + 1) * D * 4
+    res = dict(workload=f"ZeCO per-device steps on a gla_chunk_fwd shard B={B} H={H} T={T} d=128 chunk 64 "
+                        f"(bf16 q/k/v, fp32 gates), incoming state fp32, All-Scan step in {blocks} key blocks",
+               local_fwd_ms=ms_local, decay_ms=ms_decay, all_scan_step_ms=ms_scan, correct_ms=ms_corr,
+               extra_ms=ms_decay + ms_scan + ms_corr, exposed_after_receive_ms=ms_scan + ms_corr,
+               overhead_vs_local=(ms_decay + ms_scan + ms_corr) / ms_local,
+               correct_bytes=corr_bytes, correct_gbs=corr_bytes / (ms_corr * 1e-3) / 1e9,
+               correct_tflops=corr_flops / (ms_corr * 1e-3) / 1e12,
+               decay_gbs=decay_bytes / (ms_decay * 1e-3) / 1e9,
+               all_scan_step_gbs=scan_bytes / (ms_scan * 1e-3) / 1e9, wall_s=wall)
+    res["correct_frac_hbm"] = res["correct_gbs"] / PEAK_HBM_GBS
+    res["roofline_bound"] = "hbm"
+    del inp, ws, o
+    return res
+
+
 def gla_bwd_work(C=64):
     """Algorithmic FLOPs of one chunk of the GLA backward: the forward state recompute
     (V^T K^) and the state-gradient scan (dO^T Q^), then A and dA (lower), dQ^ = dO S_b,
@@ -485,7 +558,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--rows", default="decode,bf16_state,int8_state,kda,leapq,kda_leapq,gla,gla_bwd,gdn,gdn_bwd,"
+    ap.add_argument("--rows", default="decode,bf16_state,int8_state,kda,leapq,kda_leapq,gla,zeco,gla_bwd,gdn,gdn_bwd,"
                                       "kda_chunk")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true",
@@ -552,6 +625,14 @@ def main():
         out_rows["gdn_chunk"] = r
         log(f"[gdn_chunk] {r['ms']*1e3:.1f} us  {r['tflops']:.1f} TFLOP/s ({r['frac_mfma']*100:.1f}% MFMA)  "
             f"{r['achieved_gbs']:.0f} GB/s ({r['frac_hbm']*100:.1f}% HBM)  {r['tokens_per_s']/1e6:.2f} M tok/s")
+        torch.cuda.empty_cache()
+    if "zeco" in rows:
+        r = bench_zeco()
+        r["traffic_bytes_correct_kernel"] = counter_traffic("gla_shard_correct_kernel")
+        out_rows["zeco"] = r
+        log(f"[zeco] local fwd {r['local_fwd_ms']*1e3:.1f} us; decay {r['decay_ms']*1e3:.1f} us, "
+            f"All-Scan step {r['all_scan_step_ms']*1e3:.1f} us, correction {r['correct_ms']*1e3:.1f} us "
+            f"({r['correct_gbs']:.0f} GB/s, {r['correct_frac_hbm']*100:.1f}% HBM)")
         torch.cuda.empty_cache()
     if "gla_bwd" in rows:
         r = bench_gla_bwd()

@@ -83,13 +83,46 @@ __global__ __launch_bounds__(256) void gla_all_scan_step_kernel(const float* S_r
   S_send[e] = s;
 }
 
+namespace zeco {
+
+// One chunk's operands of a correction wave: the four Q^ fragments of its token block
+// and its 32 bytes of o (16 consecutive value channels of one token).
+struct CorrIn {
+  u32x4 qf[4];
+  u32x4 ov[2];
+};
+
+__device__ __forceinline__ void corr_load(CorrIn& in, const uint8_t* __restrict__ ws,
+                                          const uint16_t* __restrict__ o, int n, int nc, int c, int tb,
+                                          int vb0) {
+  const int lane = threadIdx.x & 63, l16 = lane & 15, lq = lane >> 4;
+  const uint8_t* wsc = ws + ((size_t)n * nc + c) * gla::kWChunk + gla::kWQ;
+  const uint16_t* orow = o + (((size_t)n * nc + c) * kChunk + tb * 16 + l16) * kD + 16 * (vb0 + lq);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    in.qf[ks] = *reinterpret_cast<const u32x4*>(wsc + ((size_t)(tb * 4 + ks) * 64 + lane) * 16);
+  in.ov[0] = *reinterpret_cast<const u32x4*>(orow);
+  in.ov[1] = *reinterpret_cast<const u32x4*>(orow + 8);
+}
+
+// Element offset of S[v][k] in the staged state: rows of PQ bf16, the 16-byte groups of
+// rows with bit 4 of v set moved by four groups, so that the eight rows
+// b + {0..3, 16..19} that eight lanes read together fall on distinct bank groups.
+__device__ __forceinline__ int s_off(int v, int k) {
+  return v * PQ + ((k & ~7) ^ (((v >> 4) & 1) << 5)) + (k & 7);
+}
+
+}  // namespace zeco
+
 // o[n][t] += S_in[n] (Q^ o gamma~_[c])_t over the chunks [part * cpb, part * cpb + cpb) of
-// sequence n. The block stages S_in[n] in LDS as bf16 (rows = value channels); wave w
-// forms the transposed output tiles (value blocks 4 (w >> 2) .. + 3, token block w & 3)
-// of each chunk, D[v][t] = sum_k S[v][k] (Q^ o gamma~)[t][k]: the Q^ fragment of the
-// workspace is already the B operand of that product (lane l16 = token, 8 consecutive
-// keys), scaled by the decay of its keys, and the lane's D values are four consecutive
-// value channels of one token, read from and written back to o as 8 bytes.
+// sequence n. The block stages S_in[n] in LDS as bf16; wave w forms four transposed
+// output tiles of each chunk, D[v][t] = sum_k S[v][k] (Q^ o gamma~)[t][k], for the
+// tokens of block tb = w & 3 and the 64 value channels from 16 vb0, vb0 = 4 (w >> 2):
+// the Q^ fragment of the workspace is already the B operand of that product (lane l16 =
+// token, 8 consecutive keys), scaled by the decay of its keys. Row i = 4 lq + r of tile
+// j stands for value channel 16 vb0 + 16 lq + 4 j + r, so that the 16 D values a lane
+// holds over the four tiles are 16 consecutive channels of one token: o is read and
+// written as 32 contiguous bytes per lane.
 __global__ __launch_bounds__(512) void gla_shard_correct_kernel(const uint8_t* __restrict__ ws,
                                                                 const float* __restrict__ gamma,
                                                                 const float* __restrict__ S_in,
@@ -112,59 +145,58 @@ __global__ __launch_bounds__(512) void gla_shard_correct_kernel(const uint8_t* _
       part = bid % nblk;
     }
   }
+  const int tb = wave & 3, vb0 = (wave >> 2) * 4;
+  const int c0 = part * cpb, c1 = min(nc, c0 + cpb);
+  // the first chunk's operands are requested before the state is staged
+  CorrIn in;
+  corr_load(in, ws, o, n, nc, c0, tb, vb0);
   {
     const float* Sn = S_in + (size_t)n * kD * kD;
 #pragma unroll
     for (int h = 0; h < kD * kD / 4 / NT; ++h) {
       const int i = tid + NT * h, r = i >> 5, c = (i & 31) * 4;
       const f32x4 x = *reinterpret_cast<const f32x4*>(Sn + 4 * (size_t)i);
-      *reinterpret_cast<u32x2*>(Ss + r * PQ + c) = u32x2{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
+      *reinterpret_cast<u32x2*>(Ss + s_off(r, c)) = u32x2{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
     }
   }
   lds_barrier();
 
-  const int tb = wave & 3, vb0 = (wave >> 2) * 4;
-  const int c0 = part * cpb, c1 = min(nc, c0 + cpb);
+  // the LDS row each lane reads as the A operand of tile j: value 16 vb0 + 16 (l16 >> 2) + 4 j + (l16 & 3)
+  const int vrow = 16 * vb0 + 16 * (l16 >> 2) + (l16 & 3);
   for (int c = c0; c < c1; ++c) {
     // the state fragments are read from LDS for every chunk rather than held in 64
     // registers across the loop: fewer registers let more blocks share a CU
     asm volatile("" ::: "memory");
-    const uint8_t* wsc = ws + ((size_t)n * nc + c) * gla::kWChunk;
+    if (c > c0) corr_load(in, ws, o, n, nc, c, tb, vb0);
     const float* gr = gamma + ((size_t)n * (nc + 1) + c) * kD;
-    const size_t tok = ((size_t)n * nc + c) * kChunk + tb * 16 + l16;
-    uint16_t* orow = o + tok * kD + 4 * lq;
-    u32x4 qf[4];
-    u32x2 ov[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      qf[ks] = *reinterpret_cast<const u32x4*>(wsc + gla::kWQ + ((size_t)(tb * 4 + ks) * 64 + lane) * 16);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) ov[j] = *reinterpret_cast<const u32x2*>(orow + 16 * (vb0 + j));
+    uint16_t* orow = o + (((size_t)n * nc + c) * kChunk + tb * 16 + l16) * kD + 16 * (vb0 + lq);
     bf16x8 bq[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const f32x4 g0 = *reinterpret_cast<const f32x4*>(gr + 32 * ks + 8 * lq);
       const f32x4 g1 = *reinterpret_cast<const f32x4*>(gr + 32 * ks + 8 * lq + 4);
-      const u32x4 w = qf[ks];
+      const u32x4 w = in.qf[ks];
       const u32x4 r = {pack_bf16(lo_bf(w[0]) * g0[0], hi_bf(w[0]) * g0[1]),
                        pack_bf16(lo_bf(w[1]) * g0[2], hi_bf(w[1]) * g0[3]),
                        pack_bf16(lo_bf(w[2]) * g1[0], hi_bf(w[2]) * g1[1]),
                        pack_bf16(lo_bf(w[3]) * g1[2], hi_bf(w[3]) * g1[3])};
       bq[ks] = __builtin_bit_cast(bf16x8, r);
     }
+    u32x4 out[2];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
         acc = mfma(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                       Ss + (16 * (vb0 + j) + l16) * PQ + 32 * ks + 8 * lq)),
+                       Ss + s_off(vrow + 4 * j, 32 * ks + 8 * lq))),
                    bq[ks], acc);
-      const u32x2 w = ov[j];
-      *reinterpret_cast<u32x2*>(orow + 16 * (vb0 + j)) =
-          u32x2{pack_bf16(lo_bf(w[0]) + acc[0], hi_bf(w[0]) + acc[1]),
-                pack_bf16(lo_bf(w[1]) + acc[2], hi_bf(w[1]) + acc[3])};
+      const unsigned w0 = in.ov[j >> 1][2 * (j & 1)], w1 = in.ov[j >> 1][2 * (j & 1) + 1];
+      out[j >> 1][2 * (j & 1)] = pack_bf16(lo_bf(w0) + acc[0], hi_bf(w0) + acc[1]);
+      out[j >> 1][2 * (j & 1) + 1] = pack_bf16(lo_bf(w1) + acc[2], hi_bf(w1) + acc[3]);
     }
+    *reinterpret_cast<u32x4*>(orow) = out[0];
+    *reinterpret_cast<u32x4*>(orow + 8) = out[1];
   }
 }
 
