@@ -28,7 +28,10 @@ take ZeCO's three forward phases in the page's order (local chunk states and
 cumulative decays from zero, the All-Scan update, outputs from the received
 state); they are pinned by the recurrence over the whole sequence for several
 device and block counts, by the closed form of the cumulative decays and by the
-local states at the chunk boundaries.
+local states at the chunk boundaries. ``zeco_bwd_local_state`` and ``zeco_backward``
+take the backward's phases (local state gradient from zero, the backward All-Scan,
+gradients from the received state gradient); pinned by reverse mode through the
+recurrence over the whole sequence.
 ``gla_recurrent_bwd`` (reverse mode through the recurrence) is pinned by torch
 autograd of a separately written forward, by central differences, by the textbook
 gradients of causal linear attention at zero log-gates, and by ZeCO's chunk-level
@@ -185,6 +188,57 @@ def zeco_forward(q, k, v, log_g, devices, S0=None, chunk=64, blocks=1):
         outs.append(zeco_output(q[:, sl], k[:, sl], v[:, sl], log_g[:, sl], Ss, gam, S_recv, chunk))
         S_recv = S_send
     return np.concatenate(outs, axis=1), S_recv
+
+
+def zeco_bwd_local_state(q, log_g, dO, chunk=64):
+    """Phase 1 of ZeCO's backward on one device (page section "The Backward
+    Algorithm and Gradient Flow"): from dS = 0 at the shard's end, per chunk in
+    reverse, dS <- gamma (on key columns) o dS + (dO^T (Q o Lambda)), Lambda = exp(b)
+    inclusive; the result is the gradient with respect to the state the shard
+    starts from, counting only the shard's own outputs. Returns [N][d_v][d_k]."""
+    q = np.asarray(q, np.float64)
+    lg = np.asarray(log_g, np.float64)
+    dO = np.asarray(dO, np.float64)
+    N, T, dk = q.shape
+    dv = dO.shape[2]
+    dS = np.zeros((N, dv, dk))
+    for n in range(T // chunk - 1, -1, -1):
+        sl = slice(n * chunk, (n + 1) * chunk)
+        b = np.cumsum(lg[:, sl], axis=1)
+        dS = np.exp(b[:, -1])[:, None, :] * dS + np.einsum("ntv,ntk->nvk", dO[:, sl], q[:, sl] * np.exp(b))
+    return dS
+
+
+def zeco_backward(q, k, v, log_g, dO, devices, S0=None, dST=None, chunk=64, blocks=1):
+    """ZeCO's backward over ``devices`` devices, run one after the other here: the
+    forward's All-Scan gives each device the state it starts from; phase 1 gives
+    each device its local dS_[0]; the backward All-Scan passes the state gradient
+    from the last device to the first, each sending gamma~_[N] o dS_recv + dS_[0];
+    each device then forms its gradients from its incoming state and the received
+    state gradient (``gla_recurrent_bwd`` of its shard). Returns (dq, dk, dv, dlog_g,
+    dS0) for the whole sequence."""
+    T = np.asarray(k).shape[1]
+    if T % (devices * chunk):
+        raise ValueError("T must be a multiple of devices * chunk")
+    L = T // devices
+    sls = [slice(p * L, (p + 1) * L) for p in range(devices)]
+    S_in, gam_tot = [], []
+    S = None if S0 is None else np.asarray(S0, np.float64)
+    for sl in sls:
+        Ss, gam = zeco_local(k[:, sl], v[:, sl], log_g[:, sl], chunk)
+        S_in.append(S)
+        gam_tot.append(gam[:, -1])
+        S = zeco_all_scan_step(Ss[:, -1], gam[:, -1], S, blocks)
+    local = [zeco_bwd_local_state(q[:, sl], log_g[:, sl], dO[:, sl], chunk) for sl in sls]
+    dS_recv = [None] * devices
+    d = None if dST is None else np.asarray(dST, np.float64)
+    for p in range(devices - 1, -1, -1):
+        dS_recv[p] = d
+        d = zeco_all_scan_step(local[p], gam_tot[p], d, blocks)
+    grads = [gla_recurrent_bwd(q[:, sl], k[:, sl], v[:, sl], log_g[:, sl], S_in[p], dO[:, sl], dS_recv[p])
+             for p, sl in enumerate(sls)]
+    out = [np.concatenate([g[i] for g in grads], axis=1) for i in range(4)]
+    return (*out, d)
 
 
 def gla_recurrent_bwd(q, k, v, log_g, S0, dO, dST=None, ckpt=64):

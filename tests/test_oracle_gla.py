@@ -263,3 +263,32 @@ def test_zeco_all_scan_step_blocks_and_start_device():
     for blocks in (1, 2, 8):
         np.testing.assert_array_equal(gla.zeco_all_scan_step(S_loc, gam, S_recv, blocks), ref)
     np.testing.assert_array_equal(gla.zeco_all_scan_step(S_loc, gam, None), S_loc)
+
+
+@pytest.mark.parametrize("devices,blocks,zero_ends", [(1, 1, False), (2, 4, False), (3, 2, True), (4, 1, False)])
+def test_zeco_backward_equals_reverse_mode(devices, blocks, zero_ends):
+    """ZeCO's backward over several devices (phase 1 from zero, the backward
+    All-Scan from the last device, gradients from the received state gradient)
+    gives the gradients of the recurrence over the whole sequence."""
+    rng = np.random.default_rng(49)
+    N, C, d = 2, 16, 6
+    T = devices * 2 * C
+    q, k, v, lg = _rand(rng, N, T, d, mu=1.0)
+    S0, dST = (None, None) if zero_ends else rng.standard_normal((2, N, d, d))
+    dO = rng.standard_normal((N, T, d))
+    ref = gla.gla_recurrent_bwd(q, k, v, lg, S0, dO, dST)
+    got = gla.zeco_backward(q, k, v, lg, dO, devices, S0, dST, chunk=C, blocks=blocks)
+    for name, a, b in zip(("dq", "dk", "dv", "dlog_g", "dS0"), got, ref):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-11 * np.abs(b).max(), err_msg=name)
+
+
+def test_zeco_bwd_local_state_is_the_incoming_state_gradient():
+    """Phase 1's dS_[0] is the gradient with respect to S0 when nothing arrives from
+    later tokens (reverse mode with dST = 0), and it does not depend on S0, k or v."""
+    rng = np.random.default_rng(50)
+    N, T, d, C = 2, 64, 6, 16
+    q, k, v, lg = _rand(rng, N, T, d)
+    S0 = rng.standard_normal((N, d, d))
+    dO = rng.standard_normal((N, T, d))
+    *_, dS0 = gla.gla_recurrent_bwd(q, k, v, lg, S0, dO, None)
+    np.testing.assert_allclose(gla.zeco_bwd_local_state(q, lg, dO, C), dS0, rtol=0, atol=1e-12 * np.abs(dS0).max())
