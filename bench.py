@@ -322,7 +322,8 @@ def bench_zeco(K=20, W=3, B=4, H=16, T=4096, blocks=4):
     incoming state): the cumulative decays after the local forward, one All-Scan
     step in ``blocks`` key blocks, and the output correction. Each is timed on its
     own (the two small ones as graphs of 20 calls, their host launch cost excluded);
-    the local forward from a zero state is timed beside them."""
+    the local forward from a zero state is timed beside them, and the backward's
+    phase 1 (the local state gradient) after them."""
     N = B * H
     log(f"[zeco] generating B={B} H={H} T={T}")
     inp = synth.gla_prefill(B=B, H=H, T=T, device="cuda")
@@ -347,6 +348,26 @@ def bench_zeco(K=20, W=3, B=4, H=16, T=4096, blocks=4):
     ms_decay, _ = timed_graph(decay, K)
     ms_scan, _ = timed_graph(scan, K)
     ms_corr, wall = timed(correct, K, W)
+    del ws
+    # backward phase 1: the local state gradient from the shard's own outputs
+    g = torch.Generator(device="cuda").manual_seed(77)
+    dO = torch.randn(inp["q"].shape, generator=g, device="cuda").to(torch.bfloat16)
+    bws = m.gla_chunk_bwd_workspace(N, T)
+    dS_loc = torch.empty_like(S_loc)
+
+    def bwd_state(i):
+        m.gla_shard_bwd_state(inp["q"], inp["k"], inp["log_g"], dO, dS_loc, bws)
+
+    ms_bstate, _ = timed(bwd_state, K, W)
+    gout = (torch.empty_like(inp["q"]), torch.empty_like(inp["k"]), torch.empty_like(inp["v"]),
+            torch.empty_like(inp["log_g"]), torch.empty_like(S_loc))
+    dS_recv = 0.1 * torch.randn(S_loc.shape, generator=g, device="cuda")
+
+    def bwd_grads(i):   # the gradient pass in phase 1's workspace (its preparation reused)
+        m.gla_shard_bwd_grads(inp["q"], inp["k"], inp["v"], inp["log_g"], dO, bws, inp["S0"], dS_recv, gout)
+
+    ms_bgrads, _ = timed(bwd_grads, K, W)
+    del bws, dO, gout
     nc = T // 64
     # correction: per chunk Q o e^b (bf16) and o in and out, one decay row; the state once per sequence
     corr_bytes = N * nc * (64 * D * 2 * 3 + D * 4) + N * D * D * 4
@@ -356,6 +377,7 @@ def bench_zeco(K=20, W=3, B=4, H=16, T=4096, blocks=4):
     res = dict(workload=f"ZeCO per-device steps on a gla_chunk_fwd shard B={B} H={H} T={T} d=128 chunk 64 "
                         f"(bf16 q/k/v, fp32 gates), incoming state fp32, All-Scan step in {blocks} key blocks",
                local_fwd_ms=ms_local, decay_ms=ms_decay, all_scan_step_ms=ms_scan, correct_ms=ms_corr,
+               bwd_local_state_ms=ms_bstate, bwd_grads_reusing_prep_ms=ms_bgrads,
                extra_ms=ms_decay + ms_scan + ms_corr, exposed_after_receive_ms=ms_scan + ms_corr,
                overhead_vs_local=(ms_decay + ms_scan + ms_corr) / ms_local,
                correct_bytes=corr_bytes, correct_gbs=corr_bytes / (ms_corr * 1e-3) / 1e9,
@@ -364,7 +386,7 @@ def bench_zeco(K=20, W=3, B=4, H=16, T=4096, blocks=4):
                all_scan_step_gbs=scan_bytes / (ms_scan * 1e-3) / 1e9, wall_s=wall)
     res["correct_frac_hbm"] = res["correct_gbs"] / PEAK_HBM_GBS
     res["roofline_bound"] = "hbm"
-    del inp, ws, o
+    del inp, o
     return res
 
 
@@ -632,7 +654,9 @@ def main():
         out_rows["zeco"] = r
         log(f"[zeco] local fwd {r['local_fwd_ms']*1e3:.1f} us; decay {r['decay_ms']*1e3:.1f} us, "
             f"All-Scan step {r['all_scan_step_ms']*1e3:.1f} us, correction {r['correct_ms']*1e3:.1f} us "
-            f"({r['correct_gbs']:.0f} GB/s, {r['correct_frac_hbm']*100:.1f}% HBM)")
+            f"({r['correct_gbs']:.0f} GB/s, {r['correct_frac_hbm']*100:.1f}% HBM); "
+            f"backward phase 1 {r['bwd_local_state_ms']*1e3:.1f} us, gradient pass after it "
+            f"{r['bwd_grads_reusing_prep_ms']*1e3:.1f} us")
         torch.cuda.empty_cache()
     if "gla_bwd" in rows:
         r = bench_gla_bwd()

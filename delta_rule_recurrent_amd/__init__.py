@@ -6,7 +6,8 @@ Entry points over the gdnrt HIP library (C ABI in include/gdnrt.h):
 ``leapq_window_flush``, ``kda_decode_step``, ``kda_chunk_fwd``,
 ``kda_leapq_decode_step``, ``kda_leapq_window_flush``, and the per-device calls of ZeCO's
 sequence-parallel GLA forward: ``gla_shard_local`` (``gla_chunk_fwd`` from zero and
-``gla_shard_decay``), ``gla_all_scan_step`` and ``gla_shard_output_correct``. ``synth``
+``gla_shard_decay``), ``gla_all_scan_step`` and ``gla_shard_output_correct``, and its
+backward's phase 1, ``gla_shard_bwd_state`` (then ``gla_shard_bwd_grads``). ``synth``
 draws the seeded synthetic workloads.
 """
 from .binding import (  # noqa: F401
@@ -24,6 +25,8 @@ from .binding import (  # noqa: F401
     gla_chunk_fwd,
     gla_chunk_workspace,
     gla_all_scan_step,
+    gla_shard_bwd_grads,
+    gla_shard_bwd_state,
     gla_shard_decay,
     gla_shard_local,
     gla_shard_output_correct,

@@ -45,6 +45,8 @@ SIGNATURES = {
     "kda_chunk_fwd": ([_vp] * 8 + [_c_int] * 6 + [_vp, ctypes.c_size_t, _vp], _c_int),
     "gla_chunk_bwd": ([_vp] * 12 + [_c_int] * 6 + [_vp, ctypes.c_size_t, _vp], _c_int),
     "gla_chunk_bwd_workspace_bytes": ([_c_int] * 5, ctypes.c_size_t),
+    "gla_shard_bwd_state": ([_vp] * 5 + [_c_int] * 6 + [_vp, ctypes.c_size_t, _vp], _c_int),
+    "gla_shard_bwd_grads": ([_vp] * 12 + [_c_int] * 6 + [_vp, ctypes.c_size_t, _vp], _c_int),
     "gdn_decode_step_bf16_state": ([_vp] * 7 + [_c_int] * 5 + [_vp], _c_int),
     "gdn_decode_step_int_state": ([_vp, _vp, _c_int] + [_vp] * 6 + [_c_int] * 5 + [_vp], _c_int),
     "gdn_chunk_bwd": ([_vp] * 14 + [_c_int] * 6 + [_vp, ctypes.c_size_t, _vp], _c_int),
@@ -306,7 +308,8 @@ def gla_chunk_bwd_workspace(N, T, device="cuda", chunk=CHUNK):
     return torch.empty(max(nb, 16), dtype=torch.uint8, device=device)
 
 
-def gla_chunk_bwd(q, k, v, log_g, dO, S0=None, dST=None, workspace=None, out=None, chunk=CHUNK):
+def gla_chunk_bwd(q, k, v, log_g, dO, S0=None, dST=None, workspace=None, out=None, chunk=CHUNK,
+                  _entry="gla_chunk_bwd"):
     """Gated linear attention chunkwise backward: gradients of
     sum(dO * o) + sum(dST * S_T) for the forward of gla_chunk_fwd.
 
@@ -326,11 +329,38 @@ def gla_chunk_bwd(q, k, v, log_g, dO, S0=None, dST=None, workspace=None, out=Non
     if workspace is None:
         workspace = gla_chunk_bwd_workspace(N, T, q.device, chunk)
     _need(workspace, "workspace", torch.uint8)
-    _check("gla_chunk_bwd", lib().gla_chunk_bwd(
+    _check(_entry, getattr(lib(), _entry)(
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(S0), _ptr(dO), _ptr(dST), _ptr(dq), _ptr(dk),
         _ptr(dv), _ptr(dg), _ptr(dS0), N, T, D, D, chunk, BF16, _ptr(workspace), workspace.numel(),
         _stream()))
     return dq, dk, dv, dg, dS0
+
+
+def gla_shard_bwd_state(q, k, log_g, dO, dS0=None, workspace=None, chunk=CHUNK):
+    """ZeCO's backward phase 1 on one device: the gradient with respect to the
+    shard's incoming state from its own outputs alone (dS = 0 at the shard's end).
+    q, k, dO [N][T][128] bf16; log_g fp32; workspace as for gla_chunk_bwd (allocated
+    here if None). Returns dS0 [N][128][128] fp32."""
+    N, T, _ = q.shape
+    for n_, t_ in (("q", q), ("k", k), ("dO", dO)):
+        _need(t_, n_, torch.bfloat16, (N, T, D))
+    _need(log_g, "log_g", torch.float32, (N, T, D))
+    if dS0 is None:
+        dS0 = torch.empty((N, D, D), dtype=torch.float32, device=q.device)
+    _need(dS0, "dS0", torch.float32, (N, D, D))
+    if workspace is None:
+        workspace = gla_chunk_bwd_workspace(N, T, q.device, chunk)
+    _need(workspace, "workspace", torch.uint8)
+    _check("gla_shard_bwd_state", lib().gla_shard_bwd_state(
+        _ptr(q), _ptr(k), _ptr(log_g), _ptr(dO), _ptr(dS0), N, T, D, D, chunk, BF16, _ptr(workspace),
+        workspace.numel(), _stream()))
+    return dS0
+
+
+def gla_shard_bwd_grads(q, k, v, log_g, dO, workspace, S0=None, dST=None, out=None, chunk=CHUNK):
+    """gla_chunk_bwd in a workspace where gla_shard_bwd_state has just run on the same
+    q, k, log_g (its per-chunk preparation is reused). Returns as gla_chunk_bwd."""
+    return gla_chunk_bwd(q, k, v, log_g, dO, S0, dST, workspace, out, chunk, _entry="gla_shard_bwd_grads")
 
 
 def gdn_chunk_bwd_workspace(N, T, device="cuda", chunk=CHUNK):

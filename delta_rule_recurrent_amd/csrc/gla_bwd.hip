@@ -152,7 +152,8 @@ __global__ __launch_bounds__(256) void gla_bwd_prep_kernel(const uint16_t* __res
 //   forward:  S  <- e^{b_C} o S  + V^T K^     (X = V,  Y = K^)
 //   reverse:  dS <- e^{b_C} o dS + dO^T Q^    (X = dO, Y = Q^);
 // the reverse scan also writes this tile's sum_v dS o S per key channel, S the state
-// after the chunk (the next chunk's stored state, or ST after the last one).
+// after the chunk (the next chunk's stored state, or ST after the last one), unless
+// bnd is null (the state gradient alone is wanted; the forward scan has not run).
 // The next chunk's X and Y are loaded into registers while this one is computed.
 template <bool REV>
 __global__ __launch_bounds__(256) void gla_bwd_scan_kernel(const uint16_t* __restrict__ X,
@@ -190,7 +191,7 @@ __global__ __launch_bounds__(256) void gla_bwd_scan_kernel(const uint16_t* __res
 
   // thread's pieces: X row tid / 4, values 4 (tid % 4) ..; Y 16-byte pieces tid + 256 p
   auto load = [&](int ci, u32x2& xr, u32x4 (&yr)[4], float (&ec)[2], float (&sa)[2][4]) {
-    if constexpr (REV) {
+    if (REV && bnd) {
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -221,7 +222,7 @@ __global__ __launch_bounds__(256) void gla_bwd_scan_kernel(const uint16_t* __res
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) dst[(v0 + 4 * lq + i) * kD + 32 * w + 16 * j + l16] = f32_to_bf16(acc[j][i]);
-    if constexpr (REV) {   // sum over this tile's 16 value rows of dS o S, per key channel
+    if (REV && bnd) {   // sum over this tile's 16 value rows of dS o S, per key channel
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         float x = ((acc[j][0] * sa[j][0] + acc[j][1] * sa[j][1]) + (acc[j][2] * sa[j][2] + acc[j][3] * sa[j][3]));
@@ -419,11 +420,12 @@ extern "C" size_t gla_chunk_bwd_workspace_bytes(int N, int T, int dk, int dv, in
   return (size_t)N * (T / kChunk) * (glab::kChunkB + 8 * kD * 4) + (size_t)N * kD * kD * 4;
 }
 
-extern "C" int gla_chunk_bwd(const void* q, const void* k, const void* v, const float* log_g,
-                             const float* S0, const void* dO, const float* dST, void* dq, void* dk,
-                             void* dv, float* dlog_g, float* dS0, int N, int T, int dk_, int dv_,
-                             int chunk, int io, void* workspace, size_t ws_bytes, void* stream) {
-  const char* fn = "gla_chunk_bwd";
+// prepared: the per-chunk operands are already in the workspace (gla_shard_bwd_state
+// ran on the same q, k, log_g), so the preparation kernel is not launched again
+static int chunk_bwd(const char* fn, bool prepared, const void* q, const void* k, const void* v,
+                     const float* log_g, const float* S0, const void* dO, const float* dST, void* dq,
+                     void* dk, void* dv, float* dlog_g, float* dS0, int N, int T, int dk_, int dv_, int chunk,
+                     int io, void* workspace, size_t ws_bytes, void* stream) {
   if (N < 0 || T < 0) return set_error(GDNRT_ESHAPE, "%s: N=%d T=%d must be >= 0", fn, N, T);
   if (dk_ != kD || dv_ != kD) return set_error(GDNRT_ESHAPE, "%s: d_k=%d d_v=%d, only 128 is supported", fn, dk_, dv_);
   if (chunk != kChunk) return set_error(GDNRT_ESHAPE, "%s: chunk=%d, only 64 is supported", fn, chunk);
@@ -463,7 +465,7 @@ extern "C" int gla_chunk_bwd(const void* q, const void* k, const void* v, const 
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   float* ST = reinterpret_cast<float*>(ws + nchunks * glab::kChunkB);   // recomputed final states
   float* bnd = ST + (size_t)N * kD * kD;                                // per chunk, sum_v dS_a o S_a
-  if (T > 0) {
+  if (T > 0 && !prepared) {
     hipLaunchKernelGGL(gla_bwd_prep_kernel, dim3((unsigned)nchunks), dim3(256), 0, s,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), log_g, ws, T);
     int rc = check_launch(fn);
@@ -480,5 +482,61 @@ extern "C" int gla_chunk_bwd(const void* q, const void* k, const void* v, const 
                        static_cast<uint16_t*>(dq), static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv),
                        dlog_g, T);
   }
+  return check_launch(fn);
+}
+
+extern "C" int gla_chunk_bwd(const void* q, const void* k, const void* v, const float* log_g,
+                             const float* S0, const void* dO, const float* dST, void* dq, void* dk,
+                             void* dv, float* dlog_g, float* dS0, int N, int T, int dk_, int dv_,
+                             int chunk, int io, void* workspace, size_t ws_bytes, void* stream) {
+  return chunk_bwd("gla_chunk_bwd", false, q, k, v, log_g, S0, dO, dST, dq, dk, dv, dlog_g, dS0, N, T, dk_, dv_,
+                   chunk, io, workspace, ws_bytes, stream);
+}
+
+extern "C" int gla_shard_bwd_grads(const void* q, const void* k, const void* v, const float* log_g,
+                                   const float* S0, const void* dO, const float* dST, void* dq, void* dk,
+                                   void* dv, float* dlog_g, float* dS0, int N, int T, int dk_, int dv_,
+                                   int chunk, int io, void* workspace, size_t ws_bytes, void* stream) {
+  return chunk_bwd("gla_shard_bwd_grads", true, q, k, v, log_g, S0, dO, dST, dq, dk, dv, dlog_g, dS0, N, T, dk_,
+                   dv_, chunk, io, workspace, ws_bytes, stream);
+}
+
+extern "C" int gla_shard_bwd_state(const void* q, const void* k, const float* log_g, const void* dO, float* dS0,
+                                   int N, int T, int dk_, int dv_, int chunk, int io, void* workspace,
+                                   size_t ws_bytes, void* stream) {
+  const char* fn = "gla_shard_bwd_state";
+  if (N < 0 || T < 0) return set_error(GDNRT_ESHAPE, "%s: N=%d T=%d must be >= 0", fn, N, T);
+  if (dk_ != kD || dv_ != kD) return set_error(GDNRT_ESHAPE, "%s: d_k=%d d_v=%d, only 128 is supported", fn, dk_, dv_);
+  if (chunk != kChunk) return set_error(GDNRT_ESHAPE, "%s: chunk=%d, only 64 is supported", fn, chunk);
+  if (T % kChunk) return set_error(GDNRT_ESHAPE, "%s: T=%d is not a multiple of 64", fn, T);
+  if (io != GDNRT_BF16) return set_error(GDNRT_EDTYPE, "%s: io must be GDNRT_BF16", fn);
+  if ((size_t)N * (T / kChunk) > 0x7fffffffu) return set_error(GDNRT_ESHAPE, "%s: N=%d T=%d too large", fn, N, T);
+  if (N == 0) return clear_error();
+  if (!dS0 || (T > 0 && (!q || !k || !log_g || !dO || !workspace)))
+    return set_error(GDNRT_EINVAL, "%s: null pointer argument", fn);
+  const size_t nchunks = (size_t)N * (T / kChunk);
+  const size_t need = nchunks * glab::kChunkB;
+  if (ws_bytes < need) return set_error(GDNRT_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
+  if ((T > 0 && (!aligned16(q) || !aligned16(k) || !aligned16(dO) || !aligned16(log_g) || !aligned16(workspace))) ||
+      !aligned4(dS0))
+    return set_error(GDNRT_EALIGN, "%s: q, k, dO, log_g, workspace must be 16-byte aligned", fn);
+  const size_t ntok = (size_t)N * T, nIO = ntok * kD * 2, nG = ntok * kD * 4, nS = (size_t)N * kD * kD * 4;
+  const void* ins[] = {q, k, dO};
+  for (const void* b : ins)
+    if (overlaps(dS0, nS, b, nIO) || overlaps(workspace, need, b, nIO))
+      return set_error(GDNRT_EINVAL, "%s: buffers overlap", fn);
+  if (overlaps(dS0, nS, log_g, nG) || overlaps(dS0, nS, workspace, need) || overlaps(workspace, need, log_g, nG))
+    return set_error(GDNRT_EINVAL, "%s: buffers overlap", fn);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  if (T > 0) {
+    hipLaunchKernelGGL(gla_bwd_prep_kernel, dim3((unsigned)nchunks), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), log_g, ws, T);
+    int rc = check_launch(fn);
+    if (rc != GDNRT_OK) return rc;
+  }
+  // the reverse scan from a zero gradient, without the boundary sums (no forward states)
+  hipLaunchKernelGGL(gla_bwd_scan_kernel<true>, dim3((unsigned)(N * 8)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(dO), ws, nullptr, dS0, nullptr, nullptr, T);
   return check_launch(fn);
 }

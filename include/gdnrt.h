@@ -193,6 +193,37 @@ GDNRT_API int gla_chunk_bwd(const void* q, const void* k, const void* v, const f
 GDNRT_API size_t gla_chunk_bwd_workspace_bytes(int N, int T, int dk, int dv, int chunk);
 
 /*
+ * ZeCO's backward on one device of a sequence-parallel GLA run ("ZeCO: Zero
+ * Communication Overhead Sequence Parallelism for Linear Attention", section "The
+ * Backward Algorithm and Gradient Flow"), phase 1: the gradient with respect to the
+ * state the shard starts from, counting only the shard's own outputs,
+ *     dS <- gamma o dS + dO^T (Q o e^b)   over the chunks in reverse, from dS = 0,
+ * written to dS0 [N][dv][dk] fp32. With it a device:
+ *   1. gla_shard_bwd_state: its local dS_[0];
+ *   2. gla_all_scan_step(S_recv = the state gradient received from the next device,
+ *      gamma = the shard's total decay, S_local = dS_[0]): the state gradient to send
+ *      to the previous device (the backward All-Scan, block by block along d_k);
+ *   3. gla_chunk_bwd (or gla_shard_bwd_grads, which reuses step 1's workspace) from
+ *      the shard's incoming state with dST = the received state gradient: every
+ *      gradient of the shard (its dS0 equals what step 2 sent).
+ * q, k, dO [N][T][128] bf16, log_g fp32, 16-byte aligned (k is read by the shared
+ * per-chunk preparation). workspace: at least N * (T/chunk) * 132,608 bytes (e.g. the
+ * gla_chunk_bwd workspace), 16-byte aligned, overwritten; may be NULL when T = 0.
+ */
+GDNRT_API int gla_shard_bwd_state(const void* q, const void* k, const float* log_g, const void* dO,
+                        float* dS0, int N, int T, int dk, int dv, int chunk, int io,
+                        void* workspace, size_t ws_bytes, void* stream);
+
+/* Step 3 above without repeating the per-chunk preparation: gla_chunk_bwd (same
+ * arguments and results) for a workspace of gla_chunk_bwd_workspace_bytes() bytes in
+ * which gla_shard_bwd_state has just run on the same q, k, log_g, N, T (and that
+ * nothing has used since). */
+GDNRT_API int gla_shard_bwd_grads(const void* q, const void* k, const void* v, const float* log_g,
+                        const float* S0, const void* dO, const float* dST, void* dq, void* dk,
+                        void* dv, float* dlog_g, float* dS0, int N, int T, int dk_, int dv_,
+                        int chunk, int io, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * Gated DeltaNet chunkwise forward (prefill): the same recurrence as
  * gdn_decode_step over T tokens, computed per chunk of 64 tokens through the
  * UT / WY form of the intra-chunk delta rule (derived from eq. 3 of the LeapQuant

@@ -38,7 +38,7 @@ def test_header_declares_the_entry_points():
               "gla_chunk_bwd", "gla_chunk_bwd_workspace_bytes", "gdn_chunk_bwd",
               "gdn_chunk_bwd_workspace_bytes", "gdn_decode_step_bf16_state",
               "gdn_decode_step_int_state", "gla_shard_decay", "gla_all_scan_step",
-              "gla_shard_output_correct"):
+              "gla_shard_output_correct", "gla_shard_bwd_state", "gla_shard_bwd_grads"):
         assert n in names, n
 
 
@@ -230,3 +230,18 @@ def test_gla_shard_validation(lib):
     assert f(a, ws_need, g, b, ctypes.c_void_p((1 << 30) + 1024), 2, 128, 128, 128, 64, 1, None) == EINVAL
     assert f(a, ws_need, g, b, c, 2, 100, 128, 128, 64, 1, None) == ESHAPE
     assert "gla_shard_output_correct" in _err(lib)
+
+
+def test_gla_shard_bwd_state_validation(lib):
+    p = ctypes.c_void_p(4096)
+    f = lib.gla_shard_bwd_state
+    q, k, g, dO, dS0, ws = (ctypes.c_void_p(x << 30) for x in (1, 2, 3, 4, 5, 6))
+    need = 2 * 2 * 132608
+    assert f(q, k, g, dO, dS0, 2, 128, 128, 128, 64, 1, ws, need - 1, None) == EINVAL
+    assert "gla_shard_bwd_state" in _err(lib)
+    assert f(q, k, g, dO, dS0, 2, 96, 128, 128, 64, 1, ws, need, None) == ESHAPE
+    assert f(q, k, g, dO, dS0, 2, 128, 128, 128, 64, 0, ws, need, None) == EDTYPE
+    assert f(q, ctypes.c_void_p((2 << 30) + 8), g, dO, dS0, 2, 128, 128, 128, 64, 1, ws, need, None) == EALIGN
+    assert f(q, k, g, dO, None, 2, 128, 128, 128, 64, 1, ws, need, None) == EINVAL
+    assert f(q, k, g, dO, ctypes.c_void_p((1 << 30) + 4096), 2, 128, 128, 128, 64, 1, ws, need, None) == EINVAL
+    assert f(q, k, g, dO, dS0, 0, 128, 128, 128, 64, 1, ws, need, None) == OK

@@ -1,7 +1,8 @@
 """GPU parity of the per-device calls of ZeCO's sequence-parallel GLA forward
-(gla_shard_decay, gla_all_scan_step, gla_shard_output_correct) against the fp64
-oracle of ZeCO's three phases and against the per-token recurrence over the whole
-sequence.
+(gla_shard_decay, gla_all_scan_step, gla_shard_output_correct) and backward
+(gla_shard_bwd_state, the All-Scan step run backward, gla_chunk_bwd from the
+received state gradient) against the fp64 oracle of ZeCO's phases and against the
+per-token recurrence (and reverse mode through it) over the whole sequence.
 
 The devices of a sequence-parallel run are played one after the other on the one
 GPU: every device runs its shard's forward from a zero state and its cumulative
@@ -164,3 +165,86 @@ def test_empty_and_no_incoming_state():
     m.gla_shard_output_correct(ws, gam, None, o)
     torch.cuda.synchronize()
     assert torch.equal(o, before)
+
+
+# ------------------------------------------------------------------ backward
+
+def _bwd_chain(g, dO, dST, devices, blocks, S0):
+    """The backward over the devices played in turn: the forward chain for each
+    device's incoming state, phase 1 on every device, the backward All-Scan from
+    the last device, then each device's gradients from its incoming state and the
+    state gradient it received. Returns the concatenated gradients, the state
+    gradient the first device sends, and each device's (dS0 of its gradient pass,
+    state gradient it sent)."""
+    N, T, _ = g["q"].shape
+    L = T // devices
+    _, _, local, sent = _chain(g, devices, blocks, S0)
+    S_in = [S0] + sent[:-1]
+    sls = [slice(p * L, (p + 1) * L) for p in range(devices)]
+    sh = [{n: g[n][:, sl].contiguous() for n in ("q", "k", "v", "log_g")} for sl in sls]
+    dOs = [dO[:, sl].contiguous() for sl in sls]
+    wss = [m.gla_chunk_bwd_workspace(N, L) for _ in range(devices)]
+    dS_loc = [m.gla_shard_bwd_state(x["q"], x["k"], x["log_g"], d, workspace=w) for x, d, w in zip(sh, dOs, wss)]
+    e = _edges(blocks)
+    recv, send, d = [None] * devices, [None] * devices, dST
+    for p in range(devices - 1, -1, -1):
+        recv[p] = d
+        out = torch.empty_like(dS_loc[p])
+        for k0, k1 in zip(e[:-1], e[1:]):
+            m.gla_all_scan_step(dS_loc[p], local[p][2][:, -1], d, out, k0, k1)
+        send[p] = d = out
+    grads = [m.gla_shard_bwd_grads(x["q"], x["k"], x["v"], x["log_g"], dOs[p], wss[p], S0=S_in[p], dST=recv[p])
+             for p, x in enumerate(sh)]
+    cat = [torch.cat([gr[i] for gr in grads], 1) for i in range(4)]
+    return cat, d, [(gr[4], send[p]) for p, gr in enumerate(grads)]
+
+
+@pytest.mark.parametrize("N,devices,L,blocks,zero_ends", [(3, 3, 128, 4, False), (8, 2, 192, 2, False),
+                                                        (2, 4, 64, 1, True)])
+def test_backward_chain_small(N, devices, L, blocks, zero_ends):
+    """ZeCO's backward with the devices played in turn against reverse mode through
+    the recurrence over the whole sequence; each device's gradient pass reproduces
+    the state gradient its backward All-Scan step sent."""
+    dev = need_gpu()
+    say(f"zeco backward chain: N={N} devices={devices} L={L} blocks={blocks} zero_ends={zero_ends}")
+    inp = synth.gla_prefill(B=N, H=1, T=devices * L, device="cpu", seed=740 + N)
+    gen = torch.Generator().manual_seed(741 + N)
+    dO = torch.randn((N, devices * L, D), generator=gen).to(torch.bfloat16)
+    dST = 0.1 * torch.randn((N, D, D), generator=gen)
+    g = {k_: t.to(dev) for k_, t in inp.items()}
+    S0, dST_d = (None, None) if zero_ends else (g["S0"], dST.to(dev))
+    cat, dS0, per = _bwd_chain(g, dO.to(dev), dST_d, devices, blocks, S0)
+    torch.cuda.synchronize()
+    f = {k_: np64(t) for k_, t in inp.items()}
+    ref = gla.gla_recurrent_bwd(f["q"], f["k"], f["v"], f["log_g"], None if zero_ends else f["S0"], np64(dO),
+                                None if zero_ends else np64(dST))
+    errs = [assert_rel(np64(a), r, TOL, n) for a, r, n in zip(cat + [dS0], ref, ("dq", "dk", "dv", "dlog_g", "dS0"))]
+    for p, (from_pass, sent) in enumerate(per):
+        assert_rel(np64(from_pass), np64(sent), TOL, f"device {p}: gradient pass dS0 vs All-Scan send")
+    say("  " + " ".join(f"{n} {e_:.1e}" for n, e_ in zip(("dq", "dk", "dv", "dg", "dS0"), errs)))
+
+
+def test_bwd_state_against_oracle_at_shard_shape():
+    """Phase 1 at the prefill shard's shape (64 x 4096 tokens) against the oracle's
+    chunk recurrence on 4 sampled sequences, and against the dS0 of gla_chunk_bwd
+    from the same incoming state with no state gradient arriving; the gradient pass
+    in phase 1's workspace gives the same bits as gla_chunk_bwd."""
+    dev = need_gpu()
+    say("zeco bwd phase 1: B=4 H=16 T=4096")
+    inp = synth.gla_prefill(device=dev)
+    gen = torch.Generator(device=dev).manual_seed(77)
+    dO = torch.randn(inp["q"].shape, generator=gen, device=dev).to(torch.bfloat16)
+    ws = m.gla_chunk_bwd_workspace(64, 4096)
+    dS_loc = m.gla_shard_bwd_state(inp["q"], inp["k"], inp["log_g"], dO, workspace=ws)
+    dST = 0.1 * torch.randn(inp["S0"].shape, generator=gen, device=dev)
+    reused = m.gla_shard_bwd_grads(inp["q"], inp["k"], inp["v"], inp["log_g"], dO, ws, S0=inp["S0"], dST=dST)
+    full = m.gla_chunk_bwd(inp["q"], inp["k"], inp["v"], inp["log_g"], dO, S0=inp["S0"], dST=dST)
+    *_, dS0 = m.gla_chunk_bwd(inp["q"], inp["k"], inp["v"], inp["log_g"], dO, S0=inp["S0"])
+    torch.cuda.synchronize()
+    for a, b, name in zip(reused, full, ("dq", "dk", "dv", "dlog_g", "dS0")):
+        assert torch.equal(a, b), f"gla_shard_bwd_grads {name} differs from gla_chunk_bwd"
+    e0 = assert_rel(np64(dS_loc), np64(dS0), TOL, "phase 1 vs gradient pass")
+    idx = torch.tensor([0, 21, 42, 63])
+    ref = gla.zeco_bwd_local_state(np64(inp["q"][idx]), np64(inp["log_g"][idx]), np64(dO[idx]))
+    e1 = assert_rel(np64(dS_loc[idx]), ref, TOL, "phase 1 vs oracle")
+    say(f"  vs gradient pass {e0:.1e}  vs oracle {e1:.1e}")
