@@ -57,6 +57,20 @@ def timed(fn, K, W):
     return e0.elapsed_time(e1) / K, time.perf_counter() - t0
 
 
+def per_step_median(fn, n=64, start=0):
+    """Median over n consecutive calls of fn, each between its own pair of events on
+    the current stream (the calls still run back to back)."""
+    s = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    ev[0].record(s)
+    for i in range(n):
+        fn(start + i)
+        ev[i + 1].record(s)
+    torch.cuda.synchronize()
+    ts = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(n))
+    return ts[n // 2]
+
+
 def timed_graph(fn, K, reps=20):
     """GPU time per call of a launch-bound call: ``reps`` calls captured in one HIP
     graph, the graph replayed K times between events (the host's launch cost per call
@@ -103,10 +117,11 @@ def bench_decode(K, W, gen_steps=256):
                           a[t, :, None], b[t, :, None], o)
 
     ms, wall = timed(step, K, W)
+    med = per_step_median(step, 64, W + K)
     bytes_launch = decode_bytes_per_head_step() * N
     gbs = bytes_launch / (ms * 1e-3) / 1e9
     return dict(workload=DECODE_WORKLOAD,
-                ms_per_step=ms, tokens_per_s=B / (ms * 1e-3), head_steps=N,
+                ms_per_step=ms, ms_per_step_median_of_64=med, tokens_per_s=B / (ms * 1e-3), head_steps=N,
                 bytes_per_launch=bytes_launch, achieved_gbs=gbs, frac_hbm=gbs / PEAK_HBM_GBS,
                 wall_s=wall), inp
 
