@@ -153,9 +153,9 @@ __global__ __launch_bounds__(256) void gla_bwd_prep_kernel(const uint16_t* __res
 //   reverse:  dS <- e^{b_C} o dS + dO^T Q^    (X = dO, Y = Q^);
 // the reverse scan also writes this tile's sum_v dS o S per key channel, S the state
 // after the chunk (the next chunk's stored state, or ST after the last one), unless
-// bnd is null (the state gradient alone is wanted; the forward scan has not run).
+// BND is false (the state gradient alone is wanted; the forward scan has not run).
 // The next chunk's X and Y are loaded into registers while this one is computed.
-template <bool REV>
+template <bool REV, bool BND = REV>
 __global__ __launch_bounds__(256) void gla_bwd_scan_kernel(const uint16_t* __restrict__ X,
                                                            uint8_t* __restrict__ ws,
                                                            const float* __restrict__ Sinit,
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(256) void gla_bwd_scan_kernel(const uint16_t* __res
 
   // thread's pieces: X row tid / 4, values 4 (tid % 4) ..; Y 16-byte pieces tid + 256 p
   auto load = [&](int ci, u32x2& xr, u32x4 (&yr)[4], float (&ec)[2], float (&sa)[2][4]) {
-    if (REV && bnd) {
+    if constexpr (BND) {
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(256) void gla_bwd_scan_kernel(const uint16_t* __res
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) dst[(v0 + 4 * lq + i) * kD + 32 * w + 16 * j + l16] = f32_to_bf16(acc[j][i]);
-    if (REV && bnd) {   // sum over this tile's 16 value rows of dS o S, per key channel
+    if constexpr (BND) {   // sum over this tile's 16 value rows of dS o S, per key channel
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         float x = ((acc[j][0] * sa[j][0] + acc[j][1] * sa[j][1]) + (acc[j][2] * sa[j][2] + acc[j][3] * sa[j][3]));
@@ -536,7 +536,7 @@ extern "C" int gla_shard_bwd_state(const void* q, const void* k, const float* lo
     if (rc != GDNRT_OK) return rc;
   }
   // the reverse scan from a zero gradient, without the boundary sums (no forward states)
-  hipLaunchKernelGGL(gla_bwd_scan_kernel<true>, dim3((unsigned)(N * 8)), dim3(256), 0, s,
+  hipLaunchKernelGGL((gla_bwd_scan_kernel<true, false>), dim3((unsigned)(N * 8)), dim3(256), 0, s,
                      static_cast<const uint16_t*>(dO), ws, nullptr, dS0, nullptr, nullptr, T);
   return check_launch(fn);
 }
