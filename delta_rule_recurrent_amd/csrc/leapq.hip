@@ -136,12 +136,15 @@ __global__ __launch_bounds__(256) void leapq_decode_kernel(
 
   // ---- independent loads
   // code rows of this wave's tiles as MFMA B operands: row 32 w + 16 T + n, bytes 64 s + 16 g
+  // (non-temporal: the codes of all heads do not fit the caches between two steps, and
+  // keeping them out leaves room for the buffered records, which every step re-reads)
   i32x4 zb[2][2];
 #pragma unroll
   for (int T = 0; T < 2; ++T)
 #pragma unroll
     for (int s = 0; s < 2; ++s)
-      zb[T][s] = *reinterpret_cast<const i32x4*>(codes + (hk + row[T]) * kD + 64 * s + 16 * g);
+      zb[T][s] = __builtin_nontemporal_load(
+          reinterpret_cast<const i32x4*>(codes + (hk + row[T]) * kD + 64 * s + 16 * g));
   // buffered corrections and compensator values of this lane's rows, slots = g (mod 4)
   float bur[2][kMaxWindow / 4], cur[2][kMaxRank / 4], vrow[2], vsr[2];
 #pragma unroll
