@@ -15,11 +15,14 @@
 // Mapping: every lane holds 16 bytes of its row (8 bf16 entries, or 16 codes), so a
 // row is 16 (bf16) or 8 (codes) consecutive lanes and one wave instruction moves 1 KiB
 // of state, as in the fp32 decode kernel; a 256-thread block owns 16 (bf16) or 32
-// (codes) rows of one head. Over T tokens in one launch the row stays in registers
+// (codes) rows of one head. The state is streamed with non-temporal loads and stores
+// (it is read and written once per step and does not fit the caches). Over T tokens in one launch the row stays in registers
 // and is rounded after every token exactly as a launch per token would.
 #include "common.hpp"
 
 namespace gdnrt {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 // reductions over an aligned group of L = 16 or 8 lanes (DPP inside 16-lane rows)
 template <int L>
@@ -71,16 +74,16 @@ __global__ __launch_bounds__(256) void gdn_decode_lowp_kernel(
   float s[E];
   float m = 0.f;
   if constexpr (BF16STATE) {
-    const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(Sv) + e0);
-    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+    const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(Sv) + e0));
+    const uint32_t ww[4] = {w[0], w[1], w[2], w[3]};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       s[2 * j] = __uint_as_float(ww[j] << 16);
       s[2 * j + 1] = __uint_as_float(ww[j] & 0xffff0000u);
     }
   } else {
-    const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const int8_t*>(Sv) + e0);
-    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+    const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const int8_t*>(Sv) + e0));
+    const uint32_t ww[4] = {w[0], w[1], w[2], w[3]};
     m = rowmax[r0];
     const float sv = m * qinv;
 #pragma unroll
@@ -131,10 +134,11 @@ __global__ __launch_bounds__(256) void gdn_decode_lowp_kernel(
     }
   }
   if constexpr (BF16STATE) {
-    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(Sv) + e0) =
-        make_uint4(pack_bf16(s[0], s[1]), pack_bf16(s[2], s[3]), pack_bf16(s[4], s[5]), pack_bf16(s[6], s[7]));
+    __builtin_nontemporal_store(u32x4{pack_bf16(s[0], s[1]), pack_bf16(s[2], s[3]), pack_bf16(s[4], s[5]),
+                                      pack_bf16(s[6], s[7])},
+                                reinterpret_cast<u32x4*>(static_cast<uint16_t*>(Sv) + e0));
   } else if (T > 0) {
-    *reinterpret_cast<uint4*>(static_cast<int8_t*>(Sv) + e0) = make_uint4(zw[0], zw[1], zw[2], zw[3]);
+    __builtin_nontemporal_store(u32x4{zw[0], zw[1], zw[2], zw[3]}, reinterpret_cast<u32x4*>(static_cast<int8_t*>(Sv) + e0));
     if (lead) rowmax[r0] = m;
   }
 }
