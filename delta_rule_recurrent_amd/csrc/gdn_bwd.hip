@@ -48,6 +48,7 @@ constexpr int C = kChunk;    // 64
 constexpr int PT = kD + 16;  // bf16 pitch of 128-wide rows
 constexpr int PA = C + 16;   // bf16 pitch of 64-wide rows
 constexpr int PX = 16 + 16;  // bf16 pitch of 16-wide rows
+constexpr int PF = kD + 4;   // fp32 pitch of 128-wide rows
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -163,17 +164,14 @@ __global__ __launch_bounds__(256) void gdn_bwd_fscan_kernel(const uint8_t* __res
   for (int s = 0; s < nc; ++s) {
     cur = nxt;
     if (s + 1 < nc) load(chunk0 + s + 1, nxt);
-    uint16_t* dst = Sb + (chunk0 + s) * kD * kD;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint16_t b = f32_to_bf16(acc[j][i]);
-        const int r = 4 * lq + i, c = 32 * w + 16 * j + l16;
-        dst[(size_t)(v0 + r) * kD + c] = b;
-        sS[r * PT + c] = b;
-      }
+      for (int i = 0; i < 4; ++i) sS[(4 * lq + i) * PT + 32 * w + 16 * j + l16] = f32_to_bf16(acc[j][i]);
     lds_barrier();
+    // the tile's bf16 copy to the workspace: row tid / 16, 8 columns per thread
+    *reinterpret_cast<u32x4*>(Sb + (chunk0 + s) * kD * kD + (size_t)(v0 + (tid >> 4)) * kD + 8 * (tid & 15)) =
+        *reinterpret_cast<const u32x4*>(sS + (tid >> 4) * PT + 8 * (tid & 15));
     f32x4 p = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) p = mfma(as_bf(cur.w[ks]), ld8_split(sS + l16 * PT + 32 * ks + 4 * lq), p);
@@ -218,11 +216,13 @@ __global__ __launch_bounds__(256) void gdn_bwd_rscan_kernel(const uint8_t* __res
   __shared__ __attribute__((aligned(16))) uint16_t sW[C * PT];
   __shared__ __attribute__((aligned(16))) uint16_t sO[C * PX];
   __shared__ __attribute__((aligned(16))) uint16_t sdU[16 * PA];
+  __shared__ __attribute__((aligned(16))) float sA[16 * PF];   // the state after the chunk, this tile
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, lq = lane >> 4;
   int n, vt;
   seq_tile(n, vt);
   const int v0 = 16 * vt, nc = T / C;
   const size_t chunk0 = (size_t)n * nc;
+  const int tr = tid >> 4, tc = 8 * (tid & 15);   // a thread's 8 entries of a [16][128] tile
   f32x4 acc[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
@@ -233,18 +233,22 @@ __global__ __launch_bounds__(256) void gdn_bwd_rscan_kernel(const uint8_t* __res
     u32x4 kh[4], qp[4], w[4];
     u32x2 o;
     float gc;
-    float sa[2][4];   // this lane's entries of the state after the chunk
+    f32x4 sa[2];   // this thread's 8 entries (row tr, columns tc ..) of the state after the chunk
   };
   // fragment f = w + 4 p of each 16-fragment operand, this lane's 16 bytes
   auto load = [&](int ci, Ops& o) {
     const uint8_t* pc = prep + (chunk0 + ci) * kWsChunk;
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const size_t e = (size_t)(v0 + 4 * lq + i) * kD + 32 * w + 16 * j + l16;
-        o.sa[j][i] = ci + 1 < nc ? bf16_to_f32(Sb[(chunk0 + ci + 1) * kD * kD + e]) : ST[(size_t)n * kD * kD + e];
+    {
+      const size_t e = (size_t)(v0 + tr) * kD + tc;
+      if (ci + 1 < nc) {
+        const u32x4 b = *reinterpret_cast<const u32x4*>(Sb + (chunk0 + ci + 1) * kD * kD + e);
+        o.sa[0] = f32x4{lo_bf(b.x), hi_bf(b.x), lo_bf(b.y), hi_bf(b.y)};
+        o.sa[1] = f32x4{lo_bf(b.z), hi_bf(b.z), lo_bf(b.w), hi_bf(b.w)};
+      } else {
+        o.sa[0] = *reinterpret_cast<const f32x4*>(ST + (size_t)n * kD * kD + e);
+        o.sa[1] = *reinterpret_cast<const f32x4*>(ST + (size_t)n * kD * kD + e + 4);
       }
+    }
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const size_t off = ((size_t)(w + 4 * p) * 64 + lane) * 16;
@@ -261,20 +265,12 @@ __global__ __launch_bounds__(256) void gdn_bwd_rscan_kernel(const uint8_t* __res
     const int ci = nc - 1 - s;
     cur = nxt;
     if (s + 1 < nc) load(ci - 1, nxt);
-    uint16_t* dst = dSa + (chunk0 + ci) * kD * kD;
-    float part = 0.f;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint16_t b = f32_to_bf16(acc[j][i]);
-        const int r = 4 * lq + i, c = 32 * w + 16 * j + l16;
-        dst[(size_t)(v0 + r) * kD + c] = b;
-        sD[r * PT + c] = b;
-        part += acc[j][i] * cur.sa[j][i];
-      }
-    part = sum64(part);
-    if (lane == 0) bnd[(chunk0 + ci) * 32 + 4 * vt + w] = part;
+      for (int i = 0; i < 4; ++i) sD[(4 * lq + i) * PT + 32 * w + 16 * j + l16] = f32_to_bf16(acc[j][i]);
+    *reinterpret_cast<f32x4*>(sA + tr * PF + tc) = cur.sa[0];
+    *reinterpret_cast<f32x4*>(sA + tr * PF + tc + 4) = cur.sa[1];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int f = w + 4 * p;
@@ -289,6 +285,19 @@ __global__ __launch_bounds__(256) void gdn_bwd_rscan_kernel(const uint8_t* __res
     }
     *reinterpret_cast<u32x2*>(sO + (tid >> 2) * PX + 4 * (tid & 3)) = cur.o;
     lds_barrier();
+    // the tile's bf16 copy to the workspace, one 16-byte store per thread; this tile's
+    // part of sum(dS o S) from the fp32 accumulators and the staged state after the chunk
+    *reinterpret_cast<u32x4*>(dSa + (chunk0 + ci) * kD * kD + (size_t)(v0 + tr) * kD + tc) =
+        *reinterpret_cast<const u32x4*>(sD + tr * PT + tc);
+    {
+      float part = 0.f;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part += acc[j][i] * sA[(4 * lq + i) * PF + 32 * w + 16 * j + l16];
+      part = sum64(part);
+      if (lane == 0) bnd[(chunk0 + ci) * 32 + 4 * vt + w] = part;
+    }
     // -(K^ dS^T)^T for tokens 16 w .. 16 w + 15: [v][t]
     f32x4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
