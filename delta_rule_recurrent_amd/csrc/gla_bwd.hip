@@ -165,7 +165,10 @@ __global__ __launch_bounds__(256) void gla_bwd_scan_kernel(const uint16_t* __res
   using namespace glab;
   __shared__ __attribute__((aligned(16))) uint16_t sx[C * PX];
   __shared__ __attribute__((aligned(16))) uint16_t sy[C * PT];
+  __shared__ __attribute__((aligned(16))) uint16_t sst[16 * PT];              // the tile in bf16
+  __shared__ __attribute__((aligned(16))) float ssa[BND ? 16 * (kD + 4) : 4];  // the state after the chunk
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, lq = lane >> 4;
+  const int tr = tid >> 4, tc = 8 * (tid & 15);   // a thread's 8 entries of a [16][128] tile
   // block -> (sequence, value tile); the 8 tiles of one sequence share an XCD (blocks
   // are dealt to the 8 XCDs round robin), so the scaled keys or queries they all read
   // are fetched into that XCD's L2 once
@@ -190,17 +193,19 @@ __global__ __launch_bounds__(256) void gla_bwd_scan_kernel(const uint16_t* __res
       acc[j][i] = Sinit ? Sinit[((size_t)n * kD + v0 + 4 * lq + i) * kD + 32 * w + 16 * j + l16] : 0.f;
 
   // thread's pieces: X row tid / 4, values 4 (tid % 4) ..; Y 16-byte pieces tid + 256 p
-  auto load = [&](int ci, u32x2& xr, u32x4 (&yr)[4], float (&ec)[2], float (&sa)[2][4]) {
+  // sa: this thread's 8 entries (row tr, columns tc ..) of the state after the chunk
+  auto load = [&](int ci, u32x2& xr, u32x4 (&yr)[4], float (&ec)[2], f32x4 (&sa)[2]) {
     if constexpr (BND) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const size_t e = (size_t)(v0 + 4 * lq + i) * kD + 32 * w + 16 * j + l16;
-          sa[j][i] = ci + 1 < nc
-                         ? bf16_to_f32(reinterpret_cast<const uint16_t*>(ws + (chunk0 + ci + 1) * kChunkB + kSb)[e])
-                         : ST[(size_t)n * kD * kD + e];
-        }
+      const size_t e = (size_t)(v0 + tr) * kD + tc;
+      if (ci + 1 < nc) {
+        const u32x4 b = *reinterpret_cast<const u32x4*>(
+            reinterpret_cast<const uint16_t*>(ws + (chunk0 + ci + 1) * kChunkB + kSb) + e);
+        sa[0] = f32x4{__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xffff0000u), __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xffff0000u)};
+        sa[1] = f32x4{__uint_as_float(b.z << 16), __uint_as_float(b.z & 0xffff0000u), __uint_as_float(b.w << 16), __uint_as_float(b.w & 0xffff0000u)};
+      } else {
+        sa[0] = *reinterpret_cast<const f32x4*>(ST + (size_t)n * kD * kD + e);
+        sa[1] = *reinterpret_cast<const f32x4*>(ST + (size_t)n * kD * kD + e + 4);
+      }
     }
     const size_t tok = (size_t)n * T + (size_t)ci * C;
     xr = *reinterpret_cast<const u32x2*>(X + (tok + (tid >> 2)) * kD + v0 + 4 * (tid & 3));
@@ -212,24 +217,20 @@ __global__ __launch_bounds__(256) void gla_bwd_scan_kernel(const uint16_t* __res
   };
   u32x2 xr;
   u32x4 yr[4];
-  float ec[2], sa[2][4];
+  float ec[2];
+  f32x4 sa[2];
   if (nc > 0) load(REV ? nc - 1 : 0, xr, yr, ec, sa);
   for (int s = 0; s < nc; ++s) {
     const int ci = REV ? nc - 1 - s : s;
-    // this chunk's state (forward) or state gradient (reverse), in bf16
-    uint16_t* dst = reinterpret_cast<uint16_t*>(ws + (chunk0 + ci) * kChunkB + (REV ? kdS : kSb));
+    // this chunk's state (forward) or state gradient (reverse) in bf16, staged in LDS
+    // and stored after the barrier one 16-byte piece per thread
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[(v0 + 4 * lq + i) * kD + 32 * w + 16 * j + l16] = f32_to_bf16(acc[j][i]);
-    if constexpr (BND) {   // sum over this tile's 16 value rows of dS o S, per key channel
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        float x = ((acc[j][0] * sa[j][0] + acc[j][1] * sa[j][1]) + (acc[j][2] * sa[j][2] + acc[j][3] * sa[j][3]));
-        x += __shfl_xor(x, 16);
-        x += __shfl_xor(x, 32);
-        if (lq == 0) bnd[((chunk0 + ci) * 8 + vt) * kD + 32 * w + 16 * j + l16] = x;
-      }
+      for (int i = 0; i < 4; ++i) sst[(4 * lq + i) * PT + 32 * w + 16 * j + l16] = f32_to_bf16(acc[j][i]);
+    if constexpr (BND) {
+      *reinterpret_cast<f32x4*>(ssa + tr * (kD + 4) + tc) = sa[0];
+      *reinterpret_cast<f32x4*>(ssa + tr * (kD + 4) + tc + 4) = sa[1];
     }
     *reinterpret_cast<u32x2*>(sx + (tid >> 2) * PX + 4 * (tid & 3)) = xr;
 #pragma unroll
@@ -240,6 +241,18 @@ __global__ __launch_bounds__(256) void gla_bwd_scan_kernel(const uint16_t* __res
     const float e0 = ec[0], e1 = ec[1];
     if (s + 1 < nc) load(REV ? ci - 1 : ci + 1, xr, yr, ec, sa);
     lds_barrier();
+    *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(ws + (chunk0 + ci) * kChunkB + (REV ? kdS : kSb)) +
+                              (size_t)(v0 + tr) * kD + tc) = *reinterpret_cast<const u32x4*>(sst + tr * PT + tc);
+    if constexpr (BND) {   // sum over this tile's 16 value rows of dS o S, per key channel
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float* sp = ssa + (4 * lq) * (kD + 4) + 32 * w + 16 * j + l16;
+        float x = ((acc[j][0] * sp[0] + acc[j][1] * sp[kD + 4]) + (acc[j][2] * sp[2 * (kD + 4)] + acc[j][3] * sp[3 * (kD + 4)]));
+        x += __shfl_xor(x, 16);
+        x += __shfl_xor(x, 32);
+        if (lq == 0) bnd[((chunk0 + ci) * 8 + vt) * kD + 32 * w + 16 * j + l16] = x;
+      }
+    }
     acc[0] *= e0;
     acc[1] *= e1;
 #pragma unroll
