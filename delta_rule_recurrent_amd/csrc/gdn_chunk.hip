@@ -556,6 +556,304 @@ __device__ __forceinline__ void prep_chunk(PrepSmem& sm, KdaPrepSmem<KDA>& xs, P
 
 }  // namespace gdc
 
+// ------------------------------------------------------------------ per-chunk prep, GDN, two blocks per CU
+// The same operands as prep_chunk<false, STORE_T>, laid out to fit two blocks in a
+// CU's LDS (75,776 bytes): only the ten lower 16 x 16 blocks of L and T are kept; v
+// waits in registers and is staged over k once W is formed; W and U~ stay in
+// registers as accumulator tiles and enter the Q'^T and O~ products directly as the
+// operands of v_mfma_f32_16x16x16_bf16, whose A and B lanes hold four consecutive
+// rows of a 16 x 16 block, as an accumulator tile does.
+namespace gdc {
+
+constexpr int PL = 17;   // fp32 pitch of the 16 x 16 blocks of the triangular inverse
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+// bf16 16 x 16 x 16: lane l holds A[l%16][4(l/16) + e], B[4(l/16) + e][l%16]; D[4(l/16)+i][l%16]
+__device__ __forceinline__ f32x4 mfma16(s16x4 a, s16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ s16x4 bf4(f32x4 x) {
+  return __builtin_bit_cast(s16x4, u32x2{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])});
+}
+__device__ __forceinline__ s16x4 ld4(const uint16_t* p) {
+  return __builtin_bit_cast(s16x4, *reinterpret_cast<const u32x2*>(p));
+}
+__device__ __forceinline__ int tri(int I, int J) { return I * (I + 1) / 2 + J; }   // lower block (I, J), J <= I
+
+struct alignas(16) Prep2Smem {
+  uint16_t Q[C * PQ];    // q rows [t][k]
+  uint16_t KV[C * PQ];   // k rows [t][k]; once W is formed, v rows [t][v]
+  uint16_t A[C * PC];    // masked decayed scores [r][j]
+  union {
+    struct {
+      float L[10][16 * PL];     // strict lower part of (I + L), lower blocks
+      float scr[8][16 * PL];    // one 16 x 16 fp32 tile per wave (inverse)
+    } inv;
+    struct {
+      uint16_t Tw[C * PC];      // T diag(beta g)
+      uint16_t Tu[C * PC];      // T diag(beta)
+    } t;
+  } u;
+  float T[10][16 * PL];         // (I + L)^-1, lower blocks
+  float lg[C], g[C], kd[C], bt[C], btg[C];   // log g, g, g_C/g, beta, beta g
+};
+
+template <bool STORE_T>
+__device__ __forceinline__ void prep2_chunk(Prep2Smem& sm, PrepIn<false>& in, int cid,
+                                            const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                            const uint16_t* __restrict__ v, const float* __restrict__ alpha,
+                                            const float* __restrict__ beta, uint8_t* __restrict__ ws,
+                                            uint16_t* __restrict__ Tout, int T, int nchunks) {
+  // the thread index passed through an opaque move, so that the many per-lane LDS
+  // addresses are formed inside each chunk instead of being held across the loop
+  int tid;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"((int)threadIdx.x));
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int nc = T / C;
+  uint8_t* wsc = ws + (size_t)cid * kWsChunk;
+
+  // ---- stage q, k (row-major); v stays in registers until the keys are done; decays
+  u32x4 vcur[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int p = tid + NT * h, o = (p >> 4) * PQ + (p & 15) * 8;
+    *reinterpret_cast<u32x4*>(sm.Q + o) = in.q[h];
+    *reinterpret_cast<u32x4*>(sm.KV + o) = in.k[h];
+    vcur[h] = in.v[h];
+  }
+  {
+    const float lgv = wave_scan(__logf(in.al));
+    const float lC = __shfl(lgv, C - 1);
+    if (wave == 0) {
+      const float gv = __expf(lgv);
+      sm.lg[lane] = lgv;
+      sm.g[lane] = gv;
+      sm.kd[lane] = __expf(lC - lgv);
+      sm.bt[lane] = in.be;
+      sm.btg[lane] = in.be * gv;
+    }
+    *reinterpret_cast<float*>(wsc + kWsG + (lane & 15) * 4) = __expf(lC);
+  }
+  lds_barrier();
+
+  // ---- K^ fragments (kb, js) = (f >> 1, f & 1), f = wave + 8 h, to the workspace
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int f = wave + 8 * h, j0 = (f & 1) * 32 + lq * 8;
+    const u32x4 raw = __builtin_bit_cast(u32x4, ld_tr8(sm.KV, PQ, (f & 1) * 32, (f >> 1) * 16));
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = pack_bf16(lo_bf(raw[e]) * sm.kd[j0 + 2 * e], hi_bf(raw[e]) * sm.kd[j0 + 2 * e + 1]);
+    *reinterpret_cast<u32x4*>(wsc + kWsK + ((size_t)f * 64 + lane) * 16) = w;
+  }
+  // ---- Gram k.k -> L (lower blocks) and scores q.k -> A: 20 tile products, up to
+  // three per wave, one at a time (the other block on the CU hides their latency)
+  {
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll 1
+    for (int u = wv; u < 20; u += 8) {
+      int rb, cb;
+      tri_pair(u >> 1, rb, cb);
+      const uint16_t* X = (u & 1) ? sm.Q : sm.KV;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        acc = mfma(ld8(X + (rb * 16 + l16) * PQ + kk * 32 + lq * 8), ld8(sm.KV + (cb * 16 + l16) * PQ + kk * 32 + lq * 8),
+                   acc);
+      const int j = cb * 16 + l16, r0 = rb * 16 + lq * 4;
+      const f32x4 lgr = *reinterpret_cast<const f32x4*>(sm.lg + r0);
+      const float lgj = sm.lg[j];
+      f32x4 val;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x = __expf(lgr[i] - lgj) * acc[i];   // g_r / g_j for j <= r
+        val[i] = j <= r0 + i ? x : 0.f;
+      }
+      if (u & 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm.A[(r0 + i) * PC + j] = f32_to_bf16(val[i]);
+      } else {
+        const f32x4 bt = *reinterpret_cast<const f32x4*>(sm.bt + r0);
+        float* Lb = sm.u.inv.L[u >> 1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Lb[(lq * 4 + i) * PL + l16] = j < r0 + i ? bt[i] * val[i] : 0.f;
+      }
+    }
+  }
+  lds_barrier();
+
+  // ---- T = (I + L)^-1. Diagonal blocks: wave w -> block w >> 1, columns
+  // (w & 1) * 8 + 2 * (lane >> 4) + {0, 1}; lane & 15 is the row.
+  {
+    const int b = wave >> 1, i = l16;
+    const int c0 = (wave & 1) * 8 + 2 * lq, c1 = c0 + 1;
+    float lr[16];
+    const float* Lrow = sm.u.inv.L[tri(b, b)] + i * PL;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) lr[s] = Lrow[s];
+    float a0 = i == c0 ? 1.f : 0.f, a1 = i == c1 ? 1.f : 0.f;
+    DiagSolve<0>::run(lr, a0, a1);
+    sm.T[tri(b, b)][i * PL + c0] = a0;
+    sm.T[tri(b, b)][i * PL + c1] = a1;
+  }
+  lds_barrier();
+  // Blocks below the diagonal, by distance d = I - J:
+  //   T_IJ = -D_I sum_{K=J}^{I-1} L_IK T_KJ   (D_I = T_II), wave J for J < 4 - d
+#pragma unroll
+  for (int d = 1; d < 4; ++d) {
+    if (wave < 4 - d) {
+      const int J = wave, I = J + d;
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+      for (int K = J; K < I; ++K) {
+        const float* Lb = sm.u.inv.L[tri(I, K)];
+        const float* Tb = sm.T[tri(K, J)];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) x = mfma4(Lb[l16 * PL + 4 * s + lq], Tb[(4 * s + lq) * PL + l16], x);
+      }
+      float* scr = sm.u.inv.scr[wave];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) scr[(4 * lq + i) * PL + l16] = x[i];
+      wave_lds_sync();
+      const float* Dg = sm.T[tri(I, I)];
+      f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) y = mfma4(Dg[l16 * PL + 4 * s + lq], scr[(4 * s + lq) * PL + l16], y);
+      float* Tb = sm.T[tri(I, J)];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Tb[(4 * lq + i) * PL + l16] = -y[i];
+    }
+    lds_barrier();
+  }
+
+  // ---- T diag(beta g) and T diag(beta) in bf16 (zero above the diagonal blocks), over
+  // the inverse's L and scratch: thread -> row tid / 8, columns 8 (tid % 8) .. + 7
+  {
+    const int r = tid >> 3, j0 = (tid & 7) * 8;
+    const bool low = (j0 >> 4) <= (r >> 4);
+    const float* tb = sm.T[tri(r >> 4, low ? (j0 >> 4) : (r >> 4))] + (r & 15) * PL + (j0 & 15);
+    float tt[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tt[e] = low ? tb[e] : 0.f;
+    const f32x4 g0 = *reinterpret_cast<const f32x4*>(sm.btg + j0), g1 = *reinterpret_cast<const f32x4*>(sm.btg + j0 + 4);
+    const f32x4 b0 = *reinterpret_cast<const f32x4*>(sm.bt + j0), b1 = *reinterpret_cast<const f32x4*>(sm.bt + j0 + 4);
+    *reinterpret_cast<u32x4*>(sm.u.t.Tw + r * PC + j0) =
+        u32x4{pack_bf16(tt[0] * g0.x, tt[1] * g0.y), pack_bf16(tt[2] * g0.z, tt[3] * g0.w),
+              pack_bf16(tt[4] * g1.x, tt[5] * g1.y), pack_bf16(tt[6] * g1.z, tt[7] * g1.w)};
+    *reinterpret_cast<u32x4*>(sm.u.t.Tu + r * PC + j0) =
+        u32x4{pack_bf16(tt[0] * b0.x, tt[1] * b0.y), pack_bf16(tt[2] * b0.z, tt[3] * b0.w),
+              pack_bf16(tt[4] * b1.x, tt[5] * b1.y), pack_bf16(tt[6] * b1.z, tt[7] * b1.w)};
+    if constexpr (STORE_T) {   // T itself for the backward, bf16 [r][j], zero above the diagonal
+#pragma unroll
+      for (int e = 0; e < 8; ++e) tt[e] = j0 + e <= r ? tt[e] : 0.f;
+      *reinterpret_cast<u32x4*>(Tout + (size_t)cid * C * C + r * C + j0) =
+          u32x4{pack_bf16(tt[0], tt[1]), pack_bf16(tt[2], tt[3]), pack_bf16(tt[4], tt[5]), pack_bf16(tt[6], tt[7])};
+    }
+  }
+  lds_barrier();
+
+  // ---- W = Tw K: tiles (rb, kb = wave) kept in registers (bf16, as the A operands of
+  // the Q'^T products); W^T fragments (rb, ks) to the workspace. Row block rb only
+  // reaches tokens j <= 16 rb + 15.
+  s16x4 wa[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int js = 0; js <= rb / 2; ++js)
+      acc = mfma(ld8(sm.u.t.Tw + (rb * 16 + l16) * PC + js * 32 + lq * 8), ld_tr8(sm.KV, PQ, js * 32, wave * 16), acc);
+    wa[rb] = bf4(acc);
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {      // W^T fragments (rb, ks): rb pairs {0,3}, {1,2}
+    const int rb = h ? 3 - (wave & 3) : (wave & 3), ks = (wave >> 2) + 2 * h;
+    f32x4 t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
+    for (int js = 0; js <= rb / 2; ++js) {
+      const bf16x8 b = ld8(sm.u.t.Tw + (rb * 16 + l16) * PC + js * 32 + lq * 8);
+      t0 = mfma(ld_tr8(sm.KV, PQ, js * 32, ks * 32), b, t0);
+      t1 = mfma(ld_tr8(sm.KV, PQ, js * 32, ks * 32 + 16), b, t1);
+    }
+    *reinterpret_cast<u32x4*>(wsc + kWsW + ((size_t)(rb * 4 + ks) * 64 + lane) * 16) =
+        u32x4{pack_bf16(t0[0], t0[1]), pack_bf16(t0[2], t0[3]), pack_bf16(t1[0], t1[1]), pack_bf16(t1[2], t1[3])};
+  }
+  lds_barrier();
+
+  // ---- v over k, then the next chunk's inputs are requested (the last chunk of a block
+  // loads itself again); U~ = Tu V: tiles (rb, vb = wave) to the workspace and kept
+  // (bf16, as the B operands of the O~ products)
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int p = tid + NT * h;
+    *reinterpret_cast<u32x4*>(sm.KV + (p >> 4) * PQ + (p & 15) * 8) = vcur[h];
+  }
+  {
+    const int nx = cid + (int)gridDim.x < nchunks ? cid + (int)gridDim.x : cid;
+    prep_fetch<false>(in, q, k, v, alpha, beta, (size_t)(nx / nc) * T + (size_t)(nx % nc) * C);
+  }
+  lds_barrier();
+  s16x4 ub[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int js = 0; js <= rb / 2; ++js)
+      acc = mfma(ld8(sm.u.t.Tu + (rb * 16 + l16) * PC + js * 32 + lq * 8), ld_tr8(sm.KV, PQ, js * 32, wave * 16), acc);
+    const u32x2 pk = {pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
+    *reinterpret_cast<u32x2*>(wsc + kWsU + ((size_t)(rb * 8 + wave) * 64 + lane) * 8) = pk;
+    ub[rb] = __builtin_bit_cast(s16x4, pk);
+  }
+
+  // ---- Q'^T tiles (key block kb = wave, token block rb): g_r Q[r][key] minus
+  // sum_{j <= r} W[j][key] A[r][j], with the W tiles as A operands (lane: key l16, four
+  // tokens) and A read as B operands; each tile is one half of the Q' fragments
+  // (rb, kb / 2), written as 8 of each lane's 16 bytes.
+  {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int jb = 0; jb <= rb; ++jb) acc = mfma16(wa[jb], ld4(sm.A + (rb * 16 + l16) * PC + jb * 16 + lq * 4), acc);
+      const int r = rb * 16 + l16;
+      const u32x2 qa = *reinterpret_cast<const u32x2*>(sm.Q + r * PQ + wave * 16 + lq * 4);
+      const float gr = sm.g[r];
+      *reinterpret_cast<u32x2*>(wsc + kWsQ + ((size_t)(rb * 4 + (wave >> 1)) * 64 + lane) * 16 + 8 * (wave & 1)) =
+          u32x2{pack_bf16(gr * lo_bf(qa.x) - acc[0], gr * hi_bf(qa.x) - acc[1]),
+                pack_bf16(gr * lo_bf(qa.y) - acc[2], gr * hi_bf(qa.y) - acc[3])};
+    }
+  }
+  // ---- O~ = A U~ tiles (rb, vb = wave), with the U~ tiles as B operands
+  {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int jb = 0; jb <= rb; ++jb) acc = mfma16(ld4(sm.A + (rb * 16 + l16) * PC + jb * 16 + lq * 4), ub[jb], acc);
+      *reinterpret_cast<u32x2*>(wsc + kWsO + ((size_t)(rb * 8 + wave) * 64 + lane) * 8) =
+          u32x2{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
+    }
+  }
+  lds_barrier();
+}
+
+}  // namespace gdc
+
+template <bool STORE_T>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void gdn_chunk_prep2_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ alpha, const float* __restrict__ beta, uint8_t* __restrict__ ws,
+    uint16_t* __restrict__ Tout, int T, int nchunks) {
+  using namespace gdc;
+  __shared__ Prep2Smem sm;
+  const int nc = T / C;
+  PrepIn<false> in;
+  int cid = blockIdx.x;   // the grid never exceeds nchunks
+  prep_fetch<false>(in, q, k, v, alpha, beta, (size_t)(cid / nc) * T + (size_t)(cid % nc) * C);
+  prep2_chunk<STORE_T>(sm, in, cid, q, k, v, alpha, beta, ws, Tout, T, nchunks);
+  for (cid += gridDim.x; cid < nchunks; cid += gridDim.x)
+    prep2_chunk<STORE_T>(sm, in, cid, q, k, v, alpha, beta, ws, Tout, T, nchunks);
+}
+
 // Persistent: block b handles chunks b, b + grid, ...; the next chunk's inputs are
 // loaded into registers while this one is processed, and every thread issues the
 // same loads and stores on every chunk so that those waits are exact (the first chunk
@@ -855,11 +1153,17 @@ int chunk_fwd(const char* fn, const void* q, const void* k, const void* v, const
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   if (T > 0) {
-    // one persistent block per CU (the LDS of a block fills most of one)
-    const unsigned grid = (unsigned)(nchunks < 256 ? nchunks : 256);
-    hipLaunchKernelGGL((gdn_chunk_prep_kernel<KDA, false>), dim3(grid), dim3(gdc::NT), 0, s,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                       static_cast<const uint16_t*>(v), alpha, beta, ws, nullptr, T, (int)nchunks);
+    // persistent blocks: GDN two per CU, KDA one (its LDS fills most of a CU)
+    const size_t cap = KDA ? 256 : 512;
+    const unsigned grid = (unsigned)(nchunks < cap ? nchunks : cap);
+    if constexpr (KDA)
+      hipLaunchKernelGGL((gdn_chunk_prep_kernel<true, false>), dim3(grid), dim3(gdc::NT), 0, s,
+                         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                         static_cast<const uint16_t*>(v), alpha, beta, ws, nullptr, T, (int)nchunks);
+    else
+      hipLaunchKernelGGL((gdn_chunk_prep2_kernel<false>), dim3(grid), dim3(gdc::NT), 0, s,
+                         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                         static_cast<const uint16_t*>(v), alpha, beta, ws, nullptr, T, (int)nchunks);
     int rc = check_launch(fn);
     if (rc != GDNRT_OK) return rc;
   }
@@ -882,8 +1186,8 @@ namespace gdnrt {
 void gdn_chunk_prep_with_inverse(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                  const float* alpha, const float* beta, uint8_t* ws, uint16_t* Tout,
                                  int T, int nchunks, hipStream_t s) {
-  const unsigned grid = (unsigned)(nchunks < 256 ? nchunks : 256);
-  hipLaunchKernelGGL((gdn_chunk_prep_kernel<false, true>), dim3(grid), dim3(gdc::NT), 0, s, q, k, v, alpha,
+  const unsigned grid = (unsigned)(nchunks < 512 ? nchunks : 512);
+  hipLaunchKernelGGL((gdn_chunk_prep2_kernel<true>), dim3(grid), dim3(gdc::NT), 0, s, q, k, v, alpha,
                      beta, ws, Tout, T, nchunks);
 }
 }  // namespace gdnrt
