@@ -124,6 +124,7 @@ __device__ __forceinline__ bf16x8 ld_tr8(const uint16_t* X, int pitch, int c0, i
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// LDS of the KDA prep (one block per CU)
 struct alignas(16) PrepSmem {
   uint16_t Q[C * PQ];       // [r][k]
   uint16_t K[C * PQ];       // [j][k]
@@ -140,11 +141,11 @@ struct alignas(16) PrepSmem {
   union {
     float scr[8][16 * 17];  // one 16 x 16 fp32 tile per wave (inverse)
     struct {
-      uint16_t Tw[C * PC];  // T diag(beta g)
+      uint16_t Tw[C * PC];  // T diag(beta) (the decays are inside the key operand K o Gamma)
       uint16_t Tu[C * PC];  // T diag(beta)
     } t;
   } rw;
-  float lg[C], g[C], kd[C], bt[C], btg[C];   // log g, g, g_C/g, beta, beta g
+  float bt[C], btg[C];      // beta, and beta again as the W factor
 };
 
 // one chunk's inputs for this thread: 16-byte pieces p = tid + 512 h (h = 0, 1) of
@@ -185,15 +186,10 @@ __device__ __forceinline__ void prep_fetch(PrepIn<KDA>& in, const uint16_t* __re
 // KDA: the extra LDS of the prep. Km = K o exp(b_m - b) (bf16, the second operand of
 // the Gram matrix and the scores), per-group totals of the cumulative log-decays and
 // per-channel exp(b_m), exp(b_C - b_m), b_m the cumulative log-decay at token 31.
-template <bool KDA>
 struct alignas(16) KdaPrepSmem {
   uint16_t Km[C * PQ];
   float tot[16][kD];
   float em[kD], ecm[kD];
-};
-template <>
-struct alignas(16) KdaPrepSmem<false> {
-  float unused[4];
 };
 
 // lower-triangle 16 x 16 tile pairs (rb, cb), cb <= rb
@@ -206,19 +202,17 @@ __device__ __forceinline__ void tri_pair(int p, int& rb, int& cb) {
 
 namespace gdc {
 
-// One chunk of the prep: stages the inputs held in `in`, requests the next chunk's into
-// `in`, and writes the chunk's operands to the workspace.
-template <bool KDA, bool STORE_T>
-__device__ __forceinline__ void prep_chunk(PrepSmem& sm, KdaPrepSmem<KDA>& xs, PrepIn<KDA>& in, int cid,
-                                           const uint16_t* __restrict__ q,
-                                           const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                                           const float* __restrict__ alpha, const float* __restrict__ beta,
-                                           uint8_t* __restrict__ ws, uint16_t* __restrict__ Tout, int T,
-                                           int nchunks) {
+// One chunk of the KDA prep (one block per CU): stages the inputs held in `in`, requests
+// the next chunk's into `in`, and writes the chunk's operands to the workspace.
+__device__ __forceinline__ void kda_prep_chunk(PrepSmem& sm, KdaPrepSmem& xs, PrepIn<true>& in, int cid,
+                                               const uint16_t* __restrict__ q,
+                                               const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                               const float* __restrict__ alpha, const float* __restrict__ beta,
+                                               uint8_t* __restrict__ ws, int T, int nchunks) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lq = lane >> 4;
   const int nc = T / C;
-  uint8_t* wsc = ws + (size_t)cid * ws_chunk<KDA>();
+  uint8_t* wsc = ws + (size_t)cid * kWsChunkKda;
 
   // ---- stage q, k, v (row-major); decays
 #pragma unroll
@@ -228,106 +222,80 @@ __device__ __forceinline__ void prep_chunk(PrepSmem& sm, KdaPrepSmem<KDA>& xs, P
     *reinterpret_cast<u32x4*>(sm.K + o) = in.k[h];
     *reinterpret_cast<u32x4*>(sm.V + o) = in.v[h];
   }
-  float gCw = 0.f;   // GDN: g_C (every wave computes it)
-  // KDA: cumulative log-decays of this thread's 4 tokens x 4 channels, within its group
-  f32x4 pre[KDA ? 4 : 1];
-  if constexpr (KDA) {
+  // cumulative log-decays of this thread's 4 tokens x 4 channels, within its group
+  f32x4 pre[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f32x4 a = in.a4[i];
-      const f32x4 la = {__logf(a.x), __logf(a.y), __logf(a.z), __logf(a.w)};
-      pre[i] = i == 0 ? la : pre[i - 1] + la;
-    }
-    *reinterpret_cast<f32x4*>(&xs.tot[tid >> 5][4 * (tid & 31)]) = pre[3];
-    if (wave == 0) {
-      sm.bt[lane] = in.be;
-      sm.btg[lane] = in.be;   // the decays sit in the key operand of W
-    }
-  } else {
-    const float lgv = wave_scan(__logf(in.al));
-    const float lC = __shfl(lgv, C - 1);
-    gCw = __expf(lC);
-    if (wave == 0) {
-      const float gv = __expf(lgv);
-      sm.lg[lane] = lgv;
-      sm.g[lane] = gv;
-      sm.kd[lane] = __expf(lC - lgv);
-      sm.bt[lane] = in.be;
-      sm.btg[lane] = in.be * gv;
-    }
+  for (int i = 0; i < 4; ++i) {
+    const f32x4 a = in.a4[i];
+    const f32x4 la = {__logf(a.x), __logf(a.y), __logf(a.z), __logf(a.w)};
+    pre[i] = i == 0 ? la : pre[i - 1] + la;
+  }
+  *reinterpret_cast<f32x4*>(&xs.tot[tid >> 5][4 * (tid & 31)]) = pre[3];
+  if (wave == 0) {
+    sm.bt[lane] = in.be;
+    sm.btg[lane] = in.be;   // the decays sit in the key operand of W
   }
   // next chunk's inputs (the last chunk of a block loads itself again)
   {
     const int nx = cid + (int)gridDim.x < nchunks ? cid + (int)gridDim.x : cid;
-    prep_fetch<KDA>(in, q, k, v, alpha, beta, (size_t)(nx / nc) * T + (size_t)(nx % nc) * C);
+    prep_fetch<true>(in, q, k, v, alpha, beta, (size_t)(nx / nc) * T + (size_t)(nx % nc) * C);
   }
-  if constexpr (KDA) {
-    // b = cumulative log-decay per channel; with b_m its value at token 31 (the middle),
-    // Q <- Q o exp(b - b_m), K <- K o exp(b - b_m), Km = K o exp(b_m - b): the Gram
-    // matrix and the scores then carry exp(b_r - b_j) inside their products, and no
-    // factor exceeds exp(32 max|log alpha|)
-    lds_barrier();
-    const int tq = tid >> 5, c0 = 4 * (tid & 31);
-    f32x4 base = {0.f, 0.f, 0.f, 0.f}, bm = {0.f, 0.f, 0.f, 0.f}, bC = {0.f, 0.f, 0.f, 0.f};
+  // b = cumulative log-decay per channel; with b_m its value at token 31 (the middle),
+  // Q <- Q o exp(b - b_m), K <- K o exp(b - b_m), Km = K o exp(b_m - b): the Gram
+  // matrix and the scores then carry exp(b_r - b_j) inside their products, and no
+  // factor exceeds exp(32 max|log alpha|)
+  lds_barrier();
+  const int tq = tid >> 5, c0 = 4 * (tid & 31);
+  f32x4 base = {0.f, 0.f, 0.f, 0.f}, bm = {0.f, 0.f, 0.f, 0.f}, bC = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int g = 0; g < 16; ++g) {
-      const f32x4 t4 = *reinterpret_cast<const f32x4*>(&xs.tot[g][c0]);
-      if (g < tq) base += t4;
-      if (g < 8) bm += t4;
-      bC += t4;
+  for (int g = 0; g < 16; ++g) {
+    const f32x4 t4 = *reinterpret_cast<const f32x4*>(&xs.tot[g][c0]);
+    if (g < tq) base += t4;
+    if (g < 8) bm += t4;
+    bC += t4;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = 4 * tq + i;
+    const f32x4 b = base + pre[i];
+    f32x4 fp, fm;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      fp[e] = __expf(b[e] - bm[e]);
+      fm[e] = __expf(bm[e] - b[e]);
     }
+    u32x2* qp = reinterpret_cast<u32x2*>(sm.Q + t * PQ + c0);
+    u32x2* kp = reinterpret_cast<u32x2*>(sm.K + t * PQ + c0);
+    const u32x2 qw = *qp, kw = *kp;
+    *qp = u32x2{pack_bf16(lo_bf(qw.x) * fp[0], hi_bf(qw.x) * fp[1]), pack_bf16(lo_bf(qw.y) * fp[2], hi_bf(qw.y) * fp[3])};
+    *kp = u32x2{pack_bf16(lo_bf(kw.x) * fp[0], hi_bf(kw.x) * fp[1]), pack_bf16(lo_bf(kw.y) * fp[2], hi_bf(kw.y) * fp[3])};
+    *reinterpret_cast<u32x2*>(xs.Km + t * PQ + c0) =
+        u32x2{pack_bf16(lo_bf(kw.x) * fm[0], hi_bf(kw.x) * fm[1]), pack_bf16(lo_bf(kw.y) * fm[2], hi_bf(kw.y) * fm[3])};
+  }
+  if (tq == 0) {
+    f32x4 em, ecm, gc;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = 4 * tq + i;
-      const f32x4 b = base + pre[i];
-      f32x4 fp, fm;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        fp[e] = __expf(b[e] - bm[e]);
-        fm[e] = __expf(bm[e] - b[e]);
-      }
-      u32x2* qp = reinterpret_cast<u32x2*>(sm.Q + t * PQ + c0);
-      u32x2* kp = reinterpret_cast<u32x2*>(sm.K + t * PQ + c0);
-      const u32x2 qw = *qp, kw = *kp;
-      *qp = u32x2{pack_bf16(lo_bf(qw.x) * fp[0], hi_bf(qw.x) * fp[1]), pack_bf16(lo_bf(qw.y) * fp[2], hi_bf(qw.y) * fp[3])};
-      *kp = u32x2{pack_bf16(lo_bf(kw.x) * fp[0], hi_bf(kw.x) * fp[1]), pack_bf16(lo_bf(kw.y) * fp[2], hi_bf(kw.y) * fp[3])};
-      *reinterpret_cast<u32x2*>(xs.Km + t * PQ + c0) =
-          u32x2{pack_bf16(lo_bf(kw.x) * fm[0], hi_bf(kw.x) * fm[1]), pack_bf16(lo_bf(kw.y) * fm[2], hi_bf(kw.y) * fm[3])};
+    for (int e = 0; e < 4; ++e) {
+      em[e] = __expf(bm[e]);
+      ecm[e] = __expf(bC[e] - bm[e]);
+      gc[e] = __expf(bC[e]);
     }
-    if (tq == 0) {
-      f32x4 em, ecm, gc;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        em[e] = __expf(bm[e]);
-        ecm[e] = __expf(bC[e] - bm[e]);
-        gc[e] = __expf(bC[e]);
-      }
-      *reinterpret_cast<f32x4*>(&xs.em[c0]) = em;
-      *reinterpret_cast<f32x4*>(&xs.ecm[c0]) = ecm;
-      *reinterpret_cast<f32x4*>(wsc + kWsG + c0 * 4) = gc;
-    }
-  } else {
-    *reinterpret_cast<float*>(wsc + kWsG + (lane & 15) * 4) = gCw;
+    *reinterpret_cast<f32x4*>(&xs.em[c0]) = em;
+    *reinterpret_cast<f32x4*>(&xs.ecm[c0]) = ecm;
+    *reinterpret_cast<f32x4*>(wsc + kWsG + c0 * 4) = gc;
   }
   lds_barrier();
 
-  // ---- K^ fragments (kb, js) = (f >> 1, f & 1), f = wave + 8 h, to the workspace
-  // (KDA: K^ = Km o exp(b_C - b_m), one channel per lane)
+  // ---- K^ fragments (kb, js) = (f >> 1, f & 1), f = wave + 8 h, to the workspace:
+  // K^ = Km o exp(b_C - b_m), one channel per lane
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int f = wave + 8 * h, j0 = (f & 1) * 32 + lq * 8;
     u32x4 w;
-    if constexpr (KDA) {
-      const u32x4 raw = __builtin_bit_cast(u32x4, ld_tr8(xs.Km, PQ, (f & 1) * 32, (f >> 1) * 16));
-      const float fc = xs.ecm[(f >> 1) * 16 + l16];
+    const u32x4 raw = __builtin_bit_cast(u32x4, ld_tr8(xs.Km, PQ, (f & 1) * 32, (f >> 1) * 16));
+    const float fc = xs.ecm[(f >> 1) * 16 + l16];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = pack_bf16(lo_bf(raw[e]) * fc, hi_bf(raw[e]) * fc);
-    } else {
-      const u32x4 raw = __builtin_bit_cast(u32x4, ld_tr8(sm.K, PQ, (f & 1) * 32, (f >> 1) * 16));
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        w[e] = pack_bf16(lo_bf(raw[e]) * sm.kd[j0 + 2 * e], hi_bf(raw[e]) * sm.kd[j0 + 2 * e + 1]);
-    }
+    for (int e = 0; e < 4; ++e) w[e] = pack_bf16(lo_bf(raw[e]) * fc, hi_bf(raw[e]) * fc);
     *reinterpret_cast<u32x4*>(wsc + kWsK + ((size_t)f * 64 + lane) * 16) = w;
   }
   // ---- Gram k.k -> L and scores q.k -> A: 20 tile products over the lower triangle,
@@ -343,8 +311,7 @@ __device__ __forceinline__ void prep_chunk(PrepSmem& sm, KdaPrepSmem<KDA>& xs, P
         int rb, cb;
         tri_pair(u >> 1, rb, cb);
         const uint16_t* X = (u & 1) ? sm.Q : sm.K;
-        const uint16_t* Y = sm.K;
-        if constexpr (KDA) Y = xs.Km;
+        const uint16_t* Y = xs.Km;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
           acc[t] = mfma(ld8(X + (rb * 16 + l16) * PQ + kk * 32 + lq * 8),
@@ -359,20 +326,10 @@ __device__ __forceinline__ void prep_chunk(PrepSmem& sm, KdaPrepSmem<KDA>& xs, P
         tri_pair(u >> 1, rb, cb);
         const int j = cb * 16 + l16, r0 = rb * 16 + lq * 4;
         f32x4 val;
-        if constexpr (KDA) {
-          // the decay is already inside the product; above the diagonal the product is
-          // not a decayed one, so it is dropped by selection, never multiplied by 0
+        // the decay is already inside the product; above the diagonal the product is
+        // not a decayed one, so it is dropped by selection, never multiplied by 0
 #pragma unroll
-          for (int i = 0; i < 4; ++i) val[i] = j <= r0 + i ? acc[t][i] : 0.f;
-        } else {
-          const f32x4 lgr = *reinterpret_cast<const f32x4*>(sm.lg + r0);
-          const float lgj = sm.lg[j];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float x = __expf(lgr[i] - lgj) * acc[t][i];   // g_r / g_j for j <= r
-            val[i] = j <= r0 + i ? x : 0.f;
-          }
-        }
+        for (int i = 0; i < 4; ++i) val[i] = j <= r0 + i ? acc[t][i] : 0.f;
         if (u & 1) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) sm.A[(r0 + i) * PC + j] = f32_to_bf16(val[i]);
@@ -389,8 +346,7 @@ __device__ __forceinline__ void prep_chunk(PrepSmem& sm, KdaPrepSmem<KDA>& xs, P
     sm.A[(t * 32 + (e >> 4)) * PC + t * 32 + 16 + (e & 15)] = 0;
   }
   lds_barrier();
-  if constexpr (KDA) {   // K <- K o exp(b) (the key operand of W), this thread's 4 x 4 block
-    const int tq = tid >> 5, c0 = 4 * (tid & 31);
+  {   // K <- K o exp(b) (the key operand of W), this thread's 4 x 4 block
     const f32x4 em = *reinterpret_cast<const f32x4*>(&xs.em[c0]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -460,13 +416,6 @@ __device__ __forceinline__ void prep_chunk(PrepSmem& sm, KdaPrepSmem<KDA>& xs, P
         u32x4{pack_bf16(w0.x, w0.y), pack_bf16(w0.z, w0.w), pack_bf16(w1.x, w1.y), pack_bf16(w1.z, w1.w)};
     *reinterpret_cast<u32x4*>(sm.rw.t.Tu + r * PC + j0) =
         u32x4{pack_bf16(u0.x, u0.y), pack_bf16(u0.z, u0.w), pack_bf16(u1.x, u1.y), pack_bf16(u1.z, u1.w)};
-    if constexpr (STORE_T) {   // T itself for the backward, bf16 [r][j], zero above the diagonal
-      float tt[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) tt[e] = j0 + e <= r ? tt[e] : 0.f;
-      *reinterpret_cast<u32x4*>(Tout + (size_t)cid * C * C + r * C + j0) =
-          u32x4{pack_bf16(tt[0], tt[1]), pack_bf16(tt[2], tt[3]), pack_bf16(tt[4], tt[5]), pack_bf16(tt[6], tt[7])};
-    }
   }
   lds_barrier();
 
@@ -524,16 +473,9 @@ __device__ __forceinline__ void prep_chunk(PrepSmem& sm, KdaPrepSmem<KDA>& xs, P
       const int r = rb * 16 + l16;
       const u32x2 qa = *reinterpret_cast<const u32x2*>(sm.Q + r * PQ + ks * 32 + lq * 4);
       const u32x2 qb = *reinterpret_cast<const u32x2*>(sm.Q + r * PQ + ks * 32 + 16 + lq * 4);
-      // GDN: g_r per token; KDA: exp(b_m) per channel (Q holds Q o exp(b - b_m))
-      f32x4 fa, fb;
-      if constexpr (KDA) {
-        fa = *reinterpret_cast<const f32x4*>(&xs.em[ks * 32 + lq * 4]);
-        fb = *reinterpret_cast<const f32x4*>(&xs.em[ks * 32 + 16 + lq * 4]);
-      } else {
-        const float gr = sm.g[r];
-        fa = f32x4{gr, gr, gr, gr};
-        fb = fa;
-      }
+      // exp(b_m) per channel (Q holds Q o exp(b - b_m))
+      const f32x4 fa = *reinterpret_cast<const f32x4*>(&xs.em[ks * 32 + lq * 4]);
+      const f32x4 fb = *reinterpret_cast<const f32x4*>(&xs.em[ks * 32 + 16 + lq * 4]);
       *reinterpret_cast<u32x4*>(wsc + kWsQ + ((size_t)(rb * 4 + ks) * 64 + lane) * 16) =
           u32x4{pack_bf16(fa[0] * lo_bf(qa.x) - t0[0], fa[1] * hi_bf(qa.x) - t0[1]),
                 pack_bf16(fa[2] * lo_bf(qa.y) - t0[2], fa[3] * hi_bf(qa.y) - t0[3]),
@@ -557,9 +499,9 @@ __device__ __forceinline__ void prep_chunk(PrepSmem& sm, KdaPrepSmem<KDA>& xs, P
 }  // namespace gdc
 
 // ------------------------------------------------------------------ per-chunk prep, GDN, two blocks per CU
-// The same operands as prep_chunk<false, STORE_T>, laid out to fit two blocks in a
-// CU's LDS (75,776 bytes): only the ten lower 16 x 16 blocks of L and T are kept; v
-// waits in registers and is staged over k once W is formed; W and U~ stay in
+// The GDN prep, laid out to fit two blocks in a CU's LDS (75,776 bytes): only the ten
+// lower 16 x 16 blocks of L and T are kept; v waits in registers and is staged over k
+// once W is formed; W and U~ stay in
 // registers as accumulator tiles and enter the Q'^T and O~ products directly as the
 // operands of v_mfma_f32_16x16x16_bf16, whose A and B lanes hold four consecutive
 // rows of a 16 x 16 block, as an accumulator tile does.
@@ -854,27 +796,23 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
     prep2_chunk<STORE_T>(sm, in, cid, q, k, v, alpha, beta, ws, Tout, T, nchunks);
 }
 
-// Persistent: block b handles chunks b, b + grid, ...; the next chunk's inputs are
-// loaded into registers while this one is processed, and every thread issues the
+// KDA prep, persistent: block b handles chunks b, b + grid, ...; the next chunk's inputs
+// are loaded into registers while this one is processed, and every thread issues the
 // same loads and stores on every chunk so that those waits are exact (the first chunk
 // is peeled, so that the loop's waits do not also serve the loads issued before it).
-// With STORE_T the chunk's (I + L)^-1 is also written (bf16 [64][64] per chunk, to
-// Tout) for the chunkwise backward.
-template <bool KDA, bool STORE_T>
-__global__ __launch_bounds__(512) void gdn_chunk_prep_kernel(
+__global__ __launch_bounds__(512) void kda_chunk_prep_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ alpha, const float* __restrict__ beta, uint8_t* __restrict__ ws,
-    uint16_t* __restrict__ Tout, int T, int nchunks) {
+    const float* __restrict__ alpha, const float* __restrict__ beta, uint8_t* __restrict__ ws, int T,
+    int nchunks) {
   using namespace gdc;
   __shared__ PrepSmem sm;
-  __shared__ KdaPrepSmem<KDA> xs;
+  __shared__ KdaPrepSmem xs;
   const int nc = T / C;
-  PrepIn<KDA> in;
+  PrepIn<true> in;
   int cid = blockIdx.x;   // the grid never exceeds nchunks
-  prep_fetch<KDA>(in, q, k, v, alpha, beta, (size_t)(cid / nc) * T + (size_t)(cid % nc) * C);
-  prep_chunk<KDA, STORE_T>(sm, xs, in, cid, q, k, v, alpha, beta, ws, Tout, T, nchunks);
-  for (cid += gridDim.x; cid < nchunks; cid += gridDim.x)
-    prep_chunk<KDA, STORE_T>(sm, xs, in, cid, q, k, v, alpha, beta, ws, Tout, T, nchunks);
+  prep_fetch<true>(in, q, k, v, alpha, beta, (size_t)(cid / nc) * T + (size_t)(cid % nc) * C);
+  kda_prep_chunk(sm, xs, in, cid, q, k, v, alpha, beta, ws, T, nchunks);
+  for (cid += gridDim.x; cid < nchunks; cid += gridDim.x) kda_prep_chunk(sm, xs, in, cid, q, k, v, alpha, beta, ws, T, nchunks);
 }
 
 // ------------------------------------------------------------------ sequential pass
@@ -1157,9 +1095,9 @@ int chunk_fwd(const char* fn, const void* q, const void* k, const void* v, const
     const size_t cap = KDA ? 256 : 512;
     const unsigned grid = (unsigned)(nchunks < cap ? nchunks : cap);
     if constexpr (KDA)
-      hipLaunchKernelGGL((gdn_chunk_prep_kernel<true, false>), dim3(grid), dim3(gdc::NT), 0, s,
+      hipLaunchKernelGGL(kda_chunk_prep_kernel, dim3(grid), dim3(gdc::NT), 0, s,
                          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                         static_cast<const uint16_t*>(v), alpha, beta, ws, nullptr, T, (int)nchunks);
+                         static_cast<const uint16_t*>(v), alpha, beta, ws, T, (int)nchunks);
     else
       hipLaunchKernelGGL((gdn_chunk_prep2_kernel<false>), dim3(grid), dim3(gdc::NT), 0, s,
                          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
