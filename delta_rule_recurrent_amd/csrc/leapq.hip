@@ -538,7 +538,7 @@ __device__ __forceinline__ void cholqr2_wave(float (&x)[2][RANK]) {
 __device__ __forceinline__ f32x4 lds4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 
 template <int RANK, bool KDA>
-__global__ __launch_bounds__(kFlushNT) __attribute__((amdgpu_waves_per_eu(RANK <= 5 ? 3 : 2))) void leapq_flush_kernel(
+__global__ __launch_bounds__(kFlushNT) __attribute__((amdgpu_waves_per_eu(RANK <= 4 ? 4 : RANK <= 5 ? 3 : 2))) void leapq_flush_kernel(
     int8_t* __restrict__ codes, float* __restrict__ vscale, float* __restrict__ ksmooth,
     uint16_t* __restrict__ ct_k, uint16_t* __restrict__ ct_u, const float* __restrict__ buf_k,
     const float* __restrict__ buf_u, const float* __restrict__ buf_a, int window, int m,
