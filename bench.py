@@ -240,9 +240,11 @@ def leapq_bytes_per_head_window(W=16, rank=4, kda=False):
 
 
 def bench_leapq(tokens=4096, B=DECODE_B, H=DECODE_H, W=16, rank=4, kda=False):
-    """The windowed INT8 state over ``tokens`` decode steps (every window: W decode
-    launches and one flush). With ``kda``: one decay per key channel (inputs are
-    drawn for 256 steps and reused cyclically)."""
+    """The windowed INT8 state over ``tokens`` decode steps (every window: W - 1
+    decode launches, then the window's last token and its flush in one launch; the
+    two-launch form, W decode launches and a flush, is timed beside it). With
+    ``kda``: one decay per key channel (inputs are drawn for 256 steps and reused
+    cyclically)."""
     N = B * H
     tag = "kda_leapq" if kda else "leapq"
     gen = min(tokens, 256) if kda else tokens
@@ -254,8 +256,16 @@ def bench_leapq(tokens=4096, B=DECODE_B, H=DECODE_H, W=16, rank=4, kda=False):
     o = torch.empty((N, D), dtype=torch.bfloat16, device="cuda")
     step = m.kda_leapq_decode_step if kda else m.leapq_decode_step
     flush = m.kda_leapq_window_flush if kda else m.leapq_window_flush
+    last = m.kda_leapq_decode_flush if kda else m.leapq_decode_flush
 
     def run_window(w):
+        for j in range(W - 1):
+            t = (w * W + j) % gen
+            step(st, q[t], k[t], v[t], a[t], b[t], o)
+        t = (w * W + W - 1) % gen
+        last(st, q[t], k[t], v[t], a[t], b[t], Q0, o)
+
+    def run_window_two_launch(w):
         for j in range(W):
             t = (w * W + j) % gen
             step(st, q[t], k[t], v[t], a[t], b[t], o)
@@ -264,6 +274,7 @@ def bench_leapq(tokens=4096, B=DECODE_B, H=DECODE_H, W=16, rank=4, kda=False):
     flush(st, Q0, dense=inp["S0"])      # encode the initial state
     n_win = tokens // W
     ms_win, wall = timed(run_window, n_win, 1)
+    ms_win2, _ = timed(run_window_two_launch, n_win, 1)
     ms_step = ms_win / W
     bpw = leapq_bytes_per_head_window(W, rank, kda) * N
     # per-kernel split from events around each launch of one window
@@ -275,16 +286,23 @@ def bench_leapq(tokens=4096, B=DECODE_B, H=DECODE_H, W=16, rank=4, kda=False):
         ev[j + 1].record(s)
     flush(st, Q0)
     ev[W + 1].record(s)
+    for j in range(W - 1):
+        step(st, q[j], k[j], v[j], a[j], b[j], o)
+    ev2 = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev2[0].record(s)
+    last(st, q[W - 1], k[W - 1], v[W - 1], a[W - 1], b[W - 1], Q0, o)
+    ev2[1].record(s)
     torch.cuda.synchronize()
     dec_ms = ev[0].elapsed_time(ev[W]) / W
     flush_ms = ev[W].elapsed_time(ev[W + 1])
+    last_ms = ev2[0].elapsed_time(ev2[1])
     res = dict(workload=f"{tag}_decode B={B} H={H} d=128, INT8 residual + fp32 scales + {rank} fp16 "
                         f"compensators, {W}-token fp32 buffer"
                         f"{' with per-channel fp32 decays' if kda else ''}, {tokens} tokens",
                ms_per_step=ms_step, tokens_per_s=B / (ms_step * 1e-3),
                bytes_per_head_step=bpw / N / W, achieved_gbs=bpw / (ms_win * 1e-3) / 1e9,
-               decode_kernel_ms=dec_ms, flush_kernel_ms=flush_ms, wall_s=wall,
-               decode_kernel_gbs=None)
+               decode_kernel_ms=dec_ms, flush_kernel_ms=flush_ms, decode_flush_kernel_ms=last_ms,
+               two_launch_ms_per_step=ms_win2 / W, wall_s=wall, decode_kernel_gbs=None)
     res["frac_hbm"] = res["achieved_gbs"] / PEAK_HBM_GBS
     del inp
     return res
@@ -701,21 +719,25 @@ def main():
         r = bench_leapq()
         r["traffic_bytes_decode_kernel"] = counter_traffic("leapq_decode_kernel")
         r["traffic_bytes_flush_kernel"] = counter_traffic("leapq_flush_kernel")
+        r["traffic_bytes_decode_flush_kernel"] = counter_traffic("leapq_decode_flush_kernel")
         r["speedup_vs_fp32_decode"] = res["ms_per_step"] / r["ms_per_step"] if res else None
         out_rows["leapq"] = r
-        log(f"[leapq] {r['ms_per_step']*1e3:.1f} us/step ({r['decode_kernel_ms']*1e3:.1f} us decode "
-            f"+ {r['flush_kernel_ms']*1e3:.1f} us flush per window)  {r['achieved_gbs']:.0f} GB/s  "
+        log(f"[leapq] {r['ms_per_step']*1e3:.1f} us/step ({r['decode_kernel_ms']*1e3:.1f} us decode, "
+            f"{r['decode_flush_kernel_ms']*1e3:.1f} us last token + flush per window; two launches "
+            f"{r['two_launch_ms_per_step']*1e3:.1f} us/step)  {r['achieved_gbs']:.0f} GB/s  "
             f"{r['tokens_per_s']/1e6:.3f} M tok/s")
         torch.cuda.empty_cache()
     if "kda_leapq" in rows:
         r = bench_leapq(tokens=256, kda=True)
         r["traffic_bytes_decode_kernel"] = counter_traffic("leapq_decode_kernel<kda>")
         r["traffic_bytes_flush_kernel"] = counter_traffic("leapq_flush_kernel<kda>")
+        r["traffic_bytes_decode_flush_kernel"] = counter_traffic("leapq_decode_flush_kernel<kda>")
         kda_row = out_rows.get("kda")
         r["speedup_vs_fp32_kda_decode"] = kda_row["ms_per_step"] / r["ms_per_step"] if kda_row else None
         out_rows["kda_leapq"] = r
-        log(f"[kda_leapq] {r['ms_per_step']*1e3:.1f} us/step ({r['decode_kernel_ms']*1e3:.1f} us decode "
-            f"+ {r['flush_kernel_ms']*1e3:.1f} us flush per window)  {r['achieved_gbs']:.0f} GB/s  "
+        log(f"[kda_leapq] {r['ms_per_step']*1e3:.1f} us/step ({r['decode_kernel_ms']*1e3:.1f} us decode, "
+            f"{r['decode_flush_kernel_ms']*1e3:.1f} us last token + flush per window; two launches "
+            f"{r['two_launch_ms_per_step']*1e3:.1f} us/step)  {r['achieved_gbs']:.0f} GB/s  "
             f"{r['tokens_per_s']/1e6:.3f} M tok/s")
         torch.cuda.empty_cache()
     ceil = None

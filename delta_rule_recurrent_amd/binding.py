@@ -56,6 +56,10 @@ SIGNATURES = {
     "leapq_window_flush": ([ctypes.POINTER(LeapqState), _c_int, _vp, _vp, _c_int, _c_int, _vp, _vp],
                            _c_int),
     "kda_leapq_decode_step": ([ctypes.POINTER(LeapqState), _c_int] + [_vp] * 6 + [_c_int, _vp], _c_int),
+    "leapq_decode_flush": ([ctypes.POINTER(LeapqState)] + [_vp] * 6 + [_c_int, _vp, _c_int, _c_int, _vp],
+                           _c_int),
+    "kda_leapq_decode_flush": ([ctypes.POINTER(LeapqState)] + [_vp] * 6 + [_c_int, _vp, _c_int, _c_int, _vp],
+                               _c_int),
     "kda_leapq_window_flush": ([ctypes.POINTER(LeapqState), _c_int, _vp, _vp, _c_int, _c_int, _vp, _vp],
                                _c_int),
     "gdnrt_last_error": ([], ctypes.c_char_p),
@@ -532,3 +536,38 @@ def kda_leapq_decode_step(st: LeapqBuffers, q, k, v, alpha, beta, o=None):
     if not st.kda:
         raise ValueError("kda_leapq_decode_step: allocate the buffers with kda=True")
     return _decode("kda_leapq_decode_step", st, q, k, v, alpha, beta, o, (st.N, D))
+
+
+def _decode_flush(name, st, q, k, v, alpha, beta, o, alpha_shape, q0, iters, smooth_mode):
+    N = st.N
+    if st.pos != st.window - 1:
+        raise ValueError(f"{name}: {st.pos} records buffered, the window's last token needs {st.window - 1}")
+    io = _io(q.dtype)
+    for n_, t_ in (("q", q), ("k", k), ("v", v)):
+        _need(t_, n_, q.dtype, (N, D))
+    _need(alpha, "alpha", torch.float32, alpha_shape)
+    _need(beta, "beta", torch.float32, (N,))
+    _need(q0, "q0", torch.float32, (D, st.rank) if st.rank > 0 else None)
+    if o is None:
+        o = torch.empty((N, D), dtype=q.dtype, device=q.device)
+    _need(o, "o", q.dtype, (N, D))
+    _check(name, getattr(lib(), name)(
+        ctypes.byref(st.struct), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(o), io,
+        _ptr(q0), iters, smooth_mode, _stream()))
+    st.pos = 0
+    return o
+
+
+def leapq_decode_flush(st: LeapqBuffers, q, k, v, alpha, beta, q0, o=None, iters=1, smooth_mode=0):
+    """The window's last token and the flush in one launch (window - 1 records
+    buffered). Returns o; resets the window position to 0."""
+    if st.kda:
+        raise ValueError("leapq_decode_flush: the buffers hold per-channel decays (use kda_leapq_decode_flush)")
+    return _decode_flush("leapq_decode_flush", st, q, k, v, alpha, beta, o, (st.N,), q0, iters, smooth_mode)
+
+
+def kda_leapq_decode_flush(st: LeapqBuffers, q, k, v, alpha, beta, q0, o=None, iters=1, smooth_mode=0):
+    """KDA form of leapq_decode_flush (alpha [N][128])."""
+    if not st.kda:
+        raise ValueError("kda_leapq_decode_flush: allocate the buffers with kda=True")
+    return _decode_flush("kda_leapq_decode_flush", st, q, k, v, alpha, beta, o, (st.N, D), q0, iters, smooth_mode)

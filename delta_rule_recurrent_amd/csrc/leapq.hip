@@ -537,16 +537,34 @@ __device__ __forceinline__ void cholqr2_wave(float (&x)[2][RANK]) {
 // four consecutive floats of LDS as a vector (16-byte aligned)
 __device__ __forceinline__ f32x4 lds4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 
-template <int RANK, bool KDA>
-__global__ __launch_bounds__(kFlushNT) __attribute__((amdgpu_waves_per_eu(RANK <= 4 ? 4 : RANK <= 5 ? 3 : 2))) void leapq_flush_kernel(
+// The token of the window's last position, decoded inside the flush.
+// io: GDNRT_F32 or GDNRT_BF16 for q, k, v, o.
+struct FlushToken {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* alpha;
+  const float* beta;
+  void* o;
+  int io;
+};
+
+__device__ __forceinline__ float ld_io(const void* p, size_t i, int io) {
+  return io == GDNRT_F32 ? static_cast<const float*>(p)[i] : bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+}
+
+template <int RANK, bool KDA, bool TOK>
+__global__ __launch_bounds__(kFlushNT) __attribute__((amdgpu_waves_per_eu(RANK <= 4 && !TOK ? 4 : RANK <= 5 ? 3 : 2))) void leapq_flush_kernel(
     int8_t* __restrict__ codes, float* __restrict__ vscale, float* __restrict__ ksmooth,
     uint16_t* __restrict__ ct_k, uint16_t* __restrict__ ct_u, const float* __restrict__ buf_k,
     const float* __restrict__ buf_u, const float* __restrict__ buf_a, int window, int m,
     const float* __restrict__ dense, const float* __restrict__ q0, int iters, int smooth_mode,
-    float qf, float qinv, float* __restrict__ pre_round) {
+    float qf, float qinv, float* __restrict__ pre_round, FlushToken tok) {
   constexpr int RQ = RANK <= 4 ? 4 : 8;   // padded rank of the LDS blocks
   __shared__ FlushSmem<RQ> sm;
   __shared__ FlushDecays<KDA> dk_[1];
+  // TOK: the token's k, q, decays and v (kD each), then beta
+  __shared__ __attribute__((aligned(16))) float s_tok[TOK ? 4 * kD + 4 : 4];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
   const int head = blockIdx.x;
   const size_t hk = (size_t)head * kD;
@@ -568,6 +586,16 @@ __global__ __launch_bounds__(kFlushNT) __attribute__((amdgpu_waves_per_eu(RANK <
   const int ns = (nt + 3) >> 2;          // MFMA steps of four terms
   uint4 z[2][2];
   float vs[2];
+  if constexpr (TOK) {
+    if (tid < kD) {
+      s_tok[tid] = ld_io(tok.k, hk + tid, tok.io);
+      s_tok[kD + tid] = ld_io(tok.q, hk + tid, tok.io);
+      s_tok[2 * kD + tid] = KDA ? tok.alpha[hk + tid] : tok.alpha[head];
+    } else {
+      s_tok[3 * kD + tid - kD] = ld_io(tok.v, hk + tid - kD, tok.io);
+      if (tid == kD) s_tok[4 * kD] = tok.beta[head];
+    }
+  }
   if (dense) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -662,6 +690,58 @@ __global__ __launch_bounds__(kFlushNT) __attribute__((amdgpu_waves_per_eu(RANK <
         acc[0][tc] = mfma4(a, b0, acc[0][tc]);
         acc[1][tc] = mfma4(a, b1, acc[1][tc]);
       }
+    }
+  }
+
+  // ---------------------------------------------------------------- the window's last token
+  // With m = window - 1 records rebuilt, acc holds S_m. The token is decoded from it
+  // (eq. 3 with the decay a = alpha on every key channel, or the KDA decay vector):
+  //   u = beta (v - S_m (a o k)),  o = S_m (a o q) + u (k . q),  S <- S_m Diag(a) + u k^T,
+  // the same step the decode kernel takes through eq. 10, and the flush goes on from S.
+  if constexpr (TOK) {
+    const float* s_tk = s_tok;
+    const float* s_tq = s_tok + kD;
+    const float* s_ta = s_tok + 2 * kD;
+    const float tb = s_tok[4 * kD];
+    float sk[2] = {0.f, 0.f}, sq[2] = {0.f, 0.f}, kq = 0.f;
+#pragma unroll
+    for (int tc = 0; tc < 8; ++tc) {
+      const f32x4 k4 = lds4(s_tk + 32 * g + 4 * tc), q4 = lds4(s_tq + 32 * g + 4 * tc);
+      const f32x4 a4 = lds4(s_ta + 32 * g + 4 * tc);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float ak = a4[e] * k4[e], aq = a4[e] * q4[e];
+        kq += k4[e] * q4[e];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          sk[t] += acc[t][tc][e] * ak;
+          sq[t] += acc[t][tc][e] * aq;
+        }
+      }
+    }
+    kq += xor_lane(kq, 16);
+    kq += xor_lane(kq, 32);
+    float u[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      sk[t] += xor_lane(sk[t], 16);
+      sk[t] += xor_lane(sk[t], 32);
+      sq[t] += xor_lane(sq[t], 16);
+      sq[t] += xor_lane(sq[t], 32);
+      u[t] = tb * (s_tok[3 * kD + vrow[t]] - sk[t]);
+      if (g == 0) {
+        const float oi = sq[t] + u[t] * kq;
+        if (tok.io == GDNRT_F32) static_cast<float*>(tok.o)[hk + vrow[t]] = oi;
+        else static_cast<uint16_t*>(tok.o)[hk + vrow[t]] = f32_to_bf16(oi);
+      }
+    }
+#pragma unroll
+    for (int tc = 0; tc < 8; ++tc) {
+      const f32x4 k4 = lds4(s_tk + 32 * g + 4 * tc), a4 = lds4(s_ta + 32 * g + 4 * tc);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[t][tc][e] = fmaf(acc[t][tc][e], a4[e], u[t] * k4[e]);
     }
   }
 
@@ -909,7 +989,7 @@ int decode_step(const char* fn, const leapq_state* st, int pos, const void* q, c
 
 template <bool KDA>
 int window_flush(const char* fn, const leapq_state* st, int pos, const float* dense, const float* q0,
-                 int iters, int smooth_mode, float* pre_round, void* stream) {
+                 int iters, int smooth_mode, float* pre_round, void* stream, FlushToken tok = FlushToken{}) {
   int rc = check_state(st, fn);
   if (rc != GDNRT_OK) return rc;
   if (pos < 0 || pos > st->window)
@@ -930,10 +1010,16 @@ int window_flush(const char* fn, const leapq_state* st, int pos, const float* de
   switch (st->rank) {
 #define GDNRT_FLUSH(R)                                                                            \
   case R:                                                                                         \
-    hipLaunchKernelGGL((leapq_flush_kernel<R, KDA>), dim3((unsigned)N), dim3(kFlushNT),          \
-                       0, s, st->codes, st->vscale, st->ksmooth, st->ct_k, st->ct_u, st->buf_k,   \
-                       st->buf_u, st->buf_a, st->window, pos, dense, q0, iters, smooth_mode, qf,  \
-                       qinv, pre_round);                                                          \
+    if (tok.q)                                                                                    \
+      hipLaunchKernelGGL((leapq_flush_kernel<R, KDA, true>), dim3((unsigned)N), dim3(kFlushNT),  \
+                         0, s, st->codes, st->vscale, st->ksmooth, st->ct_k, st->ct_u, st->buf_k, \
+                         st->buf_u, st->buf_a, st->window, pos, dense, q0, iters, smooth_mode,    \
+                         qf, qinv, pre_round, tok);                                               \
+    else                                                                                          \
+      hipLaunchKernelGGL((leapq_flush_kernel<R, KDA, false>), dim3((unsigned)N), dim3(kFlushNT), \
+                         0, s, st->codes, st->vscale, st->ksmooth, st->ct_k, st->ct_u, st->buf_k, \
+                         st->buf_u, st->buf_a, st->window, pos, dense, q0, iters, smooth_mode,    \
+                         qf, qinv, pre_round, tok);                                               \
     break;
     GDNRT_FLUSH(0) GDNRT_FLUSH(1) GDNRT_FLUSH(2) GDNRT_FLUSH(3) GDNRT_FLUSH(4)
     GDNRT_FLUSH(5) GDNRT_FLUSH(6) GDNRT_FLUSH(7) GDNRT_FLUSH(8)
@@ -942,7 +1028,45 @@ int window_flush(const char* fn, const leapq_state* st, int pos, const float* de
   return check_launch(fn);
 }
 
+// The last token of a window and the flush in one launch: the arguments of
+// leapq_decode_step at pos = window - 1, then those of leapq_window_flush.
+template <bool KDA>
+int decode_flush(const char* fn, const leapq_state* st, const void* q, const void* k, const void* v,
+                 const float* alpha, const float* beta, void* o, int io, const float* q0, int iters,
+                 int smooth_mode, void* stream) {
+  int rc = check_state(st, fn);
+  if (rc != GDNRT_OK) return rc;
+  if (io != GDNRT_F32 && io != GDNRT_BF16) return set_error(GDNRT_EDTYPE, "%s: io=%d", fn, io);
+  if (st->N == 0) return clear_error();
+  if (!q || !k || !v || !alpha || !beta || !o) return set_error(GDNRT_EINVAL, "%s: null pointer argument", fn);
+  if (!aligned4(q) || !aligned4(k) || !aligned4(v) || !aligned4(o) || !aligned4(alpha) || !aligned4(beta))
+    return set_error(GDNRT_EALIGN, "%s: q, k, v, o, alpha, beta must be 4-byte aligned", fn);
+  const size_t es = io == GDNRT_F32 ? 4 : 2;
+  const size_t N = st->N, nIO = N * kD * es, nB = N * st->window * kD * 4;
+  if (overlaps(o, nIO, q, nIO) || overlaps(o, nIO, k, nIO) || overlaps(o, nIO, v, nIO) ||
+      overlaps(o, nIO, st->buf_k, nB) || overlaps(o, nIO, st->buf_u, nB) ||
+      overlaps(o, nIO, st->codes, N * kD * kD) || overlaps(o, nIO, st->ct_u, N * st->rank * kD * 2) ||
+      overlaps(o, nIO, st->ct_k, N * st->rank * kD * 2))
+    return set_error(GDNRT_EINVAL, "%s: o overlaps another buffer", fn);
+  return window_flush<KDA>(fn, st, st->window - 1, nullptr, q0, iters, smooth_mode, nullptr, stream,
+                           FlushToken{q, k, v, alpha, beta, o, io});
+}
+
 }  // namespace
+
+extern "C" int leapq_decode_flush(const leapq_state* st, const void* q, const void* k, const void* v,
+                                  const float* alpha, const float* beta, void* o, int io, const float* q0,
+                                  int iters, int smooth_mode, void* stream) {
+  return decode_flush<false>("leapq_decode_flush", st, q, k, v, alpha, beta, o, io, q0, iters, smooth_mode,
+                             stream);
+}
+
+extern "C" int kda_leapq_decode_flush(const leapq_state* st, const void* q, const void* k, const void* v,
+                                      const float* alpha, const float* beta, void* o, int io,
+                                      const float* q0, int iters, int smooth_mode, void* stream) {
+  return decode_flush<true>("kda_leapq_decode_flush", st, q, k, v, alpha, beta, o, io, q0, iters, smooth_mode,
+                            stream);
+}
 
 extern "C" int leapq_decode_step(const leapq_state* st, int pos, const void* q, const void* k,
                                  const void* v, const float* alpha, const float* beta, void* o,

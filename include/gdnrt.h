@@ -450,6 +450,27 @@ GDNRT_API int kda_leapq_window_flush(const leapq_state* st, int pos, const float
                        const float* q0, int iters, int smooth_mode,
                        float* pre_round, void* stream);
 
+/*
+ * The last token of a window and the flush that closes it, in one launch: the same
+ * results as leapq_decode_step at pos = window - 1 followed by leapq_window_flush at
+ * pos = window with dense = pre_round = NULL, up to fp32 rounding order ("LeapQuant",
+ * section "Fix one: leap over a window": the token after window - 1 buffered ones
+ * ends the window, eq. 4 rebuilds S_{window-1}, the token's update is applied to it
+ * in fp32, and steps 1-5 of leapq_window_flush encode the result). The token's
+ * record is not appended: the flush consumes it. window - 1 records must be
+ * buffered. q, k, v, o [N][dk|dv] io dtype, alpha [N] fp32 (kda_: [N][dk]), beta [N]
+ * fp32, all 4-byte aligned; q0, iters, smooth_mode as in leapq_window_flush. o must
+ * not overlap an input or the state. Errors as the two calls it replaces.
+ */
+GDNRT_API int leapq_decode_flush(const leapq_state* st, const void* q, const void* k,
+                      const void* v, const float* alpha, const float* beta, void* o,
+                      int io, const float* q0, int iters, int smooth_mode, void* stream);
+
+/* KDA form of leapq_decode_flush (the kda_leapq_decode_step token, then kda_leapq_window_flush). */
+GDNRT_API int kda_leapq_decode_flush(const leapq_state* st, const void* q, const void* k,
+                      const void* v, const float* alpha, const float* beta, void* o,
+                      int io, const float* q0, int iters, int smooth_mode, void* stream);
+
 /* Message for the calling thread's last non-OK status ("" if none). */
 GDNRT_API const char* gdnrt_last_error(void);
 

@@ -38,7 +38,8 @@ def test_header_declares_the_entry_points():
               "gla_chunk_bwd", "gla_chunk_bwd_workspace_bytes", "gdn_chunk_bwd",
               "gdn_chunk_bwd_workspace_bytes", "gdn_decode_step_bf16_state",
               "gdn_decode_step_int_state", "gla_shard_decay", "gla_all_scan_step",
-              "gla_shard_output_correct", "gla_shard_bwd_state", "gla_shard_bwd_grads"):
+              "gla_shard_output_correct", "gla_shard_bwd_state", "gla_shard_bwd_grads",
+              "leapq_decode_flush", "kda_leapq_decode_flush"):
         assert n in names, n
 
 
@@ -152,6 +153,28 @@ def test_kda_leapq_validation(lib):
     assert fl(ctypes.byref(st), 17, None, p, 1, 0, None, None) == ESTATE
     assert fl(ctypes.byref(st), 0, None, None, 1, 0, None, None) == EINVAL   # q0 missing
     assert fl(ctypes.byref(_state(lib, buf_a=4100)), 0, None, p, 1, 0, None, None) == EALIGN
+
+
+def test_leapq_decode_flush_validation(lib):
+    """The window-closing entry points check the token as the decode step and the
+    flush arguments as the flush, and launch nothing on an error."""
+    q, k, v, a, b, q0 = (ctypes.c_void_p(x << 20) for x in range(1, 7))
+    o = ctypes.c_void_p(1 << 40)
+    st = _state(lib)
+    for name in ("leapq_decode_flush", "kda_leapq_decode_flush"):
+        f = getattr(lib, name)
+        assert f(None, q, k, v, a, b, o, 1, q0, 1, 0, None) == EINVAL
+        assert f(ctypes.byref(_state(lib, rank=9)), q, k, v, a, b, o, 1, q0, 1, 0, None) == ESHAPE
+        assert f(ctypes.byref(_state(lib, window=0)), q, k, v, a, b, o, 1, q0, 1, 0, None) == ESHAPE
+        assert f(ctypes.byref(st), q, k, v, a, b, o, 7, q0, 1, 0, None) == EDTYPE
+        assert f(ctypes.byref(st), q, k, v, a, b, o, 1, q0, 1, 3, None) == EINVAL     # smooth_mode
+        assert f(ctypes.byref(st), q, k, v, a, b, o, 1, q0, 65, 0, None) == EINVAL    # iters
+        assert f(ctypes.byref(st), q, k, v, a, b, o, 1, None, 1, 0, None) == EINVAL   # q0 missing
+        assert f(ctypes.byref(st), q, None, v, a, b, o, 1, q0, 1, 0, None) == EINVAL
+        assert f(ctypes.byref(st), q, k, v, a, b, ctypes.c_void_p((1 << 40) + 2), 1, q0, 1, 0, None) == EALIGN
+        assert f(ctypes.byref(st), q, k, v, a, b, q, 1, q0, 1, 0, None) == EINVAL     # o is q
+        assert name in _err(lib)
+        assert f(ctypes.byref(_state(lib, N=0)), q, k, v, a, b, o, 1, q0, 1, 0, None) == OK
 
 
 def test_kda_chunk_validation(lib):

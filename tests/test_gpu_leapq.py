@@ -39,7 +39,7 @@ def buffer(st, pos, heads=None):
     return [(bk[:, j], bu[:, j], ba[:, j]) for j in range(pos)]
 
 
-def compare_flush(st, ref, what, S, mode=0, Q=127):
+def compare_flush(st, ref, what, S, mode=0, Q=127, extra=None):
     """Compare a GPU flush of the dense state S with the oracle's; returns the code
     flips.
 
@@ -54,10 +54,11 @@ def compare_flush(st, ref, what, S, mode=0, Q=127):
     and the subtraction, 8 ulps of |S| + sum_r |uc_r| |kc_r|), the factor of
     eq. 7, c = sqrt(mean_v |R|), moves by |a - b| / (sqrt a + sqrt b) <=
     mean_v dR / (c_gpu + c_ref); the root-mean-square variant by at most
-    sqrt(mean_v dR^2) (triangle inequality)."""
+    sqrt(mean_v dR^2) (triangle inequality). ``extra`` adds to the magnitudes the
+    8-ulp term is taken of, for rounding the GPU did before its flush began."""
     assert_rel(np64(st.vscale), ref["s"], 1e-3, f"{what} vscale")
     c_g, c_r = np64(st.ksmooth), ref["c"]
-    mag = np.abs(S)
+    mag = np.abs(S) if extra is None else np.abs(S) + extra
     dR = np.zeros_like(mag)
     if st.rank > 0:
         ug, kg = np.swapaxes(np64(st.ct_u), -1, -2), np64(st.ct_k)
