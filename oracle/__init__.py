@@ -22,7 +22,11 @@ Every function is written from the two pages that define the method:
 Orientation: every state is ``[d_v][d_k]`` (rows are value channels). The pages
 write ``d_k x d_v``; their formulas are used transposed.
 
-Parity status of each function is stated in its docstring; the only function
-without a pin is ``leapq.toy_error_trend`` (a trend, "parity unpinned").
+Every function here is pinned by a test under tests/test_oracle_*.py against
+what the pages and the mathematics fix (exact rationals, closed forms, special
+cases, identities between separately written forms). What stays "parity
+unpinned" are not functions but trend statements about the method's error (the
+error-ordering tests and the GPU error study), whose page numbers come from a
+simulator the page does not fully specify.
 """
 from . import gdn, gla, kda, kda_leapq, leapq  # noqa: F401

@@ -42,7 +42,10 @@ residual is all zero stores scale 0 and codes 0.
 
 Pins (tests/test_oracle_leapq.py): window 1, rank 0, no smoothing equals the
 per-token rounding of eq. 2 (``per_step_int8``, a separate code path); the eq. 10
-read-out equals the dense eq. 4 state applied to the vector; a rank <= r state
+read-out equals the dense eq. 4 state applied to the vector; ``window_run`` from a
+stored state the grid holds exactly, with an fp64 buffer, equals the exact Gated
+DeltaNet recurrence (read-outs, corrections and rebuild), and from the encoded
+initial state equals ``decode_run``'s windows; a rank <= r state
 leaves a zero residual; Eckart-Young for the SVD mode; per-entry reconstruction
 error within half a step; codes invariant under power-of-two scaling; stored
 bytes 19,456 per 128 x 128 head; the page's BF16/FP16 decay-freezing counts

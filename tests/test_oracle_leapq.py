@@ -308,3 +308,53 @@ def test_error_ordering_trend_at_narrow_widths(bits):
                          smooth_mode=0, bits=bits)
     e_full = rel(leapq.rebuild(r["st"], r["buf"]))
     assert e_step > e_win > e_full, (e_step, e_win, e_full)
+
+
+def test_window_run_from_exact_grid_state_is_the_gdn_recurrence():
+    """Teacher-forced window of the windowed scheme (section "Fix one: leap over a
+    window", eq. 4 and eq. 10). A stored state the INT8 grid holds exactly (codes,
+    scales and smoothing factors chosen, fp16 compensator pieces given) dequantises
+    to S_hat_0 with no rounding, so one window of read-outs from it with an fp64
+    buffer must be the exact Gated DeltaNet recurrence from S_hat_0 (itself pinned by
+    exact rationals in test_oracle_gdn.py), and the eq. 4 rebuild its final state.
+    Fails if u is formed from the state after the token instead of before it, or if
+    alpha is applied twice or not at all in the correction."""
+    rng = np.random.default_rng(31)
+    T, N, d, r = 16, 3, 16, 4
+    q, k, v, a, b = _inputs(rng, T, N, d, amu=2.0)
+    st = dict(Z=rng.integers(-127, 128, (N, d, d)).astype(np.int8),
+              s=rng.uniform(0.5, 2.0, (N, d)), c=rng.uniform(0.25, 1.0, (N, d)),
+              kt=leapq.fp16(rng.standard_normal((N, r, d))),
+              ut=leapq.fp16(rng.standard_normal((N, r, d))))
+    S0 = leapq.dequant(st)
+    o, buf = leapq.window_run(st, q, k, v, a, b, buf_dtype=np.float64)
+    o_ex, S_ex = gdn.gdn_recurrent(_tn(q), _tn(k), _tn(v), a.T, b.T, S0)
+    scale = np.abs(o_ex).max()
+    np.testing.assert_allclose(o, _tn(o_ex), rtol=0, atol=1e-12 * scale)
+    np.testing.assert_allclose(leapq.rebuild(st, buf), S_ex, rtol=0,
+                               atol=1e-12 * np.abs(S_ex).max())
+    # each record's correction is u_t = beta_t (v_t - alpha_t S_{t-1} k_t): recover
+    # S_{t-1} from the recurrence's own prefix and check the buffer term by term
+    for t in range(T):
+        _, S_prev = gdn.gdn_recurrent(_tn(q[:t]), _tn(k[:t]), _tn(v[:t]), a[:t].T, b[:t].T, S0)
+        u_ref = b[t][:, None] * (v[t] - a[t][:, None] * np.einsum("nvk,nk->nv", S_prev, k[t]))
+        np.testing.assert_allclose(buf[t][1], u_ref, rtol=0, atol=1e-12 * np.abs(u_ref).max())
+        np.testing.assert_array_equal(buf[t][2], a[t])
+
+
+def test_window_run_on_the_first_window_equals_decode_run():
+    """The teacher-forced window from the encoded initial state is the first window
+    of the whole windowed run (same fp32 buffer, same flush)."""
+    rng = np.random.default_rng(32)
+    T, N, d = 24, 2, 32
+    q, k, v, a, b = _inputs(rng, T, N, d)
+    S0 = 0.05 * rng.standard_normal((N, d, d))
+    Q0 = rng.standard_normal((d, 4))
+    run = leapq.decode_run(q, k, v, a, b, S0, Q0, window=8, rank=4, collect=True)
+    for w in range(3):
+        sl = slice(8 * w, 8 * w + 8)
+        o, buf = leapq.window_run(run["starts"][w], q[sl], k[sl], v[sl], a[sl], b[sl])
+        np.testing.assert_array_equal(o, run["o"][sl])
+        if w < 2:
+            nxt = leapq.flush(leapq.rebuild(run["starts"][w], buf), Q0, rank=4)
+            np.testing.assert_array_equal(nxt["Z"], run["starts"][w + 1]["Z"])
