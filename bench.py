@@ -196,47 +196,65 @@ def bench_kda(K, W, gen_steps=256):
 def cpu_baseline_decode(inp, target_s=15.0):
     """The fp64 oracle recurrence on a bounded sample of heads (every 8th head of
     the batch, slow and fast heads alike) over all generated steps, reported as
-    stream-tokens per second (head-steps per second / 32 heads). numpy's einsum
-    runs on one thread."""
+    stream-tokens per second (head-steps per second / 32 heads). The sample is cut
+    into slices run by one thread per host core (numpy releases the interpreter
+    lock inside its array loops); ``cores`` is the thread count used."""
+    from concurrent.futures import ThreadPoolExecutor
     from oracle import gdn
     steps = inp["q"].shape[0]
     H = DECODE_H
     N = inp["q"].shape[1]
+    try:
+        threads = len(os.sched_getaffinity(0))
+    except AttributeError:
+        threads = os.cpu_count() or 1
+    threads = max(1, min(16, threads))
+    host = {n: inp[n].to("cpu", torch.float64).numpy() for n in ("q", "k", "v", "alpha", "beta")}
 
-    def run(heads, T):
-        sel = lambda x: x[:T, heads].transpose(0, 1).to("cpu", torch.float64).numpy()
-        args = [sel(inp[n]) for n in ("q", "k", "v", "alpha", "beta")]
-        S0 = inp["S0"][heads].to("cpu", torch.float64).numpy()
+    def one(heads):
+        args = [np.ascontiguousarray(np.swapaxes(host[n][:, heads], 0, 1))
+                for n in ("q", "k", "v", "alpha", "beta")]
+        gdn.gdn_recurrent(*args, inp["S0"][heads].to("cpu", torch.float64).numpy())
+
+    def run(heads):
+        parts = [p for p in np.array_split(heads, threads * 2) if len(p)]
         t0 = time.perf_counter()
-        gdn.gdn_recurrent(*args, S0)
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(one, parts))
         return time.perf_counter() - t0
 
-    probe = torch.arange(0, N, 8)[:16]       # calibration at the full step count
-    per_head_step = run(probe, steps) / (len(probe) * steps)
-    n_heads = int(min(N // 8, max(64, target_s / max(per_head_step * steps, 1e-12))))
-    heads = torch.arange(0, N, 8)[:n_heads]
-    dt = run(heads, steps)
-    return dict(value=n_heads * steps / dt / H, unit="tokens/s", cores=1, kind="oracle",
+    sample = np.arange(0, N, 8)
+    probe = sample[:4 * threads]                       # calibration at the full step count
+    per_head = run(probe) / len(probe)
+    n_heads = int(min(len(sample), max(8 * threads, target_s / max(per_head, 1e-12))))
+    heads = sample[:n_heads]
+    dt = run(heads)
+    return dict(value=n_heads * steps / dt / H, unit="tokens/s", cores=threads, kind="oracle",
                 sample=f"{n_heads} heads (every 8th of 16,384) x {steps} decode steps of the "
-                       f"B=512 H=32 workload in {dt:.1f} s; stream-tokens/s = head-steps/s / 32")
+                       f"B=512 H=32 workload in {dt:.1f} s on {threads} threads; "
+                       f"stream-tokens/s = head-steps/s / 32")
 
 
 # ------------------------------------------------------------------- LeapQuant
 
-def leapq_bytes_per_head_window(W=16, rank=4, kda=False):
-    """Algorithmic bytes of one head over one window (W decode steps + flush).
-    Step at position m reads codes 16,384 + scales 1,024 + compensators 4*r*128
-    + m buffered records (k, u fp32 and a) + q, k, v (bf16) and alpha, beta; it
-    writes one record and o (bf16). The flush reads the stored state and the W
-    records and writes the stored state. With ``kda`` every decay is a 128-long
-    fp32 vector (the token's alpha and each record's)."""
+def leapq_bytes_per_head_window(W=16, rank=4, kda=False, fused=True):
+    """Algorithmic bytes of one head over one window. A decode step at position m
+    reads codes 16,384 + scales 1,024 + compensators 4*r*128 + m buffered records
+    (k, u fp32 and a) + q, k, v (bf16) and alpha, beta; it writes one record and o
+    (bf16). With ``fused`` (the window's last token decoded inside its flush) the
+    window is W - 1 such steps and one launch that reads the stored state, the
+    W - 1 records and the token's inputs and writes o and the stored state; without
+    it, W steps and a flush that reads the stored state and the W records and
+    writes the stored state. With ``kda`` every decay is a 128-long fp32 vector
+    (the token's alpha and each record's)."""
     stored = D * D + 2 * D * 4 + rank * 2 * D * 2          # 19,456 at r = 4
     a_b = D * 4 if kda else 4
     rec = 2 * D * 4 + a_b                                 # 1,028 (KDA 1,536)
     io_in, io_out = 3 * D * 2 + a_b + 4, D * 2
-    steps = sum(stored + m * rec + io_in + rec + io_out for m in range(W))
-    flush = stored + W * rec + stored
-    return steps + flush
+    step = lambda m: stored + m * rec + io_in + rec + io_out
+    if fused:
+        return sum(step(m) for m in range(W - 1)) + stored + (W - 1) * rec + io_in + io_out + stored
+    return sum(step(m) for m in range(W)) + stored + W * rec + stored
 
 
 def bench_leapq(tokens=4096, B=DECODE_B, H=DECODE_H, W=16, rank=4, kda=False):
@@ -277,6 +295,7 @@ def bench_leapq(tokens=4096, B=DECODE_B, H=DECODE_H, W=16, rank=4, kda=False):
     ms_win2, _ = timed(run_window_two_launch, n_win, 1)
     ms_step = ms_win / W
     bpw = leapq_bytes_per_head_window(W, rank, kda) * N
+    bpw2 = leapq_bytes_per_head_window(W, rank, kda, fused=False) * N
     # per-kernel split from events around each launch of one window
     s = torch.cuda.current_stream()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(W + 2)]
@@ -302,7 +321,8 @@ def bench_leapq(tokens=4096, B=DECODE_B, H=DECODE_H, W=16, rank=4, kda=False):
                ms_per_step=ms_step, tokens_per_s=B / (ms_step * 1e-3),
                bytes_per_head_step=bpw / N / W, achieved_gbs=bpw / (ms_win * 1e-3) / 1e9,
                decode_kernel_ms=dec_ms, flush_kernel_ms=flush_ms, decode_flush_kernel_ms=last_ms,
-               two_launch_ms_per_step=ms_win2 / W, wall_s=wall, decode_kernel_gbs=None)
+               two_launch_ms_per_step=ms_win2 / W, two_launch_bytes_per_head_step=bpw2 / N / W,
+               two_launch_achieved_gbs=bpw2 / (ms_win2 * 1e-3) / 1e9, wall_s=wall, decode_kernel_gbs=None)
     res["frac_hbm"] = res["achieved_gbs"] / PEAK_HBM_GBS
     del inp
     return res
@@ -584,14 +604,22 @@ def counter_traffic(kernel):
 # ------------------------------------------------------------------- ceilings
 
 def measure_ceilings(reps=20):
-    """Ceilings measured on this GPU, reported beside the published peaks: a plain
-    2 GiB device-to-device copy (HBM read + write) and an 8192^3 bf16 matrix product
-    through torch's BLAS (dense MFMA). Neither is part of the hot path."""
+    """Ceilings measured on this GPU, reported beside the published peaks. HBM: the
+    library's streaming kernel (gdnrt_hbm_stream: 16-byte non-temporal loads and
+    stores, one read and one write of every byte) over 2 GiB of fp32, in place (as the
+    decode updates its state) and as a copy, 1, 2 and 4 pieces per thread; the best
+    rate is the ceiling. MFMA: an 8192^3 bf16 matrix product through torch's BLAS.
+    Neither is part of the hot path."""
     n = 1 << 29
     src = torch.ones(n, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
+    sweep = {}
+    for vec in (1, 2, 4):
+        for name, d in (("inplace", src), ("copy", dst)):
+            ms, _ = timed(lambda i: m.hbm_stream(d, src, vec), reps, 3)
+            sweep[f"{name}_vec{vec}"] = 2 * n * 4 / (ms * 1e-3) / 1e9
     ms, _ = timed(lambda i: dst.copy_(src), reps, 3)
-    copy_gbs = 2 * n * 4 / (ms * 1e-3) / 1e9
+    torch_copy_gbs = 2 * n * 4 / (ms * 1e-3) / 1e9
     del src, dst
     M = 8192
     g = torch.Generator(device="cuda").manual_seed(7)
@@ -601,8 +629,12 @@ def measure_ceilings(reps=20):
     gemm_tflops = 2 * M ** 3 / (ms * 1e-3) / 1e12
     del a, b
     torch.cuda.empty_cache()
-    return {"hbm_copy_gbs": copy_gbs, "bf16_gemm_tflops": gemm_tflops,
-            "how": "torch copy_ of 2 GiB fp32 (bytes read + written); torch.matmul 8192^3 bf16",
+    best = max(sweep, key=sweep.get)
+    return {"hbm_stream_gbs": sweep[best], "hbm_stream_best": best, "hbm_stream_sweep": sweep,
+            "torch_copy_gbs": torch_copy_gbs, "bf16_gemm_tflops": gemm_tflops,
+            "how": "gdnrt_hbm_stream over 2 GiB fp32 (bytes read + written; best of in-place / copy x "
+                   "1, 2, 4 pieces per thread); torch copy_ of the same for reference; torch.matmul "
+                   "8192^3 bf16 (hipBLASLt), not a dense-MFMA ceiling but what a library GEMM reaches",
             "published_hbm_gbs": PEAK_HBM_GBS, "published_bf16_tflops": PEAK_BF16_TFLOPS}
 
 
@@ -743,12 +775,13 @@ def main():
     ceil = None
     if not args.no_ceilings:
         ceil = measure_ceilings()
-        log(f"[ceilings] copy {ceil['hbm_copy_gbs']:.0f} GB/s, bf16 GEMM {ceil['bf16_gemm_tflops']:.0f} TFLOP/s")
+        log(f"[ceilings] HBM stream {ceil['hbm_stream_gbs']:.0f} GB/s ({ceil['hbm_stream_best']}), "
+            f"torch copy {ceil['torch_copy_gbs']:.0f} GB/s, bf16 GEMM {ceil['bf16_gemm_tflops']:.0f} TFLOP/s")
         for r in out_rows.values():
             if "achieved_gbs" in r:
-                r["frac_hbm_of_measured_copy"] = r["achieved_gbs"] / ceil["hbm_copy_gbs"]
+                r["frac_hbm_of_measured_stream"] = r["achieved_gbs"] / ceil["hbm_stream_gbs"]
             if "tflops" in r:
-                r["frac_mfma_of_measured_gemm"] = r["tflops"] / ceil["bf16_gemm_tflops"]
+                r["frac_of_library_gemm"] = r["tflops"] / ceil["bf16_gemm_tflops"]
     line = {
         "metric": "GDN decode tokens/s at B=512 (one layer, 32 heads, d=128)",
         "value": res["tokens_per_s"] if res else None,

@@ -31,6 +31,7 @@ from .binding import (  # noqa: F401
     gla_shard_decay,
     gla_shard_local,
     gla_shard_output_correct,
+    hbm_stream,
     kda_chunk_fwd,
     kda_chunk_workspace,
     kda_decode_step,

@@ -62,6 +62,7 @@ SIGNATURES = {
                                _c_int),
     "kda_leapq_window_flush": ([ctypes.POINTER(LeapqState), _c_int, _vp, _vp, _c_int, _c_int, _vp, _vp],
                                _c_int),
+    "gdnrt_hbm_stream": ([_vp, _vp, ctypes.c_size_t, _c_int, ctypes.c_float, _vp], _c_int),
     "gdnrt_last_error": ([], ctypes.c_char_p),
 }
 
@@ -571,3 +572,13 @@ def kda_leapq_decode_flush(st: LeapqBuffers, q, k, v, alpha, beta, q0, o=None, i
     if not st.kda:
         raise ValueError("kda_leapq_decode_flush: allocate the buffers with kda=True")
     return _decode_flush("kda_leapq_decode_flush", st, q, k, v, alpha, beta, o, (st.N, D), q0, iters, smooth_mode)
+
+
+def hbm_stream(dst, src, vec=1, scale=1.0):
+    """Streaming read + write of an fp32 array (``dst`` may be ``src``): the HBM
+    ceiling kernel. Not a step of the method."""
+    _need(src, "src", torch.float32)
+    _need(dst, "dst", torch.float32, src.shape)
+    _check("gdnrt_hbm_stream", lib().gdnrt_hbm_stream(_ptr(dst), _ptr(src), src.numel(), vec,
+                                                      float(scale), _stream()))
+    return dst

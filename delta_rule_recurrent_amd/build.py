@@ -32,25 +32,47 @@ def sources():
     return src
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into libgdnrt.so (always recompiles)."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
-           "-fvisibility=hidden", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           # MFMA accumulators in ordinary VGPRs: kernels that also work on the
-           # accumulators with VALU code then hold one copy instead of an AGPR copy
-           # plus a VGPR copy
-           "-mllvm", "-amdgpu-mfma-vgpr-form",
-           "-I", os.path.join(ROOT, "include"), "-o", tmp] + sources()
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _flags():
+    return ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",
+            "-fvisibility=hidden", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMA accumulators in ordinary VGPRs: kernels that also work on the
+            # accumulators with VALU code then hold one copy instead of an AGPR copy
+            # plus a VGPR copy
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
+            "-I", os.path.join(ROOT, "include")]
+
+
+def _run(cmd):
     r = subprocess.run(cmd, cwd=ROOT, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
-    if err.strip() and verbose:
-        print(err, file=sys.stderr)
+    return r.returncode, err
+
+
+def build(verbose: bool = False, jobs: int | None = None) -> str:
+    """Compile every HIP source into libgdnrt.so (always recompiles): one object
+    per source, compiled in parallel, then one shared-library link."""
+    from concurrent.futures import ThreadPoolExecutor
+    srcs = sources()
+    objdir = os.path.join(ROOT, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, os.path.basename(s) + ".o") for s in srcs]
+    cmds = [[hipcc()] + _flags() + ["-c", s, "-o", o] for s, o in zip(srcs, objs)]
+    if verbose:
+        for c in cmds:
+            print(" ".join(c), flush=True)
+    jobs = jobs or min(len(cmds), max(1, min(16, os.cpu_count() or 1)))
+    with ThreadPoolExecutor(jobs) as ex:
+        results = list(ex.map(_run, cmds))
+    for (rc, err), s in zip(results, srcs):
+        if rc != 0:
+            raise RuntimeError(f"hipcc failed on {os.path.basename(s)} ({rc}):\n{err}")
+        if err.strip() and verbose:
+            print(err, file=sys.stderr)
+    tmp = LIB + ".tmp"
+    rc, err = _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs)
+    if rc != 0:
+        raise RuntimeError(f"link failed ({rc}):\n{err}")
     os.replace(tmp, LIB)
     return LIB
 

@@ -335,7 +335,8 @@ struct alignas(16) G1Smem {
   uint16_t S[kD * gdb::PT], D[kD * gdb::PT];                                 // S_b, dS_a [v][c]
   uint16_t U[kChunk * gdb::PT];                                              // [t][v]
   uint16_t A[kChunk * gdb::PA];                                              // A, then dA' [r][j]
-  float lg[kChunk], g[kChunk], kd[kChunk], qdq[kChunk];
+  float lg[kChunk], g[kChunk], kd[kChunk];
+  float qdq[2][kChunk];   // q_t . dq_t over key blocks 0-3 and 4-7 (the two wave halves)
 };
 
 __global__ __launch_bounds__(512) void gdn_bwd_grad1_kernel(
@@ -369,7 +370,6 @@ __global__ __launch_bounds__(512) void gdn_bwd_grad1_kernel(
     sm.lg[lane] = lgv;
     sm.g[lane] = __expf(lgv);
     sm.kd[lane] = __expf(lC - lgv);
-    sm.qdq[lane] = 0.f;
   }
   lds_barrier();
 
@@ -456,6 +456,7 @@ __global__ __launch_bounds__(512) void gdn_bwd_grad1_kernel(
 
   // ---- dq = dA' K + diag(g) dO S_b;  dK1 = dA'^T Q + diag(g_C/g) U dS_a
   float* dK1 = ws.dK1 + (size_t)cid * C * kD;
+  float qacc[4] = {0.f, 0.f, 0.f, 0.f};   // this wave's share of q.dq, in key-block order
 #pragma unroll 1
   for (int u = 0; u < 4; ++u) {
     const int kb = (w >> 2) * 4 + u;
@@ -479,12 +480,15 @@ __global__ __launch_bounds__(512) void gdn_bwd_grad1_kernel(
       const float gq = a1[i] + sm.g[r] * a2[i];
       dq[(tok0 + r) * kD + col] = f32_to_bf16(gq);
       dK1[r * kD + col] = a3[i] + sm.kd[r] * a4[i];
-      const float s = sum16(bf16_to_f32(sm.Q[r * PT + col]) * gq);
-      if (l16 == 0) atomicAdd(&sm.qdq[r], s);
+      qacc[i] += sum16(bf16_to_f32(sm.Q[r * PT + col]) * gq);
     }
   }
+  // fixed summation order (no atomics): each half of the waves writes its own partial
+  if (l16 == 0)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sm.qdq[w >> 2][16 * rb + 4 * lq + i] = qacc[i];
   lds_barrier();
-  if (tid < C) ws.qdq[(size_t)cid * C + tid] = sm.qdq[tid];
+  if (tid < C) ws.qdq[(size_t)cid * C + tid] = sm.qdq[0][tid] + sm.qdq[1][tid];
 }
 
 // ------------------------------------------------------------------ gradients, part 2
@@ -497,7 +501,10 @@ struct alignas(16) G2Smem {
   uint16_t S[kD * gdb::PT];        // S_b [v][c], then T^T dW [t][c] and T^T dU [t][v]
   uint16_t T[kChunk * gdb::PA];    // (I + L)^-1 [r][j]
   uint16_t L[kChunk * gdb::PA];    // dL o (g_r/g_j) o beta_r and its transpose [r][j]
-  float lg[kChunk], g[kChunk], bt[kChunk], dbW[kChunk], dbU[kChunk], dbL[kChunk];
+  float lg[kChunk], g[kChunk], bt[kChunk];
+  // partial sums in a fixed order (no atomics): dbW, dbU per wave half, dbL per
+  // column block of the strict lower part
+  float dbW[2][kChunk], dbU[2][kChunk], dbL[4][kChunk];
 };
 
 __global__ __launch_bounds__(512) void gdn_bwd_grad2_kernel(
@@ -542,9 +549,8 @@ __global__ __launch_bounds__(512) void gdn_bwd_grad2_kernel(
     sm.lg[lane] = lgv;
     sm.g[lane] = __expf(lgv);
     sm.bt[lane] = beta[tok0 + lane];
-    sm.dbW[lane] = 0.f;
-    sm.dbU[lane] = 0.f;
-    sm.dbL[lane] = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sm.dbL[c][lane] = 0.f;
   }
   lds_barrier();
 
@@ -564,6 +570,7 @@ __global__ __launch_bounds__(512) void gdn_bwd_grad2_kernel(
 
   // ---- T^T dW and T^T dU; dv = beta o T^T dU; dK_W = beta g o T^T dW (kept)
   f32x4 kw[4];
+  float su_acc[4] = {0.f, 0.f, 0.f, 0.f}, sw_acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int cb = (w >> 2) * 4 + u;
@@ -583,14 +590,16 @@ __global__ __launch_bounds__(512) void gdn_bwd_grad2_kernel(
       XU[r * PT + col] = f32_to_bf16(xu[i]);
       dv[(tok0 + r) * kD + col] = f32_to_bf16(sm.bt[r] * xu[i]);
       kw[u][i] = sm.bt[r] * sm.g[r] * xw[i];
-      const float su = sum16(xu[i] * bf16_to_f32(sm.V[r * PT + col]));
-      const float sw = sum16(xw[i] * bf16_to_f32(sm.K[r * PT + col]));
-      if (l16 == 0) {
-        atomicAdd(&sm.dbU[r], su);
-        atomicAdd(&sm.dbW[r], sw);
-      }
+      su_acc[i] += sum16(xu[i] * bf16_to_f32(sm.V[r * PT + col]));
+      sw_acc[i] += sum16(xw[i] * bf16_to_f32(sm.K[r * PT + col]));
     }
   }
+  if (l16 == 0)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sm.dbU[w >> 2][16 * rb + 4 * lq + i] = su_acc[i];
+      sm.dbW[w >> 2][16 * rb + 4 * lq + i] = sw_acc[i];
+    }
   lds_barrier();
 
   // ---- dL = -(T^T dW W^T + T^T dU U~^T) on the strict lower part; with the Gram
@@ -620,7 +629,7 @@ __global__ __launch_bounds__(512) void gdn_bwd_grad2_kernel(
         sm.L[j * PA + r] = xb;
       }
       const float sy = sum16(y);
-      if (l16 == 0) atomicAdd(&sm.dbL[r], sy);
+      if (l16 == 0) sm.dbL[cb][r] = sy;   // one pair (ab, cb) per row block and column block
     }
   }
   lds_barrier();
@@ -644,8 +653,10 @@ __global__ __launch_bounds__(512) void gdn_bwd_grad2_kernel(
   lds_barrier();
   if (w == 0) {
     const int t = lane;
-    dbeta[tok0 + t] = sm.g[t] * sm.dbW[t] + sm.dbU[t] + sm.dbL[t];
-    const float dB = ws.qdq[(size_t)cid * C + t] - sm.bt[t] * sm.dbU[t];
+    const float dbU = sm.dbU[0][t] + sm.dbU[1][t], dbW = sm.dbW[0][t] + sm.dbW[1][t];
+    const float dbL = (sm.dbL[0][t] + sm.dbL[1][t]) + (sm.dbL[2][t] + sm.dbL[3][t]);
+    dbeta[tok0 + t] = sm.g[t] * dbW + dbU + dbL;
+    const float dB = ws.qdq[(size_t)cid * C + t] - sm.bt[t] * dbU;
     const float off = sum64(t < 32 ? ws.bnd[(size_t)cid * 32 + t] : 0.f);
     // reverse inclusive sum inside the chunk: lane l scans token 63 - l
     const float rs = wave_scan(__shfl(dB, C - 1 - lane));

@@ -1043,11 +1043,25 @@ int decode_flush(const char* fn, const leapq_state* st, const void* q, const voi
     return set_error(GDNRT_EALIGN, "%s: q, k, v, o, alpha, beta must be 4-byte aligned", fn);
   const size_t es = io == GDNRT_F32 ? 4 : 2;
   const size_t N = st->N, nIO = N * kD * es, nB = N * st->window * kD * 4;
-  if (overlaps(o, nIO, q, nIO) || overlaps(o, nIO, k, nIO) || overlaps(o, nIO, v, nIO) ||
-      overlaps(o, nIO, st->buf_k, nB) || overlaps(o, nIO, st->buf_u, nB) ||
-      overlaps(o, nIO, st->codes, N * kD * kD) || overlaps(o, nIO, st->ct_u, N * st->rank * kD * 2) ||
-      overlaps(o, nIO, st->ct_k, N * st->rank * kD * 2))
-    return set_error(GDNRT_EINVAL, "%s: o overlaps another buffer", fn);
+  const size_t nA = KDA ? N * kD * 4 : N * 4, nBA = KDA ? nB : N * st->window * 4;
+  const size_t nCT = N * st->rank * kD * 2, nV = N * kD * 4;
+  // o is written by every block; the stored state is rewritten by each head's block while
+  // the other blocks still read their token inputs, so no input may share a byte with o or
+  // with the state the launch writes (a cross-block race otherwise).
+  struct Span { const void* p; size_t n; };
+  const Span written[] = {{o, nIO}, {st->codes, N * kD * kD}, {st->vscale, nV}, {st->ksmooth, nV},
+                          {st->ct_k, nCT}, {st->ct_u, nCT}};
+  const Span read[] = {{q, nIO}, {k, nIO}, {v, nIO}, {alpha, nA}, {beta, N * 4},
+                       {st->buf_k, nB}, {st->buf_u, nB}, {st->buf_a, nBA}};
+  for (const Span& r : read)
+    if (overlaps(o, nIO, r.p, r.n)) return set_error(GDNRT_EINVAL, "%s: o overlaps an input", fn);
+  for (int w = 1; w < 6; ++w)
+    if (overlaps(o, nIO, written[w].p, written[w].n))
+      return set_error(GDNRT_EINVAL, "%s: o overlaps the stored state", fn);
+  for (int i = 0; i < 5; ++i)        // the token's inputs (the buffer is the state's own)
+    for (int w = 1; w < 6; ++w)
+      if (overlaps(read[i].p, read[i].n, written[w].p, written[w].n))
+        return set_error(GDNRT_EINVAL, "%s: a token input overlaps the stored state", fn);
   return window_flush<KDA>(fn, st, st->window - 1, nullptr, q0, iters, smooth_mode, nullptr, stream,
                            FlushToken{q, k, v, alpha, beta, o, io});
 }

@@ -471,6 +471,17 @@ GDNRT_API int kda_leapq_decode_flush(const leapq_state* st, const void* q, const
                       const void* v, const float* alpha, const float* beta, void* o,
                       int io, const float* q0, int iters, int smooth_mode, void* stream);
 
+/*
+ * Measurement aid, not a step of the method: one streaming read and write of n fp32
+ * values, dst[i] = scale * src[i] (dst may equal src: an in-place pass, as the decode
+ * updates its state), with 16-byte non-temporal loads and stores, vec (1, 2 or 4)
+ * pieces per thread and 256-thread blocks. Its rate is the HBM ceiling measured on the
+ * device, reported beside the published peak. dst, src 16-byte aligned; n a multiple
+ * of 4; partial overlap returns GDNRT_EINVAL.
+ */
+GDNRT_API int gdnrt_hbm_stream(float* dst, const float* src, size_t n, int vec, float scale,
+                               void* stream);
+
 /* Message for the calling thread's last non-OK status ("" if none). */
 GDNRT_API const char* gdnrt_last_error(void);
 

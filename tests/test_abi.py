@@ -174,6 +174,22 @@ def test_leapq_decode_flush_validation(lib):
         assert f(ctypes.byref(st), q, k, v, a, b, ctypes.c_void_p((1 << 40) + 2), 1, q0, 1, 0, None) == EALIGN
         assert f(ctypes.byref(st), q, k, v, a, b, q, 1, q0, 1, 0, None) == EINVAL     # o is q
         assert name in _err(lib)
+        # o against the state the launch writes, and against the buffer it reads
+        far = dict(codes=1 << 41, vscale=(1 << 41) + (1 << 22), ksmooth=(1 << 41) + (2 << 22),
+                   ct_k=(1 << 41) + (3 << 22), ct_u=(1 << 41) + (4 << 22), buf_k=(1 << 41) + (5 << 22),
+                   buf_u=(1 << 41) + (6 << 22), buf_a=(1 << 41) + (7 << 22))
+        for field in ("vscale", "ksmooth", "buf_a", "ct_u"):
+            kw = dict(far)
+            kw[field] = 1 << 40
+            assert f(ctypes.byref(_state(lib, **kw)), q, k, v, a, b, o, 1, q0, 1, 0, None) == EINVAL, field
+            assert "o overlaps" in _err(lib)
+        # a token input inside the stored state the launch rewrites (a cross-block race)
+        for field, arg in (("codes", 0), ("vscale", 4), ("ksmooth", 3), ("ct_k", 1), ("ct_u", 2)):
+            kw = dict(far)
+            kw[field] = (arg + 1) << 20
+            assert f(ctypes.byref(_state(lib, **kw)), q, k, v, a, b, o, 1, q0, 1, 0, None) == EINVAL, field
+            assert "token input overlaps" in _err(lib)
+        assert f(ctypes.byref(_state(lib, N=0, **far)), q, k, v, a, b, o, 1, q0, 1, 0, None) == OK
         assert f(ctypes.byref(_state(lib, N=0)), q, k, v, a, b, o, 1, q0, 1, 0, None) == OK
 
 
@@ -268,3 +284,15 @@ def test_gla_shard_bwd_state_validation(lib):
     assert f(q, k, g, dO, None, 2, 128, 128, 128, 64, 1, ws, need, None) == EINVAL
     assert f(q, k, g, dO, ctypes.c_void_p((1 << 30) + 4096), 2, 128, 128, 128, 64, 1, ws, need, None) == EINVAL
     assert f(q, k, g, dO, dS0, 0, 128, 128, 128, 64, 1, ws, need, None) == OK
+
+
+def test_hbm_stream_validation(lib):
+    f = lib.gdnrt_hbm_stream
+    p = ctypes.c_void_p(4096)
+    assert f(p, p, 0, 1, 1.0, None) == OK                                      # empty
+    assert f(None, p, 16, 1, 1.0, None) == EINVAL
+    assert f(p, p, 18, 1, 1.0, None) == ESHAPE                                 # n % 4
+    assert f(p, p, 16, 3, 1.0, None) == ESHAPE                                 # vec
+    assert f(ctypes.c_void_p(4100), p, 16, 1, 1.0, None) == EALIGN
+    assert f(ctypes.c_void_p(4096 + 32), p, 64, 1, 1.0, None) == EINVAL        # partial overlap
+    assert "gdnrt_hbm_stream" in _err(lib)

@@ -118,3 +118,31 @@ def test_degenerate_cases():
     mask = torch.ones(8, dtype=torch.bool)
     mask[3] = False
     assert torch.isfinite(S[mask]).all() and torch.isfinite(o[mask]).all()
+
+
+def test_erase_and_replace_and_carry():
+    """The page's special cases on the GPU: beta = 1 with a unit key stores v_t along
+    k_t exactly (S_t k_t = v_t, whatever was there: "erase and replace"), whatever
+    the decay; alpha = 1 with beta = 0 leaves the state unchanged and reads it out,
+    o_t = S q_t. fp32 throughout, 1e-4 of max|ref|."""
+    dev = need_gpu()
+    say("gdn_decode_step: beta = 1 unit key; alpha = 1 beta = 0")
+    inp = synth.gdn_decode(B=8, H=4, steps=3, device=dev, io=torch.float32)
+    N = 32
+    S0 = inp["S0"].clone()
+    k = inp["k"][0].double()
+    k = (k / k.norm(dim=-1, keepdim=True)).float()          # unit norm in fp32
+    q, v, a = inp["q"][0], inp["v"][0], inp["alpha"][0]
+    S = S0.clone()
+    m.gdn_decode_step(S, q[:, None].contiguous(), k[:, None].contiguous(), v[:, None].contiguous(),
+                      a[:, None].contiguous(), torch.ones((N, 1), device=dev))
+    torch.cuda.synchronize()
+    Sk = torch.einsum("nvk,nk->nv", S.double(), k.double())
+    assert_rel(np64(Sk), np64(v), TOL_F32, "S_t k_t = v_t")
+    # alpha = 1, beta = 0: state bitwise unchanged, o = S q
+    S = S0.clone()
+    o = m.gdn_decode_step(S, q[:, None].contiguous(), k[:, None].contiguous(), v[:, None].contiguous(),
+                          torch.ones((N, 1), device=dev), torch.zeros((N, 1), device=dev))
+    torch.cuda.synchronize()
+    assert torch.equal(S, S0)
+    assert_rel(np64(o[:, 0]), np64(torch.einsum("nvk,nk->nv", S0.double(), q.double())), TOL_F32, "o = S q")

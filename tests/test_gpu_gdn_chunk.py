@@ -90,3 +90,29 @@ def test_workspace_and_shape_errors():
     with pytest.raises(m.GdnrtError) as ei:
         m.gdn_chunk_fwd(*(bad[n] for n in ("q", "k", "v", "alpha", "beta")))
     assert ei.value.status == 2
+
+
+@pytest.mark.parametrize("case", ["no_decay_no_write", "fast_decay_full_write"])
+def test_degenerate_gates(case):
+    """alpha = 1 with beta = 0 on alternate tokens (the state carried unchanged
+    through every other token) and alpha down to 0.02 with beta = 1 (the state forgets
+    within a few tokens; each write replaces the value along k). The chunk form's
+    decay ratios g_r / g_j span 0.02^63 within a chunk there."""
+    dev = need_gpu()
+    say(f"gdn_chunk_fwd: degenerate gates, {case}")
+    N, T = 4, 192
+    inp = synth.gdn_prefill(B=N, H=1, T=T, device="cpu", seed=1180, S0_std=0.05)
+    if case == "no_decay_no_write":
+        inp["alpha"] = torch.ones_like(inp["alpha"])
+        inp["beta"][:, ::2] = 0.0
+    else:
+        g = torch.Generator().manual_seed(1181)
+        inp["alpha"] = 0.02 + 0.5 * torch.rand(inp["alpha"].shape, generator=g)
+        inp["beta"] = torch.ones_like(inp["beta"])
+    d = {k_: t.to(dev) for k_, t in inp.items()}
+    o, ST = m.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"])
+    torch.cuda.synchronize()
+    o_ref, S_ref = _ref(inp, slice(None))
+    e1 = assert_rel(np64(o), o_ref, TOL, "o")
+    e2 = assert_rel(np64(ST), S_ref, TOL, "S_T")
+    say(f"  o err {e1:.2e}  S err {e2:.2e}")

@@ -14,7 +14,7 @@ import delta_rule_recurrent_amd as m
 from delta_rule_recurrent_amd import synth
 from oracle import kda, kda_leapq, leapq
 from helpers import assert_rel, need_gpu, np64, rel_err, say
-from test_gpu_leapq import buffer, compare_flush, stored
+from test_gpu_leapq import buffer, compare_flush, rebuild_error, stored
 
 pytestmark = pytest.mark.gpu
 
@@ -57,9 +57,10 @@ def test_teacher_forced_windows(io):
         assert np.array_equal(np64(st.buf_a).transpose(1, 0, 2), np64(inp["alpha"][sl]))
         S_w = kda_leapq.rebuild(start, buffer(st, W))
         ref = leapq.flush(S_w, np64(inp["Q0"]), rank=4)
+        dS = rebuild_error(start, buffer(st, W), kda=True)
         m.kda_leapq_window_flush(st, Q0)
         torch.cuda.synchronize()
-        flips = compare_flush(st, ref, f"window {w} flush", S_w)
+        flips, _, _ = compare_flush(st, ref, f"window {w} flush", S_w, dS=dS)
         say(f"  window {w}: u err {rel_err(u_gpu, u_ref):.2e}, code flips {flips}")
 
 
@@ -81,7 +82,7 @@ def test_flush_mid_window():
     ref = leapq.flush(S_w, np64(inp["Q0"]), rank=4)
     m.kda_leapq_window_flush(st, Q0)
     torch.cuda.synchronize()
-    compare_flush(st, ref, "mid-window flush", S_w)
+    compare_flush(st, ref, "mid-window flush", S_w, dS=rebuild_error(start, buffer(st, m_), kda=True))
 
 
 def test_free_running_full_head_count():

@@ -10,7 +10,7 @@ import torch
 
 import delta_rule_recurrent_amd as m
 from delta_rule_recurrent_amd import synth
-from oracle import gdn, leapq
+from oracle import gdn, kda_leapq, leapq
 from helpers import assert_rel, need_gpu, np64, rel_err, say
 
 pytestmark = pytest.mark.gpu
@@ -39,41 +39,88 @@ def buffer(st, pos, heads=None):
     return [(bk[:, j], bu[:, j], ba[:, j]) for j in range(pos)]
 
 
-def compare_flush(st, ref, what, S, mode=0, Q=127, extra=None):
-    """Compare a GPU flush of the dense state S with the oracle's; returns the code
-    flips.
+EPS = 2.0 ** -24   # unit roundoff of fp32
 
-    The compensator fit runs the same procedure in fp32 on the GPU and fp64 in
-    the oracle; on states with large outliers its Gram matrix is ill-conditioned
-    (kappa ~ 1e5), so a compensator entry may land one fp16 step away and the
-    residual, scales and codes follow. Checked: pieces within 2 fp16 steps of
-    each vector's largest entry; scales 1e-3 of their maximum; every code within
-    one step of the oracle's; smoothing factors within what the difference of the
-    two sets of pieces does to the residual. With dR bounding |R_gpu - R_ref| per
-    entry (the two sets of subtracted pieces, plus fp32 rounding of the rebuild
-    and the subtraction, 8 ulps of |S| + sum_r |uc_r| |kc_r|), the factor of
-    eq. 7, c = sqrt(mean_v |R|), moves by |a - b| / (sqrt a + sqrt b) <=
-    mean_v dR / (c_gpu + c_ref); the root-mean-square variant by at most
-    sqrt(mean_v dR^2) (triangle inequality). ``extra`` adds to the magnitudes the
-    8-ulp term is taken of, for rounding the GPU did before its flush began."""
-    assert_rel(np64(st.vscale), ref["s"], 1e-3, f"{what} vscale")
+
+def rebuild_error(start, buf, kda=False):
+    """Per-entry bound on |S_gpu - S_ref| for the GPU's fp32 eq. 4 rebuild of the
+    stored state ``start`` and the records ``buf``, against the oracle's fp64 rebuild
+    of the same bits. With m records and r compensators, each term's fp32 factors
+    carry at most m + 4 roundings (the suffix product of the decays, the scale
+    products, the value times its decay) and each of the r + m accumulations one
+    rounding of a partial sum; every such error is at most one ulp of M, the rebuild
+    with every term taken in absolute value. Bound: (2 m + r + 6) eps M."""
+    absst = dict(Z=np.abs(start["Z"].astype(np.int32)), s=np.abs(start["s"]), c=np.abs(start["c"]),
+                 kt=np.abs(start["kt"]), ut=np.abs(start["ut"]), Q=start.get("Q", 127))
+    absbuf = [(np.abs(kj), np.abs(uj), aj) for (kj, uj, aj) in buf]
+    M = (kda_leapq if kda else leapq).rebuild(absst, absbuf)
+    n = 2 * len(buf) + start["kt"].shape[1] + 6
+    return n * EPS * M
+
+
+def token_update_error(S_prev, dS_prev, k, v, a, b):
+    """Per-entry bound on the fp32 error of the window's last token applied inside the
+    fused flush, S = S_prev Diag(a) + u k^T with u = b (v - S_prev (a o k)), given the
+    bound dS_prev on the rebuilt S_prev. The 128-term dot product is summed in 32-term
+    runs and two exchanges (at most 34 roundings of its terms' magnitudes), u takes two
+    more roundings, the update one product and one fused add. k, v [N][d], a [N] (one
+    decay) or [N][d] (per channel), b [N]."""
+    av = a[:, None] * np.ones_like(k) if a.ndim == 1 else a
+    ak = np.abs(av * k)
+    sk_abs = np.einsum("nvk,nk->nv", np.abs(S_prev), ak)
+    dsk = np.einsum("nvk,nk->nv", dS_prev, ak) + 36 * EPS * sk_abs
+    u = b[:, None] * (v - np.einsum("nvk,nk->nv", S_prev, av * k))
+    du = np.abs(b)[:, None] * dsk + 2 * EPS * np.abs(b)[:, None] * (np.abs(v) + sk_abs)
+    return (av[:, None, :] * dS_prev + du[:, :, None] * np.abs(k)[:, None, :]
+            + 2 * EPS * (av[:, None, :] * np.abs(S_prev) + np.abs(u)[:, :, None] * np.abs(k)[:, None, :]))
+
+
+def compare_flush(st, ref, what, S, mode=0, Q=127, dS=None):
+    """Compare a GPU flush with the oracle's flush of the dense state S; returns
+    (code flips, largest code difference, codes differing by more than one step).
+
+    ``dS`` bounds |S_gpu - S| per entry for the state the GPU flushed (None: the GPU
+    was handed S itself). The compensator fit runs the same procedure in fp32 on the
+    GPU and fp64 in the oracle; on outlier states its Gram matrix is ill-conditioned
+    (kappa ~ 1e5), so a compensator entry may land one fp16 step away, and the
+    residual, smoothing, scales and codes follow. Every bound below is propagated,
+    with no slack factor, from
+        dR = |P_gpu - P_ref| + dS + (r + 1) eps (|S| + sum_r |u_r| |k_r|),
+    the per-entry bound on |R_gpu - R_ref| (P the subtracted fp16 pieces, the last
+    term the r fused subtractions):
+      * smoothing (eq. 7): |sqrt(x) - sqrt(y)| = |x - y| / (sqrt x + sqrt y), so
+        c = sqrt(mean_v |R|) moves by at most mean_v dR / (c_gpu + c_ref); the root
+        mean square by at most sqrt(mean_v dR^2) (triangle inequality); plus 1e-6 c
+        (16 ulps) for the fp32 reduction tree (depth <= 9), the root and the stores;
+      * scales s_v = max_k |R / c|: max is 1-Lipschitz, so they move by at most
+        max_k (dR / c_gpu + |R_ref| |1/c_gpu - 1/c_ref|), plus 3 ulps;
+      * codes: each side is within half a step of its own pre-rounding value, and the
+        steps s_v c_k / Q differ, so |Z_gpu - Z_ref| <= 1 + dR / step_gpu
+        + Q |1 - step_ref / step_gpu| + 5 Q eps (the GPU's fp32 quotient chain).
+    Where the pieces agree this allows one step; on outlier channels (c_k ~ 1e-3 once
+    the pieces take the outliers out) a one-step fp16 difference in a piece is several
+    code steps."""
     c_g, c_r = np64(st.ksmooth), ref["c"]
-    mag = np.abs(S) if extra is None else np.abs(S) + extra
-    dR = np.zeros_like(mag)
+    s_g, s_r = np64(st.vscale), ref["s"]
+    mag = np.abs(S)
+    dR = np.zeros_like(mag) if dS is None else np.array(dS, dtype=np.float64)
     if st.rank > 0:
         ug, kg = np.swapaxes(np64(st.ct_u), -1, -2), np64(st.ct_k)
-        dR = np.abs(ug @ kg - np.swapaxes(ref["ut"], -1, -2) @ ref["kt"])
+        dR = dR + np.abs(ug @ kg - np.swapaxes(ref["ut"], -1, -2) @ ref["kt"])
         mag = mag + np.abs(ug) @ np.abs(kg)
-    dR = dR + 8 * 2.0 ** -24 * mag
+    dR = dR + (st.rank + 1) * EPS * mag
     if mode == 0:
         bound = dR.mean(axis=1) / (c_g + c_r)
     elif mode == 1:
         bound = np.sqrt((dR ** 2).mean(axis=1))
     else:
         bound = np.zeros_like(c_r)
-    err = np.abs(c_g - c_r)
-    worst = float(np.max(err / (1.25 * bound + 1e-6 * c_r)))
+    worst = float(np.max(np.abs(c_g - c_r) / (bound + 1e-6 * c_r + 1e-300)))
     assert worst <= 1.0, f"{what} ksmooth: {worst:.2f}x the propagated bound"
+    R_r = S - np.swapaxes(ref["ut"], -1, -2) @ ref["kt"]
+    ds = (dR / c_g[:, None, :] + np.abs(R_r) * np.abs(1 / c_g - 1 / c_r)[:, None, :]).max(axis=-1)
+    worst = float(np.max(np.abs(s_g - s_r) / (ds + 3 * EPS * s_r + 1e-300)))
+    assert worst <= 1.0, f"{what} vscale: {worst:.2f}x the propagated bound"
     if st.rank > 0:
         for key, name in (("kt", "ct_k"), ("ut", "ct_u")):
             g, r = np64(getattr(st, name)), ref[key]
@@ -82,22 +129,16 @@ def compare_flush(st, ref, what, S, mode=0, Q=127, extra=None):
         kt = np64(st.ct_k)
         gram = kt @ np.swapaxes(kt, -1, -2)
         assert np.abs(gram - np.eye(st.rank)).max() < 5e-3, f"{what}: compensator keys not orthonormal"
-    # codes: each side is within half a step of its own residual, the residuals
-    # differ by at most dR, and the steps s_v c_k / Q by their own difference,
-    # so |Z_gpu - Z_ref| <= 1 + dR / step + Q |1 - step_ref / step_gpu|. Where the
-    # pieces agree this is one step; on outlier channels (c_k ~ 1e-3 after the
-    # pieces take the outliers out) a one-step fp16 difference in a piece is
-    # several code steps.
     Z = st.codes.cpu().numpy().astype(np.int32)
-    flips = Z != ref["Z"].astype(np.int32)
-    step_g = np64(st.vscale)[:, :, None] * c_g[:, None, :] / Q
-    step_r = ref["s"][:, :, None] * c_r[:, None, :] / Q
+    dZ = np.abs(Z - ref["Z"].astype(np.int32))
+    step_g = s_g[:, :, None] * c_g[:, None, :] / Q
+    step_r = s_r[:, :, None] * c_r[:, None, :] / Q
     with np.errstate(divide="ignore", invalid="ignore"):
-        allow = 1 + 1.25 * (dR / step_g + Q * np.abs(1 - step_r / step_g))
+        allow = 1 + dR / step_g + Q * np.abs(1 - step_r / step_g) + 5 * Q * EPS
     allow = np.where(step_g > 0, allow, 1)
-    assert np.all(np.abs(Z - ref["Z"]) <= allow), f"{what}: a code moved beyond its propagated bound"
-    assert flips.mean() < 1e-2, f"{what}: {flips.mean():.1e} of the codes differ"
-    return int(flips.sum())
+    assert np.all(dZ <= allow), f"{what}: a code moved beyond its propagated bound"
+    assert (dZ > 0).mean() < 1e-2, f"{what}: {(dZ > 0).mean():.1e} of the codes differ"
+    return int((dZ > 0).sum()), int(dZ.max()), int((dZ > 1).sum())
 
 
 def test_codes_bit_exact_on_exact_ties():
@@ -138,7 +179,7 @@ def test_flush_dense_matches_oracle(mode):
     m.leapq_window_flush(st, Q0.to(dev), dense=S0.to(dev), smooth_mode=mode, pre_round=pre)
     torch.cuda.synchronize()
     ref = leapq.flush(np64(S0), np64(Q0), rank=4, iters=1, smooth_mode=mode)
-    flips = compare_flush(st, ref, f"mode {mode}", np64(S0), mode)
+    flips, _, _ = compare_flush(st, ref, f"mode {mode}", np64(S0), mode)
     # the INT8 decision on the GPU's own pre-rounding values is the oracle's
     assert np.array_equal(leapq.round_codes(pre.cpu().numpy()), st.codes.cpu().numpy())
     # smoothing, scales and pre-rounding values of the residual left by the GPU's
@@ -213,9 +254,10 @@ def test_teacher_forced_windows(io):
         # flush from the GPU's own stored state and buffer, oracle on the same
         S_w = leapq.rebuild(start, buffer(st, W))
         ref = leapq.flush(S_w, np64(inp["Q0"]), rank=4)
+        dS = rebuild_error(start, buffer(st, W))
         m.leapq_window_flush(st, Q0)
         torch.cuda.synchronize()
-        flips = compare_flush(st, ref, f"window {w} flush", S_w)
+        flips, _, _ = compare_flush(st, ref, f"window {w} flush", S_w, dS=dS)
         say(f"  window {w}: u err {rel_err(u_gpu, u_ref):.2e}, code flips {flips}")
 
 
@@ -283,9 +325,11 @@ def test_long_run_4096_tokens_sampled():
     o_ex = np.swapaxes(o_ex, 0, 1)
     e_gpu, e_orc = rel_err(sel(outs), o_ex), rel_err(ref["o"], o_ex)
     e_pair = rel_err(sel(outs), ref["o"])
+    # reported, not bounded: once the trajectories part at a tie they are two valid
+    # runs of the method (the per-window parity of the full-size run is in
+    # test_gpu_leapq_config4.py); the check below is a trend on the method's accuracy
     say(f"  vs exact: gpu {e_gpu:.2e}, oracle {e_orc:.2e}; gpu vs oracle {e_pair:.2e}")
     assert e_gpu <= 1.5 * e_orc + 5e-3
-    assert e_pair <= 5e-2
 
 
 def test_edge_cases():

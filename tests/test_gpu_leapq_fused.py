@@ -17,7 +17,7 @@ import delta_rule_recurrent_amd as m
 from delta_rule_recurrent_amd import synth
 from oracle import gdn, kda, kda_leapq, leapq
 from helpers import assert_rel, need_gpu, np64, say
-from test_gpu_leapq import buffer, compare_flush, stored
+from test_gpu_leapq import buffer, compare_flush, rebuild_error, stored, token_update_error
 
 pytestmark = pytest.mark.gpu
 
@@ -74,14 +74,11 @@ def test_last_token_and_flush(kda_mode, io):
         o_ref, S_w = (kda.kda_recurrent if kda_mode else gdn.gdn_recurrent)(q1, k1, v1, a1, b1, S_prev)
         assert_rel(np64(o), o_ref[:, 0], tol, f"window {w} last output")
         assert_rel(np64(o2), o_ref[:, 0], tol, f"window {w} last output (two launches)")
-        # rounding of the token's update in fp32: |S a| and |u k| entries, the dot
-        # product's terms summed over the key channels
-        ak = ((a1 if kda_mode else a1[:, :, None]) * k1)[:, 0]
-        dot_terms = np.abs(S_prev) @ np.abs(ak)[..., None]               # [N][dv][1]
-        u_mag = np.abs(b1)[:, :, None] * (np.abs(v1[:, 0])[..., None] + dot_terms)
-        extra = 16 * (u_mag * np.abs(k1))
+        # the bound on the GPU's fp32 S_{W-1} and on the token's update applied to it
+        dS = token_update_error(S_prev, rebuild_error(start, buffer(st, W - 1), kda=kda_mode),
+                                k1[:, 0], v1[:, 0], np64(inp["alpha"][tl]), b1[:, 0])
         ref = leapq.flush(S_w, np64(inp["Q0"]), rank=4)
-        flips = compare_flush(st, ref, f"window {w} fused flush", S_w, extra=extra)
+        flips, _, _ = compare_flush(st, ref, f"window {w} fused flush", S_w, dS=dS)
         rec, rec2 = leapq.dequant(stored(st)), leapq.dequant(stored(two))
         half = lambda s_: 0.5 * np64(s_.vscale)[:, :, None] / 127.0 * np64(s_.ksmooth)[:, None, :]
         gap = np.abs(rec - rec2) - (half(st) + half(two)) * (1 + 1e-4)

@@ -16,7 +16,7 @@ import delta_rule_recurrent_amd as m
 from delta_rule_recurrent_amd import synth
 from oracle import gdn, leapq
 from helpers import assert_rel, need_gpu, np64, rel_err, say
-from test_gpu_leapq import compare_flush, stored
+from test_gpu_leapq import compare_flush, rebuild_error, stored
 
 pytestmark = pytest.mark.gpu
 TOL_F32, TOL_BF16 = 1e-4, 2e-2
@@ -41,7 +41,7 @@ def test_narrow_width_flush_and_window(bits):
     Z = st.codes.cpu().numpy()
     assert np.abs(Z).max() == Q
     assert np.array_equal(leapq.round_codes(pre.cpu().numpy(), bits), Z)
-    flips = compare_flush(st, ref, f"{bits}-bit encode", np64(inp["S0"]), Q=Q)
+    flips, _, _ = compare_flush(st, ref, f"{bits}-bit encode", np64(inp["S0"]), Q=Q)
     start = stored(st)
     start["Q"] = Q
     outs = [m.leapq_decode_step(st, *(inp[n][t].to(dev) for n in ("q", "k", "v", "alpha", "beta")))
@@ -51,12 +51,12 @@ def test_narrow_width_flush_and_window(bits):
     u_gpu = np64(st.buf_u).transpose(1, 0, 2)
     assert_rel(u_gpu, np.stack([b[1] for b in buf_ref]), TOL_F32, "corrections")
     e = assert_rel(np64(torch.stack(outs)), o_ref, TOL_BF16, "outputs")
-    S_w = leapq.rebuild(start, [(np64(st.buf_k)[:, j], np64(st.buf_u)[:, j], np64(st.buf_a)[:, j])
-                                for j in range(W)])
+    recs = [(np64(st.buf_k)[:, j], np64(st.buf_u)[:, j], np64(st.buf_a)[:, j]) for j in range(W)]
+    S_w = leapq.rebuild(start, recs)
     ref = leapq.flush(S_w, np64(Q0), rank=6, bits=bits)
     m.leapq_window_flush(st, Q0.to(dev))
     torch.cuda.synchronize()
-    f2 = compare_flush(st, ref, f"{bits}-bit window flush", S_w, Q=Q)
+    f2, _, _ = compare_flush(st, ref, f"{bits}-bit window flush", S_w, Q=Q, dS=rebuild_error(start, recs))
     say(f"  outputs {e:.2e}, code flips {flips} / {f2}")
 
 
