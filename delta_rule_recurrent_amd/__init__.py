@@ -17,6 +17,7 @@ from .binding import (  # noqa: F401
     gdn_chunk_bwd,
     gdn_chunk_bwd_workspace,
     gdn_chunk_fwd,
+    gdn_chunk_fwd_noalloc,
     gdn_chunk_workspace,
     gdn_decode_step,
     gdn_decode_step_bf16_state,

@@ -62,6 +62,8 @@ SIGNATURES = {
                                _c_int),
     "kda_leapq_window_flush": ([ctypes.POINTER(LeapqState), _c_int, _vp, _vp, _c_int, _c_int, _vp, _vp],
                                _c_int),
+    "gdn_chunk_fwd_noalloc": ([_vp] * 8 + [_c_int] * 6 + [_vp], _c_int),
+    "gdn_chunk_fwd_noalloc_max_bytes": ([], ctypes.c_size_t),
     "gdnrt_hbm_stream": ([_vp, _vp, ctypes.c_size_t, _c_int, ctypes.c_float, _vp], _c_int),
     "gdnrt_last_error": ([], ctypes.c_char_p),
 }
@@ -426,6 +428,24 @@ def gdn_chunk_fwd(q, k, v, alpha, beta, S0=None, ST=None, o=None, workspace=None
     Returns (o [N][T][128] bf16, ST [N][128][128] fp32)."""
     return _chunk_fwd("gdn_chunk_fwd", gdn_chunk_workspace, (q.shape[0], q.shape[1]),
                       q, k, v, alpha, beta, S0, ST, o, workspace, chunk)
+
+
+def gdn_chunk_fwd_noalloc(q, k, v, alpha, beta, S0, ST, o):
+    """gdn_chunk_fwd through the allocation-free entry point (the library's fixed
+    scratch instead of a workspace). Every tensor, outputs included, is the caller's:
+    o [N][T][128] bf16 and ST [N][128][128] fp32 must be passed in."""
+    N, T, _ = q.shape
+    for n_, t_ in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _need(t_, n_, torch.bfloat16, (N, T, D))
+    _need(alpha, "alpha", torch.float32, (N, T))
+    _need(beta, "beta", torch.float32, (N, T))
+    _need(ST, "ST", torch.float32, (N, D, D))
+    if S0 is not None:
+        _need(S0, "S0", torch.float32, (N, D, D))
+    _check("gdn_chunk_fwd_noalloc", lib().gdn_chunk_fwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(ST), _ptr(o),
+        N, T, D, D, CHUNK, BF16, _stream()))
+    return o, ST
 
 
 def _chunk_fwd(name, alloc, alpha_shape, q, k, v, alpha, beta, S0, ST, o, workspace, chunk):

@@ -1130,6 +1130,17 @@ void gdn_chunk_prep_with_inverse(const uint16_t* q, const uint16_t* k, const uin
 }
 }  // namespace gdnrt
 
+namespace gdnrt {
+// gdn_chunk_fwd under another entry point's name (its messages carry `fn`); the
+// workspace argument as in gdn_chunk_fwd.
+int gdn_chunk_fwd_named(const char* fn, const void* q, const void* k, const void* v, const float* alpha,
+                        const float* beta, const float* S0, float* ST, void* o, int N, int T, int dk,
+                        int dv, int chunk, int io, void* workspace, size_t ws_bytes, void* stream) {
+  return chunk_fwd<false>(fn, q, k, v, alpha, beta, S0, ST, o, N, T, dk, dv, chunk, io, workspace,
+                          ws_bytes, stream);
+}
+}  // namespace gdnrt
+
 extern "C" size_t gdn_chunk_fwd_workspace_bytes(int N, int T, int dk, int dv, int chunk) {
   return chunk_workspace_bytes<false>(N, T, dk, dv, chunk);
 }

@@ -253,6 +253,27 @@ GDNRT_API int gdn_chunk_fwd(const void* q, const void* k, const void* v,
 GDNRT_API size_t gdn_chunk_fwd_workspace_bytes(int N, int T, int dk, int dv, int chunk);
 
 /*
+ * gdn_chunk_fwd for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Same arguments and
+ * results as gdn_chunk_fwd without the workspace: the per-chunk operands go to a
+ * scratch array of gdn_chunk_fwd_noalloc_max_bytes() bytes (128 MiB: 1,637 chunks of 64
+ * tokens, e.g. 32 heads x 3,264 tokens) that the library holds on each GPU it runs on
+ * until the process ends. Nothing is allocated or freed by the call. A shape whose
+ * operands exceed the scratch (gdn_chunk_fwd_workspace_bytes > the maximum) returns
+ * GDNRT_ESHAPE and launches nothing. Every call on one GPU shares that GPU's scratch,
+ * so calls that overlap in time on one GPU (different streams, or threads) race: the
+ * caller orders them. The scratch keeps the last call's contents; nothing in it needs
+ * to start at zero.
+ */
+GDNRT_API int gdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
+                                    const float* alpha, const float* beta,
+                                    const float* S0, float* ST, void* o,
+                                    int N, int T, int dk, int dv, int chunk, int io, void* stream);
+
+/* Bytes of the scratch array gdn_chunk_fwd_noalloc uses (its size limit). */
+GDNRT_API size_t gdn_chunk_fwd_noalloc_max_bytes(void);
+
+/*
  * Gated DeltaNet chunkwise backward of one sequence shard: for the forward of
  * gdn_chunk_fwd from S0 and the scalar L = sum(dO o o) + sum(dST o S_T), writes
  *   dq, dk [N][T][dk], dv [N][T][dv] (bf16), dalpha, dbeta [N][T] (fp32) and dS0
