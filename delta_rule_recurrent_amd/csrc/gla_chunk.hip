@@ -2,452 +2,358 @@
 //
 // Method: "ZeCO: Zero Communication Overhead Sequence Parallelism for Linear
 // Attention", section "Gated Linear Attention (GLA) Formulation" (per-token and
-// chunk recurrences, inter/intra-chunk output) and section "The Complete Forward
-// Algorithm" (the intra-chunk keys are divided by Lambda). In the [d_v][d_k] state
-// layout, with b the inclusive cumulative log-gate inside a chunk of C = 64 tokens:
+// chunk recurrences, inter/intra-chunk output), section "The Complete Forward
+// Algorithm" (the intra-chunk keys are divided by Lambda) and section "Global State
+// Update Formula" (eq. 6: a shard's final state is its incoming state decayed by the
+// shard's total gate plus its state from zero). In the [d_v][d_k] state layout, with
+// b the inclusive cumulative log-gate inside a chunk of C = 64 tokens:
 //
-//   O   = (Q o e^b) S^T + O~,   O~ = [ ((Q o e^b)(K o e^-b)^T) o M ] V,   M lower incl. diag,
+//   O   = (Q o e^b) S^T + [ ((Q o e^b)(K o e^-b)^T) o M ] V,   M lower incl. diag,
 //   S  <- e^{b_C} (on key columns) o S + V^T (K o e^{b_C - b}).
 //
-// Everything but the state is per chunk. A first kernel forms, for every chunk in
-// parallel, Q^ = Q o e^b, K^ = K o e^{b_C - b}, e^{b_C} and the intra-chunk output O~
-// (its score factors taken relative to the chunk's middle token m, Q o e^{b - b_m} and
-// K o e^{b_m - b}, which halves their range), and writes them to the caller's
-// workspace, in bf16 and in the register order in which the second kernel feeds them
-// to the matrix cores. The second kernel walks the chunks of each sequence in order
-// for a tile of value channels (the value rows of S evolve independently; the tiles of
-// a sequence share an XCD, so the operands they all read come from one L2): per chunk,
-// O = O~ + Q^ S^T and S <- e^{b_C} o S + V^T K^, the state in fp32 MFMA accumulators,
-// one barrier per chunk, the operands of the chunk two ahead in flight. bf16 MFMA
-// (v_mfma_f32_16x16x32_bf16) with fp32 accumulation throughout.
-#include "common.hpp"
+// The chunks of each sequence are cut into P segments (eq. 6 applied inside the call):
+//   pass 1   every segment but the last, in R pieces, from a zero state: each piece's
+//            end state B_i and total decay gamma_i = exp(sum of its log-gates) per key;
+//   combine  start states: S_0 the incoming state, then x <- gamma_i o x + B_i over the
+//            pieces of segment s in order gives S_{s+1};
+//   pass 2   every segment from its start state, with outputs.
+// A 512-thread block runs one (sequence, segment or piece), one block per CU (the
+// segments fill the GPU). Per chunk the block forms, with m the chunk's middle token
+// (which halves the range of the factors), Qr = Q o e^{b - b_m} and Kr = K o e^{b_m - b}
+// once in LDS; every product goes through them:
+//   scores      (Qr Kr^T) o M,
+//   inter-chunk (Q o e^b) S^T = Qr (S o e^{b_m})^T, the state's key columns scaled in fp32,
+//   state       V^T (K o e^{b_C - b}) = (V^T Kr) o e^{b_C - b_m}, scaled after the product.
+// Thread (lane, wave w) loads channels 2 lane, 2 lane + 1 of tokens 8 w .. 8 w + 7 of q,
+// k and the log-gates straight into registers, a chunk ahead and in three parts spread
+// over the chunk, and forms their factors there (exponentials in base 2); v goes through
+// LDS for the transposed operand reads. Wave w holds the state rows of value channels
+// 16 w .. 16 w + 15 transposed (rows = keys) in fp32 MFMA accumulators, which are also
+// the A operand of the inter-chunk product: their key order (four consecutive keys per
+// lane from each of two 16-key blocks) is matched on the Qr side by two 8-byte reads.
+// bf16 MFMA (16x16x32) with fp32 accumulation throughout.
+#include "chunk_device.hpp"
 #include "gla_chunk_layout.hpp"
 
 namespace gdnrt {
 
 namespace gla {
+using namespace gdc;   // C, PQ, PC, ld8, ld_tr8, mfma, tri_pair, lo_bf, hi_bf
 
-constexpr int C = kChunk;   // 64 tokens
-constexpr int NT = 512;     // threads per block, both kernels
-constexpr int PQ = kD + 8;   // bf16 pitch of 128-wide rows read by rows (conflict-free 16-byte reads)
-constexpr int PT = kD + 16;  // bf16 pitch of 128-wide rows read transposed (conflict-free ds_read_b64_tr_b16)
-constexpr int PC = C + 8;    // bf16 pitch of 64-wide rows
+constexpr int NB = 512;       // threads per block: 8 waves
+constexpr int PT = kD + 16;   // bf16 pitch of 128-wide rows read transposed (ds_read_b64_tr_b16)
+constexpr int kMaxSeg = 16;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr size_t kStateBytes = (size_t)kD * kD * 4;
 
-// The workspace layout per chunk (Q^, K^, O~ fragments, e^{b_C}) is in gla_chunk_layout.hpp.
-
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-__device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
-}
-__device__ __forceinline__ bf16x8 as_bf8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
-__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ float lo_bf(unsigned w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float hi_bf(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
-
-// MFMA operand from a row-major [contraction][column] bf16 matrix in LDS through the
-// transposing LDS read (ds_read_b64_tr_b16): lane (l16, lq) receives
-// X[c0 + 8 lq + e][n0 + l16], e = 0..7.
-__device__ __forceinline__ bf16x8 ld_tr8(const uint16_t* X, int pitch, int c0, int n0) {
-  const int lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
-  const uint16_t* p = X + (c0 + 8 * g + (j >> 2)) * pitch + n0 + 4 * (j & 3);
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * pitch));
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-// lower-triangle 16 x 16 tile pairs (rb, cb), cb <= rb, numbered row by row
-__device__ __forceinline__ void tri_pair(int p, int& rb, int& cb) {
-  rb = p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3;
-  cb = p - (rb * (rb + 1)) / 2;
-}
-
-// ------------------------------------------------------------------ per-chunk prep
-
-struct alignas(16) PrepSmem {
-  uint16_t Q[C * PQ];       // raw q [t][k], then Q^ = q o e^b in place
-  uint16_t K[C * PT];       // raw k, then K^ = k o e^{b_C - b} in place
-  uint16_t V[C * PT];       // raw v [t][v]
-  uint16_t Qr[C * PQ];      // q o e^{b - b_m}
-  uint16_t Kr[C * PQ];      // k o e^{b_m - b}
-  uint16_t A[C * PC];       // masked scores [r][j]
-  float tot[8 * kD];        // log-gate sums of each group of 8 tokens
+// Segments per sequence: one block per CU over the whole grid, at most kMaxSeg per
+// sequence, every segment non-empty. Pass 1 cuts each of the first P - 1 segments into R
+// pieces of L1 chunks (the combine folds them in order). Workspace after the chunks:
+// B [N][P-1][R][128][128] fp32, gamma [N][P-1][R][128] fp32, start states
+// [N][P][128][128] fp32.
+struct Plan {
+  int P, Lseg, R, L1;
+  size_t b_off, g_off, s_off, total;
 };
 
-// One chunk's inputs: 16-byte pieces p = tid + 512 h of q, k, v (token p / 16, channels
-// 8 (p % 16) ..), and the log-gates of the thread's elementwise share (channels 2 cp,
-// 2 cp + 1 of tokens 8 eg .. 8 eg + 7, cp = tid % 64, eg = tid / 64).
-struct PrepIn {
-  u32x4 q[2], k[2], v[2];
+__host__ inline Plan plan(int N, int nc) {
+  Plan p{};
+  int P = N >= 256 ? 1 : (256 + N - 1) / N;
+  P = P > kMaxSeg ? kMaxSeg : P;
+  if (P > nc) P = nc;
+  if (P < 1) P = 1;
+  p.Lseg = nc > 0 ? (nc + P - 1) / P : 0;
+  p.P = nc > 0 ? (nc + p.Lseg - 1) / p.Lseg : 1;
+  p.R = p.Lseg % 2 == 0 ? 2 : 1;
+  p.L1 = p.Lseg / p.R;
+  const size_t pieces = p.P > 1 ? (size_t)N * (p.P - 1) * p.R : 0;
+  p.b_off = (size_t)N * nc * kWChunk;
+  p.g_off = p.b_off + pieces * kStateBytes;
+  p.s_off = p.g_off + pieces * kD * 4;
+  p.total = p.s_off + (p.P > 1 ? (size_t)N * p.P * kStateBytes : 0);
+  return p;
+}
+
+struct alignas(16) Smem {
+  uint16_t Qr[C * PQ];               // q o e^{b - b_m} [t][k]
+  uint16_t Kr[C * PT];               // pass 2: k o e^{b_m - b}; pass 1: k o e^{b_C - b}
+  uint16_t V[C * PT];                // v [t][v]
+  uint16_t A[C * PC];                // masked scores [r][j]
+  float tot[8 * kD];                 // log-gate sums of each group of 8 tokens
+  float ec[kD], em[kD], ef[kD];      // e^{b_C}, e^{b_m}, e^{b_C - b_m} per key
+};
+
+// One chunk's inputs of a thread: q, k, log-gates of channels 2 cp, 2 cp + 1 of tokens
+// 8 eg .. 8 eg + 7 (cp = lane, eg = wave), and the 16-byte pieces p = tid + 512 h of v.
+struct In {
+  unsigned q[8], k[8];
   f32x2 g[8];
+  u32x4 v[2];
 };
 
-__device__ __forceinline__ void prep_fetch(PrepIn& in, const uint16_t* __restrict__ q,
-                                           const uint16_t* __restrict__ k,
-                                           const uint16_t* __restrict__ v,
-                                           const float* __restrict__ log_g, size_t tok0) {
-  const int t = threadIdx.x;
+// Loads of one chunk's inputs, in parts (PART 1: q and k, 2: log-gates, 3: v, 0: all), so
+// that a chunk's requests can be spread over the work on the previous one.
+template <bool OUT, int PART>
+__device__ __forceinline__ void fetch(In& in, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                      const uint16_t* __restrict__ v, const float* __restrict__ log_g, size_t tok0,
+                                      int t) {
+  const int cp = t & 63, eg = t >> 6;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const size_t off = (tok0 + 8 * eg + i) * kD + 2 * cp;
+    if constexpr (PART == 0 || PART == 1) {
+      if constexpr (OUT) in.q[i] = *reinterpret_cast<const unsigned*>(q + off);
+      in.k[i] = *reinterpret_cast<const unsigned*>(k + off);
+    }
+    if constexpr (PART == 0 || PART == 2) in.g[i] = *reinterpret_cast<const f32x2*>(log_g + off);
+  }
+  if constexpr (PART == 0 || PART == 3) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int p = t + NB * h;
+      in.v[h] = *reinterpret_cast<const u32x4*>(v + (tok0 + (p >> 4)) * kD + 8 * (p & 15));
+    }
+  }
+}
+
+// v to LDS; the thread's prefix sums of its log-gates in base 2 (in place) and their
+// totals per group of 8 tokens to LDS.
+__device__ __forceinline__ void stage(Smem& sm, In& in, int t) {
+  const int cp = t & 63, eg = t >> 6;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int p = t + NT * h;
-    const size_t off = (tok0 + (p >> 4)) * kD + (p & 15) * 8;
-    in.q[h] = *reinterpret_cast<const u32x4*>(q + off);
-    in.k[h] = *reinterpret_cast<const u32x4*>(k + off);
-    in.v[h] = *reinterpret_cast<const u32x4*>(v + off);
+    const int p = t + NB * h;
+    *reinterpret_cast<u32x4*>(sm.V + (p >> 4) * PT + 8 * (p & 15)) = in.v[h];
   }
+  in.g[0] *= kLog2e;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    in.g[i] = *reinterpret_cast<const f32x2*>(log_g + (tok0 + 8 * (t >> 6) + i) * kD + 2 * (t & 63));
+  for (int i = 1; i < 8; ++i) in.g[i] = in.g[i] * kLog2e + in.g[i - 1];
+  *reinterpret_cast<f32x2*>(sm.tot + eg * kD + 2 * cp) = in.g[7];
+}
+
+__device__ __forceinline__ f32x2 bf2f(unsigned w) { return f32x2{lo_bf(w), hi_bf(w)}; }
+__device__ __forceinline__ unsigned pk2(f32x2 x) { return pack_bf16(x[0], x[1]); }
+__device__ __forceinline__ u32x2 pk4(f32x4 x) { return u32x2{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])}; }
+// 2^x per component (v_exp_f32); the log-gates are carried in base 2 inside the kernel
+__device__ __forceinline__ f32x2 exp2v(f32x2 x) {
+  return f32x2{__builtin_amdgcn_exp2f(x[0]), __builtin_amdgcn_exp2f(x[1])};
 }
 
 }  // namespace gla
 
-namespace gla {
-
-// One chunk of the prep: stages the inputs held in `in`, requests the next chunk's into
-// `in`, and writes the chunk's operands to the workspace.
-__device__ __forceinline__ void prep_chunk(PrepSmem& sm, PrepIn& in, int cid, const uint16_t* __restrict__ q,
-                                           const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                                           const float* __restrict__ log_g, uint8_t* __restrict__ ws, int T,
-                                           int nchunks) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l16 = lane & 15, lq = lane >> 4;
-  const int cp = tid & 63, eg = tid >> 6;   // elementwise: key-channel pair, token group of 8
-  const int nc = T / C;
-  uint8_t* wsc = ws + (size_t)cid * kWChunk;
-
-  // ---- stage the raw inputs, prefix sums of the thread's log-gates (thread (cp, eg)
-  // owns channels 2cp, 2cp+1 of tokens 8eg .. 8eg+7); request the next chunk's inputs
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int p = tid + NT * h, r = p >> 4, c = (p & 15) * 8;
-    *reinterpret_cast<u32x4*>(sm.Q + r * PQ + c) = in.q[h];
-    *reinterpret_cast<u32x4*>(sm.K + r * PT + c) = in.k[h];
-    *reinterpret_cast<u32x4*>(sm.V + r * PT + c) = in.v[h];
-  }
-  f32x2 b[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) b[i] = i ? b[i - 1] + in.g[i] : in.g[i];
-  *reinterpret_cast<f32x2*>(sm.tot + eg * kD + 2 * cp) = b[7];
-  {
-    const int nx = cid + (int)gridDim.x < nchunks ? cid + (int)gridDim.x : cid;
-    prep_fetch(in, q, k, v, log_g, (size_t)(nx / nc) * T + (size_t)(nx % nc) * C);
-  }
-  lds_barrier();
-
-  // ---- decayed factors of the thread's elements (each read and rewritten by its owner)
-  {
-    f32x2 off = {0.f, 0.f}, bm = {0.f, 0.f}, bC = {0.f, 0.f};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const f32x2 te = *reinterpret_cast<const f32x2*>(sm.tot + e * kD + 2 * cp);
-      if (e < eg) off += te;
-      if (e < 4) bm += te;   // b at token 31, the middle of the chunk
-      bC += te;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int o = (8 * eg + i) * PQ + 2 * cp, ok = (8 * eg + i) * PT + 2 * cp;
-      const f32x2 bb = b[i] + off;
-      const unsigned qw = *reinterpret_cast<const unsigned*>(sm.Q + o);
-      const unsigned kw = *reinterpret_cast<const unsigned*>(sm.K + ok);
-      const float q0 = lo_bf(qw), q1 = hi_bf(qw), k0 = lo_bf(kw), k1 = hi_bf(kw);
-      *reinterpret_cast<unsigned*>(sm.Qr + o) =
-          pack_bf16(q0 * __expf(bb.x - bm.x), q1 * __expf(bb.y - bm.y));
-      *reinterpret_cast<unsigned*>(sm.Kr + o) =
-          pack_bf16(k0 * __expf(bm.x - bb.x), k1 * __expf(bm.y - bb.y));
-      *reinterpret_cast<unsigned*>(sm.Q + o) = pack_bf16(q0 * __expf(bb.x), q1 * __expf(bb.y));
-      *reinterpret_cast<unsigned*>(sm.K + ok) =
-          pack_bf16(k0 * __expf(bC.x - bb.x), k1 * __expf(bC.y - bb.y));
-    }
-    if (eg == 0)
-      *reinterpret_cast<f32x2*>(reinterpret_cast<float*>(wsc + kWE) + 2 * cp) =
-          f32x2{__expf(bC.x), __expf(bC.y)};
-  }
-  lds_barrier();
-
-  // ---- Q^ and K^ fragments to the workspace; masked scores A to LDS
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {   // Q^ fragment (rb, ks) = (wave & 3, (wave >> 2) + 2h)
-    const int rb = wave & 3, ks = (wave >> 2) + 2 * h;
-    *reinterpret_cast<u32x4*>(wsc + kWQ + ((size_t)(rb * 4 + ks) * 64 + lane) * 16) =
-        *reinterpret_cast<const u32x4*>(sm.Q + (rb * 16 + l16) * PQ + ks * 32 + lq * 8);
-  }
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {   // K^ fragment f = 2 kb + js = wave + 8h
-    const int f = wave + 8 * h;
-    *reinterpret_cast<u32x4*>(wsc + kWK + ((size_t)f * 64 + lane) * 16) =
-        __builtin_bit_cast(u32x4, ld_tr8(sm.K, PT, (f & 1) * 32, (f >> 1) * 16));
-  }
-  for (int u = wave; u < 10; u += 8) {   // score tiles over the lower triangle
-    int rb, cb;
-    tri_pair(u, rb, cb);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      acc = mfma(ld8(sm.Qr + (rb * 16 + l16) * PQ + ks * 32 + lq * 8),
-                 ld8(sm.Kr + (cb * 16 + l16) * PQ + ks * 32 + lq * 8), acc);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = rb * 16 + lq * 4 + i, j = cb * 16 + l16;
-      sm.A[r * PC + j] = f32_to_bf16(j <= r ? acc[i] : 0.f);
-    }
-  }
-  {   // the zero upper tiles that the 32-wide contraction slices of A reach: (0,1), (2,3)
-    const int t = tid >> 8, e = tid & 255;
-    sm.A[(t * 32 + (e >> 4)) * PC + t * 32 + 16 + (e & 15)] = 0;
-  }
-  lds_barrier();
-
-  // ---- O~ = A V: tiles (rb, vb = wave); row block rb reaches tokens <= 16 rb + 15
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int js = 0; js <= rb / 2; ++js)
-      acc = mfma(ld8(sm.A + (rb * 16 + l16) * PC + js * 32 + lq * 8),
-                 ld_tr8(sm.V, PT, js * 32, wave * 16), acc);
-    *reinterpret_cast<u32x2*>(wsc + kWO + ((size_t)(rb * 8 + wave) * 64 + lane) * 8) =
-        u32x2{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
-  }
-  lds_barrier();
-}
-
-}  // namespace gla
-
-// Persistent: block b handles chunks b, b + grid, ...; the next chunk's inputs are
-// loaded into registers while this one is processed, and every thread issues the
-// same global loads and stores on every chunk so that the waits for them are exact
-// (the first chunk is peeled, so that the loop's waits do not also serve the loads
-// issued before it).
-__global__ __launch_bounds__(512) void gla_chunk_prep_kernel(
+// OUT: pass 2 (one block per (sequence, segment), outputs, the shard calls' workspace);
+// else pass 1 (one block per (sequence, piece of a segment < P - 1): end state from zero
+// and the piece's decay). Wave w owns value channels 16 w .. 16 w + 15; in the
+// elementwise work thread (lane, w) owns channels 2 lane, 2 lane + 1 of tokens 8 w .. 8 w + 7.
+template <bool OUT>
+__global__ __launch_bounds__(512, OUT ? 2 : 4) void gla_fused_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ log_g, uint8_t* __restrict__ ws, int T, int nchunks) {
+    const float* __restrict__ log_g, uint8_t* __restrict__ ws, const float* __restrict__ S0,
+    const float* __restrict__ Sst, float* __restrict__ Bbuf, float* __restrict__ Gbuf,
+    float* __restrict__ ST, uint16_t* __restrict__ o, int T, int P, int Lseg, int R) {
   using namespace gla;
-  __shared__ PrepSmem sm;
-  const int nc = T / C;
-  PrepIn in;
-  int cid = blockIdx.x;   // the grid never exceeds nchunks
-  prep_fetch(in, q, k, v, log_g, (size_t)(cid / nc) * T + (size_t)(cid % nc) * C);
-  prep_chunk(sm, in, cid, q, k, v, log_g, ws, T, nchunks);
-  for (cid += gridDim.x; cid < nchunks; cid += gridDim.x) prep_chunk(sm, in, cid, q, k, v, log_g, ws, T, nchunks);
-}
+  __shared__ Smem sm;
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave
+  // MFMA lane roles (l16, lq) and the elementwise channel pair cp; the chunk loop forms
+  // its own from an opaque copy of the thread index
+  const int l16 = tid & 15, lq = (tid >> 4) & 3, cp = tid & 63;
+  const int segs = OUT ? P : (P - 1) * R;   // blocks per sequence
+  const int n = blockIdx.x / segs, s = blockIdx.x % segs;
+  const int nc = T / C, len = OUT ? Lseg : Lseg / R;
+  const int c0 = s * len, c1 = min(nc, c0 + len);
+  const int vrow = 16 * w + l16;   // this lane's value channel in the MFMA layouts
 
-// ------------------------------------------------------------------ sequential pass
-namespace gla {
-
-template <int VT>
-struct alignas(16) SeqSmem {
-  static constexpr int PV = VT == 16 ? 16 : 48;   // value-tile pitch (bf16)
-  static constexpr int PO = VT + 4;               // output-tile pitch (bf16)
-  uint16_t Sb[2][VT * PQ];       // bf16 copy of the state tile [v][k], by chunk parity
-  uint16_t Vs[2][C * PV];        // the chunk's value tile [t][v], by chunk parity
-  uint16_t Qs[2][16 * 64 * 8];   // the chunk's Q^ fragments, by chunk parity
-  uint16_t Os[2][C * PO];        // the chunk's output tile [t][v], stored a chunk later
-};
-
-// VT / 8 bf16 of one token row: a thread's share of a [64][VT] tile (token tid / 8)
-template <int VT>
-using piece_t = typename std::conditional<VT == 32, u32x2, unsigned>::type;
-
-// One chunk's operands for this wave, loaded two chunks ahead in three parts spread
-// over the chunk's work (a burst of all of them would stall the waves' issue). Staged
-// through LDS a chunk ahead (so loaded first): the thread's piece of the value tile and
-// Q^ fragments `wave` and `wave + 8`, which the waves then read in the order of their
-// output tiles. Kept in registers: the O~ tile (rb = wave & 3, value block
-// (wave >> 2) % NVB) of the output tile, and the K^ fragments of key block `wave` with
-// e^{b_C} of the lane's key for the state tiles.
-template <int VT>
-struct SeqIn {
-  piece_t<VT> vp;
-  u32x4 mq[2];
-  u32x2 x;
-  u32x4 kh[2];
-  float ec;
-};
-
-template <int VT, int PART>
-__device__ __forceinline__ void seq_fetch(SeqIn<VT>& in, const uint8_t* __restrict__ wsc,
-                                          const uint16_t* __restrict__ v, size_t tok0, int vt) {
-  constexpr int NVB = VT / 16;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int rb = wave & 3, vbl = (wave >> 2) % NVB;
-  if constexpr (PART == 0) {
-    in.vp = *reinterpret_cast<const piece_t<VT>*>(v + (tok0 + (tid >> 3)) * kD + vt * VT + (tid & 7) * (VT / 8));
+  // St[kb][i] = S[vrow][16 kb + 4 lq + i]
+  f32x4 St[8];
+  {
+    const float* src = nullptr;
+    if constexpr (OUT) src = P > 1 ? Sst + ((size_t)n * P + s) * kD * kD : S0 ? S0 + (size_t)n * kD * kD : nullptr;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-      in.mq[h] = *reinterpret_cast<const u32x4*>(wsc + kWQ + ((size_t)(wave + 8 * h) * 64 + lane) * 16);
-  } else if constexpr (PART == 1) {
-    in.x = *reinterpret_cast<const u32x2*>(wsc + kWO + ((size_t)(rb * 8 + vt * NVB + vbl) * 64 + lane) * 8);
-    in.kh[0] = *reinterpret_cast<const u32x4*>(wsc + kWK + ((size_t)(wave * 2) * 64 + lane) * 16);
+    for (int kb = 0; kb < 8; ++kb)
+      St[kb] = src ? *reinterpret_cast<const f32x4*>(src + (size_t)vrow * kD + 16 * kb + 4 * lq)
+                   : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  f32x2 lsum = {0.f, 0.f};   // pass 1, wave 0: the piece's log-decay (base 2)
+
+  if (c1 > c0) {
+    const size_t tokn = (size_t)n * T;
+    if constexpr (OUT) {   // the upper tiles (0,1), (2,3) that the 32-wide slices of A reach stay zero
+      const int t2 = tid >> 8, x = tid & 255;
+      sm.A[(32 * t2 + (x >> 4)) * PC + 32 * t2 + 16 + (x & 15)] = 0;
+    }
+    In in;
+    fetch<OUT, 0>(in, q, k, v, log_g, tokn + (size_t)c0 * C, tid);
+    stage(sm, in, tid);
+    // all of the first chunk's loads complete here, so that inside the loop the waits for
+    // the prefetched q and k count only what follows them (s_waitcnt vmcnt(0))
+    __builtin_amdgcn_s_waitcnt(0xF70);
+#pragma unroll 1
+    for (int c = c0;;) {
+      const size_t tok0 = tokn + (size_t)c * C;
+      uint8_t* wsc = ws + ((size_t)n * nc + c) * kWChunk;
+      // the thread index through an opaque move: the per-lane addresses are formed inside
+      // each chunk instead of being held across the loop
+      int t;
+      asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"(tid));
+      const int lane = t & 63, l16 = lane & 15, lq = lane >> 4, cp = lane;
+      lds_barrier();
+
+      // ---- factors of the thread's elements (tokens 8 w .., channels 2 cp, 2 cp + 1)
+      {
+        f32x2 off = {0.f, 0.f}, bm = off, bC = off;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const f32x2 te = *reinterpret_cast<const f32x2*>(sm.tot + e * kD + 2 * cp);
+          if (e < w) off += te;   // wave-uniform
+          if (e < 4) bm += te;    // b at token 31, the middle of the chunk
+          bC += te;
+        }
+        const f32x2 emv = exp2v(bm);
+        unsigned qh[8];   // Q^ of the thread's tokens, stored once every prefetched q and k is used
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int r = 8 * w + i;
+          const f32x2 b = in.g[i] + off;
+          const f32x2 kf = bf2f(in.k[i]);
+          if constexpr (OUT) {
+            const f32x2 d = b - bm;
+            const f32x2 qr = bf2f(in.q[i]) * exp2v(d);
+            *reinterpret_cast<unsigned*>(sm.Qr + r * PQ + 2 * cp) = pk2(qr);
+            *reinterpret_cast<unsigned*>(sm.Kr + r * PT + 2 * cp) = pk2(kf * exp2v(-d));
+            qh[i] = pk2(qr * emv);
+          } else {
+            *reinterpret_cast<unsigned*>(sm.Kr + r * PT + 2 * cp) = pk2(kf * exp2v(bC - b));
+          }
+        }
+        // the next chunk's q and k go out before this chunk's workspace stores; its
+        // log-gates and v follow later in the chunk
+        if (c + 1 < c1) fetch<OUT, 1>(in, q, k, v, log_g, tok0 + C, t);
+        if constexpr (OUT) {   // Q^ = Qr o e^{b_m}, row-major, for the shard calls
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            *reinterpret_cast<unsigned*>(wsc + kWQ + ((size_t)(8 * w + i) * kD + 2 * cp) * 2) = qh[i];
+        }
+        if (w == 0) {
+          const f32x2 ecv = exp2v(bC);
+          *reinterpret_cast<f32x2*>(sm.ec + 2 * cp) = ecv;
+          if constexpr (OUT) {
+            *reinterpret_cast<f32x2*>(sm.em + 2 * cp) = emv;
+            *reinterpret_cast<f32x2*>(sm.ef + 2 * cp) = exp2v(bC - bm);
+            *reinterpret_cast<f32x2*>(reinterpret_cast<float*>(wsc + kWE) + 2 * cp) = ecv;
+          } else {
+            lsum += bC;
+          }
+        }
+      }
+      lds_barrier();
+
+      // ---- wave w: the value operand of its tile (lane (l16, lq) holds v[32 js + 8 lq + e][16 w + l16])
+      const bf16x8 vt0 = ld_tr8(sm.V, PT, 0, 16 * w), vt1 = ld_tr8(sm.V, PT, 32, 16 * w);
+      f32x4 oacc[4];
+      if constexpr (OUT) {
+        // inter-chunk outputs, transposed: D[v][t] = sum_k (S o e^{b_m})[v][k] Qr[t][k],
+        // contraction slot 8 lq + e <-> key 32 ks + 4 lq + e (e < 4), 32 ks + 16 + 4 lq + e - 4
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) oacc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const f32x4 e0 = *reinterpret_cast<const f32x4*>(sm.em + 32 * ks + 4 * lq);
+          const f32x4 e1 = *reinterpret_cast<const f32x4*>(sm.em + 32 * ks + 16 + 4 * lq);
+          const u32x2 a = pk4(St[2 * ks] * e0), b = pk4(St[2 * ks + 1] * e1);
+          const bf16x8 sa = as_bf8(u32x4{a[0], a[1], b[0], b[1]});
+#pragma unroll
+          for (int tb = 0; tb < 4; ++tb) {
+            const uint16_t* qp = sm.Qr + (16 * tb + l16) * PQ + 32 * ks + 4 * lq;
+            const u32x2 x0 = *reinterpret_cast<const u32x2*>(qp), x1 = *reinterpret_cast<const u32x2*>(qp + 16);
+            oacc[tb] = mfma(sa, as_bf8(u32x4{x0[0], x0[1], x1[0], x1[1]}), oacc[tb]);
+          }
+        }
+      }
+      if (c + 1 < c1) fetch<OUT, 2>(in, q, k, v, log_g, tok0 + C, t);
+      // state rows of the wave's tile: S^T <- e^{b_C} o S^T + K^T V through Kr
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) {
+        const bf16x8 k0 = ld_tr8(sm.Kr, PT, 0, 16 * kb), k1 = ld_tr8(sm.Kr, PT, 32, 16 * kb);
+        const f32x4 ecv = *reinterpret_cast<const f32x4*>(sm.ec + 16 * kb + 4 * lq);
+        if constexpr (OUT) {
+          const f32x4 efv = *reinterpret_cast<const f32x4*>(sm.ef + 16 * kb + 4 * lq);
+          const f32x4 x = mfma(k1, vt1, mfma(k0, vt0, f32x4{0.f, 0.f, 0.f, 0.f}));
+          St[kb] = St[kb] * ecv + x * efv;
+        } else {
+          St[kb] = mfma(k1, vt1, mfma(k0, vt0, St[kb] * ecv));
+        }
+      }
+      if (c + 1 < c1) fetch<OUT, 3>(in, q, k, v, log_g, tok0 + C, t);
+      if constexpr (OUT) {
+        // masked scores over the lower triangle of 16 x 16 tiles
+        for (int u = w; u < 10; u += 8) {
+          int rb, cb;
+          tri_pair(u, rb, cb);
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks)
+            acc = mfma(ld8(sm.Qr + (rb * 16 + l16) * PQ + ks * 32 + lq * 8),
+                       ld8(sm.Kr + (cb * 16 + l16) * PT + ks * 32 + lq * 8), acc);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = rb * 16 + lq * 4 + i, jj = cb * 16 + l16;
+            sm.A[r * PC + jj] = f32_to_bf16(jj <= r ? acc[i] : 0.f);
+          }
+        }
+        lds_barrier();
+        // intra-chunk outputs: D[v][t] += sum_j v[j][v] A[t][j]; the lane holds token
+        // 16 tb + l16, value channels 16 w + 4 lq + i
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          oacc[tb] = mfma(vt0, ld8(sm.A + (16 * tb + l16) * PC + 8 * lq), oacc[tb]);
+          if (tb >= 2) oacc[tb] = mfma(vt1, ld8(sm.A + (16 * tb + l16) * PC + 32 + 8 * lq), oacc[tb]);
+          *reinterpret_cast<u32x2*>(o + (tok0 + 16 * tb + l16) * kD + 16 * w + 4 * lq) = pk4(oacc[tb]);
+        }
+      }
+      if (++c == c1) break;
+      // ---- the next chunk's inputs go to LDS once every wave is done with this one's; the
+      // staging follows this chunk's stores on every path, so waiting for its loads never
+      // waits for those stores
+      if constexpr (!OUT) lds_barrier();
+      stage(sm, in, t);
+    }
+  }
+
+  float* dst;
+  if constexpr (OUT) {
+    if (s != P - 1) return;
+    dst = ST + (size_t)n * kD * kD;
   } else {
-    in.kh[1] = *reinterpret_cast<const u32x4*>(wsc + kWK + ((size_t)(wave * 2 + 1) * 64 + lane) * 16);
-    in.ec = reinterpret_cast<const float*>(wsc + kWE)[wave * 16 + (lane & 15)];
+    dst = Bbuf + ((size_t)n * segs + s) * kD * kD;
+    if (w == 0) *reinterpret_cast<f32x2*>(Gbuf + ((size_t)n * segs + s) * kD + 2 * cp) = exp2v(lsum);
   }
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb)
+    *reinterpret_cast<f32x4*>(dst + (size_t)vrow * kD + 16 * kb + 4 * lq) = St[kb];
 }
 
-template <int VT>
-__device__ __forceinline__ void seq_fetch_all(SeqIn<VT>& in, const uint8_t* __restrict__ wsc,
-                                              const uint16_t* __restrict__ v, size_t tok0, int vt) {
-  seq_fetch<VT, 0>(in, wsc, v, tok0, vt);
-  seq_fetch<VT, 1>(in, wsc, v, tok0, vt);
-  seq_fetch<VT, 2>(in, wsc, v, tok0, vt);
-}
-
-template <int VT>
-__device__ __forceinline__ void stage(SeqSmem<VT>& sm, const SeqIn<VT>& in, int buf) {
-  constexpr int PV = SeqSmem<VT>::PV;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  *reinterpret_cast<piece_t<VT>*>(sm.Vs[buf] + (tid >> 3) * PV + (tid & 7) * (VT / 8)) = in.vp;
+// Start states of the segments, elementwise in fp32: Sst[n][0] = S0 (or 0), and each
+// of the R pieces i of segment s in order, x <- gamma_i (per key) o x + B_i, gives
+// Sst[n][s + 1]. One thread per four entries.
+__global__ __launch_bounds__(256) void gla_seg_combine_kernel(const float* __restrict__ S0,
+                                                              const float* __restrict__ Bbuf,
+                                                              const float* __restrict__ Gbuf,
+                                                              float* __restrict__ Sst, int P, int R) {
+  const int n = blockIdx.x >> 4;
+  const int e4 = ((blockIdx.x & 15) * 256 + threadIdx.x) * 4;   // entry of [128][128]
+  const int key = e4 & (kD - 1);
+  f32x4 x = S0 ? *reinterpret_cast<const f32x4*>(S0 + (size_t)n * kD * kD + e4) : f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0;; ++s) {
+    *reinterpret_cast<f32x4*>(Sst + ((size_t)n * P + s) * kD * kD + e4) = x;
+    if (s == P - 1) break;
+    for (int i = 0; i < R; ++i) {
+      const size_t piece = ((size_t)n * (P - 1) + s) * R + i;
+      const f32x4 g = *reinterpret_cast<const f32x4*>(Gbuf + piece * kD + key);
+      const f32x4 bb = *reinterpret_cast<const f32x4*>(Bbuf + piece * kD * kD + e4);
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
-    *reinterpret_cast<u32x4*>(sm.Qs[buf] + ((wave + 8 * h) * 64 + lane) * 8) = in.mq[h];
-}
-
-// Stores the output tile staged in Os[buf] for the chunk starting at token tok0.
-template <int VT>
-__device__ __forceinline__ void store_o(const SeqSmem<VT>& sm, uint16_t* __restrict__ o, size_t tok0,
-                                        int vt, int buf) {
-  constexpr int PO = SeqSmem<VT>::PO;
-  const int tid = threadIdx.x;
-  *reinterpret_cast<piece_t<VT>*>(o + (tok0 + (tid >> 3)) * kD + vt * VT + (tid & 7) * (VT / 8)) =
-      *reinterpret_cast<const piece_t<VT>*>(sm.Os[buf] + (tid >> 3) * PO + (tid & 7) * (VT / 8));
-}
-
-// One chunk: requests the operands of chunk ci + 2 into `nx` (in three parts), stores
-// the previous chunk's output tile, forms this chunk's output tile into LDS, stages the
-// next chunk's value tile and Q^ (from `nv`, loaded a chunk ago) and updates the state
-// from `pf`. Every thread issues the same global loads and stores on every chunk (past
-// the end the last chunk is loaded again; the first chunk is peeled), so the waits for
-// `pf` and `nv` count exactly the memory operations issued after them.
-template <int VT, bool FIRST>
-__device__ __forceinline__ void gla_seq_chunk(SeqSmem<VT>& sm, const SeqIn<VT>& pf, const SeqIn<VT>& nv,
-                                              SeqIn<VT>& nx, f32x4 (&Sacc)[VT / 16], int ci, int nc,
-                                              size_t chunk0, size_t tokn, int vt,
-                                              const uint8_t* __restrict__ ws,
-                                              const uint16_t* __restrict__ v,
-                                              uint16_t* __restrict__ o) {
-  constexpr int NVB = VT / 16, PV = SeqSmem<VT>::PV, PO = SeqSmem<VT>::PO;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int l16 = lane & 15, lq = lane >> 4;
-  const int rb = wave & 3, vbl = (wave >> 2) % NVB, kcol = wave * 16 + l16;
-  const int cur = ci & 1;
-  const int c2 = min(ci + 2, nc - 1);
-  const uint8_t* wsc = ws + (chunk0 + c2) * kWChunk;
-  const size_t tok2 = tokn + (size_t)c2 * C;
-  seq_fetch<VT, 0>(nx, wsc, v, tok2, vt);
-  if constexpr (!FIRST) store_o<VT>(sm, o, tokn + (size_t)(ci - 1) * C, vt, cur ^ 1);
-  __builtin_amdgcn_sched_barrier(0);
-
-  // ---- output tile (rb, vbl): O = O~ + Q^ S^T (waves w and w + 4 coincide when NVB = 1)
-  {
-    f32x4 acc = {lo_bf(pf.x.x), hi_bf(pf.x.x), lo_bf(pf.x.y), hi_bf(pf.x.y)};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      acc = mfma(ld8(sm.Qs[cur] + ((rb * 4 + ks) * 64 + lane) * 8),
-                 ld8(sm.Sb[cur] + (vbl * 16 + l16) * PQ + ks * 32 + lq * 8), acc);
-    }
-    if (NVB == 2 || wave < 4) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sm.Os[cur][(rb * 16 + lq * 4 + i) * PO + vbl * 16 + l16] = f32_to_bf16(acc[i]);
+      for (int j = 0; j < 4; ++j) x[j] = fmaf(g[j], x[j], bb[j]);
     }
   }
-  __builtin_amdgcn_sched_barrier(0);
-  seq_fetch<VT, 1>(nx, wsc, v, tok2, vt);
-  __builtin_amdgcn_sched_barrier(0);
-  stage<VT>(sm, nv, cur ^ 1);
-
-  // ---- state tiles (vb, kb = wave): S <- e^{b_C} o S + V^T K^, and its next bf16 copy
-#pragma unroll
-  for (int vb = 0; vb < NVB; ++vb) {
-    f32x4 acc = Sacc[vb] * pf.ec;
-#pragma unroll
-    for (int js = 0; js < 2; ++js)
-      acc = mfma(ld_tr8(sm.Vs[cur], PV, js * 32, vb * 16), as_bf8(pf.kh[js]), acc);
-    Sacc[vb] = acc;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sm.Sb[cur ^ 1][(vb * 16 + lq * 4 + i) * PQ + kcol] = f32_to_bf16(acc[i]);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  seq_fetch<VT, 2>(nx, wsc, v, tok2, vt);
-  lds_barrier();
-}
-
-}  // namespace gla
-
-template <int VT>
-__global__ __launch_bounds__(512) void gla_chunk_seq_kernel(
-    const uint8_t* __restrict__ ws, const uint16_t* __restrict__ v, const float* __restrict__ S0,
-    float* __restrict__ ST, uint16_t* __restrict__ o, int N, int T) {
-  using namespace gla;
-  constexpr int NVB = VT / 16;           // value blocks of 16 in the tile
-  constexpr int TPS = kD / VT;           // tiles per sequence
-  __shared__ SeqSmem<VT> sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l16 = lane & 15, lq = lane >> 4;
-  // block -> (sequence, value tile); the tiles of one sequence share an XCD
-  int n, vt;
-  {
-    const int bid = blockIdx.x;
-    if ((N & 7) == 0) {
-      const int xcd = bid & 7, slot = bid >> 3;
-      n = (slot / TPS) * 8 + xcd;
-      vt = slot % TPS;
-    } else {
-      n = bid / TPS;
-      vt = bid % TPS;
-    }
-  }
-  const int v0 = vt * VT;
-  const int nc = T / C;
-  const int kcol = wave * 16 + l16;
-
-  // state tiles: key block = wave, value blocks vb < NVB; the lane holds
-  // S[v0 + 16 vb + 4 lq + i][kcol]
-  f32x4 Sacc[NVB];
-#pragma unroll
-  for (int vb = 0; vb < NVB; ++vb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      Sacc[vb][i] = S0 ? S0[((size_t)n * kD + v0 + vb * 16 + lq * 4 + i) * kD + kcol] : 0.f;
-      sm.Sb[0][(vb * 16 + lq * 4 + i) * PQ + kcol] = f32_to_bf16(Sacc[vb][i]);
-    }
-
-  if (nc > 0) {
-    const size_t chunk0 = (size_t)n * nc, tokn = (size_t)n * T;
-    const uint8_t* wsn = ws + chunk0 * kWChunk;
-    // three operand sets in rotation: chunk ci computes from set ci % 3, stages the
-    // LDS operands of set (ci + 1) % 3 and loads chunk ci + 2 into set (ci + 2) % 3
-    SeqIn<VT> p0, p1, p2;
-    seq_fetch_all<VT>(p0, wsn, v, tokn, vt);
-    {
-      const int c1 = min(1, nc - 1);
-      seq_fetch_all<VT>(p1, wsn + c1 * kWChunk, v, tokn + (size_t)c1 * C, vt);
-    }
-    stage<VT>(sm, p0, 0);
-    lds_barrier();
-    gla_seq_chunk<VT, true>(sm, p0, p1, p2, Sacc, 0, nc, chunk0, tokn, vt, ws, v, o);
-    int ci = 1;
-    for (; ci + 2 < nc; ci += 3) {
-      gla_seq_chunk<VT, false>(sm, p1, p2, p0, Sacc, ci, nc, chunk0, tokn, vt, ws, v, o);
-      gla_seq_chunk<VT, false>(sm, p2, p0, p1, Sacc, ci + 1, nc, chunk0, tokn, vt, ws, v, o);
-      gla_seq_chunk<VT, false>(sm, p0, p1, p2, Sacc, ci + 2, nc, chunk0, tokn, vt, ws, v, o);
-    }
-    if (ci < nc) gla_seq_chunk<VT, false>(sm, p1, p2, p0, Sacc, ci, nc, chunk0, tokn, vt, ws, v, o);
-    if (ci + 1 < nc) gla_seq_chunk<VT, false>(sm, p2, p0, p1, Sacc, ci + 1, nc, chunk0, tokn, vt, ws, v, o);
-    store_o<VT>(sm, o, tokn + (size_t)(nc - 1) * C, vt, (nc - 1) & 1);
-  }
-
-#pragma unroll
-  for (int vb = 0; vb < NVB; ++vb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      ST[((size_t)n * kD + v0 + vb * 16 + lq * 4 + i) * kD + kcol] = Sacc[vb][i];
 }
 
 }  // namespace gdnrt
@@ -456,7 +362,7 @@ using namespace gdnrt;
 
 extern "C" size_t gla_chunk_fwd_workspace_bytes(int N, int T, int dk, int dv, int chunk) {
   if (N <= 0 || T <= 0 || dk != kD || dv != kD || chunk != kChunk || T % kChunk) return 0;
-  return (size_t)N * (T / kChunk) * gla::kWChunk;
+  return gla::plan(N, T / kChunk).total;
 }
 
 extern "C" int gla_chunk_fwd(const void* q, const void* k, const void* v, const float* log_g,
@@ -473,8 +379,8 @@ extern "C" int gla_chunk_fwd(const void* q, const void* k, const void* v, const 
   if (N == 0) return clear_error();
   if (!ST || (T > 0 && (!q || !k || !v || !log_g || !o)))
     return set_error(GDNRT_EINVAL, "gla_chunk_fwd: null pointer argument");
-  const size_t nchunks = (size_t)N * (T / kChunk);
-  const size_t need = nchunks * gla::kWChunk;
+  const gla::Plan pl = gla::plan(N, T / kChunk);
+  const size_t need = T > 0 ? pl.total : 0;
   if (ws_bytes < need || (need && !workspace))
     return set_error(GDNRT_EINVAL, "gla_chunk_fwd: workspace of %zu bytes needed, %zu given", need, ws_bytes);
   if ((T > 0 && (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_g) || !aligned16(o) ||
@@ -494,22 +400,20 @@ extern "C" int gla_chunk_fwd(const void* q, const void* k, const void* v, const 
     return set_error(GDNRT_EINVAL, "gla_chunk_fwd: buffers overlap (only ST may equal S0)");
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  if (T > 0) {
-    // one persistent block per CU (a block's LDS fills most of one)
-    const unsigned grid = (unsigned)(nchunks < 256 ? nchunks : 256);
-    hipLaunchKernelGGL(gla_chunk_prep_kernel, dim3(grid), dim3(gla::NT), 0, s,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                       static_cast<const uint16_t*>(v), log_g, ws, T, (int)nchunks);
-    int rc = check_launch("gla_chunk_fwd (prep)");
-    if (rc != GDNRT_OK) return rc;
+  const uint16_t* q16 = static_cast<const uint16_t*>(q);
+  const uint16_t* k16 = static_cast<const uint16_t*>(k);
+  const uint16_t* v16 = static_cast<const uint16_t*>(v);
+  float* Bb = pl.P > 1 ? reinterpret_cast<float*>(ws + pl.b_off) : nullptr;
+  float* Gb = pl.P > 1 ? reinterpret_cast<float*>(ws + pl.g_off) : nullptr;
+  float* Sst = pl.P > 1 ? reinterpret_cast<float*>(ws + pl.s_off) : nullptr;
+  if (pl.P > 1) {
+    hipLaunchKernelGGL(gla_fused_kernel<false>, dim3((unsigned)(N * (pl.P - 1) * pl.R)), dim3(gla::NB), 0, s, q16,
+                       k16, v16, log_g, ws, S0, (const float*)nullptr, Bb, Gb, (float*)nullptr, (uint16_t*)nullptr, T,
+                       pl.P, pl.Lseg, pl.R);
+    hipLaunchKernelGGL(gla_seg_combine_kernel, dim3((unsigned)(N * 16)), dim3(256), 0, s, S0, Bb, Gb, Sst, pl.P, pl.R);
   }
   // T == 0 launches too: the kernel then copies the incoming state (or zeros) to ST.
-  // Value tiles of 16 when there are too few sequences to fill the chip with 32.
-  if (N * 4 < 256)
-    hipLaunchKernelGGL((gla_chunk_seq_kernel<16>), dim3((unsigned)(N * 8)), dim3(gla::NT), 0, s, ws,
-                       static_cast<const uint16_t*>(v), S0, ST, static_cast<uint16_t*>(o), N, T);
-  else
-    hipLaunchKernelGGL((gla_chunk_seq_kernel<32>), dim3((unsigned)(N * 4)), dim3(gla::NT), 0, s, ws,
-                       static_cast<const uint16_t*>(v), S0, ST, static_cast<uint16_t*>(o), N, T);
+  hipLaunchKernelGGL(gla_fused_kernel<true>, dim3((unsigned)(N * pl.P)), dim3(gla::NB), 0, s, q16, k16, v16, log_g, ws,
+                     S0, Sst, Bb, Gb, ST, static_cast<uint16_t*>(o), T, pl.P, pl.Lseg, pl.R);
   return check_launch("gla_chunk_fwd");
 }

@@ -85,7 +85,7 @@ __global__ __launch_bounds__(256) void gla_all_scan_step_kernel(const float* S_r
 
 namespace zeco {
 
-// One chunk's operands of a correction wave: the four Q^ fragments of its token block
+// One chunk's operands of a correction wave: its four Q^ operands of its token block
 // and its 32 bytes of o (16 consecutive value channels of one token).
 struct CorrIn {
   u32x4 qf[4];
@@ -100,7 +100,7 @@ __device__ __forceinline__ void corr_load(CorrIn& in, const uint8_t* __restrict_
   const uint16_t* orow = o + (((size_t)n * nc + c) * kChunk + tb * 16 + l16) * kD + 16 * (vb0 + lq);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
-    in.qf[ks] = *reinterpret_cast<const u32x4*>(wsc + ((size_t)(tb * 4 + ks) * 64 + lane) * 16);
+    in.qf[ks] = *reinterpret_cast<const u32x4*>(wsc + ((size_t)(16 * tb + l16) * kD + 32 * ks + 8 * lq) * 2);
   in.ov[0] = *reinterpret_cast<const u32x4*>(orow);
   in.ov[1] = *reinterpret_cast<const u32x4*>(orow + 8);
 }
@@ -118,7 +118,7 @@ __device__ __forceinline__ int s_off(int v, int k) {
 // sequence n. The block stages S_in[n] in LDS as bf16; wave w forms four transposed
 // output tiles of each chunk, D[v][t] = sum_k S[v][k] (Q^ o gamma~)[t][k], for the
 // tokens of block tb = w & 3 and the 64 value channels from 16 vb0, vb0 = 4 (w >> 2):
-// the Q^ fragment of the workspace is already the B operand of that product (lane l16 =
+// 16 bytes of a row of Q^ in the workspace are the B operand of that product (lane l16 =
 // token, 8 consecutive keys), scaled by the decay of its keys. Row i = 4 lq + r of tile
 // j stands for value channel 16 vb0 + 16 lq + 4 j + r, so that the 16 D values a lane
 // holds over the four tiles are 16 consecutive channels of one token: o is read and

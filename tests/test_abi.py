@@ -91,7 +91,10 @@ def test_chunk_validation(lib):
     assert g(p, p, p, p, None, p, p, 2, 128, 128, 128, 32, 1, p, 1 << 30, None) == ESHAPE  # chunk
     assert g(p, p, p, p, None, p, p, 2, 128, 128, 128, 64, 0, p, 1 << 30, None) == EDTYPE  # fp32 io
     assert g(p, p, p, p, None, p, p, 2, 128, 128, 128, 64, 1, p, 10, None) == EINVAL       # workspace
-    assert lib.gla_chunk_fwd_workspace_bytes(64, 4096, 128, 128, 64) == 64 * 64 * 49664
+    # per chunk Q o e^b and e^{b_C} (16,896 B); 4 segments of 16 chunks per sequence: the
+    # end states and decays of the 2 halves of each of the first 3, the start states of 4
+    assert lib.gla_chunk_fwd_workspace_bytes(64, 4096, 128, 128, 64) == \
+        64 * 64 * 16896 + 64 * 3 * 2 * (65536 + 512) + 64 * 4 * 65536
     assert lib.gla_chunk_fwd_workspace_bytes(64, 100, 128, 128, 64) == 0
     d = lib.gdn_chunk_fwd
     assert lib.gdn_chunk_fwd_workspace_bytes(32, 16384, 128, 128, 64) == 32 * 256 * 81984
@@ -239,7 +242,7 @@ def test_gdn_bwd_validation(lib):
 
 def test_gla_shard_validation(lib):
     p = ctypes.c_void_p(4096)
-    ws_need = 2 * 2 * 49664
+    ws_need = 2 * 2 * 16896
     # gla_shard_decay(workspace, ws_bytes, gamma, N, T, dk, chunk, stream)
     f = lib.gla_shard_decay
     assert f(p, ws_need - 1, ctypes.c_void_p(1 << 30), 2, 128, 128, 64, None) == EINVAL
