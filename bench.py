@@ -385,7 +385,7 @@ def bench_zeco(K=20, W=3, B=4, H=16, T=4096, blocks=4):
     edges = [int(x) for x in np.linspace(0, D, blocks + 1)]
 
     def local(i):
-        m.gla_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_g"], None, S_loc, o, ws)
+        m.gla_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_g"], None, S_loc, o, ws, shard=True)
 
     def decay(i):
         m.gla_shard_decay(ws, N, T, gam)

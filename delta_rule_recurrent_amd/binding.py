@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(HERE, "libgdnrt.so")
 
 OK, EINVAL, ESHAPE, EALIGN, EDTYPE, ESTATE, ELAUNCH = range(7)
 F32, BF16 = 0, 1
+GLA_SHARD = 0x100   # or-ed into gla_chunk_fwd's io: keep what the shard calls read
 D = 128
 CHUNK = 64
 
@@ -213,11 +214,12 @@ def gla_chunk_workspace(N, T, device="cuda", chunk=CHUNK):
     return torch.empty(max(nb, 16), dtype=torch.uint8, device=device)
 
 
-def gla_chunk_fwd(q, k, v, log_g, S0=None, ST=None, o=None, workspace=None, chunk=CHUNK):
+def gla_chunk_fwd(q, k, v, log_g, S0=None, ST=None, o=None, workspace=None, chunk=CHUNK, shard=False):
     """Gated linear attention chunkwise forward from an incoming state.
 
     q, k, v [N][T][128] bf16; log_g [N][T][128] fp32; S0 [N][128][128] fp32 or
-    None; workspace from gla_chunk_workspace (allocated here if None).
+    None; workspace from gla_chunk_workspace (allocated here if None); shard: also
+    leave in the workspace what gla_shard_decay / gla_shard_output_correct read.
     Returns (o [N][T][128] bf16, ST [N][128][128] fp32)."""
     N, T, _ = q.shape
     for n_, t_ in (("q", q), ("k", k), ("v", v)):
@@ -236,7 +238,7 @@ def gla_chunk_fwd(q, k, v, log_g, S0=None, ST=None, o=None, workspace=None, chun
     _need(workspace, "workspace", torch.uint8)
     _check("gla_chunk_fwd", lib().gla_chunk_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(S0), _ptr(ST), _ptr(o),
-        N, T, D, D, chunk, BF16, _ptr(workspace), workspace.numel(), _stream()))
+        N, T, D, D, chunk, BF16 | (GLA_SHARD if shard else 0), _ptr(workspace), workspace.numel(), _stream()))
     return o, ST
 
 
@@ -298,7 +300,7 @@ def gla_shard_local(q, k, v, log_g, workspace=None, chunk=CHUNK):
     N, T, _ = q.shape
     if workspace is None:
         workspace = gla_chunk_workspace(N, T, q.device, chunk)
-    o, S_local = gla_chunk_fwd(q, k, v, log_g, None, None, None, workspace, chunk)
+    o, S_local = gla_chunk_fwd(q, k, v, log_g, None, None, None, workspace, chunk, shard=True)
     gamma = gla_shard_decay(workspace, N, T, chunk=chunk)
     return o, S_local, gamma, workspace
 

@@ -141,11 +141,11 @@ __device__ __forceinline__ f32x2 exp2v(f32x2 x) {
 
 }  // namespace gla
 
-// OUT: pass 2 (one block per (sequence, segment), outputs, the shard calls' workspace);
+// OUT: pass 2 (one block per (sequence, segment), outputs; KEEP: the shard calls' workspace);
 // else pass 1 (one block per (sequence, piece of a segment < P - 1): end state from zero
 // and the piece's decay). Wave w owns value channels 16 w .. 16 w + 15; in the
 // elementwise work thread (lane, w) owns channels 2 lane, 2 lane + 1 of tokens 8 w .. 8 w + 7.
-template <bool OUT>
+template <bool OUT, bool KEEP>
 __global__ __launch_bounds__(512, OUT ? 2 : 4) void gla_fused_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ log_g, uint8_t* __restrict__ ws, const float* __restrict__ S0,
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(512, OUT ? 2 : 4) void gla_fused_kernel(
           bC += te;
         }
         const f32x2 emv = exp2v(bm);
-        unsigned qh[8];   // Q^ of the thread's tokens, stored once every prefetched q and k is used
+        unsigned qh[8];   // KEEP: Q^ of the thread's tokens, stored once every prefetched q and k is used
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int r = 8 * w + i;
@@ -220,7 +220,7 @@ __global__ __launch_bounds__(512, OUT ? 2 : 4) void gla_fused_kernel(
             const f32x2 qr = bf2f(in.q[i]) * exp2v(d);
             *reinterpret_cast<unsigned*>(sm.Qr + r * PQ + 2 * cp) = pk2(qr);
             *reinterpret_cast<unsigned*>(sm.Kr + r * PT + 2 * cp) = pk2(kf * exp2v(-d));
-            qh[i] = pk2(qr * emv);
+            if constexpr (KEEP) qh[i] = pk2(qr * emv);
           } else {
             *reinterpret_cast<unsigned*>(sm.Kr + r * PT + 2 * cp) = pk2(kf * exp2v(bC - b));
           }
@@ -228,7 +228,7 @@ __global__ __launch_bounds__(512, OUT ? 2 : 4) void gla_fused_kernel(
         // the next chunk's q and k go out before this chunk's workspace stores; its
         // log-gates and v follow later in the chunk
         if (c + 1 < c1) fetch<OUT, 1>(in, q, k, v, log_g, tok0 + C, t);
-        if constexpr (OUT) {   // Q^ = Qr o e^{b_m}, row-major, for the shard calls
+        if constexpr (KEEP) {   // Q^ = Qr o e^{b_m}, row-major, for the shard calls
 #pragma unroll
           for (int i = 0; i < 8; ++i)
             *reinterpret_cast<unsigned*>(wsc + kWQ + ((size_t)(8 * w + i) * kD + 2 * cp) * 2) = qh[i];
@@ -239,7 +239,7 @@ __global__ __launch_bounds__(512, OUT ? 2 : 4) void gla_fused_kernel(
           if constexpr (OUT) {
             *reinterpret_cast<f32x2*>(sm.em + 2 * cp) = emv;
             *reinterpret_cast<f32x2*>(sm.ef + 2 * cp) = exp2v(bC - bm);
-            *reinterpret_cast<f32x2*>(reinterpret_cast<float*>(wsc + kWE) + 2 * cp) = ecv;
+            if constexpr (KEEP) *reinterpret_cast<f32x2*>(reinterpret_cast<float*>(wsc + kWE) + 2 * cp) = ecv;
           } else {
             lsum += bC;
           }
@@ -373,7 +373,9 @@ extern "C" int gla_chunk_fwd(const void* q, const void* k, const void* v, const 
     return set_error(GDNRT_ESHAPE, "gla_chunk_fwd: d_k=%d d_v=%d, only 128 is supported", dk, dv);
   if (chunk != kChunk) return set_error(GDNRT_ESHAPE, "gla_chunk_fwd: chunk=%d, only 64 is supported", chunk);
   if (T % kChunk) return set_error(GDNRT_ESHAPE, "gla_chunk_fwd: T=%d is not a multiple of 64", T);
-  if (io != GDNRT_BF16) return set_error(GDNRT_EDTYPE, "gla_chunk_fwd: io must be GDNRT_BF16");
+  const bool keep = (io & GDNRT_GLA_SHARD) != 0;
+  if ((io & ~GDNRT_GLA_SHARD) != GDNRT_BF16)
+    return set_error(GDNRT_EDTYPE, "gla_chunk_fwd: io must be GDNRT_BF16, optionally | GDNRT_GLA_SHARD");
   if ((size_t)N * (T / kChunk) > 0x7fffffffu || (size_t)N * 8 > 0x7fffffffu)
     return set_error(GDNRT_ESHAPE, "gla_chunk_fwd: N=%d T=%d too large", N, T);
   if (N == 0) return clear_error();
@@ -407,13 +409,17 @@ extern "C" int gla_chunk_fwd(const void* q, const void* k, const void* v, const 
   float* Gb = pl.P > 1 ? reinterpret_cast<float*>(ws + pl.g_off) : nullptr;
   float* Sst = pl.P > 1 ? reinterpret_cast<float*>(ws + pl.s_off) : nullptr;
   if (pl.P > 1) {
-    hipLaunchKernelGGL(gla_fused_kernel<false>, dim3((unsigned)(N * (pl.P - 1) * pl.R)), dim3(gla::NB), 0, s, q16,
+    hipLaunchKernelGGL((gla_fused_kernel<false, false>), dim3((unsigned)(N * (pl.P - 1) * pl.R)), dim3(gla::NB), 0, s, q16,
                        k16, v16, log_g, ws, S0, (const float*)nullptr, Bb, Gb, (float*)nullptr, (uint16_t*)nullptr, T,
                        pl.P, pl.Lseg, pl.R);
     hipLaunchKernelGGL(gla_seg_combine_kernel, dim3((unsigned)(N * 16)), dim3(256), 0, s, S0, Bb, Gb, Sst, pl.P, pl.R);
   }
   // T == 0 launches too: the kernel then copies the incoming state (or zeros) to ST.
-  hipLaunchKernelGGL(gla_fused_kernel<true>, dim3((unsigned)(N * pl.P)), dim3(gla::NB), 0, s, q16, k16, v16, log_g, ws,
-                     S0, Sst, Bb, Gb, ST, static_cast<uint16_t*>(o), T, pl.P, pl.Lseg, pl.R);
+  if (keep)
+    hipLaunchKernelGGL((gla_fused_kernel<true, true>), dim3((unsigned)(N * pl.P)), dim3(gla::NB), 0, s, q16, k16, v16,
+                       log_g, ws, S0, Sst, Bb, Gb, ST, static_cast<uint16_t*>(o), T, pl.P, pl.Lseg, pl.R);
+  else
+    hipLaunchKernelGGL((gla_fused_kernel<true, false>), dim3((unsigned)(N * pl.P)), dim3(gla::NB), 0, s, q16, k16, v16,
+                       log_g, ws, S0, Sst, Bb, Gb, ST, static_cast<uint16_t*>(o), T, pl.P, pl.Lseg, pl.R);
   return check_launch("gla_chunk_fwd");
 }

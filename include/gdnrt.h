@@ -52,6 +52,10 @@ typedef enum {
 
 typedef enum { GDNRT_F32 = 0, GDNRT_BF16 = 1 } gdnrt_dtype;
 
+/* Flag or-ed into gla_chunk_fwd's io: also leave in the workspace what the
+ * sequence-parallel shard calls below read (gla_shard_decay, gla_shard_output_correct). */
+enum { GDNRT_GLA_SHARD = 0x100 };
+
 /*
  * Gated DeltaNet recurrent step ("LeapQuant: an 8-bit recurrent state that stops
  * rounding every token", section "The state, from the update rule up": the delta
@@ -98,11 +102,14 @@ GDNRT_API int kda_decode_step(float* S, const void* q, const void* k, const void
  *   q, k   [N][T][dk] bf16.   v, o [N][T][dv] bf16.   log_g [N][T][dk] fp32 (<= 0).
  *   S0     [N][dv][dk] fp32 incoming state, or NULL for zero.
  *   ST     [N][dv][dk] fp32 final state (may equal S0: read before written).
+ *   io     GDNRT_BF16, or GDNRT_BF16 | GDNRT_GLA_SHARD for a shard of the
+ *          sequence-parallel calls below.
  *   workspace: caller-owned device memory of gla_chunk_fwd_workspace_bytes() bytes,
- *   16-byte aligned, overwritten (the per-chunk state-independent operands in bf16:
- *   Q o e^b, K o e^{b_C - b} and the intra-chunk output, plus e^{b_C} in fp32, b the
- *   cumulative log-gate within the chunk; 49,664 bytes per chunk). May be NULL when
- *   T = 0.
+ *   16-byte aligned, overwritten: 16,896 bytes per chunk that GDNRT_GLA_SHARD fills
+ *   (Q o e^b in bf16, row-major, and e^{b_C} in fp32, b the cumulative log-gate within
+ *   the chunk), then the call's own segment buffers (the chunks of each sequence are
+ *   cut into segments run in parallel: their end states and decays, and start states).
+ *   May be NULL when T = 0.
  * T must be a multiple of chunk (64).
  */
 GDNRT_API int gla_chunk_fwd(const void* q, const void* k, const void* v, const float* log_g,
@@ -120,9 +127,9 @@ GDNRT_API size_t gla_chunk_fwd_workspace_bytes(int N, int T, int dk, int dv, int
  * Computation", "Global State Update Formula" (eq. 6), "All-Scan Collective
  * Communication" and "The Complete Forward Algorithm"). The sequence is cut into
  * contiguous shards of whole chunks, one per device. A device:
- *   1. runs gla_chunk_fwd on its shard from a zero state (S0 = NULL): local outputs o,
- *      local final state S_[N] (its ST), and a workspace holding per chunk
- *      Q o e^b and the chunk decay gamma = e^{b_C};
+ *   1. runs gla_chunk_fwd on its shard from a zero state (S0 = NULL) with
+ *      io = GDNRT_BF16 | GDNRT_GLA_SHARD: local outputs o, local final state S_[N] (its
+ *      ST), and a workspace holding per chunk Q o e^b and the chunk decay gamma = e^{b_C};
  *   2. gla_shard_decay: the cumulative decays gamma~ from that workspace;
  *   3. gla_all_scan_step, block by block along d_k: receives block k of the state
  *      from the previous device and forms the block to send to the next one;

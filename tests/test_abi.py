@@ -90,6 +90,9 @@ def test_chunk_validation(lib):
     assert g(p, p, p, p, None, p, p, 2, 100, 128, 128, 64, 1, p, 1 << 30, None) == ESHAPE  # T % 64
     assert g(p, p, p, p, None, p, p, 2, 128, 128, 128, 32, 1, p, 1 << 30, None) == ESHAPE  # chunk
     assert g(p, p, p, p, None, p, p, 2, 128, 128, 128, 64, 0, p, 1 << 30, None) == EDTYPE  # fp32 io
+    assert g(p, p, p, p, None, p, p, 2, 128, 128, 128, 64, 0x100, p, 1 << 30, None) == EDTYPE  # shard, fp32
+    assert g(p, p, p, p, None, p, p, 2, 128, 128, 128, 64, 0x201, p, 1 << 30, None) == EDTYPE  # unknown flag
+    assert g(p, p, p, p, None, p, p, 2, 128, 128, 128, 64, 0x101, p, 10, None) == EINVAL    # shard, workspace
     assert g(p, p, p, p, None, p, p, 2, 128, 128, 128, 64, 1, p, 10, None) == EINVAL       # workspace
     # per chunk Q o e^b and e^{b_C} (16,896 B); 4 segments of 16 chunks per sequence: the
     # end states and decays of the 2 halves of each of the first 3, the start states of 4
