@@ -41,7 +41,20 @@ namespace gla {
 using namespace gdc;   // C, PQ, PC, ld8, ld_tr8, mfma, tri_pair, lo_bf, hi_bf
 
 constexpr int NB = 512;       // threads per block: 8 waves
-constexpr int PT = kD + 16;   // bf16 pitch of 128-wide rows read transposed (ds_read_b64_tr_b16)
+// Kr and v, read transposed (ds_read_b64_tr_b16) and, Kr, by rows for the scores: rows
+// of PT bf16, and in the rows with bit 3 set column c stored at c ^ 72. A transposed read
+// takes 4 rows at 8-bank steps in each group of 16 lanes, groups 8 rows apart: bit 6 of
+// the swap moves those by 32 banks. A row read takes 16 consecutive rows, row r and r + 8
+// on the same banks without the swap: bit 3 moves them by 4 banks. Both swaps move whole
+// 8-column pieces, so every access stays one piece.
+constexpr int PT = kD + 16;
+__device__ __forceinline__ int swz(int row) { return (row & 8) * 9; }
+// Qr's keys in LDS: key 32 ks + 16 h + 4 a + b at column 32 ks + 8 a + 4 h + b, so that the
+// eight keys the inter-chunk product pairs in one lane (four from each 16-key half of a
+// 32-key block) are one 16-byte piece
+__device__ __forceinline__ int qcol(int key) {
+  return (key & ~31) | ((key & 12) << 1) | ((key & 16) >> 2) | (key & 3);
+}
 constexpr int kMaxSeg = 16;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr size_t kStateBytes = (size_t)kD * kD * 4;
@@ -75,7 +88,7 @@ __host__ inline Plan plan(int N, int nc) {
 }
 
 struct alignas(16) Smem {
-  uint16_t Qr[C * PQ];               // q o e^{b - b_m} [t][k]
+  uint16_t Qr[C * PQ];               // q o e^{b - b_m} [t][qcol(k)]
   uint16_t Kr[C * PT];               // pass 2: k o e^{b_m - b}; pass 1: k o e^{b_C - b}
   uint16_t V[C * PT];                // v [t][v]
   uint16_t A[C * PC];                // masked scores [r][j]
@@ -123,12 +136,22 @@ __device__ __forceinline__ void stage(Smem& sm, In& in, int t) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int p = t + NB * h;
-    *reinterpret_cast<u32x4*>(sm.V + (p >> 4) * PT + 8 * (p & 15)) = in.v[h];
+    *reinterpret_cast<u32x4*>(sm.V + (p >> 4) * PT + ((8 * (p & 15)) ^ swz(p >> 4))) = in.v[h];
   }
   in.g[0] *= kLog2e;
 #pragma unroll
   for (int i = 1; i < 8; ++i) in.g[i] = in.g[i] * kLog2e + in.g[i - 1];
   *reinterpret_cast<f32x2*>(sm.tot + eg * kD + 2 * cp) = in.g[7];
+}
+
+// ld_tr8 (the MFMA operand X[c0 + 8 lq + e][n0 + l16]) from a matrix stored with swz
+__device__ __forceinline__ bf16x8 ld_tr8s(const uint16_t* X, int c0, int n0) {
+  const int lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
+  const int row = c0 + 8 * g + (j >> 2);
+  const uint16_t* p = X + row * PT + ((n0 + 4 * (j & 3)) ^ swz(row));
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * PT));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 __device__ __forceinline__ f32x2 bf2f(unsigned w) { return f32x2{lo_bf(w), hi_bf(w)}; }
@@ -218,11 +241,11 @@ __global__ __launch_bounds__(512, OUT ? 2 : 4) void gla_fused_kernel(
           if constexpr (OUT) {
             const f32x2 d = b - bm;
             const f32x2 qr = bf2f(in.q[i]) * exp2v(d);
-            *reinterpret_cast<unsigned*>(sm.Qr + r * PQ + 2 * cp) = pk2(qr);
-            *reinterpret_cast<unsigned*>(sm.Kr + r * PT + 2 * cp) = pk2(kf * exp2v(-d));
+            *reinterpret_cast<unsigned*>(sm.Qr + r * PQ + qcol(2 * cp)) = pk2(qr);
+            *reinterpret_cast<unsigned*>(sm.Kr + r * PT + ((2 * cp) ^ swz(r))) = pk2(kf * exp2v(-d));
             if constexpr (KEEP) qh[i] = pk2(qr * emv);
           } else {
-            *reinterpret_cast<unsigned*>(sm.Kr + r * PT + 2 * cp) = pk2(kf * exp2v(bC - b));
+            *reinterpret_cast<unsigned*>(sm.Kr + r * PT + ((2 * cp) ^ swz(r))) = pk2(kf * exp2v(bC - b));
           }
         }
         // the next chunk's q and k go out before this chunk's workspace stores; its
@@ -248,11 +271,12 @@ __global__ __launch_bounds__(512, OUT ? 2 : 4) void gla_fused_kernel(
       lds_barrier();
 
       // ---- wave w: the value operand of its tile (lane (l16, lq) holds v[32 js + 8 lq + e][16 w + l16])
-      const bf16x8 vt0 = ld_tr8(sm.V, PT, 0, 16 * w), vt1 = ld_tr8(sm.V, PT, 32, 16 * w);
+      const bf16x8 vt0 = ld_tr8s(sm.V, 0, 16 * w), vt1 = ld_tr8s(sm.V, 32, 16 * w);
       f32x4 oacc[4];
       if constexpr (OUT) {
         // inter-chunk outputs, transposed: D[v][t] = sum_k (S o e^{b_m})[v][k] Qr[t][k],
-        // contraction slot 8 lq + e <-> key 32 ks + 4 lq + e (e < 4), 32 ks + 16 + 4 lq + e - 4
+        // contraction slot 8 lq + e <-> key 32 ks + 4 lq + e (e < 4), 32 ks + 16 + 4 lq + e - 4:
+        // one 16-byte piece of Qr's row
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) oacc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -262,18 +286,14 @@ __global__ __launch_bounds__(512, OUT ? 2 : 4) void gla_fused_kernel(
           const u32x2 a = pk4(St[2 * ks] * e0), b = pk4(St[2 * ks + 1] * e1);
           const bf16x8 sa = as_bf8(u32x4{a[0], a[1], b[0], b[1]});
 #pragma unroll
-          for (int tb = 0; tb < 4; ++tb) {
-            const uint16_t* qp = sm.Qr + (16 * tb + l16) * PQ + 32 * ks + 4 * lq;
-            const u32x2 x0 = *reinterpret_cast<const u32x2*>(qp), x1 = *reinterpret_cast<const u32x2*>(qp + 16);
-            oacc[tb] = mfma(sa, as_bf8(u32x4{x0[0], x0[1], x1[0], x1[1]}), oacc[tb]);
-          }
+          for (int tb = 0; tb < 4; ++tb) oacc[tb] = mfma(sa, ld8(sm.Qr + (16 * tb + l16) * PQ + 32 * ks + 8 * lq), oacc[tb]);
         }
       }
       if (c + 1 < c1) fetch<OUT, 2>(in, q, k, v, log_g, tok0 + C, t);
       // state rows of the wave's tile: S^T <- e^{b_C} o S^T + K^T V through Kr
 #pragma unroll
       for (int kb = 0; kb < 8; ++kb) {
-        const bf16x8 k0 = ld_tr8(sm.Kr, PT, 0, 16 * kb), k1 = ld_tr8(sm.Kr, PT, 32, 16 * kb);
+        const bf16x8 k0 = ld_tr8s(sm.Kr, 0, 16 * kb), k1 = ld_tr8s(sm.Kr, 32, 16 * kb);
         const f32x4 ecv = *reinterpret_cast<const f32x4*>(sm.ec + 16 * kb + 4 * lq);
         if constexpr (OUT) {
           const f32x4 efv = *reinterpret_cast<const f32x4*>(sm.ef + 16 * kb + 4 * lq);
@@ -285,15 +305,20 @@ __global__ __launch_bounds__(512, OUT ? 2 : 4) void gla_fused_kernel(
       }
       if (c + 1 < c1) fetch<OUT, 3>(in, q, k, v, log_g, tok0 + C, t);
       if constexpr (OUT) {
-        // masked scores over the lower triangle of 16 x 16 tiles
+        // masked scores over the lower triangle of 16 x 16 tiles; the keys of a 16-byte
+        // piece of Qr come from two 8-byte pieces of Kr
         for (int u = w; u < 10; u += 8) {
           int rb, cb;
           tri_pair(u, rb, cb);
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          const uint16_t* kp = sm.Kr + (cb * 16 + l16) * PT;
 #pragma unroll
-          for (int ks = 0; ks < 4; ++ks)
-            acc = mfma(ld8(sm.Qr + (rb * 16 + l16) * PQ + ks * 32 + lq * 8),
-                       ld8(sm.Kr + (cb * 16 + l16) * PT + ks * 32 + lq * 8), acc);
+          for (int ks = 0; ks < 4; ++ks) {
+            const u32x2 x0 = *reinterpret_cast<const u32x2*>(kp + ((32 * ks + 4 * lq) ^ swz(l16)));
+            const u32x2 x1 = *reinterpret_cast<const u32x2*>(kp + ((32 * ks + 16 + 4 * lq) ^ swz(l16)));
+            acc = mfma(ld8(sm.Qr + (rb * 16 + l16) * PQ + ks * 32 + lq * 8), as_bf8(u32x4{x0[0], x0[1], x1[0], x1[1]}),
+                       acc);
+          }
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = rb * 16 + lq * 4 + i, jj = cb * 16 + l16;
