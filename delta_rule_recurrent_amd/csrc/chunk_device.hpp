@@ -93,6 +93,34 @@ __device__ __forceinline__ bf16x8 ld_tr8(const uint16_t* X, int pitch, int c0, i
 }
 
 
+// Row-major bf16 [contraction][128] tiles that are read both transposed (ld_tr8) and by
+// rows (ld8) are stored at a pitch of PS = 144 with column c of every row that has bit 3
+// set at c ^ 72. In each group of 16 lanes a transposed read takes 4 rows at 8-bank steps
+// and its groups are 8 rows apart: bit 6 of the swap moves those by 32 banks. A row read
+// takes 16 consecutive rows, r and r + 8 on the same banks without the swap: bit 3 moves
+// them by 4 banks. Both swaps move whole 8-column pieces, so every access stays one piece.
+constexpr int PS = kD + 16;
+__device__ __forceinline__ int swz(int row) { return (row & 8) * 9; }
+__device__ __forceinline__ int sw_off(int row, int col) { return row * PS + (col ^ swz(row)); }
+
+// ld_tr8 from a tile stored with swz: lane (l16, lq) receives X[c0 + 8 lq + e][n0 + l16]
+__device__ __forceinline__ bf16x8 ld_tr8s(const uint16_t* X, int c0, int n0) {
+  const int lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
+  const int row = c0 + 8 * g + (j >> 2);
+  const uint16_t* p = X + sw_off(row, n0 + 4 * (j & 3));
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * PS));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Key order of a bf16 [..][128] tile whose rows meet, in one MFMA operand, four keys from
+// each 16-key half of a 32-key block (the order of a state tile held in fp32 accumulators,
+// rows = keys): key 32 ks + 16 h + 4 a + b at column 32 ks + 8 a + 4 h + b, so that the
+// eight keys {32 ks + 4 a + e, 32 ks + 16 + 4 a + e} (e < 4) are one 16-byte piece
+__device__ __forceinline__ int qcol(int key) {
+  return (key & ~31) | ((key & 12) << 1) | ((key & 16) >> 2) | (key & 3);
+}
+
 // lower-triangle 16 x 16 tile pairs (rb, cb), cb <= rb
 __device__ __forceinline__ void tri_pair(int p, int& rb, int& cb) {
   rb = p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3;

@@ -419,7 +419,7 @@ namespace gdc {
 
 struct alignas(16) Prep2Smem {
   uint16_t Q[C * PQ];    // q rows [t][k]
-  uint16_t KV[C * PQ];   // k rows [t][k]; once W is formed, v rows [t][v]
+  uint16_t KV[C * PS];   // k rows [t][k]; once W is formed, v rows [t][v] (stored with swz)
   uint16_t A[C * PC];    // masked decayed scores [r][j]
   union {
     struct {
@@ -456,7 +456,7 @@ __device__ __forceinline__ void prep2_chunk(Prep2Smem& sm, PrepIn<false>& in, in
   for (int h = 0; h < 2; ++h) {
     const int p = tid + NT * h, o = (p >> 4) * PQ + (p & 15) * 8;
     *reinterpret_cast<u32x4*>(sm.Q + o) = in.q[h];
-    *reinterpret_cast<u32x4*>(sm.KV + o) = in.k[h];
+    *reinterpret_cast<u32x4*>(sm.KV + sw_off(p >> 4, (p & 15) * 8)) = in.k[h];
     vcur[h] = in.v[h];
   }
   {
@@ -478,7 +478,7 @@ __device__ __forceinline__ void prep2_chunk(Prep2Smem& sm, PrepIn<false>& in, in
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int f = wave + 8 * h, j0 = (f & 1) * 32 + lq * 8;
-    const u32x4 raw = __builtin_bit_cast(u32x4, ld_tr8(sm.KV, PQ, (f & 1) * 32, (f >> 1) * 16));
+    const u32x4 raw = __builtin_bit_cast(u32x4, ld_tr8s(sm.KV, (f & 1) * 32, (f >> 1) * 16));
     u32x4 w;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -493,12 +493,13 @@ __device__ __forceinline__ void prep2_chunk(Prep2Smem& sm, PrepIn<false>& in, in
     for (int u = wv; u < 20; u += 8) {
       int rb, cb;
       tri_pair(u >> 1, rb, cb);
-      const uint16_t* X = (u & 1) ? sm.Q : sm.KV;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        acc = mfma(ld8(X + (rb * 16 + l16) * PQ + kk * 32 + lq * 8), ld8(sm.KV + (cb * 16 + l16) * PQ + kk * 32 + lq * 8),
-                   acc);
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8 xa = (u & 1) ? ld8(sm.Q + (rb * 16 + l16) * PQ + kk * 32 + lq * 8)
+                                  : ld8(sm.KV + sw_off(rb * 16 + l16, kk * 32 + lq * 8));
+        acc = mfma(xa, ld8(sm.KV + sw_off(cb * 16 + l16, kk * 32 + lq * 8)), acc);
+      }
       const int j = cb * 16 + l16, r0 = rb * 16 + lq * 4;
       const f32x4 lgr = *reinterpret_cast<const f32x4*>(sm.lg + r0);
       const float lgj = sm.lg[j];
@@ -599,7 +600,7 @@ __device__ __forceinline__ void prep2_chunk(Prep2Smem& sm, PrepIn<false>& in, in
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int js = 0; js <= rb / 2; ++js)
-      acc = mfma(ld8(sm.u.t.Tw + (rb * 16 + l16) * PC + js * 32 + lq * 8), ld_tr8(sm.KV, PQ, js * 32, wave * 16), acc);
+      acc = mfma(ld8(sm.u.t.Tw + (rb * 16 + l16) * PC + js * 32 + lq * 8), ld_tr8s(sm.KV, js * 32, wave * 16), acc);
     wa[rb] = bf4(acc);
   }
 #pragma unroll
@@ -608,8 +609,8 @@ __device__ __forceinline__ void prep2_chunk(Prep2Smem& sm, PrepIn<false>& in, in
     f32x4 t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
     for (int js = 0; js <= rb / 2; ++js) {
       const bf16x8 b = ld8(sm.u.t.Tw + (rb * 16 + l16) * PC + js * 32 + lq * 8);
-      t0 = mfma(ld_tr8(sm.KV, PQ, js * 32, ks * 32), b, t0);
-      t1 = mfma(ld_tr8(sm.KV, PQ, js * 32, ks * 32 + 16), b, t1);
+      t0 = mfma(ld_tr8s(sm.KV, js * 32, ks * 32), b, t0);
+      t1 = mfma(ld_tr8s(sm.KV, js * 32, ks * 32 + 16), b, t1);
     }
     *reinterpret_cast<u32x4*>(wsc + kWsW + ((size_t)(rb * 4 + ks) * 64 + lane) * 16) =
         u32x4{pack_bf16(t0[0], t0[1]), pack_bf16(t0[2], t0[3]), pack_bf16(t1[0], t1[1]), pack_bf16(t1[2], t1[3])};
@@ -622,7 +623,7 @@ __device__ __forceinline__ void prep2_chunk(Prep2Smem& sm, PrepIn<false>& in, in
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int p = tid + NT * h;
-    *reinterpret_cast<u32x4*>(sm.KV + (p >> 4) * PQ + (p & 15) * 8) = vcur[h];
+    *reinterpret_cast<u32x4*>(sm.KV + sw_off(p >> 4, (p & 15) * 8)) = vcur[h];
   }
   {
     const int nx = cid + (int)gridDim.x < nchunks ? cid + (int)gridDim.x : cid;
@@ -635,7 +636,7 @@ __device__ __forceinline__ void prep2_chunk(Prep2Smem& sm, PrepIn<false>& in, in
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int js = 0; js <= rb / 2; ++js)
-      acc = mfma(ld8(sm.u.t.Tu + (rb * 16 + l16) * PC + js * 32 + lq * 8), ld_tr8(sm.KV, PQ, js * 32, wave * 16), acc);
+      acc = mfma(ld8(sm.u.t.Tu + (rb * 16 + l16) * PC + js * 32 + lq * 8), ld_tr8s(sm.KV, js * 32, wave * 16), acc);
     const u32x2 pk = {pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
     *reinterpret_cast<u32x2*>(wsc + kWsU + ((size_t)(rb * 8 + wave) * 64 + lane) * 8) = pk;
     ub[rb] = __builtin_bit_cast(s16x4, pk);
@@ -718,7 +719,7 @@ constexpr int kWarm = 2;    // chunks between the L2 warm-up of a chunk and its 
 
 template <int VT>
 struct alignas(16) SeqSmem {
-  uint16_t Sb[2][VT * PQ];   // bf16 state tile [v][k], double buffered
+  uint16_t Sb[2][VT * PQ];   // bf16 state tile [v][qcol(k)], double buffered
   uint16_t Ut[VT * PC];      // U^T tile [v][j]
   uint16_t Ot[2][VT * PC];   // outputs^T [v][r], by chunk parity
 };
@@ -826,12 +827,8 @@ __device__ __forceinline__ void gdn_seq_chunk(SeqSmem<VT>& sm, const Prefetch<VT
   for (int vb = 0; vb < NVB; ++vb) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const uint16_t* sp = sm.Sb[cur] + (vb * 16 + l16) * PQ + ks * 32 + lq * 4;
-      const u32x2 lo = *reinterpret_cast<const u32x2*>(sp);
-      const u32x2 hi = *reinterpret_cast<const u32x2*>(sp + 16);
-      acc = mfma(as_bf8(pf.m[ks]), as_bf8(u32x4{lo.x, lo.y, hi.x, hi.y}), acc);
-    }
+    for (int ks = 0; ks < 4; ++ks)   // keys 32 ks + 4 lq + {0..3}, 32 ks + 16 + 4 lq + {0..3}: one piece
+      acc = mfma(as_bf8(pf.m[ks]), ld8(sm.Sb[cur] + (vb * 16 + l16) * PQ + ks * 32 + lq * 8), acc);
     const u32x2 xv = pf.x[vb];
     *reinterpret_cast<u32x2*>(dst + vb * 16 * PC) =
         u32x2{pack_bf16(lo_bf(xv.x) + sgn * acc[0], hi_bf(xv.x) + sgn * acc[1]),
@@ -849,7 +846,7 @@ __device__ __forceinline__ void gdn_seq_chunk(SeqSmem<VT>& sm, const Prefetch<VT
       acc = mfma(ld8(sm.Ut + (vb * 16 + l16) * PC + js * 32 + lq * 8), as_bf8(pf.kh[js]), acc);
     Sacc[vb] = acc;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sm.Sb[cur ^ 1][(vb * 16 + lq * 4 + i) * PQ + kcol] = f32_to_bf16(acc[i]);
+    for (int i = 0; i < 4; ++i) sm.Sb[cur ^ 1][(vb * 16 + lq * 4 + i) * PQ + qcol(kcol)] = f32_to_bf16(acc[i]);
   }
   cur ^= 1;
   lds_barrier();
@@ -892,7 +889,7 @@ __global__ __launch_bounds__(512) void gdn_chunk_seq_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       Sacc[vb][i] = S0 ? S0[((size_t)n * kD + v0 + vb * 16 + lq * 4 + i) * kD + kcol] : 0.f;
-      sm.Sb[0][(vb * 16 + lq * 4 + i) * PQ + kcol] = f32_to_bf16(Sacc[vb][i]);
+      sm.Sb[0][(vb * 16 + lq * 4 + i) * PQ + qcol(kcol)] = f32_to_bf16(Sacc[vb][i]);
     }
 
   if (nc > 0) {

@@ -38,23 +38,12 @@
 namespace gdnrt {
 
 namespace gla {
-using namespace gdc;   // C, PQ, PC, ld8, ld_tr8, mfma, tri_pair, lo_bf, hi_bf
+using namespace gdc;   // C, PQ, PC, PS, swz, ld8, ld_tr8s, mfma, tri_pair, lo_bf, hi_bf
 
 constexpr int NB = 512;       // threads per block: 8 waves
-// Kr and v, read transposed (ds_read_b64_tr_b16) and, Kr, by rows for the scores: rows
-// of PT bf16, and in the rows with bit 3 set column c stored at c ^ 72. A transposed read
-// takes 4 rows at 8-bank steps in each group of 16 lanes, groups 8 rows apart: bit 6 of
-// the swap moves those by 32 banks. A row read takes 16 consecutive rows, row r and r + 8
-// on the same banks without the swap: bit 3 moves them by 4 banks. Both swaps move whole
-// 8-column pieces, so every access stays one piece.
-constexpr int PT = kD + 16;
-__device__ __forceinline__ int swz(int row) { return (row & 8) * 9; }
-// Qr's keys in LDS: key 32 ks + 16 h + 4 a + b at column 32 ks + 8 a + 4 h + b, so that the
-// eight keys the inter-chunk product pairs in one lane (four from each 16-key half of a
-// 32-key block) are one 16-byte piece
-__device__ __forceinline__ int qcol(int key) {
-  return (key & ~31) | ((key & 12) << 1) | ((key & 16) >> 2) | (key & 3);
-}
+// Kr and v are read transposed (ds_read_b64_tr_b16) and Kr also by rows: both stored
+// with swz (pitch PT = PS).
+constexpr int PT = PS;
 constexpr int kMaxSeg = 16;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr size_t kStateBytes = (size_t)kD * kD * 4;
@@ -88,7 +77,7 @@ __host__ inline Plan plan(int N, int nc) {
 }
 
 struct alignas(16) Smem {
-  uint16_t Qr[C * PQ];               // q o e^{b - b_m} [t][qcol(k)]
+  uint16_t Qr[C * PQ];               // q o e^{b - b_m} [t][qcol(k)] (key-permuted, qcol)
   uint16_t Kr[C * PT];               // pass 2: k o e^{b_m - b}; pass 1: k o e^{b_C - b}
   uint16_t V[C * PT];                // v [t][v]
   uint16_t A[C * PC];                // masked scores [r][j]
@@ -142,16 +131,6 @@ __device__ __forceinline__ void stage(Smem& sm, In& in, int t) {
 #pragma unroll
   for (int i = 1; i < 8; ++i) in.g[i] = in.g[i] * kLog2e + in.g[i - 1];
   *reinterpret_cast<f32x2*>(sm.tot + eg * kD + 2 * cp) = in.g[7];
-}
-
-// ld_tr8 (the MFMA operand X[c0 + 8 lq + e][n0 + l16]) from a matrix stored with swz
-__device__ __forceinline__ bf16x8 ld_tr8s(const uint16_t* X, int c0, int n0) {
-  const int lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
-  const int row = c0 + 8 * g + (j >> 2);
-  const uint16_t* p = X + row * PT + ((n0 + 4 * (j & 3)) ^ swz(row));
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * PT));
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 __device__ __forceinline__ f32x2 bf2f(unsigned w) { return f32x2{lo_bf(w), hi_bf(w)}; }
