@@ -118,6 +118,10 @@ __global__ __launch_bounds__(256) void leapq_decode_kernel(
     const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, IO* __restrict__ o) {
   constexpr int NV = kMaxRank + kMaxWindow;   // dot-product vectors: compensators, records, k
+  // this head's codes, straight from HBM (rows of eight 16-byte pieces; piece c of row r
+  // at slot c ^ ((r >> 1) & 7), so that the 16 rows an MFMA operand read takes fall on
+  // distinct banks)
+  __shared__ __attribute__((aligned(16))) int8_t s_codes[kD * kD];
   __shared__ __attribute__((aligned(16))) uint2 s_dig[4][8][kD / 8];   // per wave: digit rows
                                                                       // (x_k 0-2, x_q 3-5, 6-7 zero)
   __shared__ float s_dk[NV], s_dq[NV];
@@ -135,16 +139,18 @@ __global__ __launch_bounds__(256) void leapq_decode_kernel(
   const int row[2] = {32 * w + n, 32 * w + 16 + n};
 
   // ---- independent loads
-  // code rows of this wave's tiles as MFMA B operands: row 32 w + 16 T + n, bytes 64 s + 16 g
-  // (non-temporal: the codes of all heads do not fit the caches between two steps, and
-  // keeping them out leaves room for the buffered records, which every step re-reads)
-  i32x4 zb[2][2];
+  // the codes of this wave's rows go straight to LDS (LDS DMA: no registers, so more heads
+  // fit on a CU): instruction i of wave w fills rows 32 w + 8 i .. + 7, lane L slot L & 7 of
+  // row 32 w + 8 i + L / 8. Non-temporal: the codes of all heads do not fit the caches
+  // between two steps, and keeping them out leaves room for the buffered records, which
+  // every step re-reads.
 #pragma unroll
-  for (int T = 0; T < 2; ++T)
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-      zb[T][s] = __builtin_nontemporal_load(
-          reinterpret_cast<const i32x4*>(codes + (hk + row[T]) * kD + 64 * s + 16 * g));
+  for (int i = 0; i < 4; ++i) {
+    const int r = 32 * w + 8 * i + (lane >> 3), c = (lane & 7) ^ ((r >> 1) & 7);
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(codes + (hk + r) * kD + 16 * c),
+                                     (__attribute__((address_space(3))) void*)(s_codes + (32 * w + 8 * i) * kD), 16,
+                                     0, 2 /* nt */);
+  }
   // buffered corrections and compensator values of this lane's rows, slots = g (mod 4)
   float bur[2][kMaxWindow / 4], cur[2][kMaxRank / 4], vrow[2], vsr[2];
 #pragma unroll
@@ -223,22 +229,10 @@ __global__ __launch_bounds__(256) void leapq_decode_kernel(
     if (tid < kD)   // suffix products of channel tid's buffered decays
       suffix_products(buf_a + (size_t)head * window * kD + tid, kD, m,
                       [&](int j, float x) { s_gv[j][tid] = x; });
-    if (w == 0 && g == 0) {   // this token's decays as record m
-      f32x4* dst = reinterpret_cast<f32x4*>(buf_a + ((size_t)head * window + m) * kD + 8 * n);
-      dst[0] = f32x4{ax[0], ax[1], ax[2], ax[3]};
-      dst[1] = f32x4{ax[4], ax[5], ax[6], ax[7]};
-    }
     lds_barrier();
   } else {
-    if (tid == 0) {   // suffix products of the buffered decays
+    if (tid == 0)   // suffix products of the buffered decays
       suffix_products(ba, 1, m, [&](int j, float x) { s_g[j] = x; });
-      buf_a[(size_t)head * window + m] = a;
-    }
-  }
-  if (w == 0 && g == 0) {   // this token's key as record m
-    f32x4* dst = reinterpret_cast<f32x4*>(bk + (size_t)m * kD + 8 * n);
-    dst[0] = f32x4{kx[0], kx[1], kx[2], kx[3]};
-    dst[1] = f32x4{kx[4], kx[5], kx[6], kx[7]};
   }
   // KDA: the vectors the state is applied to are yk = a o k, yq = a o q; the
   // compensators and the stored residual see them decayed by G0, record j by G_j
@@ -315,7 +309,19 @@ __global__ __launch_bounds__(256) void leapq_decode_kernel(
   }
   wave_lds_sync();
 
-  // ---- Z x on the int8 matrix cores: A = digit rows (M), B = code rows (N)
+  // ---- Z x on the int8 matrix cores: A = digit rows (M), B = code rows (N): row
+  // 32 w + 16 T + n, bytes 64 s + 16 g, from the wave's own LDS copy (complete once the
+  // wave's vector memory operations are: the compiler does not order LDS reads after LDS
+  // DMA, and before this point the wave has issued no stores)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  i32x4 zb[2][2];
+#pragma unroll
+  for (int T = 0; T < 2; ++T)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int r = row[T], c = 4 * s + g;
+      zb[T][s] = *reinterpret_cast<const i32x4*>(s_codes + r * kD + 16 * (c ^ ((r >> 1) & 7)));
+    }
   i32x4 acc[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
@@ -368,6 +374,19 @@ __global__ __launch_bounds__(256) void leapq_decode_kernel(
       const float oi = KDA ? Sq + u * kq : a * Sq + u * kq;
       bu[(size_t)m * kD + row[T]] = u;
       io_traits<IO>::st(o, hk + row[T], oi);
+    }
+  }
+  // ---- this token's record m: its key, and its decay (GDN: one per head; KDA: per channel)
+  if (w == 0 && g == 0) {
+    f32x4* dst = reinterpret_cast<f32x4*>(bk + (size_t)m * kD + 8 * n);
+    dst[0] = f32x4{kx[0], kx[1], kx[2], kx[3]};
+    dst[1] = f32x4{kx[4], kx[5], kx[6], kx[7]};
+    if constexpr (KDA) {
+      f32x4* da = reinterpret_cast<f32x4*>(buf_a + ((size_t)head * window + m) * kD + 8 * n);
+      da[0] = f32x4{ax[0], ax[1], ax[2], ax[3]};
+      da[1] = f32x4{ax[4], ax[5], ax[6], ax[7]};
+    } else if (n == 0) {
+      buf_a[(size_t)head * window + m] = a;
     }
   }
 }
