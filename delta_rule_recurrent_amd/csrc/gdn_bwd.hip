@@ -32,7 +32,7 @@
 // state before every chunk, bf16), the backward state scan (the gradient after every
 // chunk, bf16, dS_0 and the chunks' sum(dS_a o S_a)), and two per-chunk gradient
 // kernels (bf16 MFMA, fp32 accumulation).
-#include "common.hpp"
+#include "chunk_device.hpp"
 #include "gdn_chunk_layout.hpp"
 
 namespace gdnrt {
@@ -43,52 +43,32 @@ void gdn_chunk_prep_with_inverse(const uint16_t* q, const uint16_t* k, const uin
 
 namespace gdb {
 
-using namespace gdc;
-constexpr int C = kChunk;    // 64
-constexpr int PT = kD + 16;  // bf16 pitch of 128-wide rows
-constexpr int PA = C + 16;   // bf16 pitch of 64-wide rows
-constexpr int PX = 16 + 16;  // bf16 pitch of 16-wide rows
-constexpr int PF = kD + 4;   // fp32 pitch of 128-wide rows
-
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-__device__ __forceinline__ bf16x8 as_bf(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
-__device__ __forceinline__ bf16x8 ld8(const uint16_t* p) { return as_bf(*reinterpret_cast<const u32x4*>(p)); }
-// 8 keys of a row in the prep fragments' order: 4 at c, 4 at c + 16
-__device__ __forceinline__ bf16x8 ld8_split(const uint16_t* p) {
-  const u32x2 a = *reinterpret_cast<const u32x2*>(p), b = *reinterpret_cast<const u32x2*>(p + 16);
-  return as_bf(u32x4{a.x, a.y, b.x, b.y});
-}
-__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-// MFMA operand from a row-major [contraction][column] bf16 matrix in LDS through the
-// transposing LDS read: lane (l16, lq) receives X[c0 + 8 lq + e][n0 + l16], e = 0..7.
-__device__ __forceinline__ bf16x8 ld_tr8(const uint16_t* X, int pitch, int c0, int n0) {
+using namespace gdc;   // C, PS, sw_off, ld8, ld_tr8, ld_tr8s, mfma, lo_bf, hi_bf, wave_scan, tri_pair
+constexpr int PT = PS;       // bf16 pitch of 128-wide rows, stored with swz
+constexpr int PA = C + 8;    // bf16 pitch of 64-wide rows (a transposed read's groups of
+                             // lanes 8 rows apart fall 32 banks apart; rows read by 16
+                             // lanes on distinct banks)
+constexpr int PX = 16 + 16;  // bf16 pitch of 16-wide rows; rows with bit 3 set are stored in
+                             // the upper half (columns 16..31), so that a transposed read's
+                             // groups of lanes, 8 rows apart, fall on distinct banks
+__device__ __forceinline__ int px_off(int row, int col) { return row * PX + col + ((row & 8) << 1); }
+// ld_tr8 from a 16-wide tile stored with px_off
+__device__ __forceinline__ bf16x8 ld_tr8x(const uint16_t* X, int c0) {
   const int lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
-  const uint16_t* p = X + (c0 + 8 * g + (j >> 2)) * pitch + n0 + 4 * (j & 3);
+  const uint16_t* p = X + px_off(c0 + 8 * g + (j >> 2), 4 * (j & 3));
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * pitch));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * PX));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
-__device__ __forceinline__ float lo_bf(unsigned w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float hi_bf(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
-__device__ __forceinline__ float wave_scan(float x) {   // inclusive prefix sum over 64 lanes
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
-  return x;
-}
-// lower-triangle 16 x 16 tile pairs (rb, cb), cb <= rb
-__device__ __forceinline__ void tri_pair(int p, int& rb, int& cb) {
-  rb = p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3;
-  cb = p - (rb * (rb + 1)) / 2;
+constexpr int PFK = kD + 4;  // fp32 pitch of 128-wide rows
+
+__device__ __forceinline__ bf16x8 as_bf(u32x4 x) { return as_bf8(x); }
+// 8 keys of row `row` of a tile stored with swz, in the prep fragments' order: 4 at
+// column c, 4 at c + 16
+__device__ __forceinline__ bf16x8 ld8_split_s(const uint16_t* X, int row, int c) {
+  const u32x2 a = *reinterpret_cast<const u32x2*>(X + sw_off(row, c));
+  const u32x2 b = *reinterpret_cast<const u32x2*>(X + sw_off(row, c + 16));
+  return as_bf(u32x4{a.x, a.y, b.x, b.y});
 }
 // block -> (sequence, value tile of 16); the 8 tiles of one sequence share an XCD
 // (blocks are dealt to the 8 XCDs round robin), so the chunk operands they all read
@@ -167,14 +147,14 @@ __global__ __launch_bounds__(256) void gdn_bwd_fscan_kernel(const uint8_t* __res
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sS[(4 * lq + i) * PT + 32 * w + 16 * j + l16] = f32_to_bf16(acc[j][i]);
+      for (int i = 0; i < 4; ++i) sS[sw_off(4 * lq + i, 32 * w + 16 * j + l16)] = f32_to_bf16(acc[j][i]);
     lds_barrier();
     // the tile's bf16 copy to the workspace: row tid / 16, 8 columns per thread
     *reinterpret_cast<u32x4*>(Sb + (chunk0 + s) * kD * kD + (size_t)(v0 + (tid >> 4)) * kD + 8 * (tid & 15)) =
-        *reinterpret_cast<const u32x4*>(sS + (tid >> 4) * PT + 8 * (tid & 15));
+        *reinterpret_cast<const u32x4*>(sS + sw_off(tid >> 4, 8 * (tid & 15)));
     f32x4 p = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) p = mfma(as_bf(cur.w[ks]), ld8_split(sS + l16 * PT + 32 * ks + 4 * lq), p);
+    for (int ks = 0; ks < 4; ++ks) p = mfma(as_bf(cur.w[ks]), ld8_split_s(sS, l16, 32 * ks + 4 * lq), p);
     const float u0 = lo_bf(cur.u.x) - p[0], u1 = hi_bf(cur.u.x) - p[1];
     const float u2 = lo_bf(cur.u.y) - p[2], u3 = hi_bf(cur.u.y) - p[3];
     *reinterpret_cast<u32x2*>(sU + l16 * PA + 16 * w + 4 * lq) = u32x2{pack_bf16(u0, u1), pack_bf16(u2, u3)};
@@ -216,7 +196,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_rscan_kernel(const uint8_t* __res
   __shared__ __attribute__((aligned(16))) uint16_t sW[C * PT];
   __shared__ __attribute__((aligned(16))) uint16_t sO[C * PX];
   __shared__ __attribute__((aligned(16))) uint16_t sdU[16 * PA];
-  __shared__ __attribute__((aligned(16))) float sA[16 * PF];   // the state after the chunk, this tile
+  __shared__ __attribute__((aligned(16))) float sA[16 * PFK];   // the state after the chunk, this tile
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, lq = lane >> 4;
   int n, vt;
   seq_tile(n, vt);
@@ -268,40 +248,41 @@ __global__ __launch_bounds__(256) void gdn_bwd_rscan_kernel(const uint8_t* __res
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sD[(4 * lq + i) * PT + 32 * w + 16 * j + l16] = f32_to_bf16(acc[j][i]);
-    *reinterpret_cast<f32x4*>(sA + tr * PF + tc) = cur.sa[0];
-    *reinterpret_cast<f32x4*>(sA + tr * PF + tc + 4) = cur.sa[1];
+      for (int i = 0; i < 4; ++i) sD[sw_off(4 * lq + i, 32 * w + 16 * j + l16)] = f32_to_bf16(acc[j][i]);
+    *reinterpret_cast<f32x4*>(sA + tr * PFK + tc) = cur.sa[0];
+    *reinterpret_cast<f32x4*>(sA + tr * PFK + tc + 4) = cur.sa[1];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int f = w + 4 * p;
       // K^ fragment (kb, js) = (f / 2, f % 2): key kb*16 + l16, tokens js*32 + lq*8 ..
       *reinterpret_cast<u32x4*>(sKt + ((f >> 1) * 16 + l16) * PA + (f & 1) * 32 + lq * 8) = cur.kh[p];
       // W, Q' fragments (rb, ks) = (f / 4, f % 4): token rb*16 + l16, keys split by 16
-      const int ro = ((f >> 2) * 16 + l16) * PT + (f & 3) * 32 + lq * 4;
-      *reinterpret_cast<u32x2*>(sW + ro) = u32x2{cur.w[p].x, cur.w[p].y};
-      *reinterpret_cast<u32x2*>(sW + ro + 16) = u32x2{cur.w[p].z, cur.w[p].w};
-      *reinterpret_cast<u32x2*>(sQ + ro) = u32x2{cur.qp[p].x, cur.qp[p].y};
-      *reinterpret_cast<u32x2*>(sQ + ro + 16) = u32x2{cur.qp[p].z, cur.qp[p].w};
+      const int rr = (f >> 2) * 16 + l16, c0 = (f & 3) * 32 + lq * 4;
+      const int o0 = sw_off(rr, c0), o1 = sw_off(rr, c0 + 16);
+      *reinterpret_cast<u32x2*>(sW + o0) = u32x2{cur.w[p].x, cur.w[p].y};
+      *reinterpret_cast<u32x2*>(sW + o1) = u32x2{cur.w[p].z, cur.w[p].w};
+      *reinterpret_cast<u32x2*>(sQ + o0) = u32x2{cur.qp[p].x, cur.qp[p].y};
+      *reinterpret_cast<u32x2*>(sQ + o1) = u32x2{cur.qp[p].z, cur.qp[p].w};
     }
-    *reinterpret_cast<u32x2*>(sO + (tid >> 2) * PX + 4 * (tid & 3)) = cur.o;
+    *reinterpret_cast<u32x2*>(sO + px_off(tid >> 2, 4 * (tid & 3))) = cur.o;
     lds_barrier();
     // the tile's bf16 copy to the workspace, one 16-byte store per thread; this tile's
     // part of sum(dS o S) from the fp32 accumulators and the staged state after the chunk
     *reinterpret_cast<u32x4*>(dSa + (chunk0 + ci) * kD * kD + (size_t)(v0 + tr) * kD + tc) =
-        *reinterpret_cast<const u32x4*>(sD + tr * PT + tc);
+        *reinterpret_cast<const u32x4*>(sD + sw_off(tr, tc));
     {
       float part = 0.f;
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) part += acc[j][i] * sA[(4 * lq + i) * PF + 32 * w + 16 * j + l16];
+        for (int i = 0; i < 4; ++i) part += acc[j][i] * sA[(4 * lq + i) * PFK + 32 * w + 16 * j + l16];
       part = sum64(part);
       if (lane == 0) bnd[(chunk0 + ci) * 32 + 4 * vt + w] = part;
     }
     // -(K^ dS^T)^T for tokens 16 w .. 16 w + 15: [v][t]
     f32x4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) x = mfma(ld8(sD + l16 * PT + 32 * ks + 8 * lq), ld_tr8(sKt, PA, 32 * ks, 16 * w), x);
+    for (int ks = 0; ks < 4; ++ks) x = mfma(ld8(sD + sw_off(l16, 32 * ks + 8 * lq)), ld_tr8(sKt, PA, 32 * ks, 16 * w), x);
 #pragma unroll
     for (int i = 0; i < 4; ++i) sdU[(4 * lq + i) * PA + 16 * w + l16] = f32_to_bf16(-x[i]);
     lds_barrier();
@@ -309,12 +290,12 @@ __global__ __launch_bounds__(256) void gdn_bwd_rscan_kernel(const uint8_t* __res
     acc[1] *= cur.gc;
 #pragma unroll
     for (int js = 0; js < 2; ++js) {
-      const bf16x8 ao = ld_tr8(sO, PX, 32 * js, 0);
+      const bf16x8 ao = ld_tr8x(sO, 32 * js);
       const bf16x8 au = ld8(sdU + l16 * PA + 32 * js + 8 * lq);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        acc[j] = mfma(ao, ld_tr8(sQ, PT, 32 * js, 32 * w + 16 * j), acc[j]);
-        acc[j] = mfma(au, ld_tr8(sW, PT, 32 * js, 32 * w + 16 * j), acc[j]);
+        acc[j] = mfma(ao, ld_tr8s(sQ, 32 * js, 32 * w + 16 * j), acc[j]);
+        acc[j] = mfma(au, ld_tr8s(sW, 32 * js, 32 * w + 16 * j), acc[j]);
       }
     }
     lds_barrier();
@@ -353,15 +334,15 @@ __global__ __launch_bounds__(512) void gdn_bwd_grad1_kernel(
   for (int p = 0; p < 2; ++p) {
     const int e = (tid + 512 * p) * 8, r = e >> 7, cc = e & 127;
     const size_t gi = (tok0 + r) * kD + cc;
-    *reinterpret_cast<u32x4*>(sm.Q + r * PT + cc) = *reinterpret_cast<const u32x4*>(q + gi);
-    *reinterpret_cast<u32x4*>(sm.K + r * PT + cc) = *reinterpret_cast<const u32x4*>(k + gi);
-    *reinterpret_cast<u32x4*>(sm.O + r * PT + cc) = *reinterpret_cast<const u32x4*>(dO + gi);
+    *reinterpret_cast<u32x4*>(sm.Q + sw_off(r, cc)) = *reinterpret_cast<const u32x4*>(q + gi);
+    *reinterpret_cast<u32x4*>(sm.K + sw_off(r, cc)) = *reinterpret_cast<const u32x4*>(k + gi);
+    *reinterpret_cast<u32x4*>(sm.O + sw_off(r, cc)) = *reinterpret_cast<const u32x4*>(dO + gi);
   }
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int e = (tid + 512 * p) * 8, r = e >> 7, cc = e & 127;
-    *reinterpret_cast<u32x4*>(sm.S + r * PT + cc) = *reinterpret_cast<const u32x4*>(ws.Sb + (size_t)cid * kD * kD + e);
-    *reinterpret_cast<u32x4*>(sm.D + r * PT + cc) = *reinterpret_cast<const u32x4*>(ws.dSa + (size_t)cid * kD * kD + e);
+    *reinterpret_cast<u32x4*>(sm.S + sw_off(r, cc)) = *reinterpret_cast<const u32x4*>(ws.Sb + (size_t)cid * kD * kD + e);
+    *reinterpret_cast<u32x4*>(sm.D + sw_off(r, cc)) = *reinterpret_cast<const u32x4*>(ws.dSa + (size_t)cid * kD * kD + e);
   }
   for (int e = tid; e < C * PA / 2; e += 512) reinterpret_cast<uint32_t*>(sm.A)[e] = 0u;
   if (w == 0) {
@@ -381,7 +362,7 @@ __global__ __launch_bounds__(512) void gdn_bwd_grad1_kernel(
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      acc = mfma(ld8(sm.Q + (16 * ab + l16) * PT + 32 * ks + 8 * lq), ld8(sm.K + (16 * cb + l16) * PT + 32 * ks + 8 * lq), acc);
+      acc = mfma(ld8(sm.Q + sw_off(16 * ab + l16, 32 * ks + 8 * lq)), ld8(sm.K + sw_off(16 * cb + l16, 32 * ks + 8 * lq)), acc);
     const int j = 16 * cb + l16;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -400,10 +381,10 @@ __global__ __launch_bounds__(512) void gdn_bwd_grad1_kernel(
       const u32x2 ut = *reinterpret_cast<const u32x2*>(pc + kWsU + ((size_t)(rb * 8 + vb) * 64 + lane) * 8);
       f32x4 p = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) p = mfma(as_bf(wf[ks]), ld8_split(sm.S + (16 * vb + l16) * PT + 32 * ks + 4 * lq), p);
+      for (int ks = 0; ks < 4; ++ks) p = mfma(as_bf(wf[ks]), ld8_split_s(sm.S, 16 * vb + l16, 32 * ks + 4 * lq), p);
       const float uu[4] = {lo_bf(ut.x) - p[0], hi_bf(ut.x) - p[1], lo_bf(ut.y) - p[2], hi_bf(ut.y) - p[3]};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sm.U[(16 * rb + 4 * lq + i) * PT + 16 * vb + l16] = f32_to_bf16(uu[i]);
+      for (int i = 0; i < 4; ++i) sm.U[sw_off(16 * rb + 4 * lq + i, 16 * vb + l16)] = f32_to_bf16(uu[i]);
     }
   }
   lds_barrier();
@@ -417,10 +398,10 @@ __global__ __launch_bounds__(512) void gdn_bwd_grad1_kernel(
 #pragma unroll
     for (int js = 0; js < 2; ++js)
       if (32 * js + 31 >= 16 * rb)   // A[j][r] is zero for j < r
-        a1 = mfma(ld_tr8(sm.A, PA, 32 * js, 16 * rb), ld_tr8(sm.O, PT, 32 * js, 16 * vb), a1);
+        a1 = mfma(ld_tr8(sm.A, PA, 32 * js, 16 * rb), ld_tr8s(sm.O, 32 * js, 16 * vb), a1);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      a2 = mfma(ld8(sm.K + (16 * rb + l16) * PT + 32 * ks + 8 * lq), ld8(sm.D + (16 * vb + l16) * PT + 32 * ks + 8 * lq), a2);
+      a2 = mfma(ld8(sm.K + sw_off(16 * rb + l16, 32 * ks + 8 * lq)), ld8(sm.D + sw_off(16 * vb + l16, 32 * ks + 8 * lq)), a2);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * rb + 4 * lq + i;
@@ -436,7 +417,7 @@ __global__ __launch_bounds__(512) void gdn_bwd_grad1_kernel(
       tri_pair(w + 8 * h, ab, cb);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        da[h] = mfma(ld8(sm.O + (16 * ab + l16) * PT + 32 * ks + 8 * lq), ld8(sm.U + (16 * cb + l16) * PT + 32 * ks + 8 * lq), da[h]);
+        da[h] = mfma(ld8(sm.O + sw_off(16 * ab + l16, 32 * ks + 8 * lq)), ld8(sm.U + sw_off(16 * cb + l16, 32 * ks + 8 * lq)), da[h]);
     }
   }
   lds_barrier();
@@ -464,14 +445,14 @@ __global__ __launch_bounds__(512) void gdn_bwd_grad1_kernel(
 #pragma unroll
     for (int js = 0; js < 2; ++js) {
       if (js <= rb / 2)   // dA'[r][j] is zero for j > r
-        a1 = mfma(ld8(sm.A + (16 * rb + l16) * PA + 32 * js + 8 * lq), ld_tr8(sm.K, PT, 32 * js, 16 * kb), a1);
+        a1 = mfma(ld8(sm.A + (16 * rb + l16) * PA + 32 * js + 8 * lq), ld_tr8s(sm.K, 32 * js, 16 * kb), a1);
       if (32 * js + 31 >= 16 * rb)   // dA'[i][r] is zero for i < r
-        a3 = mfma(ld_tr8(sm.A, PA, 32 * js, 16 * rb), ld_tr8(sm.Q, PT, 32 * js, 16 * kb), a3);
+        a3 = mfma(ld_tr8(sm.A, PA, 32 * js, 16 * rb), ld_tr8s(sm.Q, 32 * js, 16 * kb), a3);
     }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      a2 = mfma(ld8(sm.O + (16 * rb + l16) * PT + 32 * ks + 8 * lq), ld_tr8(sm.S, PT, 32 * ks, 16 * kb), a2);
-      a4 = mfma(ld8(sm.U + (16 * rb + l16) * PT + 32 * ks + 8 * lq), ld_tr8(sm.D, PT, 32 * ks, 16 * kb), a4);
+      a2 = mfma(ld8(sm.O + sw_off(16 * rb + l16, 32 * ks + 8 * lq)), ld_tr8s(sm.S, 32 * ks, 16 * kb), a2);
+      a4 = mfma(ld8(sm.U + sw_off(16 * rb + l16, 32 * ks + 8 * lq)), ld_tr8s(sm.D, 32 * ks, 16 * kb), a4);
     }
     const int col = 16 * kb + l16;
 #pragma unroll
@@ -480,7 +461,7 @@ __global__ __launch_bounds__(512) void gdn_bwd_grad1_kernel(
       const float gq = a1[i] + sm.g[r] * a2[i];
       dq[(tok0 + r) * kD + col] = f32_to_bf16(gq);
       dK1[r * kD + col] = a3[i] + sm.kd[r] * a4[i];
-      qacc[i] += sum16(bf16_to_f32(sm.Q[r * PT + col]) * gq);
+      qacc[i] += sum16(bf16_to_f32(sm.Q[sw_off(r, col)]) * gq);
     }
   }
   // fixed summation order (no atomics): each half of the waves writes its own partial
@@ -524,20 +505,20 @@ __global__ __launch_bounds__(512) void gdn_bwd_grad2_kernel(
   for (int p = 0; p < 2; ++p) {
     const int e = (tid + 512 * p) * 8, r = e >> 7, cc = e & 127;
     const size_t gi = (tok0 + r) * kD + cc;
-    *reinterpret_cast<u32x4*>(sm.K + r * PT + cc) = *reinterpret_cast<const u32x4*>(k + gi);
-    *reinterpret_cast<u32x4*>(sm.V + r * PT + cc) = *reinterpret_cast<const u32x4*>(v + gi);
-    *reinterpret_cast<u32x4*>(sm.dU + r * PT + cc) = *reinterpret_cast<const u32x4*>(ws.dU + (size_t)cid * C * kD + e);
+    *reinterpret_cast<u32x4*>(sm.K + sw_off(r, cc)) = *reinterpret_cast<const u32x4*>(k + gi);
+    *reinterpret_cast<u32x4*>(sm.V + sw_off(r, cc)) = *reinterpret_cast<const u32x4*>(v + gi);
+    *reinterpret_cast<u32x4*>(sm.dU + sw_off(r, cc)) = *reinterpret_cast<const u32x4*>(ws.dU + (size_t)cid * C * kD + e);
   }
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int e = (tid + 512 * p) * 8, r = e >> 7, cc = e & 127;
-    *reinterpret_cast<u32x4*>(sm.S + r * PT + cc) = *reinterpret_cast<const u32x4*>(ws.Sb + (size_t)cid * kD * kD + e);
+    *reinterpret_cast<u32x4*>(sm.S + sw_off(r, cc)) = *reinterpret_cast<const u32x4*>(ws.Sb + (size_t)cid * kD * kD + e);
     // U~ tile f = w + 8 p (rb, vb) = (f / 8, f % 8): tokens rb*16 + lq*4 + i of value vb*16 + l16
     const int f = w + 8 * p, ub = f >> 3, vb = f & 7;
     const u32x2 ut = *reinterpret_cast<const u32x2*>(pc + kWsU + ((size_t)f * 64 + lane) * 8);
     const float uv[4] = {lo_bf(ut.x), hi_bf(ut.x), lo_bf(ut.y), hi_bf(ut.y)};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sm.Ut[(16 * ub + 4 * lq + i) * PT + 16 * vb + l16] = f32_to_bf16(uv[i]);
+    for (int i = 0; i < 4; ++i) sm.Ut[sw_off(16 * ub + 4 * lq + i, 16 * vb + l16)] = f32_to_bf16(uv[i]);
   }
   {
     const int e = tid * 8, r = e >> 6, cc = e & 63;
@@ -562,9 +543,9 @@ __global__ __launch_bounds__(512) void gdn_bwd_grad2_kernel(
     f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      a = mfma(ld8(sm.dU + (16 * rb + l16) * PT + 32 * ks + 8 * lq), ld_tr8(sm.S, PT, 32 * ks, 16 * kb), a);
+      a = mfma(ld8(sm.dU + sw_off(16 * rb + l16, 32 * ks + 8 * lq)), ld_tr8s(sm.S, 32 * ks, 16 * kb), a);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sm.dW[(16 * rb + 4 * lq + i) * PT + 16 * kb + l16] = f32_to_bf16(-a[i]);
+    for (int i = 0; i < 4; ++i) sm.dW[sw_off(16 * rb + 4 * lq + i, 16 * kb + l16)] = f32_to_bf16(-a[i]);
   }
   lds_barrier();
 
@@ -579,19 +560,19 @@ __global__ __launch_bounds__(512) void gdn_bwd_grad2_kernel(
     for (int js = 0; js < 2; ++js)
       if (32 * js + 31 >= 16 * rb) {   // T[j][r] is zero for j < r
         const bf16x8 tt = ld_tr8(sm.T, PA, 32 * js, 16 * rb);
-        xw = mfma(tt, ld_tr8(sm.dW, PT, 32 * js, 16 * cb), xw);
-        xu = mfma(tt, ld_tr8(sm.dU, PT, 32 * js, 16 * cb), xu);
+        xw = mfma(tt, ld_tr8s(sm.dW, 32 * js, 16 * cb), xw);
+        xu = mfma(tt, ld_tr8s(sm.dU, 32 * js, 16 * cb), xu);
       }
     const int col = 16 * cb + l16;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * rb + 4 * lq + i;
-      XW[r * PT + col] = f32_to_bf16(xw[i]);
-      XU[r * PT + col] = f32_to_bf16(xu[i]);
+      XW[sw_off(r, col)] = f32_to_bf16(xw[i]);
+      XU[sw_off(r, col)] = f32_to_bf16(xu[i]);
       dv[(tok0 + r) * kD + col] = f32_to_bf16(sm.bt[r] * xu[i]);
       kw[u][i] = sm.bt[r] * sm.g[r] * xw[i];
-      su_acc[i] += sum16(xu[i] * bf16_to_f32(sm.V[r * PT + col]));
-      sw_acc[i] += sum16(xw[i] * bf16_to_f32(sm.K[r * PT + col]));
+      su_acc[i] += sum16(xu[i] * bf16_to_f32(sm.V[sw_off(r, col)]));
+      sw_acc[i] += sum16(xw[i] * bf16_to_f32(sm.K[sw_off(r, col)]));
     }
   }
   if (l16 == 0)
@@ -611,9 +592,9 @@ __global__ __launch_bounds__(512) void gdn_bwd_grad2_kernel(
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const u32x4 wfr = *reinterpret_cast<const u32x4*>(pc + kWsW + ((size_t)(cb * 4 + ks) * 64 + lane) * 16);
-      a = mfma(ld8_split(XW + (16 * ab + l16) * PT + 32 * ks + 4 * lq), as_bf(wfr), a);
-      a = mfma(ld8(XU + (16 * ab + l16) * PT + 32 * ks + 8 * lq), ld8(sm.Ut + (16 * cb + l16) * PT + 32 * ks + 8 * lq), a);
-      gk = mfma(ld8(sm.K + (16 * ab + l16) * PT + 32 * ks + 8 * lq), ld8(sm.K + (16 * cb + l16) * PT + 32 * ks + 8 * lq), gk);
+      a = mfma(ld8_split_s(XW, 16 * ab + l16, 32 * ks + 4 * lq), as_bf(wfr), a);
+      a = mfma(ld8(XU + sw_off(16 * ab + l16, 32 * ks + 8 * lq)), ld8(sm.Ut + sw_off(16 * cb + l16, 32 * ks + 8 * lq)), a);
+      gk = mfma(ld8(sm.K + sw_off(16 * ab + l16, 32 * ks + 8 * lq)), ld8(sm.K + sw_off(16 * cb + l16, 32 * ks + 8 * lq)), gk);
     }
     const int j = 16 * cb + l16;
 #pragma unroll
@@ -642,7 +623,7 @@ __global__ __launch_bounds__(512) void gdn_bwd_grad2_kernel(
     f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int js = 0; js < 2; ++js)
-      a = mfma(ld8(sm.L + (16 * rb + l16) * PA + 32 * js + 8 * lq), ld_tr8(sm.K, PT, 32 * js, 16 * kb), a);
+      a = mfma(ld8(sm.L + (16 * rb + l16) * PA + 32 * js + 8 * lq), ld_tr8s(sm.K, 32 * js, 16 * kb), a);
     const int col = 16 * kb + l16;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
