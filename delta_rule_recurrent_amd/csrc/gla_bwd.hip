@@ -31,16 +31,20 @@
 // state scan (the state before every chunk), a backward state scan (the gradient after
 // every chunk, dS_0 and the chunks' sum_v dS_a o S_a), and a per-chunk gradient kernel
 // (bf16 MFMA, fp32 accumulation; also the gate gradient).
-#include "common.hpp"
+#include "chunk_device.hpp"
 
 namespace gdnrt {
 
 namespace glab {
 
-constexpr int C = kChunk;    // 64
-constexpr int PT = kD + 16;  // bf16 pitch of 128-wide rows read transposed
-constexpr int PA = C + 16;   // bf16 pitch of 64-wide rows read transposed
-constexpr int PX = 16 + 16;  // bf16 pitch of 16-wide rows (one value tile) read transposed
+using namespace gdc;   // C, PS, sw_off, ld8, ld_tr8, ld_tr8s, mfma
+constexpr int PT = PS;       // bf16 pitch of 128-wide rows, stored with swz (rows and transposed reads)
+constexpr int PA = C + 8;    // bf16 pitch of 64-wide rows: a transposed read's groups of lanes,
+                             // 8 rows apart, fall 32 banks apart; 16 rows read by rows on distinct banks
+constexpr int PX = 16 + 16;  // bf16 pitch of 16-wide rows (one value tile), rows with bit 3 set
+                             // in the upper half (columns 16..31): a transposed read's groups
+                             // of lanes, 8 rows apart, on distinct banks
+__device__ __forceinline__ int px_off(int row, int col) { return row * PX + col + ((row & 8) << 1); }
 
 // Workspace per chunk (bytes): bf16 [64][128] Q^, K^; fp32 [64][128] E = e^{b - b_m};
 // fp32 [128] e^{b_C}, e^{b_m}, e^{b_C - b_m}; bf16 [128][128] the state before the
@@ -49,24 +53,12 @@ constexpr int PX = 16 + 16;  // bf16 pitch of 16-wide rows (one value tile) read
 constexpr size_t kQh = 0, kKh = 16384, kE = 32768, kEC = 65536, kEm = 66048, kECm = 66560,
                  kSb = 67072, kdS = 99840, kChunkB = 132608;
 
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-__device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
-}
-__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-// MFMA operand from a row-major [contraction][column] bf16 matrix in LDS through the
-// transposing LDS read: lane (l16, lq) receives X[c0 + 8 lq + e][n0 + l16], e = 0..7.
-__device__ __forceinline__ bf16x8 ld_tr8(const uint16_t* X, int pitch, int c0, int n0) {
+// ld_tr8 from a 16-wide tile stored with px_off
+__device__ __forceinline__ bf16x8 ld_tr8x(const uint16_t* X, int c0) {
   const int lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
-  const uint16_t* p = X + (c0 + 8 * g + (j >> 2)) * pitch + n0 + 4 * (j & 3);
+  const uint16_t* p = X + px_off(c0 + 8 * g + (j >> 2), 4 * (j & 3));
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * pitch));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * PX));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
@@ -227,22 +219,22 @@ __global__ __launch_bounds__(256) void gla_bwd_scan_kernel(const uint16_t* __res
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sst[(4 * lq + i) * PT + 32 * w + 16 * j + l16] = f32_to_bf16(acc[j][i]);
+      for (int i = 0; i < 4; ++i) sst[sw_off(4 * lq + i, 32 * w + 16 * j + l16)] = f32_to_bf16(acc[j][i]);
     if constexpr (BND) {
       *reinterpret_cast<f32x4*>(ssa + tr * (kD + 4) + tc) = sa[0];
       *reinterpret_cast<f32x4*>(ssa + tr * (kD + 4) + tc + 4) = sa[1];
     }
-    *reinterpret_cast<u32x2*>(sx + (tid >> 2) * PX + 4 * (tid & 3)) = xr;
+    *reinterpret_cast<u32x2*>(sx + px_off(tid >> 2, 4 * (tid & 3))) = xr;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int e = (tid + 256 * p) * 8;   // element index in [64][128]
-      *reinterpret_cast<u32x4*>(sy + (e >> 7) * PT + (e & 127)) = yr[p];
+      *reinterpret_cast<u32x4*>(sy + sw_off(e >> 7, e & 127)) = yr[p];
     }
     const float e0 = ec[0], e1 = ec[1];
     if (s + 1 < nc) load(REV ? ci - 1 : ci + 1, xr, yr, ec, sa);
     lds_barrier();
     *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(ws + (chunk0 + ci) * kChunkB + (REV ? kdS : kSb)) +
-                              (size_t)(v0 + tr) * kD + tc) = *reinterpret_cast<const u32x4*>(sst + tr * PT + tc);
+                              (size_t)(v0 + tr) * kD + tc) = *reinterpret_cast<const u32x4*>(sst + sw_off(tr, tc));
     if constexpr (BND) {   // sum over this tile's 16 value rows of dS o S, per key channel
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -257,9 +249,9 @@ __global__ __launch_bounds__(256) void gla_bwd_scan_kernel(const uint16_t* __res
     acc[1] *= e1;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 a = ld_tr8(sx, PX, 32 * ks, 0);
+      const bf16x8 a = ld_tr8x(sx, 32 * ks);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[j] = mfma(a, ld_tr8(sy, PT, 32 * ks, 32 * w + 16 * j), acc[j]);
+      for (int j = 0; j < 2; ++j) acc[j] = mfma(a, ld_tr8s(sy, 32 * ks, 32 * w + 16 * j), acc[j]);
     }
     lds_barrier();
   }
@@ -306,15 +298,15 @@ __global__ __launch_bounds__(512) void gla_bwd_grad_kernel(
       qt[j] = pack_bf16(bf16_to_f32(uint16_t(qq[j])) * ea, bf16_to_f32(uint16_t(qq[j] >> 16)) * eb);
       kt[j] = pack_bf16(bf16_to_f32(uint16_t(kk[j])) / ea, bf16_to_f32(uint16_t(kk[j] >> 16)) / eb);
     }
-    *reinterpret_cast<u32x4*>(sm.Qt + r * PT + cc) = qt;
-    *reinterpret_cast<u32x4*>(sm.Kt + r * PT + cc) = kt;
-    *reinterpret_cast<u32x4*>(sm.dO + r * PT + cc) = *reinterpret_cast<const u32x4*>(dO + (tok0 + r) * kD + cc);
+    *reinterpret_cast<u32x4*>(sm.Qt + sw_off(r, cc)) = qt;
+    *reinterpret_cast<u32x4*>(sm.Kt + sw_off(r, cc)) = kt;
+    *reinterpret_cast<u32x4*>(sm.dO + sw_off(r, cc)) = *reinterpret_cast<const u32x4*>(dO + (tok0 + r) * kD + cc);
   }
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int e = (tid + 512 * p) * 8, r = e >> 7, cc = e & 127;
-    *reinterpret_cast<u32x4*>(sm.Sb + r * PT + cc) = *reinterpret_cast<const u32x4*>(wsc + kSb + (size_t)e * 2);
-    *reinterpret_cast<u32x4*>(sm.dS + r * PT + cc) = *reinterpret_cast<const u32x4*>(wsc + kdS + (size_t)e * 2);
+    *reinterpret_cast<u32x4*>(sm.Sb + sw_off(r, cc)) = *reinterpret_cast<const u32x4*>(wsc + kSb + (size_t)e * 2);
+    *reinterpret_cast<u32x4*>(sm.dS + sw_off(r, cc)) = *reinterpret_cast<const u32x4*>(wsc + kdS + (size_t)e * 2);
   }
   for (int e = tid; e < C * PA / 2; e += 512) {
     reinterpret_cast<uint32_t*>(sm.A)[e] = 0u;
@@ -331,11 +323,11 @@ __global__ __launch_bounds__(512) void gla_bwd_grad_kernel(
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       if (grad)
-        acc = mfma(ld8(sm.dO + (16 * rb + l16) * PT + 32 * ks + 8 * lq),
+        acc = mfma(ld8(sm.dO + sw_off(16 * rb + l16, 32 * ks + 8 * lq)),
                    ld8(v + (tok0 + 16 * cb + l16) * kD + 32 * ks + 8 * lq), acc);
       else
-        acc = mfma(ld8(sm.Qt + (16 * rb + l16) * PT + 32 * ks + 8 * lq),
-                   ld8(sm.Kt + (16 * cb + l16) * PT + 32 * ks + 8 * lq), acc);
+        acc = mfma(ld8(sm.Qt + sw_off(16 * rb + l16, 32 * ks + 8 * lq)),
+                   ld8(sm.Kt + sw_off(16 * cb + l16, 32 * ks + 8 * lq)), acc);
     }
     uint16_t* dst = grad ? sm.dA : sm.A;
     const int j = 16 * cb + l16;
@@ -360,17 +352,17 @@ __global__ __launch_bounds__(512) void gla_bwd_grad_kernel(
     f32x4 dQh = {0.f, 0.f, 0.f, 0.f}, dQt = dQh, dKt = dQh, dKh = dQh, dV = dQh;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      dQh = mfma(ld8(sm.dO + (16 * rb + l16) * PT + 32 * ks + 8 * lq), ld_tr8(sm.Sb, PT, 32 * ks, 16 * cb), dQh);
-      dKh = mfma(ld8(v + (tok0 + 16 * rb + l16) * kD + 32 * ks + 8 * lq), ld_tr8(sm.dS, PT, 32 * ks, 16 * cb), dKh);
-      dV = mfma(ld8(Kh + (16 * rb + l16) * kD + 32 * ks + 8 * lq), ld8(sm.dS + (16 * cb + l16) * PT + 32 * ks + 8 * lq), dV);
+      dQh = mfma(ld8(sm.dO + sw_off(16 * rb + l16, 32 * ks + 8 * lq)), ld_tr8s(sm.Sb, 32 * ks, 16 * cb), dQh);
+      dKh = mfma(ld8(v + (tok0 + 16 * rb + l16) * kD + 32 * ks + 8 * lq), ld_tr8s(sm.dS, 32 * ks, 16 * cb), dKh);
+      dV = mfma(ld8(Kh + (16 * rb + l16) * kD + 32 * ks + 8 * lq), ld8(sm.dS + sw_off(16 * cb + l16, 32 * ks + 8 * lq)), dV);
     }
 #pragma unroll
     for (int js = 0; js < 2; ++js) {
       if (js <= rb / 2)   // dA[t][j] is zero for j > t
-        dQt = mfma(ld8(sm.dA + (16 * rb + l16) * PA + 32 * js + 8 * lq), ld_tr8(sm.Kt, PT, 32 * js, 16 * cb), dQt);
+        dQt = mfma(ld8(sm.dA + (16 * rb + l16) * PA + 32 * js + 8 * lq), ld_tr8s(sm.Kt, 32 * js, 16 * cb), dQt);
       if (32 * js + 31 >= 16 * rb) {   // dA[r][t], A[r][t] are zero for r < t
-        dKt = mfma(ld_tr8(sm.dA, PA, 32 * js, 16 * rb), ld_tr8(sm.Qt, PT, 32 * js, 16 * cb), dKt);
-        dV = mfma(ld_tr8(sm.A, PA, 32 * js, 16 * rb), ld_tr8(sm.dO, PT, 32 * js, 16 * cb), dV);
+        dKt = mfma(ld_tr8(sm.dA, PA, 32 * js, 16 * rb), ld_tr8s(sm.Qt, 32 * js, 16 * cb), dKt);
+        dV = mfma(ld_tr8(sm.A, PA, 32 * js, 16 * rb), ld_tr8s(sm.dO, 32 * js, 16 * cb), dV);
       }
     }
     const float emc = em[col], ecmc = ecm[col];
