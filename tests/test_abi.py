@@ -10,7 +10,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gdnrt.h")
-LIB = os.path.join(ROOT, "delta_rule_recurrent_amd", "libgdnrt.so")
+# GDNRT_ABI_LIB: another build of the library to check (the host-sanitized one)
+LIB = os.environ.get("GDNRT_ABI_LIB") or os.path.join(ROOT, "delta_rule_recurrent_amd", "libgdnrt.so")
 
 OK, EINVAL, ESHAPE, EALIGN, EDTYPE, ESTATE = range(6)
 
@@ -21,6 +22,8 @@ def lib():
         from delta_rule_recurrent_amd import build
         build.build()
     from delta_rule_recurrent_amd import binding
+    if binding._LIB is None:
+        binding.LIB_PATH = LIB
     return binding.lib()
 
 
