@@ -1,7 +1,7 @@
 """Benchmark of the gated delta-rule hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--rows decode,bf16_state,int8_state,kda,leapq,
-                     kda_leapq,gla,zeco,gla_bwd,gdn,gdn_bwd,kda_chunk]
+                     leapq6,leapq4,kda_leapq,gla,zeco,gla_bwd,gdn,gdn_bwd,kda_chunk]
 
 Headline (`value`): Gated DeltaNet decode of one layer, 512 streams x 32 heads,
 d_k = d_v = 128, fp32 state resident in HBM, bf16 q/k/v; one step = one token for
@@ -237,9 +237,9 @@ def cpu_baseline_decode(inp, target_s=15.0):
 
 # ------------------------------------------------------------------- LeapQuant
 
-def leapq_bytes_per_head_window(W=16, rank=4, kda=False, fused=True):
+def leapq_bytes_per_head_window(W=16, rank=4, kda=False, fused=True, bits=8):
     """Algorithmic bytes of one head over one window. A decode step at position m
-    reads codes 16,384 + scales 1,024 + compensators 4*r*128 + m buffered records
+    reads codes 16,384 (8 bits; 12,288 at 6 bits, 8,192 at 4, packed) + scales 1,024 + compensators 4*r*128 + m buffered records
     (k, u fp32 and a) + q, k, v (bf16) and alpha, beta; it writes one record and o
     (bf16). With ``fused`` (the window's last token decoded inside its flush) the
     window is W - 1 such steps and one launch that reads the stored state, the
@@ -247,7 +247,7 @@ def leapq_bytes_per_head_window(W=16, rank=4, kda=False, fused=True):
     it, W steps and a flush that reads the stored state and the W records and
     writes the stored state. With ``kda`` every decay is a 128-long fp32 vector
     (the token's alpha and each record's)."""
-    stored = D * D + 2 * D * 4 + rank * 2 * D * 2          # 19,456 at r = 4
+    stored = D * m.code_row_bytes(bits) + 2 * D * 4 + rank * 2 * D * 2   # 19,456 at r = 4, 8 bits
     a_b = D * 4 if kda else 4
     rec = 2 * D * 4 + a_b                                 # 1,028 (KDA 1,536)
     io_in, io_out = 3 * D * 2 + a_b + 4, D * 2
@@ -257,19 +257,19 @@ def leapq_bytes_per_head_window(W=16, rank=4, kda=False, fused=True):
     return sum(step(m) for m in range(W)) + stored + W * rec + stored
 
 
-def bench_leapq(tokens=4096, B=DECODE_B, H=DECODE_H, W=16, rank=4, kda=False):
+def bench_leapq(tokens=4096, B=DECODE_B, H=DECODE_H, W=16, rank=4, kda=False, bits=8):
     """The windowed INT8 state over ``tokens`` decode steps (every window: W - 1
     decode launches, then the window's last token and its flush in one launch; the
     two-launch form, W decode launches and a flush, is timed beside it). With
     ``kda``: one decay per key channel (inputs are drawn for 256 steps and reused
-    cyclically)."""
+    cyclically). ``bits`` 6 or 4: the codes stored packed at that width."""
     N = B * H
-    tag = "kda_leapq" if kda else "leapq"
+    tag = ("kda_leapq" if kda else "leapq") + (str(bits) if bits != 8 else "")
     gen = min(tokens, 256) if kda else tokens
     log(f"[{tag}] generating B={B} H={H} steps={gen}")
     inp = (synth.kda_leapq_decode if kda else synth.leapq_decode)(B=B, H=H, steps=gen, device="cuda")
-    st = m.LeapqBuffers(N, rank=rank, window=W, kda=kda)
-    Q0 = inp["Q0"].cuda()
+    st = m.LeapqBuffers(N, rank=rank, window=W, kda=kda, bits=bits)
+    Q0 = (inp["Q0"] if rank == inp["Q0"].shape[1] else synth.compensator_start(r=rank)).cuda()
     q, k, v, a, b = (inp[n] for n in ("q", "k", "v", "alpha", "beta"))
     o = torch.empty((N, D), dtype=torch.bfloat16, device="cuda")
     step = m.kda_leapq_decode_step if kda else m.leapq_decode_step
@@ -294,8 +294,8 @@ def bench_leapq(tokens=4096, B=DECODE_B, H=DECODE_H, W=16, rank=4, kda=False):
     ms_win, wall = timed(run_window, n_win, 1)
     ms_win2, _ = timed(run_window_two_launch, n_win, 1)
     ms_step = ms_win / W
-    bpw = leapq_bytes_per_head_window(W, rank, kda) * N
-    bpw2 = leapq_bytes_per_head_window(W, rank, kda, fused=False) * N
+    bpw = leapq_bytes_per_head_window(W, rank, kda, bits=bits) * N
+    bpw2 = leapq_bytes_per_head_window(W, rank, kda, fused=False, bits=bits) * N
     # per-kernel split from events around each launch of one window
     s = torch.cuda.current_stream()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(W + 2)]
@@ -315,7 +315,8 @@ def bench_leapq(tokens=4096, B=DECODE_B, H=DECODE_H, W=16, rank=4, kda=False):
     dec_ms = ev[0].elapsed_time(ev[W]) / W
     flush_ms = ev[W].elapsed_time(ev[W + 1])
     last_ms = ev2[0].elapsed_time(ev2[1])
-    res = dict(workload=f"{tag}_decode B={B} H={H} d=128, INT8 residual + fp32 scales + {rank} fp16 "
+    width = "INT8" if bits == 8 else f"{bits}-bit packed"
+    res = dict(workload=f"{tag}_decode B={B} H={H} d=128, {width} residual + fp32 scales + {rank} fp16 "
                         f"compensators, {W}-token fp32 buffer"
                         f"{' with per-channel fp32 decays' if kda else ''}, {tokens} tokens",
                ms_per_step=ms_step, tokens_per_s=B / (ms_step * 1e-3),
@@ -645,7 +646,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--rows", default="decode,bf16_state,int8_state,kda,leapq,kda_leapq,gla,zeco,gla_bwd,gdn,gdn_bwd,"
+    ap.add_argument("--rows", default="decode,bf16_state,int8_state,kda,leapq,leapq6,leapq4,kda_leapq,gla,zeco,gla_bwd,gdn,gdn_bwd,"
                                       "kda_chunk")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true",
@@ -758,6 +759,16 @@ def main():
             f"{r['decode_flush_kernel_ms']*1e3:.1f} us last token + flush per window; two launches "
             f"{r['two_launch_ms_per_step']*1e3:.1f} us/step)  {r['achieved_gbs']:.0f} GB/s  "
             f"{r['tokens_per_s']/1e6:.3f} M tok/s")
+        torch.cuda.empty_cache()
+    for bits in (6, 4):
+        if f"leapq{bits}" not in rows:
+            continue
+        r = bench_leapq(bits=bits, rank=6)
+        r["speedup_vs_int8"] = out_rows["leapq"]["ms_per_step"] / r["ms_per_step"] if "leapq" in out_rows else None
+        out_rows[f"leapq{bits}"] = r
+        log(f"[leapq{bits}] {r['ms_per_step']*1e3:.1f} us/step ({r['decode_kernel_ms']*1e3:.1f} us decode, "
+            f"{r['decode_flush_kernel_ms']*1e3:.1f} us last token + flush per window)  "
+            f"{r['achieved_gbs']:.0f} GB/s  {r['tokens_per_s']/1e6:.3f} M tok/s")
         torch.cuda.empty_cache()
     if "kda_leapq" in rows:
         r = bench_leapq(tokens=256, kda=True)

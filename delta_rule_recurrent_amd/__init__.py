@@ -14,6 +14,7 @@ draws the seeded synthetic workloads.
 from .binding import (  # noqa: F401
     GdnrtError,
     LeapqBuffers,
+    code_row_bytes,
     gdn_chunk_bwd,
     gdn_chunk_bwd_workspace,
     gdn_chunk_fwd,

@@ -473,6 +473,11 @@ def _chunk_fwd(name, alloc, alpha_shape, q, k, v, alpha, beta, S0, ST, o, worksp
     return o, ST
 
 
+def code_row_bytes(bits):
+    """Bytes of one value row of LeapQuant codes (128 codes) at this width."""
+    return 16 * bits if bits in (4, 6) else D
+
+
 class LeapqBuffers:
     """Caller-owned device memory of a LeapQuant state for N heads (see
     ``leapq_state`` in include/gdnrt.h). Allocated once by torch."""
@@ -480,7 +485,8 @@ class LeapqBuffers:
     def __init__(self, N, rank=4, window=16, device="cuda", kda=False, bits=8):
         self.N, self.rank, self.window, self.kda, self.bits = N, rank, window, kda, bits
         f = dict(dtype=torch.float32, device=device)
-        self.codes = torch.zeros((N, D, D), dtype=torch.int8, device=device)
+        # one value row of codes: packed at 4 and 6 bits (include/gdnrt.h), a byte per code otherwise
+        self.codes = torch.zeros((N, D, code_row_bytes(bits)), dtype=torch.int8, device=device)
         self.vscale = torch.zeros((N, D), **f)
         self.ksmooth = torch.ones((N, D), **f)
         # fp16 bit patterns; view as torch.float16 for reading
@@ -499,6 +505,23 @@ class LeapqBuffers:
     @property
     def struct(self):
         return self._st
+
+    def code_values(self):
+        """The signed codes [N][128][128] as int8, unpacked from the stored rows by
+        torch ops on the codes' device (for inspection and studies, not the decode
+        path): at 4 bits byte j holds codes 2j and 2j+1 in its low and high nibble, at 6
+        bits each 3 bytes hold four codes in 6-bit fields of a little-endian 24-bit
+        word, two's complement."""
+        raw = self.codes.view(torch.uint8).to(torch.int32)
+        if self.bits == 4:
+            z = torch.stack((raw & 15, raw >> 4), dim=-1).reshape(self.N, D, D)
+            return torch.where(z >= 8, z - 16, z).to(torch.int8)
+        if self.bits == 6:
+            g = raw.reshape(self.N, D, 32, 3)
+            w = g[..., 0] | (g[..., 1] << 8) | (g[..., 2] << 16)
+            z = torch.stack([(w >> (6 * i)) & 63 for i in range(4)], dim=-1).reshape(self.N, D, D)
+            return torch.where(z >= 32, z - 64, z).to(torch.int8)
+        return self.codes
 
 
 def _flush(name, st, q0, dense, iters, smooth_mode, pre_round):

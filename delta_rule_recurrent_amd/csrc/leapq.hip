@@ -22,6 +22,51 @@ __device__ __forceinline__ uint16_t f2h(float x) { return __builtin_bit_cast(uin
 // sign-extend byte b of w to float
 __device__ __forceinline__ float sb(uint32_t w, int b) { return (float)((int32_t)(w << (24 - 8 * b)) >> 24); }
 
+// Packed code rows (bits = 4 or 6; one byte per code otherwise). A value row's 128 codes
+// are 16 * bits bytes: at 4 bits byte j holds codes 2 j (low nibble) and 2 j + 1; at 6 bits
+// each 3 bytes hold four codes, code 4 c + i in bits [6 i, 6 i + 6) of the little-endian
+// 24-bit group c. Codes are two's complement in their width.
+__host__ __device__ constexpr int row_bytes(int pk) { return pk == 8 ? 128 : 16 * pk; }
+
+// four codes of width 4 or 6 in the low byte of each byte lane -> four int8 (sign extension)
+template <int PK>
+__device__ __forceinline__ uint32_t sext4(uint32_t x) {
+  constexpr uint32_t sign = 0x01010101u << (PK - 1), high = 0xffu & ~((1u << PK) - 1u);
+  return x | ((x & sign) >> (PK - 1)) * high;
+}
+// 8 codes at 4 bits (one word) -> 2 words of 4 int8, in order
+__device__ __forceinline__ void unpack4(uint32_t w, uint32_t& a, uint32_t& b) {
+  const uint32_t lo = sext4<4>(w & 0x0f0f0f0fu), hi = sext4<4>((w >> 4) & 0x0f0f0f0fu);
+  a = __builtin_amdgcn_perm(hi, lo, 0x05010400u);   // codes 0..3: lo.b0, hi.b0, lo.b1, hi.b1
+  b = __builtin_amdgcn_perm(hi, lo, 0x07030602u);   // codes 4..7
+}
+// 4 codes at 6 bits (one 24-bit group, low bits of g) -> 1 word of 4 int8
+__device__ __forceinline__ uint32_t unpack6(uint32_t g) {
+  const uint32_t x = (g & 0x3fu) | ((g << 2) & 0x3f00u) | ((g << 4) & 0x3f0000u) | ((g << 6) & 0x3f000000u);
+  return sext4<6>(x);
+}
+// 16 codes at 6 bits (three words, 12 bytes) -> 4 words of 4 int8
+__device__ __forceinline__ void unpack6x16(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t (&o)[4]) {
+  o[0] = unpack6(w0);
+  o[1] = unpack6(__builtin_amdgcn_alignbit(w1, w0, 24));
+  o[2] = unpack6(__builtin_amdgcn_alignbit(w2, w1, 16));
+  o[3] = unpack6(w2 >> 8);
+}
+// 8 int8 codes (two words) -> one word of 4-bit codes
+__device__ __forceinline__ uint32_t pack4(uint32_t a, uint32_t b) {
+  auto half = [](uint32_t x) {
+    x &= 0x0f0f0f0fu;
+    x = (x | (x >> 4)) & 0x00ff00ffu;
+    return (x | (x >> 8)) & 0xffffu;
+  };
+  return half(a) | (half(b) << 16);
+}
+// 4 int8 codes (one word) -> one 24-bit group of 6-bit codes
+__device__ __forceinline__ uint32_t pack6(uint32_t w) {
+  const uint32_t x = w & 0x3f3f3f3fu;
+  return (x & 0x3fu) | ((x >> 2) & 0xfc0u) | ((x >> 4) & 0x3f000u) | ((x >> 6) & 0xfc0000u);
+}
+
 // Suffix products of the m buffered decays a_0 .. a_{m-1} of one channel (stride
 // floats apart): put(j, prod_{j<i<m} a_i) for j < m, then put(m, prod_{i<m} a_i),
 // multiplied newest first. Every decay is requested before the first product, so
@@ -109,7 +154,9 @@ __device__ __forceinline__ int fixed_digits(const float (&x)[8], float mx, uint2
   return e;
 }
 
-template <typename IO, bool KDA>
+// PK: the code width in memory, 8 (one byte per code, read through LDS) or 4 / 6 (packed
+// rows, read into registers and widened to int8 there).
+template <typename IO, bool KDA, int PK>
 __global__ __launch_bounds__(256) void leapq_decode_kernel(
     const int8_t* __restrict__ codes, const float* __restrict__ vscale,
     const float* __restrict__ ksmooth, const uint16_t* __restrict__ ct_k,
@@ -121,7 +168,7 @@ __global__ __launch_bounds__(256) void leapq_decode_kernel(
   // this head's codes, straight from HBM (rows of eight 16-byte pieces; piece c of row r
   // at slot c ^ ((r >> 1) & 7), so that the 16 rows an MFMA operand read takes fall on
   // distinct banks)
-  __shared__ __attribute__((aligned(16))) int8_t s_codes[kD * kD];
+  __shared__ __attribute__((aligned(16))) int8_t s_codes[PK == 8 ? kD * kD : 16];
   __shared__ __attribute__((aligned(16))) uint2 s_dig[4][8][kD / 8];   // per wave: digit rows
                                                                       // (x_k 0-2, x_q 3-5, 6-7 zero)
   __shared__ float s_dk[NV], s_dq[NV];
@@ -144,12 +191,27 @@ __global__ __launch_bounds__(256) void leapq_decode_kernel(
   // row 32 w + 8 i + L / 8. Non-temporal: the codes of all heads do not fit the caches
   // between two steps, and keeping them out leaves room for the buffered records, which
   // every step re-reads.
+  // Packed rows instead: the lane's codes (row 32 w + 16 T + n, codes 64 s + 16 g ..
+  // + 15) as 8 or 12 bytes in registers.
+  constexpr int RB = row_bytes(PK);
+  uint32_t zp[2][2][PK == 6 ? 3 : 2];
+  if constexpr (PK == 8) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 32 * w + 8 * i + (lane >> 3), c = (lane & 7) ^ ((r >> 1) & 7);
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(codes + (hk + r) * kD + 16 * c),
-                                     (__attribute__((address_space(3))) void*)(s_codes + (32 * w + 8 * i) * kD), 16,
-                                     0, 2 /* nt */);
+    for (int i = 0; i < 4; ++i) {
+      const int r = 32 * w + 8 * i + (lane >> 3), c = (lane & 7) ^ ((r >> 1) & 7);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(codes + (hk + r) * kD + 16 * c),
+                                       (__attribute__((address_space(3))) void*)(s_codes + (32 * w + 8 * i) * kD),
+                                       16, 0, 2 /* nt */);
+    }
+  } else {
+#pragma unroll
+    for (int T = 0; T < 2; ++T)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(codes + (hk + row[T]) * RB + (64 * s + 16 * g) * PK / 8);
+#pragma unroll
+        for (int e = 0; e < (PK == 6 ? 3 : 2); ++e) zp[T][s][e] = __builtin_nontemporal_load(src + e);
+      }
   }
   // buffered corrections and compensator values of this lane's rows, slots = g (mod 4)
   float bur[2][kMaxWindow / 4], cur[2][kMaxRank / 4], vrow[2], vsr[2];
@@ -313,15 +375,31 @@ __global__ __launch_bounds__(256) void leapq_decode_kernel(
   // 32 w + 16 T + n, bytes 64 s + 16 g, from the wave's own LDS copy (complete once the
   // wave's vector memory operations are: the compiler does not order LDS reads after LDS
   // DMA, and before this point the wave has issued no stores)
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   i32x4 zb[2][2];
+  if constexpr (PK == 8) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
-  for (int T = 0; T < 2; ++T)
+    for (int T = 0; T < 2; ++T)
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int r = row[T], c = 4 * s + g;
-      zb[T][s] = *reinterpret_cast<const i32x4*>(s_codes + r * kD + 16 * (c ^ ((r >> 1) & 7)));
-    }
+      for (int s = 0; s < 2; ++s) {
+        const int r = row[T], c = 4 * s + g;
+        zb[T][s] = *reinterpret_cast<const i32x4*>(s_codes + r * kD + 16 * (c ^ ((r >> 1) & 7)));
+      }
+  } else {
+#pragma unroll
+    for (int T = 0; T < 2; ++T)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        uint32_t u[4];
+        if constexpr (PK == 4) {
+          unpack4(zp[T][s][0], u[0], u[1]);
+          unpack4(zp[T][s][1], u[2], u[3]);
+        } else {
+          unpack6x16(zp[T][s][0], zp[T][s][1], zp[T][s][2], u);
+        }
+        zb[T][s] = i32x4{(int)u[0], (int)u[1], (int)u[2], (int)u[3]};
+      }
+  }
   i32x4 acc[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
@@ -578,7 +656,7 @@ __global__ __launch_bounds__(kFlushNT) __attribute__((amdgpu_waves_per_eu(RANK <
     uint16_t* __restrict__ ct_k, uint16_t* __restrict__ ct_u, const float* __restrict__ buf_k,
     const float* __restrict__ buf_u, const float* __restrict__ buf_a, int window, int m,
     const float* __restrict__ dense, const float* __restrict__ q0, int iters, int smooth_mode,
-    float qf, float qinv, float* __restrict__ pre_round, FlushToken tok) {
+    float qf, float qinv, float* __restrict__ pre_round, FlushToken tok, int pk) {
   constexpr int RQ = RANK <= 4 ? 4 : 8;   // padded rank of the LDS blocks
   __shared__ FlushSmem<RQ> sm;
   __shared__ FlushDecays<KDA> dk_[1];
@@ -603,8 +681,9 @@ __global__ __launch_bounds__(kFlushNT) __attribute__((amdgpu_waves_per_eu(RANK <
   }
   const int nt = dense ? 0 : RANK + m;   // rank-one terms of the rebuild
   const int ns = (nt + 3) >> 2;          // MFMA steps of four terms
-  uint4 z[2][2];
+  uint4 z[2][2];   // the lane's 32 codes of each row: 32, 16 or 24 bytes as stored (pk)
   float vs[2];
+  const int RB = row_bytes(pk);
   if constexpr (TOK) {
     if (tid < kD) {
       s_tok[tid] = ld_io(tok.k, hk + tid, tok.io);
@@ -625,9 +704,18 @@ __global__ __launch_bounds__(kFlushNT) __attribute__((amdgpu_waves_per_eu(RANK <
     // every input of the rebuild is requested before the one wait
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const uint4* zp = reinterpret_cast<const uint4*>(codes + (hk + vrow[t]) * kD + 32 * g);
-      z[t][0] = zp[0];
-      z[t][1] = zp[1];
+      const int8_t* zr = codes + (hk + vrow[t]) * RB + 4 * pk * g;
+      if (pk == 8) {
+        z[t][0] = reinterpret_cast<const uint4*>(zr)[0];
+        z[t][1] = reinterpret_cast<const uint4*>(zr)[1];
+      } else if (pk == 4) {
+        z[t][0] = *reinterpret_cast<const uint4*>(zr);
+      } else {   // 24 bytes, 8-byte aligned
+        const uint2 a = reinterpret_cast<const uint2*>(zr)[0], b = reinterpret_cast<const uint2*>(zr)[1],
+                    c = reinterpret_cast<const uint2*>(zr)[2];
+        z[t][0] = make_uint4(a.x, a.y, b.x, b.y);
+        z[t][1] = make_uint4(c.x, c.y, 0u, 0u);
+      }
       vs[t] = vscale[hk + vrow[t]];
     }
     // term rows (compensators, then records; zero up to a multiple of four): piece q
@@ -689,8 +777,21 @@ __global__ __launch_bounds__(kFlushNT) __attribute__((amdgpu_waves_per_eu(RANK <
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const float sv = g0 * vs[t] * qinv;
-      const uint32_t zw[8] = {z[t][0].x, z[t][0].y, z[t][0].z, z[t][0].w,
-                              z[t][1].x, z[t][1].y, z[t][1].z, z[t][1].w};
+      uint32_t zw[8] = {z[t][0].x, z[t][0].y, z[t][0].z, z[t][0].w, z[t][1].x, z[t][1].y, z[t][1].z, z[t][1].w};
+      if (pk == 4) {
+        const uint4 p4 = z[t][0];
+        unpack4(p4.x, zw[0], zw[1]);
+        unpack4(p4.y, zw[2], zw[3]);
+        unpack4(p4.z, zw[4], zw[5]);
+        unpack4(p4.w, zw[6], zw[7]);
+      } else if (pk == 6) {
+        uint32_t u[4];
+        const uint4 a = z[t][0], b = z[t][1];
+        unpack6x16(a.x, a.y, a.z, u);
+        zw[0] = u[0]; zw[1] = u[1]; zw[2] = u[2]; zw[3] = u[3];
+        unpack6x16(a.w, b.x, b.y, u);
+        zw[4] = u[0]; zw[5] = u[1]; zw[6] = u[2]; zw[7] = u[3];
+      }
 #pragma unroll
       for (int tc = 0; tc < 8; ++tc) {
         const f32x4 cc = lds4(sm.col + 32 * g + 4 * tc);
@@ -931,14 +1032,31 @@ __global__ __launch_bounds__(kFlushNT) __attribute__((amdgpu_waves_per_eu(RANK <
       }
       wd[tc] = word;
     }
-    uint4* zr = reinterpret_cast<uint4*>(codes + (hk + vrow[t]) * kD + 32 * g);
-    zr[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-    zr[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
+    int8_t* zo = codes + (hk + vrow[t]) * RB + 4 * pk * g;
+    if (pk == 8) {
+      reinterpret_cast<uint4*>(zo)[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+      reinterpret_cast<uint4*>(zo)[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
+    } else if (pk == 4) {
+      *reinterpret_cast<uint4*>(zo) =
+          make_uint4(pack4(wd[0], wd[1]), pack4(wd[2], wd[3]), pack4(wd[4], wd[5]), pack4(wd[6], wd[7]));
+    } else {   // eight 24-bit groups -> six words
+      uint32_t gr[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) gr[i] = pack6(wd[i]);
+      uint2* zo2 = reinterpret_cast<uint2*>(zo);
+      zo2[0] = make_uint2(gr[0] | (gr[1] << 24), (gr[1] >> 8) | (gr[2] << 16));
+      zo2[1] = make_uint2((gr[2] >> 16) | (gr[3] << 8), gr[4] | (gr[5] << 24));
+      zo2[2] = make_uint2((gr[5] >> 8) | (gr[6] << 16), (gr[6] >> 16) | (gr[7] << 8));
+    }
   }
 }
 
 // largest code of the state's grid: 2^(bits-1) - 1, bits = 0 meaning 8
 static int code_max(const leapq_state* st) { return (1 << ((st->bits ? st->bits : 8) - 1)) - 1; }
+// code width in memory: 4 and 6 bits are packed, every other width takes a byte
+static int packing(const leapq_state* st) { return st->bits == 4 || st->bits == 6 ? st->bits : 8; }
+// bytes of the stored codes of all heads
+static size_t code_bytes(const leapq_state* st) { return (size_t)st->N * kD * row_bytes(packing(st)); }
 
 static int check_state(const leapq_state* st, const char* fn) {
   if (!st) return set_error(GDNRT_EINVAL, "%s: null state", fn);
@@ -987,22 +1105,27 @@ int decode_step(const char* fn, const leapq_state* st, int pos, const void* q, c
   const size_t N = st->N, nIO = N * kD * es, nB = N * st->window * kD * 4;
   if (overlaps(o, nIO, q, nIO) || overlaps(o, nIO, k, nIO) || overlaps(o, nIO, v, nIO) ||
       overlaps(o, nIO, st->buf_k, nB) || overlaps(o, nIO, st->buf_u, nB) ||
-      overlaps(o, nIO, st->codes, N * kD * kD))
+      overlaps(o, nIO, st->codes, code_bytes(st)))
     return set_error(GDNRT_EINVAL, "%s: o overlaps another buffer", fn);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid((unsigned)N), block(256);
   const float qinv = 1.0f / (float)code_max(st);
-  if (io == GDNRT_F32)
-    hipLaunchKernelGGL((leapq_decode_kernel<float, KDA>), grid, block, 0, s, st->codes, st->vscale,
-                       st->ksmooth, st->ct_k, st->ct_u, st->buf_k, st->buf_u, st->buf_a, st->rank,
-                       st->window, pos, qinv, static_cast<const float*>(q), static_cast<const float*>(k),
-                       static_cast<const float*>(v), alpha, beta, static_cast<float*>(o));
-  else
-    hipLaunchKernelGGL((leapq_decode_kernel<uint16_t, KDA>), grid, block, 0, s, st->codes, st->vscale,
-                       st->ksmooth, st->ct_k, st->ct_u, st->buf_k, st->buf_u, st->buf_a, st->rank,
-                       st->window, pos, qinv, static_cast<const uint16_t*>(q),
-                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), alpha,
-                       beta, static_cast<uint16_t*>(o));
+#define GDNRT_DECODE(IOT, PKV)                                                                        \
+  hipLaunchKernelGGL((leapq_decode_kernel<IOT, KDA, PKV>), grid, block, 0, s, st->codes, st->vscale,   \
+                     st->ksmooth, st->ct_k, st->ct_u, st->buf_k, st->buf_u, st->buf_a, st->rank,       \
+                     st->window, pos, qinv, static_cast<const IOT*>(q), static_cast<const IOT*>(k),   \
+                     static_cast<const IOT*>(v), alpha, beta, static_cast<IOT*>(o))
+  const int pk = packing(st);
+  if (io == GDNRT_F32) {
+    if (pk == 4) GDNRT_DECODE(float, 4);
+    else if (pk == 6) GDNRT_DECODE(float, 6);
+    else GDNRT_DECODE(float, 8);
+  } else {
+    if (pk == 4) GDNRT_DECODE(uint16_t, 4);
+    else if (pk == 6) GDNRT_DECODE(uint16_t, 6);
+    else GDNRT_DECODE(uint16_t, 8);
+  }
+#undef GDNRT_DECODE
   return check_launch(fn);
 }
 
@@ -1021,11 +1144,12 @@ int window_flush(const char* fn, const leapq_state* st, int pos, const float* de
       (KDA && !aligned16(st->buf_a)))
     return set_error(GDNRT_EALIGN, "%s: dense, pre_round%s must be 16-byte aligned", fn, KDA ? ", buf_a" : "");
   const size_t N = st->N, nS = N * kD * kD * 4;
-  if ((dense && (overlaps(dense, nS, st->codes, N * kD * kD) || overlaps(dense, nS, pre_round, nS))) ||
-      (pre_round && overlaps(pre_round, nS, st->codes, N * kD * kD)))
+  if ((dense && (overlaps(dense, nS, st->codes, code_bytes(st)) || overlaps(dense, nS, pre_round, nS))) ||
+      (pre_round && overlaps(pre_round, nS, st->codes, code_bytes(st))))
     return set_error(GDNRT_EINVAL, "%s: dense / pre_round overlap the state", fn);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float qf = (float)code_max(st), qinv = 1.0f / qf;
+  const int pk = packing(st);
   switch (st->rank) {
 #define GDNRT_FLUSH(R)                                                                            \
   case R:                                                                                         \
@@ -1033,12 +1157,12 @@ int window_flush(const char* fn, const leapq_state* st, int pos, const float* de
       hipLaunchKernelGGL((leapq_flush_kernel<R, KDA, true>), dim3((unsigned)N), dim3(kFlushNT),  \
                          0, s, st->codes, st->vscale, st->ksmooth, st->ct_k, st->ct_u, st->buf_k, \
                          st->buf_u, st->buf_a, st->window, pos, dense, q0, iters, smooth_mode,    \
-                         qf, qinv, pre_round, tok);                                               \
+                         qf, qinv, pre_round, tok, pk);                                           \
     else                                                                                          \
       hipLaunchKernelGGL((leapq_flush_kernel<R, KDA, false>), dim3((unsigned)N), dim3(kFlushNT), \
                          0, s, st->codes, st->vscale, st->ksmooth, st->ct_k, st->ct_u, st->buf_k, \
                          st->buf_u, st->buf_a, st->window, pos, dense, q0, iters, smooth_mode,    \
-                         qf, qinv, pre_round, tok);                                               \
+                         qf, qinv, pre_round, tok, pk);                                           \
     break;
     GDNRT_FLUSH(0) GDNRT_FLUSH(1) GDNRT_FLUSH(2) GDNRT_FLUSH(3) GDNRT_FLUSH(4)
     GDNRT_FLUSH(5) GDNRT_FLUSH(6) GDNRT_FLUSH(7) GDNRT_FLUSH(8)
@@ -1068,7 +1192,7 @@ int decode_flush(const char* fn, const leapq_state* st, const void* q, const voi
   // the other blocks still read their token inputs, so no input may share a byte with o or
   // with the state the launch writes (a cross-block race otherwise).
   struct Span { const void* p; size_t n; };
-  const Span written[] = {{o, nIO}, {st->codes, N * kD * kD}, {st->vscale, nV}, {st->ksmooth, nV},
+  const Span written[] = {{o, nIO}, {st->codes, code_bytes(st)}, {st->vscale, nV}, {st->ksmooth, nV},
                           {st->ct_k, nCT}, {st->ct_u, nCT}};
   const Span read[] = {{q, nIO}, {k, nIO}, {v, nIO}, {alpha, nA}, {beta, N * 4},
                        {st->buf_k, nB}, {st->buf_u, nB}, {st->buf_a, nBA}};

@@ -44,7 +44,7 @@ def _per_step_state(S0, bits):
 
 
 def _windowed_dense(st, Q):
-    S = st.vscale[:, :, None] * (st.codes.float() / Q) * st.ksmooth[:, None, :]
+    S = st.vscale[:, :, None] * (st.code_values().float() / Q) * st.ksmooth[:, None, :]
     if st.rank > 0:
         S = S + st.ct_u.float().transpose(1, 2) @ st.ct_k.float()
     return S

@@ -375,10 +375,16 @@ GDNRT_API int gdn_decode_step_int_state(int8_t* codes, float* rowmax, int bits,
  * smooth what is left" eq. 7, layout from section "What 1.19 bytes buys").
  * A host struct of caller-owned device pointers, per head n of N:
  *
- *   codes   [N][dv][dk] int8   residual codes Z in [-Q, Q]: Q = 127 at 8 bits; `bits`
- *                              = 6 or 4 narrows the grid (Q = 31, 7) in the same
- *                              int8 container (the narrower widths of section "Fix
- *                              two", which pairs them with 6 compensator tokens)
+ *   codes   [N][dv][RB] bytes  residual codes Z in [-Q, Q], Q = 2^(bits-1) - 1 (127 at 8
+ *                              bits), one value row of dk = 128 codes in RB bytes.
+ *                              bits = 6 or 4 (the narrower widths of section "Fix two",
+ *                              which pairs them with 6 compensator tokens) are packed:
+ *                              RB = 16 * bits; at 4 bits byte j holds codes 2j (low
+ *                              nibble) and 2j+1 (high nibble); at 6 bits every 3 bytes
+ *                              hold 4 codes, code 4c+i in bits [6i, 6i+6) of the
+ *                              little-endian 24-bit group c; codes are two's complement
+ *                              in their width. Any other width takes one int8 per code
+ *                              (RB = 128).
  *   vscale  [N][dv]     fp32   one scale per value channel (row): its largest
  *                              smoothed residual magnitude
  *   ksmooth [N][dk]     fp32   one smoothing factor per key channel (column)

@@ -11,7 +11,7 @@ import torch
 import delta_rule_recurrent_amd as m
 from delta_rule_recurrent_amd import synth
 from oracle import gdn, kda_leapq, leapq
-from helpers import assert_rel, need_gpu, np64, rel_err, say
+from helpers import assert_rel, need_gpu, np64, rel_err, say, codes_of
 
 pytestmark = pytest.mark.gpu
 
@@ -22,7 +22,7 @@ TOL_BF16 = 2e-2
 def stored(st, heads=None):
     """GPU stored state -> oracle dict (exact upcasts)."""
     sel = (lambda t: t) if heads is None else (lambda t: t[heads])
-    d = dict(Z=sel(st.codes).cpu().numpy(), s=np64(sel(st.vscale)), c=np64(sel(st.ksmooth)))
+    d = dict(Z=codes_of(st, heads), s=np64(sel(st.vscale)), c=np64(sel(st.ksmooth)))
     if st.rank > 0:
         d["kt"] = np64(sel(st.ct_k))
         d["ut"] = np64(sel(st.ct_u))
@@ -129,7 +129,7 @@ def compare_flush(st, ref, what, S, mode=0, Q=127, dS=None):
         kt = np64(st.ct_k)
         gram = kt @ np.swapaxes(kt, -1, -2)
         assert np.abs(gram - np.eye(st.rank)).max() < 5e-3, f"{what}: compensator keys not orthonormal"
-    Z = st.codes.cpu().numpy().astype(np.int32)
+    Z = codes_of(st).astype(np.int32)
     dZ = np.abs(Z - ref["Z"].astype(np.int32))
     step_g = s_g[:, :, None] * c_g[:, None, :] / Q
     step_r = s_r[:, :, None] * c_r[:, None, :] / Q

@@ -39,7 +39,7 @@ CHECK_WINDOWS = (0, 1, 64, 128, 255)
 
 def _snap(st, heads):
     """Copies of the sampled heads' stored state, shaped like LeapqBuffers' fields."""
-    return types.SimpleNamespace(rank=st.rank, **{n: getattr(st, n)[heads].clone()
+    return types.SimpleNamespace(rank=st.rank, bits=st.bits, **{n: getattr(st, n)[heads].clone()
                                                   for n in ("codes", "vscale", "ksmooth", "ct_k", "ct_u")})
 
 

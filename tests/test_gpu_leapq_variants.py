@@ -15,7 +15,7 @@ import torch
 import delta_rule_recurrent_amd as m
 from delta_rule_recurrent_amd import synth
 from oracle import gdn, leapq
-from helpers import assert_rel, need_gpu, np64, rel_err, say
+from helpers import assert_rel, need_gpu, np64, rel_err, say, codes_of, pack_codes
 from test_gpu_leapq import compare_flush, rebuild_error, stored
 
 pytestmark = pytest.mark.gpu
@@ -38,8 +38,10 @@ def test_narrow_width_flush_and_window(bits):
     m.leapq_window_flush(st, Q0.to(dev), dense=inp["S0"].to(dev), pre_round=pre)
     torch.cuda.synchronize()
     ref = leapq.flush(np64(inp["S0"]), np64(Q0), rank=6, bits=bits)
-    Z = st.codes.cpu().numpy()
+    Z = codes_of(st)
     assert np.abs(Z).max() == Q
+    # the stored bytes are the documented packing of those codes
+    assert np.array_equal(st.codes.cpu().numpy().view(np.uint8), pack_codes(Z, bits))
     assert np.array_equal(leapq.round_codes(pre.cpu().numpy(), bits), Z)
     flips, _, _ = compare_flush(st, ref, f"{bits}-bit encode", np64(inp["S0"]), Q=Q)
     start = stored(st)
