@@ -578,6 +578,7 @@ def bench_gdn_chunk(K=10, W=2, B=1, H=32, T=16384, kda=False):
     return res
 
 
+GLA_FWD_KERNELS = ("gla_fused_kernel<pass1>", "gla_seg_combine_kernel", "gla_fused_kernel<pass2>")
 GLA_BWD_KERNELS = ("gla_bwd_prep_kernel", "gla_bwd_scan_kernel<fwd>", "gla_bwd_scan_kernel<rev>",
                    "gla_bwd_grad_kernel")
 
@@ -700,8 +701,8 @@ def main():
         torch.cuda.empty_cache()
     if "gla" in rows:
         r = bench_gla()
-        tp, ts = counter_traffic("gla_chunk_prep_kernel"), counter_traffic("gla_chunk_seq_kernel")
-        r["traffic_bytes"] = tp + ts if tp is not None and ts is not None else None
+        parts = [counter_traffic(k) for k in GLA_FWD_KERNELS]
+        r["traffic_bytes"] = sum(parts) if None not in parts else None
         out_rows["gla"] = r
         log(f"[gla] {r['ms']*1e3:.1f} us  {r['tflops']:.1f} TFLOP/s ({r['frac_mfma']*100:.1f}% MFMA)  "
             f"{r['achieved_gbs']:.0f} GB/s ({r['frac_hbm']*100:.1f}% HBM)  {r['tokens_per_s']/1e6:.2f} M tok/s")
@@ -764,6 +765,7 @@ def main():
         if f"leapq{bits}" not in rows:
             continue
         r = bench_leapq(bits=bits, rank=6)
+        r["traffic_bytes_decode_kernel"] = counter_traffic(f"leapq_decode_kernel<{bits}bit>")
         r["speedup_vs_int8"] = out_rows["leapq"]["ms_per_step"] / r["ms_per_step"] if "leapq" in out_rows else None
         out_rows[f"leapq{bits}"] = r
         log(f"[leapq{bits}] {r['ms_per_step']*1e3:.1f} us/step ({r['decode_kernel_ms']*1e3:.1f} us decode, "

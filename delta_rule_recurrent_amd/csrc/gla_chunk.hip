@@ -155,6 +155,7 @@ __global__ __launch_bounds__(512, OUT ? 2 : 4) void gla_fused_kernel(
     float* __restrict__ ST, uint16_t* __restrict__ o, int T, int P, int Lseg, int R) {
   using namespace gla;
   __shared__ Smem sm;
+  __shared__ __attribute__((aligned(16))) uint16_t s_qh[KEEP ? C * PQ : 8];   // KEEP: Q^ [t][qcol(k)]
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave
   // MFMA lane roles (l16, lq) and the elementwise channel pair cp; the chunk loop forms
   // its own from an opaque copy of the thread index
@@ -211,7 +212,6 @@ __global__ __launch_bounds__(512, OUT ? 2 : 4) void gla_fused_kernel(
           bC += te;
         }
         const f32x2 emv = exp2v(bm);
-        unsigned qh[8];   // KEEP: Q^ of the thread's tokens, stored once every prefetched q and k is used
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int r = 8 * w + i;
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(512, OUT ? 2 : 4) void gla_fused_kernel(
             const f32x2 qr = bf2f(in.q[i]) * exp2v(d);
             *reinterpret_cast<unsigned*>(sm.Qr + r * PQ + qcol(2 * cp)) = pk2(qr);
             *reinterpret_cast<unsigned*>(sm.Kr + r * PT + ((2 * cp) ^ swz(r))) = pk2(kf * exp2v(-d));
-            if constexpr (KEEP) qh[i] = pk2(qr * emv);
+            if constexpr (KEEP) *reinterpret_cast<unsigned*>(s_qh + r * PQ + qcol(2 * cp)) = pk2(qr * emv);
           } else {
             *reinterpret_cast<unsigned*>(sm.Kr + r * PT + ((2 * cp) ^ swz(r))) = pk2(kf * exp2v(bC - b));
           }
@@ -230,11 +230,6 @@ __global__ __launch_bounds__(512, OUT ? 2 : 4) void gla_fused_kernel(
         // the next chunk's q and k go out before this chunk's workspace stores; its
         // log-gates and v follow later in the chunk
         if (c + 1 < c1) fetch<OUT, 1>(in, q, k, v, log_g, tok0 + C, t);
-        if constexpr (KEEP) {   // Q^ = Qr o e^{b_m}, row-major, for the shard calls
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            *reinterpret_cast<unsigned*>(wsc + kWQ + ((size_t)(8 * w + i) * kD + 2 * cp) * 2) = qh[i];
-        }
         if (w == 0) {
           const f32x2 ecv = exp2v(bC);
           *reinterpret_cast<f32x2*>(sm.ec + 2 * cp) = ecv;
@@ -248,6 +243,15 @@ __global__ __launch_bounds__(512, OUT ? 2 : 4) void gla_fused_kernel(
         }
       }
       lds_barrier();
+      if constexpr (KEEP) {   // Q^ for the shard calls: fragment f = 4 tb + ks, 1 KB, in the
+                              // order of the inter-chunk product's Qr pieces (16 bytes per lane)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int f = w + 8 * h;
+          *reinterpret_cast<u32x4*>(wsc + kWQ + ((size_t)f * 64 + lane) * 16) =
+              *reinterpret_cast<const u32x4*>(s_qh + (16 * (f >> 2) + l16) * PQ + 32 * (f & 3) + 8 * lq);
+        }
+      }
 
       // ---- wave w: the value operand of its tile (lane (l16, lq) holds v[32 js + 8 lq + e][16 w + l16])
       const bf16x8 vt0 = ld_tr8s(sm.V, 0, 16 * w), vt1 = ld_tr8s(sm.V, 32, 16 * w);

@@ -19,7 +19,7 @@
 // correction are the outputs ZeCO's third phase forms from S_[n-1] + gamma~ o S_recv;
 // the correction reads only Q^ (bf16) and the decays from the workspace and o, not
 // the per-chunk local states.
-#include "common.hpp"
+#include "chunk_device.hpp"
 #include "gla_chunk_layout.hpp"
 
 namespace gdnrt {
@@ -100,7 +100,7 @@ __device__ __forceinline__ void corr_load(CorrIn& in, const uint8_t* __restrict_
   const uint16_t* orow = o + (((size_t)n * nc + c) * kChunk + tb * 16 + l16) * kD + 16 * (vb0 + lq);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
-    in.qf[ks] = *reinterpret_cast<const u32x4*>(wsc + ((size_t)(16 * tb + l16) * kD + 32 * ks + 8 * lq) * 2);
+    in.qf[ks] = *reinterpret_cast<const u32x4*>(wsc + ((size_t)(tb * 4 + ks) * 64 + lane) * 16);
   in.ov[0] = *reinterpret_cast<const u32x4*>(orow);
   in.ov[1] = *reinterpret_cast<const u32x4*>(orow + 8);
 }
@@ -118,8 +118,10 @@ __device__ __forceinline__ int s_off(int v, int k) {
 // sequence n. The block stages S_in[n] in LDS as bf16; wave w forms four transposed
 // output tiles of each chunk, D[v][t] = sum_k S[v][k] (Q^ o gamma~)[t][k], for the
 // tokens of block tb = w & 3 and the 64 value channels from 16 vb0, vb0 = 4 (w >> 2):
-// 16 bytes of a row of Q^ in the workspace are the B operand of that product (lane l16 =
-// token, 8 consecutive keys), scaled by the decay of its keys. Row i = 4 lq + r of tile
+// the workspace's 16-byte pieces of Q^ are the B operand of that product (lane l16 =
+// token, keys 32 ks + 4 lq + e and 32 ks + 16 + 4 lq + e), scaled by the decay of those
+// keys; the state is staged with its keys in the same order (gdc::qcol), so that the
+// A operand is one 16-byte read. Row i = 4 lq + r of tile
 // j stands for value channel 16 vb0 + 16 lq + 4 j + r, so that the 16 D values a lane
 // holds over the four tiles are 16 consecutive channels of one token: o is read and
 // written as 32 contiguous bytes per lane.
@@ -156,7 +158,7 @@ __global__ __launch_bounds__(512) void gla_shard_correct_kernel(const uint8_t* _
     for (int h = 0; h < kD * kD / 4 / NT; ++h) {
       const int i = tid + NT * h, r = i >> 5, c = (i & 31) * 4;
       const f32x4 x = *reinterpret_cast<const f32x4*>(Sn + 4 * (size_t)i);
-      *reinterpret_cast<u32x2*>(Ss + s_off(r, c)) = u32x2{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
+      *reinterpret_cast<u32x2*>(Ss + s_off(r, gdc::qcol(c))) = u32x2{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
     }
   }
   lds_barrier();
@@ -173,8 +175,8 @@ __global__ __launch_bounds__(512) void gla_shard_correct_kernel(const uint8_t* _
     bf16x8 bq[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const f32x4 g0 = *reinterpret_cast<const f32x4*>(gr + 32 * ks + 8 * lq);
-      const f32x4 g1 = *reinterpret_cast<const f32x4*>(gr + 32 * ks + 8 * lq + 4);
+      const f32x4 g0 = *reinterpret_cast<const f32x4*>(gr + 32 * ks + 4 * lq);
+      const f32x4 g1 = *reinterpret_cast<const f32x4*>(gr + 32 * ks + 16 + 4 * lq);
       const u32x4 w = in.qf[ks];
       const u32x4 r = {pack_bf16(lo_bf(w[0]) * g0[0], hi_bf(w[0]) * g0[1]),
                        pack_bf16(lo_bf(w[1]) * g0[2], hi_bf(w[1]) * g0[3]),

@@ -106,8 +106,9 @@ GDNRT_API int kda_decode_step(float* S, const void* q, const void* k, const void
  *          sequence-parallel calls below.
  *   workspace: caller-owned device memory of gla_chunk_fwd_workspace_bytes() bytes,
  *   16-byte aligned, overwritten: 16,896 bytes per chunk that GDNRT_GLA_SHARD fills
- *   (Q o e^b in bf16, row-major, and e^{b_C} in fp32, b the cumulative log-gate within
- *   the chunk), then the call's own segment buffers (the chunks of each sequence are
+ *   (Q o e^b in bf16, in the order the output correction reads it as matrix-core
+ *   operands, and e^{b_C} in fp32; b the cumulative log-gate within the chunk), then
+ *   the call's own segment buffers (the chunks of each sequence are
  *   cut into segments run in parallel: their end states and decays, and start states).
  *   May be NULL when T = 0.
  * T must be a multiple of chunk (64).
