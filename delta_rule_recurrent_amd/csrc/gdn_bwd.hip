@@ -307,8 +307,10 @@ __global__ __launch_bounds__(256) void gdn_bwd_rscan_kernel(const uint8_t* __res
 }
 
 // ------------------------------------------------------------------ gradients, part 1
-// One block of 512 threads (8 waves) per chunk: U, A, dU (to the workspace), dA', dq
-// (final, with q_t . dq_t) and dK1 = dA'^T Q + diag(g_C/g) U dS_a (to the workspace).
+// Persistent blocks of 512 threads (8 waves), one per CU (LDS); block b takes chunks b,
+// b + grid, ... and loads the next chunk's q, k, dO, S_b, dS_a and alpha into registers
+// while it works on this one. Per chunk: U, A, dU (to the workspace), dA', dq (final,
+// with q_t . dq_t) and dK1 = dA'^T Q + diag(g_C/g) U dS_a (to the workspace).
 // Output tiles (rb, cb): wave w takes token block rb = w % 4 and column blocks
 // cb = 4 (w / 4) .. + 3; lane holds rows 16 rb + 4 lq + i of column 16 cb + l16.
 struct alignas(16) G1Smem {
@@ -320,162 +322,205 @@ struct alignas(16) G1Smem {
   float qdq[2][kChunk];   // q_t . dq_t over key blocks 0-3 and 4-7 (the two wave halves)
 };
 
-__global__ __launch_bounds__(512) void gdn_bwd_grad1_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ dO,
-    const float* __restrict__ alpha, gdb::Ws ws, uint16_t* __restrict__ dq, int T) {
-  using namespace gdb;
-  __shared__ G1Smem sm;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, lq = lane >> 4;
-  const int nc = T / C, cid = blockIdx.x;
+namespace gdb {
+// one chunk's inputs of a grad1 thread: 16-byte pieces tid + 512 p of q, k, dO (rows of
+// 128) and of S_b, dS_a; alpha of token lane
+struct G1In {
+  u32x4 q[2], k[2], o[2], s[4], d[4];
+  float al;
+};
+__device__ __forceinline__ void g1_fetch(G1In& in, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                         const uint16_t* __restrict__ dO, const float* __restrict__ alpha,
+                                         const Ws& ws, int cid, int T) {
+  const int tid = threadIdx.x, nc = T / C;
   const size_t tok0 = (size_t)(cid / nc) * T + (size_t)(cid % nc) * C;
-  const uint8_t* pc = ws.prep + (size_t)cid * kWsChunk;
-
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
-    const int e = (tid + 512 * p) * 8, r = e >> 7, cc = e & 127;
-    const size_t gi = (tok0 + r) * kD + cc;
-    *reinterpret_cast<u32x4*>(sm.Q + sw_off(r, cc)) = *reinterpret_cast<const u32x4*>(q + gi);
-    *reinterpret_cast<u32x4*>(sm.K + sw_off(r, cc)) = *reinterpret_cast<const u32x4*>(k + gi);
-    *reinterpret_cast<u32x4*>(sm.O + sw_off(r, cc)) = *reinterpret_cast<const u32x4*>(dO + gi);
+    const size_t gi = tok0 * kD + (size_t)(tid + 512 * p) * 8;
+    in.q[p] = *reinterpret_cast<const u32x4*>(q + gi);
+    in.k[p] = *reinterpret_cast<const u32x4*>(k + gi);
+    in.o[p] = *reinterpret_cast<const u32x4*>(dO + gi);
   }
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    const int e = (tid + 512 * p) * 8, r = e >> 7, cc = e & 127;
-    *reinterpret_cast<u32x4*>(sm.S + sw_off(r, cc)) = *reinterpret_cast<const u32x4*>(ws.Sb + (size_t)cid * kD * kD + e);
-    *reinterpret_cast<u32x4*>(sm.D + sw_off(r, cc)) = *reinterpret_cast<const u32x4*>(ws.dSa + (size_t)cid * kD * kD + e);
+    const size_t e = (size_t)cid * kD * kD + (size_t)(tid + 512 * p) * 8;
+    in.s[p] = *reinterpret_cast<const u32x4*>(ws.Sb + e);
+    in.d[p] = *reinterpret_cast<const u32x4*>(ws.dSa + e);
   }
-  for (int e = tid; e < C * PA / 2; e += 512) reinterpret_cast<uint32_t*>(sm.A)[e] = 0u;
-  if (w == 0) {
-    const float lgv = wave_scan(__logf(alpha[tok0 + lane]));
-    const float lC = __shfl(lgv, C - 1);
-    sm.lg[lane] = lgv;
-    sm.g[lane] = __expf(lgv);
-    sm.kd[lane] = __expf(lC - lgv);
-  }
-  lds_barrier();
+  in.al = alpha[tok0 + (tid & 63)];
+}
+}  // namespace gdb
 
-  const int rb = w & 3;
-  // ---- A = M o (g_r/g_j) o Q K^T (lower tiles) and U = U~ - W S_b^T
-  for (int t = w; t < 10; t += 8) {
-    int ab, cb;
-    tri_pair(t, ab, cb);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+__global__ __launch_bounds__(512) void gdn_bwd_grad1_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ dO,
+    const float* __restrict__ alpha, gdb::Ws ws, uint16_t* __restrict__ dq, int T, int nchunks) {
+  using namespace gdb;
+  __shared__ G1Smem sm;
+  const int nc = T / C;
+  G1In in;
+  g1_fetch(in, q, k, dO, alpha, ws, blockIdx.x, T);   // the grid never exceeds nchunks
+#pragma unroll 1
+  for (int cid = blockIdx.x; cid < nchunks; cid += gridDim.x) {
+    // the thread index through an opaque move: the per-lane addresses are formed inside
+    // each chunk instead of being held across the loop
+    int tid;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"((int)threadIdx.x));
+    const int lane = tid & 63, w = tid >> 6, l16 = lane & 15, lq = lane >> 4, rb = w & 3;
+    const size_t tok0 = (size_t)(cid / nc) * T + (size_t)(cid % nc) * C;
+    const uint8_t* pc = ws.prep + (size_t)cid * kWsChunk;
+
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      acc = mfma(ld8(sm.Q + sw_off(16 * ab + l16, 32 * ks + 8 * lq)), ld8(sm.K + sw_off(16 * cb + l16, 32 * ks + 8 * lq)), acc);
-    const int j = 16 * cb + l16;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * ab + 4 * lq + i;
-      sm.A[r * PA + j] = f32_to_bf16(j <= r ? __expf(sm.lg[r] - sm.lg[j]) * acc[i] : 0.f);
+    for (int p = 0; p < 2; ++p) {
+      const int e = (tid + 512 * p) * 8, r = e >> 7, cc = e & 127;
+      *reinterpret_cast<u32x4*>(sm.Q + sw_off(r, cc)) = in.q[p];
+      *reinterpret_cast<u32x4*>(sm.K + sw_off(r, cc)) = in.k[p];
+      *reinterpret_cast<u32x4*>(sm.O + sw_off(r, cc)) = in.o[p];
     }
-  }
-  {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int e = (tid + 512 * p) * 8, r = e >> 7, cc = e & 127;
+      *reinterpret_cast<u32x4*>(sm.S + sw_off(r, cc)) = in.s[p];
+      *reinterpret_cast<u32x4*>(sm.D + sw_off(r, cc)) = in.d[p];
+    }
+    for (int e = tid; e < C * PA / 2; e += 512) reinterpret_cast<uint32_t*>(sm.A)[e] = 0u;
+    if (w == 0) {
+      const float lgv = wave_scan(__logf(in.al));
+      const float lC = __shfl(lgv, C - 1);
+      sm.lg[lane] = lgv;
+      sm.g[lane] = __expf(lgv);
+      sm.kd[lane] = __expf(lC - lgv);
+    }
+    // this chunk's W and U~ fragments, then the next chunk's inputs (the last chunk of a
+    // block loads itself again), so that waiting for the fragments leaves those in flight
     u32x4 wf[4];
+    u32x2 ut[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
       wf[ks] = *reinterpret_cast<const u32x4*>(pc + kWsW + ((size_t)(rb * 4 + ks) * 64 + lane) * 16);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int vb = (w >> 2) * 4 + u;
-      const u32x2 ut = *reinterpret_cast<const u32x2*>(pc + kWsU + ((size_t)(rb * 8 + vb) * 64 + lane) * 8);
-      f32x4 p = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) p = mfma(as_bf(wf[ks]), ld8_split_s(sm.S, 16 * vb + l16, 32 * ks + 4 * lq), p);
-      const float uu[4] = {lo_bf(ut.x) - p[0], hi_bf(ut.x) - p[1], lo_bf(ut.y) - p[2], hi_bf(ut.y) - p[3]};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sm.U[sw_off(16 * rb + 4 * lq + i, 16 * vb + l16)] = f32_to_bf16(uu[i]);
-    }
-  }
-  lds_barrier();
+    for (int u = 0; u < 4; ++u)
+      ut[u] = *reinterpret_cast<const u32x2*>(pc + kWsU + ((size_t)(rb * 8 + (w >> 2) * 4 + u) * 64 + lane) * 8);
+    g1_fetch(in, q, k, dO, alpha, ws, cid + (int)gridDim.x < nchunks ? cid + (int)gridDim.x : cid, T);
+    lds_barrier();
 
-  // ---- dU = A^T dO + diag(g_C/g) K dS_a^T (to the workspace); dO U^T on the lower tiles
-  uint16_t* dUw = ws.dU + (size_t)cid * C * kD;
-#pragma unroll 1
-  for (int u = 0; u < 4; ++u) {
-    const int vb = (w >> 2) * 4 + u;
-    f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = a1;
-#pragma unroll
-    for (int js = 0; js < 2; ++js)
-      if (32 * js + 31 >= 16 * rb)   // A[j][r] is zero for j < r
-        a1 = mfma(ld_tr8(sm.A, PA, 32 * js, 16 * rb), ld_tr8s(sm.O, 32 * js, 16 * vb), a1);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      a2 = mfma(ld8(sm.K + sw_off(16 * rb + l16, 32 * ks + 8 * lq)), ld8(sm.D + sw_off(16 * vb + l16, 32 * ks + 8 * lq)), a2);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * rb + 4 * lq + i;
-      dUw[r * kD + 16 * vb + l16] = f32_to_bf16(a1[i] + sm.kd[r] * a2[i]);
-    }
-  }
-  f32x4 da[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    da[h] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (w + 8 * h < 10) {
+    // ---- A = M o (g_r/g_j) o Q K^T (lower tiles) and U = U~ - W S_b^T
+    for (int t = w; t < 10; t += 8) {
       int ab, cb;
-      tri_pair(w + 8 * h, ab, cb);
+      tri_pair(t, ab, cb);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        da[h] = mfma(ld8(sm.O + sw_off(16 * ab + l16, 32 * ks + 8 * lq)), ld8(sm.U + sw_off(16 * cb + l16, 32 * ks + 8 * lq)), da[h]);
-    }
-  }
-  lds_barrier();
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-    if (w + 8 * h < 10) {
-      int ab, cb;
-      tri_pair(w + 8 * h, ab, cb);
+        acc = mfma(ld8(sm.Q + sw_off(16 * ab + l16, 32 * ks + 8 * lq)), ld8(sm.K + sw_off(16 * cb + l16, 32 * ks + 8 * lq)), acc);
       const int j = 16 * cb + l16;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * ab + 4 * lq + i;
-        sm.A[r * PA + j] = f32_to_bf16(j <= r ? __expf(sm.lg[r] - sm.lg[j]) * da[h][i] : 0.f);
+        sm.A[r * PA + j] = f32_to_bf16(j <= r ? __expf(sm.lg[r] - sm.lg[j]) * acc[i] : 0.f);
       }
     }
-  lds_barrier();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int vb = (w >> 2) * 4 + u;
+      f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) p = mfma(as_bf(wf[ks]), ld8_split_s(sm.S, 16 * vb + l16, 32 * ks + 4 * lq), p);
+      const float uu[4] = {lo_bf(ut[u].x) - p[0], hi_bf(ut[u].x) - p[1], lo_bf(ut[u].y) - p[2], hi_bf(ut[u].y) - p[3]};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm.U[sw_off(16 * rb + 4 * lq + i, 16 * vb + l16)] = f32_to_bf16(uu[i]);
+    }
+    lds_barrier();
 
-  // ---- dq = dA' K + diag(g) dO S_b;  dK1 = dA'^T Q + diag(g_C/g) U dS_a
-  float* dK1 = ws.dK1 + (size_t)cid * C * kD;
-  float qacc[4] = {0.f, 0.f, 0.f, 0.f};   // this wave's share of q.dq, in key-block order
+    // ---- dU = A^T dO + diag(g_C/g) K dS_a^T (to the workspace); dO U^T on the lower tiles
+    uint16_t* dUw = ws.dU + (size_t)cid * C * kD;
 #pragma unroll 1
-  for (int u = 0; u < 4; ++u) {
-    const int kb = (w >> 2) * 4 + u;
-    f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = a1, a3 = a1, a4 = a1;
+    for (int u = 0; u < 4; ++u) {
+      const int vb = (w >> 2) * 4 + u;
+      f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = a1;
 #pragma unroll
-    for (int js = 0; js < 2; ++js) {
-      if (js <= rb / 2)   // dA'[r][j] is zero for j > r
-        a1 = mfma(ld8(sm.A + (16 * rb + l16) * PA + 32 * js + 8 * lq), ld_tr8s(sm.K, 32 * js, 16 * kb), a1);
-      if (32 * js + 31 >= 16 * rb)   // dA'[i][r] is zero for i < r
-        a3 = mfma(ld_tr8(sm.A, PA, 32 * js, 16 * rb), ld_tr8s(sm.Q, 32 * js, 16 * kb), a3);
-    }
+      for (int js = 0; js < 2; ++js)
+        if (32 * js + 31 >= 16 * rb)   // A[j][r] is zero for j < r
+          a1 = mfma(ld_tr8(sm.A, PA, 32 * js, 16 * rb), ld_tr8s(sm.O, 32 * js, 16 * vb), a1);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      a2 = mfma(ld8(sm.O + sw_off(16 * rb + l16, 32 * ks + 8 * lq)), ld_tr8s(sm.S, 32 * ks, 16 * kb), a2);
-      a4 = mfma(ld8(sm.U + sw_off(16 * rb + l16, 32 * ks + 8 * lq)), ld_tr8s(sm.D, 32 * ks, 16 * kb), a4);
-    }
-    const int col = 16 * kb + l16;
+      for (int ks = 0; ks < 4; ++ks)
+        a2 = mfma(ld8(sm.K + sw_off(16 * rb + l16, 32 * ks + 8 * lq)), ld8(sm.D + sw_off(16 * vb + l16, 32 * ks + 8 * lq)), a2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * rb + 4 * lq + i;
-      const float gq = a1[i] + sm.g[r] * a2[i];
-      dq[(tok0 + r) * kD + col] = f32_to_bf16(gq);
-      dK1[r * kD + col] = a3[i] + sm.kd[r] * a4[i];
-      qacc[i] += sum16(bf16_to_f32(sm.Q[sw_off(r, col)]) * gq);
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rb + 4 * lq + i;
+        dUw[r * kD + 16 * vb + l16] = f32_to_bf16(a1[i] + sm.kd[r] * a2[i]);
+      }
     }
+    f32x4 da[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      da[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (w + 8 * h < 10) {
+        int ab, cb;
+        tri_pair(w + 8 * h, ab, cb);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          da[h] = mfma(ld8(sm.O + sw_off(16 * ab + l16, 32 * ks + 8 * lq)), ld8(sm.U + sw_off(16 * cb + l16, 32 * ks + 8 * lq)), da[h]);
+      }
+    }
+    lds_barrier();
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      if (w + 8 * h < 10) {
+        int ab, cb;
+        tri_pair(w + 8 * h, ab, cb);
+        const int j = 16 * cb + l16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * ab + 4 * lq + i;
+          sm.A[r * PA + j] = f32_to_bf16(j <= r ? __expf(sm.lg[r] - sm.lg[j]) * da[h][i] : 0.f);
+        }
+      }
+    lds_barrier();
+
+    // ---- dq = dA' K + diag(g) dO S_b;  dK1 = dA'^T Q + diag(g_C/g) U dS_a
+    float* dK1 = ws.dK1 + (size_t)cid * C * kD;
+    float qacc[4] = {0.f, 0.f, 0.f, 0.f};   // this wave's share of q.dq, in key-block order
+#pragma unroll 1
+    for (int u = 0; u < 4; ++u) {
+      const int kb = (w >> 2) * 4 + u;
+      f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = a1, a3 = a1, a4 = a1;
+#pragma unroll
+      for (int js = 0; js < 2; ++js) {
+        if (js <= rb / 2)   // dA'[r][j] is zero for j > r
+          a1 = mfma(ld8(sm.A + (16 * rb + l16) * PA + 32 * js + 8 * lq), ld_tr8s(sm.K, 32 * js, 16 * kb), a1);
+        if (32 * js + 31 >= 16 * rb)   // dA'[i][r] is zero for i < r
+          a3 = mfma(ld_tr8(sm.A, PA, 32 * js, 16 * rb), ld_tr8s(sm.Q, 32 * js, 16 * kb), a3);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        a2 = mfma(ld8(sm.O + sw_off(16 * rb + l16, 32 * ks + 8 * lq)), ld_tr8s(sm.S, 32 * ks, 16 * kb), a2);
+        a4 = mfma(ld8(sm.U + sw_off(16 * rb + l16, 32 * ks + 8 * lq)), ld_tr8s(sm.D, 32 * ks, 16 * kb), a4);
+      }
+      const int col = 16 * kb + l16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rb + 4 * lq + i;
+        const float gq = a1[i] + sm.g[r] * a2[i];
+        dq[(tok0 + r) * kD + col] = f32_to_bf16(gq);
+        dK1[r * kD + col] = a3[i] + sm.kd[r] * a4[i];
+        qacc[i] += sum16(bf16_to_f32(sm.Q[sw_off(r, col)]) * gq);
+      }
+    }
+    // fixed summation order (no atomics): each half of the waves writes its own partial
+    if (l16 == 0)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm.qdq[w >> 2][16 * rb + 4 * lq + i] = qacc[i];
+    lds_barrier();
+    if (tid < C) ws.qdq[(size_t)cid * C + tid] = sm.qdq[0][tid] + sm.qdq[1][tid];
   }
-  // fixed summation order (no atomics): each half of the waves writes its own partial
-  if (l16 == 0)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sm.qdq[w >> 2][16 * rb + 4 * lq + i] = qacc[i];
-  lds_barrier();
-  if (tid < C) ws.qdq[(size_t)cid * C + tid] = sm.qdq[0][tid] + sm.qdq[1][tid];
 }
 
 // ------------------------------------------------------------------ gradients, part 2
-// One block of 512 threads per chunk: dW = -dU S_b, the WY gradients T^T dW and
-// T^T dU, dv, dL, dk (with dK1), dbeta, and dalpha from dL/dB_t = q_t.dq_t - v_t.dv_t
-// summed in reverse inside the chunk plus the chunk's sum(dS_a o S_a).
+// Persistent blocks of 512 threads, one per CU (LDS), chunks strided by the grid. Per
+// chunk: dW = -dU S_b, the WY gradients T^T dW and T^T dU, dv, dL, dk (with dK1), dbeta,
+// and dalpha from dL/dB_t = q_t.dq_t - v_t.dv_t summed in reverse inside the chunk plus
+// the chunk's sum(dS_a o S_a). The next chunk's k, v, dU, S_b, U~, T, alpha and beta are
+// loaded into registers from the dL step on, after this chunk's own W fragments and dK1,
+// so that no wait inside the chunk also waits for them.
 struct alignas(16) G2Smem {
   uint16_t K[kChunk * gdb::PT], V[kChunk * gdb::PT], dU[kChunk * gdb::PT], dW[kChunk * gdb::PT];
   uint16_t Ut[kChunk * gdb::PT];   // U~ [t][v]
@@ -488,160 +533,216 @@ struct alignas(16) G2Smem {
   float dbW[2][kChunk], dbU[2][kChunk], dbL[4][kChunk];
 };
 
-__global__ __launch_bounds__(512) void gdn_bwd_grad2_kernel(
-    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ alpha,
-    const float* __restrict__ beta, gdb::Ws ws, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
-    float* __restrict__ dbeta, float* __restrict__ dalpha, int T) {
-  using namespace gdb;
-  __shared__ G2Smem sm;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, lq = lane >> 4;
-  const int nc = T / C, cid = blockIdx.x, n = cid / nc;
-  const size_t tok0 = (size_t)n * T + (size_t)(cid % nc) * C;
+namespace gdb {
+// one chunk's inputs of a grad2 thread: 16-byte pieces tid + 512 p of k, v, dU and of
+// S_b; the U~ fragments f = wave + 8 p (lane's 8 bytes); 16 bytes of T; alpha, beta of
+// token lane
+struct G2In {
+  u32x4 k[2], v[2], du[2], s[4], t;
+  u32x2 ut[4];
+  float al, be;
+};
+__device__ __forceinline__ void g2_fetch(G2In& in, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                         const float* __restrict__ alpha, const float* __restrict__ beta,
+                                         const Ws& ws, int cid, int T) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nc = T / C;
+  const size_t tok0 = (size_t)(cid / nc) * T + (size_t)(cid % nc) * C;
   const uint8_t* pc = ws.prep + (size_t)cid * kWsChunk;
-  uint16_t* XW = sm.S;             // T^T dW, after dW is formed
-  uint16_t* XU = sm.S + C * PT;    // T^T dU
-
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
-    const int e = (tid + 512 * p) * 8, r = e >> 7, cc = e & 127;
-    const size_t gi = (tok0 + r) * kD + cc;
-    *reinterpret_cast<u32x4*>(sm.K + sw_off(r, cc)) = *reinterpret_cast<const u32x4*>(k + gi);
-    *reinterpret_cast<u32x4*>(sm.V + sw_off(r, cc)) = *reinterpret_cast<const u32x4*>(v + gi);
-    *reinterpret_cast<u32x4*>(sm.dU + sw_off(r, cc)) = *reinterpret_cast<const u32x4*>(ws.dU + (size_t)cid * C * kD + e);
+    const size_t gi = tok0 * kD + (size_t)(tid + 512 * p) * 8;
+    in.k[p] = *reinterpret_cast<const u32x4*>(k + gi);
+    in.v[p] = *reinterpret_cast<const u32x4*>(v + gi);
+    in.du[p] = *reinterpret_cast<const u32x4*>(ws.dU + (size_t)cid * C * kD + (size_t)(tid + 512 * p) * 8);
   }
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    const int e = (tid + 512 * p) * 8, r = e >> 7, cc = e & 127;
-    *reinterpret_cast<u32x4*>(sm.S + sw_off(r, cc)) = *reinterpret_cast<const u32x4*>(ws.Sb + (size_t)cid * kD * kD + e);
-    // U~ tile f = w + 8 p (rb, vb) = (f / 8, f % 8): tokens rb*16 + lq*4 + i of value vb*16 + l16
-    const int f = w + 8 * p, ub = f >> 3, vb = f & 7;
-    const u32x2 ut = *reinterpret_cast<const u32x2*>(pc + kWsU + ((size_t)f * 64 + lane) * 8);
-    const float uv[4] = {lo_bf(ut.x), hi_bf(ut.x), lo_bf(ut.y), hi_bf(ut.y)};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sm.Ut[sw_off(16 * ub + 4 * lq + i, 16 * vb + l16)] = f32_to_bf16(uv[i]);
+    in.s[p] = *reinterpret_cast<const u32x4*>(ws.Sb + (size_t)cid * kD * kD + (size_t)(tid + 512 * p) * 8);
+    in.ut[p] = *reinterpret_cast<const u32x2*>(pc + kWsU + ((size_t)(w + 8 * p) * 64 + lane) * 8);
   }
-  {
-    const int e = tid * 8, r = e >> 6, cc = e & 63;
-    *reinterpret_cast<u32x4*>(sm.T + r * PA + cc) = *reinterpret_cast<const u32x4*>(ws.T + (size_t)cid * C * C + e);
-  }
-  for (int e = tid; e < C * PA / 2; e += 512) reinterpret_cast<uint32_t*>(sm.L)[e] = 0u;
-  if (w == 0) {
-    const float lgv = wave_scan(__logf(alpha[tok0 + lane]));
-    sm.lg[lane] = lgv;
-    sm.g[lane] = __expf(lgv);
-    sm.bt[lane] = beta[tok0 + lane];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) sm.dbL[c][lane] = 0.f;
-  }
-  lds_barrier();
+  in.t = *reinterpret_cast<const u32x4*>(ws.T + (size_t)cid * C * C + tid * 8);
+  in.al = alpha[tok0 + lane];
+  in.be = beta[tok0 + lane];
+}
+}  // namespace gdb
 
-  const int rb = w & 3;
-  // ---- dW = -dU S_b
+__global__ __launch_bounds__(512) void gdn_bwd_grad2_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ alpha,
+    const float* __restrict__ beta, gdb::Ws ws, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
+    float* __restrict__ dbeta, float* __restrict__ dalpha, int T, int nchunks) {
+  using namespace gdb;
+  __shared__ G2Smem sm;
+  const int nc = T / C;
+  uint16_t* XW = sm.S;             // T^T dW, after dW is formed
+  uint16_t* XU = sm.S + C * PT;    // T^T dU
+  G2In in;
+  g2_fetch(in, k, v, alpha, beta, ws, blockIdx.x, T);   // the grid never exceeds nchunks
 #pragma unroll 1
-  for (int u = 0; u < 4; ++u) {
-    const int kb = (w >> 2) * 4 + u;
-    f32x4 a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      a = mfma(ld8(sm.dU + sw_off(16 * rb + l16, 32 * ks + 8 * lq)), ld_tr8s(sm.S, 32 * ks, 16 * kb), a);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sm.dW[sw_off(16 * rb + 4 * lq + i, 16 * kb + l16)] = f32_to_bf16(-a[i]);
-  }
-  lds_barrier();
+  for (int cid = blockIdx.x; cid < nchunks; cid += gridDim.x) {
+    // the thread index through an opaque move (per-lane addresses formed per chunk)
+    int tid;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"((int)threadIdx.x));
+    const int lane = tid & 63, w = tid >> 6, l16 = lane & 15, lq = lane >> 4, rb = w & 3;
+    const size_t tok0 = (size_t)(cid / nc) * T + (size_t)(cid % nc) * C;
+    const uint8_t* pc = ws.prep + (size_t)cid * kWsChunk;
 
-  // ---- T^T dW and T^T dU; dv = beta o T^T dU; dK_W = beta g o T^T dW (kept)
-  f32x4 kw[4];
-  float su_acc[4] = {0.f, 0.f, 0.f, 0.f}, sw_acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int cb = (w >> 2) * 4 + u;
-    f32x4 xw = {0.f, 0.f, 0.f, 0.f}, xu = xw;
+    for (int p = 0; p < 2; ++p) {
+      const int e = (tid + 512 * p) * 8, r = e >> 7, cc = e & 127;
+      *reinterpret_cast<u32x4*>(sm.K + sw_off(r, cc)) = in.k[p];
+      *reinterpret_cast<u32x4*>(sm.V + sw_off(r, cc)) = in.v[p];
+      *reinterpret_cast<u32x4*>(sm.dU + sw_off(r, cc)) = in.du[p];
+    }
 #pragma unroll
-    for (int js = 0; js < 2; ++js)
-      if (32 * js + 31 >= 16 * rb) {   // T[j][r] is zero for j < r
-        const bf16x8 tt = ld_tr8(sm.T, PA, 32 * js, 16 * rb);
-        xw = mfma(tt, ld_tr8s(sm.dW, 32 * js, 16 * cb), xw);
-        xu = mfma(tt, ld_tr8s(sm.dU, 32 * js, 16 * cb), xu);
+    for (int p = 0; p < 4; ++p) {
+      const int e = (tid + 512 * p) * 8, r = e >> 7, cc = e & 127;
+      *reinterpret_cast<u32x4*>(sm.S + sw_off(r, cc)) = in.s[p];
+      // U~ tile f = w + 8 p (rb, vb) = (f / 8, f % 8): tokens rb*16 + lq*4 + i of value vb*16 + l16
+      const int f = w + 8 * p, ub = f >> 3, vb = f & 7;
+      const float uv[4] = {lo_bf(in.ut[p].x), hi_bf(in.ut[p].x), lo_bf(in.ut[p].y), hi_bf(in.ut[p].y)};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm.Ut[sw_off(16 * ub + 4 * lq + i, 16 * vb + l16)] = f32_to_bf16(uv[i]);
+    }
+    {
+      const int e = tid * 8, r = e >> 6, cc = e & 63;
+      *reinterpret_cast<u32x4*>(sm.T + r * PA + cc) = in.t;
+    }
+    for (int e = tid; e < C * PA / 2; e += 512) reinterpret_cast<uint32_t*>(sm.L)[e] = 0u;
+    if (w == 0) {
+      const float lgv = wave_scan(__logf(in.al));
+      sm.lg[lane] = lgv;
+      sm.g[lane] = __expf(lgv);
+      sm.bt[lane] = in.be;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) sm.dbL[c][lane] = 0.f;
+    }
+    lds_barrier();
+
+    // ---- dW = -dU S_b
+#pragma unroll 1
+    for (int u = 0; u < 4; ++u) {
+      const int kb = (w >> 2) * 4 + u;
+      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        a = mfma(ld8(sm.dU + sw_off(16 * rb + l16, 32 * ks + 8 * lq)), ld_tr8s(sm.S, 32 * ks, 16 * kb), a);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm.dW[sw_off(16 * rb + 4 * lq + i, 16 * kb + l16)] = f32_to_bf16(-a[i]);
+    }
+    lds_barrier();
+
+    // ---- T^T dW and T^T dU; dv = beta o T^T dU; dK_W = beta g o T^T dW (kept)
+    f32x4 kw[4];
+    float su_acc[4] = {0.f, 0.f, 0.f, 0.f}, sw_acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int cb = (w >> 2) * 4 + u;
+      f32x4 xw = {0.f, 0.f, 0.f, 0.f}, xu = xw;
+#pragma unroll
+      for (int js = 0; js < 2; ++js)
+        if (32 * js + 31 >= 16 * rb) {   // T[j][r] is zero for j < r
+          const bf16x8 tt = ld_tr8(sm.T, PA, 32 * js, 16 * rb);
+          xw = mfma(tt, ld_tr8s(sm.dW, 32 * js, 16 * cb), xw);
+          xu = mfma(tt, ld_tr8s(sm.dU, 32 * js, 16 * cb), xu);
+        }
+      const int col = 16 * cb + l16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rb + 4 * lq + i;
+        XW[sw_off(r, col)] = f32_to_bf16(xw[i]);
+        XU[sw_off(r, col)] = f32_to_bf16(xu[i]);
+        dv[(tok0 + r) * kD + col] = f32_to_bf16(sm.bt[r] * xu[i]);
+        kw[u][i] = sm.bt[r] * sm.g[r] * xw[i];
+        su_acc[i] += sum16(xu[i] * bf16_to_f32(sm.V[sw_off(r, col)]));
+        sw_acc[i] += sum16(xw[i] * bf16_to_f32(sm.K[sw_off(r, col)]));
       }
-    const int col = 16 * cb + l16;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * rb + 4 * lq + i;
-      XW[sw_off(r, col)] = f32_to_bf16(xw[i]);
-      XU[sw_off(r, col)] = f32_to_bf16(xu[i]);
-      dv[(tok0 + r) * kD + col] = f32_to_bf16(sm.bt[r] * xu[i]);
-      kw[u][i] = sm.bt[r] * sm.g[r] * xw[i];
-      su_acc[i] += sum16(xu[i] * bf16_to_f32(sm.V[sw_off(r, col)]));
-      sw_acc[i] += sum16(xw[i] * bf16_to_f32(sm.K[sw_off(r, col)]));
     }
-  }
-  if (l16 == 0)
+    if (l16 == 0)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sm.dbU[w >> 2][16 * rb + 4 * lq + i] = su_acc[i];
-      sm.dbW[w >> 2][16 * rb + 4 * lq + i] = sw_acc[i];
-    }
-  lds_barrier();
-
-  // ---- dL = -(T^T dW W^T + T^T dU U~^T) on the strict lower part; with the Gram
-  // matrix K K^T for dbeta; dL o (g_r/g_j) o beta_r and its transpose to LDS
-  for (int t = w; t < 10; t += 8) {
-    int ab, cb;
-    tri_pair(t, ab, cb);
-    f32x4 a = {0.f, 0.f, 0.f, 0.f}, gk = a;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const u32x4 wfr = *reinterpret_cast<const u32x4*>(pc + kWsW + ((size_t)(cb * 4 + ks) * 64 + lane) * 16);
-      a = mfma(ld8_split_s(XW, 16 * ab + l16, 32 * ks + 4 * lq), as_bf(wfr), a);
-      a = mfma(ld8(XU + sw_off(16 * ab + l16, 32 * ks + 8 * lq)), ld8(sm.Ut + sw_off(16 * cb + l16, 32 * ks + 8 * lq)), a);
-      gk = mfma(ld8(sm.K + sw_off(16 * ab + l16, 32 * ks + 8 * lq)), ld8(sm.K + sw_off(16 * cb + l16, 32 * ks + 8 * lq)), gk);
-    }
-    const int j = 16 * cb + l16;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * ab + 4 * lq + i;
-      float x = 0.f, y = 0.f;
-      if (j < r) {
-        const float dl = -a[i] * __expf(sm.lg[r] - sm.lg[j]);
-        x = dl * sm.bt[r];
-        y = dl * gk[i];
-        const uint16_t xb = f32_to_bf16(x);
-        sm.L[r * PA + j] = xb;
-        sm.L[j * PA + r] = xb;
+      for (int i = 0; i < 4; ++i) {
+        sm.dbU[w >> 2][16 * rb + 4 * lq + i] = su_acc[i];
+        sm.dbW[w >> 2][16 * rb + 4 * lq + i] = sw_acc[i];
       }
-      const float sy = sum16(y);
-      if (l16 == 0) sm.dbL[cb][r] = sy;   // one pair (ab, cb) per row block and column block
+    // this chunk's W fragments (the wave's one or two lower tiles of dL) and dK1, then the
+    // next chunk's inputs (the last chunk of a block loads itself again)
+    u32x4 wfr[2][4];
+    float k1[4][4];
+    const float* dK1 = ws.dK1 + (size_t)cid * C * kD;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      int ab, cb;
+      tri_pair(w + 8 * h < 10 ? w + 8 * h : w, ab, cb);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        wfr[h][ks] = *reinterpret_cast<const u32x4*>(pc + kWsW + ((size_t)(cb * 4 + ks) * 64 + lane) * 16);
     }
-  }
-  lds_barrier();
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) k1[u][i] = dK1[(16 * rb + 4 * lq + i) * kD + 16 * ((w >> 2) * 4 + u) + l16];
+    g2_fetch(in, k, v, alpha, beta, ws, cid + (int)gridDim.x < nchunks ? cid + (int)gridDim.x : cid, T);
+    lds_barrier();
 
-  // ---- dk = dK1 + dK_W + (dL' + dL'^T) K
-  const float* dK1 = ws.dK1 + (size_t)cid * C * kD;
+    // ---- dL = -(T^T dW W^T + T^T dU U~^T) on the strict lower part; with the Gram
+    // matrix K K^T for dbeta; dL o (g_r/g_j) o beta_r and its transpose to LDS
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int kb = (w >> 2) * 4 + u;
-    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < 2; ++h) {
+      if (w + 8 * h >= 10) continue;
+      int ab, cb;
+      tri_pair(w + 8 * h, ab, cb);
+      f32x4 a = {0.f, 0.f, 0.f, 0.f}, gk = a;
 #pragma unroll
-    for (int js = 0; js < 2; ++js)
-      a = mfma(ld8(sm.L + (16 * rb + l16) * PA + 32 * js + 8 * lq), ld_tr8s(sm.K, 32 * js, 16 * kb), a);
-    const int col = 16 * kb + l16;
+      for (int ks = 0; ks < 4; ++ks) {
+        a = mfma(ld8_split_s(XW, 16 * ab + l16, 32 * ks + 4 * lq), as_bf(wfr[h][ks]), a);
+        a = mfma(ld8(XU + sw_off(16 * ab + l16, 32 * ks + 8 * lq)), ld8(sm.Ut + sw_off(16 * cb + l16, 32 * ks + 8 * lq)), a);
+        gk = mfma(ld8(sm.K + sw_off(16 * ab + l16, 32 * ks + 8 * lq)), ld8(sm.K + sw_off(16 * cb + l16, 32 * ks + 8 * lq)), gk);
+      }
+      const int j = 16 * cb + l16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * rb + 4 * lq + i;
-      dk[(tok0 + r) * kD + col] = f32_to_bf16(dK1[r * kD + col] + kw[u][i] + a[i]);
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * ab + 4 * lq + i;
+        float x = 0.f, y = 0.f;
+        if (j < r) {
+          const float dl = -a[i] * __expf(sm.lg[r] - sm.lg[j]);
+          x = dl * sm.bt[r];
+          y = dl * gk[i];
+          const uint16_t xb = f32_to_bf16(x);
+          sm.L[r * PA + j] = xb;
+          sm.L[j * PA + r] = xb;
+        }
+        const float sy = sum16(y);
+        if (l16 == 0) sm.dbL[cb][r] = sy;   // one pair (ab, cb) per row block and column block
+      }
     }
-  }
-  lds_barrier();
-  if (w == 0) {
-    const int t = lane;
-    const float dbU = sm.dbU[0][t] + sm.dbU[1][t], dbW = sm.dbW[0][t] + sm.dbW[1][t];
-    const float dbL = (sm.dbL[0][t] + sm.dbL[1][t]) + (sm.dbL[2][t] + sm.dbL[3][t]);
-    dbeta[tok0 + t] = sm.g[t] * dbW + dbU + dbL;
-    const float dB = ws.qdq[(size_t)cid * C + t] - sm.bt[t] * dbU;
-    const float off = sum64(t < 32 ? ws.bnd[(size_t)cid * 32 + t] : 0.f);
-    // reverse inclusive sum inside the chunk: lane l scans token 63 - l
-    const float rs = wave_scan(__shfl(dB, C - 1 - lane));
-    dalpha[tok0 + t] = (__shfl(rs, C - 1 - t) + off) / alpha[tok0 + t];
+    lds_barrier();
+
+    // ---- dk = dK1 + dK_W + (dL' + dL'^T) K
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int kb = (w >> 2) * 4 + u;
+      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int js = 0; js < 2; ++js)
+        a = mfma(ld8(sm.L + (16 * rb + l16) * PA + 32 * js + 8 * lq), ld_tr8s(sm.K, 32 * js, 16 * kb), a);
+      const int col = 16 * kb + l16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rb + 4 * lq + i;
+        dk[(tok0 + r) * kD + col] = f32_to_bf16(k1[u][i] + kw[u][i] + a[i]);
+      }
+    }
+    lds_barrier();
+    if (w == 0) {
+      const int t = lane;
+      const float dbU = sm.dbU[0][t] + sm.dbU[1][t], dbW = sm.dbW[0][t] + sm.dbW[1][t];
+      const float dbL = (sm.dbL[0][t] + sm.dbL[1][t]) + (sm.dbL[2][t] + sm.dbL[3][t]);
+      dbeta[tok0 + t] = sm.g[t] * dbW + dbU + dbL;
+      const float dB = ws.qdq[(size_t)cid * C + t] - sm.bt[t] * dbU;
+      const float off = sum64(t < 32 ? ws.bnd[(size_t)cid * 32 + t] : 0.f);
+      // reverse inclusive sum inside the chunk: lane l scans token 63 - l
+      const float rs = wave_scan(__shfl(dB, C - 1 - lane));
+      dalpha[tok0 + t] = (__shfl(rs, C - 1 - t) + off) / alpha[tok0 + t];
+    }
   }
 }
 
@@ -744,9 +845,11 @@ extern "C" int gdn_chunk_bwd(const void* q, const void* k, const void* v, const 
   hipLaunchKernelGGL(gdn_bwd_fscan_kernel, dim3((unsigned)(N * 8)), dim3(256), 0, s, ws.prep, S0, ws.Sb, ws.ST, T);
   hipLaunchKernelGGL(gdn_bwd_rscan_kernel, dim3((unsigned)(N * 8)), dim3(256), 0, s, ws.prep, o16, dST, ws.Sb,
                      ws.ST, ws.dSa, ws.bnd, dS0, T);
-  hipLaunchKernelGGL(gdn_bwd_grad1_kernel, dim3((unsigned)nchunks), dim3(512), 0, s, q16, k16, o16, alpha, ws,
-                     static_cast<uint16_t*>(dq), T);
-  hipLaunchKernelGGL(gdn_bwd_grad2_kernel, dim3((unsigned)nchunks), dim3(512), 0, s, k16, v16, alpha, beta, ws,
-                     static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), dbeta, dalpha, T);
+  // persistent gradient blocks, one per CU (their LDS fills one)
+  const unsigned ggrid = (unsigned)(nchunks < 256 ? nchunks : 256);
+  hipLaunchKernelGGL(gdn_bwd_grad1_kernel, dim3(ggrid), dim3(512), 0, s, q16, k16, o16, alpha, ws,
+                     static_cast<uint16_t*>(dq), T, (int)nchunks);
+  hipLaunchKernelGGL(gdn_bwd_grad2_kernel, dim3(ggrid), dim3(512), 0, s, k16, v16, alpha, beta, ws,
+                     static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), dbeta, dalpha, T, (int)nchunks);
   return check_launch(fn);
 }
