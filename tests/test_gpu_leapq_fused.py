@@ -90,6 +90,51 @@ def test_last_token_and_flush(kda_mode, io):
     assert torch.isfinite(o.float()).all()
 
 
+@pytest.mark.parametrize("bits", [6, 4])
+def test_packed_widths_last_token_and_flush(bits):
+    """The fused launch on packed 6- and 4-bit codes (rank 6, as the bench's rows): the
+    last token against one exact step from the oracle's rebuild of the GPU's stored
+    state, the fused flush against the oracle's flush at Q = 2^(b-1) - 1 within the
+    bounds of ``compare_flush``, and against the two-launch path within half a code step
+    of each side."""
+    dev = need_gpu()
+    say(f"leapq decode+flush at {bits} bits, rank 6")
+    Q = (1 << (bits - 1)) - 1
+    B, H, W = 4, 8, 16
+    N = B * H
+    inp = synth.leapq_decode(B=B, H=H, steps=W, device="cpu")
+    Q0 = synth.compensator_start(r=6).to(dev)
+    st = m.LeapqBuffers(N, rank=6, window=W, bits=bits)
+    m.leapq_window_flush(st, Q0, dense=inp["S0"].to(dev))
+    start = stored(st)
+    start["Q"] = Q
+    for t in range(W - 1):
+        m.leapq_decode_step(st, *(inp[n][t].to(dev) for n in ("q", "k", "v", "alpha", "beta")))
+    two = _copy(st)
+    tok = [inp[n][W - 1].to(dev) for n in ("q", "k", "v", "alpha", "beta")]
+    o = m.leapq_decode_flush(st, *tok, Q0)
+    o2 = m.leapq_decode_step(two, *tok)
+    m.leapq_window_flush(two, Q0)
+    torch.cuda.synchronize()
+    S_prev = leapq.rebuild(start, buffer(st, W - 1))
+    q1, k1, v1 = (np64(inp[n][W - 1])[:, None] for n in ("q", "k", "v"))
+    a1, b1 = np64(inp["alpha"][W - 1])[:, None], np64(inp["beta"][W - 1])[:, None]
+    o_ref, S_w = gdn.gdn_recurrent(q1, k1, v1, a1, b1, S_prev)
+    assert_rel(np64(o), o_ref[:, 0], TOL_BF16, "last output")
+    assert_rel(np64(o2), o_ref[:, 0], TOL_BF16, "last output (two launches)")
+    dS = token_update_error(S_prev, rebuild_error(start, buffer(st, W - 1)), k1[:, 0], v1[:, 0],
+                            np64(inp["alpha"][W - 1]), b1[:, 0])
+    ref = leapq.flush(S_w, np64(Q0.cpu()), rank=6, bits=bits)
+    flips, _, _ = compare_flush(st, ref, f"{bits}-bit fused flush", S_w, Q=Q, dS=dS)
+    s1, s2 = stored(st), stored(two)
+    s1["Q"] = s2["Q"] = Q
+    rec, rec2 = leapq.dequant(s1), leapq.dequant(s2)
+    half = lambda s_: 0.5 * np64(s_.vscale)[:, :, None] / Q * np64(s_.ksmooth)[:, None, :]
+    gap = np.abs(rec - rec2) - (half(st) + half(two)) * (1 + 1e-4)
+    assert gap.max() <= 1e-5 * np.abs(S_w).max(), "fused and two-launch states differ"
+    say(f"  code flips vs oracle {flips}")
+
+
 def test_edge_cases():
     dev = need_gpu()
     say("leapq decode+flush: window 1, rank 0, wrong position")
