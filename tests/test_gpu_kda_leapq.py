@@ -13,7 +13,7 @@ import torch
 import delta_rule_recurrent_amd as m
 from delta_rule_recurrent_amd import synth
 from oracle import kda, kda_leapq, leapq
-from helpers import assert_rel, need_gpu, np64, rel_err, say
+from helpers import assert_rel, need_gpu, np64, rel_err, say, codes_of, pack_codes
 from test_gpu_leapq import buffer, compare_flush, rebuild_error, stored
 
 pytestmark = pytest.mark.gpu
@@ -62,6 +62,45 @@ def test_teacher_forced_windows(io):
         torch.cuda.synchronize()
         flips, _, _ = compare_flush(st, ref, f"window {w} flush", S_w, dS=dS)
         say(f"  window {w}: u err {rel_err(u_gpu, u_ref):.2e}, code flips {flips}")
+
+
+@pytest.mark.parametrize("bits", [6, 4])
+def test_packed_widths_window(bits):
+    """Per-channel decays on packed 6- and 4-bit codes (rank 6): the encode (stored
+    bytes equal to the host packer applied to the host-unpacked codes; codes within the
+    flush bounds at Q = 2^(b-1) - 1), one teacher-forced window of read-outs and
+    corrections (bf16 io), and the flush that closes it."""
+    dev = need_gpu()
+    say(f"kda_leapq at {bits} bits, rank 6: flush + window")
+    Q = (1 << (bits - 1)) - 1
+    B, H, W = 4, 8, 16
+    N = B * H
+    inp = synth.kda_leapq_decode(B=B, H=H, steps=W, device="cpu")
+    Q0 = synth.compensator_start(r=6)
+    st = m.LeapqBuffers(N, rank=6, window=W, kda=True, bits=bits)
+    m.kda_leapq_window_flush(st, Q0.to(dev), dense=inp["S0"].to(dev))
+    torch.cuda.synchronize()
+    Z = codes_of(st)
+    assert np.abs(Z).max() <= Q
+    assert np.array_equal(st.codes.cpu().numpy().view(np.uint8), pack_codes(Z, bits))
+    ref = leapq.flush(np64(inp["S0"]), np64(Q0), rank=6, bits=bits)
+    compare_flush(st, ref, f"{bits}-bit encode", np64(inp["S0"]), Q=Q)
+    start = stored(st)
+    start["Q"] = Q
+    outs = [m.kda_leapq_decode_step(st, *(inp[n][t].to(dev) for n in ("q", "k", "v", "alpha", "beta")))
+            for t in range(W)]
+    torch.cuda.synchronize()
+    o_ref, buf_ref = kda_leapq.window_run(start, *(np64(inp[n]) for n in ("q", "k", "v", "alpha", "beta")))
+    u_gpu = np64(st.buf_u).transpose(1, 0, 2)
+    assert_rel(u_gpu, np.stack([b_[1] for b_ in buf_ref]), TOL_F32, "corrections")
+    e = assert_rel(np64(torch.stack(outs)), o_ref, TOL_BF16, "outputs")
+    S_w = kda_leapq.rebuild(start, buffer(st, W))
+    ref = leapq.flush(S_w, np64(Q0), rank=6, bits=bits)
+    dS = rebuild_error(start, buffer(st, W), kda=True)
+    m.kda_leapq_window_flush(st, Q0.to(dev))
+    torch.cuda.synchronize()
+    flips, _, _ = compare_flush(st, ref, f"{bits}-bit window flush", S_w, Q=Q, dS=dS)
+    say(f"  outputs {e:.2e}, code flips {flips}")
 
 
 def test_flush_mid_window():
