@@ -139,11 +139,12 @@ __global__ __launch_bounds__(256) void gdn_bwd_fscan_kernel(const uint8_t* __res
     o.u = *reinterpret_cast<const u32x2*>(pc + kWsU + ((size_t)(w * 8 + vt) * 64 + lane) * 8);
     o.gc = *reinterpret_cast<const float*>(pc + kWsG + l16 * 4);
   };
-  Ops cur, nxt;
-  if (nc > 0) load(chunk0, nxt);
-  for (int s = 0; s < nc; ++s) {
-    cur = nxt;
-    if (s + 1 < nc) load(chunk0 + s + 1, nxt);
+  // chunk s: its operands were requested two chunks earlier; it requests those of
+  // chunk s + 2 (past the end the last chunk's again, so that every chunk issues the same
+  // loads and the waits count exactly) into the set chunk s - 1 used. The three sets
+  // rotate through an unrolled loop, so each stays in registers.
+  auto body = [&](int s, const Ops& cur, Ops& fut) {
+    load(chunk0 + min(s + 2, nc - 1), fut);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -167,6 +168,19 @@ __global__ __launch_bounds__(256) void gdn_bwd_fscan_kernel(const uint8_t* __res
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[j] = mfma(a, as_bf(cur.kh[2 * j + js]), acc[j]);
     }
+  };
+  if (nc > 0) {
+    Ops P0, P1, P2;
+    load(chunk0, P0);
+    load(chunk0 + min(1, nc - 1), P1);
+    int s = 0;
+    for (; s + 3 <= nc; s += 3) {
+      body(s, P0, P2);
+      body(s + 1, P1, P0);
+      body(s + 2, P2, P1);
+    }
+    if (s < nc) body(s, P0, P2);
+    if (s + 1 < nc) body(s + 1, P1, P0);
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j)
