@@ -30,8 +30,8 @@
 //
 // Kernels: the forward's chunk prep (which also stores T), a forward state scan (the
 // state before every chunk, bf16), the backward state scan (the gradient after every
-// chunk, bf16, dS_0 and the chunks' sum(dS_a o S_a)), and two per-chunk gradient
-// kernels (bf16 MFMA, fp32 accumulation).
+// chunk, bf16, dS_0 and the chunks' sum(dS_a o S_a)), and two gradient kernels over
+// the chunks (persistent, one block per CU; bf16 MFMA, fp32 accumulation).
 #include "chunk_device.hpp"
 #include "gdn_chunk_layout.hpp"
 

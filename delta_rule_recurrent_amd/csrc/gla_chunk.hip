@@ -17,8 +17,8 @@
 //   combine  start states: S_0 the incoming state, then x <- gamma_i o x + B_i over the
 //            pieces of segment s in order gives S_{s+1};
 //   pass 2   every segment from its start state, with outputs.
-// A 512-thread block runs one (sequence, segment or piece), one block per CU (the
-// segments fill the GPU). Per chunk the block forms, with m the chunk's middle token
+// A 512-thread block runs one (sequence, segment or piece); the segments fill the GPU,
+// pass 2 at one block per CU (the segment's state in registers), pass 1 at two. Per chunk the block forms, with m the chunk's middle token
 // (which halves the range of the factors), Qr = Q o e^{b - b_m} and Kr = K o e^{b_m - b}
 // once in LDS; every product goes through them:
 //   scores      (Qr Kr^T) o M,
@@ -30,7 +30,8 @@
 // LDS for the transposed operand reads. Wave w holds the state rows of value channels
 // 16 w .. 16 w + 15 transposed (rows = keys) in fp32 MFMA accumulators, which are also
 // the A operand of the inter-chunk product: their key order (four consecutive keys per
-// lane from each of two 16-key blocks) is matched on the Qr side by two 8-byte reads.
+// lane from each of two 16-key blocks) is matched by storing Qr key-permuted in LDS, so
+// that the B operand is one 16-byte read.
 // bf16 MFMA (16x16x32) with fp32 accumulation throughout.
 #include "chunk_device.hpp"
 #include "gla_chunk_layout.hpp"
