@@ -12,10 +12,11 @@
 //                m_i <- max |S_i|, Z_i <- clamp(rint(S_i (Q / m_i)), -Q, Q).
 //                No smoothing and no compensator tokens: the page's eq. 2 scheme.
 //
-// Mapping: every lane holds 16 bytes of its row (8 bf16 entries, or 16 codes), so a
-// row is 16 (bf16) or 8 (codes) consecutive lanes and one wave instruction moves 1 KiB
-// of state, as in the fp32 decode kernel; a 256-thread block owns 16 (bf16) or 32
-// (codes) rows of one head. The state is streamed with non-temporal loads and stores
+// Mapping: every lane holds 16 bytes of each of its rows (8 bf16 entries, or 16 codes),
+// so a row is 16 (bf16) or 8 (codes) consecutive lanes and one wave instruction moves 1
+// KiB of state, as in the fp32 decode kernel; each lane group carries 2 rows, 16 (bf16)
+// or 32 (codes) apart, so that its q and k entries, loaded once, serve both, and a
+// 256-thread block owns 32 (bf16) or 64 (codes) rows of one head. The state is streamed with non-temporal loads and stores
 // (it is read and written once per step and does not fit the caches). Over T tokens in one launch the row stays in registers
 // and is rounded after every token exactly as a launch per token would.
 #include "common.hpp"
@@ -59,37 +60,44 @@ __global__ __launch_bounds__(256) void gdn_decode_lowp_kernel(
     void* __restrict__ Sv, float* __restrict__ rowmax, float qf, float qinv, const IO* __restrict__ q,
     const IO* __restrict__ k, const IO* __restrict__ v, const float* __restrict__ alpha,
     const float* __restrict__ beta, IO* __restrict__ o, int T) {
-  constexpr int E = BF16STATE ? 8 : 16;   // entries per lane (16 bytes)
+  constexpr int E = BF16STATE ? 8 : 16;   // entries per lane and row (16 bytes)
   constexpr int L = kD / E;               // lanes per row
-  constexpr int RPB = 256 / L;            // rows per block
+  constexpr int R = 2;                    // rows per lane group: q and k are loaded once for R rows
+  constexpr int RPB = 256 / L * R;        // rows per block
   constexpr int BPH = kD / RPB;           // blocks per head
   const int tid = threadIdx.x;
   const int head = blockIdx.x / BPH;
-  const int row = (blockIdx.x % BPH) * RPB + tid / L;
+  const int row0 = (blockIdx.x % BPH) * RPB + tid / L;   // rows row0 + (256 / L) r
   const int col = (tid % L) * E;
-  const size_t e0 = (size_t)head * kD * kD + (size_t)row * kD + col;
-  const size_t r0 = (size_t)head * kD + row;
   const bool lead = (tid % L) == 0;
+  auto erow = [&](int r) { return (size_t)head * kD * kD + (size_t)(row0 + (256 / L) * r) * kD + col; };
+  auto rrow = [&](int r) { return (size_t)head * kD + row0 + (256 / L) * r; };
 
-  float s[E];
-  float m = 0.f;
-  if constexpr (BF16STATE) {
-    const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(Sv) + e0));
-    const uint32_t ww[4] = {w[0], w[1], w[2], w[3]};
+  float s[R][E];
+  float m[R];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      s[2 * j] = __uint_as_float(ww[j] << 16);
-      s[2 * j + 1] = __uint_as_float(ww[j] & 0xffff0000u);
+  for (int r = 0; r < R; ++r) {
+    m[r] = 0.f;
+    if constexpr (BF16STATE) {
+      const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(Sv) + erow(r)));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s[r][2 * j] = __uint_as_float(w[j] << 16);
+        s[r][2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+      }
+    } else {
+      const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const int8_t*>(Sv) + erow(r)));
+      m[r] = rowmax[rrow(r)];
+      const float sv = m[r] * qinv;
+#pragma unroll
+      for (int e = 0; e < E; ++e) s[r][e] = sv * (float)(int8_t)((w[e >> 2] >> (8 * (e & 3))) & 0xff);
     }
-  } else {
-    const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const int8_t*>(Sv) + e0));
-    const uint32_t ww[4] = {w[0], w[1], w[2], w[3]};
-    m = rowmax[r0];
-    const float sv = m * qinv;
-#pragma unroll
-    for (int e = 0; e < E; ++e) s[e] = sv * (float)(int8_t)((ww[e >> 2] >> (8 * (e & 3))) & 0xff);
   }
-  uint32_t zw[4] = {0u, 0u, 0u, 0u};
+  uint32_t zw[R][4];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) zw[r][j] = 0u;
 
   for (int t = 0; t < T; ++t) {
     const size_t tok = (size_t)head * T + t;
@@ -97,49 +105,59 @@ __global__ __launch_bounds__(256) void gdn_decode_lowp_kernel(
     load_vec<IO, E>(k + tok * kD + col, k4);
     load_vec<IO, E>(q + tok * kD + col, q4);
     const float a = alpha[tok], b = beta[tok];
-    const float vi = io_traits<IO>::ld(v, tok * kD + row);
-    float kq = 0.f, pk = 0.f, pq = 0.f;
+    float kq = 0.f;
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      kq += k4[e] * q4[e];
-      pk += s[e] * k4[e];
-      pq += s[e] * q4[e];
-    }
+    for (int e = 0; e < E; ++e) kq += k4[e] * q4[e];
     kq = group_sum<L>(kq);
-    pk = group_sum<L>(pk);
-    pq = group_sum<L>(pq);
-    const float u = b * (vi - a * pk);
-    const float oi = a * pq + u * kq;
-    if (lead) io_traits<IO>::st(o, tok * kD + row, oi);
-    float sn[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) sn[e] = a * s[e] + u * k4[e];
-    if constexpr (BF16STATE) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) s[e] = bf16_round(sn[e]);
-    } else {
-      float mx = 0.f;
-#pragma unroll
-      for (int e = 0; e < E; ++e) mx = fmaxf(mx, fabsf(sn[e]));
-      m = group_max<L>(mx);
-      const float sc = m > 0.f ? qf / m : 0.f, sv = m * qinv;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) zw[j] = 0u;
+    for (int r = 0; r < R; ++r) {
+      const int row = row0 + (256 / L) * r;
+      const float vi = io_traits<IO>::ld(v, tok * kD + row);
+      float pk = 0.f, pq = 0.f;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        const float z = fminf(fmaxf(rintf(sn[e] * sc), -qf), qf);
-        s[e] = sv * z;
-        zw[e >> 2] |= (uint32_t)((int32_t)z & 0xff) << (8 * (e & 3));
+        pk += s[r][e] * k4[e];
+        pq += s[r][e] * q4[e];
+      }
+      pk = group_sum<L>(pk);
+      pq = group_sum<L>(pq);
+      const float u = b * (vi - a * pk);
+      const float oi = a * pq + u * kq;
+      if (lead) io_traits<IO>::st(o, tok * kD + row, oi);
+      float sn[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) sn[e] = a * s[r][e] + u * k4[e];
+      if constexpr (BF16STATE) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) s[r][e] = bf16_round(sn[e]);
+      } else {
+        float mx = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) mx = fmaxf(mx, fabsf(sn[e]));
+        m[r] = group_max<L>(mx);
+        const float sc = m[r] > 0.f ? qf / m[r] : 0.f, sv = m[r] * qinv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) zw[r][j] = 0u;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float z = fminf(fmaxf(rintf(sn[e] * sc), -qf), qf);
+          s[r][e] = sv * z;
+          zw[r][e >> 2] |= (uint32_t)((int32_t)z & 0xff) << (8 * (e & 3));
+        }
       }
     }
   }
-  if constexpr (BF16STATE) {
-    __builtin_nontemporal_store(u32x4{pack_bf16(s[0], s[1]), pack_bf16(s[2], s[3]), pack_bf16(s[4], s[5]),
-                                      pack_bf16(s[6], s[7])},
-                                reinterpret_cast<u32x4*>(static_cast<uint16_t*>(Sv) + e0));
-  } else if (T > 0) {
-    __builtin_nontemporal_store(u32x4{zw[0], zw[1], zw[2], zw[3]}, reinterpret_cast<u32x4*>(static_cast<int8_t*>(Sv) + e0));
-    if (lead) rowmax[r0] = m;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if constexpr (BF16STATE) {
+      __builtin_nontemporal_store(u32x4{pack_bf16(s[r][0], s[r][1]), pack_bf16(s[r][2], s[r][3]),
+                                        pack_bf16(s[r][4], s[r][5]), pack_bf16(s[r][6], s[r][7])},
+                                  reinterpret_cast<u32x4*>(static_cast<uint16_t*>(Sv) + erow(r)));
+    } else if (T > 0) {
+      __builtin_nontemporal_store(u32x4{zw[r][0], zw[r][1], zw[r][2], zw[r][3]},
+                                  reinterpret_cast<u32x4*>(static_cast<int8_t*>(Sv) + erow(r)));
+      if (lead) rowmax[rrow(r)] = m[r];
+    }
   }
 }
 
@@ -175,8 +193,8 @@ static int lowp_decode(const char* fn, bool bf16state, void* S, float* rowmax, i
       (rowmax && (overlaps(rowmax, nM, S, nS) || overlaps(rowmax, nM, o, nIO))))
     return set_error(GDNRT_EINVAL, "%s: buffers overlap", fn);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // blocks per head: 8 (bf16 rows, 16 per block) or 4 (code rows, 32 per block)
-  const dim3 grid((unsigned)(N * (bf16state ? 8 : 4))), block(256);
+  // blocks per head: 4 (bf16 rows, 32 per block) or 2 (code rows, 64 per block)
+  const dim3 grid((unsigned)(N * (bf16state ? 4 : 2))), block(256);
   const float qf = bf16state ? 0.f : (float)((1 << (bits - 1)) - 1), qinv = bf16state ? 0.f : 1.0f / qf;
 #define GDNRT_LOWP(IOT, B)                                                                              \
   hipLaunchKernelGGL((gdn_decode_lowp_kernel<IOT, B>), grid, block, 0, s, S, rowmax, qf, qinv,         \
