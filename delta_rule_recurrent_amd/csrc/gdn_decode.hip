@@ -11,15 +11,17 @@
 // so one read and one write of each 512-byte row per token is the whole traffic;
 // o uses the pre-update row and k.q instead of a second pass over the new row.
 //
-// Mapping: a 256-thread block (four 64-lane waves) owns 8 rows of one head, so a
-// head is 16 blocks. Each row is held by 32 lanes, four consecutive floats per
-// lane: one 16-byte load per lane covers two whole rows, a perfectly coalesced
-// 1 KiB per wave instruction. The state is touched once per step and does not fit
-// in any cache, so it is read and written with non-temporal hints. Measured on
-// MI355X, many small blocks holding one float4 per lane beat fewer blocks that
-// keep more rows in flight per wave (and beat a plain copy kernel), which is why
-// the block is this small. Row sums use DPP inside 16-lane rows plus one swizzle
-// across the two halves of a 32-lane group.
+// Mapping: a 256-thread block (four 64-lane waves) owns 16 rows of one head, so a
+// head is 8 blocks. Each row is held by 32 lanes, four consecutive floats per lane:
+// one 16-byte load per lane covers two whole rows, a perfectly coalesced 1 KiB per
+// wave instruction. Each 32-lane group holds two rows 8 apart, so the lane's q and
+// k entries (and k.q) serve both. The state is touched once per step and does not
+// fit in any cache, so it is read and written with non-temporal hints. Measured on
+// MI355X, two rows per lane group beat one (KDA 2% faster, its decay vector loaded
+// once for both rows; GDN up to 2%, on some boxes within noise) and four (4% slower,
+// fewer blocks in flight); small blocks beat larger persistent tiles and a plain copy
+// kernel. Row sums use DPP inside 16-lane rows plus one swizzle across the two halves
+// of a 32-lane group.
 //
 // Kimi Delta Attention (same section: the decay becomes a vector alpha_t, one factor
 // per key channel, eq. 1) runs through the same kernel: with the decay folded into
@@ -31,56 +33,74 @@
 namespace gdnrt {
 
 // VEC: alpha is [N][T][d_k] (one decay per key channel, KDA) instead of [N][T].
-template <typename IO, bool VEC>
+// R: rows per lane, 8 apart, so that the lane's q, k (and decay) entries serve R rows.
+template <typename IO, bool VEC, int R>
 __global__ __launch_bounds__(256) void gdn_decode_kernel(
     float* __restrict__ S, const IO* __restrict__ q, const IO* __restrict__ k,
     const IO* __restrict__ v, const float* __restrict__ alpha, const float* __restrict__ beta,
     IO* __restrict__ o, int T) {
-  constexpr int kRowsPerBlock = 8;
+  constexpr int kRowsPerBlock = 8 * R;
   constexpr int BPH = kD / kRowsPerBlock;   // blocks per head
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int head = blockIdx.x / BPH;
-  const int row = (blockIdx.x % BPH) * kRowsPerBlock + wave * 2 + (lane >> 5);
+  const int row0 = (blockIdx.x % BPH) * kRowsPerBlock + wave * 2 + (lane >> 5);   // rows row0 + 8 r
   const int col = (lane & 31) * 4;      // first key column of this lane
 
-  f32x4* Sp = reinterpret_cast<f32x4*>(S + (size_t)head * kD * kD + (size_t)row * kD + col);
-  f32x4 s = __builtin_nontemporal_load(Sp);
+  f32x4* Sp[R];
+  f32x4 s[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    Sp[r] = reinterpret_cast<f32x4*>(S + (size_t)head * kD * kD + (size_t)(row0 + 8 * r) * kD + col);
+    s[r] = __builtin_nontemporal_load(Sp[r]);
+  }
 
   for (int t = 0; t < T; ++t) {
     const size_t tok = (size_t)head * T + t;
     const f32x4 k4 = io_traits<IO>::ld4(k, tok * kD + col);
     const f32x4 q4 = io_traits<IO>::ld4(q, tok * kD + col);
     const float b = beta[tok];
-    const float vi = io_traits<IO>::ld(v, tok * kD + row);
     const float kq = sum32(k4.x * q4.x + k4.y * q4.y + k4.z * q4.z + k4.w * q4.w);
-    float u, oi;
+    f32x4 a4, ak, aq;
+    float a = 1.f;
     if constexpr (VEC) {
-      const f32x4 a4 = *reinterpret_cast<const f32x4*>(alpha + tok * kD + col);
-      const f32x4 ak = a4 * k4, aq = a4 * q4;
-      const float pk = sum32(s.x * ak.x + s.y * ak.y + s.z * ak.z + s.w * ak.w);
-      const float pq = sum32(s.x * aq.x + s.y * aq.y + s.z * aq.z + s.w * aq.w);
-      u = b * (vi - pk);
-      oi = pq + u * kq;
-      s = a4 * s + u * k4;
+      a4 = *reinterpret_cast<const f32x4*>(alpha + tok * kD + col);
+      ak = a4 * k4;
+      aq = a4 * q4;
     } else {
-      const float a = alpha[tok];
-      const float pk = sum32(s.x * k4.x + s.y * k4.y + s.z * k4.z + s.w * k4.w);
-      const float pq = sum32(s.x * q4.x + s.y * q4.y + s.z * q4.z + s.w * q4.w);
-      u = b * (vi - a * pk);
-      oi = a * pq + u * kq;
-      s = a * s + u * k4;
+      a = alpha[tok];
     }
-    if ((lane & 31) == 0) io_traits<IO>::st(o, tok * kD + row, oi);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int row = row0 + 8 * r;
+      const float vi = io_traits<IO>::ld(v, tok * kD + row);
+      float u, oi;
+      if constexpr (VEC) {
+        const float pk = sum32(s[r].x * ak.x + s[r].y * ak.y + s[r].z * ak.z + s[r].w * ak.w);
+        const float pq = sum32(s[r].x * aq.x + s[r].y * aq.y + s[r].z * aq.z + s[r].w * aq.w);
+        u = b * (vi - pk);
+        oi = pq + u * kq;
+        s[r] = a4 * s[r] + u * k4;
+      } else {
+        const float pk = sum32(s[r].x * k4.x + s[r].y * k4.y + s[r].z * k4.z + s[r].w * k4.w);
+        const float pq = sum32(s[r].x * q4.x + s[r].y * q4.y + s[r].z * q4.z + s[r].w * q4.w);
+        u = b * (vi - a * pk);
+        oi = a * pq + u * kq;
+        s[r] = a * s[r] + u * k4;
+      }
+      if ((lane & 31) == 0) io_traits<IO>::st(o, tok * kD + row, oi);
+    }
   }
-  __builtin_nontemporal_store(s, Sp);
+#pragma unroll
+  for (int r = 0; r < R; ++r) __builtin_nontemporal_store(s[r], Sp[r]);
 }
 
 template <typename IO, bool VEC>
 static void launch_decode(float* S, const void* q, const void* k, const void* v,
                           const float* alpha, const float* beta, void* o, int N, int T,
                           hipStream_t stream) {
-  hipLaunchKernelGGL((gdn_decode_kernel<IO, VEC>), dim3(N * (kD / 8)), dim3(256), 0, stream, S,
+  constexpr int R = 2;
+  hipLaunchKernelGGL((gdn_decode_kernel<IO, VEC, R>), dim3(N * (kD / (8 * R))), dim3(256), 0, stream, S,
                      static_cast<const IO*>(q), static_cast<const IO*>(k),
                      static_cast<const IO*>(v), alpha, beta, static_cast<IO*>(o), T);
 }
