@@ -28,10 +28,15 @@
 // (dST o S_T after the last chunk); the rest is a sum over at most 64 tokens, and no
 // rounding error accumulates along the sequence. dalpha = d log alpha / alpha.
 //
-// Kernels: the forward's chunk prep (which also stores T), a forward state scan (the
-// state before every chunk, bf16), the backward state scan (the gradient after every
-// chunk, bf16, dS_0 and the chunks' sum(dS_a o S_a)), and two gradient kernels over
-// the chunks (persistent, one block per CU; bf16 MFMA, fp32 accumulation).
+// Since S_a = g_C S_b + U^T K^, that boundary sum is g_C sum(dS_a o S_b) +
+// sum(diag(g_C/g) U dS_a o K), two products the chunk's gradients form anyway, so the
+// backward state scan needs no forward state.
+//
+// Kernels: the forward's chunk prep (which also stores T); the forward state scan (the
+// state before every chunk, bf16) and the backward state scan (the gradient after every
+// chunk, bf16, and dS_0), independent of each other, side by side in one launch; and
+// two gradient kernels over the chunks (persistent, one block per CU; bf16 MFMA, fp32
+// accumulation), the first of which also forms each chunk's boundary sum.
 #include "chunk_device.hpp"
 #include "gdn_chunk_layout.hpp"
 
@@ -73,9 +78,8 @@ __device__ __forceinline__ bf16x8 ld8_split_s(const uint16_t* X, int row, int c)
 // block -> (sequence, value tile of 16); the 8 tiles of one sequence share an XCD
 // (blocks are dealt to the 8 XCDs round robin), so the chunk operands they all read
 // are fetched into that XCD's L2 once
-__device__ __forceinline__ void seq_tile(int& n, int& vt) {
-  const int bid = blockIdx.x;
-  if ((gridDim.x & 63) == 0) {
+__device__ __forceinline__ void seq_tile(int& n, int& vt, int bid, int grid) {
+  if ((grid & 63) == 0) {
     n = (bid >> 6) * 8 + (bid & 7);
     vt = (bid >> 3) & 7;
   } else {
@@ -93,8 +97,7 @@ struct Ws {
   uint16_t* dU;    // dU, bf16 [64][128]
   float* dK1;      // dA'^T Q + diag(g_C/g) U dS_a, fp32 [64][128]
   float* qdq;      // q_t . dq_t, fp32 [64]
-  float* bnd;      // sum(dS_a o S_a) in 32 parts (value tile, wave), fp32
-  float* ST;       // per sequence, the recomputed final state, fp32 [128][128]
+  float* bnd;      // sum(dS_a o S_a), fp32, one per chunk
 };
 
 }  // namespace gdb
@@ -105,16 +108,15 @@ struct Ws {
 // 32 w + 16 j + l16) and token block w of U. Per chunk: store the state (bf16), then
 // U = U~ - W S^T for this tile's values and S <- g_C S + U^T K^, with the prep's
 // fragments as MFMA operands straight from registers (next chunk's loaded ahead).
-__global__ __launch_bounds__(256) void gdn_bwd_fscan_kernel(const uint8_t* __restrict__ prep,
-                                                            const float* __restrict__ S0,
-                                                            uint16_t* __restrict__ Sb,
-                                                            float* __restrict__ ST, int T) {
+// (bid, grid): this tile's block among the scan's blocks.
+__device__ __forceinline__ void fscan_tile(const uint8_t* __restrict__ prep, const float* __restrict__ S0,
+                                           uint16_t* __restrict__ Sb, int T, int bid, int grid) {
   using namespace gdb;
   __shared__ __attribute__((aligned(16))) uint16_t sS[16 * PT];
   __shared__ __attribute__((aligned(16))) uint16_t sU[16 * PA];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, lq = lane >> 4;
   int n, vt;
-  seq_tile(n, vt);
+  seq_tile(n, vt, bid, grid);
   const int v0 = 16 * vt, nc = T / C;
   const size_t chunk0 = (size_t)n * nc;
   f32x4 acc[2];
@@ -182,27 +184,18 @@ __global__ __launch_bounds__(256) void gdn_bwd_fscan_kernel(const uint8_t* __res
     if (s < nc) body(s, P0, P2);
     if (s + 1 < nc) body(s + 1, P1, P0);
   }
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ST[((size_t)n * kD + v0 + 4 * lq + i) * kD + 32 * w + 16 * j + l16] = acc[j][i];
 }
 
 // ------------------------------------------------------------------ backward state scan
 // One block of 256 threads per (sequence, value tile of 16 rows), chunks last to
 // first; wave w owns key columns [32 w, 32 w + 32) of dS and token block w of
-// K^ dS^T. Per chunk: store dS (bf16, the gradient after the chunk) and this tile's
-// part of sum(dS o S) with S the state after the chunk, stage K^ (as K^^T), Q', W and
-// this tile's dO in LDS, then
+// K^ dS^T. Per chunk: store dS (bf16, the gradient after the chunk), stage K^ (as
+// K^^T), Q', W and this tile's dO in LDS, then
 //   dS <- g_C dS + dO^T Q' - (K^ dS^T)^T W.
-__global__ __launch_bounds__(256) void gdn_bwd_rscan_kernel(const uint8_t* __restrict__ prep,
-                                                            const uint16_t* __restrict__ dO,
-                                                            const float* __restrict__ dST,
-                                                            const uint16_t* __restrict__ Sb,
-                                                            const float* __restrict__ ST,
-                                                            uint16_t* __restrict__ dSa,
-                                                            float* __restrict__ bnd,
-                                                            float* __restrict__ dS0, int T) {
+// It reads no forward state, so it runs beside the forward scan (below).
+__device__ __forceinline__ void rscan_tile(const uint8_t* __restrict__ prep, const uint16_t* __restrict__ dO,
+                                           const float* __restrict__ dST, uint16_t* __restrict__ dSa,
+                                           float* __restrict__ dS0, int T, int bid, int grid) {
   using namespace gdb;
   __shared__ __attribute__((aligned(16))) uint16_t sD[16 * PT];
   __shared__ __attribute__((aligned(16))) uint16_t sKt[kD * PA];
@@ -210,10 +203,9 @@ __global__ __launch_bounds__(256) void gdn_bwd_rscan_kernel(const uint8_t* __res
   __shared__ __attribute__((aligned(16))) uint16_t sW[C * PT];
   __shared__ __attribute__((aligned(16))) uint16_t sO[C * PX];
   __shared__ __attribute__((aligned(16))) uint16_t sdU[16 * PA];
-  __shared__ __attribute__((aligned(16))) float sA[16 * PFK];   // the state after the chunk, this tile
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, lq = lane >> 4;
   int n, vt;
-  seq_tile(n, vt);
+  seq_tile(n, vt, bid, grid);
   const int v0 = 16 * vt, nc = T / C;
   const size_t chunk0 = (size_t)n * nc;
   const int tr = tid >> 4, tc = 8 * (tid & 15);   // a thread's 8 entries of a [16][128] tile
@@ -227,22 +219,10 @@ __global__ __launch_bounds__(256) void gdn_bwd_rscan_kernel(const uint8_t* __res
     u32x4 kh[4], qp[4], w[4];
     u32x2 o;
     float gc;
-    f32x4 sa[2];   // this thread's 8 entries (row tr, columns tc ..) of the state after the chunk
   };
   // fragment f = w + 4 p of each 16-fragment operand, this lane's 16 bytes
   auto load = [&](int ci, Ops& o) {
     const uint8_t* pc = prep + (chunk0 + ci) * kWsChunk;
-    {
-      const size_t e = (size_t)(v0 + tr) * kD + tc;
-      if (ci + 1 < nc) {
-        const u32x4 b = *reinterpret_cast<const u32x4*>(Sb + (chunk0 + ci + 1) * kD * kD + e);
-        o.sa[0] = f32x4{lo_bf(b.x), hi_bf(b.x), lo_bf(b.y), hi_bf(b.y)};
-        o.sa[1] = f32x4{lo_bf(b.z), hi_bf(b.z), lo_bf(b.w), hi_bf(b.w)};
-      } else {
-        o.sa[0] = *reinterpret_cast<const f32x4*>(ST + (size_t)n * kD * kD + e);
-        o.sa[1] = *reinterpret_cast<const f32x4*>(ST + (size_t)n * kD * kD + e + 4);
-      }
-    }
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const size_t off = ((size_t)(w + 4 * p) * 64 + lane) * 16;
@@ -263,8 +243,6 @@ __global__ __launch_bounds__(256) void gdn_bwd_rscan_kernel(const uint8_t* __res
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) sD[sw_off(4 * lq + i, 32 * w + 16 * j + l16)] = f32_to_bf16(acc[j][i]);
-    *reinterpret_cast<f32x4*>(sA + tr * PFK + tc) = cur.sa[0];
-    *reinterpret_cast<f32x4*>(sA + tr * PFK + tc + 4) = cur.sa[1];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int f = w + 4 * p;
@@ -280,19 +258,9 @@ __global__ __launch_bounds__(256) void gdn_bwd_rscan_kernel(const uint8_t* __res
     }
     *reinterpret_cast<u32x2*>(sO + px_off(tid >> 2, 4 * (tid & 3))) = cur.o;
     lds_barrier();
-    // the tile's bf16 copy to the workspace, one 16-byte store per thread; this tile's
-    // part of sum(dS o S) from the fp32 accumulators and the staged state after the chunk
+    // the tile's bf16 copy to the workspace, one 16-byte store per thread
     *reinterpret_cast<u32x4*>(dSa + (chunk0 + ci) * kD * kD + (size_t)(v0 + tr) * kD + tc) =
         *reinterpret_cast<const u32x4*>(sD + sw_off(tr, tc));
-    {
-      float part = 0.f;
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) part += acc[j][i] * sA[(4 * lq + i) * PFK + 32 * w + 16 * j + l16];
-      part = sum64(part);
-      if (lane == 0) bnd[(chunk0 + ci) * 32 + 4 * vt + w] = part;
-    }
     // -(K^ dS^T)^T for tokens 16 w .. 16 w + 15: [v][t]
     f32x4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -320,6 +288,32 @@ __global__ __launch_bounds__(256) void gdn_bwd_rscan_kernel(const uint8_t* __res
     for (int i = 0; i < 4; ++i) dS0[((size_t)n * kD + v0 + 4 * lq + i) * kD + 32 * w + 16 * j + l16] = acc[j][i];
 }
 
+// The two state scans in one launch: the first half of the blocks runs the forward
+// scan's tiles, the second half the backward scan's, tile for tile, so that a tile's
+// XCD (blocks are dealt to the XCDs round robin) is the same in both halves. Both are
+// serial chains over the chunks at one block per tile. Measured on MI355X: with the
+// halves interleaved every 8 blocks (so that a CU's two blocks took the same scan)
+// the launch took 687 us at 32 x 16,384 tokens, with the halves 629 us, against
+// 258 + 490 us as two launches.
+__global__ __launch_bounds__(256) void gdn_bwd_scans_kernel(const uint8_t* __restrict__ prep,
+                                                            const float* __restrict__ S0,
+                                                            uint16_t* __restrict__ Sb,
+                                                            const uint16_t* __restrict__ dO,
+                                                            const float* __restrict__ dST,
+                                                            uint16_t* __restrict__ dSa,
+                                                            float* __restrict__ dS0, int T) {
+  const int grid = (int)gridDim.x >> 1, b = blockIdx.x, tile = b < grid ? b : b - grid;
+  if (b < grid)
+    fscan_tile(prep, S0, Sb, T, tile, grid);
+  else
+    rscan_tile(prep, dO, dST, dSa, dS0, T, tile, grid);
+}
+
+// T = 0: the state gradient passes through (dS0 = dST, or zero)
+__global__ __launch_bounds__(256) void gdn_bwd_pass_kernel(const float* __restrict__ dST, float* __restrict__ dS0) {
+  rscan_tile(nullptr, nullptr, dST, nullptr, dS0, 0, blockIdx.x, gridDim.x);
+}
+
 // ------------------------------------------------------------------ gradients, part 1
 // Persistent blocks of 512 threads (8 waves), one per CU (LDS); block b takes chunks b,
 // b + grid, ... and loads the next chunk's q, k, dO, S_b, dS_a and alpha into registers
@@ -334,6 +328,7 @@ struct alignas(16) G1Smem {
   uint16_t A[kChunk * gdb::PA];                                              // A, then dA' [r][j]
   float lg[kChunk], g[kChunk], kd[kChunk];
   float qdq[2][kChunk];   // q_t . dq_t over key blocks 0-3 and 4-7 (the two wave halves)
+  float bs[8][2];         // per wave: sum(dS_a o S_b), sum(diag(g_C/g) U dS_a o K)
 };
 
 namespace gdb {
@@ -390,11 +385,16 @@ __global__ __launch_bounds__(512) void gdn_bwd_grad1_kernel(
       *reinterpret_cast<u32x4*>(sm.K + sw_off(r, cc)) = in.k[p];
       *reinterpret_cast<u32x4*>(sm.O + sw_off(r, cc)) = in.o[p];
     }
+    float bs1 = 0.f;   // this thread's part of sum(dS_a o S_b)
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int e = (tid + 512 * p) * 8, r = e >> 7, cc = e & 127;
       *reinterpret_cast<u32x4*>(sm.S + sw_off(r, cc)) = in.s[p];
       *reinterpret_cast<u32x4*>(sm.D + sw_off(r, cc)) = in.d[p];
+      const uint32_t sv[4] = {in.s[p].x, in.s[p].y, in.s[p].z, in.s[p].w};
+      const uint32_t dv[4] = {in.d[p].x, in.d[p].y, in.d[p].z, in.d[p].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bs1 += lo_bf(sv[i]) * lo_bf(dv[i]) + hi_bf(sv[i]) * hi_bf(dv[i]);
     }
     for (int e = tid; e < C * PA / 2; e += 512) reinterpret_cast<uint32_t*>(sm.A)[e] = 0u;
     if (w == 0) {
@@ -493,6 +493,7 @@ __global__ __launch_bounds__(512) void gdn_bwd_grad1_kernel(
     // ---- dq = dA' K + diag(g) dO S_b;  dK1 = dA'^T Q + diag(g_C/g) U dS_a
     float* dK1 = ws.dK1 + (size_t)cid * C * kD;
     float qacc[4] = {0.f, 0.f, 0.f, 0.f};   // this wave's share of q.dq, in key-block order
+    float bs2 = 0.f;                         // this lane's part of sum(diag(g_C/g) U dS_a o K)
 #pragma unroll 1
     for (int u = 0; u < 4; ++u) {
       const int kb = (w >> 2) * 4 + u;
@@ -515,16 +516,34 @@ __global__ __launch_bounds__(512) void gdn_bwd_grad1_kernel(
         const int r = 16 * rb + 4 * lq + i;
         const float gq = a1[i] + sm.g[r] * a2[i];
         dq[(tok0 + r) * kD + col] = f32_to_bf16(gq);
-        dK1[r * kD + col] = a3[i] + sm.kd[r] * a4[i];
+        const float ud = sm.kd[r] * a4[i];
+        dK1[r * kD + col] = a3[i] + ud;
         qacc[i] += sum16(bf16_to_f32(sm.Q[sw_off(r, col)]) * gq);
+        bs2 += ud * bf16_to_f32(sm.K[sw_off(r, col)]);
       }
     }
     // fixed summation order (no atomics): each half of the waves writes its own partial
     if (l16 == 0)
 #pragma unroll
       for (int i = 0; i < 4; ++i) sm.qdq[w >> 2][16 * rb + 4 * lq + i] = qacc[i];
+    bs1 = sum64(bs1);
+    bs2 = sum64(bs2);
+    if (lane == 0) {
+      sm.bs[w][0] = bs1;
+      sm.bs[w][1] = bs2;
+    }
     lds_barrier();
     if (tid < C) ws.qdq[(size_t)cid * C + tid] = sm.qdq[0][tid] + sm.qdq[1][tid];
+    // sum(dS_a o S_a) with S_a = g_C S_b + U^T K^ = g_C S_b + U^T diag(g_C/g) K
+    if (tid == 0) {
+      float b1 = 0.f, b2 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        b1 += sm.bs[i][0];
+        b2 += sm.bs[i][1];
+      }
+      ws.bnd[cid] = sm.g[C - 1] * b1 + b2;
+    }
   }
 }
 
@@ -752,7 +771,7 @@ __global__ __launch_bounds__(512) void gdn_bwd_grad2_kernel(
       const float dbL = (sm.dbL[0][t] + sm.dbL[1][t]) + (sm.dbL[2][t] + sm.dbL[3][t]);
       dbeta[tok0 + t] = sm.g[t] * dbW + dbU + dbL;
       const float dB = ws.qdq[(size_t)cid * C + t] - sm.bt[t] * dbU;
-      const float off = sum64(t < 32 ? ws.bnd[(size_t)cid * 32 + t] : 0.f);
+      const float off = ws.bnd[cid];
       // reverse inclusive sum inside the chunk: lane l scans token 63 - l
       const float rs = wave_scan(__shfl(dB, C - 1 - lane));
       dalpha[tok0 + t] = (__shfl(rs, C - 1 - t) + off) / alpha[tok0 + t];
@@ -767,11 +786,10 @@ using namespace gdnrt;
 namespace {
 
 struct BwdLayout {
-  size_t prep, T, Sb, dSa, dU, dK1, qdq, bnd, ST, total;
+  size_t prep, T, Sb, dSa, dU, dK1, qdq, bnd, total;
 };
 
 BwdLayout bwd_layout(size_t N, size_t nchunks) {
-  auto a16 = [](size_t x) { return (x + 15) & ~size_t(15); };
   BwdLayout L;
   L.prep = 0;
   L.T = L.prep + nchunks * gdc::kWsChunk;
@@ -781,8 +799,7 @@ BwdLayout bwd_layout(size_t N, size_t nchunks) {
   L.dK1 = L.dU + nchunks * kChunk * kD * 2;
   L.qdq = L.dK1 + nchunks * kChunk * kD * 4;
   L.bnd = L.qdq + nchunks * kChunk * 4;
-  L.ST = a16(L.bnd + nchunks * 32 * 4);
-  L.total = L.ST + N * kD * kD * 4;
+  L.total = L.bnd + nchunks * 4;
   return L;
 }
 
@@ -804,7 +821,7 @@ extern "C" int gdn_chunk_bwd(const void* q, const void* k, const void* v, const 
   if (chunk != kChunk) return set_error(GDNRT_ESHAPE, "%s: chunk=%d, only 64 is supported", fn, chunk);
   if (T % kChunk) return set_error(GDNRT_ESHAPE, "%s: T=%d is not a multiple of 64", fn, T);
   if (io != GDNRT_BF16) return set_error(GDNRT_EDTYPE, "%s: io must be GDNRT_BF16", fn);
-  if ((size_t)N * (T / kChunk) > 0x7fffffffu || (size_t)N * 8 > 0x7fffffffu)
+  if ((size_t)N * (T / kChunk) > 0x7fffffffu || (size_t)N * 16 > 0x7fffffffu)
     return set_error(GDNRT_ESHAPE, "%s: N=%d T=%d too large", fn, N, T);
   if (N == 0) return clear_error();
   if (!dS0 || (T > 0 && (!q || !k || !v || !alpha || !beta || !dO || !dq || !dk || !dv || !dalpha || !dbeta)))
@@ -834,8 +851,7 @@ extern "C" int gdn_chunk_bwd(const void* q, const void* k, const void* v, const 
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (T == 0) {   // no tokens: the state gradient passes through
-    hipLaunchKernelGGL(gdn_bwd_rscan_kernel, dim3((unsigned)(N * 8)), dim3(256), 0, s, nullptr, nullptr, dST,
-                       nullptr, nullptr, nullptr, nullptr, dS0, 0);
+    hipLaunchKernelGGL(gdn_bwd_pass_kernel, dim3((unsigned)(N * 8)), dim3(256), 0, s, dST, dS0);
     return check_launch(fn);
   }
   uint8_t* base = static_cast<uint8_t*>(workspace);
@@ -848,7 +864,6 @@ extern "C" int gdn_chunk_bwd(const void* q, const void* k, const void* v, const 
   ws.dK1 = reinterpret_cast<float*>(base + lay.dK1);
   ws.qdq = reinterpret_cast<float*>(base + lay.qdq);
   ws.bnd = reinterpret_cast<float*>(base + lay.bnd);
-  ws.ST = reinterpret_cast<float*>(base + lay.ST);
   const uint16_t* q16 = static_cast<const uint16_t*>(q);
   const uint16_t* k16 = static_cast<const uint16_t*>(k);
   const uint16_t* v16 = static_cast<const uint16_t*>(v);
@@ -856,9 +871,8 @@ extern "C" int gdn_chunk_bwd(const void* q, const void* k, const void* v, const 
   gdn_chunk_prep_with_inverse(q16, k16, v16, alpha, beta, ws.prep, ws.T, T, (int)nchunks, s);
   int rc = check_launch(fn);
   if (rc != GDNRT_OK) return rc;
-  hipLaunchKernelGGL(gdn_bwd_fscan_kernel, dim3((unsigned)(N * 8)), dim3(256), 0, s, ws.prep, S0, ws.Sb, ws.ST, T);
-  hipLaunchKernelGGL(gdn_bwd_rscan_kernel, dim3((unsigned)(N * 8)), dim3(256), 0, s, ws.prep, o16, dST, ws.Sb,
-                     ws.ST, ws.dSa, ws.bnd, dS0, T);
+  hipLaunchKernelGGL(gdn_bwd_scans_kernel, dim3((unsigned)(N * 16)), dim3(256), 0, s, ws.prep, S0, ws.Sb, o16,
+                     dST, ws.dSa, dS0, T);
   // persistent gradient blocks, one per CU (their LDS fills one)
   const unsigned ggrid = (unsigned)(nchunks < 256 ? nchunks : 256);
   hipLaunchKernelGGL(gdn_bwd_grad1_kernel, dim3(ggrid), dim3(512), 0, s, q16, k16, o16, alpha, ws,
