@@ -583,8 +583,8 @@ GLA_BWD_KERNELS = ("gla_bwd_prep_kernel", "gla_bwd_scan_kernel<fwd>", "gla_bwd_s
                    "gla_bwd_grad_kernel")
 
 
-GDN_BWD_KERNELS = ("gdn_chunk_prep_kernel<bwd>", "gdn_bwd_fscan_kernel", "gdn_bwd_rscan_kernel",
-                   "gdn_bwd_grad1_kernel", "gdn_bwd_grad2_kernel")
+GDN_BWD_KERNELS = ("gdn_chunk_prep_kernel<bwd>", "gdn_bwd_scans_kernel", "gdn_bwd_grad1_kernel",
+                   "gdn_bwd_grad2_kernel")
 
 
 def counter_traffic(kernel):
