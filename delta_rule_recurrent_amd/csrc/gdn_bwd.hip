@@ -394,7 +394,8 @@ __global__ __launch_bounds__(512) void gdn_bwd_grad1_kernel(
       const uint32_t sv[4] = {in.s[p].x, in.s[p].y, in.s[p].z, in.s[p].w};
       const uint32_t dv[4] = {in.d[p].x, in.d[p].y, in.d[p].z, in.d[p].w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) bs1 += lo_bf(sv[i]) * lo_bf(dv[i]) + hi_bf(sv[i]) * hi_bf(dv[i]);
+      for (int i = 0; i < 4; ++i)   // two bf16 products per instruction, summed in fp32
+        bs1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, sv[i]), __builtin_bit_cast(bf16x2, dv[i]), bs1, false);
     }
     for (int e = tid; e < C * PA / 2; e += 512) reinterpret_cast<uint32_t*>(sm.A)[e] = 0u;
     if (w == 0) {
@@ -492,7 +493,7 @@ __global__ __launch_bounds__(512) void gdn_bwd_grad1_kernel(
 
     // ---- dq = dA' K + diag(g) dO S_b;  dK1 = dA'^T Q + diag(g_C/g) U dS_a
     float* dK1 = ws.dK1 + (size_t)cid * C * kD;
-    float qacc[4] = {0.f, 0.f, 0.f, 0.f};   // this wave's share of q.dq, in key-block order
+    float qacc[4] = {0.f, 0.f, 0.f, 0.f};   // this lane's share of q.dq over its 4 key blocks
     float bs2 = 0.f;                         // this lane's part of sum(diag(g_C/g) U dS_a o K)
 #pragma unroll 1
     for (int u = 0; u < 4; ++u) {
@@ -518,11 +519,14 @@ __global__ __launch_bounds__(512) void gdn_bwd_grad1_kernel(
         dq[(tok0 + r) * kD + col] = f32_to_bf16(gq);
         const float ud = sm.kd[r] * a4[i];
         dK1[r * kD + col] = a3[i] + ud;
-        qacc[i] += sum16(bf16_to_f32(sm.Q[sw_off(r, col)]) * gq);
+        qacc[i] += bf16_to_f32(sm.Q[sw_off(r, col)]) * gq;
         bs2 += ud * bf16_to_f32(sm.K[sw_off(r, col)]);
       }
     }
-    // fixed summation order (no atomics): each half of the waves writes its own partial
+    // fixed summation order (no atomics): the 16 lanes of a row, then each half of the
+    // waves writes its own partial
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qacc[i] = sum16(qacc[i]);
     if (l16 == 0)
 #pragma unroll
       for (int i = 0; i < 4; ++i) sm.qdq[w >> 2][16 * rb + 4 * lq + i] = qacc[i];
@@ -686,9 +690,14 @@ __global__ __launch_bounds__(512) void gdn_bwd_grad2_kernel(
         XU[sw_off(r, col)] = f32_to_bf16(xu[i]);
         dv[(tok0 + r) * kD + col] = f32_to_bf16(sm.bt[r] * xu[i]);
         kw[u][i] = sm.bt[r] * sm.g[r] * xw[i];
-        su_acc[i] += sum16(xu[i] * bf16_to_f32(sm.V[sw_off(r, col)]));
-        sw_acc[i] += sum16(xw[i] * bf16_to_f32(sm.K[sw_off(r, col)]));
+        su_acc[i] += xu[i] * bf16_to_f32(sm.V[sw_off(r, col)]);
+        sw_acc[i] += xw[i] * bf16_to_f32(sm.K[sw_off(r, col)]);
       }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {   // the lane's 4 column blocks, then the 16 lanes of a row
+      su_acc[i] = sum16(su_acc[i]);
+      sw_acc[i] = sum16(sw_acc[i]);
     }
     if (l16 == 0)
 #pragma unroll
