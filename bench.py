@@ -579,8 +579,7 @@ def bench_gdn_chunk(K=10, W=2, B=1, H=32, T=16384, kda=False):
 
 
 GLA_FWD_KERNELS = ("gla_fused_kernel<pass1>", "gla_seg_combine_kernel", "gla_fused_kernel<pass2>")
-GLA_BWD_KERNELS = ("gla_bwd_prep_kernel", "gla_bwd_scan_kernel<fwd>", "gla_bwd_scan_kernel<rev>",
-                   "gla_bwd_grad_kernel")
+GLA_BWD_KERNELS = ("gla_bwd_prep_kernel", "gla_bwd_scans_kernel", "gla_bwd_grad_kernel")
 
 
 GDN_BWD_KERNELS = ("gdn_chunk_prep_kernel<bwd>", "gdn_bwd_scans_kernel", "gdn_bwd_grad1_kernel",

@@ -27,10 +27,15 @@
 // chunk): only sums over at most 64 tokens remain, and no rounding error accumulates
 // along the sequence.
 //
-// Four kernels: a per-chunk prep (cumulative gates, the scaled operands), a forward
-// state scan (the state before every chunk), a backward state scan (the gradient after
-// every chunk, dS_0 and the chunks' sum_v dS_a o S_a), and a per-chunk gradient kernel
-// (bf16 MFMA, fp32 accumulation; also the gate gradient).
+// Since S_a = e^{b_C} o S_b + V^T K^, that boundary sum is, per key channel,
+// e^{b_C} sum_v dS_a o S_b + sum_t K^ o (V dS_a): both products are at hand where a
+// chunk's gradients are formed, so the backward state scan needs no forward state.
+//
+// Three launches: a per-chunk prep (cumulative gates, the scaled operands); the forward
+// state scan (the state before every chunk) and the backward state scan (the gradient
+// after every chunk, and dS_0), independent of each other, side by side in one launch;
+// and a per-chunk gradient kernel (bf16 MFMA, fp32 accumulation; also the boundary sums
+// and the gate gradient).
 #include "chunk_device.hpp"
 
 namespace gdnrt {
@@ -48,8 +53,7 @@ __device__ __forceinline__ int px_off(int row, int col) { return row * PX + col 
 
 // Workspace per chunk (bytes): bf16 [64][128] Q^, K^; fp32 [64][128] E = e^{b - b_m};
 // fp32 [128] e^{b_C}, e^{b_m}, e^{b_C - b_m}; bf16 [128][128] the state before the
-// chunk and the state gradient after it. Then per sequence the fp32 final state of the
-// recomputed forward, and per chunk fp32 [8][128] sum_v dS_a o S_a by value tile.
+// chunk and the state gradient after it.
 constexpr size_t kQh = 0, kKh = 16384, kE = 32768, kEC = 65536, kEm = 66048, kECm = 66560,
                  kSb = 67072, kdS = 99840, kChunkB = 132608;
 
@@ -142,31 +146,24 @@ __global__ __launch_bounds__(256) void gla_bwd_prep_kernel(const uint16_t* __res
 // 4 lq + i, column 32 w + 16 j + l16). Per chunk (forward: first to last; reverse: last
 // to first) the state is stored in bf16 to the workspace, then
 //   forward:  S  <- e^{b_C} o S  + V^T K^     (X = V,  Y = K^)
-//   reverse:  dS <- e^{b_C} o dS + dO^T Q^    (X = dO, Y = Q^);
-// the reverse scan also writes this tile's sum_v dS o S per key channel, S the state
-// after the chunk (the next chunk's stored state, or ST after the last one), unless
-// BND is false (the state gradient alone is wanted; the forward scan has not run).
+//   reverse:  dS <- e^{b_C} o dS + dO^T Q^    (X = dO, Y = Q^).
 // The next chunk's X and Y are loaded into registers while this one is computed.
-template <bool REV, bool BND = REV>
-__global__ __launch_bounds__(256) void gla_bwd_scan_kernel(const uint16_t* __restrict__ X,
-                                                           uint8_t* __restrict__ ws,
-                                                           const float* __restrict__ Sinit,
-                                                           float* __restrict__ Sout,
-                                                           const float* __restrict__ ST,
-                                                           float* __restrict__ bnd, int T) {
+// (bid, grid): this tile's block among the scan's blocks.
+template <bool REV>
+__device__ __forceinline__ void gla_scan_tile(const uint16_t* __restrict__ X, uint8_t* __restrict__ ws,
+                                              const float* __restrict__ Sinit, float* __restrict__ Sout,
+                                              int T, int bid, int grid) {
   using namespace glab;
   __shared__ __attribute__((aligned(16))) uint16_t sx[C * PX];
   __shared__ __attribute__((aligned(16))) uint16_t sy[C * PT];
-  __shared__ __attribute__((aligned(16))) uint16_t sst[16 * PT];              // the tile in bf16
-  __shared__ __attribute__((aligned(16))) float ssa[BND ? 16 * (kD + 4) : 4];  // the state after the chunk
+  __shared__ __attribute__((aligned(16))) uint16_t sst[16 * PT];   // the tile in bf16
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, lq = lane >> 4;
   const int tr = tid >> 4, tc = 8 * (tid & 15);   // a thread's 8 entries of a [16][128] tile
   // block -> (sequence, value tile); the 8 tiles of one sequence share an XCD (blocks
   // are dealt to the 8 XCDs round robin), so the scaled keys or queries they all read
   // are fetched into that XCD's L2 once
-  const int bid = blockIdx.x;
   int n, vt;
-  if ((gridDim.x & 63) == 0) {
+  if ((grid & 63) == 0) {
     n = (bid >> 6) * 8 + (bid & 7);
     vt = (bid >> 3) & 7;
   } else {
@@ -185,20 +182,7 @@ __global__ __launch_bounds__(256) void gla_bwd_scan_kernel(const uint16_t* __res
       acc[j][i] = Sinit ? Sinit[((size_t)n * kD + v0 + 4 * lq + i) * kD + 32 * w + 16 * j + l16] : 0.f;
 
   // thread's pieces: X row tid / 4, values 4 (tid % 4) ..; Y 16-byte pieces tid + 256 p
-  // sa: this thread's 8 entries (row tr, columns tc ..) of the state after the chunk
-  auto load = [&](int ci, u32x2& xr, u32x4 (&yr)[4], float (&ec)[2], f32x4 (&sa)[2]) {
-    if constexpr (BND) {
-      const size_t e = (size_t)(v0 + tr) * kD + tc;
-      if (ci + 1 < nc) {
-        const u32x4 b = *reinterpret_cast<const u32x4*>(
-            reinterpret_cast<const uint16_t*>(ws + (chunk0 + ci + 1) * kChunkB + kSb) + e);
-        sa[0] = f32x4{__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xffff0000u), __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xffff0000u)};
-        sa[1] = f32x4{__uint_as_float(b.z << 16), __uint_as_float(b.z & 0xffff0000u), __uint_as_float(b.w << 16), __uint_as_float(b.w & 0xffff0000u)};
-      } else {
-        sa[0] = *reinterpret_cast<const f32x4*>(ST + (size_t)n * kD * kD + e);
-        sa[1] = *reinterpret_cast<const f32x4*>(ST + (size_t)n * kD * kD + e + 4);
-      }
-    }
+  auto load = [&](int ci, u32x2& xr, u32x4 (&yr)[4], float (&ec)[2]) {
     const size_t tok = (size_t)n * T + (size_t)ci * C;
     xr = *reinterpret_cast<const u32x2*>(X + (tok + (tid >> 2)) * kD + v0 + 4 * (tid & 3));
     const uint8_t* wsc = ws + (chunk0 + ci) * kChunkB;
@@ -210,8 +194,7 @@ __global__ __launch_bounds__(256) void gla_bwd_scan_kernel(const uint16_t* __res
   u32x2 xr;
   u32x4 yr[4];
   float ec[2];
-  f32x4 sa[2];
-  if (nc > 0) load(REV ? nc - 1 : 0, xr, yr, ec, sa);
+  if (nc > 0) load(REV ? nc - 1 : 0, xr, yr, ec);
   for (int s = 0; s < nc; ++s) {
     const int ci = REV ? nc - 1 - s : s;
     // this chunk's state (forward) or state gradient (reverse) in bf16, staged in LDS
@@ -220,10 +203,6 @@ __global__ __launch_bounds__(256) void gla_bwd_scan_kernel(const uint16_t* __res
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) sst[sw_off(4 * lq + i, 32 * w + 16 * j + l16)] = f32_to_bf16(acc[j][i]);
-    if constexpr (BND) {
-      *reinterpret_cast<f32x4*>(ssa + tr * (kD + 4) + tc) = sa[0];
-      *reinterpret_cast<f32x4*>(ssa + tr * (kD + 4) + tc + 4) = sa[1];
-    }
     *reinterpret_cast<u32x2*>(sx + px_off(tid >> 2, 4 * (tid & 3))) = xr;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -231,20 +210,10 @@ __global__ __launch_bounds__(256) void gla_bwd_scan_kernel(const uint16_t* __res
       *reinterpret_cast<u32x4*>(sy + sw_off(e >> 7, e & 127)) = yr[p];
     }
     const float e0 = ec[0], e1 = ec[1];
-    if (s + 1 < nc) load(REV ? ci - 1 : ci + 1, xr, yr, ec, sa);
+    if (s + 1 < nc) load(REV ? ci - 1 : ci + 1, xr, yr, ec);
     lds_barrier();
     *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(ws + (chunk0 + ci) * kChunkB + (REV ? kdS : kSb)) +
                               (size_t)(v0 + tr) * kD + tc) = *reinterpret_cast<const u32x4*>(sst + sw_off(tr, tc));
-    if constexpr (BND) {   // sum over this tile's 16 value rows of dS o S, per key channel
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const float* sp = ssa + (4 * lq) * (kD + 4) + 32 * w + 16 * j + l16;
-        float x = ((acc[j][0] * sp[0] + acc[j][1] * sp[kD + 4]) + (acc[j][2] * sp[2 * (kD + 4)] + acc[j][3] * sp[3 * (kD + 4)]));
-        x += __shfl_xor(x, 16);
-        x += __shfl_xor(x, 32);
-        if (lq == 0) bnd[((chunk0 + ci) * 8 + vt) * kD + 32 * w + 16 * j + l16] = x;
-      }
-    }
     acc[0] *= e0;
     acc[1] *= e1;
 #pragma unroll
@@ -255,10 +224,36 @@ __global__ __launch_bounds__(256) void gla_bwd_scan_kernel(const uint16_t* __res
     }
     lds_barrier();
   }
+  if (Sout)
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) Sout[((size_t)n * kD + v0 + 4 * lq + i) * kD + 32 * w + 16 * j + l16] = acc[j][i];
+      for (int i = 0; i < 4; ++i) Sout[((size_t)n * kD + v0 + 4 * lq + i) * kD + 32 * w + 16 * j + l16] = acc[j][i];
+}
+
+// The two state scans in one launch: the first half of the blocks runs the forward
+// scan's tiles (states before every chunk), the second half the backward scan's
+// (gradients after every chunk, and dS_0), tile for tile, so that a tile's XCD is the
+// same in both halves. Both are serial chains over the chunks at one block per tile.
+__global__ __launch_bounds__(256) void gla_bwd_scans_kernel(const uint16_t* __restrict__ v,
+                                                            const uint16_t* __restrict__ dO,
+                                                            uint8_t* __restrict__ ws,
+                                                            const float* __restrict__ S0,
+                                                            const float* __restrict__ dST,
+                                                            float* __restrict__ dS0, int T) {
+  const int grid = (int)gridDim.x >> 1, b = blockIdx.x;
+  if (b < grid)
+    gla_scan_tile<false>(v, ws, S0, nullptr, T, b, grid);
+  else
+    gla_scan_tile<true>(dO, ws, dST, dS0, T, b - grid, grid);
+}
+
+// The backward state scan alone (a shard's dS_0 from a zero gradient, or T = 0).
+__global__ __launch_bounds__(256) void gla_bwd_rscan_kernel(const uint16_t* __restrict__ dO,
+                                                            uint8_t* __restrict__ ws,
+                                                            const float* __restrict__ dST,
+                                                            float* __restrict__ dS0, int T) {
+  gla_scan_tile<true>(dO, ws, dST, dS0, T, blockIdx.x, gridDim.x);
 }
 
 // ------------------------------------------------------------------ gradients
@@ -267,12 +262,13 @@ struct alignas(16) GradSmem {
   uint16_t Qt[kChunk * glab::PT], Kt[kChunk * glab::PT], dO[kChunk * glab::PT];   // [t][128]
   uint16_t Sb[kD * glab::PT], dS[kD * glab::PT];                                 // [v][c]
   uint16_t A[kChunk * glab::PA], dA[kChunk * glab::PA];                          // [r][j], upper tiles zero
+  // per key channel: sum_v dS_a o S_b per wave, sum_t K~ o (V dS_a) per token block
+  float b1[8][kD], b2[4][kD];
 };
 
 __global__ __launch_bounds__(512) void gla_bwd_grad_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ dO, const uint8_t* __restrict__ ws, const float* __restrict__ bnd,
-    uint16_t* __restrict__ dq, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
+    const uint16_t* __restrict__ dO, const uint8_t* __restrict__ ws, uint16_t* __restrict__ dq, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
     float* __restrict__ dg, int T) {
   using namespace glab;
   __shared__ GradSmem sm;
@@ -302,12 +298,30 @@ __global__ __launch_bounds__(512) void gla_bwd_grad_kernel(
     *reinterpret_cast<u32x4*>(sm.Kt + sw_off(r, cc)) = kt;
     *reinterpret_cast<u32x4*>(sm.dO + sw_off(r, cc)) = *reinterpret_cast<const u32x4*>(dO + (tok0 + r) * kD + cc);
   }
+  // and this thread's part of sum_v dS_a o S_b for its 8 key channels 8 (tid % 16) ..
+  float b1[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int e = (tid + 512 * p) * 8, r = e >> 7, cc = e & 127;
-    *reinterpret_cast<u32x4*>(sm.Sb + sw_off(r, cc)) = *reinterpret_cast<const u32x4*>(wsc + kSb + (size_t)e * 2);
-    *reinterpret_cast<u32x4*>(sm.dS + sw_off(r, cc)) = *reinterpret_cast<const u32x4*>(wsc + kdS + (size_t)e * 2);
+    const u32x4 sb = *reinterpret_cast<const u32x4*>(wsc + kSb + (size_t)e * 2);
+    const u32x4 ds = *reinterpret_cast<const u32x4*>(wsc + kdS + (size_t)e * 2);
+    *reinterpret_cast<u32x4*>(sm.Sb + sw_off(r, cc)) = sb;
+    *reinterpret_cast<u32x4*>(sm.dS + sw_off(r, cc)) = ds;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      b1[2 * j] += lo_bf(sb[j]) * lo_bf(ds[j]);
+      b1[2 * j + 1] += hi_bf(sb[j]) * hi_bf(ds[j]);
+    }
   }
+  // the four lanes of a wave with these channels, then one row of partials per wave
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    b1[j] += __shfl_xor(b1[j], 16);
+    b1[j] += __shfl_xor(b1[j], 32);
+  }
+  if (lq == 0)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sm.b1[w][8 * l16 + j] = b1[j];
   for (int e = tid; e < C * PA / 2; e += 512) {
     reinterpret_cast<uint32_t*>(sm.A)[e] = 0u;
     reinterpret_cast<uint32_t*>(sm.dA)[e] = 0u;
@@ -366,6 +380,7 @@ __global__ __launch_bounds__(512) void gla_bwd_grad_kernel(
       }
     }
     const float emc = em[col], ecmc = ecm[col];
+    float b2 = 0.f;   // sum over this lane's 4 tokens of K~ o (V dS_a); K^ = K~ e^{b_C - b_m}
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = 16 * rb + 4 * lq + i;
@@ -377,15 +392,19 @@ __global__ __launch_bounds__(512) void gla_bwd_grad_kernel(
       dk[g] = f32_to_bf16(gk);
       dv[g] = f32_to_bf16(dV[i]);
       const float x = bf16_to_f32(q[g]) * gq - bf16_to_f32(k[g]) * gk;
+      b2 += bf16_to_f32(sm.Kt[sw_off(t, col)]) * dKh[i];
 #pragma unroll
       for (int uu = 0; uu < 4; ++uu)   // constant register index under the rolled tile loop
         if (uu == u) dB[uu][i] = x;
     }
+    b2 += __shfl_xor(b2, 16);
+    b2 += __shfl_xor(b2, 32);
+    if (lq == 0) sm.b2[rb][col] = b2 * ecmc;
   }
 
   // ---- d log_g: the reverse cumulative sum of dL/dB over the chunk's tokens (fp32
   // [64][132] over the state tiles, 16-token segment totals over A) plus the chunk's
-  // sum_v dS_a o S_a (eight value-tile parts)
+  // sum_v dS_a o S_a = e^{b_C} sum_v dS_a o S_b + sum_t K^ o (V dS_a)
   constexpr int PG = kD + 4;
   float* G = reinterpret_cast<float*>(sm.Sb);
   float* seg = reinterpret_cast<float*>(sm.A);   // [4][128] segment totals
@@ -395,9 +414,15 @@ __global__ __launch_bounds__(512) void gla_bwd_grad_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) G[(16 * rb + 4 * lq + i) * PG + 16 * ((w >> 2) * 4 + u) + l16] = dB[u][i];
   const int c = tid & (kD - 1), h = tid >> 7;
-  float start = 0.f;
+  float start;
+  {
+    float s1 = 0.f, s2 = 0.f;
 #pragma unroll
-  for (int p = 0; p < 8; ++p) start += bnd[((size_t)cid * 8 + p) * kD + c];
+    for (int i = 0; i < 8; ++i) s1 += sm.b1[i][c];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s2 += sm.b2[i][c];
+    start = reinterpret_cast<const float*>(wsc + kEC)[c] * s1 + s2;
+  }
   lds_barrier();
   float run = 0.f, x[16];
 #pragma unroll
@@ -420,9 +445,8 @@ using namespace gdnrt;
 
 extern "C" size_t gla_chunk_bwd_workspace_bytes(int N, int T, int dk, int dv, int chunk) {
   if (N <= 0 || T <= 0 || dk != kD || dv != kD || chunk != kChunk || T % kChunk) return 0;
-  // per chunk the operands and states, then per sequence the recomputed final state,
-  // then per chunk sum_v dS_a o S_a by value tile
-  return (size_t)N * (T / kChunk) * (glab::kChunkB + 8 * kD * 4) + (size_t)N * kD * kD * 4;
+  // per chunk the operands and states
+  return (size_t)N * (T / kChunk) * glab::kChunkB;
 }
 
 // prepared: the per-chunk operands are already in the workspace (gla_shard_bwd_state
@@ -436,13 +460,14 @@ static int chunk_bwd(const char* fn, bool prepared, const void* q, const void* k
   if (chunk != kChunk) return set_error(GDNRT_ESHAPE, "%s: chunk=%d, only 64 is supported", fn, chunk);
   if (T % kChunk) return set_error(GDNRT_ESHAPE, "%s: T=%d is not a multiple of 64", fn, T);
   if (io != GDNRT_BF16) return set_error(GDNRT_EDTYPE, "%s: io must be GDNRT_BF16", fn);
-  if ((size_t)N * (T / kChunk) > 0x7fffffffu) return set_error(GDNRT_ESHAPE, "%s: N=%d T=%d too large", fn, N, T);
+  if ((size_t)N * (T / kChunk) > 0x7fffffffu || (size_t)N * 16 > 0x7fffffffu)
+    return set_error(GDNRT_ESHAPE, "%s: N=%d T=%d too large", fn, N, T);
   if (N == 0) return clear_error();
   if (!dS0 || (T > 0 && (!q || !k || !v || !log_g || !dO || !dq || !dk || !dv || !dlog_g)))
     return set_error(GDNRT_EINVAL, "%s: null pointer argument", fn);
   const size_t nchunks = (size_t)N * (T / kChunk);
-  const size_t need = nchunks * (glab::kChunkB + 8 * kD * 4) + (size_t)N * kD * kD * 4;
-  if (ws_bytes < need || !workspace)
+  const size_t need = nchunks * glab::kChunkB;
+  if (ws_bytes < need || (need && !workspace))
     return set_error(GDNRT_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
   if ((T > 0 && (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned16(log_g) ||
                  !aligned4(dq) || !aligned4(dk) || !aligned4(dv) || !aligned4(dlog_g))) ||
@@ -468,25 +493,24 @@ static int chunk_bwd(const char* fn, bool prepared, const void* q, const void* k
     return set_error(GDNRT_EINVAL, "%s: buffers overlap", fn);
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  float* ST = reinterpret_cast<float*>(ws + nchunks * glab::kChunkB);   // recomputed final states
-  float* bnd = ST + (size_t)N * kD * kD;                                // per chunk, sum_v dS_a o S_a
-  if (T > 0 && !prepared) {
+  if (T == 0) {   // no tokens: the state gradient passes through
+    hipLaunchKernelGGL(gla_bwd_rscan_kernel, dim3((unsigned)(N * 8)), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(dO), ws, dST, dS0, 0);
+    return check_launch(fn);
+  }
+  if (!prepared) {
     hipLaunchKernelGGL(gla_bwd_prep_kernel, dim3((unsigned)nchunks), dim3(256), 0, s,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), log_g, ws, T);
     int rc = check_launch(fn);
     if (rc != GDNRT_OK) return rc;
   }
-  hipLaunchKernelGGL(gla_bwd_scan_kernel<false>, dim3((unsigned)(N * 8)), dim3(256), 0, s,
-                     static_cast<const uint16_t*>(v), ws, S0, ST, nullptr, nullptr, T);
-  hipLaunchKernelGGL(gla_bwd_scan_kernel<true>, dim3((unsigned)(N * 8)), dim3(256), 0, s,
-                     static_cast<const uint16_t*>(dO), ws, dST, dS0, ST, bnd, T);
-  if (T > 0) {
-    hipLaunchKernelGGL(gla_bwd_grad_kernel, dim3((unsigned)nchunks), dim3(512), 0, s,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dO), ws, bnd,
-                       static_cast<uint16_t*>(dq), static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv),
-                       dlog_g, T);
-  }
+  hipLaunchKernelGGL(gla_bwd_scans_kernel, dim3((unsigned)(N * 16)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dO), ws, S0, dST, dS0, T);
+  hipLaunchKernelGGL(gla_bwd_grad_kernel, dim3((unsigned)nchunks), dim3(512), 0, s,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dO), ws,
+                     static_cast<uint16_t*>(dq), static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv),
+                     dlog_g, T);
   return check_launch(fn);
 }
 
@@ -540,8 +564,8 @@ extern "C" int gla_shard_bwd_state(const void* q, const void* k, const float* lo
     int rc = check_launch(fn);
     if (rc != GDNRT_OK) return rc;
   }
-  // the reverse scan from a zero gradient, without the boundary sums (no forward states)
-  hipLaunchKernelGGL((gla_bwd_scan_kernel<true, false>), dim3((unsigned)(N * 8)), dim3(256), 0, s,
-                     static_cast<const uint16_t*>(dO), ws, nullptr, dS0, nullptr, nullptr, T);
+  // the reverse scan from a zero gradient
+  hipLaunchKernelGGL(gla_bwd_rscan_kernel, dim3((unsigned)(N * 8)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(dO), ws, nullptr, dS0, T);
   return check_launch(fn);
 }

@@ -186,8 +186,7 @@ GDNRT_API int gla_shard_output_correct(const void* workspace, size_t ws_bytes, c
  *   q, k, v, dO [N][T][d] bf16 and log_g fp32: 16-byte aligned. S0, dST may be NULL
  *   (zero). workspace: gla_chunk_bwd_workspace_bytes() bytes, 16-byte aligned,
  *   overwritten (per chunk the scaled operands, the state before the chunk and the
- *   state gradient after it, in bf16, and sum_v dS o S by value tile: 136,704 bytes; per
- *   sequence the recomputed final state).
+ *   state gradient after it, in bf16: 132,608 bytes). May be NULL when T = 0.
  * The gate gradient is the reverse cumulative sum of q o dq - k o dk (plus dST o S_T
  * summed over value channels at the last token). T must be a multiple of 64.
  */

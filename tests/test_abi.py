@@ -218,7 +218,7 @@ def test_kda_chunk_validation(lib):
 def test_gla_bwd_validation(lib):
     p = ctypes.c_void_p(4096)
     f = lib.gla_chunk_bwd
-    assert lib.gla_chunk_bwd_workspace_bytes(64, 4096, 128, 128, 64) == 64 * 64 * (132608 + 4096) + 64 * 65536
+    assert lib.gla_chunk_bwd_workspace_bytes(64, 4096, 128, 128, 64) == 64 * 64 * 132608
     assert lib.gla_chunk_bwd_workspace_bytes(64, 100, 128, 128, 64) == 0
     args = lambda T, ws_bytes, **kw: [kw.get(n, p) for n in ("q", "k", "v", "g", "S0", "dO", "dST", "dq", "dk",
                                                           "dv", "dg", "dS0")] + [2, T, 128, 128, 64, 1, p,
