@@ -223,6 +223,8 @@ __device__ __forceinline__ void rscan_tile(const uint8_t* __restrict__ prep, con
   // fragment f = w + 4 p of each 16-fragment operand, this lane's 16 bytes
   auto load = [&](int ci, Ops& o) {
     const uint8_t* pc = prep + (chunk0 + ci) * kWsChunk;
+    o.gc = *reinterpret_cast<const float*>(pc + kWsG + l16 * 4);
+    o.o = *reinterpret_cast<const u32x2*>(dO + ((size_t)n * T + (size_t)ci * C + (tid >> 2)) * kD + v0 + 4 * (tid & 3));
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const size_t off = ((size_t)(w + 4 * p) * 64 + lane) * 16;
@@ -230,15 +232,12 @@ __device__ __forceinline__ void rscan_tile(const uint8_t* __restrict__ prep, con
       o.qp[p] = *reinterpret_cast<const u32x4*>(pc + kWsQ + off);
       o.w[p] = *reinterpret_cast<const u32x4*>(pc + kWsW + off);
     }
-    o.o = *reinterpret_cast<const u32x2*>(dO + ((size_t)n * T + (size_t)ci * C + (tid >> 2)) * kD + v0 + 4 * (tid & 3));
-    o.gc = *reinterpret_cast<const float*>(pc + kWsG + l16 * 4);
   };
   Ops cur, nxt;
   if (nc > 0) load(nc - 1, nxt);
   for (int s = 0; s < nc; ++s) {
     const int ci = nc - 1 - s;
     cur = nxt;
-    if (s + 1 < nc) load(ci - 1, nxt);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -258,9 +257,13 @@ __device__ __forceinline__ void rscan_tile(const uint8_t* __restrict__ prep, con
     }
     *reinterpret_cast<u32x2*>(sO + px_off(tid >> 2, 4 * (tid & 3))) = cur.o;
     lds_barrier();
-    // the tile's bf16 copy to the workspace, one 16-byte store per thread
+    // the tile's bf16 copy to the workspace, one 16-byte store per thread; then the
+    // previous chunk's operands are requested (every chunk issues the same loads, the
+    // last one chunk 0 again): the waits for them then never include this store
     *reinterpret_cast<u32x4*>(dSa + (chunk0 + ci) * kD * kD + (size_t)(v0 + tr) * kD + tc) =
         *reinterpret_cast<const u32x4*>(sD + sw_off(tr, tc));
+    __builtin_amdgcn_sched_barrier(0);   // keeps the loads after the store
+    load(ci > 0 ? ci - 1 : 0, nxt);
     // -(K^ dS^T)^T for tokens 16 w .. 16 w + 15: [v][t]
     f32x4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
