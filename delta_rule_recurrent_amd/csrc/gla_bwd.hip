@@ -182,20 +182,27 @@ __device__ __forceinline__ void gla_scan_tile(const uint16_t* __restrict__ X, ui
       acc[j][i] = Sinit ? Sinit[((size_t)n * kD + v0 + 4 * lq + i) * kD + 32 * w + 16 * j + l16] : 0.f;
 
   // thread's pieces: X row tid / 4, values 4 (tid % 4) ..; Y 16-byte pieces tid + 256 p
-  auto load = [&](int ci, u32x2& xr, u32x4 (&yr)[4], float (&ec)[2]) {
+  struct Ops {
+    u32x2 xr;
+    u32x4 yr[4];
+    float ec[2];
+  };
+  auto load = [&](int ci, Ops& o) {
     const size_t tok = (size_t)n * T + (size_t)ci * C;
-    xr = *reinterpret_cast<const u32x2*>(X + (tok + (tid >> 2)) * kD + v0 + 4 * (tid & 3));
+    o.xr = *reinterpret_cast<const u32x2*>(X + (tok + (tid >> 2)) * kD + v0 + 4 * (tid & 3));
     const uint8_t* wsc = ws + (chunk0 + ci) * kChunkB;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) yr[p] = *reinterpret_cast<const u32x4*>(wsc + soff + (size_t)(tid + 256 * p) * 16);
+    for (int p = 0; p < 4; ++p) o.yr[p] = *reinterpret_cast<const u32x4*>(wsc + soff + (size_t)(tid + 256 * p) * 16);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) ec[j] = reinterpret_cast<const float*>(wsc + kEC)[32 * w + 16 * j + l16];
+    for (int j = 0; j < 2; ++j) o.ec[j] = reinterpret_cast<const float*>(wsc + kEC)[32 * w + 16 * j + l16];
   };
-  u32x2 xr;
-  u32x4 yr[4];
-  float ec[2];
-  if (nc > 0) load(REV ? nc - 1 : 0, xr, yr, ec);
-  for (int s = 0; s < nc; ++s) {
+  // chunk s from `cur`, requesting the next chunk's operands into `nxt` (past the end the
+  // last chunk's again, so that every chunk issues the same loads and the waits count
+  // exactly); the two sets alternate through a loop unrolled by two, so neither is
+  // copied into the other (a copy would wait for the loads in the chunk that issued
+  // them), and the first chunk is peeled, so that the loop is entered with the same
+  // operations in flight on both paths (the next set's loads, then a store)
+  auto body = [&](int s, const Ops& cur, Ops& nxt) {
     const int ci = REV ? nc - 1 - s : s;
     // this chunk's state (forward) or state gradient (reverse) in bf16, staged in LDS
     // and stored after the barrier one 16-byte piece per thread
@@ -203,19 +210,18 @@ __device__ __forceinline__ void gla_scan_tile(const uint16_t* __restrict__ X, ui
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) sst[sw_off(4 * lq + i, 32 * w + 16 * j + l16)] = f32_to_bf16(acc[j][i]);
-    *reinterpret_cast<u32x2*>(sx + px_off(tid >> 2, 4 * (tid & 3))) = xr;
+    *reinterpret_cast<u32x2*>(sx + px_off(tid >> 2, 4 * (tid & 3))) = cur.xr;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int e = (tid + 256 * p) * 8;   // element index in [64][128]
-      *reinterpret_cast<u32x4*>(sy + sw_off(e >> 7, e & 127)) = yr[p];
+      *reinterpret_cast<u32x4*>(sy + sw_off(e >> 7, e & 127)) = cur.yr[p];
     }
-    const float e0 = ec[0], e1 = ec[1];
-    if (s + 1 < nc) load(REV ? ci - 1 : ci + 1, xr, yr, ec);
+    load(REV ? (ci > 0 ? ci - 1 : 0) : (ci + 1 < nc ? ci + 1 : ci), nxt);
     lds_barrier();
     *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(ws + (chunk0 + ci) * kChunkB + (REV ? kdS : kSb)) +
                               (size_t)(v0 + tr) * kD + tc) = *reinterpret_cast<const u32x4*>(sst + sw_off(tr, tc));
-    acc[0] *= e0;
-    acc[1] *= e1;
+    acc[0] *= cur.ec[0];
+    acc[1] *= cur.ec[1];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const bf16x8 a = ld_tr8x(sx, 32 * ks);
@@ -223,6 +229,17 @@ __device__ __forceinline__ void gla_scan_tile(const uint16_t* __restrict__ X, ui
       for (int j = 0; j < 2; ++j) acc[j] = mfma(a, ld_tr8s(sy, 32 * ks, 32 * w + 16 * j), acc[j]);
     }
     lds_barrier();
+  };
+  if (nc > 0) {
+    Ops A, B;
+    load(REV ? nc - 1 : 0, A);
+    body(0, A, B);
+    int s = 1;
+    for (; s + 2 <= nc; s += 2) {
+      body(s, B, A);
+      body(s + 1, A, B);
+    }
+    if (s < nc) body(s, B, A);
   }
   if (Sout)
 #pragma unroll
