@@ -95,7 +95,8 @@ struct Ws {
   uint16_t* Sb;    // state before the chunk, bf16 [128][128]
   uint16_t* dSa;   // state gradient after the chunk, bf16 [128][128]
   uint16_t* dU;    // dU, bf16 [64][128]
-  float* dK1;      // dA'^T Q + diag(g_C/g) U dS_a, fp32 [64][128]
+  u32x2* dK1;      // dA'^T Q + diag(g_C/g) U dS_a, bf16 in the gradient kernels' lane order:
+                   // piece (wave, u, lane) holds the lane's 4 rows of tile (w % 4, 4 (w / 4) + u)
   float* qdq;      // q_t . dq_t, fp32 [64]
   float* bnd;      // sum(dS_a o S_a), fp32, one per chunk
 };
@@ -495,7 +496,7 @@ __global__ __launch_bounds__(512) void gdn_bwd_grad1_kernel(
     lds_barrier();
 
     // ---- dq = dA' K + diag(g) dO S_b;  dK1 = dA'^T Q + diag(g_C/g) U dS_a
-    float* dK1 = ws.dK1 + (size_t)cid * C * kD;
+    u32x2* dK1 = ws.dK1 + (size_t)cid * (C * kD / 4);
     float qacc[4] = {0.f, 0.f, 0.f, 0.f};   // this lane's share of q.dq over its 4 key blocks
     float bs2 = 0.f;                         // this lane's part of sum(diag(g_C/g) U dS_a o K)
 #pragma unroll 1
@@ -515,16 +516,18 @@ __global__ __launch_bounds__(512) void gdn_bwd_grad1_kernel(
         a4 = mfma(ld8(sm.U + sw_off(16 * rb + l16, 32 * ks + 8 * lq)), ld_tr8s(sm.D, 32 * ks, 16 * kb), a4);
       }
       const int col = 16 * kb + l16;
+      float k1[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rb + 4 * lq + i;
         const float gq = a1[i] + sm.g[r] * a2[i];
         dq[(tok0 + r) * kD + col] = f32_to_bf16(gq);
         const float ud = sm.kd[r] * a4[i];
-        dK1[r * kD + col] = a3[i] + ud;
+        k1[i] = a3[i] + ud;
         qacc[i] += bf16_to_f32(sm.Q[sw_off(r, col)]) * gq;
         bs2 += ud * bf16_to_f32(sm.K[sw_off(r, col)]);
       }
+      dK1[(w * 4 + u) * 64 + lane] = u32x2{pack_bf16(k1[0], k1[1]), pack_bf16(k1[2], k1[3])};
     }
     // fixed summation order (no atomics): the 16 lanes of a row, then each half of the
     // waves writes its own partial
@@ -712,7 +715,7 @@ __global__ __launch_bounds__(512) void gdn_bwd_grad2_kernel(
     // next chunk's inputs (the last chunk of a block loads itself again)
     u32x4 wfr[2][4];
     float k1[4][4];
-    const float* dK1 = ws.dK1 + (size_t)cid * C * kD;
+    const u32x2* dK1 = ws.dK1 + (size_t)cid * (C * kD / 4);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       int ab, cb;
@@ -722,9 +725,13 @@ __global__ __launch_bounds__(512) void gdn_bwd_grad2_kernel(
         wfr[h][ks] = *reinterpret_cast<const u32x4*>(pc + kWsW + ((size_t)(cb * 4 + ks) * 64 + lane) * 16);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) k1[u][i] = dK1[(16 * rb + 4 * lq + i) * kD + 16 * ((w >> 2) * 4 + u) + l16];
+    for (int u = 0; u < 4; ++u) {
+      const u32x2 pk = dK1[(w * 4 + u) * 64 + lane];   // rows 16 rb + 4 lq + i of column block 4 (w / 4) + u
+      k1[u][0] = lo_bf(pk.x);
+      k1[u][1] = hi_bf(pk.x);
+      k1[u][2] = lo_bf(pk.y);
+      k1[u][3] = hi_bf(pk.y);
+    }
     g2_fetch(in, k, v, alpha, beta, ws, cid + (int)gridDim.x < nchunks ? cid + (int)gridDim.x : cid, T);
     lds_barrier();
 
@@ -809,7 +816,7 @@ BwdLayout bwd_layout(size_t N, size_t nchunks) {
   L.dSa = L.Sb + nchunks * kD * kD * 2;
   L.dU = L.dSa + nchunks * kD * kD * 2;
   L.dK1 = L.dU + nchunks * kChunk * kD * 2;
-  L.qdq = L.dK1 + nchunks * kChunk * kD * 4;
+  L.qdq = L.dK1 + nchunks * kChunk * kD * 2;
   L.bnd = L.qdq + nchunks * kChunk * 4;
   L.total = L.bnd + nchunks * 4;
   return L;
@@ -873,7 +880,7 @@ extern "C" int gdn_chunk_bwd(const void* q, const void* k, const void* v, const 
   ws.Sb = reinterpret_cast<uint16_t*>(base + lay.Sb);
   ws.dSa = reinterpret_cast<uint16_t*>(base + lay.dSa);
   ws.dU = reinterpret_cast<uint16_t*>(base + lay.dU);
-  ws.dK1 = reinterpret_cast<float*>(base + lay.dK1);
+  ws.dK1 = reinterpret_cast<gdc::u32x2*>(base + lay.dK1);
   ws.qdq = reinterpret_cast<float*>(base + lay.qdq);
   ws.bnd = reinterpret_cast<float*>(base + lay.bnd);
   const uint16_t* q16 = static_cast<const uint16_t*>(q);

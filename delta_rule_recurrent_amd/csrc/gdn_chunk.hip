@@ -660,8 +660,9 @@ __device__ __forceinline__ void prep2_chunk(Prep2Smem& sm, PrepIn<false>& in, in
                 pack_bf16(gr * lo_bf(qa.y) - acc[2], gr * hi_bf(qa.y) - acc[3])};
     }
   }
-  // ---- O~ = A U~ tiles (rb, vb = wave), with the U~ tiles as B operands
-  {
+  // ---- O~ = A U~ tiles (rb, vb = wave), with the U~ tiles as B operands (the forward's
+  // outputs only: the backward, STORE_T, reads no O~)
+  if constexpr (!STORE_T) {
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};

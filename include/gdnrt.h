@@ -297,8 +297,8 @@ GDNRT_API size_t gdn_chunk_fwd_noalloc_max_bytes(void);
  *   S0, dST [N][dv][dk] fp32 or NULL (zero). Outputs must not overlap inputs.
  *   workspace: gdn_chunk_bwd_workspace_bytes() bytes, 16-byte aligned, overwritten
  *   (per chunk the forward's operands, (I + L)^-1, the state before the chunk and the
- *   state gradient after it in bf16, dU, a partial dk, q.dq and the chunk's
- *   sum(dS o S): 205,124 bytes). May be NULL when T = 0.
+ *   state gradient after it, dU and a partial dk in bf16, q.dq and the chunk's
+ *   sum(dS o S): 188,740 bytes). May be NULL when T = 0.
  * T must be a multiple of 64 (chunk).
  */
 GDNRT_API int gdn_chunk_bwd(const void* q, const void* k, const void* v,

@@ -233,7 +233,7 @@ def test_gla_bwd_validation(lib):
 def test_gdn_bwd_validation(lib):
     p = ctypes.c_void_p(4096)
     f = lib.gdn_chunk_bwd
-    per_chunk = 81984 + 8192 + 2 * 32768 + 16384 + 32768 + 256 + 4
+    per_chunk = 81984 + 8192 + 2 * 32768 + 16384 + 16384 + 256 + 4
     assert lib.gdn_chunk_bwd_workspace_bytes(32, 16384, 128, 128, 64) == 32 * 256 * per_chunk
     assert lib.gdn_chunk_bwd_workspace_bytes(32, 100, 128, 128, 64) == 0
     names = ("q", "k", "v", "a", "b", "S0", "dO", "dST", "dq", "dk", "dv", "da", "db", "dS0")
