@@ -10,7 +10,12 @@ stream-tokens per second over K timed steps. The other rows of the hot path are
 measured in the same run and reported under "rows".
 
 Timing: W untimed warm-up steps, then K steps bracketed by synchronisation;
-HIP events recorded on the stream the kernels run on give the per-launch time.
+HIP events recorded on the stream the kernels run on give the per-launch time. The
+prefill and backward rows take warm-up calls of their own on the buffers they then time:
+10, and 30 for the GDN and KDA chunk calls, which reach their steady time only after some
+tens of calls on fresh buffers (GDN: 540-555 us per call after 2 warm-up calls, 492 after
+10, 474 after 30). The CPU baseline runs after every GPU row, so that no row follows the
+tens of seconds the GPU idles meanwhile.
 The CPU baseline times the fp64 oracle on a bounded sample of heads.
 """
 from __future__ import annotations
@@ -340,7 +345,7 @@ def gla_chunk_work(C=64):
     return alg, dense
 
 
-def bench_gla(K=20, W=3, B=4, H=16, T=4096):
+def bench_gla(K=20, W=10, B=4, H=16, T=4096):
     N = B * H
     log(f"[gla] generating B={B} H={H} T={T}")
     inp = synth.gla_prefill(B=B, H=H, T=T, device="cuda")
@@ -370,7 +375,7 @@ def bench_gla(K=20, W=3, B=4, H=16, T=4096):
     return res
 
 
-def bench_zeco(K=20, W=3, B=4, H=16, T=4096, blocks=4):
+def bench_zeco(K=20, W=10, B=4, H=16, T=4096, blocks=4):
     """The per-device work that ZeCO's sequence parallelism adds to a GLA prefill
     shard (one device's share at the prefill shape, receiving the workload's
     incoming state): the cumulative decays after the local forward, one All-Scan
@@ -453,7 +458,7 @@ def gla_bwd_work(C=64):
     return 2 * full + (2 * low + full + 2 * low + full + low + full)
 
 
-def bench_gla_bwd(K=10, W=2, B=4, H=16, T=4096):
+def bench_gla_bwd(K=10, W=10, B=4, H=16, T=4096):
     N = B * H
     log(f"[gla_bwd] generating B={B} H={H} T={T}")
     inp = synth.gla_prefill(B=B, H=H, T=T, device="cuda")
@@ -500,7 +505,7 @@ def gdn_bwd_work(C=64):
     return fwd_ops + scans + grad1 + grad2
 
 
-def bench_gdn_bwd(K=10, W=2, B=1, H=32, T=16384):
+def bench_gdn_bwd(K=10, W=10, B=1, H=32, T=16384):
     N = B * H
     log(f"[gdn_bwd] generating B={B} H={H} T={T}")
     inp = synth.gdn_prefill(B=B, H=H, T=T, device="cuda")
@@ -542,7 +547,7 @@ def gdn_chunk_work(C=64):
     return alg, dense
 
 
-def bench_gdn_chunk(K=10, W=2, B=1, H=32, T=16384, kda=False):
+def bench_gdn_chunk(K=10, W=30, B=1, H=32, T=16384, kda=False):
     """Chunkwise prefill of the Gated DeltaNet workload; with ``kda`` the same shape
     with one decay per key channel and token (kda_chunk_fwd). The FLOP count is the
     GDN one (the per-channel decays only rescale operands)."""
@@ -664,7 +669,7 @@ def main():
     m.lib()
     rows = [r.strip() for r in args.rows.split(",") if r.strip()]
     out_rows = {}
-    res, cpu = None, None
+    res, cpu, decode_inp = None, None, None
     if "decode" in rows:
         res, inp = bench_decode(args.steps, args.warmup)
         log(f"[decode] {res['ms_per_step']*1e3:.1f} us/step  {res['achieved_gbs']:.0f} GB/s  "
@@ -678,9 +683,8 @@ def main():
                 dst.copy_(src)
             torch.cuda.synchronize()
             del src, dst
-        if not args.no_cpu_baseline:
-            log("[cpu] timing the oracle on a sample")
-            cpu = cpu_baseline_decode(inp)
+        # the oracle runs on the CPU after the GPU rows (the GPU would idle meanwhile)
+        decode_inp = None if args.no_cpu_baseline else inp
         del inp
         torch.cuda.empty_cache()
     for bits, key in ((16, "bf16_state"), (8, "int8_state")):
@@ -785,6 +789,11 @@ def main():
             f"{r['tokens_per_s']/1e6:.3f} M tok/s")
         torch.cuda.empty_cache()
     ceil = None
+    if decode_inp is not None:
+        log("[cpu] timing the oracle on a sample")
+        cpu = cpu_baseline_decode(decode_inp)
+        del decode_inp
+        torch.cuda.empty_cache()
     if not args.no_ceilings:
         ceil = measure_ceilings()
         log(f"[ceilings] HBM stream {ceil['hbm_stream_gbs']:.0f} GB/s ({ceil['hbm_stream_best']}), "
