@@ -570,14 +570,25 @@ __device__ __forceinline__ double lane64(double x, int L) {
   const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), L);
   return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
-// sum over the 64 lanes of a wave, fp64: within rows of 16 by DPP, then the four
-// row totals (wave-uniform)
+// DPP move of an fp64 value with a row mask: rows outside ROWS read zero
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp64_rows(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, ROWS, 0xF, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, ROWS, 0xF, false);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+// sum over the 64 lanes of a wave, fp64 (wave-uniform): within rows of 16 by DPP (every
+// lane then holds its row's total), rows 1 and 3 add the totals of rows 0 and 2
+// (row_bcast:15), rows 2 and 3 that of rows 0-1 (row_bcast:31); lane 63 holds the sum
 __device__ __forceinline__ double wave_sum_f64(double x) {
   x += dpp64<0x140>(x);
   x += dpp64<0x141>(x);
   x += dpp64<0x4E>(x);
   x += dpp64<0xB1>(x);
-  return (lane64(x, 0) + lane64(x, 16)) + (lane64(x, 32) + lane64(x, 48));
+  x += dpp64_rows<0x142, 0xA>(x);
+  x += dpp64_rows<0x143, 0xC>(x);
+  return lane64(x, 63);
 }
 
 // CholeskyQR2 of a 128 x RANK block held by one wave, rows lane and lane + 64:
@@ -607,9 +618,14 @@ __device__ __forceinline__ void cholqr2_wave(float (&x)[2][RANK]) {
 #pragma unroll
         for (int p = 0; p < j; ++p) s -= L[i * (i + 1) / 2 + p] * L[j * (j + 1) / 2 + p];
         if (i == j) {
-          const double d = sqrt(fmax(s, 0.0));
-          L[i * (i + 1) / 2 + i] = d;
-          rd[i] = 1.0 / d;
+          // 1 / sqrt(s) from the hardware estimate and two Newton steps (each squares
+          // the relative error), instead of a square root and a division
+          double r = __builtin_amdgcn_rsq(s);
+          r = r * (1.5 - 0.5 * s * r * r);
+          r = r * (1.5 - 0.5 * s * r * r);
+          const bool pos = s > 0.0;
+          L[i * (i + 1) / 2 + i] = pos ? s * r : 0.0;
+          rd[i] = pos ? r : __builtin_inf();
         } else {
           L[i * (i + 1) / 2 + j] = s * rd[j];
         }
