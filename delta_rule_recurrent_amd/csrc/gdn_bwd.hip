@@ -372,8 +372,10 @@ __global__ __launch_bounds__(512) void gdn_bwd_grad1_kernel(
   const int nc = T / C;
   G1In in;
   g1_fetch(in, q, k, dO, alpha, ws, blockIdx.x, T);   // the grid never exceeds nchunks
-#pragma unroll 1
-  for (int cid = blockIdx.x; cid < nchunks; cid += gridDim.x) {
+  // the first chunk is peeled, so that the loop is entered with the same memory
+  // operations in flight on both paths (the next chunk's loads, then this chunk's
+  // stores) and the waits for the prefetched inputs never include the stores
+  auto chunk = [&](const int cid) {
     // the thread index through an opaque move: the per-lane addresses are formed inside
     // each chunk instead of being held across the loop
     int tid;
@@ -554,7 +556,10 @@ __global__ __launch_bounds__(512) void gdn_bwd_grad1_kernel(
       }
       ws.bnd[cid] = sm.g[C - 1] * b1 + b2;
     }
-  }
+  };
+  chunk(blockIdx.x);
+#pragma unroll 1
+  for (int cid = blockIdx.x + gridDim.x; cid < nchunks; cid += gridDim.x) chunk(cid);
 }
 
 // ------------------------------------------------------------------ gradients, part 2
@@ -620,8 +625,10 @@ __global__ __launch_bounds__(512) void gdn_bwd_grad2_kernel(
   uint16_t* XU = sm.S + C * PT;    // T^T dU
   G2In in;
   g2_fetch(in, k, v, alpha, beta, ws, blockIdx.x, T);   // the grid never exceeds nchunks
-#pragma unroll 1
-  for (int cid = blockIdx.x; cid < nchunks; cid += gridDim.x) {
+  // the first chunk is peeled, so that the loop is entered with the same memory
+  // operations in flight on both paths (the next chunk's loads, then this chunk's
+  // stores) and the waits for the prefetched inputs never include the stores
+  auto chunk = [&](const int cid) {
     // the thread index through an opaque move (per-lane addresses formed per chunk)
     int tid;
     asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"((int)threadIdx.x));
@@ -795,7 +802,10 @@ __global__ __launch_bounds__(512) void gdn_bwd_grad2_kernel(
       const float rs = wave_scan(__shfl(dB, C - 1 - lane));
       dalpha[tok0 + t] = (__shfl(rs, C - 1 - t) + off) / alpha[tok0 + t];
     }
-  }
+  };
+  chunk(blockIdx.x);
+#pragma unroll 1
+  for (int cid = blockIdx.x + gridDim.x; cid < nchunks; cid += gridDim.x) chunk(cid);
 }
 
 }  // namespace gdnrt
