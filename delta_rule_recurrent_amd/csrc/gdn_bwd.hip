@@ -298,7 +298,8 @@ __device__ __forceinline__ void rscan_tile(const uint8_t* __restrict__ prep, con
 // serial chains over the chunks at one block per tile. Measured on MI355X: with the
 // halves interleaved every 8 blocks (so that a CU's two blocks took the same scan)
 // the launch took 687 us at 32 x 16,384 tokens, with the halves 629 us, against
-// 258 + 490 us as two launches.
+// 258 + 490 us as two launches; with the backward scan's waves at a higher issue
+// priority (s_setprio) 531 us.
 __global__ __launch_bounds__(256) void gdn_bwd_scans_kernel(const uint8_t* __restrict__ prep,
                                                             const float* __restrict__ S0,
                                                             uint16_t* __restrict__ Sb,
@@ -307,10 +308,14 @@ __global__ __launch_bounds__(256) void gdn_bwd_scans_kernel(const uint8_t* __res
                                                             uint16_t* __restrict__ dSa,
                                                             float* __restrict__ dS0, int T) {
   const int grid = (int)gridDim.x >> 1, b = blockIdx.x, tile = b < grid ? b : b - grid;
-  if (b < grid)
+  if (b < grid) {
     fscan_tile(prep, S0, Sb, T, tile, grid);
-  else
+  } else {
+    // the backward scan is the longer chain (about 490 against 258 us alone at 32 x
+    // 16,384 tokens): its waves issue first, the forward scan's fill in around them
+    __builtin_amdgcn_s_setprio(2);
     rscan_tile(prep, dO, dST, dSa, dS0, T, tile, grid);
+  }
 }
 
 // T = 0: the state gradient passes through (dS0 = dST, or zero)
