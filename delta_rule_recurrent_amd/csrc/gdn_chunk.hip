@@ -98,6 +98,25 @@ __device__ __forceinline__ void prep_fetch(PrepIn<KDA>& in, const uint16_t* __re
   in.be = beta[tok0 + (tid & 63)];
 }
 
+// A use of every input request of a block's last chunk at the end of the kernel. Those
+// requests (the last chunk loads itself again) are otherwise dead on the way out, and
+// the compiler then sinks the first chunk's requests below that chunk's stores into the
+// loop's preheader; the loop's first wait, counting for both ways in, then also waits
+// for most of the previous chunk's stores on every chunk.
+template <bool KDA>
+__device__ __forceinline__ void keep_inputs(const PrepIn<KDA>& in) {
+  unsigned s = __float_as_uint(in.be);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) s ^= in.q[h].x ^ in.k[h].x ^ in.v[h].x;
+  if constexpr (KDA) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s ^= __float_as_uint(in.a4[i][0]);
+  } else {
+    s ^= __float_as_uint(in.al);
+  }
+  asm volatile("" ::"v"(s));
+}
+
 // KDA: the extra LDS of the prep. Km = K o exp(b_m - b) (bf16, the second operand of
 // the Gram matrix and the scores), per-group totals of the cumulative log-decays and
 // per-channel exp(b_m), exp(b_C - b_m), b_m the cumulative log-decay at token 31.
@@ -691,6 +710,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void g
   prep2_chunk<STORE_T>(sm, in, cid, q, k, v, alpha, beta, ws, Tout, T, nchunks);
   for (cid += gridDim.x; cid < nchunks; cid += gridDim.x)
     prep2_chunk<STORE_T>(sm, in, cid, q, k, v, alpha, beta, ws, Tout, T, nchunks);
+  keep_inputs(in);
 }
 
 // KDA prep, persistent: block b handles chunks b, b + grid, ...; the next chunk's inputs
@@ -710,6 +730,7 @@ __global__ __launch_bounds__(512) void kda_chunk_prep_kernel(
   prep_fetch<true>(in, q, k, v, alpha, beta, (size_t)(cid / nc) * T + (size_t)(cid % nc) * C);
   kda_prep_chunk(sm, xs, in, cid, q, k, v, alpha, beta, ws, T, nchunks);
   for (cid += gridDim.x; cid < nchunks; cid += gridDim.x) kda_prep_chunk(sm, xs, in, cid, q, k, v, alpha, beta, ws, T, nchunks);
+  keep_inputs(in);
 }
 
 // ------------------------------------------------------------------ sequential pass
