@@ -298,12 +298,43 @@ __global__ __launch_bounds__(512) void gla_bwd_grad_kernel(
   // elements each), the state before the chunk and the gradient after it ([128][128]:
   // 2048 pieces each); zeros for A and dA
   const float* E = reinterpret_cast<const float*>(wsc + kE);
+  // every global read of the staging is requested before the first one is used, so
+  // that a block (one per CU) waits one memory round trip here instead of three
+  u32x4 qin[2], kin[2], oin[2], sbin[4], dsin[4];
+  f32x4 e0in[2], e1in[2];
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     const int e = (tid + 512 * p) * 8, r = e >> 7, cc = e & 127;
-    const u32x4 qq = *reinterpret_cast<const u32x4*>(q + (tok0 + r) * kD + cc);
-    const u32x4 kk = *reinterpret_cast<const u32x4*>(k + (tok0 + r) * kD + cc);
-    const f32x4 e0 = *reinterpret_cast<const f32x4*>(E + e), e1 = *reinterpret_cast<const f32x4*>(E + e + 4);
+    qin[p] = *reinterpret_cast<const u32x4*>(q + (tok0 + r) * kD + cc);
+    kin[p] = *reinterpret_cast<const u32x4*>(k + (tok0 + r) * kD + cc);
+    e0in[p] = *reinterpret_cast<const f32x4*>(E + e);
+    e1in[p] = *reinterpret_cast<const f32x4*>(E + e + 4);
+    oin[p] = *reinterpret_cast<const u32x4*>(dO + (tok0 + r) * kD + cc);
+  }
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int e = (tid + 512 * p) * 8;
+    sbin[p] = *reinterpret_cast<const u32x4*>(wsc + kSb + (size_t)e * 2);
+    dsin[p] = *reinterpret_cast<const u32x4*>(wsc + kdS + (size_t)e * 2);
+  }
+  // V fragments of the odd waves' dA tiles (below): tile u = w + 8 i, rows 16 cb + l16
+  bf16x8 vin[3][4];
+  if (w & 1) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int u = w + 8 * i;
+      if (u >= 20) break;
+      const int p = u >> 1;
+      const int rb = p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3, cb = p - (rb * (rb + 1)) / 2;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) vin[i][ks] = ld8(v + (tok0 + 16 * cb + l16) * kD + 32 * ks + 8 * lq);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int e = (tid + 512 * p) * 8, r = e >> 7, cc = e & 127;
+    const u32x4 qq = qin[p], kk = kin[p];
+    const f32x4 e0 = e0in[p], e1 = e1in[p];
     u32x4 qt, kt;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -313,15 +344,14 @@ __global__ __launch_bounds__(512) void gla_bwd_grad_kernel(
     }
     *reinterpret_cast<u32x4*>(sm.Qt + sw_off(r, cc)) = qt;
     *reinterpret_cast<u32x4*>(sm.Kt + sw_off(r, cc)) = kt;
-    *reinterpret_cast<u32x4*>(sm.dO + sw_off(r, cc)) = *reinterpret_cast<const u32x4*>(dO + (tok0 + r) * kD + cc);
+    *reinterpret_cast<u32x4*>(sm.dO + sw_off(r, cc)) = oin[p];
   }
   // and this thread's part of sum_v dS_a o S_b for its 8 key channels 8 (tid % 16) ..
   float b1[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int e = (tid + 512 * p) * 8, r = e >> 7, cc = e & 127;
-    const u32x4 sb = *reinterpret_cast<const u32x4*>(wsc + kSb + (size_t)e * 2);
-    const u32x4 ds = *reinterpret_cast<const u32x4*>(wsc + kdS + (size_t)e * 2);
+    const u32x4 sb = sbin[p], ds = dsin[p];
     *reinterpret_cast<u32x4*>(sm.Sb + sw_off(r, cc)) = sb;
     *reinterpret_cast<u32x4*>(sm.dS + sw_off(r, cc)) = ds;
 #pragma unroll
@@ -345,18 +375,24 @@ __global__ __launch_bounds__(512) void gla_bwd_grad_kernel(
   }
   lds_barrier();
 
-  // ---- A = (Q~ K~^T) o M and dA = (dO V^T) o M: 10 lower tiles each
-  for (int u = w; u < 20; u += 8) {
+  // ---- A = (Q~ K~^T) o M and dA = (dO V^T) o M: 10 lower tiles each; wave w takes
+  // tiles u = w, w + 8, w + 16 (< 20), dA tiles on the odd waves, whose V fragments
+  // were requested with the staging reads
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int u = w + 8 * i;
+    if (u >= 20) break;
     const int p = u >> 1;
     const int rb = p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3, cb = p - (rb * (rb + 1)) / 2;
     const bool grad = u & 1;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (grad) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if (grad)
-        acc = mfma(ld8(sm.dO + sw_off(16 * rb + l16, 32 * ks + 8 * lq)),
-                   ld8(v + (tok0 + 16 * cb + l16) * kD + 32 * ks + 8 * lq), acc);
-      else
+      for (int ks = 0; ks < 4; ++ks)
+        acc = mfma(ld8(sm.dO + sw_off(16 * rb + l16, 32 * ks + 8 * lq)), vin[i][ks], acc);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
         acc = mfma(ld8(sm.Qt + sw_off(16 * rb + l16, 32 * ks + 8 * lq)),
                    ld8(sm.Kt + sw_off(16 * cb + l16, 32 * ks + 8 * lq)), acc);
     }
